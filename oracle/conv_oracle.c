@@ -1,0 +1,184 @@
+/*
+ * oracle/conv_oracle.c -- plain CPU reference for the 2-D convolution forward
+ * pass (FPROP).  TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and
+ * the CPU-baseline leg of the benchmark may load this library.  It shares no
+ * code, header, table or helper with the GPU path.
+ *
+ * What it computes (direct convolution, cross-correlation form, zero padding):
+ *
+ *   acc[n,k,p,q] = sum_{c<C} sum_{r<R} sum_{s<S}  X(n, c, p*u + r - pad_top,
+ *                                                       q*v + s - pad_left)
+ *                                                 * F[k, c, r, s]
+ *   X(n,c,h,w)   = x[n*sn + c*sc + h*sh + w*sw]  if 0 <= h < H and 0 <= w < W,
+ *                  0 otherwise
+ *   y[n,k,p,q]   = alpha * acc + beta * y_old[n,k,p,q]   (y_old unread if beta == 0)
+ *   B[n,k,p,q]   = sum_{c,r,s} |X(...) * F[k,c,r,s]|      (error-bound weight)
+ *
+ *   P = floor((H + pad_top + pad_bottom - R) / u) + 1
+ *   Q = floor((W + pad_left + pad_right - S) / v) + 1
+ *
+ * Sources: the maxDNN page (Lavin, "maxDNN: An Efficient Convolution Kernel
+ * for Deep Learning with Maxwell GPUs"), section "Proposed Method": every
+ * output feature-map coordinate is the product of the input receptive field
+ * with the filter weights; the zero-memory direct-convolution page (Zhang,
+ * Franchetti et al., "High Performance Zero-Memory Overhead Direct
+ * Convolutions"), Abstract and "Proposed Method": the convolution is computed
+ * directly, with no packing or copying; the cuDNN page (Chetlur et al.,
+ * "cuDNN: Efficient Primitives for Deep Learning"), "Proposed Method":
+ * tensors are described by dimensions plus arbitrary strides, and padding may
+ * be asymmetric (non-square inputs, asymmetric padding).  The pages print no
+ * formula: no filter flip, zero padding, floor output size, BLAS-style
+ * alpha/beta and element (not byte) strides are the plain readings taken.
+ *
+ * Arithmetic: everything in IEEE double, accumulated in the fixed order
+ * c, r, s.  Build with -ffp-contract=off so no fused multiply-add changes the
+ * rounding.  Inputs of lower precision (fp32, bf16) are widened to double by
+ * the caller, which is exact.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One convolution problem.  Mirrored field by field by a ctypes Structure in
+ * oracle/__init__.py; keep the two in the same order. */
+typedef struct {
+    int64_t N, C, H, W;            /* input dims */
+    int64_t sn, sc, sh, sw;        /* input element strides */
+    int64_t K, R, S;               /* filter dims; filter is packed K,C,R,S */
+    int64_t pad_top, pad_bottom, pad_left, pad_right;
+    int64_t u, v;                  /* stride along H, along W */
+} oracle_conv_problem;
+
+/* 0 on success, -1 if the problem is malformed or the output would be empty. */
+int oracle_output_dims(const oracle_conv_problem* pb, int64_t* P, int64_t* Q)
+{
+    if (pb->N < 1 || pb->C < 1 || pb->H < 1 || pb->W < 1) return -1;
+    if (pb->K < 1 || pb->R < 1 || pb->S < 1) return -1;
+    if (pb->u < 1 || pb->v < 1) return -1;
+    if (pb->pad_top < 0 || pb->pad_bottom < 0 || pb->pad_left < 0 || pb->pad_right < 0) return -1;
+    int64_t hspan = pb->H + pb->pad_top + pb->pad_bottom - pb->R;
+    int64_t wspan = pb->W + pb->pad_left + pb->pad_right - pb->S;
+    if (hspan < 0 || wspan < 0) return -1;
+    *P = hspan / pb->u + 1;      /* both spans are >= 0 here, so '/' is floor */
+    *Q = wspan / pb->v + 1;
+    return 0;
+}
+
+/* Input value with zero padding outside the H x W plane. */
+static double input_at(const oracle_conv_problem* pb, const double* x,
+                       int64_t n, int64_t c, int64_t h, int64_t w)
+{
+    if (h < 0 || h >= pb->H || w < 0 || w >= pb->W) return 0.0;
+    return x[n * pb->sn + c * pb->sc + h * pb->sh + w * pb->sw];
+}
+
+/* The sum for one output coordinate, and its absolute-value twin. */
+static void one_output(const oracle_conv_problem* pb, const double* x, const double* f,
+                       int64_t n, int64_t k, int64_t p, int64_t q,
+                       double* acc_out, double* bound_out)
+{
+    double acc = 0.0, bound = 0.0;
+    for (int64_t c = 0; c < pb->C; ++c) {
+        for (int64_t r = 0; r < pb->R; ++r) {
+            for (int64_t s = 0; s < pb->S; ++s) {
+                int64_t h = p * pb->u + r - pb->pad_top;
+                int64_t w = q * pb->v + s - pb->pad_left;
+                double xv = input_at(pb, x, n, c, h, w);
+                double fv = f[((k * pb->C + c) * pb->R + r) * pb->S + s];
+                double prod = xv * fv;
+                acc += prod;
+                bound += fabs(prod);
+            }
+        }
+    }
+    *acc_out = acc;
+    *bound_out = bound;
+}
+
+/*
+ * Full output.  y and bound (either may be NULL) are packed N,K,P,Q.
+ * y_old is packed N,K,P,Q and read only when beta != 0.
+ * nthreads <= 0 means the OpenMP default.  Returns 0, or -1 on a bad problem.
+ */
+int oracle_conv2d_fprop(const oracle_conv_problem* pb,
+                        const double* x, const double* f,
+                        double alpha, double beta, const double* y_old,
+                        double* y, double* bound, int nthreads)
+{
+    int64_t P, Q;
+    if (oracle_output_dims(pb, &P, &Q) != 0) return -1;
+    if (beta != 0.0 && y_old == NULL) return -1;
+    const int64_t N = pb->N, K = pb->K;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            for (int64_t p = 0; p < P; ++p) {
+                for (int64_t q = 0; q < Q; ++q) {
+                    double acc, bnd;
+                    one_output(pb, x, f, n, k, p, q, &acc, &bnd);
+                    int64_t o = ((n * K + k) * P + p) * Q + q;
+                    double val = alpha * acc;
+                    if (beta != 0.0) val += beta * y_old[o];
+                    if (y) y[o] = val;
+                    if (bound) bound[o] = bnd;
+                }
+            }
+        }
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/*
+ * Selected outputs only.  idx holds count coordinates as (n, k, p, q) int64
+ * quadruples.  y_old_vals (read only when beta != 0) holds y_old at those
+ * coordinates, in the same order; y and bound receive count values each.
+ * Returns 0, or -1 on a bad problem or a coordinate out of range.
+ */
+int oracle_conv2d_fprop_at(const oracle_conv_problem* pb,
+                           const double* x, const double* f,
+                           double alpha, double beta, const double* y_old_vals,
+                           const int64_t* idx, int64_t count,
+                           double* y, double* bound, int nthreads)
+{
+    int64_t P, Q;
+    if (oracle_output_dims(pb, &P, &Q) != 0) return -1;
+    if (beta != 0.0 && y_old_vals == NULL) return -1;
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t* t = idx + 4 * i;
+        if (t[0] < 0 || t[0] >= pb->N || t[1] < 0 || t[1] >= pb->K ||
+            t[2] < 0 || t[2] >= P || t[3] < 0 || t[3] >= Q) return -1;
+    }
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t* t = idx + 4 * i;
+        double acc, bnd;
+        one_output(pb, x, f, t[0], t[1], t[2], t[3], &acc, &bnd);
+        double val = alpha * acc;
+        if (beta != 0.0) val += beta * y_old_vals[i];
+        if (y) y[i] = val;
+        if (bound) bound[i] = bnd;
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/* Number of OpenMP threads a call with nthreads <= 0 would use. */
+int oracle_default_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,61 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each mutant is conv_oracle.c with one plausible slip planted by text
+substitution (on the CPU, in a temporary directory).  The pin suite
+(test_oracle.py) runs against the mutant's library in a child process and
+must fail.  A mutant the pins let through would mean a hole in the pins.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "conv_oracle.c")
+
+MUTANTS = {
+    "drop_last_s_tap": ("s < pb->S; ++s", "s < pb->S - 1; ++s"),
+    "drop_first_channel": ("int64_t c = 0; c < pb->C", "int64_t c = 1; c < pb->C"),
+    "flipped_filter_rows": ("* pb->R + r) * pb->S + s]", "* pb->R + (pb->R - 1 - r)) * pb->S + s]"),
+    "flipped_filter_cols": ("* pb->S + s]", "* pb->S + (pb->S - 1 - s)]"),
+    "pad_sign": ("r - pb->pad_top", "r + pb->pad_top"),
+    "left_pad_for_top": ("r - pb->pad_top", "r - pb->pad_left"),
+    "stride_swapped": ("p * pb->u + r", "p * pb->v + r"),
+    "c_r_swapped_in_filter": ("((k * pb->C + c) * pb->R + r)", "((k * pb->C + r % pb->C) * pb->R + c % pb->R)"),
+    "ceil_output_width": ("*Q = wspan / pb->v + 1;", "*Q = (wspan + pb->v - 1) / pb->v + 1;"),
+    "bottom_pad_ignored": ("pb->H + pb->pad_top + pb->pad_bottom - pb->R", "pb->H + pb->pad_top - pb->R"),
+    "beta_dropped": ("val += beta * y_old[o];", "val += 0.0 * y_old[o];"),
+    "alpha_dropped": ("double val = alpha * acc;\n                    if (beta", "double val = acc;\n                    if (beta"),
+    "bound_without_abs": ("bound += fabs(prod);", "bound += prod;"),
+    "no_zero_padding_right": ("w < 0 || w >= pb->W", "w < 0 || w > pb->W"),
+}
+
+
+def _build_and_run(name, old, new, tmp):
+    with open(SRC) as fh:
+        text = fh.read()
+    assert text.count(old) >= 1, "mutant %s no longer applies to the source" % name
+    text = text.replace(old, new)
+    src = os.path.join(tmp, name + ".c")
+    lib = os.path.join(tmp, name + ".so")
+    with open(src, "w") as fh:
+        fh.write(text)
+    subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    "-std=c11", "-o", lib, src, "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    proc = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", "test_oracle.py")],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return name, proc.returncode
+
+
+def test_every_mutant_is_caught():
+    with tempfile.TemporaryDirectory() as tmp:
+        with ThreadPoolExecutor(max_workers=4) as pool:
+            results = list(pool.map(lambda kv: _build_and_run(kv[0], kv[1][0], kv[1][1], tmp),
+                                    MUTANTS.items()))
+    survivors = [name for name, rc in results if rc == 0]
+    assert not survivors, "pins let these oracle mutants through: %s" % survivors
