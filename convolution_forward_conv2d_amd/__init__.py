@@ -1,0 +1,339 @@
+"""Python binding of libmiconv, the MI355X 2-D convolution forward pass.
+
+Argument marshalling only: every step of the convolution runs in the HIP
+kernels of ``libmiconv.so`` behind the C ABI declared in
+``include/miconv.h``.  PyTorch supplies device memory and the stream.
+The ``mic_*`` functions mirror the C calls one for one (descriptors are
+ctypes handles); ``conv2d_forward`` and ``ConvPlan`` wrap them for torch
+tensors.
+
+There is no fallback: if the library is missing the import fails.
+"""
+import ctypes
+import os
+import re
+
+import torch  # loads the HIP runtime that libmiconv then shares
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmiconv.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "miconv.h")
+
+# ---------------------------------------------------------------- enums (miconv.h)
+MIC_STATUS_SUCCESS = 0
+MIC_STATUS_BAD_PARAM = 1
+MIC_STATUS_NOT_SUPPORTED = 2
+MIC_STATUS_LAUNCH_FAILED = 3
+MIC_STATUS_INTERNAL_ERROR = 4
+MIC_STATUS_ALLOC_FAILED = 5
+
+MIC_DTYPE_F32 = 0
+MIC_DTYPE_F64 = 1
+MIC_DTYPE_BF16 = 2
+
+MIC_LAYOUT_NCHW = 0
+MIC_LAYOUT_NHWC = 1
+
+_TORCH_DTYPE = {torch.float32: MIC_DTYPE_F32, torch.float64: MIC_DTYPE_F64,
+                torch.bfloat16: MIC_DTYPE_BF16}
+_OUT_DTYPE = {torch.float32: torch.float32, torch.float64: torch.float64,
+              torch.bfloat16: torch.float32}
+
+
+class MicError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_ip = ctypes.POINTER(ctypes.c_int)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+_SIGS = {
+    "mic_status_string": ([_i], ctypes.c_char_p),
+    "mic_get_version": ([_ip, _ip, _ip], _i),
+    "mic_create": ([ctypes.POINTER(_vp)], _i),
+    "mic_destroy": ([_vp], _i),
+    "mic_set_stream": ([_vp, _vp], _i),
+    "mic_get_stream": ([_vp, ctypes.POINTER(_vp)], _i),
+    "mic_tensor_desc_create": ([ctypes.POINTER(_vp)], _i),
+    "mic_tensor_desc_destroy": ([_vp], _i),
+    "mic_tensor_desc_set": ([_vp, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64], _i),
+    "mic_tensor_desc_set_packed": ([_vp, _i, _i, _i, _i, _i, _i], _i),
+    "mic_tensor_desc_get": ([_vp, _ip, _ip, _ip, _ip, _ip, _i64p], _i),
+    "mic_filter_desc_create": ([ctypes.POINTER(_vp)], _i),
+    "mic_filter_desc_destroy": ([_vp], _i),
+    "mic_filter_desc_set": ([_vp, _i, _i, _i, _i, _i], _i),
+    "mic_filter_desc_get": ([_vp, _ip, _ip, _ip, _ip, _ip], _i),
+    "mic_conv_desc_create": ([ctypes.POINTER(_vp)], _i),
+    "mic_conv_desc_destroy": ([_vp], _i),
+    "mic_conv_desc_set": ([_vp, _i, _i, _i, _i, _i, _i], _i),
+    "mic_conv_desc_get": ([_vp, _ip, _ip, _ip, _ip, _ip, _ip], _i),
+    "mic_conv_forward_output_dim": ([_vp, _vp, _vp, _ip, _ip, _ip, _ip], _i),
+    "mic_conv_forward": ([_vp, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, ctypes.c_double,
+                          _vp, _vp], _i),
+    "mic_conv_forward_kernel_name": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_char_p, ctypes.c_size_t],
+                                     _i),
+}
+
+
+def lib():
+    """The loaded libmiconv (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmiconv.so is not built (%s); run "
+                              "`python -m convolution_forward_conv2d_amd.build`" % LIB_PATH)
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(l, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = l
+    return _lib
+
+
+def header_functions():
+    """Names of every function miconv.h declares."""
+    with open(HEADER_PATH) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mic_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status, where):
+    if status != MIC_STATUS_SUCCESS:
+        raise MicError(status, where)
+
+
+# ---------------------------------------------------------------- one-for-one wrappers
+
+def status_string(status):
+    return lib().mic_status_string(int(status)).decode()
+
+
+mic_status_string = status_string
+
+
+def mic_get_version():
+    a, b, c = _i(), _i(), _i()
+    _check(lib().mic_get_version(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "mic_get_version")
+    return a.value, b.value, c.value
+
+
+def mic_create():
+    h = _vp()
+    _check(lib().mic_create(ctypes.byref(h)), "mic_create")
+    return h
+
+
+def mic_destroy(handle):
+    _check(lib().mic_destroy(handle), "mic_destroy")
+
+
+def mic_set_stream(handle, stream):
+    """stream: a hipStream_t as an int (torch: ``stream.cuda_stream``) or None."""
+    _check(lib().mic_set_stream(handle, _vp(stream or 0)), "mic_set_stream")
+
+
+def mic_get_stream(handle):
+    s = _vp()
+    _check(lib().mic_get_stream(handle, ctypes.byref(s)), "mic_get_stream")
+    return s.value or 0
+
+
+def _create(fn, where):
+    d = _vp()
+    _check(fn(ctypes.byref(d)), where)
+    return d
+
+
+def mic_tensor_desc_create():
+    return _create(lib().mic_tensor_desc_create, "mic_tensor_desc_create")
+
+
+def mic_tensor_desc_destroy(d):
+    _check(lib().mic_tensor_desc_destroy(d), "mic_tensor_desc_destroy")
+
+
+def mic_tensor_desc_set(d, dtype, n, c, h, w, sn, sc, sh, sw):
+    _check(lib().mic_tensor_desc_set(d, dtype, n, c, h, w, sn, sc, sh, sw), "mic_tensor_desc_set")
+
+
+def mic_tensor_desc_set_packed(d, dtype, layout, n, c, h, w):
+    _check(lib().mic_tensor_desc_set_packed(d, dtype, layout, n, c, h, w), "mic_tensor_desc_set_packed")
+
+
+def mic_tensor_desc_get(d):
+    dt, n, c, h, w = _i(), _i(), _i(), _i(), _i()
+    st = (_i64 * 4)()
+    _check(lib().mic_tensor_desc_get(d, ctypes.byref(dt), ctypes.byref(n), ctypes.byref(c),
+                                     ctypes.byref(h), ctypes.byref(w), st), "mic_tensor_desc_get")
+    return dt.value, (n.value, c.value, h.value, w.value), tuple(st)
+
+
+def mic_filter_desc_create():
+    return _create(lib().mic_filter_desc_create, "mic_filter_desc_create")
+
+
+def mic_filter_desc_destroy(d):
+    _check(lib().mic_filter_desc_destroy(d), "mic_filter_desc_destroy")
+
+
+def mic_filter_desc_set(d, dtype, k, c, r, s):
+    _check(lib().mic_filter_desc_set(d, dtype, k, c, r, s), "mic_filter_desc_set")
+
+
+def mic_filter_desc_get(d):
+    vals = [_i() for _ in range(5)]
+    _check(lib().mic_filter_desc_get(d, *[ctypes.byref(v) for v in vals]), "mic_filter_desc_get")
+    return vals[0].value, tuple(v.value for v in vals[1:])
+
+
+def mic_conv_desc_create():
+    return _create(lib().mic_conv_desc_create, "mic_conv_desc_create")
+
+
+def mic_conv_desc_destroy(d):
+    _check(lib().mic_conv_desc_destroy(d), "mic_conv_desc_destroy")
+
+
+def mic_conv_desc_set(d, pad_top, pad_bottom, pad_left, pad_right, stride_h, stride_w):
+    _check(lib().mic_conv_desc_set(d, pad_top, pad_bottom, pad_left, pad_right, stride_h, stride_w),
+           "mic_conv_desc_set")
+
+
+def mic_conv_desc_get(d):
+    vals = [_i() for _ in range(6)]
+    _check(lib().mic_conv_desc_get(d, *[ctypes.byref(v) for v in vals]), "mic_conv_desc_get")
+    return tuple(v.value for v in vals)
+
+
+def mic_conv_forward_output_dim(conv, x_desc, w_desc):
+    vals = [_i() for _ in range(4)]
+    _check(lib().mic_conv_forward_output_dim(conv, x_desc, w_desc, *[ctypes.byref(v) for v in vals]),
+           "mic_conv_forward_output_dim")
+    return tuple(v.value for v in vals)
+
+
+def mic_conv_forward(handle, alpha, x_desc, x_ptr, w_desc, w_ptr, conv, beta, y_desc, y_ptr):
+    _check(lib().mic_conv_forward(handle, float(alpha), x_desc, _vp(x_ptr), w_desc, _vp(w_ptr),
+                                  conv, float(beta), y_desc, _vp(y_ptr)), "mic_conv_forward")
+
+
+def mic_conv_forward_kernel_name(handle, x_desc, w_desc, conv, y_desc):
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().mic_conv_forward_kernel_name(handle, x_desc, w_desc, conv, y_desc, buf, 128),
+           "mic_conv_forward_kernel_name")
+    return buf.value.decode()
+
+
+# ---------------------------------------------------------------- torch-facing helpers
+
+_handles = {}
+
+
+def handle_for(device=None):
+    """One library handle per device, bound to torch's current stream at call time."""
+    dev = torch.cuda.current_device() if device is None else torch.device(device).index
+    if dev not in _handles:
+        with torch.cuda.device(dev):
+            _handles[dev] = mic_create()
+    return _handles[dev]
+
+
+def output_shape(x_shape, w_shape, stride=(1, 1), padding=(0, 0, 0, 0)):
+    """(N, K, P, Q) from the library's own output-size rule (host only)."""
+    xd, wd, cd = mic_tensor_desc_create(), mic_filter_desc_create(), mic_conv_desc_create()
+    try:
+        N, C, H, W = x_shape
+        mic_tensor_desc_set_packed(xd, MIC_DTYPE_F32, MIC_LAYOUT_NCHW, N, C, H, W)
+        mic_filter_desc_set(wd, MIC_DTYPE_F32, *w_shape)
+        mic_conv_desc_set(cd, *padding, *stride)
+        return mic_conv_forward_output_dim(cd, xd, wd)
+    finally:
+        mic_tensor_desc_destroy(xd)
+        mic_filter_desc_destroy(wd)
+        mic_conv_desc_destroy(cd)
+
+
+def _element_strides(t):
+    return tuple(int(s) for s in t.stride())
+
+
+class ConvPlan:
+    """Descriptors for one (x, w, y) triple, reusable across calls.
+
+    x: (N, C, H, W) tensor of any strides; w: contiguous (K, C, R, S);
+    y: (N, K, P, Q) tensor of any strides.  Tensors must stay alive and in
+    place while the plan is used.
+    """
+
+    def __init__(self, x, w, y, stride=(1, 1), padding=(0, 0, 0, 0), handle=None):
+        if x.dim() != 4 or w.dim() != 4 or y.dim() != 4:
+            raise ValueError("x, w, y must be 4-D")
+        if not w.is_contiguous():
+            raise ValueError("w must be packed K,C,R,S (contiguous)")
+        for t in (x, w, y):
+            if t.dtype not in _TORCH_DTYPE:
+                raise TypeError("unsupported dtype %s" % t.dtype)
+        self.x, self.w, self.y = x, w, y
+        self.handle = handle if handle is not None else handle_for(x.device)
+        self.xd, self.wd, self.yd = mic_tensor_desc_create(), mic_filter_desc_create(), mic_tensor_desc_create()
+        self.cd = mic_conv_desc_create()
+        mic_tensor_desc_set(self.xd, _TORCH_DTYPE[x.dtype], *x.shape, *_element_strides(x))
+        mic_filter_desc_set(self.wd, _TORCH_DTYPE[w.dtype], *w.shape)
+        mic_tensor_desc_set(self.yd, _TORCH_DTYPE[y.dtype], *y.shape, *_element_strides(y))
+        mic_conv_desc_set(self.cd, *padding, *stride)
+        self.flops = 2.0 * y.shape[0] * y.shape[1] * y.shape[2] * y.shape[3] * w.shape[1] * w.shape[2] * w.shape[3]
+
+    def kernel_name(self):
+        return mic_conv_forward_kernel_name(self.handle, self.xd, self.wd, self.cd, self.yd)
+
+    def __call__(self, alpha=1.0, beta=0.0, stream=None):
+        s = stream if stream is not None else torch.cuda.current_stream(self.x.device)
+        mic_set_stream(self.handle, s.cuda_stream)
+        mic_conv_forward(self.handle, alpha, self.xd, self.x.data_ptr(), self.wd, self.w.data_ptr(),
+                         self.cd, beta, self.yd, self.y.data_ptr())
+        return self.y
+
+    def close(self):
+        for d, fn in ((self.xd, mic_tensor_desc_destroy), (self.yd, mic_tensor_desc_destroy),
+                      (self.wd, mic_filter_desc_destroy), (self.cd, mic_conv_desc_destroy)):
+            if d is not None:
+                fn(d)
+        self.xd = self.yd = self.wd = self.cd = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def conv2d_forward(x, w, stride=(1, 1), padding=(0, 0, 0, 0), y=None, alpha=1.0, beta=0.0):
+    """y <- alpha * conv(x, w) + beta * y on torch's current stream.
+
+    padding = (top, bottom, left, right); stride = (u along H, v along W).
+    With y None a new output is allocated (caller memory, in x's memory
+    format; fp32 for bf16 inputs) and beta must be 0.
+    """
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    N, K, P, Q = output_shape(tuple(x.shape), tuple(w.shape), stride, padding)
+    if y is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing y")
+        fmt = torch.channels_last if (x.stride(1) == 1 and x.shape[1] > 1) else torch.contiguous_format
+        y = torch.empty((N, K, P, Q), dtype=_OUT_DTYPE[x.dtype], device=x.device, memory_format=fmt)
+    plan = ConvPlan(x, w.contiguous(), y, stride, padding)
+    try:
+        plan(alpha, beta)
+    finally:
+        plan.close()
+    return y

@@ -1,0 +1,34 @@
+// kernels.h -- kernel variants of libmiconv and their launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "conv_params.h"
+
+namespace miconv {
+
+enum class Variant : int {
+    DIRECT = 0,          // one thread per output, any dtype/layout (plain loop, no MFMA)
+    MFMA_F32_128x128,
+    MFMA_F32_128x64,
+    MFMA_F32_256x32,
+    MFMA_F32_64x128,
+    MFMA_F64_128x128,
+    MFMA_F64_128x64,
+    MFMA_F64_64x64,
+    MFMA_BF16_128x128,
+    MFMA_BF16_128x64,
+    MFMA_BF16_256x32,
+    COUNT
+};
+
+enum class DType : int { F32 = 0, F64 = 1, BF16 = 2 };
+
+// Launch an implicit-GEMM MFMA variant.  bvec: the filter may be read with
+// 16-byte loads (w 16-byte aligned and C*R*S a multiple of the vector).
+hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, hipStream_t stream);
+
+// Launch the plain direct kernel (one thread per output element).
+hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);
+
+}  // namespace miconv

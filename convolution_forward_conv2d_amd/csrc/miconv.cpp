@@ -1,0 +1,524 @@
+// miconv.cpp -- host side of the libmiconv C ABI: descriptors, validation,
+// output size, kernel-variant choice and launch.
+//
+// Descriptor model: cuDNN page (Chetlur et al.), "Proposed Method": opaque
+// tensor and filter descriptors with arbitrary strides, user-owned device
+// memory, no auxiliary buffers, asymmetric padding.  Variant choice: the
+// zero-memory direct-convolution page, "Proposed Method": blocking
+// parameters chosen per shape by an analytical model.
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include <hip/hip_runtime.h>
+
+#include "miconv.h"
+#include "conv_params.h"
+#include "kernels.h"
+
+struct mic_handle_st {
+    int device;
+    int num_cu;
+    hipStream_t stream;
+};
+
+struct mic_tensor_desc_st {
+    bool set;
+    mic_dtype dtype;
+    int n, c, h, w;
+    int64_t sn, sc, sh, sw;
+};
+
+struct mic_filter_desc_st {
+    bool set;
+    mic_dtype dtype;
+    int k, c, r, s;
+};
+
+struct mic_conv_desc_st {
+    bool set;
+    int pad_top, pad_bottom, pad_left, pad_right;
+    int u, v;
+};
+
+namespace {
+
+using miconv::ConvParams;
+using miconv::DType;
+using miconv::FastDiv;
+using miconv::Variant;
+
+constexpr int64_t kMaxOffset = int64_t(1) << 30;   // element offsets stay far below 2^31
+constexpr int kDefaultCUs = 256;                   // MI355X
+
+bool valid_dtype(mic_dtype d) { return d == MIC_DTYPE_F32 || d == MIC_DTYPE_F64 || d == MIC_DTYPE_BF16; }
+
+size_t dtype_size(mic_dtype d)
+{
+    switch (d) {
+    case MIC_DTYPE_F32: return 4;
+    case MIC_DTYPE_F64: return 8;
+    case MIC_DTYPE_BF16: return 2;
+    }
+    return 0;
+}
+
+// Highest element offset a strided N,C,H,W tensor reaches, plus one.
+int64_t extent(const mic_tensor_desc_st& d)
+{
+    return (int64_t)(d.n - 1) * d.sn + (int64_t)(d.c - 1) * d.sc + (int64_t)(d.h - 1) * d.sh +
+           (int64_t)(d.w - 1) * d.sw + 1;
+}
+
+mic_status output_dims(const mic_conv_desc_st* cd, const mic_tensor_desc_st* xd,
+                       const mic_filter_desc_st* wd, int* n, int* k, int* p, int* q)
+{
+    if (!cd || !xd || !wd || !cd->set || !xd->set || !wd->set) return MIC_STATUS_BAD_PARAM;
+    if (xd->c != wd->c) return MIC_STATUS_BAD_PARAM;
+    const int64_t hspan = (int64_t)xd->h + cd->pad_top + cd->pad_bottom - wd->r;
+    const int64_t wspan = (int64_t)xd->w + cd->pad_left + cd->pad_right - wd->s;
+    if (hspan < 0 || wspan < 0) return MIC_STATUS_BAD_PARAM;   // filter exceeds padded input
+    const int64_t P = hspan / cd->u + 1;                          // floor: spans are >= 0
+    const int64_t Q = wspan / cd->v + 1;
+    if (P > INT32_MAX || Q > INT32_MAX) return MIC_STATUS_NOT_SUPPORTED;
+    *n = xd->n;
+    *k = wd->k;
+    *p = (int)P;
+    *q = (int)Q;
+    return MIC_STATUS_SUCCESS;
+}
+
+struct Candidate {
+    Variant v;
+    int tm, tn;
+    const char* name;
+};
+
+const Candidate kF32[] = {
+    {Variant::MFMA_F32_128x128, 128, 128, "mfma_f32_128x128"},
+    {Variant::MFMA_F32_128x64, 128, 64, "mfma_f32_128x64"},
+    {Variant::MFMA_F32_64x128, 64, 128, "mfma_f32_64x128"},
+    {Variant::MFMA_F32_256x32, 256, 32, "mfma_f32_256x32"},
+};
+const Candidate kF64[] = {
+    {Variant::MFMA_F64_128x128, 128, 128, "mfma_f64_128x128"},
+    {Variant::MFMA_F64_128x64, 128, 64, "mfma_f64_128x64"},
+    {Variant::MFMA_F64_64x64, 64, 64, "mfma_f64_64x64"},
+};
+const Candidate kBF16[] = {
+    {Variant::MFMA_BF16_128x128, 128, 128, "mfma_bf16_128x128"},
+    {Variant::MFMA_BF16_128x64, 128, 64, "mfma_bf16_128x64"},
+    {Variant::MFMA_BF16_256x32, 256, 32, "mfma_bf16_256x32"},
+};
+const Candidate kDirect = {Variant::DIRECT, 0, 0, "direct"};
+
+struct Plan {
+    mic_status status;
+    DType dt;
+    ConvParams p;
+    Candidate cand;
+    bool bvec;
+};
+
+void candidates(DType dt, const Candidate** list, int* count)
+{
+    switch (dt) {
+    case DType::F32: *list = kF32; *count = (int)(sizeof(kF32) / sizeof(kF32[0])); return;
+    case DType::F64: *list = kF64; *count = (int)(sizeof(kF64) / sizeof(kF64[0])); return;
+    case DType::BF16: *list = kBF16; *count = (int)(sizeof(kBF16) / sizeof(kBF16[0])); return;
+    }
+    *list = nullptr;
+    *count = 0;
+}
+
+// Analytical tile choice: the busiest compute unit runs ceil(tiles / CUs)
+// tiles; a tile costs its MFMA work divided by a reuse factor that drops
+// for thin tiles (fewer MACs per loaded element).
+Candidate choose_tile(DType dt, int M, int K, int num_cu)
+{
+    const Candidate* list;
+    int count;
+    candidates(dt, &list, &count);
+    double best = 0;
+    int best_i = 0;
+    for (int i = 0; i < count; ++i) {
+        const int64_t tiles = (int64_t)((M + list[i].tm - 1) / list[i].tm) * ((K + list[i].tn - 1) / list[i].tn);
+        const int64_t rounds = (tiles + num_cu - 1) / num_cu;
+        const double reuse = (double)list[i].tm * list[i].tn / (list[i].tm + list[i].tn);
+        const double eff = reuse >= 48.0 ? 1.0 : reuse / 48.0;
+        const double cost = (double)rounds * list[i].tm * list[i].tn / eff;
+        if (i == 0 || cost < best) {
+            best = cost;
+            best_i = i;
+        }
+    }
+    return list[best_i];
+}
+
+Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void* x,
+               const mic_filter_desc_st* wd, const void* w, const mic_conv_desc_st* cd,
+               const mic_tensor_desc_st* yd, const void* y, double alpha, double beta,
+               bool need_pointers)
+{
+    Plan pl;
+    memset(&pl, 0, sizeof(pl));
+    pl.status = MIC_STATUS_BAD_PARAM;
+    if (!xd || !wd || !cd || !yd) return pl;
+    if (!xd->set || !wd->set || !cd->set || !yd->set) return pl;
+    if (need_pointers && (!x || !w || !y)) return pl;
+    int n, k, P, Q;
+    mic_status st = output_dims(cd, xd, wd, &n, &k, &P, &Q);
+    if (st != MIC_STATUS_SUCCESS) {
+        pl.status = st;
+        return pl;
+    }
+    if (yd->n != n || yd->c != k || yd->h != P || yd->w != Q) return pl;
+
+    // dtype combination
+    if (xd->dtype == MIC_DTYPE_F32 && wd->dtype == MIC_DTYPE_F32 && yd->dtype == MIC_DTYPE_F32)
+        pl.dt = DType::F32;
+    else if (xd->dtype == MIC_DTYPE_F64 && wd->dtype == MIC_DTYPE_F64 && yd->dtype == MIC_DTYPE_F64)
+        pl.dt = DType::F64;
+    else if (xd->dtype == MIC_DTYPE_BF16 && wd->dtype == MIC_DTYPE_BF16 && yd->dtype == MIC_DTYPE_F32)
+        pl.dt = DType::BF16;
+    else {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;
+        return pl;
+    }
+
+    // size limits: 32-bit element offsets with headroom
+    const int64_t M = (int64_t)n * P * Q;
+    const int64_t Kred = (int64_t)wd->c * wd->r * wd->s;
+    const int64_t wsize = (int64_t)wd->k * Kred;
+    if (extent(*xd) >= kMaxOffset || extent(*yd) >= kMaxOffset || wsize >= kMaxOffset ||
+        M >= kMaxOffset || Kred >= kMaxOffset || xd->sn >= kMaxOffset || xd->sc >= kMaxOffset ||
+        xd->sh >= kMaxOffset || xd->sw >= kMaxOffset || yd->sn >= kMaxOffset ||
+        yd->sc >= kMaxOffset || yd->sh >= kMaxOffset || yd->sw >= kMaxOffset) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;
+        return pl;
+    }
+    // element alignment of the data pointers
+    if (need_pointers) {
+        const size_t ie = dtype_size(xd->dtype), oe = dtype_size(yd->dtype);
+        if ((uintptr_t)x % ie || (uintptr_t)w % ie || (uintptr_t)y % oe) return pl;
+    }
+
+    ConvParams& p = pl.p;
+    p.x = x;
+    p.w = w;
+    p.y = const_cast<void*>(y);
+    p.N = n;
+    p.C = xd->c;
+    p.H = xd->h;
+    p.W = xd->w;
+    p.K = k;
+    p.R = wd->r;
+    p.S = wd->s;
+    p.P = P;
+    p.Q = Q;
+    p.u = cd->u;
+    p.v = cd->v;
+    p.pad_top = cd->pad_top;
+    p.pad_left = cd->pad_left;
+    p.sxn = (int)xd->sn;
+    p.sxc = (int)xd->sc;
+    p.sxh = (int)xd->sh;
+    p.sxw = (int)xd->sw;
+    p.syn = (int)yd->sn;
+    p.syk = (int)yd->sc;
+    p.syp = (int)yd->sh;
+    p.syq = (int)yd->sw;
+    p.M = (int)M;
+    p.Kred = (int)Kred;
+    p.div_pq = FastDiv((uint32_t)(P * Q));
+    p.div_q = FastDiv((uint32_t)Q);
+    p.div_rs = FastDiv((uint32_t)(wd->r * wd->s));
+    p.div_s = FastDiv((uint32_t)wd->s);
+    p.alpha = alpha;
+    p.beta = beta;
+
+    const int num_cu = h ? h->num_cu : kDefaultCUs;
+    pl.cand = choose_tile(pl.dt, p.M, p.K, num_cu);
+
+    // MIC_FORCE_VARIANT=<name> pins a variant (tests walk every variant with it)
+    if (const char* force = getenv("MIC_FORCE_VARIANT")) {
+        if (force[0]) {
+            if (strcmp(force, kDirect.name) == 0) {
+                pl.cand = kDirect;
+            } else {
+                const Candidate* list;
+                int count;
+                candidates(pl.dt, &list, &count);
+                int found = -1;
+                for (int i = 0; i < count; ++i)
+                    if (strcmp(force, list[i].name) == 0) found = i;
+                if (found < 0) {
+                    pl.status = MIC_STATUS_NOT_SUPPORTED;
+                    return pl;
+                }
+                pl.cand = list[found];
+            }
+        }
+    }
+    const size_t ie = dtype_size(xd->dtype);
+    pl.bvec = ((Kred * (int64_t)ie) % 16 == 0) && ((uintptr_t)w % 16 == 0);
+    pl.status = MIC_STATUS_SUCCESS;
+    return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mic_status_string(mic_status status)
+{
+    switch (status) {
+    case MIC_STATUS_SUCCESS: return "success";
+    case MIC_STATUS_BAD_PARAM: return "bad parameter";
+    case MIC_STATUS_NOT_SUPPORTED: return "not supported";
+    case MIC_STATUS_LAUNCH_FAILED: return "kernel launch failed";
+    case MIC_STATUS_INTERNAL_ERROR: return "internal error";
+    case MIC_STATUS_ALLOC_FAILED: return "host allocation failed";
+    }
+    return "unknown status";
+}
+
+mic_status mic_get_version(int* major, int* minor, int* patch)
+{
+    if (major) *major = MICONV_VERSION_MAJOR;
+    if (minor) *minor = MICONV_VERSION_MINOR;
+    if (patch) *patch = MICONV_VERSION_PATCH;
+    return MIC_STATUS_SUCCESS;
+}
+
+// ---------------------------------------------------------------- handle
+
+mic_status mic_create(mic_handle* handle)
+{
+    if (!handle) return MIC_STATUS_BAD_PARAM;
+    *handle = nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MIC_STATUS_INTERNAL_ERROR;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MIC_STATUS_INTERNAL_ERROR;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MIC_STATUS_NOT_SUPPORTED;
+    mic_handle_st* h = new (std::nothrow) mic_handle_st;
+    if (!h) return MIC_STATUS_ALLOC_FAILED;
+    h->device = dev;
+    h->num_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kDefaultCUs;
+    h->stream = nullptr;
+    *handle = h;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_destroy(mic_handle handle)
+{
+    if (!handle) return MIC_STATUS_BAD_PARAM;
+    delete handle;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_set_stream(mic_handle handle, void* stream)
+{
+    if (!handle) return MIC_STATUS_BAD_PARAM;
+    handle->stream = static_cast<hipStream_t>(stream);
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_get_stream(mic_handle handle, void** stream)
+{
+    if (!handle || !stream) return MIC_STATUS_BAD_PARAM;
+    *stream = handle->stream;
+    return MIC_STATUS_SUCCESS;
+}
+
+// ---------------------------------------------------------------- tensor descriptor
+
+mic_status mic_tensor_desc_create(mic_tensor_desc* desc)
+{
+    if (!desc) return MIC_STATUS_BAD_PARAM;
+    *desc = new (std::nothrow) mic_tensor_desc_st();
+    return *desc ? MIC_STATUS_SUCCESS : MIC_STATUS_ALLOC_FAILED;
+}
+
+mic_status mic_tensor_desc_destroy(mic_tensor_desc desc)
+{
+    if (!desc) return MIC_STATUS_BAD_PARAM;
+    delete desc;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_tensor_desc_set(mic_tensor_desc desc, mic_dtype dtype, int n, int c, int h, int w,
+                               int64_t sn, int64_t sc, int64_t sh, int64_t sw)
+{
+    if (!desc || !valid_dtype(dtype)) return MIC_STATUS_BAD_PARAM;
+    if (n < 1 || c < 1 || h < 1 || w < 1) return MIC_STATUS_BAD_PARAM;
+    if (sn < 1 || sc < 1 || sh < 1 || sw < 1) return MIC_STATUS_BAD_PARAM;
+    desc->set = true;
+    desc->dtype = dtype;
+    desc->n = n;
+    desc->c = c;
+    desc->h = h;
+    desc->w = w;
+    desc->sn = sn;
+    desc->sc = sc;
+    desc->sh = sh;
+    desc->sw = sw;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_tensor_desc_set_packed(mic_tensor_desc desc, mic_dtype dtype, mic_layout layout,
+                                      int n, int c, int h, int w)
+{
+    if (n < 1 || c < 1 || h < 1 || w < 1) return MIC_STATUS_BAD_PARAM;
+    const int64_t C = c, H = h, W = w;
+    switch (layout) {
+    case MIC_LAYOUT_NCHW: return mic_tensor_desc_set(desc, dtype, n, c, h, w, C * H * W, H * W, W, 1);
+    case MIC_LAYOUT_NHWC: return mic_tensor_desc_set(desc, dtype, n, c, h, w, H * W * C, 1, W * C, C);
+    }
+    return MIC_STATUS_BAD_PARAM;
+}
+
+mic_status mic_tensor_desc_get(mic_tensor_desc desc, mic_dtype* dtype, int* n, int* c, int* h,
+                               int* w, int64_t* strides)
+{
+    if (!desc || !desc->set) return MIC_STATUS_BAD_PARAM;
+    if (dtype) *dtype = desc->dtype;
+    if (n) *n = desc->n;
+    if (c) *c = desc->c;
+    if (h) *h = desc->h;
+    if (w) *w = desc->w;
+    if (strides) {
+        strides[0] = desc->sn;
+        strides[1] = desc->sc;
+        strides[2] = desc->sh;
+        strides[3] = desc->sw;
+    }
+    return MIC_STATUS_SUCCESS;
+}
+
+// ---------------------------------------------------------------- filter descriptor
+
+mic_status mic_filter_desc_create(mic_filter_desc* desc)
+{
+    if (!desc) return MIC_STATUS_BAD_PARAM;
+    *desc = new (std::nothrow) mic_filter_desc_st();
+    return *desc ? MIC_STATUS_SUCCESS : MIC_STATUS_ALLOC_FAILED;
+}
+
+mic_status mic_filter_desc_destroy(mic_filter_desc desc)
+{
+    if (!desc) return MIC_STATUS_BAD_PARAM;
+    delete desc;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_filter_desc_set(mic_filter_desc desc, mic_dtype dtype, int k, int c, int r, int s)
+{
+    if (!desc || !valid_dtype(dtype)) return MIC_STATUS_BAD_PARAM;
+    if (k < 1 || c < 1 || r < 1 || s < 1) return MIC_STATUS_BAD_PARAM;
+    desc->set = true;
+    desc->dtype = dtype;
+    desc->k = k;
+    desc->c = c;
+    desc->r = r;
+    desc->s = s;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_filter_desc_get(mic_filter_desc desc, mic_dtype* dtype, int* k, int* c, int* r, int* s)
+{
+    if (!desc || !desc->set) return MIC_STATUS_BAD_PARAM;
+    if (dtype) *dtype = desc->dtype;
+    if (k) *k = desc->k;
+    if (c) *c = desc->c;
+    if (r) *r = desc->r;
+    if (s) *s = desc->s;
+    return MIC_STATUS_SUCCESS;
+}
+
+// ---------------------------------------------------------------- convolution descriptor
+
+mic_status mic_conv_desc_create(mic_conv_desc* desc)
+{
+    if (!desc) return MIC_STATUS_BAD_PARAM;
+    *desc = new (std::nothrow) mic_conv_desc_st();
+    return *desc ? MIC_STATUS_SUCCESS : MIC_STATUS_ALLOC_FAILED;
+}
+
+mic_status mic_conv_desc_destroy(mic_conv_desc desc)
+{
+    if (!desc) return MIC_STATUS_BAD_PARAM;
+    delete desc;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_conv_desc_set(mic_conv_desc desc, int pad_top, int pad_bottom, int pad_left,
+                             int pad_right, int stride_h, int stride_w)
+{
+    if (!desc) return MIC_STATUS_BAD_PARAM;
+    if (pad_top < 0 || pad_bottom < 0 || pad_left < 0 || pad_right < 0) return MIC_STATUS_BAD_PARAM;
+    if (stride_h < 1 || stride_w < 1) return MIC_STATUS_BAD_PARAM;
+    desc->set = true;
+    desc->pad_top = pad_top;
+    desc->pad_bottom = pad_bottom;
+    desc->pad_left = pad_left;
+    desc->pad_right = pad_right;
+    desc->u = stride_h;
+    desc->v = stride_w;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_conv_desc_get(mic_conv_desc desc, int* pad_top, int* pad_bottom, int* pad_left,
+                             int* pad_right, int* stride_h, int* stride_w)
+{
+    if (!desc || !desc->set) return MIC_STATUS_BAD_PARAM;
+    if (pad_top) *pad_top = desc->pad_top;
+    if (pad_bottom) *pad_bottom = desc->pad_bottom;
+    if (pad_left) *pad_left = desc->pad_left;
+    if (pad_right) *pad_right = desc->pad_right;
+    if (stride_h) *stride_h = desc->u;
+    if (stride_w) *stride_w = desc->v;
+    return MIC_STATUS_SUCCESS;
+}
+
+// ---------------------------------------------------------------- forward
+
+mic_status mic_conv_forward_output_dim(mic_conv_desc conv, mic_tensor_desc x_desc,
+                                       mic_filter_desc w_desc, int* n, int* k, int* p, int* q)
+{
+    if (!n || !k || !p || !q) return MIC_STATUS_BAD_PARAM;
+    return output_dims(conv, x_desc, w_desc, n, k, p, q);
+}
+
+mic_status mic_conv_forward(mic_handle handle, double alpha, mic_tensor_desc x_desc, const void* x,
+                            mic_filter_desc w_desc, const void* w, mic_conv_desc conv, double beta,
+                            mic_tensor_desc y_desc, void* y)
+{
+    if (!handle) return MIC_STATUS_BAD_PARAM;
+    Plan pl = make_plan(handle, x_desc, x, w_desc, w, conv, y_desc, y, alpha, beta, true);
+    if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    hipError_t err;
+    if (pl.cand.v == Variant::DIRECT)
+        err = miconv::launch_direct(pl.dt, pl.p, handle->stream);
+    else
+        err = miconv::launch_mfma(pl.cand.v, pl.p, pl.bvec, handle->stream);
+    return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
+}
+
+mic_status mic_conv_forward_kernel_name(mic_handle handle, mic_tensor_desc x_desc,
+                                        mic_filter_desc w_desc, mic_conv_desc conv,
+                                        mic_tensor_desc y_desc, char* buf, size_t buflen)
+{
+    if (!buf) return MIC_STATUS_BAD_PARAM;
+    Plan pl = make_plan(handle, x_desc, nullptr, w_desc, nullptr, conv, y_desc, nullptr, 1.0, 0.0, false);
+    if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    const size_t len = strlen(pl.cand.name);
+    if (len + 1 > buflen) return MIC_STATUS_BAD_PARAM;
+    memcpy(buf, pl.cand.name, len + 1);
+    return MIC_STATUS_SUCCESS;
+}
+
+}  // extern "C"

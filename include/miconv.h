@@ -1,0 +1,184 @@
+/*
+ * miconv.h -- C ABI of libmiconv, the 2-D convolution forward pass (FPROP)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (direct convolution, cross-correlation form, zero padding):
+ *
+ *   y[n,k,p,q] = alpha * sum_{c,r,s} X(n, c, p*u + r - pad_top, q*v + s - pad_left) * F[k,c,r,s]
+ *              + beta  * y[n,k,p,q]
+ *
+ *   X(n,c,h,w) = x[n*sn + c*sc + h*sh + w*sw] inside 0 <= h < H, 0 <= w < W, else 0
+ *   P = floor((H + pad_top + pad_bottom - R) / u) + 1
+ *   Q = floor((W + pad_left + pad_right - S) / v) + 1
+ *
+ * Sources: cuDNN page (Chetlur et al., "cuDNN: Efficient Primitives for Deep
+ * Learning"), "Proposed Method": a C API over opaque tensor and filter
+ * descriptors with arbitrary strides and layouts, single and double
+ * precision, user-owned GPU memory and no auxiliary buffers, non-square
+ * inputs and asymmetric padding.  maxDNN page (Lavin), "Proposed Method":
+ * each output coordinate is the product of the input receptive field with
+ * the filter weights.  Zero-memory direct-convolution page (Zhang, Franchetti
+ * et al.), Abstract and "Proposed Method": computed directly, without packing
+ * or copying, with no memory beyond the operands.
+ *
+ * Conventions for every call:
+ *   - Every call returns a mic_status; nothing is thrown across the ABI.
+ *   - Descriptors and handles are host objects owned by the caller (create /
+ *     destroy).  They hold no device memory.
+ *   - Data pointers are device pointers owned by the caller.  The library
+ *     never allocates, frees or keeps device memory: there is no workspace.
+ *   - Strides are counted in elements, not bytes, and must be >= 1.
+ *   - Not thread-safe per handle: one handle, one host thread at a time.
+ */
+#ifndef MICONV_H
+#define MICONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MICONV_VERSION_MAJOR 0
+#define MICONV_VERSION_MINOR 1
+#define MICONV_VERSION_PATCH 0
+
+typedef enum {
+    MIC_STATUS_SUCCESS = 0,
+    MIC_STATUS_BAD_PARAM = 1,       /* null pointer, bad dimension/stride, shape mismatch */
+    MIC_STATUS_NOT_SUPPORTED = 2,   /* valid request this library does not implement */
+    MIC_STATUS_LAUNCH_FAILED = 3,   /* the HIP runtime refused a kernel launch */
+    MIC_STATUS_INTERNAL_ERROR = 4,  /* HIP runtime error outside a launch (device query) */
+    MIC_STATUS_ALLOC_FAILED = 5     /* host allocation of a handle or descriptor failed */
+} mic_status;
+
+/* Element types.  Allowed (x, w, y) combinations: (F32, F32, F32),
+ * (F64, F64, F64) and (BF16, BF16, F32) (bf16 inputs, fp32 accumulation and
+ * output).  Anything else is MIC_STATUS_NOT_SUPPORTED. */
+typedef enum {
+    MIC_DTYPE_F32 = 0,
+    MIC_DTYPE_F64 = 1,
+    MIC_DTYPE_BF16 = 2
+} mic_dtype;
+
+/* Packed layouts for mic_tensor_desc_set_packed.  Any other layout is given
+ * through explicit strides with mic_tensor_desc_set. */
+typedef enum {
+    MIC_LAYOUT_NCHW = 0,
+    MIC_LAYOUT_NHWC = 1
+} mic_layout;
+
+typedef struct mic_handle_st* mic_handle;
+typedef struct mic_tensor_desc_st* mic_tensor_desc;
+typedef struct mic_filter_desc_st* mic_filter_desc;
+typedef struct mic_conv_desc_st* mic_conv_desc;
+
+/* Static, never-NULL text for a status (unknown values give "unknown status"). */
+const char* mic_status_string(mic_status status);
+
+/* Library version; any pointer may be NULL. */
+mic_status mic_get_version(int* major, int* minor, int* patch);
+
+/* ---------------------------------------------------------------- handle */
+
+/* Binds the calling thread's current HIP device and the null stream.
+ * Queries the device (compute-unit count, architecture); fails with
+ * MIC_STATUS_INTERNAL_ERROR when no HIP device is usable and with
+ * MIC_STATUS_NOT_SUPPORTED on a device other than gfx950.  No device memory
+ * is allocated. */
+mic_status mic_create(mic_handle* handle);
+mic_status mic_destroy(mic_handle handle);
+
+/* stream is a hipStream_t (NULL = the null stream).  Later calls on this
+ * handle enqueue their kernels on it.  The caller keeps the stream alive. */
+mic_status mic_set_stream(mic_handle handle, void* stream);
+mic_status mic_get_stream(mic_handle handle, void** stream);
+
+/* ---------------------------------------------------------------- tensor descriptor */
+
+mic_status mic_tensor_desc_create(mic_tensor_desc* desc);
+mic_status mic_tensor_desc_destroy(mic_tensor_desc desc);
+
+/* Logical N, C, H, W with element strides sn, sc, sh, sw (any order, any
+ * gaps: NCHW, NHWC, padded rows and sub-tensor views all fit).  Dimensions
+ * and strides must be >= 1, else MIC_STATUS_BAD_PARAM. */
+mic_status mic_tensor_desc_set(mic_tensor_desc desc, mic_dtype dtype,
+                               int n, int c, int h, int w,
+                               int64_t sn, int64_t sc, int64_t sh, int64_t sw);
+
+/* Same, with the strides of a packed NCHW or NHWC tensor. */
+mic_status mic_tensor_desc_set_packed(mic_tensor_desc desc, mic_dtype dtype, mic_layout layout,
+                                      int n, int c, int h, int w);
+
+/* Read back; any output pointer may be NULL.  strides receives 4 values
+ * (sn, sc, sh, sw).  MIC_STATUS_BAD_PARAM if the descriptor was never set. */
+mic_status mic_tensor_desc_get(mic_tensor_desc desc, mic_dtype* dtype,
+                               int* n, int* c, int* h, int* w, int64_t* strides);
+
+/* ---------------------------------------------------------------- filter descriptor */
+
+mic_status mic_filter_desc_create(mic_filter_desc* desc);
+mic_status mic_filter_desc_destroy(mic_filter_desc desc);
+
+/* K filters of C channels and R x S taps, packed K,C,R,S (S fastest).
+ * Dimensions must be >= 1. */
+mic_status mic_filter_desc_set(mic_filter_desc desc, mic_dtype dtype, int k, int c, int r, int s);
+mic_status mic_filter_desc_get(mic_filter_desc desc, mic_dtype* dtype, int* k, int* c, int* r, int* s);
+
+/* ---------------------------------------------------------------- convolution descriptor */
+
+mic_status mic_conv_desc_create(mic_conv_desc* desc);
+mic_status mic_conv_desc_destroy(mic_conv_desc desc);
+
+/* Per-side zero padding (>= 0) and stride u along H, v along W (>= 1).
+ * No dilation, no groups, no filter flip. */
+mic_status mic_conv_desc_set(mic_conv_desc desc, int pad_top, int pad_bottom,
+                             int pad_left, int pad_right, int stride_h, int stride_w);
+mic_status mic_conv_desc_get(mic_conv_desc desc, int* pad_top, int* pad_bottom,
+                             int* pad_left, int* pad_right, int* stride_h, int* stride_w);
+
+/* ---------------------------------------------------------------- forward */
+
+/* Output dimensions (N, K, P, Q).  Host only, no device needed.
+ * MIC_STATUS_BAD_PARAM if a descriptor is unset, the channel counts differ,
+ * or the output would be empty (P < 1 or Q < 1). */
+mic_status mic_conv_forward_output_dim(mic_conv_desc conv, mic_tensor_desc x_desc,
+                                       mic_filter_desc w_desc, int* n, int* k, int* p, int* q);
+
+/* y <- alpha * conv(x, w) + beta * y, on the handle's stream, asynchronously.
+ *
+ * x: device memory described by x_desc; w: packed K,C,R,S device memory;
+ * y: device memory described by y_desc, whose dims must equal the output
+ * dims.  alpha and beta are rounded to the accumulation type (fp32 for F32
+ * and BF16 inputs, fp64 for F64).  With beta == 0, y is only written (its
+ * old contents, NaN included, never reach the result).
+ *
+ * No workspace: nothing is allocated.  The return value covers validation
+ * and the launch only; execution errors surface at the next synchronisation.
+ * y must not overlap x or w, and y's strides must not map two outputs to one
+ * address (neither is checked).  Tensors whose highest element offset
+ * reaches 2^31 are MIC_STATUS_NOT_SUPPORTED.
+ *
+ * Errors: MIC_STATUS_BAD_PARAM (null handle/descriptor/pointer, unset
+ * descriptor, shape mismatch), MIC_STATUS_NOT_SUPPORTED (dtype combination,
+ * size limit), MIC_STATUS_LAUNCH_FAILED. */
+mic_status mic_conv_forward(mic_handle handle, double alpha,
+                            mic_tensor_desc x_desc, const void* x,
+                            mic_filter_desc w_desc, const void* w,
+                            mic_conv_desc conv, double beta,
+                            mic_tensor_desc y_desc, void* y);
+
+/* Name of the kernel variant mic_conv_forward would launch for these
+ * descriptors (host only; for profiling and reports).  Writes a NUL-
+ * terminated string of at most buflen bytes; MIC_STATUS_BAD_PARAM if the
+ * descriptors are invalid or buflen is too small. */
+mic_status mic_conv_forward_kernel_name(mic_handle handle, mic_tensor_desc x_desc,
+                                        mic_filter_desc w_desc, mic_conv_desc conv,
+                                        mic_tensor_desc y_desc, char* buf, size_t buflen);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MICONV_H */

@@ -1,0 +1,93 @@
+"""Shared helpers for the GPU parity tests: seeded inputs, device layouts,
+oracle comparison with the tolerances of each element type.
+
+Tolerances (per element type, fixed in the tests, not tuned to results):
+  f32 : relative L2 error <= 1e-5 and |y - y_ref| <= 2e-6 * B per element,
+        B = sum |x*f| over the receptive field (the oracle returns it);
+        with alpha/beta the bound is 2e-6 * (|alpha| B + |beta y_old|).
+  f64 : relative L2 error <= 1e-12.
+  bf16: relative L2 error <= 1e-2 (bf16 inputs, fp32 accumulation and output).
+"""
+import numpy as np
+import torch
+
+import gen
+import oracle
+from gen import workloads
+
+TORCH_DT = {"f32": torch.float32, "f64": torch.float64, "bf16": torch.bfloat16}
+OUT_DT = {"f32": torch.float32, "f64": torch.float64, "bf16": torch.float32}
+RELL2 = {"f32": 1e-5, "f64": 1e-12, "bf16": 1e-2}
+ELEM_BOUND = {"f32": 2e-6}
+
+
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return torch.device("cuda", 0)
+
+
+def inputs(lay, x_dist=None, w_dist=None):
+    """float64 numpy x (N,C,H,W), w (K,C,R,S), rounded to the layer's storage type."""
+    x = gen.draw(x_dist or lay.x_dist, gen.derive_seed(lay.config, lay.layer, 0), lay.x_shape)
+    w = gen.draw(w_dist or lay.w_dist, gen.derive_seed(lay.config, lay.layer, 1), lay.w_shape)
+    return gen.round_to(x, lay.dtype), gen.round_to(w, lay.dtype)
+
+
+def strided_empty(shape, strides, dtype, device, fill=float("nan")):
+    """A tensor view of the given element strides over a fresh allocation."""
+    N, C, H, W = shape
+    n = workloads.storage_elems(N, C, H, W, strides)
+    base = torch.full((n,), fill, dtype=dtype, device=device)
+    return base.as_strided(shape, strides)
+
+
+def to_device(a64, dtype_key, layout="nchw", row_pitch=0, device=None):
+    """Upload logical N,C,H,W float64 data into a tensor of the given layout."""
+    device = device or dev()
+    N, C, H, W = a64.shape
+    st = workloads.padded_strides(N, C, H, W, layout, row_pitch)
+    t = strided_empty(a64.shape, st, TORCH_DT[dtype_key], device)
+    t.copy_(torch.from_numpy(a64).to(TORCH_DT[dtype_key]))
+    return t
+
+
+def out_tensor(lay, shape, device=None, fill=float("nan")):
+    device = device or dev()
+    st = workloads.padded_strides(*shape, lay.layout, lay.row_pitch)
+    return strided_empty(shape, st, OUT_DT[lay.dtype], device, fill)
+
+
+def sample_coords(rng, N, K, P, Q, count):
+    """Random output coordinates plus every corner and edge midpoint."""
+    pts = {(n, k, p, q) for n in (0, N - 1) for k in (0, K // 2, K - 1)
+           for p in (0, P // 2, P - 1) for q in (0, Q // 2, Q - 1)}
+    rnd = np.stack([rng.integers(0, N, count), rng.integers(0, K, count),
+                    rng.integers(0, P, count), rng.integers(0, Q, count)], axis=1)
+    return np.concatenate([np.array(sorted(pts), dtype=np.int64), rnd.astype(np.int64)])
+
+
+def gather(y, idx):
+    t = torch.from_numpy(idx).to(y.device)
+    return y[t[:, 0], t[:, 1], t[:, 2], t[:, 3]].double().cpu().numpy()
+
+
+def check(dtype_key, got, ref, bound, alpha=1.0, beta=0.0, y_old=None, what=""):
+    """Assert the element type's tolerance; return (rel_l2, max_err/bound)."""
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), "%s: non-finite output" % what
+    diff = got - ref
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(diff) / nref if nref > 0 else np.linalg.norm(diff)
+    assert rel <= RELL2[dtype_key], "%s: relative L2 error %.3e > %.1e" % (what, rel, RELL2[dtype_key])
+    worst = 0.0
+    if dtype_key in ELEM_BOUND:
+        scale = abs(alpha) * bound
+        if beta != 0.0:
+            scale = scale + np.abs(beta * y_old)
+        lim = ELEM_BOUND[dtype_key] * scale
+        bad = np.abs(diff) > lim
+        assert not np.any(bad), "%s: %d elements beyond 2e-6*B (worst ratio %.3g)" % (
+            what, int(bad.sum()), float(np.max(np.abs(diff)[bad] / np.maximum(lim[bad], 1e-300))))
+        nz = scale > 0
+        worst = float(np.max(np.abs(diff[nz]) / scale[nz])) if np.any(nz) else 0.0
+    return rel, worst

@@ -1,0 +1,235 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function miconv.h declares, validates descriptors and computes output sizes
+the same way the oracle does.  No kernel is launched here."""
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import convolution_forward_conv2d_amd as mic
+import oracle
+from gen import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "convolution_forward_conv2d_amd", "csrc")
+
+
+def test_library_exports_every_declared_function():
+    names = mic.header_functions()
+    assert "mic_conv_forward" in names and len(names) >= 20
+    lib = mic.lib()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # every declared function has a Python wrapper of the same name
+    assert not [n for n in names if not hasattr(mic, n)]
+
+
+def test_status_strings_and_version():
+    assert mic.status_string(0) == "success"
+    assert mic.status_string(1) == "bad parameter"
+    assert mic.status_string(2) == "not supported"
+    assert mic.status_string(99) == "unknown status"
+    assert mic.mic_get_version() == (0, 1, 0)
+
+
+def test_tensor_descriptor_roundtrip_and_validation():
+    d = mic.mic_tensor_desc_create()
+    try:
+        with pytest.raises(mic.MicError) as e:
+            mic.mic_tensor_desc_get(d)            # never set
+        assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+        mic.mic_tensor_desc_set(d, mic.MIC_DTYPE_F32, 2, 3, 4, 5, 60, 20, 5, 1)
+        assert mic.mic_tensor_desc_get(d) == (0, (2, 3, 4, 5), (60, 20, 5, 1))
+        mic.mic_tensor_desc_set_packed(d, mic.MIC_DTYPE_BF16, mic.MIC_LAYOUT_NHWC, 2, 3, 4, 5)
+        assert mic.mic_tensor_desc_get(d) == (2, (2, 3, 4, 5), (60, 1, 15, 3))
+        for bad in [(0, 3, 4, 5, 1, 1, 1, 1), (2, 3, 4, 5, 0, 1, 1, 1), (2, 3, 4, 5, 1, 1, -2, 1),
+                    (2, -1, 4, 5, 1, 1, 1, 1)]:
+            with pytest.raises(mic.MicError) as e:
+                mic.mic_tensor_desc_set(d, mic.MIC_DTYPE_F32, *bad)
+            assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+        with pytest.raises(mic.MicError):
+            mic.mic_tensor_desc_set(d, 7, 1, 1, 1, 1, 1, 1, 1, 1)      # unknown dtype
+    finally:
+        mic.mic_tensor_desc_destroy(d)
+
+
+def test_filter_and_conv_descriptor_validation():
+    f = mic.mic_filter_desc_create()
+    c = mic.mic_conv_desc_create()
+    try:
+        mic.mic_filter_desc_set(f, mic.MIC_DTYPE_F64, 4, 3, 2, 1)
+        assert mic.mic_filter_desc_get(f) == (1, (4, 3, 2, 1))
+        with pytest.raises(mic.MicError):
+            mic.mic_filter_desc_set(f, mic.MIC_DTYPE_F32, 4, 0, 2, 1)
+        mic.mic_conv_desc_set(c, 1, 2, 3, 4, 5, 6)
+        assert mic.mic_conv_desc_get(c) == (1, 2, 3, 4, 5, 6)
+        for bad in [(-1, 0, 0, 0, 1, 1), (0, 0, 0, -1, 1, 1), (0, 0, 0, 0, 0, 1), (0, 0, 0, 0, 1, -1)]:
+            with pytest.raises(mic.MicError):
+                mic.mic_conv_desc_set(c, *bad)
+    finally:
+        mic.mic_filter_desc_destroy(f)
+        mic.mic_conv_desc_destroy(c)
+
+
+def test_null_arguments_are_bad_param():
+    l = mic.lib()
+    assert l.mic_destroy(None) == mic.MIC_STATUS_BAD_PARAM
+    assert l.mic_tensor_desc_destroy(None) == mic.MIC_STATUS_BAD_PARAM
+    assert l.mic_set_stream(None, None) == mic.MIC_STATUS_BAD_PARAM
+    assert l.mic_conv_forward(None, 1.0, None, None, None, None, None, 0.0, None, None) == \
+        mic.MIC_STATUS_BAD_PARAM
+    buf = ctypes.create_string_buffer(8)
+    assert l.mic_conv_forward_kernel_name(None, None, None, None, None, buf, 8) == mic.MIC_STATUS_BAD_PARAM
+
+
+@pytest.mark.parametrize("lay", workloads.ALL_LAYERS, ids=lambda l: l.name)
+def test_output_dims_match_oracle(lay):
+    pb = oracle.make_problem(lay.x_shape, (1, 1, 1, 1), lay.w_shape, lay.stride, lay.padding)
+    P, Q = oracle.output_dims(pb)
+    assert mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding) == (lay.N, lay.K, P, Q)
+
+
+def test_output_dims_errors():
+    with pytest.raises(mic.MicError) as e:        # channel mismatch
+        mic.output_shape((1, 3, 8, 8), (2, 4, 3, 3))
+    assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+    with pytest.raises(mic.MicError):             # filter larger than padded input
+        mic.output_shape((1, 1, 3, 3), (1, 1, 5, 1), (1, 1), (0, 1, 0, 0))
+    # exactly fitting after padding is fine: one output row
+    assert mic.output_shape((1, 1, 3, 3), (1, 1, 5, 1), (1, 1), (1, 1, 0, 0)) == (1, 1, 1, 3)
+
+
+def _descs(lay, x_dt, w_dt, y_dt, y_dims=None):
+    xd, wd, yd, cd = (mic.mic_tensor_desc_create(), mic.mic_filter_desc_create(),
+                      mic.mic_tensor_desc_create(), mic.mic_conv_desc_create())
+    xs = workloads.padded_strides(lay.N, lay.C, lay.H, lay.W, lay.layout, lay.row_pitch)
+    mic.mic_tensor_desc_set(xd, x_dt, *lay.x_shape, *xs)
+    mic.mic_filter_desc_set(wd, w_dt, *lay.w_shape)
+    mic.mic_conv_desc_set(cd, *lay.padding, *lay.stride)
+    N, K, P, Q = mic.mic_conv_forward_output_dim(cd, xd, wd) if y_dims is None else y_dims
+    mic.mic_tensor_desc_set_packed(yd, y_dt, mic.MIC_LAYOUT_NCHW, N, K, P, Q)
+    return xd, wd, cd, yd
+
+
+def _free(xd, wd, cd, yd):
+    mic.mic_tensor_desc_destroy(xd)
+    mic.mic_filter_desc_destroy(wd)
+    mic.mic_conv_desc_destroy(cd)
+    mic.mic_tensor_desc_destroy(yd)
+
+
+def test_kernel_choice_host_only():
+    F32 = mic.MIC_DTYPE_F32
+    names = {}
+    for lay in workloads.ALL_LAYERS:
+        dt = {"f32": (F32, F32, F32), "f64": (1, 1, 1), "bf16": (2, 2, F32)}[lay.dtype]
+        d = _descs(lay, *dt)
+        try:
+            names[lay.name] = mic.mic_conv_forward_kernel_name(None, *d)
+        finally:
+            _free(*d)
+    assert names["alexnet_conv3"].startswith("mfma_f32_")
+    assert names["prec_conv3_f64_nchw"].startswith("mfma_f64_")
+    assert names["prec_conv3_bf16_nhwc"].startswith("mfma_bf16_")
+
+
+def test_dtype_combinations_and_shape_mismatch():
+    lay = workloads.TINY[0]
+    for combo in [(0, 0, 1), (1, 1, 0), (2, 2, 2), (0, 2, 0)]:
+        d = _descs(lay, *combo)
+        try:
+            with pytest.raises(mic.MicError) as e:
+                mic.mic_conv_forward_kernel_name(None, *d)
+            assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+        finally:
+            _free(*d)
+    d = _descs(lay, 0, 0, 0, y_dims=(2, 16, 12, 11))
+    try:
+        with pytest.raises(mic.MicError) as e:
+            mic.mic_conv_forward_kernel_name(None, *d)
+        assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+    finally:
+        _free(*d)
+
+
+def test_forced_variant_must_match_dtype(monkeypatch):
+    lay = workloads.TINY[0]
+    monkeypatch.setenv("MIC_FORCE_VARIANT", "mfma_f64_64x64")
+    d = _descs(lay, 0, 0, 0)
+    try:
+        with pytest.raises(mic.MicError) as e:
+            mic.mic_conv_forward_kernel_name(None, *d)
+        assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+        monkeypatch.setenv("MIC_FORCE_VARIANT", "direct")
+        assert mic.mic_conv_forward_kernel_name(None, *d) == "direct"
+    finally:
+        _free(*d)
+
+
+def test_size_limit_is_not_supported():
+    d = mic.mic_tensor_desc_create()
+    wd, cd, yd = mic.mic_filter_desc_create(), mic.mic_conv_desc_create(), mic.mic_tensor_desc_create()
+    try:
+        mic.mic_tensor_desc_set(d, 0, 1, 1, 1, 4, 1, 1, 1, 1 << 29)    # highest offset 3 * 2^29
+        mic.mic_filter_desc_set(wd, 0, 1, 1, 1, 1)
+        mic.mic_conv_desc_set(cd, 0, 0, 0, 0, 1, 1)
+        mic.mic_tensor_desc_set_packed(yd, 0, 0, 1, 1, 1, 4)
+        with pytest.raises(mic.MicError) as e:
+            mic.mic_conv_forward_kernel_name(None, d, wd, cd, yd)
+        assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+    finally:
+        _free(d, wd, cd, yd)
+
+
+HOST_CHECK = r"""
+#include <cstdio>
+#include <cstdint>
+#include <vector>
+#include "conv_params.h"
+#include "tile_map.h"
+using namespace miconv;
+int main() {
+    // FastDiv: every divisor up to 70000 against plain division, on edge and spread numerators
+    for (uint32_t d = 1; d <= 70000; ++d) {
+        FastDiv f(d);
+        const uint32_t probes[] = {0u, 1u, d - 1, d, d + 1, 2 * d - 1, 2 * d, 12345u * d + d - 1,
+                                   0x7FFFFFFFu, 0x7FFFFFFEu, 0x40000000u, 0x3FFFFFFFu};
+        for (uint32_t n : probes) {
+            if (n > 0x7FFFFFFFu) continue;
+            uint32_t q, r; f.divmod(n, q, r);
+            if (q != n / d || r != n % d) { printf("fastdiv %u %u\n", d, n); return 1; }
+        }
+        for (uint64_t n = 0; n < 0x80000000ull; n += 0x7FFFFull + d) {
+            uint32_t q, r; f.divmod((uint32_t)n, q, r);
+            if (q != (uint32_t)n / d || r != (uint32_t)n % d) { printf("fastdiv %u %llu\n", d, (unsigned long long)n); return 1; }
+        }
+    }
+    // XCD tile map: a bijection on [0, tiles) for every tile count up to 5000
+    for (int tiles = 1; tiles <= 5000; ++tiles) {
+        std::vector<int> seen(tiles, 0);
+        for (int b = 0; b < tiles; ++b) {
+            int t = xcd_logical_tile(b, tiles);
+            if (t < 0 || t >= tiles || seen[t]++) { printf("map %d %d\n", tiles, b); return 1; }
+            // ids on one XCD form one contiguous run
+            if (b >= 8 && xcd_logical_tile(b - 8, tiles) != t - 1) { printf("run %d %d\n", tiles, b); return 1; }
+        }
+    }
+    printf("ok\n");
+    return 0;
+}
+"""
+
+
+def test_fastdiv_and_tile_map_on_host():
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "check.cpp")
+        exe = os.path.join(tmp, "check")
+        with open(src, "w") as fh:
+            fh.write(HOST_CHECK)
+        subprocess.run(["/opt/rocm/bin/hipcc", "-O2", "-I", CSRC, src, "-o", exe], check=True,
+                       capture_output=True)
+        out = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+        assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout

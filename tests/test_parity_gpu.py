@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small shapes that span several tiles with ragged tails are compared element
+by element in full, for every kernel variant; every workload layer is run at
+its full size and compared on sampled outputs (corners, edge midpoints and
+random coordinates), plus properties that hold at any size: integer-valued
+inputs give bit-exact results, reruns are bit-identical, NaN in y never
+leaks when beta = 0, and nothing outside y is written.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import convolution_forward_conv2d_amd as mic
+import gen
+import oracle
+from gen import workloads
+from gen.workloads import Layer
+
+import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = {
+    "f32": ["direct", "mfma_f32_128x128", "mfma_f32_128x64", "mfma_f32_64x128", "mfma_f32_256x32"],
+    "f64": ["direct", "mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64"],
+    "bf16": ["direct", "mfma_bf16_128x128", "mfma_bf16_128x64", "mfma_bf16_256x32"],
+}
+
+U = ("uniform", -1.0, 1.0)
+
+
+def _small(name, N, C, Hh, Ww, K, R, S, stride, pads, dtype, layout="nchw", pitch=0):
+    return Layer(name, 9, 1, N, C, Hh, Ww, K, R, S, stride, pads, dtype, U, U,
+                 layout=layout, row_pitch=pitch)
+
+
+SMALL_SHAPES = [
+    # several 128-row tiles plus a ragged tail; K = 100 is ragged against every n-tile
+    dict(name="ragged3x3", N=3, C=40, Hh=15, Ww=15, K=100, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
+    # 11x11 / stride 4 / no padding, K = 96, C*R*S = 363 (odd)
+    dict(name="big_filter", N=2, C=3, Hh=63, Ww=63, K=96, R=11, S=11, stride=(4, 4), pads=(0, 0, 0, 0)),
+    # non-square filter, mixed stride, asymmetric padding
+    dict(name="asym", N=2, C=5, Hh=33, Ww=70, K=33, R=7, S=5, stride=(2, 1), pads=(3, 2, 0, 4)),
+    # channels-last storage
+    dict(name="nhwc", N=2, C=64, Hh=13, Ww=13, K=64, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1),
+         layout="nhwc"),
+    # padded row pitch (16) on x and y
+    dict(name="pitch16", N=2, C=24, Hh=13, Ww=13, K=40, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1),
+         pitch=16),
+    # one output element per image, one channel
+    dict(name="degenerate", N=5, C=1, Hh=3, Ww=2, K=3, R=3, S=2, stride=(3, 3), pads=(0, 0, 0, 0)),
+]
+
+
+def _run(lay, x, w, y, alpha=1.0, beta=0.0):
+    plan = mic.ConvPlan(x, w, y, lay.stride, lay.padding)
+    try:
+        plan(alpha, beta)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    return y
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: s["name"])
+def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
+    lay = _small(dtype=dtype, **{k: v for k, v in shape.items()})
+    x64, w64 = H.inputs(lay)
+    ref, bound = oracle.conv2d_fprop(x64, w64, lay.stride, lay.padding)
+    x = H.to_device(x64, dtype, lay.layout, lay.row_pitch)
+    w = torch.from_numpy(w64).to(H.TORCH_DT[dtype]).to(H.dev())
+    for var in VARIANTS[dtype]:
+        monkeypatch.setenv("MIC_FORCE_VARIANT", var)
+        print("case", shape["name"], dtype, var, flush=True)
+        y = H.out_tensor(lay, ref.shape)
+        _run(lay, x, w, y)
+        H.check(dtype, y.double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (shape["name"], dtype, var))
+
+
+def test_tiny_workload_full_and_deterministic():
+    lay = workloads.TINY[0]
+    x64, w64 = H.inputs(lay)
+    ref, bound = oracle.conv2d_fprop(x64, w64, lay.stride, lay.padding)
+    x = H.to_device(x64, "f32")
+    w = torch.from_numpy(w64).float().to(H.dev())
+    y1 = _run(lay, x, w, H.out_tensor(lay, ref.shape))
+    y2 = _run(lay, x, w, H.out_tensor(lay, ref.shape))
+    H.check("f32", y1.double().cpu().numpy(), ref, bound, what="tiny")
+    assert torch.equal(y1, y2)
+
+
+_cache = {}
+
+
+def _layer_inputs(lay, integer=False):
+    key = (lay.config, lay.layer, lay.dtype, integer)
+    if key not in _cache:
+        _cache.clear()
+        dist = ("integers", -4, 4) if integer else None
+        _cache[key] = H.inputs(lay, dist, dist)
+    return _cache[key]
+
+
+@pytest.mark.parametrize("lay", workloads.ALL_LAYERS, ids=lambda l: l.name)
+def test_workload_layer_sampled(lay):
+    """Full-size layer, default variant: sampled parity, rerun bit-identity, NaN-safe beta=0."""
+    print("layer", lay.name, flush=True)
+    x64, w64 = _layer_inputs(lay)
+    x = H.to_device(x64, lay.dtype, lay.layout, lay.row_pitch)
+    w = torch.from_numpy(w64).to(H.TORCH_DT[lay.dtype]).to(H.dev())
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    y = H.out_tensor(lay, (N, K, P, Q))                # NaN-filled: beta = 0 must overwrite all
+    _run(lay, x, w, y)
+    assert bool(torch.isfinite(y).all()), "unwritten or non-finite outputs"
+    rng = np.random.default_rng(lay.config * 1000 + lay.layer)
+    idx = H.sample_coords(rng, N, K, P, Q, 3000)
+    ref, bound = oracle.conv2d_fprop_at(x64, w64, idx, lay.stride, lay.padding)
+    rel, worst = H.check(lay.dtype, H.gather(y, idx), ref, bound, what=lay.name)
+    print("  sampled rel-L2 %.3e, worst |err|/B %.3e" % (rel, worst), flush=True)
+    y2 = H.out_tensor(lay, (N, K, P, Q), fill=0.0)
+    _run(lay, x, w, y2)
+    assert torch.equal(y, y2), "rerun not bit-identical"
+
+
+@pytest.mark.parametrize("lay", [l for l in workloads.ALL_LAYERS if not l.name.endswith("nhwc")],
+                         ids=lambda l: l.name)
+def test_workload_layer_integer_exact(lay):
+    """Integer inputs in [-4, 4]: every partial sum is an exact integer below 2^24."""
+    print("layer", lay.name, flush=True)
+    x64, w64 = _layer_inputs(lay, integer=True)
+    x = H.to_device(x64, lay.dtype, lay.layout, lay.row_pitch)
+    w = torch.from_numpy(w64).to(H.TORCH_DT[lay.dtype]).to(H.dev())
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    y = H.out_tensor(lay, (N, K, P, Q))
+    _run(lay, x, w, y)
+    rng = np.random.default_rng(7 + lay.config * 1000 + lay.layer)
+    idx = H.sample_coords(rng, N, K, P, Q, 3000)
+    ref, _ = oracle.conv2d_fprop_at(x64, w64, idx, lay.stride, lay.padding)
+    got = H.gather(y, idx)
+    assert np.array_equal(got, ref), "%s: %d mismatches" % (lay.name, int((got != ref).sum()))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
+def test_alpha_beta(dtype, monkeypatch):
+    lay = _small("ab", 2, 20, 11, 9, 70, 3, 2, (1, 2), (1, 0, 2, 1), dtype)
+    xi, wi = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
+    acc, _ = oracle.conv2d_fprop(xi, wi, lay.stride, lay.padding)
+    y_old = gen.integers(99, acc.shape)
+    x = H.to_device(xi, dtype)
+    w = torch.from_numpy(wi).to(H.TORCH_DT[dtype]).to(H.dev())
+    for var in VARIANTS[dtype]:
+        monkeypatch.setenv("MIC_FORCE_VARIANT", var)
+        y = torch.from_numpy(y_old).to(H.OUT_DT[dtype]).to(H.dev())
+        _run(lay, x, w, y, alpha=0.5, beta=0.25)
+        assert np.array_equal(y.double().cpu().numpy(), 0.5 * acc + 0.25 * y_old), var
+        y = torch.from_numpy(y_old).to(H.OUT_DT[dtype]).to(H.dev())
+        _run(lay, x, w, y, alpha=0.0, beta=-2.0)
+        assert np.array_equal(y.double().cpu().numpy(), -2.0 * y_old), var
+    # non-integer values with the tolerance of the type
+    monkeypatch.delenv("MIC_FORCE_VARIANT")
+    x64, w64 = H.inputs(lay)
+    yo = gen.round_to(gen.uniform(98, acc.shape), "f32" if dtype != "f64" else "f64")
+    ref, bound = oracle.conv2d_fprop(x64, w64, lay.stride, lay.padding, alpha=-2.0, beta=1.0, y_old=yo)
+    y = torch.from_numpy(yo).to(H.OUT_DT[dtype]).to(H.dev())
+    _run(lay, H.to_device(x64, dtype), torch.from_numpy(w64).to(H.TORCH_DT[dtype]).to(H.dev()), y,
+         alpha=-2.0, beta=1.0)
+    H.check(dtype, y.double().cpu().numpy(), ref, bound, alpha=-2.0, beta=1.0, y_old=yo, what="alpha-beta")
+
+
+@pytest.mark.parametrize("layout", ["nchw", "nhwc"])
+def test_subtensor_output_and_canaries(layout):
+    """y is a channel slice of a larger tensor: neighbours and guard cells stay untouched."""
+    lay = _small("sub", 3, 16, 14, 14, 50, 3, 3, (1, 1), (1, 1, 1, 1), "f32", layout=layout)
+    x64, w64 = H.inputs(lay)
+    ref, bound = oracle.conv2d_fprop(x64, w64, lay.stride, lay.padding)
+    N, K, P, Q = ref.shape
+    big = torch.full((N, K + 9, P, Q), 7.25, dtype=torch.float32, device=H.dev())
+    if layout == "nhwc":
+        big = big.contiguous(memory_format=torch.channels_last)
+    guard = torch.full((4096,), -3.5, dtype=torch.float32, device=H.dev())
+    y = big[:, 4:4 + K]
+    x = H.to_device(x64, "f32", layout)
+    w = torch.from_numpy(w64).float().to(H.dev())
+    _run(lay, x, w, y)
+    H.check("f32", y.double().cpu().numpy(), ref, bound, what="subtensor")
+    assert bool((big[:, :4] == 7.25).all()) and bool((big[:, 4 + K:] == 7.25).all())
+    assert bool((guard == -3.5).all())
+
+
+def test_nondefault_stream():
+    lay = _small("stream", 2, 32, 13, 13, 64, 3, 3, (1, 1), (1, 1, 1, 1), "f32")
+    x64, w64 = H.inputs(lay)
+    ref, bound = oracle.conv2d_fprop(x64, w64, lay.stride, lay.padding)
+    s = torch.cuda.Stream()
+    x = H.to_device(x64, "f32")
+    w = torch.from_numpy(w64).float().to(H.dev())
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y = mic.conv2d_forward(x, w, lay.stride, lay.padding)
+    s.synchronize()
+    H.check("f32", y.double().cpu().numpy(), ref, bound, what="stream")
+
+
+def test_error_statuses_on_device():
+    h = mic.handle_for()
+    lay = workloads.TINY[0]
+    x = torch.zeros(lay.x_shape, device=H.dev())
+    w = torch.zeros(lay.w_shape, device=H.dev())
+    y = torch.zeros((2, 16, 12, 12), device=H.dev())
+    plan = mic.ConvPlan(x, w, y, lay.stride, lay.padding, handle=h)
+    try:
+        with pytest.raises(mic.MicError) as e:            # null input pointer
+            mic.mic_conv_forward(h, 1.0, plan.xd, 0, plan.wd, w.data_ptr(), plan.cd, 0.0, plan.yd,
+                                 y.data_ptr())
+        assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+        with pytest.raises(mic.MicError) as e:            # misaligned output pointer
+            mic.mic_conv_forward(h, 1.0, plan.xd, x.data_ptr(), plan.wd, w.data_ptr(), plan.cd, 0.0,
+                                 plan.yd, y.data_ptr() + 2)
+        assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+    finally:
+        plan.close()
+
+
+def test_no_device_memory_allocated_by_calls():
+    lay = workloads.by_name("alexnet_conv3")
+    lay = Layer("nomem", 2, 3, 8, lay.C, lay.H, lay.W, lay.K, lay.R, lay.S, lay.stride, lay.padding,
+                "f32", U, U)
+    x = torch.randn(lay.x_shape, device=H.dev())
+    w = torch.randn(lay.w_shape, device=H.dev())
+    y = torch.empty((8, lay.K, 13, 13), device=H.dev())
+    plan = mic.ConvPlan(x, w, y, lay.stride, lay.padding)
+    plan()
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(20):
+        plan()
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    plan.close()
+    assert free1 == free0
