@@ -1,0 +1,279 @@
+// conv_fwd_halo.hip -- convolution forward pass as a batch-reduce GEMM over
+// the R x S filter taps, with the input read once per channel block.
+//
+// Same implicit GEMM as conv_fwd_mfma.hip (rows m = (n, p, q), columns k,
+// reduction kappa = (c, r, s)), but the reduction is cut into chunks of CB
+// whole channels with all R*S taps, kappa = (c_local, r, s) in KCRS order.
+// Per chunk a workgroup stages in LDS:
+//
+//  * the input halo: for each of the CB channels, every zero-padded input
+//    row ("slot") that the tile's TM output rows touch, WP columns wide
+//    (padding positions hold zeros), loaded once along W;
+//  * the filter slab: for each of its TN filters, the CB*R*S contiguous
+//    values F[k, c0 .. c0+CB, :, :] (plain 16-byte loads of packed KCRS).
+//
+// Tap (r, s) of output row m then reads its A operand from LDS at
+// slot(m, r) * WP + q*v + s: a per-lane base plus a compile-time offset,
+// so the gather costs one LDS read per MFMA operand and no index math.
+// This is the batch-reduce GEMM of the single-building-block page
+// ("Proposed Method": a batch of sub-tensor block products reduced into one
+// output block; here one block product per filter tap), computed directly
+// from x with no packed copy (zero-memory direct-convolution page, Abstract
+// and "Proposed Method"), double-buffered through LDS (maxDNN page,
+// "Proposed Method").
+//
+// Eligibility (checked by the host): R, S equal to the instance's; the
+// padded width W + pad_left + pad_right <= WP; every tile's slot span
+// <= SL; C a multiple of CB; the filter 8- or 16-byte aligned as the
+// instance's vector loads need.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "conv_params.h"
+#include "kernels.h"
+#include "mfma_common.h"
+#include "tile_map.h"
+
+namespace miconv {
+
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL>
+__global__ void __launch_bounds__(256)
+conv_fwd_halo_kernel(const ConvParams p)
+{
+    using In = typename Pol::In;
+    using AccV = typename Pol::AccV;
+    constexpr int NT = 256;
+    constexpr int BM = Pol::BM;
+    constexpr int ES = (int)sizeof(In);
+    constexpr int RS = R * S;
+    constexpr int TK = CB * RS;                  // reduction elements per chunk
+    constexpr int CPG = CB / Pol::G;             // channels per lane group
+    constexpr int SEG = CPG * RS;                // reduction elements per lane group = MFMA steps
+    constexpr int WM = TM / WAVES_M;
+    constexpr int WN = TN / WAVES_N;
+    constexpr int FM = WM / BM;
+    constexpr int FN = WN / BM;
+    // halo: CB planes of SL slots x WP columns; the plane pitch is skewed by
+    // 16 elements so the lane groups (one channel set each) hit other banks
+    constexpr int PLANE = SL * WP + 16;
+    constexpr int HALO_BYTES = CB * PLANE * ES;
+    constexpr int HE = (CB * SL * WP) / NT;      // halo elements per thread per chunk
+    // filter slab: TN rows of TK values; row pitch an odd number of 8-byte units
+    constexpr int ROW8 = (TK * ES + 7) / 8;
+    constexpr int BROW = 8 * (ROW8 % 2 ? ROW8 : ROW8 + 1);
+    constexpr int B_BYTES = TN * BROW;
+    constexpr int VB = (TK * ES) % 16 == 0 ? 16 : 8;   // global vector width for the slab
+    constexpr int VPR = TK * ES / VB;                   // vectors per filter row
+    constexpr int NVB = (TN * VPR + NT - 1) / NT;       // slab vectors per thread per chunk
+    constexpr int BUF_BYTES = ((HALO_BYTES + B_BYTES) + 15) / 16 * 16;
+    static_assert(Pol::V == 1, "scalar-operand MFMA policies only");
+    static_assert(CB % Pol::G == 0, "whole channels per lane group");
+    static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
+    static_assert((CB * SL * WP) % NT == 0, "halo elements split evenly over the threads");
+    static_assert((TK * ES) % 8 == 0, "slab rows are whole 8-byte vectors");
+    static_assert(4 * BM * (BM + 1) * (int)sizeof(typename Pol::Acc) <= 2 * BUF_BYTES, "epilogue stage fits");
+    static_assert(((CPG - 1) * PLANE + (R - 1) * WP + S) * ES < 65536, "LDS immediate offsets");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int mt = tile / p.n_tiles;
+    const int nt = tile - mt * p.n_tiles;
+    const int m0 = mt * TM;
+    const int n0 = nt * TN;
+
+    const In* __restrict__ x = static_cast<const In*>(p.x);
+    const In* __restrict__ w = static_cast<const In*>(p.w);
+
+    // virtual padded row of output row m (tap r adds r): n * Hp + p * u
+    auto vrow = [&](int m) {
+        uint32_t n, pq, pp, q;
+        p.div_pq.divmod((uint32_t)m, n, pq);
+        p.div_q.divmod(pq, pp, q);
+        return (int)n * p.Hp + (int)pp * p.u;
+    };
+    const int vr_first = vrow(m0);
+    const int m_last = min(m0 + TM, p.M) - 1;
+    const int nslots = vrow(m_last) + R - vr_first;     // <= SL (host-checked)
+
+    // ---- halo loader: thread -> HE (channel, slot, column) positions, fixed for the tile
+    int h_off[HE];
+    uint32_t h_ok = 0;
+#pragma unroll
+    for (int i = 0; i < HE; ++i) {
+        const int e = tid + NT * i;
+        const int col = e % WP;
+        const int slot = (e / WP) % SL;
+        const int cl = e / (WP * SL);
+        uint32_t n, hp;
+        p.div_hp.divmod((uint32_t)(vr_first + slot), n, hp);
+        const int h = (int)hp - p.pad_top;
+        const int wcol = col - p.pad_left;
+        const bool ok = slot < nslots && (int)n < p.N && h >= 0 && h < p.H && wcol >= 0 && wcol < p.W;
+        h_off[i] = ok ? (int)n * p.sxn + cl * p.sxc + h * p.sxh + wcol * p.sxw : 0;
+        h_ok |= (ok ? 1u : 0u) << i;
+    }
+
+    // ---- slab loader: thread -> NVB (filter row, vector) positions
+    int b_off[NVB];
+    uint32_t b_ok = 0;
+#pragma unroll
+    for (int i = 0; i < NVB; ++i) {
+        const int e = tid + NT * i;
+        const int row = e / VPR;
+        const int vec = e - row * VPR;
+        const bool ok = e < TN * VPR && n0 + row < p.K;
+        b_off[i] = ok ? (n0 + row) * p.Kred + vec * (VB / ES) : 0;   // elements
+        b_ok |= (ok ? 1u : 0u) << i;
+    }
+
+    In h_val[HE];
+    u32x4 b_val[NVB];
+
+    auto load_chunk = [&](int c0) {
+        const int xo = c0 * p.sxc;
+#pragma unroll
+        for (int i = 0; i < HE; ++i) h_val[i] = ((h_ok >> i) & 1) ? load_elem(x + h_off[i] + xo) : In(0);
+        const int wo = c0 * RS;
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) {
+            if constexpr (VB == 16) {
+                b_val[i] = ((b_ok >> i) & 1) ? *reinterpret_cast<const u32x4*>(w + b_off[i] + wo)
+                                             : u32x4{0, 0, 0, 0};
+            } else {
+                const u32x2 t = ((b_ok >> i) & 1) ? *reinterpret_cast<const u32x2*>(w + b_off[i] + wo)
+                                                  : u32x2{0, 0};
+                b_val[i] = u32x4{t[0], t[1], 0, 0};
+            }
+        }
+    };
+
+    auto store_chunk = [&](int buf) {
+        unsigned char* hb = smem + buf * BUF_BYTES;
+#pragma unroll
+        for (int i = 0; i < HE; ++i) {
+            const int e = tid + NT * i;
+            const int col = e % WP;
+            const int slot = (e / WP) % SL;
+            const int cl = e / (WP * SL);
+            reinterpret_cast<In*>(hb)[cl * PLANE + slot * WP + col] = h_val[i];
+        }
+        unsigned char* bb = hb + HALO_BYTES;
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) {
+            const int e = tid + NT * i;
+            if (e < TN * VPR) {
+                const int row = e / VPR;
+                const int vec = e - row * VPR;
+                u32x2* dst = reinterpret_cast<u32x2*>(bb + row * BROW + vec * VB);
+                dst[0] = u32x2{b_val[i][0], b_val[i][1]};
+                if constexpr (VB == 16) dst[1] = u32x2{b_val[i][2], b_val[i][3]};
+            }
+        }
+    };
+
+    // ---- per-wave MFMA geometry
+    const int wm = wave / WAVES_N;
+    const int wn = wave % WAVES_N;
+    const int lrow = lane % BM;
+    const int lgrp = lane / BM;
+    int a_base[FM];                     // element offset of tap (0,0) of this lane's row, per block
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WM + i * BM + lrow;
+        int base = 0;
+        if (m < p.M) {
+            uint32_t n, pq, pp, q;
+            p.div_pq.divmod((uint32_t)m, n, pq);
+            p.div_q.divmod(pq, pp, q);
+            base = ((int)n * p.Hp + (int)pp * p.u - vr_first) * WP + (int)q * p.v;
+        }
+        a_base[i] = base + lgrp * CPG * PLANE;
+    }
+    int b_row[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b_row[j] = (wn * WN + j * BM + lrow) * BROW + lgrp * SEG * ES;
+
+    AccV acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = AccV{};
+
+    const int nchunks = p.C / CB;
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int cur = ch & 1;
+        const bool more = ch + 1 < nchunks;
+        if (more) load_chunk((ch + 1) * CB);
+
+        const In* halo = reinterpret_cast<const In*>(smem + cur * BUF_BYTES);
+        const unsigned char* slab = smem + cur * BUF_BYTES + HALO_BYTES;
+        In bf[FN][SEG];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const In* src = reinterpret_cast<const In*>(slab + b_row[j]);
+#pragma unroll
+            for (int t = 0; t < SEG; ++t) bf[j][t] = src[t];
+        }
+#pragma unroll
+        for (int t = 0; t < SEG; ++t) {
+            const int off = (t / RS) * PLANE + ((t % RS) / S) * WP + (t % RS) % S;
+            In a[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a[i] = halo[a_base[i] + off];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Pol::mfma_s(a[i], bf[j][t], acc[i][j]);
+        }
+        if (more) store_chunk(cur ^ 1);
+        __syncthreads();
+    }
+
+    store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, wave, lane);
+}
+
+// ------------------------------------------------------------------ instances and launch
+
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL>
+static hipError_t launch_halo_variant(const ConvParams& p0, hipStream_t stream)
+{
+    ConvParams p = p0;
+    p.m_tiles = (p.M + TM - 1) / TM;
+    p.n_tiles = (p.K + TN - 1) / TN;
+    const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
+    hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL>),
+                       grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+//        name                  policy   TM   TN  waves  R  S  CB  WP  SL
+#define MICONV_HALO_VARIANTS(X)                                      \
+    X(HALO_F32_3x3_128x128, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16)  \
+    X(HALO_F32_3x3_128x64, PolF32, 128, 64, 2, 2, 3, 3, 4, 16, 16)    \
+    X(HALO_F32_3x3_64x128, PolF32, 64, 128, 2, 2, 3, 3, 4, 16, 16)    \
+    X(HALO_F32_5x5_128x128, PolF32, 128, 128, 2, 2, 5, 5, 4, 32, 16)  \
+    X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16)  \
+    X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16)
+
+hipError_t launch_halo(Variant v, const ConvParams& p, hipStream_t stream)
+{
+    switch (v) {
+#define X(name, pol, tm, tn, wmm, wnn, r, s, cb, wp, sl) \
+    case Variant::name: return launch_halo_variant<pol, tm, tn, wmm, wnn, r, s, cb, wp, sl>(p, stream);
+        MICONV_HALO_VARIANTS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace miconv

@@ -51,10 +51,11 @@ struct ConvParams {
     int pad_top, pad_left;
     int sxn, sxc, sxh, sxw;   // input element strides
     int syn, syk, syp, syq;   // output element strides
+    int Hp;              // H + pad_top + pad_bottom (rows of the zero-padded input)
     int M;               // N * P * Q   (rows of the implicit GEMM)
     int Kred;            // C * R * S   (reduction length)
     int m_tiles, n_tiles;
-    FastDiv div_pq, div_q, div_rs, div_s;
+    FastDiv div_pq, div_q, div_rs, div_s, div_hp;
     double alpha, beta;  // converted to the accumulation type inside the kernel
 };
 

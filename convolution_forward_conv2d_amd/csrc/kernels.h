@@ -19,6 +19,12 @@ enum class Variant : int {
     MFMA_BF16_128x128,
     MFMA_BF16_128x64,
     MFMA_BF16_256x32,
+    HALO_F32_3x3_128x128,   // tap-batched kernel with an LDS input halo (conv_fwd_halo.hip)
+    HALO_F32_3x3_128x64,
+    HALO_F32_3x3_64x128,
+    HALO_F32_5x5_128x128,
+    HALO_F64_3x3_128x128,
+    HALO_F64_3x3_64x64,
     COUNT
 };
 
@@ -27,6 +33,9 @@ enum class DType : int { F32 = 0, F64 = 1, BF16 = 2 };
 // Launch an implicit-GEMM MFMA variant.  bvec: the filter may be read with
 // 16-byte loads (w 16-byte aligned and C*R*S a multiple of the vector).
 hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, hipStream_t stream);
+
+// Launch a tap-batched halo variant (the host has checked its eligibility).
+hipError_t launch_halo(Variant v, const ConvParams& p, hipStream_t stream);
 
 // Launch the plain direct kernel (one thread per output element).
 hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);

@@ -114,6 +114,23 @@ const Candidate kBF16[] = {
 };
 const Candidate kDirect = {Variant::DIRECT, 0, 0, "direct"};
 
+// Tap-batched halo kernels (conv_fwd_halo.hip): fixed R x S, CB channels per
+// chunk, padded input width <= WP, per-tile slot span <= SL.
+struct HaloCandidate {
+    Candidate c;
+    DType dt;
+    int r, s, cb, wp, sl;
+};
+
+const HaloCandidate kHalo[] = {
+    {{Variant::HALO_F32_3x3_128x128, 128, 128, "halo_f32_3x3_128x128"}, DType::F32, 3, 3, 4, 16, 16},
+    {{Variant::HALO_F32_3x3_128x64, 128, 64, "halo_f32_3x3_128x64"}, DType::F32, 3, 3, 4, 16, 16},
+    {{Variant::HALO_F32_3x3_64x128, 64, 128, "halo_f32_3x3_64x128"}, DType::F32, 3, 3, 4, 16, 16},
+    {{Variant::HALO_F32_5x5_128x128, 128, 128, "halo_f32_5x5_128x128"}, DType::F32, 5, 5, 4, 32, 16},
+    {{Variant::HALO_F64_3x3_128x128, 128, 128, "halo_f64_3x3_128x128"}, DType::F64, 3, 3, 4, 16, 16},
+    {{Variant::HALO_F64_3x3_64x64, 64, 64, "halo_f64_3x3_64x64"}, DType::F64, 3, 3, 4, 16, 16},
+};
+
 struct Plan {
     mic_status status;
     DType dt;
@@ -155,6 +172,37 @@ Candidate choose_tile(DType dt, int M, int K, int num_cu)
         }
     }
     return list[best_i];
+}
+
+bool is_halo(Variant v)
+{
+    for (const HaloCandidate& hc : kHalo)
+        if (hc.c.v == v) return true;
+    return false;
+}
+
+// Largest number of padded input rows ("slots") one tile of TM consecutive
+// output rows touches: rows n*Hp + p*u .. of its first and last output row.
+int max_tile_slots(const ConvParams& p, int tm)
+{
+    int worst = 0;
+    for (int64_t m0 = 0; m0 < p.M; m0 += tm) {
+        const int64_t m1 = (m0 + tm < p.M ? m0 + tm : p.M) - 1;
+        const int64_t pq = (int64_t)p.P * p.Q;
+        const int64_t v0 = (m0 / pq) * p.Hp + ((m0 % pq) / p.Q) * p.u;
+        const int64_t v1 = (m1 / pq) * p.Hp + ((m1 % pq) / p.Q) * p.u;
+        const int64_t slots = v1 + p.R - v0;
+        if (slots > worst) worst = (int)(slots > INT32_MAX ? INT32_MAX : slots);
+    }
+    return worst;
+}
+
+bool halo_eligible(const HaloCandidate& h, DType dt, const ConvParams& p, const void* w, bool check_ptr)
+{
+    if (h.dt != dt || h.r != p.R || h.s != p.S) return false;
+    if (p.C % h.cb != 0) return false;
+    if (check_ptr && (uintptr_t)w % 16 != 0) return false;
+    return true;
 }
 
 Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void* x,
@@ -236,16 +284,50 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
     p.div_q = FastDiv((uint32_t)Q);
     p.div_rs = FastDiv((uint32_t)(wd->r * wd->s));
     p.div_s = FastDiv((uint32_t)wd->s);
+    p.Hp = xd->h + cd->pad_top + cd->pad_bottom;
+    p.div_hp = FastDiv((uint32_t)p.Hp);
     p.alpha = alpha;
     p.beta = beta;
+    const int Wp = xd->w + cd->pad_left + cd->pad_right;
 
     const int num_cu = h ? h->num_cu : kDefaultCUs;
     pl.cand = choose_tile(pl.dt, p.M, p.K, num_cu);
+    // prefer a tap-batched halo kernel where one fits, chosen by the same tile cost
+    {
+        double best = 0;
+        bool found = false;
+        for (const HaloCandidate& hc : kHalo) {
+            if (!halo_eligible(hc, pl.dt, p, w, need_pointers) || Wp > hc.wp) continue;
+            if (max_tile_slots(p, hc.c.tm) > hc.sl) continue;
+            const int64_t tiles = (int64_t)((p.M + hc.c.tm - 1) / hc.c.tm) * ((p.K + hc.c.tn - 1) / hc.c.tn);
+            const int64_t rounds = (tiles + num_cu - 1) / num_cu;
+            const double reuse = (double)hc.c.tm * hc.c.tn / (hc.c.tm + hc.c.tn);
+            const double eff = reuse >= 48.0 ? 1.0 : reuse / 48.0;
+            const double cost = (double)rounds * hc.c.tm * hc.c.tn / eff;
+            if (!found || cost < best) {
+                best = cost;
+                pl.cand = hc.c;
+                found = true;
+            }
+        }
+    }
 
     // MIC_FORCE_VARIANT=<name> pins a variant (tests walk every variant with it)
     if (const char* force = getenv("MIC_FORCE_VARIANT")) {
         if (force[0]) {
-            if (strcmp(force, kDirect.name) == 0) {
+            bool halo_forced = false;
+            for (const HaloCandidate& hc : kHalo) {
+                if (strcmp(force, hc.c.name) != 0) continue;
+                if (!halo_eligible(hc, pl.dt, p, w, need_pointers) || Wp > hc.wp ||
+                    max_tile_slots(p, hc.c.tm) > hc.sl) {
+                    pl.status = MIC_STATUS_NOT_SUPPORTED;
+                    return pl;
+                }
+                pl.cand = hc.c;
+                halo_forced = true;
+            }
+            if (halo_forced) {
+            } else if (strcmp(force, kDirect.name) == 0) {
                 pl.cand = kDirect;
             } else {
                 const Candidate* list;
@@ -503,6 +585,8 @@ mic_status mic_conv_forward(mic_handle handle, double alpha, mic_tensor_desc x_d
     hipError_t err;
     if (pl.cand.v == Variant::DIRECT)
         err = miconv::launch_direct(pl.dt, pl.p, handle->stream);
+    else if (is_halo(pl.cand.v))
+        err = miconv::launch_halo(pl.cand.v, pl.p, handle->stream);
     else
         err = miconv::launch_mfma(pl.cand.v, pl.p, pl.bvec, handle->stream);
     return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;

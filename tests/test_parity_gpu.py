@@ -24,10 +24,15 @@ import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 VARIANTS = {
-    "f32": ["direct", "mfma_f32_128x128", "mfma_f32_128x64", "mfma_f32_64x128", "mfma_f32_256x32"],
-    "f64": ["direct", "mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64"],
+    "f32": ["direct", "mfma_f32_128x128", "mfma_f32_128x64", "mfma_f32_64x128", "mfma_f32_256x32",
+            "halo_f32_3x3_128x128", "halo_f32_3x3_128x64", "halo_f32_3x3_64x128", "halo_f32_5x5_128x128"],
+    "f64": ["direct", "mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64",
+            "halo_f64_3x3_128x128", "halo_f64_3x3_64x64"],
     "bf16": ["direct", "mfma_bf16_128x128", "mfma_bf16_128x64", "mfma_bf16_256x32"],
 }
+# halo variants only take the shapes they were built for (the library answers
+# NOT_SUPPORTED otherwise); every one of them must run on at least one shape
+_ran = set()
 
 U = ("uniform", -1.0, 1.0)
 
@@ -52,6 +57,12 @@ SMALL_SHAPES = [
          pitch=16),
     # one output element per image, one channel
     dict(name="degenerate", N=5, C=1, Hh=3, Ww=2, K=3, R=3, S=2, stride=(3, 3), pads=(0, 0, 0, 0)),
+    # 3x3 on 13x13: several ragged m tiles (M = 507), images straddling tiles, K = 100
+    dict(name="halo3", N=3, C=20, Hh=13, Ww=13, K=100, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
+    # 3x3, stride 2 along H, asymmetric padding (only the 64-row tiles fit its slot span)
+    dict(name="halo3_strided", N=2, C=8, Hh=12, Ww=11, K=40, R=3, S=3, stride=(2, 1), pads=(1, 0, 2, 1)),
+    # 5x5 / pad 2 on 20x20
+    dict(name="halo5", N=2, C=8, Hh=20, Ww=20, K=70, R=5, S=5, stride=(1, 1), pads=(2, 2, 2, 2)),
 ]
 
 
@@ -77,8 +88,19 @@ def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
         monkeypatch.setenv("MIC_FORCE_VARIANT", var)
         print("case", shape["name"], dtype, var, flush=True)
         y = H.out_tensor(lay, ref.shape)
-        _run(lay, x, w, y)
+        try:
+            _run(lay, x, w, y)
+        except mic.MicError as e:
+            if var.startswith("halo_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+                continue
+            raise
         H.check(dtype, y.double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (shape["name"], dtype, var))
+        _ran.add(var)
+
+
+def test_every_variant_was_exercised():
+    want = {v for vs in VARIANTS.values() for v in vs}
+    assert want <= _ran, "variants never run: %s" % sorted(want - _ran)
 
 
 def test_tiny_workload_full_and_deterministic():
@@ -145,8 +167,11 @@ def test_workload_layer_integer_exact(lay):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
-def test_alpha_beta(dtype, monkeypatch):
-    lay = _small("ab", 2, 20, 11, 9, 70, 3, 2, (1, 2), (1, 0, 2, 1), dtype)
+@pytest.mark.parametrize("geom", [(11, 9, 3, 2, (1, 2), (1, 0, 2, 1)), (13, 13, 3, 3, (1, 1), (1, 1, 1, 1))],
+                         ids=["3x2", "3x3"])
+def test_alpha_beta(dtype, geom, monkeypatch):
+    Hh, Ww, R, S, stride, pads = geom
+    lay = _small("ab", 2, 20, Hh, Ww, 70, R, S, stride, pads, dtype)
     xi, wi = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
     acc, _ = oracle.conv2d_fprop(xi, wi, lay.stride, lay.padding)
     y_old = gen.integers(99, acc.shape)
@@ -155,7 +180,12 @@ def test_alpha_beta(dtype, monkeypatch):
     for var in VARIANTS[dtype]:
         monkeypatch.setenv("MIC_FORCE_VARIANT", var)
         y = torch.from_numpy(y_old).to(H.OUT_DT[dtype]).to(H.dev())
-        _run(lay, x, w, y, alpha=0.5, beta=0.25)
+        try:
+            _run(lay, x, w, y, alpha=0.5, beta=0.25)
+        except mic.MicError as e:
+            if var.startswith("halo_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+                continue
+            raise
         assert np.array_equal(y.double().cpu().numpy(), 0.5 * acc + 0.25 * y_old), var
         y = torch.from_numpy(y_old).to(H.OUT_DT[dtype]).to(H.dev())
         _run(lay, x, w, y, alpha=0.0, beta=-2.0)
