@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the steps, run one plain device copy of this many MiB "
+                         "(a known-size kernel to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -99,6 +102,14 @@ def main():
         plans.append((lay, mic.ConvPlan(xt, wt, yt, lay.stride, lay.padding), (x, w)))
     stream = torch.cuda.current_stream(dev)
     flops_step = sum(p.flops for _, p, _ in plans)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         for _, plan, _ in plans:
