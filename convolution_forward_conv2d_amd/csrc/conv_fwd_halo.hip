@@ -234,8 +234,12 @@ conv_fwd_halo_kernel(const ConvParams p)
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = Pol::mfma_s(a[i], bf[j][t], acc[i][j]);
+            // Halfway through the chunk, park the next chunk in the other
+            // buffer: its last readers finished before the previous barrier,
+            // and the store's wait on the global loads and its LDS latency
+            // now overlap the second half of the MFMAs.
+            if (t == SEG / 2 && more) store_chunk(cur ^ 1);
         }
-        if (more) store_chunk(cur ^ 1);
         __syncthreads();
     }
 
@@ -261,7 +265,9 @@ static hipError_t launch_halo_variant(const ConvParams& p0, hipStream_t stream)
     X(HALO_F32_3x3_128x128, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16)  \
     X(HALO_F32_3x3_128x64, PolF32, 128, 64, 2, 2, 3, 3, 4, 16, 16)    \
     X(HALO_F32_3x3_64x128, PolF32, 64, 128, 2, 2, 3, 3, 4, 16, 16)    \
+    X(HALO_F32_3x3_96x128, PolF32, 96, 128, 1, 4, 3, 3, 4, 16, 16)    \
     X(HALO_F32_5x5_128x128, PolF32, 128, 128, 2, 2, 5, 5, 4, 32, 16)  \
+    X(HALO_F32_5x5_128x128_C2, PolF32, 128, 128, 2, 2, 5, 5, 2, 32, 16) \
     X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16)  \
     X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16)
 

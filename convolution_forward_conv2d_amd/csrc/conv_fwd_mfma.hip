@@ -209,13 +209,16 @@ conv_fwd_mfma_kernel(const ConvParams p)
             for (int v = 0; v < FRAG_VECS; ++v) fb[j][v] = src[v];
         }
 #pragma unroll
-        for (int t = 0; t < STEPS; ++t)
+        for (int t = 0; t < STEPS; ++t) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = Pol::mfma(fa[i], fb[j], t, acc[i][j]);
-        if (more) store_tiles(cur ^ 1);
+            // store the next chunk into the other buffer halfway through (its
+            // last readers finished before the previous barrier)
+            if (t == STEPS / 2 && more) store_tiles(cur ^ 1);
+        }
         __syncthreads();
     }
 

@@ -22,7 +22,9 @@ enum class Variant : int {
     HALO_F32_3x3_128x128,   // tap-batched kernel with an LDS input halo (conv_fwd_halo.hip)
     HALO_F32_3x3_128x64,
     HALO_F32_3x3_64x128,
+    HALO_F32_3x3_96x128,
     HALO_F32_5x5_128x128,
+    HALO_F32_5x5_128x128_C2,
     HALO_F64_3x3_128x128,
     HALO_F64_3x3_64x64,
     COUNT

@@ -120,15 +120,18 @@ struct HaloCandidate {
     Candidate c;
     DType dt;
     int r, s, cb, wp, sl;
+    double eff;   // relative per-tile efficiency, measured on MI355X (128x128 = 1)
 };
 
 const HaloCandidate kHalo[] = {
-    {{Variant::HALO_F32_3x3_128x128, 128, 128, "halo_f32_3x3_128x128"}, DType::F32, 3, 3, 4, 16, 16},
-    {{Variant::HALO_F32_3x3_128x64, 128, 64, "halo_f32_3x3_128x64"}, DType::F32, 3, 3, 4, 16, 16},
-    {{Variant::HALO_F32_3x3_64x128, 64, 128, "halo_f32_3x3_64x128"}, DType::F32, 3, 3, 4, 16, 16},
-    {{Variant::HALO_F32_5x5_128x128, 128, 128, "halo_f32_5x5_128x128"}, DType::F32, 5, 5, 4, 32, 16},
-    {{Variant::HALO_F64_3x3_128x128, 128, 128, "halo_f64_3x3_128x128"}, DType::F64, 3, 3, 4, 16, 16},
-    {{Variant::HALO_F64_3x3_64x64, 64, 64, "halo_f64_3x3_64x64"}, DType::F64, 3, 3, 4, 16, 16},
+    {{Variant::HALO_F32_3x3_128x128, 128, 128, "halo_f32_3x3_128x128"}, DType::F32, 3, 3, 4, 16, 16, 1.0},
+    {{Variant::HALO_F32_3x3_128x64, 128, 64, "halo_f32_3x3_128x64"}, DType::F32, 3, 3, 4, 16, 16, 0.93},
+    {{Variant::HALO_F32_3x3_64x128, 64, 128, "halo_f32_3x3_64x128"}, DType::F32, 3, 3, 4, 16, 16, 0.8},
+    {{Variant::HALO_F32_3x3_96x128, 96, 128, "halo_f32_3x3_96x128"}, DType::F32, 3, 3, 4, 16, 16, 0.97},
+    {{Variant::HALO_F32_5x5_128x128, 128, 128, "halo_f32_5x5_128x128"}, DType::F32, 5, 5, 4, 32, 16, 0.93},
+    {{Variant::HALO_F32_5x5_128x128_C2, 128, 128, "halo_f32_5x5_128x128_c2"}, DType::F32, 5, 5, 2, 32, 16, 1.0},
+    {{Variant::HALO_F64_3x3_128x128, 128, 128, "halo_f64_3x3_128x128"}, DType::F64, 3, 3, 4, 16, 16, 1.0},
+    {{Variant::HALO_F64_3x3_64x64, 64, 64, "halo_f64_3x3_64x64"}, DType::F64, 3, 3, 4, 16, 16, 0.8},
 };
 
 struct Plan {
@@ -292,7 +295,8 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
 
     const int num_cu = h ? h->num_cu : kDefaultCUs;
     pl.cand = choose_tile(pl.dt, p.M, p.K, num_cu);
-    // prefer a tap-batched halo kernel where one fits, chosen by the same tile cost
+    // prefer a tap-batched halo kernel where one fits: the busiest compute unit
+    // runs ceil(tiles / CUs) tiles, each costing its area over its efficiency
     {
         double best = 0;
         bool found = false;
@@ -301,9 +305,7 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
             if (max_tile_slots(p, hc.c.tm) > hc.sl) continue;
             const int64_t tiles = (int64_t)((p.M + hc.c.tm - 1) / hc.c.tm) * ((p.K + hc.c.tn - 1) / hc.c.tn);
             const int64_t rounds = (tiles + num_cu - 1) / num_cu;
-            const double reuse = (double)hc.c.tm * hc.c.tn / (hc.c.tm + hc.c.tn);
-            const double eff = reuse >= 48.0 ? 1.0 : reuse / 48.0;
-            const double cost = (double)rounds * hc.c.tm * hc.c.tn / eff;
+            const double cost = (double)rounds * hc.c.tm * hc.c.tn / hc.eff;
             if (!found || cost < best) {
                 best = cost;
                 pl.cand = hc.c;

@@ -134,8 +134,8 @@ def test_kernel_choice_host_only():
     for name in ("alexnet_conv3", "alexnet_conv4", "alexnet_conv5", "overfeat_l3", "overfeat_l4",
                  "overfeat_l5"):
         assert names[name].startswith("halo_f32_3x3_"), (name, names[name])
-    assert names["alexnet_conv2"] == "halo_f32_5x5_128x128"
-    assert names["overfeat_l2"] == "halo_f32_5x5_128x128"
+    assert names["alexnet_conv2"].startswith("halo_f32_5x5_")
+    assert names["overfeat_l2"].startswith("halo_f32_5x5_")
     assert names["overfeat_l1"].startswith("mfma_f32_")
     assert names["prec_conv3_f64_nchw"].startswith("halo_f64_3x3_")
     assert names["prec_conv3_bf16_nhwc"].startswith("mfma_bf16_")
