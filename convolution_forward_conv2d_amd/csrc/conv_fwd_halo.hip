@@ -84,7 +84,10 @@ conv_fwd_halo_kernel(const ConvParams p)
     const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
-    const int m0 = mt * TM;
+    // a tile covers rows m0 .. m_end-1: TM consecutive rows, or one output
+    // image (m_step = P*Q <= TM, the rest of the tile idle)
+    const int m0 = mt * p.m_step;
+    const int m_end = min(m0 + p.m_step, p.M);
     const int n0 = nt * TN;
 
     const In* __restrict__ x = static_cast<const In*>(p.x);
@@ -98,8 +101,7 @@ conv_fwd_halo_kernel(const ConvParams p)
         return (int)n * p.Hp + (int)pp * p.u;
     };
     const int vr_first = vrow(m0);
-    const int m_last = min(m0 + TM, p.M) - 1;
-    const int nslots = vrow(m_last) + R - vr_first;     // <= SL (host-checked)
+    const int nslots = vrow(m_end - 1) + R - vr_first;  // <= SL (host-checked)
 
     // ---- halo loader: thread -> HE (channel, slot, column) positions, fixed for the tile
     int h_off[HE];
@@ -187,7 +189,7 @@ conv_fwd_halo_kernel(const ConvParams p)
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * WM + i * BM + lrow;
         int base = 0;
-        if (m < p.M) {
+        if (m < m_end) {
             uint32_t n, pq, pp, q;
             p.div_pq.divmod((uint32_t)m, n, pq);
             p.div_q.divmod(pq, pp, q);
@@ -243,7 +245,7 @@ conv_fwd_halo_kernel(const ConvParams p)
         __syncthreads();
     }
 
-    store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, wave, lane);
+    store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, m_end, wave, lane);
 }
 
 // ------------------------------------------------------------------ instances and launch
@@ -252,7 +254,8 @@ template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int
 static hipError_t launch_halo_variant(const ConvParams& p0, hipStream_t stream)
 {
     ConvParams p = p0;
-    p.m_tiles = (p.M + TM - 1) / TM;
+    if (p.m_step <= 0 || p.m_step > TM) p.m_step = TM;   // the host sets P*Q for image tiles
+    p.m_tiles = (p.M + p.m_step - 1) / p.m_step;
     p.n_tiles = (p.K + TN - 1) / TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
     hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL>),
@@ -268,6 +271,8 @@ static hipError_t launch_halo_variant(const ConvParams& p0, hipStream_t stream)
     X(HALO_F32_3x3_96x128, PolF32, 96, 128, 1, 4, 3, 3, 4, 16, 16)    \
     X(HALO_F32_5x5_128x128, PolF32, 128, 128, 2, 2, 5, 5, 4, 32, 16)  \
     X(HALO_F32_5x5_128x128_C2, PolF32, 128, 128, 2, 2, 5, 5, 2, 32, 16) \
+    X(HALO_F32x16_3x3_176x128, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16) \
+    X(HALO_F32x16_3x3_144x128, PolF32x16, 144, 128, 1, 4, 3, 3, 4, 16, 16) \
     X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16)  \
     X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16)
 

@@ -223,7 +223,7 @@ conv_fwd_mfma_kernel(const ConvParams p)
     }
 
     // ---- epilogue
-    store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, wave, lane);
+    store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, p.M, wave, lane);
 }
 
 // ------------------------------------------------------------------ instances and launch

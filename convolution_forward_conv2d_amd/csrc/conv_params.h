@@ -55,6 +55,7 @@ struct ConvParams {
     int M;               // N * P * Q   (rows of the implicit GEMM)
     int Kred;            // C * R * S   (reduction length)
     int m_tiles, n_tiles;
+    int m_step;          // output rows per m tile (halo kernel: TM, or P*Q for one image per tile)
     FastDiv div_pq, div_q, div_rs, div_s, div_hp;
     double alpha, beta;  // converted to the accumulation type inside the kernel
 };

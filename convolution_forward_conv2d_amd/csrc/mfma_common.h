@@ -12,6 +12,7 @@
 namespace miconv {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -43,6 +44,23 @@ struct PolF32 {
     // accumulator value i of lane l is D[8 (i/4) + 4 (l/32) + i%4][l % 32]
     __device__ static int row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
     __device__ static int col(int, int lane) { return lane & 31; }
+};
+
+// fp32 on 16x16 blocks: finer tile granularity (multiples of 16 rows) at
+// the same rate as the 32x32x2 instruction.
+struct PolF32x16 {
+    using In = float;
+    using Acc = float;
+    using Out = float;
+    using AccV = f32x4;
+    static constexpr int BM = 16, G = 4, V = 1, NACC = 4;
+    // v_mfma_f32_16x16x4_f32: lane l gives A[l%16][l/16], B[l/16][l%16].
+    __device__ static AccV mfma_s(float a, float b, AccV c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    // accumulator value i of lane l is D[4 (l/16) + i][l % 16] (checked on gfx950)
+    __device__ static int row(int i, int lane) { return 4 * (lane >> 4) + i; }
+    __device__ static int col(int, int lane) { return lane & 15; }
 };
 
 struct PolF64 {
@@ -141,13 +159,14 @@ template <class In> __device__ __forceinline__ In load_elem(const In* p) { retur
 // per-wave LDS stage so that the global stores run along y's unit-stride
 // direction: along m (NCHW-like y) or along k (NHWC-like y, syk == 1)
 // (maxDNN page, "Proposed Method": outputs reorganised in shared memory for
-// coalesced writes).  smem must hold 4 * BM * (BM + 1) accumulators and be
-// free (every wave past its last read of the main loop's tiles).  With
-// beta == 0, y is never read.  Called by all four waves alike.
+// coalesced writes).  Rows at or past m_end belong to no output (tile
+// padding) and are dropped.  smem must hold 4 * BM * (BM + 1) accumulators
+// and be free (every wave past its last read of the main loop's tiles).
+// With beta == 0, y is never read.  Called by all four waves alike.
 template <class Pol, int FM, int FN>
 __device__ __forceinline__ void store_acc_tile(const ConvParams& p, unsigned char* smem,
                                                typename Pol::AccV (&acc)[FM][FN],
-                                               int mw0, int nw0, int wave, int lane)
+                                               int mw0, int nw0, int m_end, int wave, int lane)
 {
     using Acc = typename Pol::Acc;
     using Out = typename Pol::Out;
@@ -176,7 +195,7 @@ __device__ __forceinline__ void store_acc_tile(const ConvParams& p, unsigned cha
                 const int kl = k_fast ? (lane % BM) : (lane / BM + LG * t);
                 const int gm = bm0 + ml;
                 const int gk = bk0 + kl;
-                if (gm < p.M && gk < p.K) {
+                if (gm < m_end && gk < p.K) {
                     uint32_t n, pq, pp, q;
                     p.div_pq.divmod((uint32_t)gm, n, pq);
                     p.div_q.divmod(pq, pp, q);

@@ -130,6 +130,8 @@ const HaloCandidate kHalo[] = {
     {{Variant::HALO_F32_3x3_96x128, 96, 128, "halo_f32_3x3_96x128"}, DType::F32, 3, 3, 4, 16, 16, 0.97},
     {{Variant::HALO_F32_5x5_128x128, 128, 128, "halo_f32_5x5_128x128"}, DType::F32, 5, 5, 4, 32, 16, 0.93},
     {{Variant::HALO_F32_5x5_128x128_C2, 128, 128, "halo_f32_5x5_128x128_c2"}, DType::F32, 5, 5, 2, 32, 16, 1.0},
+    {{Variant::HALO_F32x16_3x3_176x128, 176, 128, "halo_f32x16_3x3_176x128"}, DType::F32, 3, 3, 4, 16, 16, 0.9},
+    {{Variant::HALO_F32x16_3x3_144x128, 144, 128, "halo_f32x16_3x3_144x128"}, DType::F32, 3, 3, 4, 16, 16, 0.95},
     {{Variant::HALO_F64_3x3_128x128, 128, 128, "halo_f64_3x3_128x128"}, DType::F64, 3, 3, 4, 16, 16, 1.0},
     {{Variant::HALO_F64_3x3_64x64, 64, 64, "halo_f64_3x3_64x64"}, DType::F64, 3, 3, 4, 16, 16, 0.8},
 };
@@ -141,6 +143,32 @@ struct Plan {
     Candidate cand;
     bool bvec;
 };
+
+int max_tile_slots(const ConvParams& p, int step);
+
+// Cheapest way to run halo instance hc on p: tiles of hc.c.tm consecutive
+// output rows, or one output image per tile (P*Q <= tm).  Returns false if
+// neither fits; else the cost (busiest CU's tile count x tile area /
+// efficiency) and the rows per tile.
+bool halo_cost(const HaloCandidate& hc, const ConvParams& p, int Wp, int num_cu, double* cost, int* step)
+{
+    if (Wp > hc.wp) return false;
+    const int pq = p.P * p.Q;
+    const int steps[2] = {hc.c.tm, pq <= hc.c.tm ? pq : 0};
+    bool ok = false;
+    for (int st : steps) {
+        if (st <= 0 || max_tile_slots(p, st) > hc.sl) continue;
+        const int64_t tiles = (int64_t)((p.M + st - 1) / st) * ((p.K + hc.c.tn - 1) / hc.c.tn);
+        const int64_t rounds = (tiles + num_cu - 1) / num_cu;
+        const double c = (double)rounds * hc.c.tm * hc.c.tn / hc.eff;
+        if (!ok || c < *cost) {
+            *cost = c;
+            *step = st;
+            ok = true;
+        }
+    }
+    return ok;
+}
 
 void candidates(DType dt, const Candidate** list, int* count)
 {
@@ -184,13 +212,14 @@ bool is_halo(Variant v)
     return false;
 }
 
-// Largest number of padded input rows ("slots") one tile of TM consecutive
-// output rows touches: rows n*Hp + p*u .. of its first and last output row.
-int max_tile_slots(const ConvParams& p, int tm)
+// Largest number of padded input rows ("slots") one tile of `step`
+// consecutive output rows touches: rows n*Hp + p*u .. of its first and last
+// output row.
+int max_tile_slots(const ConvParams& p, int step)
 {
     int worst = 0;
-    for (int64_t m0 = 0; m0 < p.M; m0 += tm) {
-        const int64_t m1 = (m0 + tm < p.M ? m0 + tm : p.M) - 1;
+    for (int64_t m0 = 0; m0 < p.M; m0 += step) {
+        const int64_t m1 = (m0 + step < p.M ? m0 + step : p.M) - 1;
         const int64_t pq = (int64_t)p.P * p.Q;
         const int64_t v0 = (m0 / pq) * p.Hp + ((m0 % pq) / p.Q) * p.u;
         const int64_t v1 = (m1 / pq) * p.Hp + ((m1 % pq) / p.Q) * p.u;
@@ -301,14 +330,14 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
         double best = 0;
         bool found = false;
         for (const HaloCandidate& hc : kHalo) {
-            if (!halo_eligible(hc, pl.dt, p, w, need_pointers) || Wp > hc.wp) continue;
-            if (max_tile_slots(p, hc.c.tm) > hc.sl) continue;
-            const int64_t tiles = (int64_t)((p.M + hc.c.tm - 1) / hc.c.tm) * ((p.K + hc.c.tn - 1) / hc.c.tn);
-            const int64_t rounds = (tiles + num_cu - 1) / num_cu;
-            const double cost = (double)rounds * hc.c.tm * hc.c.tn / hc.eff;
+            double cost;
+            int step;
+            if (!halo_eligible(hc, pl.dt, p, w, need_pointers)) continue;
+            if (!halo_cost(hc, p, Wp, num_cu, &cost, &step)) continue;
             if (!found || cost < best) {
                 best = cost;
                 pl.cand = hc.c;
+                p.m_step = step;
                 found = true;
             }
         }
@@ -320,14 +349,18 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
             bool halo_forced = false;
             for (const HaloCandidate& hc : kHalo) {
                 if (strcmp(force, hc.c.name) != 0) continue;
-                if (!halo_eligible(hc, pl.dt, p, w, need_pointers) || Wp > hc.wp ||
-                    max_tile_slots(p, hc.c.tm) > hc.sl) {
+                double cost;
+                int step;
+                if (!halo_eligible(hc, pl.dt, p, w, need_pointers) ||
+                    !halo_cost(hc, p, Wp, num_cu, &cost, &step)) {
                     pl.status = MIC_STATUS_NOT_SUPPORTED;
                     return pl;
                 }
                 pl.cand = hc.c;
+                p.m_step = step;
                 halo_forced = true;
             }
+            if (!halo_forced) p.m_step = 0;
             if (halo_forced) {
             } else if (strcmp(force, kDirect.name) == 0) {
                 pl.cand = kDirect;

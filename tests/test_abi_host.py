@@ -133,7 +133,7 @@ def test_kernel_choice_host_only():
             _free(*d)
     for name in ("alexnet_conv3", "alexnet_conv4", "alexnet_conv5", "overfeat_l3", "overfeat_l4",
                  "overfeat_l5"):
-        assert names[name].startswith("halo_f32_3x3_"), (name, names[name])
+        assert names[name].startswith(("halo_f32_3x3_", "halo_f32x16_3x3_")), (name, names[name])
     assert names["alexnet_conv2"].startswith("halo_f32_5x5_")
     assert names["overfeat_l2"].startswith("halo_f32_5x5_")
     assert names["overfeat_l1"].startswith("mfma_f32_")
