@@ -37,8 +37,8 @@
 
 namespace miconv {
 
-template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL>
-__global__ void __launch_bounds__(256)
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS>
+__global__ void __launch_bounds__(256 * KS)
 conv_fwd_halo_kernel(const ConvParams p)
 {
     using In = typename Pol::In;
@@ -74,12 +74,20 @@ conv_fwd_halo_kernel(const ConvParams p)
     static_assert((TK * ES) % 8 == 0, "slab rows are whole 8-byte vectors");
     static_assert(4 * BM * (BM + 1) * (int)sizeof(typename Pol::Acc) <= 2 * BUF_BYTES, "epilogue stage fits");
     static_assert(((CPG - 1) * PLANE + (R - 1) * WP + S) * ES < 65536, "LDS immediate offsets");
+    // KS = 2: two 4-wave halves share one output tile and split its
+    // reduction (alternate channel blocks); half 1 hands its partial sums to
+    // half 0 through LDS at the end, so each SIMD holds two waves of the tile
+    static_assert(KS == 1 || KS == 2, "one or two halves");
+    constexpr int RED_BYTES = KS == 2 ? 4 * FM * FN * Pol::NACC * 64 * (int)sizeof(typename Pol::Acc) : 0;
+    static_assert(RED_BYTES <= KS * 2 * BUF_BYTES, "partial sums fit in the chunk buffers");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char smem_all[KS * 2 * BUF_BYTES];
 
-    const int tid = threadIdx.x;
+    const int half = KS == 2 ? (int)(threadIdx.x >> 8) : 0;
+    const int tid = threadIdx.x & 255;           // thread within its half
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = tid >> 6;                   // wave within its half
+    unsigned char* smem = smem_all + half * 2 * BUF_BYTES;
 
     const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
     const int mt = tile / p.n_tiles;
@@ -207,16 +215,11 @@ conv_fwd_halo_kernel(const ConvParams p)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = AccV{};
 
-    const int nchunks = p.C / CB;
-    load_chunk(0);
-    store_chunk(0);
-    __syncthreads();
-
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int cur = ch & 1;
-        const bool more = ch + 1 < nchunks;
-        if (more) load_chunk((ch + 1) * CB);
-
+    // MFMAs of the chunk in LDS buffer `cur`.  Halfway through, the next
+    // chunk (already in registers) is parked in the other buffer: its last
+    // readers finished before the previous barrier, and the store's wait on
+    // the global loads and its LDS latency overlap the second half.
+    auto compute = [&](int cur, bool park) {
         const In* halo = reinterpret_cast<const In*>(smem + cur * BUF_BYTES);
         const unsigned char* slab = smem + cur * BUF_BYTES + HALO_BYTES;
         In bf[FN][SEG];
@@ -236,21 +239,59 @@ conv_fwd_halo_kernel(const ConvParams p)
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = Pol::mfma_s(a[i], bf[j][t], acc[i][j]);
-            // Halfway through the chunk, park the next chunk in the other
-            // buffer: its last readers finished before the previous barrier,
-            // and the store's wait on the global loads and its LDS latency
-            // now overlap the second half of the MFMAs.
-            if (t == SEG / 2 && more) store_chunk(cur ^ 1);
+            if (t == SEG / 2 && park) store_chunk(cur ^ 1);
+        }
+    };
+
+    // chunk j of this half is channel block j*KS + half
+    const int nblocks = p.C / CB;
+    const int iters = (nblocks + KS - 1) / KS;
+    auto chunk_of = [&](int j) { return j * KS + half; };
+    if (chunk_of(0) < nblocks) {
+        load_chunk(chunk_of(0) * CB);
+        store_chunk(0);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < iters; ++it) {
+        const int cur = it & 1;
+        const bool mine = chunk_of(it) < nblocks;          // uniform per half
+        const bool more = chunk_of(it + 1) < nblocks;
+        if (more) load_chunk(chunk_of(it + 1) * CB);
+        if (mine) compute(cur, more);
+        __syncthreads();
+    }
+
+    if constexpr (KS == 2) {
+        // half 1's partial sums -> LDS -> added by half 0 in a fixed order
+        typename Pol::Acc* red = reinterpret_cast<typename Pol::Acc*>(smem_all);
+        auto red_at = [&](int i, int j, int e) { return ((((wave * FM + i) * FN + j) * Pol::NACC + e) << 6) + lane; };
+        if (half == 1) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int e = 0; e < Pol::NACC; ++e) red[red_at(i, j, e)] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (half == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int e = 0; e < Pol::NACC; ++e) acc[i][j][e] += red[red_at(i, j, e)];
         }
         __syncthreads();
     }
 
-    store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, m_end, wave, lane);
+    store_acc_tile<Pol, FM, FN>(p, smem_all, acc, m0 + wm * WM, n0 + wn * WN, m_end, wave, lane, half == 0);
 }
 
 // ------------------------------------------------------------------ instances and launch
 
-template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL>
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS>
 static hipError_t launch_halo_variant(const ConvParams& p0, hipStream_t stream)
 {
     ConvParams p = p0;
@@ -258,29 +299,31 @@ static hipError_t launch_halo_variant(const ConvParams& p0, hipStream_t stream)
     p.m_tiles = (p.M + p.m_step - 1) / p.m_step;
     p.n_tiles = (p.K + TN - 1) / TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
-    hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL>),
-                       grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS>),
+                       grid, dim3(256 * KS), 0, stream, p);
     return hipGetLastError();
 }
 
-//        name                  policy   TM   TN  waves  R  S  CB  WP  SL
-#define MICONV_HALO_VARIANTS(X)                                      \
-    X(HALO_F32_3x3_128x128, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16)  \
-    X(HALO_F32_3x3_128x64, PolF32, 128, 64, 2, 2, 3, 3, 4, 16, 16)    \
-    X(HALO_F32_3x3_64x128, PolF32, 64, 128, 2, 2, 3, 3, 4, 16, 16)    \
-    X(HALO_F32_3x3_96x128, PolF32, 96, 128, 1, 4, 3, 3, 4, 16, 16)    \
-    X(HALO_F32_5x5_128x128, PolF32, 128, 128, 2, 2, 5, 5, 4, 32, 16)  \
-    X(HALO_F32_5x5_128x128_C2, PolF32, 128, 128, 2, 2, 5, 5, 2, 32, 16) \
-    X(HALO_F32x16_3x3_176x128, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16) \
-    X(HALO_F32x16_3x3_144x128, PolF32x16, 144, 128, 1, 4, 3, 3, 4, 16, 16) \
-    X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16)  \
-    X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16)
+//        name                     policy     TM   TN  waves  R  S  CB  WP  SL  KS
+#define MICONV_HALO_VARIANTS(X)                                                 \
+    X(HALO_F32_3x3_128x128, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1)          \
+    X(HALO_F32_3x3_128x64, PolF32, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1)            \
+    X(HALO_F32_3x3_64x128, PolF32, 64, 128, 2, 2, 3, 3, 4, 16, 16, 1)            \
+    X(HALO_F32_3x3_96x128, PolF32, 96, 128, 1, 4, 3, 3, 4, 16, 16, 1)            \
+    X(HALO_F32_5x5_128x128, PolF32, 128, 128, 2, 2, 5, 5, 4, 32, 16, 1)          \
+    X(HALO_F32_5x5_128x128_C2, PolF32, 128, 128, 2, 2, 5, 5, 2, 32, 16, 1)       \
+    X(HALO_F32x16_3x3_176x128, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 1)    \
+    X(HALO_F32x16_3x3_144x128, PolF32x16, 144, 128, 1, 4, 3, 3, 4, 16, 16, 1)    \
+    X(HALO_F32x16_3x3_176x128_KS2, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 2) \
+    X(HALO_F32_3x3_128x128_KS2, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 2)      \
+    X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1)          \
+    X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16, 1)
 
 hipError_t launch_halo(Variant v, const ConvParams& p, hipStream_t stream)
 {
     switch (v) {
-#define X(name, pol, tm, tn, wmm, wnn, r, s, cb, wp, sl) \
-    case Variant::name: return launch_halo_variant<pol, tm, tn, wmm, wnn, r, s, cb, wp, sl>(p, stream);
+#define X(name, pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks) \
+    case Variant::name: return launch_halo_variant<pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks>(p, stream);
         MICONV_HALO_VARIANTS(X)
 #undef X
     default: return hipErrorInvalidValue;

@@ -162,11 +162,13 @@ template <class In> __device__ __forceinline__ In load_elem(const In* p) { retur
 // coalesced writes).  Rows at or past m_end belong to no output (tile
 // padding) and are dropped.  smem must hold 4 * BM * (BM + 1) accumulators
 // and be free (every wave past its last read of the main loop's tiles).
-// With beta == 0, y is never read.  Called by all four waves alike.
+// With beta == 0, y is never read.  Called by every wave of the workgroup
+// alike (it holds barriers); waves with active == false only keep step.
 template <class Pol, int FM, int FN>
 __device__ __forceinline__ void store_acc_tile(const ConvParams& p, unsigned char* smem,
                                                typename Pol::AccV (&acc)[FM][FN],
-                                               int mw0, int nw0, int m_end, int wave, int lane)
+                                               int mw0, int nw0, int m_end, int wave, int lane,
+                                               bool active = true)
 {
     using Acc = typename Pol::Acc;
     using Out = typename Pol::Out;
@@ -183,9 +185,11 @@ __device__ __forceinline__ void store_acc_tile(const ConvParams& p, unsigned cha
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
+            if (active) {
 #pragma unroll
-            for (int e = 0; e < Pol::NACC; ++e)
-                stage[Pol::col(e, lane) * STAGE_PITCH + Pol::row(e, lane)] = acc[i][j][e];
+                for (int e = 0; e < Pol::NACC; ++e)
+                    stage[Pol::col(e, lane) * STAGE_PITCH + Pol::row(e, lane)] = acc[i][j][e];
+            }
             __syncthreads();
             const int bm0 = mw0 + i * BM;
             const int bk0 = nw0 + j * BM;
@@ -195,7 +199,7 @@ __device__ __forceinline__ void store_acc_tile(const ConvParams& p, unsigned cha
                 const int kl = k_fast ? (lane % BM) : (lane / BM + LG * t);
                 const int gm = bm0 + ml;
                 const int gk = bk0 + kl;
-                if (gm < m_end && gk < p.K) {
+                if (active && gm < m_end && gk < p.K) {
                     uint32_t n, pq, pp, q;
                     p.div_pq.divmod((uint32_t)gm, n, pq);
                     p.div_q.divmod(pq, pp, q);

@@ -121,19 +121,22 @@ struct HaloCandidate {
     DType dt;
     int r, s, cb, wp, sl;
     double eff;   // relative per-tile efficiency, measured on MI355X (128x128 = 1)
+    int ks;       // 2: a 512-thread workgroup whose halves split one tile's reduction
 };
 
 const HaloCandidate kHalo[] = {
-    {{Variant::HALO_F32_3x3_128x128, 128, 128, "halo_f32_3x3_128x128"}, DType::F32, 3, 3, 4, 16, 16, 1.0},
-    {{Variant::HALO_F32_3x3_128x64, 128, 64, "halo_f32_3x3_128x64"}, DType::F32, 3, 3, 4, 16, 16, 0.93},
-    {{Variant::HALO_F32_3x3_64x128, 64, 128, "halo_f32_3x3_64x128"}, DType::F32, 3, 3, 4, 16, 16, 0.8},
-    {{Variant::HALO_F32_3x3_96x128, 96, 128, "halo_f32_3x3_96x128"}, DType::F32, 3, 3, 4, 16, 16, 0.97},
-    {{Variant::HALO_F32_5x5_128x128, 128, 128, "halo_f32_5x5_128x128"}, DType::F32, 5, 5, 4, 32, 16, 0.93},
-    {{Variant::HALO_F32_5x5_128x128_C2, 128, 128, "halo_f32_5x5_128x128_c2"}, DType::F32, 5, 5, 2, 32, 16, 1.0},
-    {{Variant::HALO_F32x16_3x3_176x128, 176, 128, "halo_f32x16_3x3_176x128"}, DType::F32, 3, 3, 4, 16, 16, 0.9},
-    {{Variant::HALO_F32x16_3x3_144x128, 144, 128, "halo_f32x16_3x3_144x128"}, DType::F32, 3, 3, 4, 16, 16, 0.95},
-    {{Variant::HALO_F64_3x3_128x128, 128, 128, "halo_f64_3x3_128x128"}, DType::F64, 3, 3, 4, 16, 16, 1.0},
-    {{Variant::HALO_F64_3x3_64x64, 64, 64, "halo_f64_3x3_64x64"}, DType::F64, 3, 3, 4, 16, 16, 0.8},
+    {{Variant::HALO_F32_3x3_128x128, 128, 128, "halo_f32_3x3_128x128"}, DType::F32, 3, 3, 4, 16, 16, 1.0, 1},
+    {{Variant::HALO_F32_3x3_128x64, 128, 64, "halo_f32_3x3_128x64"}, DType::F32, 3, 3, 4, 16, 16, 0.93, 1},
+    {{Variant::HALO_F32_3x3_64x128, 64, 128, "halo_f32_3x3_64x128"}, DType::F32, 3, 3, 4, 16, 16, 0.8, 1},
+    {{Variant::HALO_F32_3x3_96x128, 96, 128, "halo_f32_3x3_96x128"}, DType::F32, 3, 3, 4, 16, 16, 0.97, 1},
+    {{Variant::HALO_F32_5x5_128x128, 128, 128, "halo_f32_5x5_128x128"}, DType::F32, 5, 5, 4, 32, 16, 0.93, 1},
+    {{Variant::HALO_F32_5x5_128x128_C2, 128, 128, "halo_f32_5x5_128x128_c2"}, DType::F32, 5, 5, 2, 32, 16, 1.0, 1},
+    {{Variant::HALO_F32x16_3x3_176x128, 176, 128, "halo_f32x16_3x3_176x128"}, DType::F32, 3, 3, 4, 16, 16, 0.9, 1},
+    {{Variant::HALO_F32x16_3x3_144x128, 144, 128, "halo_f32x16_3x3_144x128"}, DType::F32, 3, 3, 4, 16, 16, 0.95, 1},
+    {{Variant::HALO_F32x16_3x3_176x128_KS2, 176, 128, "halo_f32x16_3x3_176x128_ks2"}, DType::F32, 3, 3, 4, 16, 16, 0.95, 2},
+    {{Variant::HALO_F32_3x3_128x128_KS2, 128, 128, "halo_f32_3x3_128x128_ks2"}, DType::F32, 3, 3, 4, 16, 16, 0.9, 2},
+    {{Variant::HALO_F64_3x3_128x128, 128, 128, "halo_f64_3x3_128x128"}, DType::F64, 3, 3, 4, 16, 16, 1.0, 1},
+    {{Variant::HALO_F64_3x3_64x64, 64, 64, "halo_f64_3x3_64x64"}, DType::F64, 3, 3, 4, 16, 16, 0.8, 1},
 };
 
 struct Plan {
@@ -160,7 +163,11 @@ bool halo_cost(const HaloCandidate& hc, const ConvParams& p, int Wp, int num_cu,
         if (st <= 0 || max_tile_slots(p, st) > hc.sl) continue;
         const int64_t tiles = (int64_t)((p.M + st - 1) / st) * ((p.K + hc.c.tn - 1) / hc.c.tn);
         const int64_t rounds = (tiles + num_cu - 1) / num_cu;
-        const double c = (double)rounds * hc.c.tm * hc.c.tn / hc.eff;
+        // a split workgroup fills a CU: only worth it with at most one tile per CU;
+        // a plain one alone on its CU has no second workgroup to hide latency
+        if (hc.ks == 2 && tiles > num_cu) continue;
+        const double occ = (hc.ks == 1 && tiles <= num_cu) ? 0.92 : 1.0;
+        const double c = (double)rounds * hc.c.tm * hc.c.tn / (hc.eff * occ);
         if (!ok || c < *cost) {
             *cost = c;
             *step = st;

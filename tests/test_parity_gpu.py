@@ -27,7 +27,7 @@ VARIANTS = {
     "f32": ["direct", "mfma_f32_128x128", "mfma_f32_128x64", "mfma_f32_64x128", "mfma_f32_256x32",
             "halo_f32_3x3_128x128", "halo_f32_3x3_128x64", "halo_f32_3x3_64x128", "halo_f32_3x3_96x128",
             "halo_f32_5x5_128x128", "halo_f32_5x5_128x128_c2", "halo_f32x16_3x3_176x128",
-            "halo_f32x16_3x3_144x128"],
+            "halo_f32x16_3x3_144x128", "halo_f32x16_3x3_176x128_ks2", "halo_f32_3x3_128x128_ks2"],
     "f64": ["direct", "mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64",
             "halo_f64_3x3_128x128", "halo_f64_3x3_64x64"],
     "bf16": ["direct", "mfma_bf16_128x128", "mfma_bf16_128x64", "mfma_bf16_256x32"],
@@ -63,6 +63,8 @@ SMALL_SHAPES = [
     dict(name="halo3", N=3, C=20, Hh=13, Ww=13, K=100, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
     # 3x3, stride 2 along H, asymmetric padding (only the 64-row tiles fit its slot span)
     dict(name="halo3_strided", N=2, C=8, Hh=12, Ww=11, K=40, R=3, S=3, stride=(2, 1), pads=(1, 0, 2, 1)),
+    # one channel block only: with the reduction split in two, the second half has no work
+    dict(name="halo3_c4", N=1, C=4, Hh=13, Ww=13, K=16, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
     # 5x5 / pad 2 on 20x20
     dict(name="halo5", N=2, C=8, Hh=20, Ww=20, K=70, R=5, S=5, stride=(1, 1), pads=(2, 2, 2, 2)),
 ]
