@@ -35,7 +35,7 @@ namespace miconv {
 
 // ------------------------------------------------------------------ the kernel
 
-template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int TK, bool BVEC>
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int TK, bool BVEC, bool TAP>
 __global__ void __launch_bounds__(256)
 conv_fwd_mfma_kernel(const ConvParams p)
 {
@@ -113,8 +113,32 @@ conv_fwd_mfma_kernel(const ConvParams p)
     In a_val[A_EPT];
     In b_val[B_EPT];
 
-    auto load_a = [&](int kc0) {
-        const int kap = kc0 + a_seg * A_EPT;        // wave-uniform
+    // Reduction order.  Flat: chunk ch = kappa in [ch*TK, ch*TK + TK), kappa
+    // = (c, r, s) in KCRS order, decoded per element.  Tap: chunk ch = TK
+    // consecutive channels at one filter tap, ch = channel_block * R*S + tap;
+    // one bounds check per chunk and a plain channel stride per element.
+    auto tap_of = [&](int ch, int& c0, int& r, int& s) {
+        uint32_t cb, rs, rr, ss;
+        p.div_rs.divmod((uint32_t)ch, cb, rs);
+        p.div_s.divmod(rs, rr, ss);
+        c0 = (int)cb * TK;
+        r = (int)rr;
+        s = (int)ss;
+    };
+
+    auto load_a = [&](int ch) {
+        if constexpr (TAP) {
+            int c0, r, s;
+            tap_of(ch, c0, r, s);
+            c0 += a_seg * A_EPT;                     // wave-uniform
+            const bool tap_ok = ((unsigned)(hb + r) < (unsigned)p.H) && ((unsigned)(wb + s) < (unsigned)p.W);
+            const In* src = x + (abase + c0 * p.sxc + r * p.sxh + s * p.sxw);
+#pragma unroll
+            for (int j = 0; j < A_EPT; ++j)
+                a_val[j] = (tap_ok && c0 + j < p.C) ? load_elem(src + j * p.sxc) : In(0);
+            return;
+        }
+        const int kap = ch * TK + a_seg * A_EPT;    // wave-uniform
         uint32_t c, rs, r, s;
         p.div_rs.divmod((uint32_t)kap, c, rs);
         p.div_s.divmod(rs, r, s);
@@ -132,8 +156,19 @@ conv_fwd_mfma_kernel(const ConvParams p)
         }
     };
 
-    auto load_b = [&](int kc0) {
-        const int kap = kc0 + b_seg * B_EPT;
+    auto load_b = [&](int ch) {
+        if constexpr (TAP) {
+            int c0, r, s;
+            tap_of(ch, c0, r, s);
+            c0 += b_seg * B_EPT;
+            const In* src = wrow + (c0 * p.R + r) * p.S + s;
+            const int rs = p.R * p.S;
+#pragma unroll
+            for (int j = 0; j < B_EPT; ++j)
+                b_val[j] = (b_ok && c0 + j < p.C) ? load_elem(src + j * rs) : In(0);
+            return;
+        }
+        const int kap = ch * TK + b_seg * B_EPT;
         if constexpr (BVEC) {
             // the host guarantees Kred % (16 / sizeof(In)) == 0 and a 16-byte aligned w
             constexpr int VE = 16 / (int)sizeof(In);
@@ -176,7 +211,7 @@ conv_fwd_mfma_kernel(const ConvParams p)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = AccV{};
 
-    const int nchunks = (p.Kred + TK - 1) / TK;
+    const int nchunks = TAP ? (p.C + TK - 1) / TK * p.R * p.S : (p.Kred + TK - 1) / TK;
 
     load_a(0);
     load_b(0);
@@ -187,8 +222,8 @@ conv_fwd_mfma_kernel(const ConvParams p)
         const int cur = ch & 1;
         const bool more = ch + 1 < nchunks;
         if (more) {
-            load_a((ch + 1) * TK);
-            load_b((ch + 1) * TK);
+            load_a(ch + 1);
+            load_b(ch + 1);
         }
         const unsigned char* a_src = smem + cur * BUF_BYTES;
         const unsigned char* b_src = a_src + A_BYTES;
@@ -229,7 +264,7 @@ conv_fwd_mfma_kernel(const ConvParams p)
 // ------------------------------------------------------------------ instances and launch
 
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int TK>
-static hipError_t launch_variant(const ConvParams& p0, bool bvec, hipStream_t stream)
+static hipError_t launch_variant(const ConvParams& p0, bool bvec, bool tap, hipStream_t stream)
 {
     ConvParams p = p0;
     p.m_tiles = (p.M + TM - 1) / TM;
@@ -239,11 +274,14 @@ static hipError_t launch_variant(const ConvParams& p0, bool bvec, hipStream_t st
     constexpr int B_EPT = TK * TN / 256;
     constexpr bool CAN_VEC = (B_EPT * (int)sizeof(typename Pol::In)) % 16 == 0;
     if constexpr (!CAN_VEC) bvec = false;
-    if (bvec)
-        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, CAN_VEC>),
+    if (tap)
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, true>),
+                           grid, dim3(256), 0, stream, p);
+    else if (bvec)
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, CAN_VEC, false>),
                            grid, dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false>),
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, false>),
                            grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
@@ -261,11 +299,11 @@ static hipError_t launch_variant(const ConvParams& p0, bool bvec, hipStream_t st
     X(MFMA_BF16_128x64, PolBF16, 128, 64, 2, 2, 32)          \
     X(MFMA_BF16_256x32, PolBF16, 256, 32, 4, 1, 32)
 
-hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, hipStream_t stream)
+hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, bool tap, hipStream_t stream)
 {
     switch (v) {
 #define X(name, pol, tm, tn, wmm, wnn, tk) \
-    case Variant::name: return launch_variant<pol, tm, tn, wmm, wnn, tk>(p, bvec, stream);
+    case Variant::name: return launch_variant<pol, tm, tn, wmm, wnn, tk>(p, bvec, tap, stream);
         MICONV_VARIANTS(X)
 #undef X
     default: return hipErrorInvalidValue;

@@ -32,6 +32,9 @@ VARIANTS = {
             "halo_f64_3x3_128x128", "halo_f64_3x3_64x64"],
     "bf16": ["direct", "mfma_bf16_128x128", "mfma_bf16_128x64", "mfma_bf16_256x32"],
 }
+# the gather variants also run with the reduction in channel blocks per filter tap
+for _dt in VARIANTS:
+    VARIANTS[_dt] += [v + "_tap" for v in VARIANTS[_dt] if v.startswith("mfma_")]
 # halo variants only take the shapes they were built for (the library answers
 # NOT_SUPPORTED otherwise); every one of them must run on at least one shape
 _ran = set()
