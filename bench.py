@@ -1,12 +1,13 @@
 """Benchmark: effective convolution TFLOP/s on one MI355X.
 
-Workload: the AlexNet-style fp32 NCHW stack at batch 128 (conv2: 96->256,
-27x27, 5x5/s1/pad2; conv3: 256->384, conv4: 384->384, conv5: 384->256, all
-13x13, 3x3/s1/pad1), synthetic seeded inputs (uniform[-1,1] data,
-He-normal weights).  One step = the four layers' forward passes, each one
-kernel launch of libmiconv through the C ABI.
+Default workload: the AlexNet-style fp32 NCHW stack at batch 128 (conv2:
+96->256, 27x27, 5x5/s1/pad2; conv3: 256->384, conv4: 384->384, conv5:
+384->256, all 13x13, 3x3/s1/pad1), synthetic seeded inputs (uniform[-1,1]
+data, He-normal weights).  One step = the workload's forward passes, each
+one kernel launch of libmiconv through the C ABI.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                    [--workload alexnet|overfeat|speech|tiny|prec_f64|prec_bf16]
 
 Prints one JSON line.  ``value`` = 2*N*K*C*R*S*P*Q summed over the step's
 layers / mean step time (inputs resident in HBM, no host traffic inside
@@ -22,13 +23,13 @@ import os
 import sys
 import time
 
-import numpy as np
-
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-FP32_MFMA_PEAK_TFLOPS = 157.3      # MI355X dense fp32 matrix peak (256 CU x 256 FLOP/clk x 2.4 GHz)
+# MI355X dense MFMA peaks (256 CU x 2.4 GHz): fp32 256, fp64 128, bf16 4096 FLOP/clk/CU
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "bf16": 2516.6}
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_alexnet_fp32.md")
+WORKLOADS = ("alexnet", "overfeat", "speech", "tiny", "prec_f64", "prec_bf16")
 
 
 def parse():
@@ -36,6 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="alexnet", choices=WORKLOADS)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -43,6 +45,23 @@ def parse():
                     help="before the steps, run one plain device copy of this many MiB "
                          "(a known-size kernel to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
+
+
+def workload_layers(name):
+    from gen import workloads
+    if name == "alexnet":
+        return workloads.ALEXNET, "alexnet_conv2-5_fp32_nchw_n128"
+    if name == "overfeat":
+        return workloads.OVERFEAT, "overfeat_l1-5_fp32_nchw_n128"
+    if name == "speech":
+        return workloads.SPEECH, "speech_l1-2_fp32_nchw_n32"
+    if name == "tiny":
+        return workloads.TINY, "tiny_fp32_nchw_n2"
+    if name == "prec_f64":
+        return [l for l in workloads.PRECISION if l.dtype == "f64"], \
+            "alexnet_conv3-5_fp64_nchw+nhwc_pitch16_n64"
+    return [l for l in workloads.PRECISION if l.dtype == "bf16"], \
+        "alexnet_conv3-5_bf16in_fp32acc_nchw+nhwc_pitch16_n64"
 
 
 def source_hash():
@@ -76,6 +95,19 @@ def stored_traffic(kernel):
         return None
 
 
+def upload(a64, dtype, layout, row_pitch, dev):
+    """Logical N,C,H,W float64 data -> device tensor in the layer's storage layout."""
+    import torch
+    from gen import workloads
+    tdt = {"f32": torch.float32, "f64": torch.float64, "bf16": torch.bfloat16}[dtype]
+    N, C, H, W = a64.shape
+    st = workloads.padded_strides(N, C, H, W, layout, row_pitch)
+    base = torch.zeros(workloads.storage_elems(N, C, H, W, st), dtype=tdt, device=dev)
+    t = base.as_strided(a64.shape, st)
+    t.copy_(torch.from_numpy(a64).to(tdt))
+    return t
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -90,15 +122,26 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
-    layers = workloads.ALEXNET
+    layers, wl_name = workload_layers(args.workload)
+    dtype = layers[0].dtype
+    peak = MFMA_PEAK_TFLOPS[dtype]
+    out_dt = torch.float64 if dtype == "f64" else torch.float32
     plans = []
+    cache = {}
     for lay in layers:
-        x = gen.round_to(gen.draw(lay.x_dist, gen.derive_seed(lay.config, lay.layer, 0), lay.x_shape), "f32")
-        w = gen.round_to(gen.draw(lay.w_dist, gen.derive_seed(lay.config, lay.layer, 1), lay.w_shape), "f32")
-        xt = torch.from_numpy(x).float().to(dev)
-        wt = torch.from_numpy(w).float().to(dev)
+        key = (lay.config, lay.layer)
+        if key not in cache:       # precision variants share their logical values
+            cache.clear()
+            x = gen.round_to(gen.draw(lay.x_dist, gen.derive_seed(lay.config, lay.layer, 0), lay.x_shape), dtype)
+            w = gen.round_to(gen.draw(lay.w_dist, gen.derive_seed(lay.config, lay.layer, 1), lay.w_shape), dtype)
+            cache[key] = (x, w)
+        x, w = cache[key]
+        xt = upload(x, dtype, lay.layout, lay.row_pitch, dev)
+        wt = torch.from_numpy(w).to(xt.dtype).to(dev)
         N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
-        yt = torch.empty((N, K, P, Q), dtype=torch.float32, device=dev)
+        yst = workloads.padded_strides(N, K, P, Q, lay.layout, lay.row_pitch)
+        yt = torch.zeros(workloads.storage_elems(N, K, P, Q, yst), dtype=out_dt,
+                         device=dev).as_strided((N, K, P, Q), yst)
         plans.append((lay, mic.ConvPlan(xt, wt, yt, lay.stride, lay.padding), (x, w)))
     stream = torch.cuda.current_stream(dev)
     flops_step = sum(p.flops for _, p, _ in plans)
@@ -142,7 +185,7 @@ def main():
         tf = plan.flops / (ms * 1e-3) / 1e12
         per_layer.append({"layer": lay.name, "kernel": plan.kernel_name(), "us": round(ms * 1e3, 2),
                           "gflop": round(plan.flops / 1e9, 3), "tflops": round(tf, 2),
-                          "pct_fp32_mfma_peak": round(100 * tf / FP32_MFMA_PEAK_TFLOPS, 1)})
+                          "pct_mfma_peak": round(100 * tf / peak, 1)})
 
     # dominant kernel: most time per step, launches grouped by kernel variant
     groups = {}
@@ -154,9 +197,9 @@ def main():
     dom = max(groups, key=lambda k: groups[k]["us"])
     g = groups[dom]
     achieved = (g["flops"] / g["launches"]) / (g["us"] / g["launches"] * 1e-6) / 1e12
-    traffic = stored_traffic(dom)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
+    traffic = stored_traffic(dom) if args.workload == "alexnet" else None
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "kernel": dom, "launches_per_step": g["launches"],
                 "avg_us": round(g["us"] / g["launches"], 2)}
 
@@ -175,11 +218,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded uniform[-1,1] inputs, He-normal weights)",
-        "config": {"workload": "alexnet_conv2-5_fp32_nchw_n128", "global_batch": 128,
+        "dtype": dtype,
+        "data": "synthetic (seeded inputs with the workload's value distributions)",
+        "config": {"workload": wl_name, "global_batch": layers[0].N,
                    "layers": [l.name for l in layers], "gflop_per_step": round(flops_step / 1e9, 3),
-                   "pct_fp32_mfma_peak": round(100 * value / FP32_MFMA_PEAK_TFLOPS, 1)},
+                   "pct_mfma_peak": round(100 * value / peak, 1)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "layers": per_layer,
@@ -198,18 +241,24 @@ def cpu_baseline(plans, target_s):
     t0 = time.perf_counter()
     oracle.conv2d_fprop(x[:1], w, lay.stride, lay.padding)
     t1 = time.perf_counter() - t0
-    per_image = t1 * sum(p.flops for _, p, _ in plans) / plans[0][1].flops
-    n_img = int(max(1, min(lay.N, target_s / max(per_image, 1e-9))))
+    per_image = t1 * sum(p.flops / l.N for l, p, _ in plans) / (plan.flops / lay.N)
+    n_max = min(l.N for l, _, _ in plans)
+    n_img = int(max(1, min(n_max, target_s / max(per_image, 1e-9))))
     flops = 0.0
+    done = set()
     t0 = time.perf_counter()
     for lay, plan, (x, w) in plans:
+        key = (lay.config, lay.layer)
+        if key in done:            # one oracle run per logical layer (layouts share values)
+            continue
+        done.add(key)
         oracle.conv2d_fprop(x[:n_img], w, lay.stride, lay.padding)
         flops += plan.flops * n_img / lay.N
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": "first %d of 128 images of each of the 4 layers (%.1f GFLOP, %.1f s, fp64 "
-                      "7-loop with the error bound)" % (n_img, flops / 1e9, dt)}
+            "sample": "first %d of %d images of each of the %d layers (%.1f GFLOP, %.1f s, fp64 "
+                      "7-loop with the error bound)" % (n_img, n_max, len(done), flops / 1e9, dt)}
 
 
 if __name__ == "__main__":
