@@ -326,7 +326,7 @@ hipError_t launch_halo(Variant v, const ConvParams& p, hipStream_t stream)
     case Variant::name: return launch_halo_variant<pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks>(p, stream);
         MICONV_HALO_VARIANTS(X)
 #undef X
-    default: return hipErrorInvalidValue;
+    default: return launch_halo_bf16(v, p, stream);
     }
 }
 

@@ -1,0 +1,332 @@
+// conv_fwd_halo_bf16.hip -- bf16 convolution forward pass (fp32 accumulate,
+// fp32 output) as a batch-reduce GEMM over the R x S filter taps.
+//
+// The tap-batched scheme of conv_fwd_halo.hip, laid out for the
+// v_mfma_f32_32x32x16_bf16 instruction, whose lanes each supply eight
+// consecutive reduction elements.  With the reduction ordered as
+// (channel block, tap, 16 channels), eight consecutive elements are eight
+// channels at one tap, so both operands are stored channel-innermost in LDS
+// and every MFMA operand is one 16-byte LDS read:
+//
+//  * input halo: the zero-padded input rows ("slots") that the tile's output
+//    rows touch, WP pixels per slot; per pixel the chunk's 16 channels as two
+//    8-channel groups of 16 bytes, on a 48-byte pixel pitch (the odd number
+//    of 16-byte units keeps a wave's reads of consecutive pixels on distinct
+//    banks);
+//  * filter slab: per tap, per filter, the same two 8-channel groups, the
+//    group order swapped for filters with ((n >> 2) ^ (n >> 3)) odd, which
+//    spreads 8 or 16 consecutive filters over all banks without padding.
+//
+// The filter arrives in packed KCRS order, where a filter's 8 channels x R*S
+// taps form one contiguous run: a thread loads that run with 16-byte loads
+// and regroups it by tap in registers (byte permutes) before its LDS stores,
+// so no separate transpose pass or buffer exists.  Input halo pixels come in
+// as eight 2-byte loads per 8-channel group, or as one 16-byte load when the
+// channels of x are contiguous and aligned (NHWC-like layouts).
+//
+// Batch-reduce GEMM of the single-building-block page ("Proposed Method"),
+// read directly from x with no packed copy (zero-memory direct-convolution
+// page, "Proposed Method"), double-buffered through LDS (maxDNN page,
+// "Proposed Method").
+//
+// Eligibility (checked by the host): R and S equal to the instance's; C a
+// multiple of 16; W + pad_left + pad_right <= WP; every tile's slot span
+// <= SL; w 16-byte aligned.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "conv_params.h"
+#include "kernels.h"
+#include "mfma_common.h"
+#include "tile_map.h"
+
+namespace miconv {
+
+// filter n of a tile keeps group g of a tap at 16-byte unit 2n + (g ^ swz(n))
+__device__ __forceinline__ int slab_swz(int n) { return ((n >> 2) ^ (n >> 3)) & 1; }
+
+template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL, bool CVEC>
+__global__ void __launch_bounds__(256)
+conv_fwd_halo_bf16_kernel(const ConvParams p)
+{
+    using Pol = PolBF16;
+    constexpr int NT = 256;
+    constexpr int BM = 32;
+    constexpr int RS = R * S;
+    constexpr int CB = 16;                        // channels per chunk = one MFMA k-step per tap
+    constexpr int WM = TM / WAVES_M;
+    constexpr int WN = TN / WAVES_N;
+    constexpr int FM = WM / BM;
+    constexpr int FN = WN / BM;
+    constexpr int PIX = 48;                       // bytes per halo pixel: two 16-byte groups + pad
+    constexpr int HALO_BYTES = SL * WP * PIX;
+    constexpr int HU = 2 * SL * WP;               // halo units (8-channel group, pixel) per chunk
+    constexpr int HUT = (HU + NT - 1) / NT;       // per thread
+    constexpr int TAP_BYTES = TN * 32;            // one tap of the slab: TN filters x 16 channels
+    constexpr int SLAB_BYTES = RS * TAP_BYTES;
+    constexpr int SU = 2 * TN;                    // slab units (filter, 8-channel group) per chunk
+    constexpr int SUT = (SU + NT - 1) / NT;
+    constexpr int NV = RS;                        // 16-byte vectors per slab unit: 8 channels x RS taps
+    constexpr int BUF_BYTES = HALO_BYTES + SLAB_BYTES;
+    static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
+    static_assert(BUF_BYTES % 16 == 0, "16-byte aligned buffers");
+    static_assert(4 * BM * (BM + 1) * 4 <= 2 * BUF_BYTES, "epilogue stage fits");
+    static_assert(((R - 1) * WP + S - 1) * PIX + 16 < 65536 && (RS - 1) * TAP_BYTES < 65536,
+                  "LDS immediate offsets");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int mt = tile / p.n_tiles;
+    const int nt = tile - mt * p.n_tiles;
+    const int m0 = mt * p.m_step;
+    const int m_end = min(m0 + p.m_step, p.M);
+    const int n0 = nt * TN;
+
+    const uint16_t* __restrict__ x = static_cast<const uint16_t*>(p.x);
+    const uint16_t* __restrict__ w = static_cast<const uint16_t*>(p.w);
+
+    auto vrow = [&](int m) {
+        uint32_t n, pq, pp, q;
+        p.div_pq.divmod((uint32_t)m, n, pq);
+        p.div_q.divmod(pq, pp, q);
+        return (int)n * p.Hp + (int)pp * p.u;
+    };
+    const int vr_first = vrow(m0);
+    const int nslots = vrow(m_end - 1) + R - vr_first;   // <= SL (host-checked)
+
+    // ---- halo loader: unit e = (group g, pixel), pixel fastest along the lanes
+    int h_off[HUT];
+    uint32_t h_ok = 0;
+#pragma unroll
+    for (int i = 0; i < HUT; ++i) {
+        const int e = tid + NT * i;
+        const int pix = e % (SL * WP);
+        const int g = e / (SL * WP);
+        const int col = pix % WP;
+        const int slot = pix / WP;
+        uint32_t n, hp;
+        p.div_hp.divmod((uint32_t)(vr_first + slot), n, hp);
+        const int h = (int)hp - p.pad_top;
+        const int wcol = col - p.pad_left;
+        const bool ok = e < HU && slot < nslots && (int)n < p.N && h >= 0 && h < p.H && wcol >= 0 &&
+                        wcol < p.W;
+        h_off[i] = ok ? (int)n * p.sxn + 8 * g * p.sxc + h * p.sxh + wcol * p.sxw : 0;
+        h_ok |= (ok ? 1u : 0u) << i;
+    }
+
+    // ---- slab loader: unit e = (filter row, 8-channel group)
+    int s_off[SUT];
+    uint32_t s_ok = 0;
+#pragma unroll
+    for (int i = 0; i < SUT; ++i) {
+        const int e = tid + NT * i;
+        const int row = e >> 1;
+        const int g = e & 1;
+        const bool ok = e < SU && n0 + row < p.K;
+        s_off[i] = ok ? (n0 + row) * p.Kred + 8 * g * RS : 0;
+        s_ok |= (ok ? 1u : 0u) << i;
+    }
+
+    // registers of the chunk in flight
+    uint32_t h_raw[CVEC ? 1 : HUT][8];
+    u32x4 h_vec[CVEC ? HUT : 1];
+    u32x4 s_val[SUT][NV];
+
+    // Loads are unconditional (a unit outside the input or past K reads the
+    // chunk's first element of x or w instead, which exists) and their
+    // values are replaced by zeros afterwards, so no load sits in a branch.
+    auto load_chunk = [&](int c0) {
+        const int xo = c0 * p.sxc;
+#pragma unroll
+        for (int i = 0; i < HUT; ++i) {
+            if constexpr (CVEC) {
+                h_vec[i] = *reinterpret_cast<const u32x4*>(x + h_off[i] + xo);
+            } else {
+                const uint16_t* src = x + h_off[i] + xo;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) h_raw[i][j] = src[j * p.sxc];
+            }
+        }
+        const int wo = c0 * RS;
+#pragma unroll
+        for (int i = 0; i < SUT; ++i) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(w + s_off[i] + wo);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) s_val[i][v] = src[v];
+        }
+    };
+
+    auto store_chunk = [&](int buf) {
+        unsigned char* hb = smem + buf * BUF_BYTES;
+#pragma unroll
+        for (int i = 0; i < HUT; ++i) {
+            const int e = tid + NT * i;
+            if (HU % NT == 0 || e < HU) {
+                const int pix = e % (SL * WP);
+                const int g = e / (SL * WP);
+                const bool ok = (h_ok >> i) & 1;
+                u32x4 val;
+                if constexpr (CVEC) {
+                    val = h_vec[i];
+                } else {
+                    // the empty asm keeps the packing here, after the compute it
+                    // overlaps; hoisted next to the loads it would wait for them
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(h_raw[i][j]));
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) val[d] = h_raw[i][2 * d] | (h_raw[i][2 * d + 1] << 16);
+                }
+#pragma unroll
+                for (int d = 0; d < 4; ++d) val[d] = ok ? val[d] : 0u;
+                *reinterpret_cast<u32x4*>(hb + pix * PIX + 16 * g) = val;
+            }
+        }
+        unsigned char* sb = hb + HALO_BYTES;
+#pragma unroll
+        for (int i = 0; i < SUT; ++i) {
+            const int e = tid + NT * i;
+            if (SU % NT == 0 || e < SU) {
+                const int row = e >> 1;
+                const int g = e & 1;
+                const bool ok = (s_ok >> i) & 1;
+                unsigned char* dst = sb + 16 * (2 * row + (g ^ slab_swz(row)));
+                // element k of the unit's run is channel k / RS at tap k % RS:
+                // dword d of tap t holds channels 2d and 2d+1 of that tap
+                const uint32_t* words = reinterpret_cast<const uint32_t*>(&s_val[i][0]);
+#pragma unroll
+                for (int t = 0; t < RS; ++t) {
+                    u32x4 out;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const int klo = (2 * d) * RS + t;
+                        const int khi = (2 * d + 1) * RS + t;
+                        const uint32_t wlo = words[klo >> 1];
+                        const uint32_t whi = words[khi >> 1];
+                        const uint32_t lo = (klo & 1) ? (wlo >> 16) : (wlo & 0xffffu);
+                        const uint32_t hi = (khi & 1) ? (whi & 0xffff0000u) : (whi << 16);
+                        out[d] = ok ? (lo | hi) : 0u;
+                    }
+                    *reinterpret_cast<u32x4*>(dst + t * TAP_BYTES) = out;
+                }
+            }
+        }
+    };
+
+    // ---- per-wave MFMA geometry
+    const int wm = wave / WAVES_N;
+    const int wn = wave % WAVES_N;
+    const int lrow = lane & 31;
+    const int lgrp = lane >> 5;
+    int a_base[FM];                      // byte offset of tap (0,0), channel group lgrp, per block
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WM + i * BM + lrow;
+        int pix = 0;
+        if (m < m_end) {
+            uint32_t n, pq, pp, q;
+            p.div_pq.divmod((uint32_t)m, n, pq);
+            p.div_q.divmod(pq, pp, q);
+            pix = ((int)n * p.Hp + (int)pp * p.u - vr_first) * WP + (int)q * p.v;
+        }
+        a_base[i] = pix * PIX + 16 * lgrp;
+    }
+    int b_base[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int n = wn * WN + j * BM + lrow;
+        b_base[j] = HALO_BYTES + 16 * (2 * n + (lgrp ^ slab_swz(n)));
+    }
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    // one MFMA k-step per tap; halfway through, the next chunk (already in
+    // registers) goes to the other buffer, whose last readers finished
+    // before the previous barrier
+    auto compute = [&](int cur, bool park) {
+        const unsigned char* buf = smem + cur * BUF_BYTES;
+#pragma unroll
+        for (int t = 0; t < RS; ++t) {
+            const int aoff = ((t / S) * WP + (t % S)) * PIX;
+            bf16x8 a[FM], b[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + a_base[i] + aoff));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                b[j] = __builtin_bit_cast(bf16x8,
+                                          *reinterpret_cast<const u32x4*>(buf + b_base[j] + t * TAP_BYTES));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            if (t == RS / 2 && park) store_chunk(cur ^ 1);
+        }
+    };
+
+    const int nblocks = p.C / CB;
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    for (int it = 0; it < nblocks; ++it) {
+        const int cur = it & 1;
+        const bool more = it + 1 < nblocks;
+        if (more) load_chunk((it + 1) * CB);
+        compute(cur, more);
+        __syncthreads();
+    }
+
+    store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, m_end, wave, lane);
+}
+
+// ------------------------------------------------------------------ instances and launch
+
+template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL>
+static hipError_t launch_halo_bf16_variant(const ConvParams& p0, hipStream_t stream)
+{
+    ConvParams p = p0;
+    if (p.m_step <= 0 || p.m_step > TM) p.m_step = TM;   // the host sets P*Q for image tiles
+    p.m_tiles = (p.M + p.m_step - 1) / p.m_step;
+    p.n_tiles = (p.K + TN - 1) / TN;
+    const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
+    // 16-byte input loads when the 8 channels of a group are contiguous and
+    // every group starts on a 16-byte boundary
+    const bool cvec = p.sxc == 1 && (uintptr_t)p.x % 16 == 0 && p.sxn % 8 == 0 && p.sxh % 8 == 0 &&
+                      p.sxw % 8 == 0;
+    if (cvec)
+        hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, true>), grid,
+                           dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, false>), grid,
+                           dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+//        name                     TM   TN  waves  R  S  WP  SL
+#define MICONV_HALO_BF16_VARIANTS(X)                      \
+    X(HALO_BF16_3x3_128x128, 128, 128, 2, 2, 3, 3, 16, 16) \
+    X(HALO_BF16_3x3_128x64, 128, 64, 2, 2, 3, 3, 16, 16)   \
+    X(HALO_BF16_3x3_192x128, 192, 128, 2, 2, 3, 3, 16, 16)
+
+hipError_t launch_halo_bf16(Variant v, const ConvParams& p, hipStream_t stream)
+{
+    switch (v) {
+#define X(name, tm, tn, wmm, wnn, r, s, wp, sl) \
+    case Variant::name: return launch_halo_bf16_variant<tm, tn, wmm, wnn, r, s, wp, sl>(p, stream);
+        MICONV_HALO_BF16_VARIANTS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace miconv

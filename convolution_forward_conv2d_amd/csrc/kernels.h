@@ -31,6 +31,9 @@ enum class Variant : int {
     HALO_F32_3x3_128x128_KS2,
     HALO_F64_3x3_128x128,
     HALO_F64_3x3_64x64,
+    HALO_BF16_3x3_128x128,  // bf16 halo kernel, channel-innermost LDS (conv_fwd_halo_bf16.hip)
+    HALO_BF16_3x3_128x64,
+    HALO_BF16_3x3_192x128,
     COUNT
 };
 
@@ -43,6 +46,7 @@ hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, bool tap, hipS
 
 // Launch a tap-batched halo variant (the host has checked its eligibility).
 hipError_t launch_halo(Variant v, const ConvParams& p, hipStream_t stream);
+hipError_t launch_halo_bf16(Variant v, const ConvParams& p, hipStream_t stream);
 
 // Launch the plain direct kernel (one thread per output element).
 hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);

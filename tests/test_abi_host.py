@@ -138,7 +138,8 @@ def test_kernel_choice_host_only():
     assert names["overfeat_l2"].startswith("halo_f32_5x5_")
     assert names["overfeat_l1"].startswith("mfma_f32_")
     assert names["prec_conv3_f64_nchw"].startswith("halo_f64_3x3_")
-    assert names["prec_conv3_bf16_nhwc"].startswith("mfma_bf16_")
+    assert names["prec_conv3_bf16_nhwc"].startswith("halo_bf16_3x3_")
+    assert names["prec_conv5_bf16_nchw"].startswith("halo_bf16_3x3_")
 
 
 def test_dtype_combinations_and_shape_mismatch():

@@ -30,7 +30,8 @@ VARIANTS = {
             "halo_f32x16_3x3_144x128", "halo_f32x16_3x3_176x128_ks2", "halo_f32_3x3_128x128_ks2"],
     "f64": ["direct", "mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64",
             "halo_f64_3x3_128x128", "halo_f64_3x3_64x64"],
-    "bf16": ["direct", "mfma_bf16_128x128", "mfma_bf16_128x64", "mfma_bf16_256x32"],
+    "bf16": ["direct", "mfma_bf16_128x128", "mfma_bf16_128x64", "mfma_bf16_256x32",
+             "halo_bf16_3x3_128x128", "halo_bf16_3x3_128x64", "halo_bf16_3x3_192x128"],
 }
 # the gather variants also run with the reduction in channel blocks per filter tap
 for _dt in VARIANTS:
@@ -70,6 +71,13 @@ SMALL_SHAPES = [
     dict(name="halo3_c4", N=1, C=4, Hh=13, Ww=13, K=16, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
     # 5x5 / pad 2 on 20x20
     dict(name="halo5", N=2, C=8, Hh=20, Ww=20, K=70, R=5, S=5, stride=(1, 1), pads=(2, 2, 2, 2)),
+    # whole 16-channel blocks (bf16 halo kernel): three blocks, ragged m and K tiles
+    dict(name="halo3_c48", N=3, C=48, Hh=13, Ww=13, K=100, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
+    # channels-last with a padded row pitch: 16-byte channel loads of x
+    dict(name="halo3_nhwc_pitch", N=2, C=32, Hh=13, Ww=13, K=72, R=3, S=3, stride=(1, 1),
+         pads=(1, 1, 1, 1), layout="nhwc", pitch=16),
+    # one 16-channel block, stride 2, asymmetric padding, non-square input
+    dict(name="halo3_c16_s2", N=2, C=16, Hh=14, Ww=12, K=40, R=3, S=3, stride=(2, 2), pads=(1, 0, 1, 1)),
 ]
 
 
