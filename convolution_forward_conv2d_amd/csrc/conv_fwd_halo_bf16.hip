@@ -34,6 +34,8 @@
 // <= SL; w 16-byte aligned.
 #include <stdint.h>
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include "conv_params.h"
@@ -138,34 +140,34 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
     u32x4 h_vec[CVEC ? HUT : 1];
     u32x4 s_val[SUT][NV];
 
+    // A chunk moves global -> registers -> LDS in pieces: load piece q is
+    // one global load (a 2-byte channel value or a 16-byte vector), store
+    // piece q one 16-byte LDS write (a halo unit, or one tap of a slab unit).
+    constexpr int NLH = CVEC ? HUT : 8 * HUT;    // halo load pieces
+    constexpr int NL = NLH + SUT * NV;           // load pieces per chunk
+    constexpr int NS = HUT + SUT * RS;           // store pieces per chunk
+
     // Loads are unconditional (a unit outside the input or past K reads the
     // chunk's first element of x or w instead, which exists) and their
-    // values are replaced by zeros afterwards, so no load sits in a branch.
-    auto load_chunk = [&](int c0) {
-        const int xo = c0 * p.sxc;
-#pragma unroll
-        for (int i = 0; i < HUT; ++i) {
+    // values are replaced by zeros at the store, so no load sits in a branch.
+    auto load_piece = [&](int q, int c0) {
+        if (q < NLH) {
             if constexpr (CVEC) {
-                h_vec[i] = *reinterpret_cast<const u32x4*>(x + h_off[i] + xo);
+                h_vec[q] = *reinterpret_cast<const u32x4*>(x + h_off[q] + c0);
             } else {
-                const uint16_t* src = x + h_off[i] + xo;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) h_raw[i][j] = src[j * p.sxc];
+                const int i = q / 8, j = q % 8;
+                h_raw[i][j] = x[h_off[i] + (c0 + j) * p.sxc];
             }
-        }
-        const int wo = c0 * RS;
-#pragma unroll
-        for (int i = 0; i < SUT; ++i) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(w + s_off[i] + wo);
-#pragma unroll
-            for (int v = 0; v < NV; ++v) s_val[i][v] = src[v];
+        } else {
+            const int i = (q - NLH) / NV, v = (q - NLH) % NV;
+            s_val[i][v] = *reinterpret_cast<const u32x4*>(w + s_off[i] + c0 * RS + 8 * v);
         }
     };
 
-    auto store_chunk = [&](int buf) {
+    auto store_piece = [&](int q, int buf) {
         unsigned char* hb = smem + buf * BUF_BYTES;
-#pragma unroll
-        for (int i = 0; i < HUT; ++i) {
+        if (q < HUT) {
+            const int i = q;
             const int e = tid + NT * i;
             if (HU % NT == 0 || e < HU) {
                 const int pix = e % (SL * WP);
@@ -175,8 +177,8 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
                 if constexpr (CVEC) {
                     val = h_vec[i];
                 } else {
-                    // the empty asm keeps the packing here, after the compute it
-                    // overlaps; hoisted next to the loads it would wait for them
+                    // the empty asm keeps the packing at this point of the
+                    // compute; hoisted next to the loads it would wait for them
 #pragma unroll
                     for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(h_raw[i][j]));
 #pragma unroll
@@ -186,34 +188,29 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
                 for (int d = 0; d < 4; ++d) val[d] = ok ? val[d] : 0u;
                 *reinterpret_cast<u32x4*>(hb + pix * PIX + 16 * g) = val;
             }
-        }
-        unsigned char* sb = hb + HALO_BYTES;
-#pragma unroll
-        for (int i = 0; i < SUT; ++i) {
+        } else {
+            const int i = (q - HUT) / RS, t = (q - HUT) % RS;
             const int e = tid + NT * i;
             if (SU % NT == 0 || e < SU) {
                 const int row = e >> 1;
                 const int g = e & 1;
                 const bool ok = (s_ok >> i) & 1;
-                unsigned char* dst = sb + 16 * (2 * row + (g ^ slab_swz(row)));
+                unsigned char* dst = hb + HALO_BYTES + 16 * (2 * row + (g ^ slab_swz(row)));
                 // element k of the unit's run is channel k / RS at tap k % RS:
                 // dword d of tap t holds channels 2d and 2d+1 of that tap
                 const uint32_t* words = reinterpret_cast<const uint32_t*>(&s_val[i][0]);
+                u32x4 out;
 #pragma unroll
-                for (int t = 0; t < RS; ++t) {
-                    u32x4 out;
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        const int klo = (2 * d) * RS + t;
-                        const int khi = (2 * d + 1) * RS + t;
-                        const uint32_t wlo = words[klo >> 1];
-                        const uint32_t whi = words[khi >> 1];
-                        const uint32_t lo = (klo & 1) ? (wlo >> 16) : (wlo & 0xffffu);
-                        const uint32_t hi = (khi & 1) ? (whi & 0xffff0000u) : (whi << 16);
-                        out[d] = ok ? (lo | hi) : 0u;
-                    }
-                    *reinterpret_cast<u32x4*>(dst + t * TAP_BYTES) = out;
+                for (int d = 0; d < 4; ++d) {
+                    const int klo = (2 * d) * RS + t;
+                    const int khi = (2 * d + 1) * RS + t;
+                    const uint32_t wlo = words[klo >> 1];
+                    const uint32_t whi = words[khi >> 1];
+                    const uint32_t lo = (klo & 1) ? (wlo >> 16) : (wlo & 0xffffu);
+                    const uint32_t hi = (khi & 1) ? (whi & 0xffff0000u) : (whi << 16);
+                    out[d] = ok ? (lo | hi) : 0u;
                 }
+                *reinterpret_cast<u32x4*>(dst + t * TAP_BYTES) = out;
             }
         }
     };
@@ -249,42 +246,73 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    // one MFMA k-step per tap; halfway through, the next chunk (already in
-    // registers) goes to the other buffer, whose last readers finished
-    // before the previous barrier
-    auto compute = [&](int cur, bool park) {
+    // One MFMA k-step per tap; the operands of step t + PFD are read from
+    // LDS during step t.  The chunk held in registers (the next one) is
+    // written to the other LDS buffer over steps 0 .. SPLIT-1 (that buffer's
+    // last readers finished before the previous barrier), then the loads of
+    // the chunk after it are issued over the remaining steps.  Each step's
+    // memory instructions stay between its MFMAs, so no step waits on a
+    // burst; one barrier ends each chunk.
+    constexpr int SPLIT = RS / 2;
+    constexpr int PFD = 1;
+    bf16x8 fa[PFD + 1][FM], fb[PFD + 1][FN];
+    auto frags = [&](const unsigned char* buf, int t, int k) {
+        const int aoff = ((t / S) * WP + (t % S)) * PIX;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            fa[k][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + a_base[i] + aoff));
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            fb[k][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + b_base[j] + t * TAP_BYTES));
+    };
+    // STORE / LOAD are compile-time so that a step is straight-line code the
+    // scheduler can interleave with the MFMAs
+    auto compute = [&](auto store_c, auto load_c, int cur, int c_load) {
+        constexpr bool STORE = decltype(store_c)::value;
+        constexpr bool LOAD = decltype(load_c)::value;
         const unsigned char* buf = smem + cur * BUF_BYTES;
 #pragma unroll
+        for (int t = 0; t < PFD; ++t) frags(buf, t, t);
+#pragma unroll
         for (int t = 0; t < RS; ++t) {
-            const int aoff = ((t / S) * WP + (t % S)) * PIX;
-            bf16x8 a[FM], b[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + a_base[i] + aoff));
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                b[j] = __builtin_bit_cast(bf16x8,
-                                          *reinterpret_cast<const u32x4*>(buf + b_base[j] + t * TAP_BYTES));
+            if (t + PFD < RS) frags(buf, t + PFD, (t + PFD) % (PFD + 1));
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-            if (t == RS / 2 && park) store_chunk(cur ^ 1);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t % (PFD + 1)][i], fb[t % (PFD + 1)][j],
+                                                                        acc[i][j], 0, 0, 0);
+            if constexpr (STORE) {
+#pragma unroll
+                for (int q = 0; q < NS; ++q)
+                    if (q * SPLIT / NS == t) store_piece(q, cur ^ 1);
+            }
+            if constexpr (LOAD) {
+#pragma unroll
+                for (int q = 0; q < NL; ++q)
+                    if (SPLIT + q * (RS - SPLIT) / NL == t) load_piece(q, c_load);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        __syncthreads();
     };
+    using yes = std::true_type;
+    using no = std::false_type;
 
     const int nblocks = p.C / CB;
-    load_chunk(0);
-    store_chunk(0);
-    __syncthreads();
-    for (int it = 0; it < nblocks; ++it) {
-        const int cur = it & 1;
-        const bool more = it + 1 < nblocks;
-        if (more) load_chunk((it + 1) * CB);
-        compute(cur, more);
-        __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NL; ++q) load_piece(q, 0);
+#pragma unroll
+    for (int q = 0; q < NS; ++q) store_piece(q, 0);
+    if (nblocks > 1) {
+#pragma unroll
+        for (int q = 0; q < NL; ++q) load_piece(q, CB);
     }
+    __syncthreads();
+    int it = 0;
+    for (; it + 2 < nblocks; ++it) compute(yes{}, yes{}, it & 1, (it + 2) * CB);
+    if (it + 1 < nblocks) compute(yes{}, no{}, (it++) & 1, 0);
+    compute(no{}, no{}, it & 1, 0);
 
     store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, m_end, wave, lane);
 }

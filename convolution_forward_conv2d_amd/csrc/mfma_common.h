@@ -155,15 +155,20 @@ template <class In> __device__ __forceinline__ In load_elem(const In* p) { retur
 // ------------------------------------------------------------------ epilogue
 //
 // y = alpha * acc + beta * y for one wave's FM x FN accumulator blocks whose
-// top-left output is (row mw0, filter nw0).  Each block goes through a
-// per-wave LDS stage so that the global stores run along y's unit-stride
-// direction: along m (NCHW-like y) or along k (NHWC-like y, syk == 1)
-// (maxDNN page, "Proposed Method": outputs reorganised in shared memory for
-// coalesced writes).  Rows at or past m_end belong to no output (tile
-// padding) and are dropped.  smem must hold 4 * BM * (BM + 1) accumulators
-// and be free (every wave past its last read of the main loop's tiles).
-// With beta == 0, y is never read.  Called by every wave of the workgroup
-// alike (it holds barriers); waves with active == false only keep step.
+// top-left output is (row mw0, filter nw0), with the global stores running
+// along y's unit-stride direction (maxDNN page, "Proposed Method": outputs
+// reorganised in shared memory for coalesced writes):
+//  * along k (NHWC-like y, syk == 1): the lanes of an accumulator register
+//    already hold consecutive filters of one output row, so they store
+//    straight from registers;
+//  * otherwise along m: each block goes through a per-wave LDS stage
+//    (BM x (BM + 1) accumulators at smem + wave * BM * (BM + 1)), and a lane
+//    then stores consecutive rows of one filter.
+// Rows at or past m_end belong to no output (tile padding) and are dropped.
+// The stage is private to the wave, so no workgroup barrier is needed; the
+// caller guarantees that every wave has finished reading the main loop's
+// LDS buffers (a barrier after the loop).  With beta == 0, y is never read.
+// Waves with active == false store nothing.
 template <class Pol, int FM, int FN>
 __device__ __forceinline__ void store_acc_tile(const ConvParams& p, unsigned char* smem,
                                                typename Pol::AccV (&acc)[FM][FN],
@@ -175,41 +180,60 @@ __device__ __forceinline__ void store_acc_tile(const ConvParams& p, unsigned cha
     constexpr int BM = Pol::BM;
     constexpr int STAGE_PITCH = BM + 1;
     constexpr int LG = 64 / BM;                 // lanes sharing one staged column index
+    if (!active) return;
     const Acc alpha = (Acc)p.alpha;
     const Acc beta = (Acc)p.beta;
     Out* __restrict__ y = static_cast<Out*>(p.y);
-    Acc* stage = reinterpret_cast<Acc*>(smem) + wave * BM * STAGE_PITCH;
-    const bool k_fast = (p.syk == 1);
 
+    auto row_offset = [&](int gm) {
+        uint32_t n, pq, pp, q;
+        p.div_pq.divmod((uint32_t)gm, n, pq);
+        p.div_q.divmod(pq, pp, q);
+        return (int)n * p.syn + (int)pp * p.syp + (int)q * p.syq;
+    };
+    auto put = [&](int off, Acc v) {
+        Acc val = alpha * v;
+        if (beta != Acc(0)) val += beta * (Acc)y[off];
+        y[off] = (Out)val;
+    };
+
+    if (p.syk == 1) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int e = 0; e < Pol::NACC; ++e) {
+                const int gm = mw0 + i * BM + Pol::row(e, lane);
+                if (gm >= m_end) continue;
+                const int moff = row_offset(gm);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int gk = nw0 + j * BM + Pol::col(e, lane);
+                    if (gk < p.K) put(moff + gk, acc[i][j][e]);
+                }
+            }
+        }
+        return;
+    }
+
+    Acc* stage = reinterpret_cast<Acc*>(smem) + wave * BM * STAGE_PITCH;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        // a lane stores rows ml = lane % BM of the block, for LG-strided filters
+        const int gm = mw0 + i * BM + lane % BM;
+        const bool row_ok = gm < m_end;
+        const int moff = row_ok ? row_offset(gm) : 0;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            if (active) {
 #pragma unroll
-                for (int e = 0; e < Pol::NACC; ++e)
-                    stage[Pol::col(e, lane) * STAGE_PITCH + Pol::row(e, lane)] = acc[i][j][e];
-            }
-            __syncthreads();
-            const int bm0 = mw0 + i * BM;
+            for (int e = 0; e < Pol::NACC; ++e)
+                stage[Pol::col(e, lane) * STAGE_PITCH + Pol::row(e, lane)] = acc[i][j][e];
             const int bk0 = nw0 + j * BM;
 #pragma unroll
             for (int t = 0; t < BM / LG; ++t) {
-                const int ml = k_fast ? (lane / BM + LG * t) : (lane % BM);
-                const int kl = k_fast ? (lane % BM) : (lane / BM + LG * t);
-                const int gm = bm0 + ml;
+                const int kl = lane / BM + LG * t;
                 const int gk = bk0 + kl;
-                if (active && gm < m_end && gk < p.K) {
-                    uint32_t n, pq, pp, q;
-                    p.div_pq.divmod((uint32_t)gm, n, pq);
-                    p.div_q.divmod(pq, pp, q);
-                    const int off = (int)n * p.syn + gk * p.syk + (int)pp * p.syp + (int)q * p.syq;
-                    Acc val = alpha * stage[kl * STAGE_PITCH + ml];
-                    if (beta != Acc(0)) val += beta * (Acc)y[off];
-                    y[off] = (Out)val;
-                }
+                if (row_ok && gk < p.K) put(moff + gk * p.syk, stage[kl * STAGE_PITCH + lane % BM]);
             }
-            __syncthreads();
         }
     }
 }
