@@ -1,4 +1,5 @@
-"""CPU oracle for the 2-D convolution forward pass (fp64, plain 7-nested loop).
+"""CPU oracle for the 2-D convolution forward pass and its data gradient (fp64,
+plain 7-nested loops).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
@@ -64,6 +65,12 @@ def _load():
         lib.oracle_conv2d_fprop_at.argtypes = [pp, dp, dp, ctypes.c_double, ctypes.c_double,
                                                dp, ip, ctypes.c_int64, dp, dp, ctypes.c_int]
         lib.oracle_conv2d_fprop_at.restype = ctypes.c_int
+        lib.oracle_conv2d_bwd_data.argtypes = [pp, dp, ip, dp, ctypes.c_double, ctypes.c_double,
+                                               dp, dp, dp, ctypes.c_int]
+        lib.oracle_conv2d_bwd_data.restype = ctypes.c_int
+        lib.oracle_conv2d_bwd_data_at.argtypes = [pp, dp, ip, dp, ctypes.c_double, ctypes.c_double,
+                                                  dp, ip, ctypes.c_int64, dp, dp, ctypes.c_int]
+        lib.oracle_conv2d_bwd_data_at.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
@@ -168,3 +175,65 @@ def conv2d_fprop_at(x, w, idx, stride=(1, 1), padding=(0, 0, 0, 0), alpha=1.0, b
     if rc != 0:
         raise ValueError("oracle rejected the problem or a coordinate")
     return y, bound
+
+
+def _dgrad_problem(dy, w, x_shape, stride, padding):
+    db, ds = _input_view(dy)
+    wc = np.ascontiguousarray(w, dtype=np.float64)
+    N, C, H, W = x_shape
+    # the forward problem of the same geometry; its input strides are unused
+    pb = make_problem(x_shape, (C * H * W, H * W, W, 1), wc.shape, stride, padding)
+    P, Q = output_dims(pb)
+    if tuple(dy.shape) != (N, wc.shape[0], P, Q):
+        raise ValueError("dy shape %s != forward output shape %s" % (tuple(dy.shape), (N, wc.shape[0], P, Q)))
+    sdy = np.asarray(ds, dtype=np.int64)
+    return pb, db, sdy, wc
+
+
+def conv2d_bwd_data(dy, w, x_shape, stride=(1, 1), padding=(0, 0, 0, 0), alpha=1.0, beta=0.0,
+                    dx_old=None, nthreads=0):
+    """Whole data gradient of the forward convolution with input shape x_shape.
+
+    dy: float64 (N, K, P, Q), any non-negative strides; w: float64 (K, C, R, S).
+    Returns (dx, bound), both float64 packed (N, C, H, W).
+    """
+    pb, db, sdy, wc = _dgrad_problem(dy, w, x_shape, stride, padding)
+    dx = np.empty(tuple(x_shape), dtype=np.float64)
+    bound = np.empty(tuple(x_shape), dtype=np.float64)
+    xo = None
+    if beta != 0.0:
+        if dx_old is None:
+            raise ValueError("beta != 0 needs dx_old")
+        xo = np.ascontiguousarray(dx_old, dtype=np.float64)
+        if xo.shape != dx.shape:
+            raise ValueError("dx_old shape %s != input shape %s" % (xo.shape, dx.shape))
+    rc = _load().oracle_conv2d_bwd_data(
+        ctypes.byref(pb), _dptr(db), sdy.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _dptr(wc),
+        float(alpha), float(beta), _dptr(xo), _dptr(dx), _dptr(bound), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return dx, bound
+
+
+def conv2d_bwd_data_at(dy, w, x_shape, idx, stride=(1, 1), padding=(0, 0, 0, 0), alpha=1.0,
+                       beta=0.0, dx_old_vals=None, nthreads=0):
+    """Selected data-gradient values.  idx: int64 array (count, 4) of (n, c, h, w)."""
+    pb, db, sdy, wc = _dgrad_problem(dy, w, x_shape, stride, padding)
+    ic = np.ascontiguousarray(idx, dtype=np.int64).reshape(-1, 4)
+    count = ic.shape[0]
+    dx = np.empty(count, dtype=np.float64)
+    bound = np.empty(count, dtype=np.float64)
+    xo = None
+    if beta != 0.0:
+        if dx_old_vals is None:
+            raise ValueError("beta != 0 needs dx_old_vals")
+        xo = np.ascontiguousarray(dx_old_vals, dtype=np.float64).reshape(-1)
+        if xo.shape[0] != count:
+            raise ValueError("dx_old_vals must hold one value per coordinate")
+    rc = _load().oracle_conv2d_bwd_data_at(
+        ctypes.byref(pb), _dptr(db), sdy.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _dptr(wc),
+        float(alpha), float(beta), _dptr(xo), ic.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        count, _dptr(dx), _dptr(bound), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem or a coordinate")
+    return dx, bound

@@ -1,6 +1,6 @@
 /*
  * oracle/conv_oracle.c -- plain CPU reference for the 2-D convolution forward
- * pass (FPROP).  TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and
+ * pass (FPROP) and its data gradient (backward pass with respect to x).  TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and
  * the CPU-baseline leg of the benchmark may load this library.  It shares no
  * code, header, table or helper with the GPU path.
  *
@@ -167,6 +167,125 @@ int oracle_conv2d_fprop_at(const oracle_conv_problem* pb,
         double val = alpha * acc;
         if (beta != 0.0) val += beta * y_old_vals[i];
         if (y) y[i] = val;
+        if (bound) bound[i] = bnd;
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/*
+ * Backward pass with respect to the input (data gradient).  The pages name
+ * the backward pass (cuDNN page, "Proposed Method": forward and backward
+ * routines for convolution; maxDNN page, Abstract and research question RQ4:
+ * the same techniques are expected to carry over to BPROP) but print no
+ * formula.  The plain reading taken: the gradient of the forward sum above
+ * with respect to x, i.e. its adjoint, for the same geometry:
+ *
+ *   dacc[n,c,h,w] = sum_{k<K} sum_{r<R} sum_{s<S}  dY(n, k, p, q) * F[k, c, r, s]
+ *                   over the (r, s) with  p*u = h + pad_top - r,   0 <= p < P,
+ *                                         q*v = w + pad_left - s,  0 <= q < Q
+ *   dY(n,k,p,q)   = dy[n*sdy[0] + k*sdy[1] + p*sdy[2] + q*sdy[3]]
+ *   dx[n,c,h,w]   = alpha * dacc + beta * dx_old[n,c,h,w]   (dx_old unread if beta == 0)
+ *   B[n,c,h,w]    = sum of |dY * F| over the same terms     (error-bound weight)
+ *
+ * with P, Q the forward output size of the problem (oracle_output_dims) and
+ * N, C, H, W the input (= dx) dims.  Accumulated in double in the fixed
+ * order k, r, s.
+ */
+static void one_dgrad(const oracle_conv_problem* pb, int64_t P, int64_t Q,
+                      const double* dy, const int64_t* sdy, const double* f,
+                      int64_t n, int64_t c, int64_t h, int64_t w,
+                      double* acc_out, double* bound_out)
+{
+    double acc = 0.0, bound = 0.0;
+    for (int64_t k = 0; k < pb->K; ++k) {
+        for (int64_t r = 0; r < pb->R; ++r) {
+            int64_t hh = h + pb->pad_top - r;
+            if (hh < 0 || hh % pb->u != 0 || hh / pb->u >= P) continue;
+            int64_t p = hh / pb->u;
+            for (int64_t s = 0; s < pb->S; ++s) {
+                int64_t ww = w + pb->pad_left - s;
+                if (ww < 0 || ww % pb->v != 0 || ww / pb->v >= Q) continue;
+                int64_t q = ww / pb->v;
+                double dv = dy[n * sdy[0] + k * sdy[1] + p * sdy[2] + q * sdy[3]];
+                double fv = f[((k * pb->C + c) * pb->R + r) * pb->S + s];
+                double prod = dv * fv;
+                acc += prod;
+                bound += fabs(prod);
+            }
+        }
+    }
+    *acc_out = acc;
+    *bound_out = bound;
+}
+
+/*
+ * Whole data gradient.  dx and bound (either may be NULL) are packed N,C,H,W;
+ * dx_old is packed N,C,H,W and read only when beta != 0.  dy is read through
+ * the element strides sdy[4] (n, k, p, q).  Returns 0, or -1 on a bad problem.
+ */
+int oracle_conv2d_bwd_data(const oracle_conv_problem* pb,
+                           const double* dy, const int64_t* sdy, const double* f,
+                           double alpha, double beta, const double* dx_old,
+                           double* dx, double* bound, int nthreads)
+{
+    int64_t P, Q;
+    if (oracle_output_dims(pb, &P, &Q) != 0) return -1;
+    if (beta != 0.0 && dx_old == NULL) return -1;
+    const int64_t N = pb->N, C = pb->C, H = pb->H, W = pb->W;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t c = 0; c < C; ++c) {
+            for (int64_t h = 0; h < H; ++h) {
+                for (int64_t w = 0; w < W; ++w) {
+                    double acc, bnd;
+                    one_dgrad(pb, P, Q, dy, sdy, f, n, c, h, w, &acc, &bnd);
+                    int64_t o = ((n * C + c) * H + h) * W + w;
+                    double val = alpha * acc;
+                    if (beta != 0.0) val += beta * dx_old[o];
+                    if (dx) dx[o] = val;
+                    if (bound) bound[o] = bnd;
+                }
+            }
+        }
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/*
+ * Selected data-gradient values.  idx holds count (n, c, h, w) int64
+ * quadruples; dx_old_vals (read only when beta != 0) the old values there.
+ * Returns 0, or -1 on a bad problem or a coordinate out of range.
+ */
+int oracle_conv2d_bwd_data_at(const oracle_conv_problem* pb,
+                              const double* dy, const int64_t* sdy, const double* f,
+                              double alpha, double beta, const double* dx_old_vals,
+                              const int64_t* idx, int64_t count,
+                              double* dx, double* bound, int nthreads)
+{
+    int64_t P, Q;
+    if (oracle_output_dims(pb, &P, &Q) != 0) return -1;
+    if (beta != 0.0 && dx_old_vals == NULL) return -1;
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t* t = idx + 4 * i;
+        if (t[0] < 0 || t[0] >= pb->N || t[1] < 0 || t[1] >= pb->C ||
+            t[2] < 0 || t[2] >= pb->H || t[3] < 0 || t[3] >= pb->W) return -1;
+    }
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t* t = idx + 4 * i;
+        double acc, bnd;
+        one_dgrad(pb, P, Q, dy, sdy, f, t[0], t[1], t[2], t[3], &acc, &bnd);
+        double val = alpha * acc;
+        if (beta != 0.0) val += beta * dx_old_vals[i];
+        if (dx) dx[i] = val;
         if (bound) bound[i] = bnd;
     }
     (void)nthreads;

@@ -33,8 +33,23 @@ MUTANTS = {
     "no_zero_padding_right": ("w < 0 || w >= pb->W", "w < 0 || w > pb->W"),
 }
 
+# slips in the data-gradient code, caught by test_oracle_dgrad.py
+MUTANTS_DGRAD = {
+    "dgrad_pad_sign": ("hh = h + pb->pad_top - r", "hh = h - pb->pad_top + r"),
+    "dgrad_left_pad_sign": ("ww = w + pb->pad_left - s", "ww = w + pb->pad_left + s"),
+    "dgrad_stride_swapped": ("hh % pb->u != 0", "hh % pb->v != 0"),
+    "dgrad_last_row_dropped": ("hh / pb->u >= P", "hh / pb->u >= P - 1"),
+    "dgrad_divisibility_ignored": ("ww < 0 || ww % pb->v != 0 || ww / pb->v >= Q", "ww < 0 || ww / pb->v >= Q"),
+    "dgrad_filter_flipped": ("double fv = f[((k * pb->C + c) * pb->R + r) * pb->S + s];\n                double prod = dv",
+                             "double fv = f[((k * pb->C + c) * pb->R + (pb->R - 1 - r)) * pb->S + s];\n                double prod = dv"),
+    "dgrad_dy_p_q_swapped": ("p * sdy[2] + q * sdy[3]", "q * sdy[2] + p * sdy[3]"),
+    "dgrad_first_filter_dropped": ("for (int64_t k = 0; k < pb->K; ++k) {\n        for (int64_t r = 0; r < pb->R; ++r) {\n            int64_t hh",
+                                   "for (int64_t k = 1; k < pb->K; ++k) {\n        for (int64_t r = 0; r < pb->R; ++r) {\n            int64_t hh"),
+    "dgrad_beta_dropped": ("val += beta * dx_old[o];", "val += 0.0 * dx_old[o];"),
+}
 
-def _build_and_run(name, old, new, tmp):
+
+def _build_and_run(name, old, new, tmp, pins="test_oracle.py"):
     with open(SRC) as fh:
         text = fh.read()
     assert text.count(old) >= 1, "mutant %s no longer applies to the source" % name
@@ -47,15 +62,16 @@ def _build_and_run(name, old, new, tmp):
                     "-std=c11", "-o", lib, src, "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB=lib, OMP_NUM_THREADS="2")
     proc = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                           os.path.join(ROOT, "tests", "test_oracle.py")],
+                           os.path.join(ROOT, "tests", pins)],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return name, proc.returncode
 
 
 def test_every_mutant_is_caught():
+    jobs = [(n, o, w, "test_oracle.py") for n, (o, w) in MUTANTS.items()]
+    jobs += [(n, o, w, "test_oracle_dgrad.py") for n, (o, w) in MUTANTS_DGRAD.items()]
     with tempfile.TemporaryDirectory() as tmp:
         with ThreadPoolExecutor(max_workers=4) as pool:
-            results = list(pool.map(lambda kv: _build_and_run(kv[0], kv[1][0], kv[1][1], tmp),
-                                    MUTANTS.items()))
+            results = list(pool.map(lambda j: _build_and_run(j[0], j[1], j[2], tmp, j[3]), jobs))
     survivors = [name for name, rc in results if rc == 0]
     assert not survivors, "pins let these oracle mutants through: %s" % survivors
