@@ -1,11 +1,12 @@
-"""Python binding of libmiconv, the MI355X 2-D convolution forward pass.
+"""Python binding of libmiconv, the MI355X 2-D convolution forward pass and
+its data gradient.
 
 Argument marshalling only: every step of the convolution runs in the HIP
 kernels of ``libmiconv.so`` behind the C ABI declared in
 ``include/miconv.h``.  PyTorch supplies device memory and the stream.
 The ``mic_*`` functions mirror the C calls one for one (descriptors are
-ctypes handles); ``conv2d_forward`` and ``ConvPlan`` wrap them for torch
-tensors.
+ctypes handles); ``conv2d_forward`` / ``ConvPlan`` and
+``conv2d_backward_data`` / ``DgradPlan`` wrap them for torch tensors.
 
 There is no fallback: if the library is missing the import fails.
 """
@@ -79,6 +80,10 @@ _SIGS = {
                           _vp, _vp], _i),
     "mic_conv_forward_kernel_name": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_char_p, ctypes.c_size_t],
                                      _i),
+    "mic_conv_backward_data": ([_vp, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, ctypes.c_double,
+                                _vp, _vp], _i),
+    "mic_conv_backward_data_kernel_name": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_char_p, ctypes.c_size_t],
+                                           _i),
 }
 
 
@@ -233,6 +238,18 @@ def mic_conv_forward_kernel_name(handle, x_desc, w_desc, conv, y_desc):
     return buf.value.decode()
 
 
+def mic_conv_backward_data(handle, alpha, w_desc, w_ptr, dy_desc, dy_ptr, conv, beta, dx_desc, dx_ptr):
+    _check(lib().mic_conv_backward_data(handle, float(alpha), w_desc, _vp(w_ptr), dy_desc, _vp(dy_ptr),
+                                        conv, float(beta), dx_desc, _vp(dx_ptr)), "mic_conv_backward_data")
+
+
+def mic_conv_backward_data_kernel_name(handle, w_desc, dy_desc, conv, dx_desc):
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().mic_conv_backward_data_kernel_name(handle, w_desc, dy_desc, conv, dx_desc, buf, 128),
+           "mic_conv_backward_data_kernel_name")
+    return buf.value.decode()
+
+
 # ---------------------------------------------------------------- torch-facing helpers
 
 _handles = {}
@@ -337,3 +354,76 @@ def conv2d_forward(x, w, stride=(1, 1), padding=(0, 0, 0, 0), y=None, alpha=1.0,
     finally:
         plan.close()
     return y
+
+
+class DgradPlan:
+    """Descriptors for one data-gradient call (dy, w -> dx), reusable.
+
+    dy: (N, K, P, Q) tensor of any strides; w: contiguous (K, C, R, S);
+    dx: (N, C, H, W) tensor of any strides, the forward input's shape.
+    """
+
+    def __init__(self, dy, w, dx, stride=(1, 1), padding=(0, 0, 0, 0), handle=None):
+        if dy.dim() != 4 or w.dim() != 4 or dx.dim() != 4:
+            raise ValueError("dy, w, dx must be 4-D")
+        if not w.is_contiguous():
+            raise ValueError("w must be packed K,C,R,S (contiguous)")
+        for t in (dy, w, dx):
+            if t.dtype not in _TORCH_DTYPE:
+                raise TypeError("unsupported dtype %s" % t.dtype)
+        self.dy, self.w, self.dx = dy, w, dx
+        self.handle = handle if handle is not None else handle_for(dy.device)
+        self.dyd, self.wd, self.dxd = mic_tensor_desc_create(), mic_filter_desc_create(), mic_tensor_desc_create()
+        self.cd = mic_conv_desc_create()
+        mic_tensor_desc_set(self.dyd, _TORCH_DTYPE[dy.dtype], *dy.shape, *_element_strides(dy))
+        mic_filter_desc_set(self.wd, _TORCH_DTYPE[w.dtype], *w.shape)
+        mic_tensor_desc_set(self.dxd, _TORCH_DTYPE[dx.dtype], *dx.shape, *_element_strides(dx))
+        mic_conv_desc_set(self.cd, *padding, *stride)
+        # the forward pass's multiply-adds, counted once each
+        self.flops = 2.0 * dy.shape[0] * dy.shape[1] * dy.shape[2] * dy.shape[3] * w.shape[1] * w.shape[2] * w.shape[3]
+
+    def kernel_name(self):
+        return mic_conv_backward_data_kernel_name(self.handle, self.wd, self.dyd, self.cd, self.dxd)
+
+    def __call__(self, alpha=1.0, beta=0.0, stream=None):
+        s = stream if stream is not None else torch.cuda.current_stream(self.dy.device)
+        mic_set_stream(self.handle, s.cuda_stream)
+        mic_conv_backward_data(self.handle, alpha, self.wd, self.w.data_ptr(), self.dyd, self.dy.data_ptr(),
+                               self.cd, beta, self.dxd, self.dx.data_ptr())
+        return self.dx
+
+    def close(self):
+        for d, fn in ((self.dyd, mic_tensor_desc_destroy), (self.dxd, mic_tensor_desc_destroy),
+                      (self.wd, mic_filter_desc_destroy), (self.cd, mic_conv_desc_destroy)):
+            if d is not None:
+                fn(d)
+        self.dyd = self.dxd = self.wd = self.cd = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def conv2d_backward_data(dy, w, x_shape, stride=(1, 1), padding=(0, 0, 0, 0), dx=None, alpha=1.0,
+                         beta=0.0):
+    """dx <- alpha * dgrad(dy, w) + beta * dx on torch's current stream.
+
+    x_shape is the forward input's (N, C, H, W); with dx None a new one is
+    allocated (caller memory, in dy's memory format; fp32 for bf16 inputs)
+    and beta must be 0.
+    """
+    if not dy.is_cuda:
+        raise ValueError("dy must be a GPU tensor")
+    if dx is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing dx")
+        fmt = torch.channels_last if (dy.stride(1) == 1 and dy.shape[1] > 1) else torch.contiguous_format
+        dx = torch.empty(tuple(x_shape), dtype=_OUT_DTYPE[dy.dtype], device=dy.device, memory_format=fmt)
+    plan = DgradPlan(dy, w.contiguous(), dx, stride, padding)
+    try:
+        plan(alpha, beta)
+    finally:
+        plan.close()
+    return dx

@@ -26,6 +26,15 @@
 // padded width W + pad_left + pad_right <= WP; every tile's slot span
 // <= SL; C a multiple of CB; the filter 8- or 16-byte aligned as the
 // instance's vector loads need.
+//
+// DG = true computes the data gradient of a stride-1 convolution as the
+// forward pass of dy with the filter transposed (K <-> C) and flipped
+// (r -> R-1-r, s -> S-1-s), the padding becoming R-1-pad_top and
+// S-1-pad_left: the adjoint of the forward sum in x.  The host passes the
+// parameters of that forward problem (x = dy, y = dx, C and K exchanged);
+// only the slab loader differs, reading for each slab row (a channel of dx)
+// and chunk channel (a filter of the real problem) the run of R*S taps of
+// F[k, c, :, :] and storing it reversed.
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -37,7 +46,8 @@
 
 namespace miconv {
 
-template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS>
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS,
+          bool DG>
 __global__ void __launch_bounds__(256 * KS)
 conv_fwd_halo_kernel(const ConvParams p)
 {
@@ -130,6 +140,22 @@ conv_fwd_halo_kernel(const ConvParams p)
     }
 
     // ---- slab loader: thread -> NVB (filter row, vector) positions
+    // (DG: thread -> NDU (slab row, channel) runs of R*S taps instead)
+    constexpr int DU = TN * CB;
+    constexpr int NDU = DG ? (DU + NT - 1) / NT : 1;
+    int d_off[NDU];
+    uint32_t d_ok = 0;
+    if constexpr (DG) {
+#pragma unroll
+        for (int i = 0; i < NDU; ++i) {
+            const int e = tid + NT * i;
+            const int row = e % TN;
+            const int cl = e / TN;
+            const bool ok = e < DU && n0 + row < p.K;
+            d_off[i] = ok ? (cl * p.K + n0 + row) * RS : 0;          // elements
+            d_ok |= (ok ? 1u : 0u) << i;
+        }
+    }
     int b_off[NVB];
     uint32_t b_ok = 0;
 #pragma unroll
@@ -143,22 +169,33 @@ conv_fwd_halo_kernel(const ConvParams p)
     }
 
     In h_val[HE];
-    u32x4 b_val[NVB];
+    u32x4 b_val[DG ? 1 : NVB];
+    In d_val[NDU][DG ? RS : 1];
 
     auto load_chunk = [&](int c0) {
         const int xo = c0 * p.sxc;
 #pragma unroll
         for (int i = 0; i < HE; ++i) h_val[i] = ((h_ok >> i) & 1) ? load_elem(x + h_off[i] + xo) : In(0);
-        const int wo = c0 * RS;
+        if constexpr (DG) {
+            const int wo = c0 * p.K * RS;
 #pragma unroll
-        for (int i = 0; i < NVB; ++i) {
-            if constexpr (VB == 16) {
-                b_val[i] = ((b_ok >> i) & 1) ? *reinterpret_cast<const u32x4*>(w + b_off[i] + wo)
-                                             : u32x4{0, 0, 0, 0};
-            } else {
-                const u32x2 t = ((b_ok >> i) & 1) ? *reinterpret_cast<const u32x2*>(w + b_off[i] + wo)
-                                                  : u32x2{0, 0};
-                b_val[i] = u32x4{t[0], t[1], 0, 0};
+            for (int i = 0; i < NDU; ++i) {
+                const bool ok = (d_ok >> i) & 1;
+#pragma unroll
+                for (int t = 0; t < RS; ++t) d_val[i][t] = ok ? load_elem(w + d_off[i] + wo + t) : In(0);
+            }
+        } else {
+            const int wo = c0 * RS;
+#pragma unroll
+            for (int i = 0; i < NVB; ++i) {
+                if constexpr (VB == 16) {
+                    b_val[i] = ((b_ok >> i) & 1) ? *reinterpret_cast<const u32x4*>(w + b_off[i] + wo)
+                                                 : u32x4{0, 0, 0, 0};
+                } else {
+                    const u32x2 t = ((b_ok >> i) & 1) ? *reinterpret_cast<const u32x2*>(w + b_off[i] + wo)
+                                                      : u32x2{0, 0};
+                    b_val[i] = u32x4{t[0], t[1], 0, 0};
+                }
             }
         }
     };
@@ -174,15 +211,30 @@ conv_fwd_halo_kernel(const ConvParams p)
             reinterpret_cast<In*>(hb)[cl * PLANE + slot * WP + col] = h_val[i];
         }
         unsigned char* bb = hb + HALO_BYTES;
+        if constexpr (DG) {
+            // run element t is tap RS-1-t of the slab row (the filter flipped)
 #pragma unroll
-        for (int i = 0; i < NVB; ++i) {
-            const int e = tid + NT * i;
-            if (e < TN * VPR) {
-                const int row = e / VPR;
-                const int vec = e - row * VPR;
-                u32x2* dst = reinterpret_cast<u32x2*>(bb + row * BROW + vec * VB);
-                dst[0] = u32x2{b_val[i][0], b_val[i][1]};
-                if constexpr (VB == 16) dst[1] = u32x2{b_val[i][2], b_val[i][3]};
+            for (int i = 0; i < NDU; ++i) {
+                const int e = tid + NT * i;
+                if (DU % NT == 0 || e < DU) {
+                    const int row = e % TN;
+                    const int cl = e / TN;
+                    In* dst = reinterpret_cast<In*>(bb + row * BROW) + cl * RS;
+#pragma unroll
+                    for (int t = 0; t < RS; ++t) dst[RS - 1 - t] = d_val[i][t];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NVB; ++i) {
+                const int e = tid + NT * i;
+                if (e < TN * VPR) {
+                    const int row = e / VPR;
+                    const int vec = e - row * VPR;
+                    u32x2* dst = reinterpret_cast<u32x2*>(bb + row * BROW + vec * VB);
+                    dst[0] = u32x2{b_val[i][0], b_val[i][1]};
+                    if constexpr (VB == 16) dst[1] = u32x2{b_val[i][2], b_val[i][3]};
+                }
             }
         }
     };
@@ -292,15 +344,19 @@ conv_fwd_halo_kernel(const ConvParams p)
 // ------------------------------------------------------------------ instances and launch
 
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS>
-static hipError_t launch_halo_variant(const ConvParams& p0, hipStream_t stream)
+static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStream_t stream)
 {
     ConvParams p = p0;
     if (p.m_step <= 0 || p.m_step > TM) p.m_step = TM;   // the host sets P*Q for image tiles
     p.m_tiles = (p.M + p.m_step - 1) / p.m_step;
     p.n_tiles = (p.K + TN - 1) / TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
-    hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS>),
-                       grid, dim3(256 * KS), 0, stream, p);
+    if (dgrad)
+        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, true>),
+                           grid, dim3(256 * KS), 0, stream, p);
+    else
+        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false>),
+                           grid, dim3(256 * KS), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -319,14 +375,14 @@ static hipError_t launch_halo_variant(const ConvParams& p0, hipStream_t stream)
     X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1)          \
     X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16, 1)
 
-hipError_t launch_halo(Variant v, const ConvParams& p, hipStream_t stream)
+hipError_t launch_halo(Variant v, const ConvParams& p, bool dgrad, hipStream_t stream)
 {
     switch (v) {
 #define X(name, pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks) \
-    case Variant::name: return launch_halo_variant<pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks>(p, stream);
+    case Variant::name: return launch_halo_variant<pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks>(p, dgrad, stream);
         MICONV_HALO_VARIANTS(X)
 #undef X
-    default: return launch_halo_bf16(v, p, stream);
+    default: return dgrad ? hipErrorInvalidValue : launch_halo_bf16(v, p, stream);
     }
 }
 

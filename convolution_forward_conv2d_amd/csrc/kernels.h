@@ -45,10 +45,16 @@ enum class DType : int { F32 = 0, F64 = 1, BF16 = 2 };
 hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, bool tap, hipStream_t stream);
 
 // Launch a tap-batched halo variant (the host has checked its eligibility).
-hipError_t launch_halo(Variant v, const ConvParams& p, hipStream_t stream);
+// dgrad: p describes the forward problem equivalent to a stride-1 data
+// gradient (conv_fwd_halo.hip); fp32 and fp64 instances only.
+hipError_t launch_halo(Variant v, const ConvParams& p, bool dgrad, hipStream_t stream);
 hipError_t launch_halo_bf16(Variant v, const ConvParams& p, hipStream_t stream);
 
 // Launch the plain direct kernel (one thread per output element).
 hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);
+
+// Data gradient, plain direct kernel (one thread per dx element); p is laid
+// out as conv_bwd_data.hip describes.
+hipError_t launch_bwd_data_direct(DType dt, const ConvParams& p, hipStream_t stream);
 
 }  // namespace miconv

@@ -257,10 +257,12 @@ int max_tile_slots(const ConvParams& p, int step)
     return worst;
 }
 
-bool halo_eligible(const HaloCandidate& h, DType dt, const ConvParams& p, const void* w, bool check_ptr)
+bool halo_eligible(const HaloCandidate& h, DType dt, const ConvParams& p, const void* w, bool check_ptr,
+                   bool dgrad = false)
 {
     if (h.dt != dt || h.r != p.R || h.s != p.S) return false;
     if (p.C % h.cb != 0) return false;
+    if (dgrad) return dt != DType::BF16;     // scalar filter loads: no alignment needed
     if (check_ptr && (uintptr_t)w % 16 != 0) return false;
     return true;
 }
@@ -426,6 +428,152 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
     const bool gather = pl.cand.v != Variant::DIRECT && !is_halo(pl.cand.v);
     if (!gather) pl.tap = false;
     snprintf(pl.name, sizeof(pl.name), "%s%s", pl.cand.name, pl.tap ? "_tap" : "");
+    pl.status = MIC_STATUS_SUCCESS;
+    return pl;
+}
+
+// ---------------------------------------------------------------- data gradient
+
+// dx <- alpha * dgrad(dy, w) + beta * dx.  The forward geometry is (dx, w,
+// conv); dy must have the forward output's dims.  Stride-1 problems of the
+// halo shapes (fp32, fp64) run as the forward pass of dy with the filter
+// transposed and flipped (conv_fwd_halo.hip, DG instances); everything else
+// takes the direct kernel (conv_bwd_data.hip).
+Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, const void* dy,
+                     const mic_filter_desc_st* wd, const void* w, const mic_conv_desc_st* cd,
+                     const mic_tensor_desc_st* dxd, const void* dx, double alpha, double beta,
+                     bool need_pointers)
+{
+    Plan pl;
+    memset(&pl, 0, sizeof(pl));
+    pl.status = MIC_STATUS_BAD_PARAM;
+    if (!dyd || !wd || !cd || !dxd) return pl;
+    if (!dyd->set || !wd->set || !cd->set || !dxd->set) return pl;
+    if (need_pointers && (!dy || !w || !dx)) return pl;
+    int n, k, P, Q;
+    mic_status st = output_dims(cd, dxd, wd, &n, &k, &P, &Q);
+    if (st != MIC_STATUS_SUCCESS) {
+        pl.status = st;
+        return pl;
+    }
+    if (dyd->n != n || dyd->c != k || dyd->h != P || dyd->w != Q) return pl;
+
+    if (dyd->dtype == MIC_DTYPE_F32 && wd->dtype == MIC_DTYPE_F32 && dxd->dtype == MIC_DTYPE_F32)
+        pl.dt = DType::F32;
+    else if (dyd->dtype == MIC_DTYPE_F64 && wd->dtype == MIC_DTYPE_F64 && dxd->dtype == MIC_DTYPE_F64)
+        pl.dt = DType::F64;
+    else if (dyd->dtype == MIC_DTYPE_BF16 && wd->dtype == MIC_DTYPE_BF16 && dxd->dtype == MIC_DTYPE_F32)
+        pl.dt = DType::BF16;
+    else {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;
+        return pl;
+    }
+
+    const int64_t M = (int64_t)dxd->n * dxd->h * dxd->w;
+    const int64_t RS = (int64_t)wd->r * wd->s;
+    const int64_t wsize = (int64_t)wd->k * wd->c * RS;
+    if (extent(*dyd) >= kMaxOffset || extent(*dxd) >= kMaxOffset || wsize >= kMaxOffset ||
+        M >= kMaxOffset || (int64_t)wd->k * RS >= kMaxOffset || dyd->sn >= kMaxOffset ||
+        dyd->sc >= kMaxOffset || dyd->sh >= kMaxOffset || dyd->sw >= kMaxOffset ||
+        dxd->sn >= kMaxOffset || dxd->sc >= kMaxOffset || dxd->sh >= kMaxOffset || dxd->sw >= kMaxOffset) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;
+        return pl;
+    }
+    if (need_pointers) {
+        const size_t ie = dtype_size(dyd->dtype), oe = dtype_size(dxd->dtype);
+        if ((uintptr_t)dy % ie || (uintptr_t)w % ie || (uintptr_t)dx % oe) return pl;
+    }
+
+    const int R = wd->r, S = wd->s, C = dxd->c, H = dxd->h, W = dxd->w;
+    const int pt = cd->pad_top, pl_ = cd->pad_left;
+    ConvParams& p = pl.p;
+    p.x = dy;
+    p.w = w;
+    p.y = const_cast<void*>(dx);
+    p.sxn = (int)dyd->sn;
+    p.sxc = (int)dyd->sc;
+    p.sxh = (int)dyd->sh;
+    p.sxw = (int)dyd->sw;
+    p.syn = (int)dxd->sn;
+    p.syk = (int)dxd->sc;
+    p.syp = (int)dxd->sh;
+    p.syq = (int)dxd->sw;
+    p.N = n;
+    p.R = R;
+    p.S = S;
+    p.M = (int)M;
+    p.div_pq = FastDiv((uint32_t)(H * W));
+    p.div_q = FastDiv((uint32_t)W);
+    p.div_rs = FastDiv((uint32_t)RS);
+    p.div_s = FastDiv((uint32_t)S);
+    p.alpha = alpha;
+    p.beta = beta;
+    pl.cand = kDirect;
+
+    // the equivalent forward problem of a stride-1 data gradient: input dy
+    // (C' = K channels, H' x W' = P x Q), K' = C filters, padding R-1-pad_top
+    // on top and H-P+pad_top below (S-1-pad_left, W-Q+pad_left across), output
+    // H x W
+    const int pb2 = H - P + pt, pr2 = W - Q + pl_;
+    const bool halo_ok = cd->u == 1 && cd->v == 1 && pt <= R - 1 && pl_ <= S - 1 && pb2 >= 0 && pr2 >= 0 &&
+                         pl.dt != DType::BF16;
+    if (halo_ok) {
+        ConvParams v = p;
+        v.C = k;
+        v.H = P;
+        v.W = Q;
+        v.K = C;
+        v.P = H;
+        v.Q = W;
+        v.u = 1;
+        v.v = 1;
+        v.pad_top = R - 1 - pt;
+        v.pad_left = S - 1 - pl_;
+        v.Hp = P + v.pad_top + pb2;
+        v.div_hp = FastDiv((uint32_t)v.Hp);
+        v.Kred = (int)((int64_t)k * RS);
+        const int Wp = Q + v.pad_left + pr2;
+        const int num_cu = h ? h->num_cu : kDefaultCUs;
+        const char* force = getenv("MIC_FORCE_DGRAD_VARIANT");
+        const bool forced = force && force[0];
+        double best = 0;
+        bool found = false;
+        for (const HaloCandidate& hc : kHalo) {
+            double cost;
+            int step;
+            if (forced && strcmp(force, hc.c.name) != 0) continue;
+            if (!halo_eligible(hc, pl.dt, v, w, need_pointers, true)) continue;
+            if (!halo_cost(hc, v, Wp, num_cu, &cost, &step)) continue;
+            if (!found || cost < best) {
+                best = cost;
+                pl.cand = hc.c;
+                v.m_step = step;
+                found = true;
+            }
+        }
+        if (found) p = v;
+    }
+    if (pl.cand.v == Variant::DIRECT) {
+        // direct kernel layout (conv_bwd_data.hip)
+        p.C = C;
+        p.H = H;
+        p.W = W;
+        p.K = k;
+        p.P = P;
+        p.Q = Q;
+        p.u = cd->u;
+        p.v = cd->v;
+        p.pad_top = pt;
+        p.pad_left = pl_;
+        p.Kred = (int)((int64_t)C * RS);
+    }
+    if (const char* force = getenv("MIC_FORCE_DGRAD_VARIANT")) {
+        if (force[0] && strcmp(force, pl.cand.name) != 0) {
+            pl.status = MIC_STATUS_NOT_SUPPORTED;   // the forced variant does not fit this problem
+            return pl;
+        }
+    }
+    snprintf(pl.name, sizeof(pl.name), "dgrad_%s", pl.cand.name);
     pl.status = MIC_STATUS_SUCCESS;
     return pl;
 }
@@ -666,10 +814,38 @@ mic_status mic_conv_forward(mic_handle handle, double alpha, mic_tensor_desc x_d
     if (pl.cand.v == Variant::DIRECT)
         err = miconv::launch_direct(pl.dt, pl.p, handle->stream);
     else if (is_halo(pl.cand.v))
-        err = miconv::launch_halo(pl.cand.v, pl.p, handle->stream);
+        err = miconv::launch_halo(pl.cand.v, pl.p, false, handle->stream);
     else
         err = miconv::launch_mfma(pl.cand.v, pl.p, pl.bvec, pl.tap, handle->stream);
     return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
+}
+
+mic_status mic_conv_backward_data(mic_handle handle, double alpha, mic_filter_desc w_desc, const void* w,
+                                  mic_tensor_desc dy_desc, const void* dy, mic_conv_desc conv, double beta,
+                                  mic_tensor_desc dx_desc, void* dx)
+{
+    if (!handle) return MIC_STATUS_BAD_PARAM;
+    Plan pl = make_dgrad_plan(handle, dy_desc, dy, w_desc, w, conv, dx_desc, dx, alpha, beta, true);
+    if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    hipError_t err;
+    if (pl.cand.v == Variant::DIRECT)
+        err = miconv::launch_bwd_data_direct(pl.dt, pl.p, handle->stream);
+    else
+        err = miconv::launch_halo(pl.cand.v, pl.p, true, handle->stream);
+    return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
+}
+
+mic_status mic_conv_backward_data_kernel_name(mic_handle handle, mic_filter_desc w_desc,
+                                              mic_tensor_desc dy_desc, mic_conv_desc conv,
+                                              mic_tensor_desc dx_desc, char* buf, size_t buflen)
+{
+    if (!buf) return MIC_STATUS_BAD_PARAM;
+    Plan pl = make_dgrad_plan(handle, dy_desc, nullptr, w_desc, nullptr, conv, dx_desc, nullptr, 1.0, 0.0, false);
+    if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    const size_t len = strlen(pl.name);
+    if (len + 1 > buflen) return MIC_STATUS_BAD_PARAM;
+    memcpy(buf, pl.name, len + 1);
+    return MIC_STATUS_SUCCESS;
 }
 
 mic_status mic_conv_forward_kernel_name(mic_handle handle, mic_tensor_desc x_desc,

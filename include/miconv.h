@@ -1,6 +1,6 @@
 /*
  * miconv.h -- C ABI of libmiconv, the 2-D convolution forward pass (FPROP)
- * for AMD Instinct MI355X (gfx950).
+ * and its data gradient for AMD Instinct MI355X (gfx950).
  *
  * The operation (direct convolution, cross-correlation form, zero padding):
  *
@@ -176,6 +176,43 @@ mic_status mic_conv_forward(mic_handle handle, double alpha,
 mic_status mic_conv_forward_kernel_name(mic_handle handle, mic_tensor_desc x_desc,
                                         mic_filter_desc w_desc, mic_conv_desc conv,
                                         mic_tensor_desc y_desc, char* buf, size_t buflen);
+
+/* ---------------------------------------------------------------- data gradient */
+
+/* dx <- alpha * dgrad(dy, w) + beta * dx: the backward pass with respect to
+ * the input, i.e. the adjoint of the forward sum in x,
+ *
+ *   dx[n,c,h,w] = alpha * sum_{k,r,s} dY(n, k, p, q) * F[k,c,r,s]
+ *                 over p*u = h + pad_top - r (0 <= p < P),
+ *                      q*v = w + pad_left - s (0 <= q < Q)
+ *               + beta * dx[n,c,h,w]
+ *
+ * on the handle's stream, asynchronously.  The cuDNN page ("Proposed
+ * Method") names forward and backward routines and the maxDNN page
+ * (Abstract, RQ4) the backward pass, without a formula; this is the plain
+ * reading.
+ *
+ * The geometry is the forward problem's: dx_desc plays x (N, C, H, W),
+ * w_desc the packed K,C,R,S filter, conv its padding and strides, and
+ * dy_desc must have the forward output dims (N, K, P, Q).  Element types
+ * (dy, w, dx): (F32, F32, F32), (F64, F64, F64), (BF16, BF16, F32).  dy and
+ * dx are device memory with any element strides; alpha, beta, beta == 0,
+ * ownership, overlap and size rules as for mic_conv_forward.  No workspace.
+ *
+ * Errors: MIC_STATUS_BAD_PARAM (null handle/descriptor/pointer, unset
+ * descriptor, dy dims not the forward output dims), MIC_STATUS_NOT_SUPPORTED
+ * (dtype combination, size limit), MIC_STATUS_LAUNCH_FAILED. */
+mic_status mic_conv_backward_data(mic_handle handle, double alpha,
+                                  mic_filter_desc w_desc, const void* w,
+                                  mic_tensor_desc dy_desc, const void* dy,
+                                  mic_conv_desc conv, double beta,
+                                  mic_tensor_desc dx_desc, void* dx);
+
+/* Name of the kernel variant mic_conv_backward_data would launch (host
+ * only), as mic_conv_forward_kernel_name. */
+mic_status mic_conv_backward_data_kernel_name(mic_handle handle, mic_filter_desc w_desc,
+                                              mic_tensor_desc dy_desc, mic_conv_desc conv,
+                                              mic_tensor_desc dx_desc, char* buf, size_t buflen);
 
 #ifdef __cplusplus
 }

@@ -239,3 +239,62 @@ def test_fastdiv_and_tile_map_on_host():
                        capture_output=True)
         out = subprocess.run([exe], capture_output=True, text=True, timeout=300)
         assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
+
+
+# ---------------------------------------------------------------- data gradient (host side)
+
+def _dgrad_name(lay, dts=None):
+    """Kernel the data gradient of a forward layer would use: (dy, w, dx) descriptors."""
+    F32 = mic.MIC_DTYPE_F32
+    dts = dts or {"f32": (F32, F32, F32), "f64": (1, 1, 1), "bf16": (2, 2, F32)}[lay.dtype]
+    xd, wd, cd, yd = _descs(lay, dts[2], dts[1], dts[0])   # dx plays x, dy plays y
+    try:
+        return mic.mic_conv_backward_data_kernel_name(None, wd, yd, cd, xd)
+    finally:
+        _free(xd, wd, cd, yd)
+
+
+def test_dgrad_kernel_choice_host_only():
+    names = {lay.name: _dgrad_name(lay) for lay in workloads.ALL_LAYERS}
+    for name in ("alexnet_conv2", "alexnet_conv3", "alexnet_conv4", "alexnet_conv5", "overfeat_l3",
+                 "overfeat_l4", "overfeat_l5", "prec_conv3_f64_nchw", "prec_conv4_f64_nhwc"):
+        assert names[name].startswith("dgrad_halo_f"), (name, names[name])
+    # strided layers and bf16 take the direct kernel
+    for name in ("overfeat_l1", "speech_l1", "speech_l2", "prec_conv3_bf16_nchw"):
+        assert names[name] == "dgrad_direct", (name, names[name])
+
+
+def test_dgrad_shape_and_type_errors():
+    lay = workloads.TINY[0]
+    F32 = mic.MIC_DTYPE_F32
+    # dy dims that are not the forward output dims
+    xd, wd, cd, yd = _descs(lay, F32, F32, F32, y_dims=(lay.N, lay.K, 11, 12))
+    try:
+        with pytest.raises(mic.MicError) as e:
+            mic.mic_conv_backward_data_kernel_name(None, wd, yd, cd, xd)
+        assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+    finally:
+        _free(xd, wd, cd, yd)
+    for combo in [(0, 0, 1), (2, 2, 2), (1, 0, 1)]:
+        xd, wd, cd, yd = _descs(lay, combo[2], combo[1], combo[0])
+        try:
+            with pytest.raises(mic.MicError) as e:
+                mic.mic_conv_backward_data_kernel_name(None, wd, yd, cd, xd)
+            assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+        finally:
+            _free(xd, wd, cd, yd)
+    l = mic.lib()
+    assert l.mic_conv_backward_data(None, 1.0, None, None, None, None, None, 0.0, None, None) == \
+        mic.MIC_STATUS_BAD_PARAM
+
+
+def test_dgrad_forced_variant(monkeypatch):
+    lay = workloads.by_name("alexnet_conv3")
+    monkeypatch.setenv("MIC_FORCE_DGRAD_VARIANT", "direct")
+    assert _dgrad_name(lay) == "dgrad_direct"
+    monkeypatch.setenv("MIC_FORCE_DGRAD_VARIANT", "halo_f32_3x3_64x128")
+    assert _dgrad_name(lay) == "dgrad_halo_f32_3x3_64x128"
+    monkeypatch.setenv("MIC_FORCE_DGRAD_VARIANT", "halo_f32_5x5_128x128")    # wrong filter size
+    with pytest.raises(mic.MicError) as e:
+        _dgrad_name(lay)
+    assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED

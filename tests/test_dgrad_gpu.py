@@ -1,0 +1,180 @@
+"""GPU parity of the data gradient (mic_conv_backward_data) against the oracle.
+
+Small shapes spanning several tiles with ragged tails are compared in full
+for every kernel variant; every workload layer's data gradient is run at
+full size and compared on sampled coordinates, with integer-valued inputs
+bit-exact, NaN-prefilled dx fully overwritten and reruns bit-identical.
+dy is seeded uniform [-1, 1] (tensor id 3 of the layer's seed), rounded to
+the layer's storage type.
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_forward_conv2d_amd as mic
+import gen
+import oracle
+from gen import workloads
+from gen.workloads import Layer
+
+import gpu_harness as H
+from test_parity_gpu import SMALL_SHAPES, U
+
+pytestmark = pytest.mark.gpu
+
+DG_VARIANTS = {
+    "f32": ["direct", "halo_f32_3x3_128x128", "halo_f32_3x3_128x64", "halo_f32_3x3_64x128",
+            "halo_f32_3x3_96x128", "halo_f32_5x5_128x128", "halo_f32_5x5_128x128_c2",
+            "halo_f32x16_3x3_176x128", "halo_f32x16_3x3_144x128", "halo_f32x16_3x3_176x128_ks2",
+            "halo_f32_3x3_128x128_ks2"],
+    "f64": ["direct", "halo_f64_3x3_128x128", "halo_f64_3x3_64x64"],
+    "bf16": ["direct"],
+}
+_ran = set()
+
+# the forward shapes, plus a 5x5 one whose filter count (the data gradient's
+# reduction channels) is a multiple of 4
+SHAPES = SMALL_SHAPES + [
+    dict(name="dg_halo5_k72", N=2, C=12, Hh=20, Ww=20, K=72, R=5, S=5, stride=(1, 1), pads=(2, 2, 2, 2)),
+]
+
+
+def _small(name, N, C, Hh, Ww, K, R, S, stride, pads, dtype, layout="nchw", pitch=0):
+    return Layer(name, 9, 2, N, C, Hh, Ww, K, R, S, stride, pads, dtype, U, U,
+                 layout=layout, row_pitch=pitch)
+
+
+def _dy(lay, shape, integer=False):
+    seed = gen.derive_seed(lay.config, lay.layer, 3)
+    d = gen.integers(seed, shape, -4, 4) if integer else gen.uniform(seed, shape, -1.0, 1.0)
+    return gen.round_to(d, lay.dtype)
+
+
+def _run(lay, dy, w, dx, alpha=1.0, beta=0.0):
+    plan = mic.DgradPlan(dy, w, dx, lay.stride, lay.padding)
+    try:
+        plan(alpha, beta)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    return dx
+
+
+def _out(lay, fill=float("nan")):
+    return H.out_tensor(lay, lay.x_shape, fill=fill)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: s["name"])
+def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
+    lay = _small(dtype=dtype, **{k: v for k, v in shape.items()})
+    _, w64 = H.inputs(lay)
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    dy64 = _dy(lay, (N, K, P, Q))
+    ref, bound = oracle.conv2d_bwd_data(dy64, w64, lay.x_shape, lay.stride, lay.padding)
+    dy = H.to_device(dy64, dtype, lay.layout, lay.row_pitch)
+    w = torch.from_numpy(w64).to(H.TORCH_DT[dtype]).to(H.dev())
+    for var in DG_VARIANTS[dtype]:
+        monkeypatch.setenv("MIC_FORCE_DGRAD_VARIANT", var)
+        print("case", shape["name"], dtype, var, flush=True)
+        dx = _out(lay)
+        try:
+            _run(lay, dy, w, dx)
+        except mic.MicError as e:
+            if var.startswith("halo_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+                continue
+            raise
+        H.check(dtype, dx.double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (shape["name"], dtype, var))
+        _ran.add(var)
+
+
+def test_every_dgrad_variant_was_exercised():
+    want = {v for vs in DG_VARIANTS.values() for v in vs}
+    assert want <= _ran, "data-gradient variants never run: %s" % sorted(want - _ran)
+
+
+def _sample(rng, shape, count):
+    N, C, Hh, Ww = shape
+    return H.sample_coords(rng, N, C, Hh, Ww, count)
+
+
+@pytest.mark.parametrize("lay", workloads.ALL_LAYERS, ids=lambda l: l.name)
+def test_workload_layer_sampled(lay):
+    """Full-size data gradient, default variant: sampled parity, NaN-safe beta=0, rerun bit-identity."""
+    print("layer", lay.name, flush=True)
+    _, w64 = H.inputs(lay)
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    dy64 = _dy(lay, (N, K, P, Q))
+    dy = H.to_device(dy64, lay.dtype, lay.layout, lay.row_pitch)
+    w = torch.from_numpy(w64).to(H.TORCH_DT[lay.dtype]).to(H.dev())
+    dx = _out(lay)
+    _run(lay, dy, w, dx)
+    assert bool(torch.isfinite(dx).all()), "unwritten or non-finite dx"
+    rng = np.random.default_rng(lay.config * 1000 + lay.layer + 17)
+    idx = _sample(rng, lay.x_shape, 3000)
+    ref, bound = oracle.conv2d_bwd_data_at(dy64, w64, lay.x_shape, idx, lay.stride, lay.padding)
+    rel, worst = H.check(lay.dtype, H.gather(dx, idx), ref, bound, what=lay.name)
+    print("  sampled rel-L2 %.3e, worst |err|/B %.3e" % (rel, worst), flush=True)
+    dx2 = _out(lay, fill=0.0)
+    _run(lay, dy, w, dx2)
+    assert torch.equal(dx, dx2), "rerun not bit-identical"
+
+
+@pytest.mark.parametrize("lay", [l for l in workloads.ALL_LAYERS if not l.name.endswith("nhwc")],
+                         ids=lambda l: l.name)
+def test_workload_layer_integer_exact(lay):
+    """Integer dy and filter in [-4, 4]: every partial sum is an exact integer below 2^24."""
+    print("layer", lay.name, flush=True)
+    _, w64 = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    dy64 = _dy(lay, (N, K, P, Q), integer=True)
+    dy = H.to_device(dy64, lay.dtype, lay.layout, lay.row_pitch)
+    w = torch.from_numpy(w64).to(H.TORCH_DT[lay.dtype]).to(H.dev())
+    dx = _out(lay)
+    _run(lay, dy, w, dx)
+    rng = np.random.default_rng(lay.config * 1000 + lay.layer + 29)
+    idx = _sample(rng, lay.x_shape, 3000)
+    ref, _ = oracle.conv2d_bwd_data_at(dy64, w64, lay.x_shape, idx, lay.stride, lay.padding)
+    got = H.gather(dx, idx)
+    assert np.array_equal(got, ref), "%s: %d mismatches" % (lay.name, int((got != ref).sum()))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
+def test_alpha_beta(dtype, monkeypatch):
+    lay = _small("dg_ab", 2, 20, 13, 11, 36, 3, 3, (1, 1), (1, 1, 1, 0), dtype)
+    _, wi = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    dyi = _dy(lay, (N, K, P, Q), integer=True)
+    acc, _ = oracle.conv2d_bwd_data(dyi, wi, lay.x_shape, lay.stride, lay.padding)
+    old = gen.integers(98, acc.shape)
+    dy = H.to_device(dyi, dtype)
+    w = torch.from_numpy(wi).to(H.TORCH_DT[dtype]).to(H.dev())
+    for var in DG_VARIANTS[dtype]:
+        monkeypatch.setenv("MIC_FORCE_DGRAD_VARIANT", var)
+        dx = torch.from_numpy(old).to(H.OUT_DT[dtype]).to(H.dev())
+        try:
+            _run(lay, dy, w, dx, alpha=0.5, beta=0.25)
+        except mic.MicError as e:
+            if var.startswith("halo_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+                continue
+            raise
+        assert np.array_equal(dx.double().cpu().numpy(), 0.5 * acc + 0.25 * old), var
+
+
+def test_dgrad_error_statuses_on_device():
+    lay = workloads.TINY[0]
+    dy = torch.zeros((2, 16, 11, 12), device=H.dev())          # forward output is 12 x 12
+    w = torch.zeros(lay.w_shape, device=H.dev())
+    dx = torch.zeros(lay.x_shape, device=H.dev())
+    with pytest.raises(mic.MicError) as e:
+        mic.conv2d_backward_data(dy, w, lay.x_shape, lay.stride, lay.padding, dx=dx)
+    assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+    dy = torch.zeros((2, 16, 12, 12), device=H.dev())
+    plan = mic.DgradPlan(dy, w, dx, lay.stride, lay.padding)
+    try:
+        with pytest.raises(mic.MicError) as e:                   # null dy pointer
+            mic.mic_conv_backward_data(plan.handle, 1.0, plan.wd, w.data_ptr(), plan.dyd, 0, plan.cd, 0.0,
+                                       plan.dxd, dx.data_ptr())
+        assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+    finally:
+        plan.close()
