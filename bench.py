@@ -8,13 +8,15 @@ one kernel launch of libmiconv through the C ABI.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
                     [--workload alexnet|overfeat|speech|tiny|prec_f64|prec_bf16]
+                    [--op fprop|dgrad]
 
 Prints one JSON line.  ``value`` = 2*N*K*C*R*S*P*Q summed over the step's
 layers / mean step time (inputs resident in HBM, no host traffic inside
 the timed region).  ``roofline`` covers the kernel with the most time per
 step, timed with HIP events on the stream it runs on.  ``cpu_baseline``
 times the CPU oracle on a bounded sample of the same workload (the first
-few images of every layer).
+few images of every layer).  ``--op dgrad`` times the data gradient of the
+same layers instead (dy seeded uniform [-1, 1]; the same FLOP count).
 """
 import argparse
 import hashlib
@@ -38,6 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="alexnet", choices=WORKLOADS)
+    ap.add_argument("--op", default="fprop", choices=("fprop", "dgrad"),
+                    help="forward pass (default) or data gradient of the workload's layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -136,13 +140,22 @@ def main():
             w = gen.round_to(gen.draw(lay.w_dist, gen.derive_seed(lay.config, lay.layer, 1), lay.w_shape), dtype)
             cache[key] = (x, w)
         x, w = cache[key]
-        xt = upload(x, dtype, lay.layout, lay.row_pitch, dev)
-        wt = torch.from_numpy(w).to(xt.dtype).to(dev)
         N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
-        yst = workloads.padded_strides(N, K, P, Q, lay.layout, lay.row_pitch)
-        yt = torch.zeros(workloads.storage_elems(N, K, P, Q, yst), dtype=out_dt,
-                         device=dev).as_strided((N, K, P, Q), yst)
-        plans.append((lay, mic.ConvPlan(xt, wt, yt, lay.stride, lay.padding), (x, w)))
+        wt = torch.from_numpy(w).to({"f32": torch.float32, "f64": torch.float64,
+                                     "bf16": torch.bfloat16}[dtype]).to(dev)
+        if args.op == "fprop":
+            xt = upload(x, dtype, lay.layout, lay.row_pitch, dev)
+            yst = workloads.padded_strides(N, K, P, Q, lay.layout, lay.row_pitch)
+            yt = torch.zeros(workloads.storage_elems(N, K, P, Q, yst), dtype=out_dt,
+                             device=dev).as_strided((N, K, P, Q), yst)
+            plans.append((lay, mic.ConvPlan(xt, wt, yt, lay.stride, lay.padding), (x, w)))
+        else:
+            dy = gen.round_to(gen.uniform(gen.derive_seed(lay.config, lay.layer, 3), (N, K, P, Q)), dtype)
+            dyt = upload(dy, dtype, lay.layout, lay.row_pitch, dev)
+            xst = workloads.padded_strides(*lay.x_shape, lay.layout, lay.row_pitch)
+            dxt = torch.zeros(workloads.storage_elems(*lay.x_shape, xst), dtype=out_dt,
+                              device=dev).as_strided(lay.x_shape, xst)
+            plans.append((lay, mic.DgradPlan(dyt, wt, dxt, lay.stride, lay.padding), (dy, w)))
     stream = torch.cuda.current_stream(dev)
     flops_step = sum(p.flops for _, p, _ in plans)
     if args.copy_probe_mib:
@@ -197,7 +210,7 @@ def main():
     dom = max(groups, key=lambda k: groups[k]["us"])
     g = groups[dom]
     achieved = (g["flops"] / g["launches"]) / (g["us"] / g["launches"] * 1e-6) / 1e12
-    traffic = stored_traffic(dom) if args.workload == "alexnet" else None
+    traffic = stored_traffic(dom) if (args.workload == "alexnet" and args.op == "fprop") else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "kernel": dom, "launches_per_step": g["launches"],
@@ -205,7 +218,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(plans, args.cpu_seconds)
+        cpu = cpu_baseline(plans, args.cpu_seconds, args.op)
 
     line = {
         "metric": "effective conv TFLOP/s (2NKCRSPQ/t) per layer + % of MFMA peak, 1 MI355X",
@@ -220,7 +233,8 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded inputs with the workload's value distributions)",
-        "config": {"workload": wl_name, "global_batch": layers[0].N,
+        "config": {"workload": wl_name if args.op == "fprop" else wl_name + "_dgrad", "op": args.op,
+                   "global_batch": layers[0].N,
                    "layers": [l.name for l in layers], "gflop_per_step": round(flops_step / 1e9, 3),
                    "pct_mfma_peak": round(100 * value / peak, 1)},
         "roofline": roofline,
@@ -232,14 +246,22 @@ def main():
         plan.close()
 
 
-def cpu_baseline(plans, target_s):
+def run_oracle(op, lay, a, w):
+    """One oracle call on images a (x for the forward pass, dy for the data gradient)."""
+    import oracle
+    if op == "fprop":
+        return oracle.conv2d_fprop(a, w, lay.stride, lay.padding)
+    return oracle.conv2d_bwd_data(a, w, (a.shape[0],) + tuple(lay.x_shape[1:]), lay.stride, lay.padding)
+
+
+def cpu_baseline(plans, target_s, op="fprop"):
     """The oracle as it is, on the first n images of every layer of the step."""
     import oracle
     threads = oracle.default_threads()
     # calibrate on one image of the first layer, then size the sample
     lay, plan, (x, w) = plans[0]
     t0 = time.perf_counter()
-    oracle.conv2d_fprop(x[:1], w, lay.stride, lay.padding)
+    run_oracle(op, lay, x[:1], w)
     t1 = time.perf_counter() - t0
     per_image = t1 * sum(p.flops / l.N for l, p, _ in plans) / (plan.flops / lay.N)
     n_max = min(l.N for l, _, _ in plans)
@@ -252,7 +274,7 @@ def cpu_baseline(plans, target_s):
         if key in done:            # one oracle run per logical layer (layouts share values)
             continue
         done.add(key)
-        oracle.conv2d_fprop(x[:n_img], w, lay.stride, lay.padding)
+        run_oracle(op, lay, x[:n_img], w)
         flops += plan.flops * n_img / lay.N
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,

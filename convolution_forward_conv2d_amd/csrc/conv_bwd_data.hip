@@ -54,9 +54,17 @@ __global__ void __launch_bounds__(256) conv_bwd_data_direct_kernel(const ConvPar
 {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)p.M * p.C) return;
-    // consecutive threads take consecutive (n, h, w) rows for one channel c
-    const int c = (int)(idx / p.M);
-    const int m = (int)(idx - (int64_t)c * p.M);
+    // consecutive threads take consecutive (n, h, w) rows for one channel c,
+    // or, when dx is channel-innermost, consecutive channels of one row: the
+    // stores run along dx's unit stride and the threads of a row share dy
+    int c, m;
+    if (p.syk == 1) {
+        m = (int)(idx / p.C);
+        c = (int)(idx - (int64_t)m * p.C);
+    } else {
+        c = (int)(idx / p.M);
+        m = (int)(idx - (int64_t)c * p.M);
+    }
     uint32_t n, hw, h, w;
     p.div_pq.divmod((uint32_t)m, n, hw);
     p.div_q.divmod(hw, h, w);

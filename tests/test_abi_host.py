@@ -259,6 +259,8 @@ def test_dgrad_kernel_choice_host_only():
     for name in ("alexnet_conv2", "alexnet_conv3", "alexnet_conv4", "alexnet_conv5", "overfeat_l3",
                  "overfeat_l4", "overfeat_l5", "prec_conv3_f64_nchw", "prec_conv4_f64_nhwc"):
         assert names[name].startswith("dgrad_halo_f"), (name, names[name])
+    # onto 96 channels: the 96-wide tiles
+    assert names["alexnet_conv2"] == "dgrad_halo_f32x16_5x5_128x96"
     # strided layers and bf16 take the direct kernel
     for name in ("overfeat_l1", "speech_l1", "speech_l2", "prec_conv3_bf16_nchw"):
         assert names[name] == "dgrad_direct", (name, names[name])
