@@ -22,6 +22,15 @@
 // Method": outputs reorganised in shared memory for coalesced writes).
 // Nothing but x, w and y is touched in device memory: no workspace
 // (zero-memory direct-convolution page, Abstract).
+//
+// DG = true computes the data gradient (the adjoint of the forward sum in
+// x) for any stride, in tap order: rows m = (n, h, w) of dx, columns c,
+// reduction (k, r, s) with
+//   A[m, (k,r,s)] = dy[n, k, p, q] where p*u = h + pad_top - r and
+//                   q*v = w + pad_left - s (0 outside or off the stride grid)
+//   B[(k,r,s), c] = F[k, c, r, s]
+// The host passes C = the filter count, K = the channel count of dx,
+// H, W = dy's dims, P, Q = dx's dims, x = dy, y = dx.
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -35,7 +44,7 @@ namespace miconv {
 
 // ------------------------------------------------------------------ the kernel
 
-template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int TK, bool BVEC, bool TAP>
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int TK, bool BVEC, bool TAP, bool DG>
 __global__ void __launch_bounds__(256)
 conv_fwd_mfma_kernel(const ConvParams p)
 {
@@ -67,6 +76,7 @@ conv_fwd_mfma_kernel(const ConvParams p)
     static_assert((A_EPT * (int)sizeof(In)) % 4 == 0 && (B_EPT * (int)sizeof(In)) % 4 == 0,
                   "loader slices must be whole words");
     static_assert(4 * BM * (BM + 1) * (int)sizeof(Acc) <= 2 * BUF_BYTES, "epilogue stage fits");
+    static_assert(!DG || TAP, "the data gradient runs in tap order");
     constexpr int A_WORDS = A_EPT * (int)sizeof(In) / 4;
     constexpr int B_WORDS = B_EPT * (int)sizeof(In) / 4;
 
@@ -95,9 +105,16 @@ conv_fwd_mfma_kernel(const ConvParams p)
             uint32_t n, pq, pp, q;
             p.div_pq.divmod((uint32_t)m, n, pq);
             p.div_q.divmod(pq, pp, q);
-            hb = (int)pp * p.u - p.pad_top;
-            wb = (int)q * p.v - p.pad_left;
-            abase = (int)n * p.sxn + hb * p.sxh + wb * p.sxw;
+            if constexpr (DG) {
+                // (pp, q) is the dx position (h, w): keep h + pad_top, w + pad_left
+                hb = (int)pp + p.pad_top;
+                wb = (int)q + p.pad_left;
+                abase = (int)n * p.sxn;
+            } else {
+                hb = (int)pp * p.u - p.pad_top;
+                wb = (int)q * p.v - p.pad_left;
+                abase = (int)n * p.sxn + hb * p.sxh + wb * p.sxw;
+            }
         } else {
             hb = -0x40000000;      // every h = hb + r falls outside [0, H): row reads as zeros
             wb = 0;
@@ -108,7 +125,8 @@ conv_fwd_mfma_kernel(const ConvParams p)
     const int b_row = tid % TN;
     const int b_seg = tid / TN;
     const bool b_ok = (n0 + b_row) < p.K;
-    const In* __restrict__ wrow = w + (size_t)(b_ok ? n0 + b_row : 0) * (size_t)p.Kred;
+    // (DG: column c's filter values F[k, c, :, :] start at c*R*S, filter k at k*K*R*S)
+    const In* __restrict__ wrow = w + (size_t)(b_ok ? n0 + b_row : 0) * (size_t)(DG ? p.R * p.S : p.Kred);
 
     In a_val[A_EPT];
     In b_val[B_EPT];
@@ -127,6 +145,24 @@ conv_fwd_mfma_kernel(const ConvParams p)
     };
 
     auto load_a = [&](int ch) {
+        if constexpr (DG) {
+            int k0, r, s;
+            tap_of(ch, k0, r, s);
+            k0 += a_seg * A_EPT;                     // wave-uniform
+            const int hh = hb - r, ww = wb - s;      // p*u and q*v if on the stride grid
+            uint32_t pp = 0, qq = 0;
+            bool tap_ok = hh >= 0 && ww >= 0;
+            if (tap_ok) {
+                pp = p.div_u.div((uint32_t)hh);
+                qq = p.div_v.div((uint32_t)ww);
+                tap_ok = (int)pp * p.u == hh && (int)qq * p.v == ww && (int)pp < p.H && (int)qq < p.W;
+            }
+            const In* src = x + (abase + k0 * p.sxc + (int)pp * p.sxh + (int)qq * p.sxw);
+#pragma unroll
+            for (int j = 0; j < A_EPT; ++j)
+                a_val[j] = (tap_ok && k0 + j < p.C) ? load_elem(src + j * p.sxc) : In(0);
+            return;
+        }
         if constexpr (TAP) {
             int c0, r, s;
             tap_of(ch, c0, r, s);
@@ -157,6 +193,17 @@ conv_fwd_mfma_kernel(const ConvParams p)
     };
 
     auto load_b = [&](int ch) {
+        if constexpr (DG) {
+            int k0, r, s;
+            tap_of(ch, k0, r, s);
+            k0 += b_seg * B_EPT;
+            const int rs = p.R * p.S;
+            const In* src = wrow + (size_t)k0 * p.K * rs + r * p.S + s;
+#pragma unroll
+            for (int j = 0; j < B_EPT; ++j)
+                b_val[j] = (b_ok && k0 + j < p.C) ? load_elem(src + (size_t)j * p.K * rs) : In(0);
+            return;
+        }
         if constexpr (TAP) {
             int c0, r, s;
             tap_of(ch, c0, r, s);
@@ -264,7 +311,7 @@ conv_fwd_mfma_kernel(const ConvParams p)
 // ------------------------------------------------------------------ instances and launch
 
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int TK>
-static hipError_t launch_variant(const ConvParams& p0, bool bvec, bool tap, hipStream_t stream)
+static hipError_t launch_variant(const ConvParams& p0, bool bvec, bool tap, bool dgrad, hipStream_t stream)
 {
     ConvParams p = p0;
     p.m_tiles = (p.M + TM - 1) / TM;
@@ -274,14 +321,17 @@ static hipError_t launch_variant(const ConvParams& p0, bool bvec, bool tap, hipS
     constexpr int B_EPT = TK * TN / 256;
     constexpr bool CAN_VEC = (B_EPT * (int)sizeof(typename Pol::In)) % 16 == 0;
     if constexpr (!CAN_VEC) bvec = false;
-    if (tap)
-        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, true>),
+    if (dgrad)
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, true, true>),
+                           grid, dim3(256), 0, stream, p);
+    else if (tap)
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, true, false>),
                            grid, dim3(256), 0, stream, p);
     else if (bvec)
-        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, CAN_VEC, false>),
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, CAN_VEC, false, false>),
                            grid, dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, false>),
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, false, false>),
                            grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
@@ -299,11 +349,11 @@ static hipError_t launch_variant(const ConvParams& p0, bool bvec, bool tap, hipS
     X(MFMA_BF16_128x64, PolBF16, 128, 64, 2, 2, 32)          \
     X(MFMA_BF16_256x32, PolBF16, 256, 32, 4, 1, 32)
 
-hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, bool tap, hipStream_t stream)
+hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, bool tap, bool dgrad, hipStream_t stream)
 {
     switch (v) {
 #define X(name, pol, tm, tn, wmm, wnn, tk) \
-    case Variant::name: return launch_variant<pol, tm, tn, wmm, wnn, tk>(p, bvec, tap, stream);
+    case Variant::name: return launch_variant<pol, tm, tn, wmm, wnn, tk>(p, bvec, tap, dgrad, stream);
         MICONV_VARIANTS(X)
 #undef X
     default: return hipErrorInvalidValue;

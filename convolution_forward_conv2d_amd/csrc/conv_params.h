@@ -57,6 +57,7 @@ struct ConvParams {
     int m_tiles, n_tiles;
     int m_step;          // output rows per m tile (halo kernel: TM, or P*Q for one image per tile)
     FastDiv div_pq, div_q, div_rs, div_s, div_hp;
+    FastDiv div_u, div_v;   // by the strides (data-gradient gather kernel)
     double alpha, beta;  // converted to the accumulation type inside the kernel
 };
 

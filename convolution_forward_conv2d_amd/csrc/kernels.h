@@ -43,7 +43,9 @@ enum class DType : int { F32 = 0, F64 = 1, BF16 = 2 };
 // Launch an implicit-GEMM MFMA variant.  bvec: the filter may be read with
 // 16-byte loads (w 16-byte aligned and C*R*S a multiple of the vector).
 // tap: reduction in channel blocks per filter tap instead of flat KCRS order.
-hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, bool tap, hipStream_t stream);
+// dgrad: the data gradient, any stride (p laid out as conv_fwd_mfma.hip
+// describes).
+hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, bool tap, bool dgrad, hipStream_t stream);
 
 // Launch a tap-batched halo variant (the host has checked its eligibility).
 // dgrad: p describes the forward problem equivalent to a stride-1 data

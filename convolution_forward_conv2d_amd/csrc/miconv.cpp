@@ -349,6 +349,8 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
     p.div_s = FastDiv((uint32_t)wd->s);
     p.Hp = xd->h + cd->pad_top + cd->pad_bottom;
     p.div_hp = FastDiv((uint32_t)p.Hp);
+    p.div_u = FastDiv((uint32_t)p.u);
+    p.div_v = FastDiv((uint32_t)p.v);
     p.alpha = alpha;
     p.beta = beta;
     const int Wp = xd->w + cd->pad_left + cd->pad_right;
@@ -510,6 +512,8 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
     p.alpha = alpha;
     p.beta = beta;
     pl.cand = kDirect;
+    const char* forced_dgrad_name = getenv("MIC_FORCE_DGRAD_VARIANT");
+    if (forced_dgrad_name && !forced_dgrad_name[0]) forced_dgrad_name = nullptr;
 
     // the equivalent forward problem of a stride-1 data gradient: input dy
     // (C' = K channels, H' x W' = P x Q), K' = C filters, padding R-1-pad_top
@@ -535,14 +539,12 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
         v.Kred = (int)((int64_t)k * RS);
         const int Wp = Q + v.pad_left + pr2;
         const int num_cu = h ? h->num_cu : kDefaultCUs;
-        const char* force = getenv("MIC_FORCE_DGRAD_VARIANT");
-        const bool forced = force && force[0];
         double best = 0;
         bool found = false;
         for (const HaloCandidate& hc : kHalo) {
             double cost;
             int step;
-            if (forced && strcmp(force, hc.c.name) != 0) continue;
+            if (forced_dgrad_name && strcmp(forced_dgrad_name, hc.c.name) != 0) continue;
             if (!halo_eligible(hc, pl.dt, v, w, need_pointers, true)) continue;
             if (!halo_cost(hc, v, Wp, num_cu, &cost, &step)) continue;
             if (!found || cost < best) {
@@ -555,24 +557,53 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
         if (found) p = v;
     }
     if (pl.cand.v == Variant::DIRECT) {
-        // direct kernel layout (conv_bwd_data.hip)
-        p.C = C;
-        p.H = H;
-        p.W = W;
-        p.K = k;
-        p.P = P;
-        p.Q = Q;
-        p.u = cd->u;
-        p.v = cd->v;
-        p.pad_top = pt;
-        p.pad_left = pl_;
-        p.Kred = (int)((int64_t)C * RS);
-    }
-    if (const char* force = getenv("MIC_FORCE_DGRAD_VARIANT")) {
-        if (force[0] && strcmp(force, pl.cand.name) != 0) {
-            pl.status = MIC_STATUS_NOT_SUPPORTED;   // the forced variant does not fit this problem
-            return pl;
+        // no halo instance: the gather kernel in data-gradient mode (any
+        // stride), laid out as conv_fwd_mfma.hip describes; the direct kernel
+        // (conv_bwd_data.hip) when forced, or onto fewer than 16 channels,
+        // where the gather kernel's tiles would be almost empty (measured on
+        // MI355X: 1 channel 5.2 ms direct vs 36 ms gathered, 3 channels 8 vs 53)
+        const bool direct = forced_dgrad_name ? strcmp(forced_dgrad_name, kDirect.name) == 0 : C < 16;
+        if (!direct) {
+            p.C = k;
+            p.K = C;
+            p.H = P;
+            p.W = Q;
+            p.P = H;
+            p.Q = W;
+            p.u = cd->u;
+            p.v = cd->v;
+            p.div_u = FastDiv((uint32_t)cd->u);
+            p.div_v = FastDiv((uint32_t)cd->v);
+            p.pad_top = pt;
+            p.pad_left = pl_;
+            p.Kred = (int)((int64_t)k * RS);
+            const int num_cu = h ? h->num_cu : kDefaultCUs;
+            pl.cand = choose_tile(pl.dt, p.M, p.K, num_cu);
+            if (forced_dgrad_name) {
+                const Candidate* list;
+                int count;
+                candidates(pl.dt, &list, &count);
+                for (int i = 0; i < count; ++i)
+                    if (strcmp(forced_dgrad_name, list[i].name) == 0) pl.cand = list[i];
+            }
+        } else {
+            // direct kernel layout (conv_bwd_data.hip)
+            p.C = C;
+            p.H = H;
+            p.W = W;
+            p.K = k;
+            p.P = P;
+            p.Q = Q;
+            p.u = cd->u;
+            p.v = cd->v;
+            p.pad_top = pt;
+            p.pad_left = pl_;
+            p.Kred = (int)((int64_t)C * RS);
         }
+    }
+    if (forced_dgrad_name && strcmp(forced_dgrad_name, pl.cand.name) != 0) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;   // the forced variant does not fit this problem
+        return pl;
     }
     snprintf(pl.name, sizeof(pl.name), "dgrad_%s", pl.cand.name);
     pl.status = MIC_STATUS_SUCCESS;
@@ -817,7 +848,7 @@ mic_status mic_conv_forward(mic_handle handle, double alpha, mic_tensor_desc x_d
     else if (is_halo(pl.cand.v))
         err = miconv::launch_halo(pl.cand.v, pl.p, false, handle->stream);
     else
-        err = miconv::launch_mfma(pl.cand.v, pl.p, pl.bvec, pl.tap, handle->stream);
+        err = miconv::launch_mfma(pl.cand.v, pl.p, pl.bvec, pl.tap, false, handle->stream);
     return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
 }
 
@@ -831,8 +862,10 @@ mic_status mic_conv_backward_data(mic_handle handle, double alpha, mic_filter_de
     hipError_t err;
     if (pl.cand.v == Variant::DIRECT)
         err = miconv::launch_bwd_data_direct(pl.dt, pl.p, handle->stream);
-    else
+    else if (is_halo(pl.cand.v))
         err = miconv::launch_halo(pl.cand.v, pl.p, true, handle->stream);
+    else
+        err = miconv::launch_mfma(pl.cand.v, pl.p, false, true, true, handle->stream);
     return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
 }
 

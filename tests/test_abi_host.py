@@ -261,8 +261,11 @@ def test_dgrad_kernel_choice_host_only():
         assert names[name].startswith("dgrad_halo_f"), (name, names[name])
     # onto 96 channels: the 96-wide tiles
     assert names["alexnet_conv2"] == "dgrad_halo_f32x16_5x5_128x96"
-    # strided layers and bf16 take the direct kernel
-    for name in ("overfeat_l1", "speech_l1", "speech_l2", "prec_conv3_bf16_nchw"):
+    # strided layers and bf16 take the gather kernel in data-gradient mode,
+    # gradients onto 1 or 3 channels the direct kernel
+    for name in ("speech_l2", "prec_conv3_bf16_nchw", "prec_conv5_bf16_nhwc"):
+        assert names[name].startswith("dgrad_mfma_"), (name, names[name])
+    for name in ("overfeat_l1", "speech_l1"):
         assert names[name] == "dgrad_direct", (name, names[name])
 
 

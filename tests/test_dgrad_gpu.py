@@ -31,6 +31,10 @@ DG_VARIANTS = {
     "f64": ["direct", "halo_f64_3x3_128x128", "halo_f64_3x3_64x64"],
     "bf16": ["direct"],
 }
+# the gather kernel in data-gradient mode (any stride)
+DG_VARIANTS["f32"] += ["mfma_f32_128x128", "mfma_f32_128x64", "mfma_f32_64x128", "mfma_f32_256x32"]
+DG_VARIANTS["f64"] += ["mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64"]
+DG_VARIANTS["bf16"] += ["mfma_bf16_128x128", "mfma_bf16_128x64", "mfma_bf16_256x32"]
 _ran = set()
 
 # the forward shapes, plus a 5x5 one whose filter count (the data gradient's
