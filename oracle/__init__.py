@@ -1,5 +1,5 @@
-"""CPU oracle for the 2-D convolution forward pass and its data gradient (fp64,
-plain 7-nested loops).
+"""CPU oracle for the 2-D convolution forward pass and its data and filter
+gradients (fp64, plain 7-nested loops).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
@@ -71,6 +71,9 @@ def _load():
         lib.oracle_conv2d_bwd_data_at.argtypes = [pp, dp, ip, dp, ctypes.c_double, ctypes.c_double,
                                                   dp, ip, ctypes.c_int64, dp, dp, ctypes.c_int]
         lib.oracle_conv2d_bwd_data_at.restype = ctypes.c_int
+        lib.oracle_conv2d_bwd_filter.argtypes = [pp, dp, dp, ip, ctypes.c_double, ctypes.c_double,
+                                                 dp, dp, dp, ctypes.c_int]
+        lib.oracle_conv2d_bwd_filter.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
@@ -237,3 +240,34 @@ def conv2d_bwd_data_at(dy, w, x_shape, idx, stride=(1, 1), padding=(0, 0, 0, 0),
     if rc != 0:
         raise ValueError("oracle rejected the problem or a coordinate")
     return dx, bound
+
+
+def conv2d_bwd_filter(x, dy, w_shape, stride=(1, 1), padding=(0, 0, 0, 0), alpha=1.0, beta=0.0,
+                      dw_old=None, nthreads=0):
+    """Whole filter gradient of the forward convolution of x with a (K, C, R, S) filter.
+
+    x: float64 (N, C, H, W) and dy: float64 (N, K, P, Q), any non-negative strides.
+    Returns (dw, bound), both float64 packed (K, C, R, S).
+    """
+    xb, xs = _input_view(x)
+    db, ds = _input_view(dy)
+    pb = make_problem(x.shape, xs, tuple(w_shape), stride, padding)
+    P, Q = output_dims(pb)
+    if tuple(dy.shape) != (x.shape[0], w_shape[0], P, Q):
+        raise ValueError("dy shape %s != forward output shape %s" % (tuple(dy.shape), (x.shape[0], w_shape[0], P, Q)))
+    sdy = np.asarray(ds, dtype=np.int64)
+    dw = np.empty(tuple(w_shape), dtype=np.float64)
+    bound = np.empty(tuple(w_shape), dtype=np.float64)
+    wo = None
+    if beta != 0.0:
+        if dw_old is None:
+            raise ValueError("beta != 0 needs dw_old")
+        wo = np.ascontiguousarray(dw_old, dtype=np.float64)
+        if wo.shape != dw.shape:
+            raise ValueError("dw_old shape %s != filter shape %s" % (wo.shape, dw.shape))
+    rc = _load().oracle_conv2d_bwd_filter(
+        ctypes.byref(pb), _dptr(xb), _dptr(db), sdy.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        float(alpha), float(beta), _dptr(wo), _dptr(dw), _dptr(bound), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return dw, bound

@@ -1,6 +1,6 @@
 /*
  * oracle/conv_oracle.c -- plain CPU reference for the 2-D convolution forward
- * pass (FPROP) and its data gradient (backward pass with respect to x).  TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and
+ * pass (FPROP) and its gradients (backward passes with respect to x and F).  TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and
  * the CPU-baseline leg of the benchmark may load this library.  It shares no
  * code, header, table or helper with the GPU path.
  *
@@ -287,6 +287,79 @@ int oracle_conv2d_bwd_data_at(const oracle_conv_problem* pb,
         if (beta != 0.0) val += beta * dx_old_vals[i];
         if (dx) dx[i] = val;
         if (bound) bound[i] = bnd;
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/*
+ * Backward pass with respect to the filter (filter gradient): the gradient
+ * of the forward sum with respect to F, i.e. its adjoint in F (same reading
+ * as the data gradient above; the pages print no formula):
+ *
+ *   dacc[k,c,r,s] = sum_{n<N} sum_{p<P} sum_{q<Q}  dY(n, k, p, q) * X(n, c, p*u + r - pad_top,
+ *                                                                         q*v + s - pad_left)
+ *   dw[k,c,r,s]   = alpha * dacc + beta * dw_old[k,c,r,s]   (dw_old unread if beta == 0)
+ *   B[k,c,r,s]    = sum of |dY * X| over the same terms     (error-bound weight)
+ *
+ * X is x read through the problem's element strides with zero padding, dY
+ * is dy read through sdy[4]; dw is packed K,C,R,S.  Accumulated in double in
+ * the fixed order n, p, q.
+ */
+static void one_wgrad(const oracle_conv_problem* pb, int64_t P, int64_t Q,
+                      const double* x, const double* dy, const int64_t* sdy,
+                      int64_t k, int64_t c, int64_t r, int64_t s,
+                      double* acc_out, double* bound_out)
+{
+    double acc = 0.0, bound = 0.0;
+    for (int64_t n = 0; n < pb->N; ++n) {
+        for (int64_t p = 0; p < P; ++p) {
+            for (int64_t q = 0; q < Q; ++q) {
+                double xv = input_at(pb, x, n, c, p * pb->u + r - pb->pad_top, q * pb->v + s - pb->pad_left);
+                double dv = dy[n * sdy[0] + k * sdy[1] + p * sdy[2] + q * sdy[3]];
+                double prod = dv * xv;
+                acc += prod;
+                bound += fabs(prod);
+            }
+        }
+    }
+    *acc_out = acc;
+    *bound_out = bound;
+}
+
+/*
+ * Whole filter gradient.  dw and bound (either may be NULL) are packed
+ * K,C,R,S; dw_old is packed K,C,R,S and read only when beta != 0.  x is read
+ * through the problem's strides, dy through sdy[4] (n, k, p, q).
+ * Returns 0, or -1 on a bad problem.
+ */
+int oracle_conv2d_bwd_filter(const oracle_conv_problem* pb,
+                             const double* x, const double* dy, const int64_t* sdy,
+                             double alpha, double beta, const double* dw_old,
+                             double* dw, double* bound, int nthreads)
+{
+    int64_t P, Q;
+    if (oracle_output_dims(pb, &P, &Q) != 0) return -1;
+    if (beta != 0.0 && dw_old == NULL) return -1;
+    const int64_t K = pb->K, C = pb->C, R = pb->R, S = pb->S;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t c = 0; c < C; ++c) {
+            for (int64_t r = 0; r < R; ++r) {
+                for (int64_t s = 0; s < S; ++s) {
+                    double acc, bnd;
+                    one_wgrad(pb, P, Q, x, dy, sdy, k, c, r, s, &acc, &bnd);
+                    int64_t o = ((k * C + c) * R + r) * S + s;
+                    double val = alpha * acc;
+                    if (beta != 0.0) val += beta * dw_old[o];
+                    if (dw) dw[o] = val;
+                    if (bound) bound[o] = bnd;
+                }
+            }
+        }
     }
     (void)nthreads;
     return 0;

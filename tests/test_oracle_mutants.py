@@ -48,6 +48,18 @@ MUTANTS_DGRAD = {
     "dgrad_beta_dropped": ("val += beta * dx_old[o];", "val += 0.0 * dx_old[o];"),
 }
 
+# slips in the filter-gradient code, caught by test_oracle_wgrad.py
+MUTANTS_WGRAD = {
+    "wgrad_pad_sign": ("n, c, p * pb->u + r - pb->pad_top, q * pb->v", "n, c, p * pb->u + r + pb->pad_top, q * pb->v"),
+    "wgrad_tap_flipped": ("q * pb->v + s - pb->pad_left);\n                double dv", "q * pb->v - s - pb->pad_left);\n                double dv"),
+    "wgrad_strides_swapped": ("n, c, p * pb->u + r - pb->pad_top, q * pb->v", "n, c, p * pb->v + r - pb->pad_top, q * pb->u"),
+    "wgrad_first_image_dropped": ("for (int64_t n = 0; n < pb->N; ++n) {\n        for (int64_t p = 0; p < P; ++p) {",
+                                  "for (int64_t n = 1; n < pb->N; ++n) {\n        for (int64_t p = 0; p < P; ++p) {"),
+    "wgrad_r_s_swapped_in_output": ("int64_t o = ((k * C + c) * R + r) * S + s;", "int64_t o = ((k * C + c) * S + s) * R + r;"),
+    "wgrad_beta_dropped": ("val += beta * dw_old[o];", "val += 0.0 * dw_old[o];"),
+    "wgrad_last_column_dropped": ("for (int64_t q = 0; q < Q; ++q) {\n                double xv", "for (int64_t q = 0; q < Q - 1; ++q) {\n                double xv"),
+}
+
 
 def _build_and_run(name, old, new, tmp, pins="test_oracle.py"):
     with open(SRC) as fh:
@@ -70,6 +82,7 @@ def _build_and_run(name, old, new, tmp, pins="test_oracle.py"):
 def test_every_mutant_is_caught():
     jobs = [(n, o, w, "test_oracle.py") for n, (o, w) in MUTANTS.items()]
     jobs += [(n, o, w, "test_oracle_dgrad.py") for n, (o, w) in MUTANTS_DGRAD.items()]
+    jobs += [(n, o, w, "test_oracle_wgrad.py") for n, (o, w) in MUTANTS_WGRAD.items()]
     with tempfile.TemporaryDirectory() as tmp:
         with ThreadPoolExecutor(max_workers=4) as pool:
             results = list(pool.map(lambda j: _build_and_run(j[0], j[1], j[2], tmp, j[3]), jobs))
