@@ -8,15 +8,16 @@ one kernel launch of libmiconv through the C ABI.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
                     [--workload alexnet|overfeat|speech|tiny|prec_f64|prec_bf16]
-                    [--op fprop|dgrad]
+                    [--op fprop|dgrad|wgrad]
 
 Prints one JSON line.  ``value`` = 2*N*K*C*R*S*P*Q summed over the step's
 layers / mean step time (inputs resident in HBM, no host traffic inside
 the timed region).  ``roofline`` covers the kernel with the most time per
 step, timed with HIP events on the stream it runs on.  ``cpu_baseline``
 times the CPU oracle on a bounded sample of the same workload (the first
-few images of every layer).  ``--op dgrad`` times the data gradient of the
-same layers instead (dy seeded uniform [-1, 1]; the same FLOP count).
+few images of every layer).  ``--op dgrad`` / ``--op wgrad`` time the data /
+filter gradient of the same layers instead (dy seeded uniform [-1, 1]; the
+same FLOP count).
 """
 import argparse
 import hashlib
@@ -40,8 +41,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="alexnet", choices=WORKLOADS)
-    ap.add_argument("--op", default="fprop", choices=("fprop", "dgrad"),
-                    help="forward pass (default) or data gradient of the workload's layers")
+    ap.add_argument("--op", default="fprop", choices=("fprop", "dgrad", "wgrad"),
+                    help="forward pass (default), data gradient or filter gradient of the layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -149,6 +150,12 @@ def main():
             yt = torch.zeros(workloads.storage_elems(N, K, P, Q, yst), dtype=out_dt,
                              device=dev).as_strided((N, K, P, Q), yst)
             plans.append((lay, mic.ConvPlan(xt, wt, yt, lay.stride, lay.padding), (x, w)))
+        elif args.op == "wgrad":
+            xt = upload(x, dtype, lay.layout, lay.row_pitch, dev)
+            dy = gen.round_to(gen.uniform(gen.derive_seed(lay.config, lay.layer, 3), (N, K, P, Q)), dtype)
+            dyt = upload(dy, dtype, lay.layout, lay.row_pitch, dev)
+            dwt = torch.zeros(lay.w_shape, dtype=out_dt, device=dev)
+            plans.append((lay, mic.WgradPlan(xt, dyt, dwt, lay.stride, lay.padding), (x, dy)))
         else:
             dy = gen.round_to(gen.uniform(gen.derive_seed(lay.config, lay.layer, 3), (N, K, P, Q)), dtype)
             dyt = upload(dy, dtype, lay.layout, lay.row_pitch, dev)
@@ -233,7 +240,7 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded inputs with the workload's value distributions)",
-        "config": {"workload": wl_name if args.op == "fprop" else wl_name + "_dgrad", "op": args.op,
+        "config": {"workload": wl_name if args.op == "fprop" else wl_name + "_" + args.op, "op": args.op,
                    "global_batch": layers[0].N,
                    "layers": [l.name for l in layers], "gflop_per_step": round(flops_step / 1e9, 3),
                    "pct_mfma_peak": round(100 * value / peak, 1)},
@@ -251,6 +258,8 @@ def run_oracle(op, lay, a, w):
     import oracle
     if op == "fprop":
         return oracle.conv2d_fprop(a, w, lay.stride, lay.padding)
+    if op == "wgrad":       # (a, w) = (x, dy) images
+        return oracle.conv2d_bwd_filter(a, w[:a.shape[0]], lay.w_shape, lay.stride, lay.padding)
     return oracle.conv2d_bwd_data(a, w, (a.shape[0],) + tuple(lay.x_shape[1:]), lay.stride, lay.padding)
 
 

@@ -6,7 +6,8 @@ kernels of ``libmiconv.so`` behind the C ABI declared in
 ``include/miconv.h``.  PyTorch supplies device memory and the stream.
 The ``mic_*`` functions mirror the C calls one for one (descriptors are
 ctypes handles); ``conv2d_forward`` / ``ConvPlan`` and
-``conv2d_backward_data`` / ``DgradPlan`` wrap them for torch tensors.
+``conv2d_backward_data`` / ``DgradPlan`` and ``conv2d_backward_filter`` /
+``WgradPlan`` wrap them for torch tensors.
 
 There is no fallback: if the library is missing the import fails.
 """
@@ -84,6 +85,10 @@ _SIGS = {
                                 _vp, _vp], _i),
     "mic_conv_backward_data_kernel_name": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_char_p, ctypes.c_size_t],
                                            _i),
+    "mic_conv_backward_filter": ([_vp, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, ctypes.c_double,
+                                  _vp, _vp], _i),
+    "mic_conv_backward_filter_kernel_name": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_char_p, ctypes.c_size_t],
+                                             _i),
 }
 
 
@@ -247,6 +252,18 @@ def mic_conv_backward_data_kernel_name(handle, w_desc, dy_desc, conv, dx_desc):
     buf = ctypes.create_string_buffer(128)
     _check(lib().mic_conv_backward_data_kernel_name(handle, w_desc, dy_desc, conv, dx_desc, buf, 128),
            "mic_conv_backward_data_kernel_name")
+    return buf.value.decode()
+
+
+def mic_conv_backward_filter(handle, alpha, x_desc, x_ptr, dy_desc, dy_ptr, conv, beta, dw_desc, dw_ptr):
+    _check(lib().mic_conv_backward_filter(handle, float(alpha), x_desc, _vp(x_ptr), dy_desc, _vp(dy_ptr),
+                                          conv, float(beta), dw_desc, _vp(dw_ptr)), "mic_conv_backward_filter")
+
+
+def mic_conv_backward_filter_kernel_name(handle, x_desc, dy_desc, conv, dw_desc):
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().mic_conv_backward_filter_kernel_name(handle, x_desc, dy_desc, conv, dw_desc, buf, 128),
+           "mic_conv_backward_filter_kernel_name")
     return buf.value.decode()
 
 
@@ -427,3 +444,74 @@ def conv2d_backward_data(dy, w, x_shape, stride=(1, 1), padding=(0, 0, 0, 0), dx
     finally:
         plan.close()
     return dx
+
+
+class WgradPlan:
+    """Descriptors for one filter-gradient call (x, dy -> dw), reusable.
+
+    x: (N, C, H, W) and dy: (N, K, P, Q) tensors of any strides;
+    dw: contiguous (K, C, R, S) (fp32 for bf16 inputs).
+    """
+
+    def __init__(self, x, dy, dw, stride=(1, 1), padding=(0, 0, 0, 0), handle=None):
+        if x.dim() != 4 or dy.dim() != 4 or dw.dim() != 4:
+            raise ValueError("x, dy, dw must be 4-D")
+        if not dw.is_contiguous():
+            raise ValueError("dw must be packed K,C,R,S (contiguous)")
+        for t in (x, dy, dw):
+            if t.dtype not in _TORCH_DTYPE:
+                raise TypeError("unsupported dtype %s" % t.dtype)
+        self.x, self.dy, self.dw = x, dy, dw
+        self.handle = handle if handle is not None else handle_for(x.device)
+        self.xd, self.dyd, self.wd = mic_tensor_desc_create(), mic_tensor_desc_create(), mic_filter_desc_create()
+        self.cd = mic_conv_desc_create()
+        mic_tensor_desc_set(self.xd, _TORCH_DTYPE[x.dtype], *x.shape, *_element_strides(x))
+        mic_tensor_desc_set(self.dyd, _TORCH_DTYPE[dy.dtype], *dy.shape, *_element_strides(dy))
+        mic_filter_desc_set(self.wd, _TORCH_DTYPE[dw.dtype], *dw.shape)
+        mic_conv_desc_set(self.cd, *padding, *stride)
+        # the forward pass's multiply-adds, counted once each
+        self.flops = 2.0 * dy.shape[0] * dy.shape[1] * dy.shape[2] * dy.shape[3] * dw.shape[1] * dw.shape[2] * dw.shape[3]
+
+    def kernel_name(self):
+        return mic_conv_backward_filter_kernel_name(self.handle, self.xd, self.dyd, self.cd, self.wd)
+
+    def __call__(self, alpha=1.0, beta=0.0, stream=None):
+        s = stream if stream is not None else torch.cuda.current_stream(self.x.device)
+        mic_set_stream(self.handle, s.cuda_stream)
+        mic_conv_backward_filter(self.handle, alpha, self.xd, self.x.data_ptr(), self.dyd, self.dy.data_ptr(),
+                                 self.cd, beta, self.wd, self.dw.data_ptr())
+        return self.dw
+
+    def close(self):
+        for d, fn in ((self.xd, mic_tensor_desc_destroy), (self.dyd, mic_tensor_desc_destroy),
+                      (self.wd, mic_filter_desc_destroy), (self.cd, mic_conv_desc_destroy)):
+            if d is not None:
+                fn(d)
+        self.xd = self.dyd = self.wd = self.cd = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def conv2d_backward_filter(x, dy, w_shape, stride=(1, 1), padding=(0, 0, 0, 0), dw=None, alpha=1.0,
+                           beta=0.0):
+    """dw <- alpha * wgrad(x, dy) + beta * dw on torch's current stream.
+
+    w_shape is the filter's (K, C, R, S); with dw None a new packed one is
+    allocated (caller memory; fp32 for bf16 inputs) and beta must be 0.
+    """
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    if dw is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing dw")
+        dw = torch.empty(tuple(w_shape), dtype=_OUT_DTYPE[x.dtype], device=x.device)
+    plan = WgradPlan(x, dy, dw, stride, padding)
+    try:
+        plan(alpha, beta)
+    finally:
+        plan.close()
+    return dw

@@ -58,6 +58,9 @@ struct ConvParams {
     int m_step;          // output rows per m tile (halo kernel: TM, or P*Q for one image per tile)
     FastDiv div_pq, div_q, div_rs, div_s, div_hp;
     FastDiv div_u, div_v;   // by the strides (data-gradient gather kernel)
+    // filter gradient: dy's element strides and division by P*Q and by Q
+    int sdn, sdk, sdp, sdq;
+    FastDiv div_opq, div_oq;
     double alpha, beta;  // converted to the accumulation type inside the kernel
 };
 

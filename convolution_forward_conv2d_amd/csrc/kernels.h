@@ -35,6 +35,14 @@ enum class Variant : int {
     HALO_BF16_3x3_128x128,  // bf16 halo kernel, channel-innermost LDS (conv_fwd_halo_bf16.hip)
     HALO_BF16_3x3_128x64,
     HALO_BF16_3x3_192x128,
+    WG_F32_128x128,         // filter gradient (conv_bwd_filter.hip)
+    WG_F32_64x128,
+    WG_F32_128x64,
+    WG_F32_64x64,
+    WG_F64_128x64,
+    WG_F64_64x64,
+    WG_BF16_128x128,
+    WG_BF16_64x64,
     COUNT
 };
 
@@ -55,6 +63,10 @@ hipError_t launch_halo_bf16(Variant v, const ConvParams& p, hipStream_t stream);
 
 // Launch the plain direct kernel (one thread per output element).
 hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);
+
+// Filter gradient (implicit GEMM over the output positions); p laid out as
+// conv_bwd_filter.hip describes.
+hipError_t launch_bwd_filter(Variant v, const ConvParams& p, hipStream_t stream);
 
 // Data gradient, plain direct kernel (one thread per dx element); p is laid
 // out as conv_bwd_data.hip describes.

@@ -114,6 +114,21 @@ const Candidate kBF16[] = {
     {Variant::MFMA_BF16_256x32, 256, 32, "mfma_bf16_256x32"},
 };
 const Candidate kDirect = {Variant::DIRECT, 0, 0, "direct"};
+// filter gradient (conv_bwd_filter.hip)
+const Candidate kWgF32[] = {
+    {Variant::WG_F32_128x128, 128, 128, "wg_f32_128x128"},
+    {Variant::WG_F32_64x128, 64, 128, "wg_f32_64x128"},
+    {Variant::WG_F32_128x64, 128, 64, "wg_f32_128x64"},
+    {Variant::WG_F32_64x64, 64, 64, "wg_f32_64x64"},
+};
+const Candidate kWgF64[] = {
+    {Variant::WG_F64_128x64, 128, 64, "wg_f64_128x64"},
+    {Variant::WG_F64_64x64, 64, 64, "wg_f64_64x64"},
+};
+const Candidate kWgBF16[] = {
+    {Variant::WG_BF16_128x128, 128, 128, "wg_bf16_128x128"},
+    {Variant::WG_BF16_64x64, 64, 64, "wg_bf16_64x64"},
+};
 
 // Tap-batched halo kernels (conv_fwd_halo.hip): fixed R x S, CB channels per
 // chunk, padded input width <= WP, per-tile slot span <= SL.
@@ -610,6 +625,129 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
     return pl;
 }
 
+// ---------------------------------------------------------------- filter gradient
+
+// dw <- alpha * wgrad(x, dy) + beta * dw for the forward geometry (x, dw,
+// conv); dy must have the forward output's dims.  One kernel family
+// (conv_bwd_filter.hip); the tile shape by the quantisation cost model over
+// the dw tiles (the reduction over positions is not split: no workspace).
+Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void* x,
+                     const mic_tensor_desc_st* dyd, const void* dy, const mic_conv_desc_st* cd,
+                     const mic_filter_desc_st* wd, const void* dw, double alpha, double beta,
+                     bool need_pointers)
+{
+    Plan pl;
+    memset(&pl, 0, sizeof(pl));
+    pl.status = MIC_STATUS_BAD_PARAM;
+    if (!xd || !dyd || !cd || !wd) return pl;
+    if (!xd->set || !dyd->set || !cd->set || !wd->set) return pl;
+    if (need_pointers && (!x || !dy || !dw)) return pl;
+    int n, k, P, Q;
+    mic_status st = output_dims(cd, xd, wd, &n, &k, &P, &Q);
+    if (st != MIC_STATUS_SUCCESS) {
+        pl.status = st;
+        return pl;
+    }
+    if (dyd->n != n || dyd->c != k || dyd->h != P || dyd->w != Q) return pl;
+    if (xd->dtype == MIC_DTYPE_F32 && dyd->dtype == MIC_DTYPE_F32 && wd->dtype == MIC_DTYPE_F32)
+        pl.dt = DType::F32;
+    else if (xd->dtype == MIC_DTYPE_F64 && dyd->dtype == MIC_DTYPE_F64 && wd->dtype == MIC_DTYPE_F64)
+        pl.dt = DType::F64;
+    else if (xd->dtype == MIC_DTYPE_BF16 && dyd->dtype == MIC_DTYPE_BF16 && wd->dtype == MIC_DTYPE_F32)
+        pl.dt = DType::BF16;
+    else {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;
+        return pl;
+    }
+    const int64_t L = (int64_t)n * P * Q;
+    const int64_t CRS = (int64_t)wd->c * wd->r * wd->s;
+    if (extent(*xd) >= kMaxOffset || extent(*dyd) >= kMaxOffset || (int64_t)wd->k * CRS >= kMaxOffset ||
+        L >= kMaxOffset || xd->sn >= kMaxOffset || xd->sc >= kMaxOffset || xd->sh >= kMaxOffset ||
+        xd->sw >= kMaxOffset || dyd->sn >= kMaxOffset || dyd->sc >= kMaxOffset || dyd->sh >= kMaxOffset ||
+        dyd->sw >= kMaxOffset) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;
+        return pl;
+    }
+    if (need_pointers) {
+        const size_t ie = dtype_size(xd->dtype), oe = dtype_size(wd->dtype);
+        if ((uintptr_t)x % ie || (uintptr_t)dy % ie || (uintptr_t)dw % oe) return pl;
+    }
+    ConvParams& p = pl.p;
+    p.x = x;
+    p.w = dy;
+    p.y = const_cast<void*>(dw);
+    p.N = n;
+    p.C = xd->c;
+    p.H = xd->h;
+    p.W = xd->w;
+    p.R = wd->r;
+    p.S = wd->s;
+    p.P = P;
+    p.Q = Q;
+    p.u = cd->u;
+    p.v = cd->v;
+    p.pad_top = cd->pad_top;
+    p.pad_left = cd->pad_left;
+    p.sxn = (int)xd->sn;
+    p.sxc = (int)xd->sc;
+    p.sxh = (int)xd->sh;
+    p.sxw = (int)xd->sw;
+    p.sdn = (int)dyd->sn;
+    p.sdk = (int)dyd->sc;
+    p.sdp = (int)dyd->sh;
+    p.sdq = (int)dyd->sw;
+    p.syn = (int)CRS;       // dw packed K,C,R,S: row k, column (c, r, s)
+    p.syk = 1;
+    p.syp = 0;
+    p.syq = 0;
+    p.M = k;
+    p.K = (int)CRS;
+    p.Kred = (int)L;
+    p.div_pq = FastDiv(1);
+    p.div_q = FastDiv(1);
+    p.div_rs = FastDiv((uint32_t)(wd->r * wd->s));
+    p.div_s = FastDiv((uint32_t)wd->s);
+    p.div_opq = FastDiv((uint32_t)(P * Q));
+    p.div_oq = FastDiv((uint32_t)Q);
+    p.alpha = alpha;
+    p.beta = beta;
+
+    const Candidate* list = kWgF32;
+    int count = (int)(sizeof(kWgF32) / sizeof(kWgF32[0]));
+    if (pl.dt == DType::F64) {
+        list = kWgF64;
+        count = (int)(sizeof(kWgF64) / sizeof(kWgF64[0]));
+    } else if (pl.dt == DType::BF16) {
+        list = kWgBF16;
+        count = (int)(sizeof(kWgBF16) / sizeof(kWgBF16[0]));
+    }
+    const int num_cu = h ? h->num_cu : kDefaultCUs;
+    const char* force = getenv("MIC_FORCE_WGRAD_VARIANT");
+    if (force && !force[0]) force = nullptr;
+    double best = 0;
+    bool found = false;
+    for (int i = 0; i < count; ++i) {
+        if (force && strcmp(force, list[i].name) != 0) continue;
+        const int64_t tiles = (int64_t)((p.M + list[i].tm - 1) / list[i].tm) * ((p.K + list[i].tn - 1) / list[i].tn);
+        const int64_t rounds = (tiles + num_cu - 1) / num_cu;
+        const double reuse = (double)list[i].tm * list[i].tn / (list[i].tm + list[i].tn);
+        const double eff = reuse >= 48.0 ? 1.0 : reuse / 48.0;
+        const double cost = (double)rounds * list[i].tm * list[i].tn / eff;
+        if (!found || cost < best) {
+            best = cost;
+            pl.cand = list[i];
+            found = true;
+        }
+    }
+    if (!found) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;   // a forced variant of another type
+        return pl;
+    }
+    snprintf(pl.name, sizeof(pl.name), "%s", pl.cand.name);
+    pl.status = MIC_STATUS_SUCCESS;
+    return pl;
+}
+
 }  // namespace
 
 extern "C" {
@@ -875,6 +1013,30 @@ mic_status mic_conv_backward_data_kernel_name(mic_handle handle, mic_filter_desc
 {
     if (!buf) return MIC_STATUS_BAD_PARAM;
     Plan pl = make_dgrad_plan(handle, dy_desc, nullptr, w_desc, nullptr, conv, dx_desc, nullptr, 1.0, 0.0, false);
+    if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    const size_t len = strlen(pl.name);
+    if (len + 1 > buflen) return MIC_STATUS_BAD_PARAM;
+    memcpy(buf, pl.name, len + 1);
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_conv_backward_filter(mic_handle handle, double alpha, mic_tensor_desc x_desc, const void* x,
+                                    mic_tensor_desc dy_desc, const void* dy, mic_conv_desc conv, double beta,
+                                    mic_filter_desc dw_desc, void* dw)
+{
+    if (!handle) return MIC_STATUS_BAD_PARAM;
+    Plan pl = make_wgrad_plan(handle, x_desc, x, dy_desc, dy, conv, dw_desc, dw, alpha, beta, true);
+    if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    const hipError_t err = miconv::launch_bwd_filter(pl.cand.v, pl.p, handle->stream);
+    return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
+}
+
+mic_status mic_conv_backward_filter_kernel_name(mic_handle handle, mic_tensor_desc x_desc,
+                                                mic_tensor_desc dy_desc, mic_conv_desc conv,
+                                                mic_filter_desc dw_desc, char* buf, size_t buflen)
+{
+    if (!buf) return MIC_STATUS_BAD_PARAM;
+    Plan pl = make_wgrad_plan(handle, x_desc, nullptr, dy_desc, nullptr, conv, dw_desc, nullptr, 1.0, 0.0, false);
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
     const size_t len = strlen(pl.name);
     if (len + 1 > buflen) return MIC_STATUS_BAD_PARAM;

@@ -1,6 +1,6 @@
 /*
  * miconv.h -- C ABI of libmiconv, the 2-D convolution forward pass (FPROP)
- * and its data gradient for AMD Instinct MI355X (gfx950).
+ * and its data and filter gradients for AMD Instinct MI355X (gfx950).
  *
  * The operation (direct convolution, cross-correlation form, zero padding):
  *
@@ -213,6 +213,39 @@ mic_status mic_conv_backward_data(mic_handle handle, double alpha,
 mic_status mic_conv_backward_data_kernel_name(mic_handle handle, mic_filter_desc w_desc,
                                               mic_tensor_desc dy_desc, mic_conv_desc conv,
                                               mic_tensor_desc dx_desc, char* buf, size_t buflen);
+
+/* ---------------------------------------------------------------- filter gradient */
+
+/* dw <- alpha * wgrad(x, dy) + beta * dw: the backward pass with respect to
+ * the filter, i.e. the adjoint of the forward sum in F,
+ *
+ *   dw[k,c,r,s] = alpha * sum_{n,p,q} dY(n, k, p, q) * X(n, c, p*u + r - pad_top, q*v + s - pad_left)
+ *               + beta * dw[k,c,r,s]
+ *
+ * on the handle's stream, asynchronously (same reading of the pages as
+ * mic_conv_backward_data).  The geometry is the forward problem's: x_desc
+ * the input, dw_desc the packed K,C,R,S filter (its dtype is the output's),
+ * conv the padding and strides; dy_desc must have the forward output dims
+ * (N, K, P, Q).  Element types (x, dy, dw): (F32, F32, F32), (F64, F64,
+ * F64), (BF16, BF16, F32).  x and dy with any element strides; dw packed.
+ * alpha, beta, ownership and size rules as for mic_conv_forward.  No
+ * workspace: the reduction over N*P*Q positions is not split across
+ * workgroups, so the parallelism is the number of dw tiles.
+ *
+ * Errors: MIC_STATUS_BAD_PARAM (null handle/descriptor/pointer, unset
+ * descriptor, dy dims not the forward output dims), MIC_STATUS_NOT_SUPPORTED
+ * (dtype combination, size limit), MIC_STATUS_LAUNCH_FAILED. */
+mic_status mic_conv_backward_filter(mic_handle handle, double alpha,
+                                    mic_tensor_desc x_desc, const void* x,
+                                    mic_tensor_desc dy_desc, const void* dy,
+                                    mic_conv_desc conv, double beta,
+                                    mic_filter_desc dw_desc, void* dw);
+
+/* Name of the kernel variant mic_conv_backward_filter would launch (host
+ * only), as mic_conv_forward_kernel_name. */
+mic_status mic_conv_backward_filter_kernel_name(mic_handle handle, mic_tensor_desc x_desc,
+                                                mic_tensor_desc dy_desc, mic_conv_desc conv,
+                                                mic_filter_desc dw_desc, char* buf, size_t buflen);
 
 #ifdef __cplusplus
 }

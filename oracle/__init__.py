@@ -74,6 +74,9 @@ def _load():
         lib.oracle_conv2d_bwd_filter.argtypes = [pp, dp, dp, ip, ctypes.c_double, ctypes.c_double,
                                                  dp, dp, dp, ctypes.c_int]
         lib.oracle_conv2d_bwd_filter.restype = ctypes.c_int
+        lib.oracle_conv2d_bwd_filter_at.argtypes = [pp, dp, dp, ip, ctypes.c_double, ctypes.c_double,
+                                                    dp, ip, ctypes.c_int64, dp, dp, ctypes.c_int]
+        lib.oracle_conv2d_bwd_filter_at.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
@@ -270,4 +273,32 @@ def conv2d_bwd_filter(x, dy, w_shape, stride=(1, 1), padding=(0, 0, 0, 0), alpha
         float(alpha), float(beta), _dptr(wo), _dptr(dw), _dptr(bound), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the problem")
+    return dw, bound
+
+
+def conv2d_bwd_filter_at(x, dy, w_shape, idx, stride=(1, 1), padding=(0, 0, 0, 0), alpha=1.0, beta=0.0,
+                         dw_old_vals=None, nthreads=0):
+    """Selected filter-gradient values.  idx: int64 array (count, 4) of (k, c, r, s)."""
+    xb, xs = _input_view(x)
+    db, ds = _input_view(dy)
+    pb = make_problem(x.shape, xs, tuple(w_shape), stride, padding)
+    P, Q = output_dims(pb)
+    if tuple(dy.shape) != (x.shape[0], w_shape[0], P, Q):
+        raise ValueError("dy shape %s != forward output shape %s" % (tuple(dy.shape), (x.shape[0], w_shape[0], P, Q)))
+    sdy = np.asarray(ds, dtype=np.int64)
+    ic = np.ascontiguousarray(idx, dtype=np.int64).reshape(-1, 4)
+    count = ic.shape[0]
+    dw = np.empty(count, dtype=np.float64)
+    bound = np.empty(count, dtype=np.float64)
+    wo = None
+    if beta != 0.0:
+        if dw_old_vals is None:
+            raise ValueError("beta != 0 needs dw_old_vals")
+        wo = np.ascontiguousarray(dw_old_vals, dtype=np.float64).reshape(-1)
+    rc = _load().oracle_conv2d_bwd_filter_at(
+        ctypes.byref(pb), _dptr(xb), _dptr(db), sdy.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        float(alpha), float(beta), _dptr(wo), ic.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), count,
+        _dptr(dw), _dptr(bound), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem or a coordinate")
     return dw, bound

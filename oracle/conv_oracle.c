@@ -365,6 +365,42 @@ int oracle_conv2d_bwd_filter(const oracle_conv_problem* pb,
     return 0;
 }
 
+/*
+ * Selected filter-gradient values.  idx holds count (k, c, r, s) int64
+ * quadruples; dw_old_vals (read only when beta != 0) the old values there.
+ * Returns 0, or -1 on a bad problem or a coordinate out of range.
+ */
+int oracle_conv2d_bwd_filter_at(const oracle_conv_problem* pb,
+                                const double* x, const double* dy, const int64_t* sdy,
+                                double alpha, double beta, const double* dw_old_vals,
+                                const int64_t* idx, int64_t count,
+                                double* dw, double* bound, int nthreads)
+{
+    int64_t P, Q;
+    if (oracle_output_dims(pb, &P, &Q) != 0) return -1;
+    if (beta != 0.0 && dw_old_vals == NULL) return -1;
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t* t = idx + 4 * i;
+        if (t[0] < 0 || t[0] >= pb->K || t[1] < 0 || t[1] >= pb->C ||
+            t[2] < 0 || t[2] >= pb->R || t[3] < 0 || t[3] >= pb->S) return -1;
+    }
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t* t = idx + 4 * i;
+        double acc, bnd;
+        one_wgrad(pb, P, Q, x, dy, sdy, t[0], t[1], t[2], t[3], &acc, &bnd);
+        double val = alpha * acc;
+        if (beta != 0.0) val += beta * dw_old_vals[i];
+        if (dw) dw[i] = val;
+        if (bound) bound[i] = bnd;
+    }
+    (void)nthreads;
+    return 0;
+}
+
 /* Number of OpenMP threads a call with nthreads <= 0 would use. */
 int oracle_default_threads(void)
 {

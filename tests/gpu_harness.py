@@ -5,6 +5,10 @@ Tolerances (per element type, fixed in the tests, not tuned to results):
   f32 : relative L2 error <= 1e-5 and |y - y_ref| <= 2e-6 * B per element,
         B = sum |x*f| over the receptive field (the oracle returns it);
         with alpha/beta the bound is 2e-6 * (|alpha| B + |beta y_old|).
+        The filter gradient sums over N*P*Q positions, up to 50x more terms
+        than any forward sum: its relative-L2 gate grows with the square
+        root of the reduction length (rel_l2_scale), the per-element bound
+        does not change.
   f64 : relative L2 error <= 1e-12.
   bf16: relative L2 error <= 1e-2 (bf16 inputs, fp32 accumulation and output).
 """
@@ -71,14 +75,34 @@ def gather(y, idx):
     return y[t[:, 0], t[:, 1], t[:, 2], t[:, 3]].double().cpu().numpy()
 
 
-def check(dtype_key, got, ref, bound, alpha=1.0, beta=0.0, y_old=None, what=""):
-    """Assert the element type's tolerance; return (rel_l2, max_err/bound)."""
+# The forward pass's longest reduction in the workloads (Overfeat L5: C*R*S).
+FWD_MAX_REDUCTION = 1024 * 9
+
+
+def rel_l2_scale(reduction_length):
+    """Factor on the fp32/bf16 relative-L2 gate for a reduction of the given length.
+
+    The gate is stated for the forward pass, whose sums run over at most
+    C*R*S = 9216 terms.  With terms of mixed sign, the rounding error of an
+    fp32 sum of L terms relative to its value grows like u * sqrt(L) (the
+    partial sums and their roundings both random-walk), so a sum over
+    L > 9216 terms gets the gate times sqrt(L / 9216); never less than 1.
+    """
+    return max(1.0, float(np.sqrt(reduction_length / FWD_MAX_REDUCTION)))
+
+
+def check(dtype_key, got, ref, bound, alpha=1.0, beta=0.0, y_old=None, what="", rel_scale=1.0):
+    """Assert the element type's tolerance; return (rel_l2, max_err/bound).
+
+    rel_scale multiplies the relative-L2 gate (see rel_l2_scale); the
+    per-element bound 2e-6 * B is never relaxed."""
     got = np.asarray(got, dtype=np.float64)
     assert np.all(np.isfinite(got)), "%s: non-finite output" % what
     diff = got - ref
     nref = np.linalg.norm(ref)
     rel = np.linalg.norm(diff) / nref if nref > 0 else np.linalg.norm(diff)
-    assert rel <= RELL2[dtype_key], "%s: relative L2 error %.3e > %.1e" % (what, rel, RELL2[dtype_key])
+    gate = RELL2[dtype_key] * (rel_scale if dtype_key != "f64" else 1.0)
+    assert rel <= gate, "%s: relative L2 error %.3e > %.1e" % (what, rel, gate)
     worst = 0.0
     if dtype_key in ELEM_BOUND:
         scale = abs(alpha) * bound

@@ -303,3 +303,46 @@ def test_dgrad_forced_variant(monkeypatch):
     with pytest.raises(mic.MicError) as e:
         _dgrad_name(lay)
     assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+
+
+# ---------------------------------------------------------------- filter gradient (host side)
+
+def _wgrad_name(lay, dts=None):
+    """Kernel the filter gradient of a forward layer would use: (x, dy, dw) descriptors."""
+    F32 = mic.MIC_DTYPE_F32
+    dts = dts or {"f32": (F32, F32, F32), "f64": (1, 1, 1), "bf16": (2, 2, F32)}[lay.dtype]
+    xd, wd, cd, yd = _descs(lay, dts[0], dts[2], dts[1])   # wd plays dw, yd plays dy
+    try:
+        return mic.mic_conv_backward_filter_kernel_name(None, xd, yd, cd, wd)
+    finally:
+        _free(xd, wd, cd, yd)
+
+
+def test_wgrad_kernel_choice_host_only():
+    for lay in workloads.ALL_LAYERS:
+        assert _wgrad_name(lay).startswith("wg_%s_" % lay.dtype), lay.name
+
+
+def test_wgrad_shape_and_type_errors(monkeypatch):
+    lay = workloads.TINY[0]
+    F32 = mic.MIC_DTYPE_F32
+    xd, wd, cd, yd = _descs(lay, F32, F32, F32, y_dims=(lay.N, lay.K, 12, 11))
+    try:
+        with pytest.raises(mic.MicError) as e:
+            mic.mic_conv_backward_filter_kernel_name(None, xd, yd, cd, wd)
+        assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+    finally:
+        _free(xd, wd, cd, yd)
+    for combo in [(0, 0, 1), (2, 2, 2), (1, 0, 1)]:
+        with pytest.raises(mic.MicError) as e:
+            _wgrad_name(lay, combo)
+        assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+    monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", "wg_f32_64x64")
+    assert _wgrad_name(lay) == "wg_f32_64x64"
+    monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", "wg_f64_64x64")       # another element type
+    with pytest.raises(mic.MicError) as e:
+        _wgrad_name(lay)
+    assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+    l = mic.lib()
+    assert l.mic_conv_backward_filter(None, 1.0, None, None, None, None, None, 0.0, None, None) == \
+        mic.MIC_STATUS_BAD_PARAM

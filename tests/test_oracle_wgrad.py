@@ -145,3 +145,8 @@ def test_layouts_and_alpha_beta():
     dw, _ = oracle.conv2d_bwd_filter(x, dy, (K, C, R, S), stride, pads, alpha=0.5, beta=-2.0, dw_old=old)
     np.testing.assert_allclose(dw, 0.5 * base - 2.0 * old, rtol=0, atol=1e-15)
     assert np.all(bound >= np.abs(base))
+    idx = np.array([[0, 0, 0, 0], [3, 2, 2, 2], [1, 1, 0, 2], [2, 0, 1, 1]], dtype=np.int64)
+    vals, bnd = oracle.conv2d_bwd_filter_at(x, dy, (K, C, R, S), idx, stride, pads, alpha=0.5, beta=-2.0,
+                                            dw_old_vals=old[tuple(idx.T)])
+    assert np.array_equal(vals, dw[tuple(idx.T)])
+    assert np.array_equal(bnd, bound[tuple(idx.T)])

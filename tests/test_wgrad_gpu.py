@@ -1,0 +1,175 @@
+"""GPU parity of the filter gradient (mic_conv_backward_filter) against the oracle.
+
+Small shapes spanning several dw tiles with ragged edges are compared in
+full for every kernel variant; every workload layer's filter gradient is run
+at full size and compared on sampled (k, c, r, s) coordinates, with
+integer-valued inputs bit-exact and reruns bit-identical.  x is the layer's
+seeded input, dy seeded uniform [-1, 1] (tensor id 3), both rounded to the
+layer's storage type.
+
+The fp32 per-element tolerance is the forward pass's, |err| <= 2e-6 * B
+with B = sum |dy * x| over the reduction.  The reduction here runs over
+N*P*Q positions (up to 907200, speech L1) instead of at most 9216 terms:
+the relative-L2 gate (1e-5 fp32, 1e-2 bf16) is scaled by sqrt(L / 9216),
+the growth of an fp32 sum's relative rounding error with its length when
+the terms have mixed signs (gpu_harness.rel_l2_scale).  Measured without
+the scaling, Overfeat L1 (L = 401408) gives 1.1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_forward_conv2d_amd as mic
+import gen
+import oracle
+from gen import workloads
+from gen.workloads import Layer
+
+import gpu_harness as H
+from test_parity_gpu import SMALL_SHAPES, U
+
+pytestmark = pytest.mark.gpu
+
+WG_VARIANTS = {
+    "f32": ["wg_f32_128x128", "wg_f32_64x128", "wg_f32_128x64", "wg_f32_64x64"],
+    "f64": ["wg_f64_128x64", "wg_f64_64x64"],
+    "bf16": ["wg_bf16_128x128", "wg_bf16_64x64"],
+}
+_ran = set()
+
+
+def _small(name, N, C, Hh, Ww, K, R, S, stride, pads, dtype, layout="nchw", pitch=0):
+    return Layer(name, 9, 3, N, C, Hh, Ww, K, R, S, stride, pads, dtype, U, U,
+                 layout=layout, row_pitch=pitch)
+
+
+def _dy(lay, shape, integer=False):
+    seed = gen.derive_seed(lay.config, lay.layer, 3)
+    d = gen.integers(seed, shape, -4, 4) if integer else gen.uniform(seed, shape, -1.0, 1.0)
+    return gen.round_to(d, lay.dtype)
+
+
+def _run(lay, x, dy, dw, alpha=1.0, beta=0.0):
+    plan = mic.WgradPlan(x, dy, dw, lay.stride, lay.padding)
+    try:
+        plan(alpha, beta)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    return dw
+
+
+def _out(lay, fill=float("nan")):
+    return torch.full(lay.w_shape, fill, dtype=H.OUT_DT[lay.dtype], device=H.dev())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: s["name"])
+def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
+    lay = _small(dtype=dtype, **{k: v for k, v in shape.items()})
+    x64, _ = H.inputs(lay)
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    dy64 = _dy(lay, (N, K, P, Q))
+    ref, bound = oracle.conv2d_bwd_filter(x64, dy64, lay.w_shape, lay.stride, lay.padding)
+    x = H.to_device(x64, dtype, lay.layout, lay.row_pitch)
+    dy = H.to_device(dy64, dtype, lay.layout, lay.row_pitch)
+    for var in WG_VARIANTS[dtype]:
+        monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", var)
+        print("case", shape["name"], dtype, var, flush=True)
+        dw = _out(lay)
+        _run(lay, x, dy, dw)
+        H.check(dtype, dw.double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (shape["name"], dtype, var),
+                rel_scale=H.rel_l2_scale(N * P * Q))
+        _ran.add(var)
+
+
+def test_every_wgrad_variant_was_exercised():
+    want = {v for vs in WG_VARIANTS.values() for v in vs}
+    assert want <= _ran, "filter-gradient variants never run: %s" % sorted(want - _ran)
+
+
+def _sample(rng, w_shape, count):
+    K, C, R, S = w_shape
+    pts = {(k, c, r, s) for k in (0, K - 1) for c in (0, C - 1) for r in (0, R - 1) for s in (0, S - 1)}
+    rnd = np.stack([rng.integers(0, K, count), rng.integers(0, C, count),
+                    rng.integers(0, R, count), rng.integers(0, S, count)], axis=1)
+    return np.concatenate([np.array(sorted(pts), dtype=np.int64), rnd.astype(np.int64)])
+
+
+@pytest.mark.parametrize("lay", workloads.ALL_LAYERS, ids=lambda l: l.name)
+def test_workload_layer_sampled(lay):
+    """Full-size filter gradient, default variant: sampled parity, NaN-safe beta=0, rerun bit-identity."""
+    print("layer", lay.name, flush=True)
+    x64, _ = H.inputs(lay)
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    dy64 = _dy(lay, (N, K, P, Q))
+    x = H.to_device(x64, lay.dtype, lay.layout, lay.row_pitch)
+    dy = H.to_device(dy64, lay.dtype, lay.layout, lay.row_pitch)
+    dw = _out(lay)
+    _run(lay, x, dy, dw)
+    assert bool(torch.isfinite(dw).all()), "unwritten or non-finite dw"
+    rng = np.random.default_rng(lay.config * 1000 + lay.layer + 41)
+    idx = _sample(rng, lay.w_shape, 400)
+    ref, bound = oracle.conv2d_bwd_filter_at(x64, dy64, lay.w_shape, idx, lay.stride, lay.padding)
+    rel, worst = H.check(lay.dtype, H.gather(dw, idx), ref, bound, what=lay.name,
+                         rel_scale=H.rel_l2_scale(N * P * Q))
+    print("  sampled rel-L2 %.3e, worst |err|/B %.3e" % (rel, worst), flush=True)
+    dw2 = _out(lay, fill=0.0)
+    _run(lay, x, dy, dw2)
+    assert torch.equal(dw, dw2), "rerun not bit-identical"
+
+
+@pytest.mark.parametrize("lay", [l for l in workloads.ALL_LAYERS if not l.name.endswith("nhwc")],
+                         ids=lambda l: l.name)
+def test_workload_layer_integer_exact(lay):
+    """Integer x and dy in [-4, 4]: |partial sums| <= 16 * N*P*Q < 2^24, all exact."""
+    print("layer", lay.name, flush=True)
+    x64, _ = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    assert 16 * N * P * Q < 2 ** 24
+    dy64 = _dy(lay, (N, K, P, Q), integer=True)
+    x = H.to_device(x64, lay.dtype, lay.layout, lay.row_pitch)
+    dy = H.to_device(dy64, lay.dtype, lay.layout, lay.row_pitch)
+    dw = _out(lay)
+    _run(lay, x, dy, dw)
+    rng = np.random.default_rng(lay.config * 1000 + lay.layer + 53)
+    idx = _sample(rng, lay.w_shape, 200)
+    ref, _ = oracle.conv2d_bwd_filter_at(x64, dy64, lay.w_shape, idx, lay.stride, lay.padding)
+    got = H.gather(dw, idx)
+    assert np.array_equal(got, ref), "%s: %d mismatches" % (lay.name, int((got != ref).sum()))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
+def test_alpha_beta(dtype, monkeypatch):
+    lay = _small("wg_ab", 2, 20, 13, 11, 36, 3, 3, (1, 2), (1, 1, 1, 0), dtype)
+    xi, _ = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    dyi = _dy(lay, (N, K, P, Q), integer=True)
+    acc, _ = oracle.conv2d_bwd_filter(xi, dyi, lay.w_shape, lay.stride, lay.padding)
+    old = gen.integers(97, acc.shape)
+    x = H.to_device(xi, dtype)
+    dy = H.to_device(dyi, dtype)
+    for var in WG_VARIANTS[dtype]:
+        monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", var)
+        dw = torch.from_numpy(old).to(H.OUT_DT[dtype]).to(H.dev())
+        _run(lay, x, dy, dw, alpha=0.5, beta=0.25)
+        assert np.array_equal(dw.double().cpu().numpy(), 0.5 * acc + 0.25 * old), var
+
+
+def test_wgrad_error_statuses_on_device():
+    lay = workloads.TINY[0]
+    x = torch.zeros(lay.x_shape, device=H.dev())
+    dy = torch.zeros((2, 16, 12, 11), device=H.dev())          # forward output is 12 x 12
+    dw = torch.zeros(lay.w_shape, device=H.dev())
+    with pytest.raises(mic.MicError) as e:
+        mic.conv2d_backward_filter(x, dy, lay.w_shape, lay.stride, lay.padding, dw=dw)
+    assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+    dy = torch.zeros((2, 16, 12, 12), device=H.dev())
+    plan = mic.WgradPlan(x, dy, dw, lay.stride, lay.padding)
+    try:
+        with pytest.raises(mic.MicError) as e:                   # null dw pointer
+            mic.mic_conv_backward_filter(plan.handle, 1.0, plan.xd, x.data_ptr(), plan.dyd, dy.data_ptr(),
+                                         plan.cd, 0.0, plan.wd, 0)
+        assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+    finally:
+        plan.close()
