@@ -1,5 +1,5 @@
-"""CPU oracle for the 2-D convolution forward pass and its data and filter
-gradients (fp64, plain 7-nested loops).
+"""CPU oracle for the 2-D convolution forward pass, its data and filter
+gradients, and pooling (fp64, plain nested loops).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
@@ -77,6 +77,9 @@ def _load():
         lib.oracle_conv2d_bwd_filter_at.argtypes = [pp, dp, dp, ip, ctypes.c_double, ctypes.c_double,
                                                     dp, ip, ctypes.c_int64, dp, dp, ctypes.c_int]
         lib.oracle_conv2d_bwd_filter_at.restype = ctypes.c_int
+        lib.oracle_pool_forward.argtypes = [pp, dp, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                            dp, dp, ctypes.c_int]
+        lib.oracle_pool_forward.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
@@ -302,3 +305,28 @@ def conv2d_bwd_filter_at(x, dy, w_shape, idx, stride=(1, 1), padding=(0, 0, 0, 0
     if rc != 0:
         raise ValueError("oracle rejected the problem or a coordinate")
     return dw, bound
+
+
+POOL_MODES = {"max": 0, "avg_include_pad": 1, "avg_exclude_pad": 2}
+
+
+def pool2d_forward(x, window, stride=(1, 1), padding=(0, 0, 0, 0), mode="max", alpha=1.0, beta=0.0,
+                   y_old=None, nthreads=0):
+    """Pooled output, float64 packed (N, C, P, Q).  window = (R, S); mode in POOL_MODES."""
+    xb, xs = _input_view(x)
+    N, C = x.shape[:2]
+    pb = make_problem(x.shape, xs, (1, C) + tuple(window), stride, padding)
+    P, Q = output_dims(pb)
+    y = np.empty((N, C, P, Q), dtype=np.float64)
+    yo = None
+    if beta != 0.0:
+        if y_old is None:
+            raise ValueError("beta != 0 needs y_old")
+        yo = np.ascontiguousarray(y_old, dtype=np.float64)
+        if yo.shape != y.shape:
+            raise ValueError("y_old shape %s != output shape %s" % (yo.shape, y.shape))
+    rc = _load().oracle_pool_forward(ctypes.byref(pb), _dptr(xb), POOL_MODES[mode], float(alpha), float(beta),
+                                     _dptr(yo), _dptr(y), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return y

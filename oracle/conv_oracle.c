@@ -1,6 +1,7 @@
 /*
  * oracle/conv_oracle.c -- plain CPU reference for the 2-D convolution forward
- * pass (FPROP) and its gradients (backward passes with respect to x and F).  TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and
+ * pass (FPROP), its gradients (backward passes with respect to x and F) and
+ * the pooling forward pass.  TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and
  * the CPU-baseline leg of the benchmark may load this library.  It shares no
  * code, header, table or helper with the GPU path.
  *
@@ -396,6 +397,74 @@ int oracle_conv2d_bwd_filter_at(const oracle_conv_problem* pb,
         if (beta != 0.0) val += beta * dw_old_vals[i];
         if (dw) dw[i] = val;
         if (bound) bound[i] = bnd;
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/*
+ * Pooling forward pass.  The cuDNN page ("Proposed Method") lists pooling
+ * among the library's forward and backward routines; it prints no formula.
+ * The plain reading taken, over the same window geometry as the convolution
+ * (window R x S, strides u, v, per-side padding; output size P x Q by the
+ * same floor rule), with C channels pooled independently:
+ *
+ *   mode 0 (max):           acc = max of X over the window positions inside
+ *                            the H x W plane (padding never wins), 0 if none
+ *   mode 1 (average, pad):  acc = (sum of X over the window positions inside
+ *                            the plane) / (R * S)     (padding counts as 0)
+ *   mode 2 (average):       acc = that sum / (number of positions inside the
+ *                            plane), 0 if none
+ *   y[n,c,p,q] = alpha * acc + beta * y_old[n,c,p,q]   (y_old unread if beta == 0)
+ *
+ * X is x read through the problem's strides.  The problem's K is unused.
+ * y is packed N,C,P,Q.  Sums run in the fixed order r, s in double.
+ */
+static double one_pool(const oracle_conv_problem* pb, const double* x, int mode,
+                       int64_t n, int64_t c, int64_t p, int64_t q)
+{
+    double best = 0.0, sum = 0.0;
+    int64_t inside = 0;
+    for (int64_t r = 0; r < pb->R; ++r) {
+        for (int64_t s = 0; s < pb->S; ++s) {
+            int64_t h = p * pb->u + r - pb->pad_top;
+            int64_t w = q * pb->v + s - pb->pad_left;
+            if (h < 0 || h >= pb->H || w < 0 || w >= pb->W) continue;
+            double v = x[n * pb->sn + c * pb->sc + h * pb->sh + w * pb->sw];
+            if (inside == 0 || v > best) best = v;
+            sum += v;
+            ++inside;
+        }
+    }
+    if (mode == 0) return inside ? best : 0.0;
+    if (mode == 1) return sum / (double)(pb->R * pb->S);
+    return inside ? sum / (double)inside : 0.0;
+}
+
+/* Whole pooled output; y packed N,C,P,Q.  Returns 0, or -1 on a bad problem or mode. */
+int oracle_pool_forward(const oracle_conv_problem* pb, const double* x, int mode,
+                        double alpha, double beta, const double* y_old, double* y, int nthreads)
+{
+    int64_t P, Q;
+    if (oracle_output_dims(pb, &P, &Q) != 0) return -1;
+    if (mode < 0 || mode > 2) return -1;
+    if (beta != 0.0 && y_old == NULL) return -1;
+    const int64_t N = pb->N, C = pb->C;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t c = 0; c < C; ++c) {
+            for (int64_t p = 0; p < P; ++p) {
+                for (int64_t q = 0; q < Q; ++q) {
+                    int64_t o = ((n * C + c) * P + p) * Q + q;
+                    double val = alpha * one_pool(pb, x, mode, n, c, p, q);
+                    if (beta != 0.0) val += beta * y_old[o];
+                    y[o] = val;
+                }
+            }
+        }
     }
     (void)nthreads;
     return 0;

@@ -60,6 +60,21 @@ MUTANTS_WGRAD = {
     "wgrad_last_column_dropped": ("for (int64_t q = 0; q < Q; ++q) {\n                double xv", "for (int64_t q = 0; q < Q - 1; ++q) {\n                double xv"),
 }
 
+# slips in the pooling code, caught by test_oracle_pool.py
+MUTANTS_POOL = {
+    "pool_padding_wins_max": ("if (inside == 0 || v > best) best = v;", "if (v > best) best = v;"),
+    "pool_include_divides_by_inside": ("if (mode == 1) return sum / (double)(pb->R * pb->S);",
+                                       "if (mode == 1) return sum / (double)(inside ? inside : 1);"),
+    "pool_exclude_divides_by_window": ("return inside ? sum / (double)inside : 0.0;",
+                                       "return inside ? sum / (double)(pb->R * pb->S) : 0.0;"),
+    "pool_pad_sign": ("int64_t h = p * pb->u + r - pb->pad_top;\n            int64_t w = q * pb->v + s - pb->pad_left;\n            if (h < 0",
+                      "int64_t h = p * pb->u + r + pb->pad_top;\n            int64_t w = q * pb->v + s - pb->pad_left;\n            if (h < 0"),
+    "pool_strides_swapped": ("int64_t h = p * pb->u + r - pb->pad_top;\n            int64_t w = q * pb->v + s - pb->pad_left;\n            if (h < 0",
+                             "int64_t h = p * pb->v + r - pb->pad_top;\n            int64_t w = q * pb->u + s - pb->pad_left;\n            if (h < 0"),
+    "pool_last_window_col_dropped": ("for (int64_t s = 0; s < pb->S; ++s) {\n            int64_t h = p * pb->u",
+                                     "for (int64_t s = 0; s < pb->S - 1; ++s) {\n            int64_t h = p * pb->u"),
+}
+
 
 def _build_and_run(name, old, new, tmp, pins="test_oracle.py"):
     with open(SRC) as fh:
@@ -83,6 +98,7 @@ def test_every_mutant_is_caught():
     jobs = [(n, o, w, "test_oracle.py") for n, (o, w) in MUTANTS.items()]
     jobs += [(n, o, w, "test_oracle_dgrad.py") for n, (o, w) in MUTANTS_DGRAD.items()]
     jobs += [(n, o, w, "test_oracle_wgrad.py") for n, (o, w) in MUTANTS_WGRAD.items()]
+    jobs += [(n, o, w, "test_oracle_pool.py") for n, (o, w) in MUTANTS_POOL.items()]
     with tempfile.TemporaryDirectory() as tmp:
         with ThreadPoolExecutor(max_workers=4) as pool:
             results = list(pool.map(lambda j: _build_and_run(j[0], j[1], j[2], tmp, j[3]), jobs))
