@@ -7,7 +7,7 @@ data, He-normal weights).  One step = the workload's forward passes, each
 one kernel launch of libmiconv through the C ABI.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                    [--workload alexnet|overfeat|speech|tiny|prec_f64|prec_bf16]
+                    [--workload alexnet|overfeat|speech|tiny|prec_f64|prec_bf16|alexnet_pool]
                     [--op fprop|dgrad|wgrad]
 
 Prints one JSON line.  ``value`` = 2*N*K*C*R*S*P*Q summed over the step's
@@ -17,7 +17,9 @@ step, timed with HIP events on the stream it runs on.  ``cpu_baseline``
 times the CPU oracle on a bounded sample of the same workload (the first
 few images of every layer).  ``--op dgrad`` / ``--op wgrad`` time the data /
 filter gradient of the same layers instead (dy seeded uniform [-1, 1]; the
-same FLOP count).
+same FLOP count).  ``--workload alexnet_pool`` times AlexNet's two max-pooling
+layers (after conv2 and conv5) and reports bandwidth (|x| + |y| per second)
+against the HBM roofline.
 """
 import argparse
 import hashlib
@@ -32,7 +34,8 @@ sys.path.insert(0, ROOT)
 # MI355X dense MFMA peaks (256 CU x 2.4 GHz): fp32 256, fp64 128, bf16 4096 FLOP/clk/CU
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "bf16": 2516.6}
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_alexnet_fp32.md")
-WORKLOADS = ("alexnet", "overfeat", "speech", "tiny", "prec_f64", "prec_bf16")
+WORKLOADS = ("alexnet", "overfeat", "speech", "tiny", "prec_f64", "prec_bf16", "alexnet_pool")
+HBM_PEAK_GBS = 8000.0
 
 
 def parse():
@@ -131,6 +134,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
+    if args.workload == "alexnet_pool":
+        return bench_pool(args, torch, mic, gen, workloads, dev)
     layers, wl_name = workload_layers(args.workload)
     dtype = layers[0].dtype
     peak = MFMA_PEAK_TFLOPS[dtype]
@@ -249,6 +254,75 @@ def main():
                    "layers": [l.name for l in layers], "gflop_per_step": round(flops_step / 1e9, 3),
                    "pct_mfma_peak": round(100 * value / peak, 1)},
         "roofline": roofline,
+        "cpu_baseline": cpu,
+        "layers": per_layer,
+    }
+    print(json.dumps(line), flush=True)
+    for _, plan, _ in plans:
+        plan.close()
+
+
+def bench_pool(args, torch, mic, gen, workloads, dev):
+    """AlexNet's max-pooling layers: bandwidth against the HBM roofline."""
+    plans = []
+    for lay in workloads.POOLING:
+        x = gen.round_to(gen.uniform(gen.derive_seed(lay.config, lay.layer, 0), lay.x_shape), lay.dtype)
+        xt = upload(x, lay.dtype, lay.layout, lay.row_pitch, dev)
+        shape = mic.pool_output_shape(lay.x_shape, (lay.R, lay.S), lay.stride, lay.padding)
+        yt = torch.zeros(shape, dtype=torch.float32, device=dev)
+        plans.append((lay, mic.PoolPlan(xt, yt, (lay.R, lay.S), lay.stride, lay.padding, "max"), x))
+    stream = torch.cuda.current_stream(dev)
+    bytes_step = sum(p.bytes for _, p, _ in plans)
+
+    def step():
+        for _, plan, _ in plans:
+            plan(1.0, 0.0, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_layer = []
+    reps = max(5, args.steps)
+    for lay, plan, _ in plans:
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        plan(1.0, 0.0, stream)
+        ev0.record(stream)
+        for _ in range(reps):
+            plan(1.0, 0.0, stream)
+        ev1.record(stream)
+        ev1.synchronize()
+        us = ev0.elapsed_time(ev1) / reps * 1e3
+        per_layer.append({"layer": lay.name, "kernel": plan.kernel_name(), "us": round(us, 2),
+                          "mb": round(plan.bytes / 1e6, 2), "gbs": round(plan.bytes / (us * 1e-6) / 1e9, 1)})
+    dom = max(per_layer, key=lambda r: r["us"])
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        lay, plan, x = plans[0]
+        n = max(1, min(lay.N, int(args.cpu_seconds / 0.05)))
+        t0 = time.perf_counter()
+        oracle.pool2d_forward(x[:n], (lay.R, lay.S), lay.stride, lay.padding, "max")
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(plan.bytes * n / lay.N / dt / 1e9, 3), "unit": "GB/s",
+               "cores": oracle.default_threads(), "kind": "oracle",
+               "sample": "first %d of %d images of %s (%.2f s)" % (n, lay.N, lay.name, dt)}
+    value = bytes_step / (elapsed / args.steps) / 1e9
+    line = {
+        "metric": "pooling bandwidth ((|x|+|y|)/t), 1 MI355X",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded uniform [-1, 1])",
+        "config": {"workload": "alexnet_pool2+pool5_max_fp32_nchw_n128", "op": "pool",
+                   "layers": [l.name for l, _, _ in plans]},
+        "roofline": {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom["kernel"],
+                     "avg_us": dom["us"]},
         "cpu_baseline": cpu,
         "layers": per_layer,
     }

@@ -36,6 +36,12 @@ MIC_DTYPE_BF16 = 2
 MIC_LAYOUT_NCHW = 0
 MIC_LAYOUT_NHWC = 1
 
+MIC_POOL_MAX = 0
+MIC_POOL_AVG_INCLUDE_PAD = 1
+MIC_POOL_AVG_EXCLUDE_PAD = 2
+POOL_MODES = {"max": MIC_POOL_MAX, "avg_include_pad": MIC_POOL_AVG_INCLUDE_PAD,
+              "avg_exclude_pad": MIC_POOL_AVG_EXCLUDE_PAD}
+
 _TORCH_DTYPE = {torch.float32: MIC_DTYPE_F32, torch.float64: MIC_DTYPE_F64,
                 torch.bfloat16: MIC_DTYPE_BF16}
 _OUT_DTYPE = {torch.float32: torch.float32, torch.float64: torch.float64,
@@ -89,6 +95,12 @@ _SIGS = {
                                   _vp, _vp], _i),
     "mic_conv_backward_filter_kernel_name": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_char_p, ctypes.c_size_t],
                                              _i),
+    "mic_pool_desc_create": ([ctypes.POINTER(_vp)], _i),
+    "mic_pool_desc_destroy": ([_vp], _i),
+    "mic_pool_desc_set": ([_vp, _i, _i, _i, _i, _i, _i, _i, _i, _i], _i),
+    "mic_pool_desc_get": ([_vp, _ip, _ip, _ip, _ip, _ip, _ip, _ip, _ip, _ip], _i),
+    "mic_pool_forward_output_dim": ([_vp, _vp, _ip, _ip, _ip, _ip], _i),
+    "mic_pool_forward": ([_vp, ctypes.c_double, _vp, _vp, _vp, ctypes.c_double, _vp, _vp], _i),
 }
 
 
@@ -265,6 +277,37 @@ def mic_conv_backward_filter_kernel_name(handle, x_desc, dy_desc, conv, dw_desc)
     _check(lib().mic_conv_backward_filter_kernel_name(handle, x_desc, dy_desc, conv, dw_desc, buf, 128),
            "mic_conv_backward_filter_kernel_name")
     return buf.value.decode()
+
+
+def mic_pool_desc_create():
+    return _create(lib().mic_pool_desc_create, "mic_pool_desc_create")
+
+
+def mic_pool_desc_destroy(d):
+    _check(lib().mic_pool_desc_destroy(d), "mic_pool_desc_destroy")
+
+
+def mic_pool_desc_set(d, mode, window_h, window_w, pad_top, pad_bottom, pad_left, pad_right, stride_h, stride_w):
+    _check(lib().mic_pool_desc_set(d, mode, window_h, window_w, pad_top, pad_bottom, pad_left, pad_right,
+                                   stride_h, stride_w), "mic_pool_desc_set")
+
+
+def mic_pool_desc_get(d):
+    vals = [_i() for _ in range(9)]
+    _check(lib().mic_pool_desc_get(d, *[ctypes.byref(v) for v in vals]), "mic_pool_desc_get")
+    return tuple(v.value for v in vals)
+
+
+def mic_pool_forward_output_dim(pool, x_desc):
+    vals = [_i() for _ in range(4)]
+    _check(lib().mic_pool_forward_output_dim(pool, x_desc, *[ctypes.byref(v) for v in vals]),
+           "mic_pool_forward_output_dim")
+    return tuple(v.value for v in vals)
+
+
+def mic_pool_forward(handle, alpha, pool, x_desc, x_ptr, beta, y_desc, y_ptr):
+    _check(lib().mic_pool_forward(handle, float(alpha), pool, x_desc, _vp(x_ptr), float(beta), y_desc,
+                                  _vp(y_ptr)), "mic_pool_forward")
 
 
 # ---------------------------------------------------------------- torch-facing helpers
@@ -515,3 +558,74 @@ def conv2d_backward_filter(x, dy, w_shape, stride=(1, 1), padding=(0, 0, 0, 0), 
     finally:
         plan.close()
     return dw
+
+
+def pool_output_shape(x_shape, window, stride=(1, 1), padding=(0, 0, 0, 0), mode="max"):
+    """(N, C, P, Q) from the library's own output-size rule (host only)."""
+    xd, pd = mic_tensor_desc_create(), mic_pool_desc_create()
+    try:
+        mic_tensor_desc_set_packed(xd, MIC_DTYPE_F32, MIC_LAYOUT_NCHW, *x_shape)
+        mic_pool_desc_set(pd, POOL_MODES[mode], *window, *padding, *stride)
+        return mic_pool_forward_output_dim(pd, xd)
+    finally:
+        mic_tensor_desc_destroy(xd)
+        mic_pool_desc_destroy(pd)
+
+
+class PoolPlan:
+    """Descriptors for one pooling call (x -> y), reusable.  mode in POOL_MODES."""
+
+    def __init__(self, x, y, window, stride=(1, 1), padding=(0, 0, 0, 0), mode="max", handle=None):
+        if x.dim() != 4 or y.dim() != 4:
+            raise ValueError("x, y must be 4-D")
+        for t in (x, y):
+            if t.dtype not in _TORCH_DTYPE:
+                raise TypeError("unsupported dtype %s" % t.dtype)
+        self.x, self.y = x, y
+        self.handle = handle if handle is not None else handle_for(x.device)
+        self.xd, self.yd, self.pd = mic_tensor_desc_create(), mic_tensor_desc_create(), mic_pool_desc_create()
+        mic_tensor_desc_set(self.xd, _TORCH_DTYPE[x.dtype], *x.shape, *_element_strides(x))
+        mic_tensor_desc_set(self.yd, _TORCH_DTYPE[y.dtype], *y.shape, *_element_strides(y))
+        mic_pool_desc_set(self.pd, POOL_MODES[mode], *window, *padding, *stride)
+        # algorithmic bytes: x read once, y written once
+        self.bytes = x.numel() * x.element_size() + y.numel() * y.element_size()
+
+    def kernel_name(self):
+        return "pool_direct"
+
+    def __call__(self, alpha=1.0, beta=0.0, stream=None):
+        s = stream if stream is not None else torch.cuda.current_stream(self.x.device)
+        mic_set_stream(self.handle, s.cuda_stream)
+        mic_pool_forward(self.handle, alpha, self.pd, self.xd, self.x.data_ptr(), beta, self.yd, self.y.data_ptr())
+        return self.y
+
+    def close(self):
+        for d, fn in ((self.xd, mic_tensor_desc_destroy), (self.yd, mic_tensor_desc_destroy),
+                      (self.pd, mic_pool_desc_destroy)):
+            if d is not None:
+                fn(d)
+        self.xd = self.yd = self.pd = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def pool2d_forward(x, window, stride=(1, 1), padding=(0, 0, 0, 0), mode="max", y=None, alpha=1.0, beta=0.0):
+    """y <- alpha * pool(x) + beta * y on torch's current stream (y allocated if None, beta then 0)."""
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    shape = pool_output_shape(tuple(x.shape), window, stride, padding, mode)
+    if y is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing y")
+        fmt = torch.channels_last if (x.stride(1) == 1 and x.shape[1] > 1) else torch.contiguous_format
+        y = torch.empty(shape, dtype=_OUT_DTYPE[x.dtype], device=x.device, memory_format=fmt)
+    plan = PoolPlan(x, y, window, stride, padding, mode)
+    try:
+        plan(alpha, beta)
+    finally:
+        plan.close()
+    return y

@@ -68,6 +68,9 @@ hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);
 // conv_bwd_filter.hip describes.
 hipError_t launch_bwd_filter(Variant v, const ConvParams& p, hipStream_t stream);
 
+// Pooling forward pass (one thread per output); p laid out as pool_fwd.hip describes.
+hipError_t launch_pool_forward(DType dt, const ConvParams& p, hipStream_t stream);
+
 // Data gradient, plain direct kernel (one thread per dx element); p is laid
 // out as conv_bwd_data.hip describes.
 hipError_t launch_bwd_data_direct(DType dt, const ConvParams& p, hipStream_t stream);

@@ -44,6 +44,14 @@ struct mic_conv_desc_st {
     int u, v;
 };
 
+struct mic_pool_desc_st {
+    bool set;
+    mic_pool_mode mode;
+    int r, s;
+    int pad_top, pad_bottom, pad_left, pad_right;
+    int u, v;
+};
+
 namespace {
 
 using miconv::ConvParams;
@@ -748,6 +756,93 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
     return pl;
 }
 
+// ---------------------------------------------------------------- pooling
+
+// Output dims of pooling: the convolution's floor rule over the window.
+mic_status pool_output_dims(const mic_pool_desc_st* pd, const mic_tensor_desc_st* xd, int* n, int* c, int* p,
+                            int* q)
+{
+    if (!pd || !xd || !pd->set || !xd->set) return MIC_STATUS_BAD_PARAM;
+    const int64_t hspan = (int64_t)xd->h + pd->pad_top + pd->pad_bottom - pd->r;
+    const int64_t wspan = (int64_t)xd->w + pd->pad_left + pd->pad_right - pd->s;
+    if (hspan < 0 || wspan < 0) return MIC_STATUS_BAD_PARAM;
+    *n = xd->n;
+    *c = xd->c;
+    *p = (int)(hspan / pd->u + 1);
+    *q = (int)(wspan / pd->v + 1);
+    return MIC_STATUS_SUCCESS;
+}
+
+Plan make_pool_plan(const mic_pool_desc_st* pd, const mic_tensor_desc_st* xd, const void* x,
+                    const mic_tensor_desc_st* yd, const void* y, double alpha, double beta, bool need_pointers)
+{
+    Plan pl;
+    memset(&pl, 0, sizeof(pl));
+    pl.status = MIC_STATUS_BAD_PARAM;
+    if (!yd || !yd->set) return pl;
+    if (need_pointers && (!x || !y)) return pl;
+    int n, c, P, Q;
+    mic_status st = pool_output_dims(pd, xd, &n, &c, &P, &Q);
+    if (st != MIC_STATUS_SUCCESS) {
+        pl.status = st;
+        return pl;
+    }
+    if (yd->n != n || yd->c != c || yd->h != P || yd->w != Q) return pl;
+    if (xd->dtype == MIC_DTYPE_F32 && yd->dtype == MIC_DTYPE_F32)
+        pl.dt = DType::F32;
+    else if (xd->dtype == MIC_DTYPE_F64 && yd->dtype == MIC_DTYPE_F64)
+        pl.dt = DType::F64;
+    else if (xd->dtype == MIC_DTYPE_BF16 && yd->dtype == MIC_DTYPE_F32)
+        pl.dt = DType::BF16;
+    else {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;
+        return pl;
+    }
+    const int64_t M = (int64_t)n * P * Q;
+    if (extent(*xd) >= kMaxOffset || extent(*yd) >= kMaxOffset || M * c >= kMaxOffset ||
+        xd->sn >= kMaxOffset || xd->sc >= kMaxOffset || xd->sh >= kMaxOffset || xd->sw >= kMaxOffset ||
+        yd->sn >= kMaxOffset || yd->sc >= kMaxOffset || yd->sh >= kMaxOffset || yd->sw >= kMaxOffset) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;
+        return pl;
+    }
+    if (need_pointers) {
+        const size_t ie = dtype_size(xd->dtype), oe = dtype_size(yd->dtype);
+        if ((uintptr_t)x % ie || (uintptr_t)y % oe) return pl;
+    }
+    ConvParams& p = pl.p;
+    p.x = x;
+    p.y = const_cast<void*>(y);
+    p.N = n;
+    p.C = c;
+    p.H = xd->h;
+    p.W = xd->w;
+    p.R = pd->r;
+    p.S = pd->s;
+    p.P = P;
+    p.Q = Q;
+    p.u = pd->u;
+    p.v = pd->v;
+    p.pad_top = pd->pad_top;
+    p.pad_left = pd->pad_left;
+    p.sxn = (int)xd->sn;
+    p.sxc = (int)xd->sc;
+    p.sxh = (int)xd->sh;
+    p.sxw = (int)xd->sw;
+    p.syn = (int)yd->sn;
+    p.syk = (int)yd->sc;
+    p.syp = (int)yd->sh;
+    p.syq = (int)yd->sw;
+    p.M = (int)M;
+    p.Kred = (int)pd->mode;    // pool_fwd.hip reads the mode here
+    p.div_pq = FastDiv((uint32_t)(P * Q));
+    p.div_q = FastDiv((uint32_t)Q);
+    p.alpha = alpha;
+    p.beta = beta;
+    snprintf(pl.name, sizeof(pl.name), "pool_direct");
+    pl.status = MIC_STATUS_SUCCESS;
+    return pl;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1042,6 +1137,73 @@ mic_status mic_conv_backward_filter_kernel_name(mic_handle handle, mic_tensor_de
     if (len + 1 > buflen) return MIC_STATUS_BAD_PARAM;
     memcpy(buf, pl.name, len + 1);
     return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_pool_desc_create(mic_pool_desc* desc)
+{
+    if (!desc) return MIC_STATUS_BAD_PARAM;
+    *desc = new (std::nothrow) mic_pool_desc_st();
+    return *desc ? MIC_STATUS_SUCCESS : MIC_STATUS_ALLOC_FAILED;
+}
+
+mic_status mic_pool_desc_destroy(mic_pool_desc desc)
+{
+    if (!desc) return MIC_STATUS_BAD_PARAM;
+    delete desc;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_pool_desc_set(mic_pool_desc desc, mic_pool_mode mode, int window_h, int window_w, int pad_top,
+                             int pad_bottom, int pad_left, int pad_right, int stride_h, int stride_w)
+{
+    if (!desc) return MIC_STATUS_BAD_PARAM;
+    if (mode != MIC_POOL_MAX && mode != MIC_POOL_AVG_INCLUDE_PAD && mode != MIC_POOL_AVG_EXCLUDE_PAD)
+        return MIC_STATUS_BAD_PARAM;
+    if (window_h < 1 || window_w < 1 || stride_h < 1 || stride_w < 1) return MIC_STATUS_BAD_PARAM;
+    if (pad_top < 0 || pad_bottom < 0 || pad_left < 0 || pad_right < 0) return MIC_STATUS_BAD_PARAM;
+    desc->set = true;
+    desc->mode = mode;
+    desc->r = window_h;
+    desc->s = window_w;
+    desc->pad_top = pad_top;
+    desc->pad_bottom = pad_bottom;
+    desc->pad_left = pad_left;
+    desc->pad_right = pad_right;
+    desc->u = stride_h;
+    desc->v = stride_w;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_pool_desc_get(mic_pool_desc desc, mic_pool_mode* mode, int* window_h, int* window_w, int* pad_top,
+                             int* pad_bottom, int* pad_left, int* pad_right, int* stride_h, int* stride_w)
+{
+    if (!desc || !desc->set) return MIC_STATUS_BAD_PARAM;
+    if (mode) *mode = desc->mode;
+    if (window_h) *window_h = desc->r;
+    if (window_w) *window_w = desc->s;
+    if (pad_top) *pad_top = desc->pad_top;
+    if (pad_bottom) *pad_bottom = desc->pad_bottom;
+    if (pad_left) *pad_left = desc->pad_left;
+    if (pad_right) *pad_right = desc->pad_right;
+    if (stride_h) *stride_h = desc->u;
+    if (stride_w) *stride_w = desc->v;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_pool_forward_output_dim(mic_pool_desc pool, mic_tensor_desc x_desc, int* n, int* c, int* p, int* q)
+{
+    if (!n || !c || !p || !q) return MIC_STATUS_BAD_PARAM;
+    return pool_output_dims(pool, x_desc, n, c, p, q);
+}
+
+mic_status mic_pool_forward(mic_handle handle, double alpha, mic_pool_desc pool, mic_tensor_desc x_desc,
+                            const void* x, double beta, mic_tensor_desc y_desc, void* y)
+{
+    if (!handle) return MIC_STATUS_BAD_PARAM;
+    Plan pl = make_pool_plan(pool, x_desc, x, y_desc, y, alpha, beta, true);
+    if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    const hipError_t err = miconv::launch_pool_forward(pl.dt, pl.p, handle->stream);
+    return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
 }
 
 mic_status mic_conv_forward_kernel_name(mic_handle handle, mic_tensor_desc x_desc,

@@ -102,8 +102,25 @@ def _precision():
 
 PRECISION = _precision()
 
+# Pooling between AlexNet's convolutions (3x3 windows, stride 2, no padding,
+# max): after conv2 (27x27x256 -> 13x13, conv3's input size) and after
+# conv5 (13x13x256 -> 6x6).  R, S are the window; K and w_dist are unused.
+POOLING = [
+    Layer("alexnet_pool2", 6, 2, 128, 256, 27, 27, 256, 3, 3, (2, 2), (0, 0, 0, 0), "f32", U11, U11,
+          tags=("pool", "max")),
+    Layer("alexnet_pool5", 6, 5, 128, 256, 13, 13, 256, 3, 3, (2, 2), (0, 0, 0, 0), "f32", U11, U11,
+          tags=("pool", "max")),
+]
+
 CONFIGS = {1: TINY, 2: ALEXNET, 3: OVERFEAT, 4: SPEECH, 5: PRECISION}
 ALL_LAYERS = [l for c in sorted(CONFIGS) for l in CONFIGS[c]]
+
+
+def pool_by_name(name):
+    for lay in POOLING:
+        if lay.name == name:
+            return lay
+    raise KeyError(name)
 
 
 def by_name(name):

@@ -1,6 +1,6 @@
 /*
  * miconv.h -- C ABI of libmiconv, the 2-D convolution forward pass (FPROP)
- * and its data and filter gradients for AMD Instinct MI355X (gfx950).
+ * its data and filter gradients, and pooling, for AMD Instinct MI355X (gfx950).
  *
  * The operation (direct convolution, cross-correlation form, zero padding):
  *
@@ -246,6 +246,57 @@ mic_status mic_conv_backward_filter(mic_handle handle, double alpha,
 mic_status mic_conv_backward_filter_kernel_name(mic_handle handle, mic_tensor_desc x_desc,
                                                 mic_tensor_desc dy_desc, mic_conv_desc conv,
                                                 mic_filter_desc dw_desc, char* buf, size_t buflen);
+
+/* ---------------------------------------------------------------- pooling */
+
+/* Pooling forward pass (cuDNN page, "Proposed Method": pooling among the
+ * library's routines; no formula printed, so the plain reading):
+ *
+ *   MIC_POOL_MAX:             max of X over the window positions inside the
+ *                             H x W plane (padding never wins; 0 if none)
+ *   MIC_POOL_AVG_INCLUDE_PAD: (sum of X over the positions inside) / (R*S)
+ *   MIC_POOL_AVG_EXCLUDE_PAD: (sum over the positions inside) / (their
+ *                             number; 0 if none)
+ *   y[n,c,p,q] = alpha * that + beta * y[n,c,p,q]
+ *
+ * The window geometry is the convolution's: R x S window at (p*u - pad_top,
+ * q*v - pad_left), output size by the same floor rule.  Channels are pooled
+ * independently. */
+typedef enum {
+    MIC_POOL_MAX = 0,
+    MIC_POOL_AVG_INCLUDE_PAD = 1,
+    MIC_POOL_AVG_EXCLUDE_PAD = 2
+} mic_pool_mode;
+
+typedef struct mic_pool_desc_st* mic_pool_desc;
+
+mic_status mic_pool_desc_create(mic_pool_desc* desc);
+mic_status mic_pool_desc_destroy(mic_pool_desc desc);
+
+/* Mode, window (>= 1), per-side padding (>= 0), strides (>= 1); else
+ * MIC_STATUS_BAD_PARAM. */
+mic_status mic_pool_desc_set(mic_pool_desc desc, mic_pool_mode mode, int window_h, int window_w,
+                             int pad_top, int pad_bottom, int pad_left, int pad_right,
+                             int stride_h, int stride_w);
+mic_status mic_pool_desc_get(mic_pool_desc desc, mic_pool_mode* mode, int* window_h, int* window_w,
+                             int* pad_top, int* pad_bottom, int* pad_left, int* pad_right,
+                             int* stride_h, int* stride_w);
+
+/* Output dims (N, C, P, Q), host only; MIC_STATUS_BAD_PARAM if a descriptor
+ * is unset or the window exceeds the padded input. */
+mic_status mic_pool_forward_output_dim(mic_pool_desc pool, mic_tensor_desc x_desc,
+                                       int* n, int* c, int* p, int* q);
+
+/* y <- alpha * pool(x) + beta * y on the handle's stream, asynchronously.
+ * Element types (x, y): (F32, F32), (F64, F64), (BF16, F32).  x and y with
+ * any element strides; y's dims must equal the output dims.  Ownership,
+ * alpha/beta, beta == 0 and size rules as for mic_conv_forward.  No
+ * workspace.  Errors: MIC_STATUS_BAD_PARAM (null handle/descriptor/pointer,
+ * unset descriptor, shape mismatch), MIC_STATUS_NOT_SUPPORTED (dtype
+ * combination, size limit), MIC_STATUS_LAUNCH_FAILED. */
+mic_status mic_pool_forward(mic_handle handle, double alpha, mic_pool_desc pool,
+                            mic_tensor_desc x_desc, const void* x, double beta,
+                            mic_tensor_desc y_desc, void* y);
 
 #ifdef __cplusplus
 }

@@ -346,3 +346,29 @@ def test_wgrad_shape_and_type_errors(monkeypatch):
     l = mic.lib()
     assert l.mic_conv_backward_filter(None, 1.0, None, None, None, None, None, 0.0, None, None) == \
         mic.MIC_STATUS_BAD_PARAM
+
+
+# ---------------------------------------------------------------- pooling (host side)
+
+def test_pool_descriptor_and_output_dims():
+    d = mic.mic_pool_desc_create()
+    try:
+        with pytest.raises(mic.MicError):
+            mic.mic_pool_desc_get(d)                       # never set
+        mic.mic_pool_desc_set(d, mic.MIC_POOL_AVG_EXCLUDE_PAD, 3, 2, 1, 0, 2, 1, 2, 1)
+        assert mic.mic_pool_desc_get(d) == (2, 3, 2, 1, 0, 2, 1, 2, 1)
+        for bad in [(3, 3, 3, 0, 0, 0, 0, 1, 1), (0, 0, 3, 0, 0, 0, 0, 1, 1), (0, 3, 3, -1, 0, 0, 0, 1, 1),
+                    (0, 3, 3, 0, 0, 0, 0, 0, 1)]:
+            with pytest.raises(mic.MicError) as e:
+                mic.mic_pool_desc_set(d, *bad)
+            assert e.value.status == mic.MIC_STATUS_BAD_PARAM
+    finally:
+        mic.mic_pool_desc_destroy(d)
+    for lay in workloads.POOLING:
+        pb = oracle.make_problem(lay.x_shape, (1, 1, 1, 1), (1, lay.C, lay.R, lay.S), lay.stride, lay.padding)
+        P, Q = oracle.output_dims(pb)
+        assert mic.pool_output_shape(lay.x_shape, (lay.R, lay.S), lay.stride, lay.padding) == (lay.N, lay.C, P, Q)
+    with pytest.raises(mic.MicError):                      # window larger than the padded input
+        mic.pool_output_shape((1, 1, 3, 3), (5, 1), (1, 1), (0, 1, 0, 0))
+    l = mic.lib()
+    assert l.mic_pool_forward(None, 1.0, None, None, None, 0.0, None, None) == mic.MIC_STATUS_BAD_PARAM
