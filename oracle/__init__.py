@@ -1,5 +1,5 @@
 """CPU oracle for the 2-D convolution forward pass, its data and filter
-gradients, and pooling (fp64, plain nested loops).
+gradients, pooling and the batch-reduce GEMM (fp64, plain nested loops).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
@@ -80,6 +80,10 @@ def _load():
         lib.oracle_pool_forward.argtypes = [pp, dp, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                             dp, dp, ctypes.c_int]
         lib.oracle_pool_forward.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        lib.oracle_brgemm.argtypes = [i64, i64, i64, i64, dp, i64, i64, i64, dp, i64, i64, i64,
+                                      ctypes.c_double, ctypes.c_double, dp, dp, dp, ctypes.c_int]
+        lib.oracle_brgemm.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
@@ -330,3 +334,33 @@ def pool2d_forward(x, window, stride=(1, 1), padding=(0, 0, 0, 0), mode="max", a
     if rc != 0:
         raise ValueError("oracle rejected the problem")
     return y
+
+
+def brgemm(a, b, alpha=1.0, beta=0.0, c_old=None, nthreads=0):
+    """Batch-reduce GEMM: C = alpha * sum_i a[i] @ b[i] + beta * c_old.
+
+    a: float64 (batch, M, K), b: float64 (batch, K, N), any non-negative
+    strides (views are fine).  Returns (C, bound), float64 packed (M, N).
+    """
+    if a.dtype != np.float64 or b.dtype != np.float64:
+        raise TypeError("oracle inputs are float64")
+    if a.ndim != 3 or b.ndim != 3 or a.shape[0] != b.shape[0] or a.shape[2] != b.shape[1]:
+        raise ValueError("shapes must be (batch, M, K) and (batch, K, N)")
+    sa = [s // 8 for s in a.strides]
+    sb = [s // 8 for s in b.strides]
+    if any(s < 0 for s in sa + sb):
+        raise ValueError("strides must be non-negative")
+    batch, M, K = a.shape
+    N = b.shape[2]
+    c = np.empty((M, N))
+    bound = np.empty((M, N))
+    co = None
+    if beta != 0.0:
+        if c_old is None:
+            raise ValueError("beta != 0 needs c_old")
+        co = np.ascontiguousarray(c_old, dtype=np.float64)
+    rc = _load().oracle_brgemm(M, N, K, batch, _dptr(a), sa[0], sa[1], sa[2], _dptr(b), sb[0], sb[1], sb[2],
+                               float(alpha), float(beta), _dptr(co), _dptr(c), _dptr(bound), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the sizes")
+    return c, bound

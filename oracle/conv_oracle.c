@@ -1,7 +1,7 @@
 /*
  * oracle/conv_oracle.c -- plain CPU reference for the 2-D convolution forward
- * pass (FPROP), its gradients (backward passes with respect to x and F) and
- * the pooling forward pass.  TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and
+ * pass (FPROP), its gradients (backward passes with respect to x and F), the
+ * pooling forward pass and the batch-reduce GEMM.  TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and
  * the CPU-baseline leg of the benchmark may load this library.  It shares no
  * code, header, table or helper with the GPU path.
  *
@@ -464,6 +464,50 @@ int oracle_pool_forward(const oracle_conv_problem* pb, const double* x, int mode
                     y[o] = val;
                 }
             }
+        }
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/*
+ * Batch-reduce GEMM, the single-building-block page's kernel ("Proposed
+ * Method": the products of a batch of input sub-tensor blocks reduced into
+ * one output block), written out:
+ *
+ *   C[m,n] = alpha * sum_{i<batch} sum_{k<K} A_i[m,k] * B_i[k,n] + beta * C_old[m,n]
+ *   A_i[m,k] = a[i*sa_i + m*sa_m + k*sa_k],  B_i[k,n] = b[i*sb_i + k*sb_k + n*sb_n]
+ *   bound[m,n] = sum of |A_i[m,k] * B_i[k,n]|
+ *
+ * C and bound are packed M x N row-major; C_old (read only when beta != 0)
+ * likewise.  Order i, k, in double.  Returns 0, or -1 on bad sizes.
+ */
+int oracle_brgemm(int64_t M, int64_t N, int64_t K, int64_t batch,
+                  const double* a, int64_t sa_i, int64_t sa_m, int64_t sa_k,
+                  const double* b, int64_t sb_i, int64_t sb_k, int64_t sb_n,
+                  double alpha, double beta, const double* c_old,
+                  double* c, double* bound, int nthreads)
+{
+    if (M < 1 || N < 1 || K < 1 || batch < 1) return -1;
+    if (beta != 0.0 && c_old == NULL) return -1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic, 16) num_threads(nthreads)
+#endif
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, bnd = 0.0;
+            for (int64_t i = 0; i < batch; ++i) {
+                for (int64_t k = 0; k < K; ++k) {
+                    double prod = a[i * sa_i + m * sa_m + k * sa_k] * b[i * sb_i + k * sb_k + n * sb_n];
+                    acc += prod;
+                    bnd += fabs(prod);
+                }
+            }
+            double val = alpha * acc;
+            if (beta != 0.0) val += beta * c_old[m * N + n];
+            if (c) c[m * N + n] = val;
+            if (bound) bound[m * N + n] = bnd;
         }
     }
     (void)nthreads;

@@ -75,6 +75,14 @@ MUTANTS_POOL = {
                                      "for (int64_t s = 0; s < pb->S - 1; ++s) {\n            int64_t h = p * pb->u"),
 }
 
+# slips in the batch-reduce GEMM, caught by test_oracle_brgemm.py
+MUTANTS_BRGEMM = {
+    "brgemm_last_batch_dropped": ("for (int64_t i = 0; i < batch; ++i) {", "for (int64_t i = 0; i < batch - 1; ++i) {"),
+    "brgemm_b_strides_swapped": ("b[i * sb_i + k * sb_k + n * sb_n]", "b[i * sb_i + k * sb_n + n * sb_k]"),
+    "brgemm_a_batch_stride_ignored": ("a[i * sa_i + m * sa_m + k * sa_k]", "a[m * sa_m + k * sa_k]"),
+    "brgemm_beta_dropped": ("if (beta != 0.0) val += beta * c_old[m * N + n];", "if (beta != 0.0) val += 0.0 * c_old[m * N + n];"),
+}
+
 
 def _build_and_run(name, old, new, tmp, pins="test_oracle.py"):
     with open(SRC) as fh:
@@ -99,6 +107,7 @@ def test_every_mutant_is_caught():
     jobs += [(n, o, w, "test_oracle_dgrad.py") for n, (o, w) in MUTANTS_DGRAD.items()]
     jobs += [(n, o, w, "test_oracle_wgrad.py") for n, (o, w) in MUTANTS_WGRAD.items()]
     jobs += [(n, o, w, "test_oracle_pool.py") for n, (o, w) in MUTANTS_POOL.items()]
+    jobs += [(n, o, w, "test_oracle_brgemm.py") for n, (o, w) in MUTANTS_BRGEMM.items()]
     with tempfile.TemporaryDirectory() as tmp:
         with ThreadPoolExecutor(max_workers=4) as pool:
             results = list(pool.map(lambda j: _build_and_run(j[0], j[1], j[2], tmp, j[3]), jobs))
