@@ -7,7 +7,8 @@ data, He-normal weights).  One step = the workload's forward passes, each
 one kernel launch of libmiconv through the C ABI.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                    [--workload alexnet|overfeat|speech|tiny|prec_f64|prec_bf16|alexnet_pool]
+                    [--workload alexnet|overfeat|speech|tiny|prec_f64|prec_bf16|alexnet_pool|
+                                alexnet_fc|alexnet_fc_f64|alexnet_fc_bf16]
                     [--op fprop|dgrad|wgrad]
 
 Prints one JSON line.  ``value`` = 2*N*K*C*R*S*P*Q summed over the step's
@@ -19,7 +20,9 @@ few images of every layer).  ``--op dgrad`` / ``--op wgrad`` time the data /
 filter gradient of the same layers instead (dy seeded uniform [-1, 1]; the
 same FLOP count).  ``--workload alexnet_pool`` times AlexNet's two max-pooling
 layers (after conv2 and conv5) and reports bandwidth (|x| + |y| per second)
-against the HBM roofline.
+against the HBM roofline.  ``--workload alexnet_fc`` times AlexNet's
+fully-connected layers fc6-fc8 at minibatch 128 as batch-reduce GEMMs
+(``_f64`` / ``_bf16``: fc6 in that type), 2*m*n*k*batch FLOP per layer.
 """
 import argparse
 import hashlib
@@ -34,7 +37,8 @@ sys.path.insert(0, ROOT)
 # MI355X dense MFMA peaks (256 CU x 2.4 GHz): fp32 256, fp64 128, bf16 4096 FLOP/clk/CU
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "bf16": 2516.6}
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_alexnet_fp32.md")
-WORKLOADS = ("alexnet", "overfeat", "speech", "tiny", "prec_f64", "prec_bf16", "alexnet_pool")
+WORKLOADS = ("alexnet", "overfeat", "speech", "tiny", "prec_f64", "prec_bf16", "alexnet_pool", "alexnet_fc",
+             "alexnet_fc_f64", "alexnet_fc_bf16")
 HBM_PEAK_GBS = 8000.0
 
 
@@ -136,6 +140,8 @@ def main():
     dev = torch.device("cuda", 0)
     if args.workload == "alexnet_pool":
         return bench_pool(args, torch, mic, gen, workloads, dev)
+    if args.workload.startswith("alexnet_fc"):
+        return bench_fc(args, torch, mic, gen, workloads, dev)
     layers, wl_name = workload_layers(args.workload)
     dtype = layers[0].dtype
     peak = MFMA_PEAK_TFLOPS[dtype]
@@ -329,6 +335,110 @@ def bench_pool(args, torch, mic, gen, workloads, dev):
     print(json.dumps(line), flush=True)
     for _, plan, _ in plans:
         plan.close()
+
+
+def bench_fc(args, torch, mic, gen, workloads, dev):
+    """AlexNet's fully-connected layers as batch-reduce GEMMs: TFLOP/s against the MFMA roofline."""
+    if args.workload == "alexnet_fc":
+        layers = [workloads.fc_by_name(n) for n in ("alexnet_fc6", "alexnet_fc7", "alexnet_fc8")]
+        wl_name = "alexnet_fc6-8_fp32_n128"
+    elif args.workload == "alexnet_fc_f64":
+        layers, wl_name = [workloads.fc_by_name("alexnet_fc6_f64")], "alexnet_fc6_fp64_n128"
+    else:
+        layers, wl_name = [workloads.fc_by_name("alexnet_fc6_bf16")], "alexnet_fc6_bf16in_fp32acc_n128"
+    dtype = layers[0].dtype
+    tdt = {"f32": torch.float32, "f64": torch.float64, "bf16": torch.bfloat16}[dtype]
+    odt = torch.float64 if dtype == "f64" else torch.float32
+    peak = MFMA_PEAK_TFLOPS[dtype]
+    runs = []
+    for lay in layers:
+        F = lay.features
+        x = gen.round_to(gen.draw(lay.x_dist, gen.derive_seed(lay.config, lay.layer, 0), (lay.m, F)), dtype)
+        w = gen.round_to(gen.draw(lay.w_dist, gen.derive_seed(lay.config, lay.layer, 1), (lay.n, F)), dtype)
+        xt = torch.from_numpy(x).to(tdt).to(dev)
+        wt = torch.from_numpy(w).to(tdt).to(dev)
+        a = xt.as_strided((lay.batch, lay.m, lay.k), (lay.k, F, 1))
+        b = wt.as_strided((lay.batch, lay.k, lay.n), (lay.k, 1, F))
+        c = torch.zeros((lay.m, lay.n), dtype=odt, device=dev)
+        flops = 2.0 * lay.m * lay.n * F
+        runs.append((lay, a, b, c, flops, x, w))
+    # algorithmic HBM bytes of a layer: A and B read once, C written once
+    esz = {"f32": 4, "f64": 8, "bf16": 2}[dtype]
+    osz = 8 if dtype == "f64" else 4
+    hbm_bytes = {r[0].name: esz * (r[0].m + r[0].n) * r[0].features + osz * r[0].m * r[0].n for r in runs}
+    stream = torch.cuda.current_stream(dev)
+    flops_step = sum(r[4] for r in runs)
+
+    def step():
+        for _, a, b, c, _, _, _ in runs:
+            mic.brgemm(a, b, c)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_layer = []
+    reps = max(5, args.steps)
+    for lay, a, b, c, flops, _, _ in runs:
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        mic.brgemm(a, b, c)
+        ev0.record(stream)
+        for _ in range(reps):
+            mic.brgemm(a, b, c)
+        ev1.record(stream)
+        ev1.synchronize()
+        us = ev0.elapsed_time(ev1) / reps * 1e3
+        per_layer.append({"layer": lay.name, "kernel": mic.brgemm_kernel_name_for(a, b, c),
+                          "us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+                          "gbs": round(hbm_bytes[lay.name] / (us * 1e-6) / 1e9, 1),
+                          "flop_per_byte": round(flops / hbm_bytes[lay.name], 1)})
+    dom = max(per_layer, key=lambda r: r["us"])
+    # the dominant layer's bound: MFMA when its FLOP per HBM byte exceeds the
+    # ridge point (peak FLOP/s over peak bytes/s), else HBM
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if dom["flop_per_byte"] >= ridge:
+        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": peak, "unit": "TFLOP/s",
+                "frac": round(dom["tflops"] / peak, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": None, "kernel": dom["kernel"], "avg_us": dom["us"], "ridge_flop_per_byte": round(ridge, 1)})
+    cpu = None
+    if not args.no_cpu:
+        import numpy as np
+        import oracle
+        lay, _, _, _, flops, x, w = runs[0]
+
+        def ora(rows):
+            xa = np.ascontiguousarray(x[:rows].reshape(rows, lay.batch, lay.k).transpose(1, 0, 2))
+            wb = np.ascontiguousarray(w.reshape(lay.n, lay.batch, lay.k).transpose(1, 2, 0))
+            t = time.perf_counter()
+            oracle.brgemm(xa, wb)
+            return time.perf_counter() - t
+
+        t1 = ora(1)
+        rows = int(max(1, min(lay.m, args.cpu_seconds / max(t1, 1e-9))))
+        dt = ora(rows) if rows > 1 else t1
+        cpu = {"value": round(flops * rows / lay.m / dt / 1e12, 5), "unit": "TFLOP/s",
+               "cores": oracle.default_threads(), "kind": "oracle",
+               "sample": "first %d of %d rows of %s (%.2f s)" % (rows, lay.m, lay.name, dt)}
+    value = flops_step / (elapsed / args.steps) / 1e12
+    line = {
+        "metric": "fully-connected layer throughput as batch-reduce GEMM (2*m*n*k/t), 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded uniform [-1, 1] inputs, He-normal weights)",
+        "config": {"workload": wl_name, "op": "brgemm", "layers": [r[0].name for r in runs]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layers": per_layer,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def run_oracle(op, lay, a, w):

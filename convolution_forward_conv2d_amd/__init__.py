@@ -101,6 +101,10 @@ _SIGS = {
     "mic_pool_desc_get": ([_vp, _ip, _ip, _ip, _ip, _ip, _ip, _ip, _ip, _ip], _i),
     "mic_pool_forward_output_dim": ([_vp, _vp, _ip, _ip, _ip, _ip], _i),
     "mic_pool_forward": ([_vp, ctypes.c_double, _vp, _vp, _vp, ctypes.c_double, _vp, _vp], _i),
+    "mic_brgemm": ([_vp, _i, _i, _i, _i, _i, ctypes.c_double, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                    ctypes.c_double, _vp, _i64, _i64], _i),
+    "mic_brgemm_kernel_name": ([_vp, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                ctypes.c_char_p, ctypes.c_size_t], _i),
 }
 
 
@@ -308,6 +312,22 @@ def mic_pool_forward_output_dim(pool, x_desc):
 def mic_pool_forward(handle, alpha, pool, x_desc, x_ptr, beta, y_desc, y_ptr):
     _check(lib().mic_pool_forward(handle, float(alpha), pool, x_desc, _vp(x_ptr), float(beta), y_desc,
                                   _vp(y_ptr)), "mic_pool_forward")
+
+
+def mic_brgemm(handle, dtype, m, n, k, batch, alpha, a_ptr, a_stride_batch, a_stride_m, a_stride_k, b_ptr,
+               b_stride_batch, b_stride_k, b_stride_n, beta, c_ptr, c_stride_m, c_stride_n):
+    _check(lib().mic_brgemm(handle, dtype, m, n, k, batch, float(alpha), _vp(a_ptr), a_stride_batch, a_stride_m,
+                            a_stride_k, _vp(b_ptr), b_stride_batch, b_stride_k, b_stride_n, float(beta),
+                            _vp(c_ptr), c_stride_m, c_stride_n), "mic_brgemm")
+
+
+def mic_brgemm_kernel_name(handle, dtype, m, n, k, batch, a_stride_batch, a_stride_m, a_stride_k, b_stride_batch,
+                           b_stride_k, b_stride_n, c_stride_m, c_stride_n):
+    buf = ctypes.create_string_buffer(64)
+    _check(lib().mic_brgemm_kernel_name(handle, dtype, m, n, k, batch, a_stride_batch, a_stride_m, a_stride_k,
+                                        b_stride_batch, b_stride_k, b_stride_n, c_stride_m, c_stride_n, buf,
+                                        len(buf)), "mic_brgemm_kernel_name")
+    return buf.value.decode()
 
 
 # ---------------------------------------------------------------- torch-facing helpers
@@ -629,3 +649,51 @@ def pool2d_forward(x, window, stride=(1, 1), padding=(0, 0, 0, 0), mode="max", y
     finally:
         plan.close()
     return y
+
+
+def brgemm(a, b, c=None, alpha=1.0, beta=0.0):
+    """c <- alpha * sum_i a[i] @ b[i] + beta * c on torch's current stream.
+
+    a: (batch, m, k) and b: (batch, k, n) GPU tensors of one dtype (any
+    element strides, e.g. views of blocks of a larger matrix); c: (m, n),
+    allocated when None (fp32 for bf16 inputs; beta must then be 0).
+    """
+    if not a.is_cuda or not b.is_cuda:
+        raise ValueError("a and b must be GPU tensors")
+    if a.dim() != 3 or b.dim() != 3:
+        raise ValueError("a must be (batch, m, k) and b (batch, k, n)")
+    batch, m, k = a.shape
+    if b.shape[0] != batch or b.shape[1] != k:
+        raise ValueError("a %s and b %s do not chain" % (tuple(a.shape), tuple(b.shape)))
+    if a.dtype != b.dtype or a.dtype not in _TORCH_DTYPE:
+        raise TypeError("a and b need one supported dtype, got %s and %s" % (a.dtype, b.dtype))
+    n = b.shape[2]
+    if c is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing c")
+        c = torch.empty((m, n), dtype=_OUT_DTYPE[a.dtype], device=a.device)
+    if c.dim() != 2 or tuple(c.shape) != (m, n) or c.dtype != _OUT_DTYPE[a.dtype]:
+        raise ValueError("c must be (%d, %d) of %s" % (m, n, _OUT_DTYPE[a.dtype]))
+    h = handle_for(a.device)
+    mic_set_stream(h, torch.cuda.current_stream(a.device).cuda_stream)
+    mic_brgemm(h, _TORCH_DTYPE[a.dtype], m, n, k, batch, alpha, a.data_ptr(), *a.stride(), b.data_ptr(),
+               *b.stride(), beta, c.data_ptr(), *c.stride())
+    return c
+
+
+def brgemm_kernel_name(dtype, m, n, k, batch=1, a_strides=None, b_strides=None, c_strides=None):
+    """Kernel variant mic_brgemm picks (host only; dtype a torch dtype).
+
+    Strides in elements as mic_brgemm takes them; by default A (batch, m, k),
+    B (batch, k, n) and C (m, n) packed row-major.  Also accepts tensors'
+    .stride() tuples."""
+    sa = tuple(a_strides) if a_strides is not None else (m * k, k, 1)
+    sb = tuple(b_strides) if b_strides is not None else (k * n, n, 1)
+    sc = tuple(c_strides) if c_strides is not None else (n, 1)
+    return mic_brgemm_kernel_name(None, _TORCH_DTYPE[dtype], m, n, k, batch, *sa, *sb, *sc)
+
+
+def brgemm_kernel_name_for(a, b, c):
+    """Kernel variant mic_brgemm picks for these tensors (as brgemm() would pass them)."""
+    batch, m, k = a.shape
+    return brgemm_kernel_name(a.dtype, m, b.shape[2], k, batch, a.stride(), b.stride(), c.stride())

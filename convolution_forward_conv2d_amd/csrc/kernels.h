@@ -43,6 +43,21 @@ enum class Variant : int {
     WG_F64_64x64,
     WG_BF16_128x128,
     WG_BF16_64x64,
+    BR_F32_128x128,         // batch-reduce GEMM, shared-LDS tiles (brgemm.hip)
+    BR_F32_64x64,
+    BR_F32_32x64,
+    BR_F64_64x64,
+    BR_F64_32x64,
+    BR_BF16_128x128,
+    BR_BF16_64x64,
+    BR_BF16_32x128,
+    WS_F32_64x64,           // batch-reduce GEMM, waves split the reduction (brgemm.hip)
+    WS_F32_32x64,
+    WS_F32_16x32,
+    WS_F64_32x64,
+    WS_F64_16x32,
+    WS_BF16_32x64,
+    WS_BF16_16x32,
     COUNT
 };
 
@@ -67,6 +82,14 @@ hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);
 // Filter gradient (implicit GEMM over the output positions); p laid out as
 // conv_bwd_filter.hip describes.
 hipError_t launch_bwd_filter(Variant v, const ConvParams& p, hipStream_t stream);
+
+// Batch-reduce GEMM; p laid out as brgemm.hip describes.  16-byte operand
+// loads are chosen inside when strides, k and alignment allow them.
+hipError_t launch_brgemm(Variant v, const ConvParams& p, hipStream_t stream);
+// Wave-split variants: the reduction elements one 16-byte load reads (A and
+// B must be contiguous along k, k a multiple of it, loads 16-byte aligned);
+// 0 for every other variant.
+int brgemm_ws_run(Variant v);
 
 // Pooling forward pass (one thread per output); p laid out as pool_fwd.hip describes.
 hipError_t launch_pool_forward(DType dt, const ConvParams& p, hipStream_t stream);

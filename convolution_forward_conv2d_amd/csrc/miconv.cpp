@@ -137,6 +137,35 @@ const Candidate kWgBF16[] = {
     {Variant::WG_BF16_128x128, 128, 128, "wg_bf16_128x128"},
     {Variant::WG_BF16_64x64, 64, 64, "wg_bf16_64x64"},
 };
+// batch-reduce GEMM (brgemm.hip): shared-LDS tiles for large products
+const Candidate kBrF32[] = {
+    {Variant::BR_F32_128x128, 128, 128, "br_f32_128x128"},
+    {Variant::BR_F32_64x64, 64, 64, "br_f32_64x64"},
+    {Variant::BR_F32_32x64, 32, 64, "br_f32_32x64"},
+};
+const Candidate kBrF64[] = {
+    {Variant::BR_F64_64x64, 64, 64, "br_f64_64x64"},
+    {Variant::BR_F64_32x64, 32, 64, "br_f64_32x64"},
+};
+const Candidate kBrBF16[] = {
+    {Variant::BR_BF16_128x128, 128, 128, "br_bf16_128x128"},
+    {Variant::BR_BF16_64x64, 64, 64, "br_bf16_64x64"},
+    {Variant::BR_BF16_32x128, 32, 128, "br_bf16_32x128"},
+};
+// ... and the wave-split kernel for skinny ones (contiguous k only), largest tile first
+const Candidate kWsF32[] = {
+    {Variant::WS_F32_64x64, 64, 64, "ws_f32_64x64"},
+    {Variant::WS_F32_32x64, 32, 64, "ws_f32_32x64"},
+    {Variant::WS_F32_16x32, 16, 32, "ws_f32_16x32"},
+};
+const Candidate kWsF64[] = {
+    {Variant::WS_F64_32x64, 32, 64, "ws_f64_32x64"},
+    {Variant::WS_F64_16x32, 16, 32, "ws_f64_16x32"},
+};
+const Candidate kWsBF16[] = {
+    {Variant::WS_BF16_32x64, 32, 64, "ws_bf16_32x64"},
+    {Variant::WS_BF16_16x32, 16, 32, "ws_bf16_16x32"},
+};
 
 // Tap-batched halo kernels (conv_fwd_halo.hip): fixed R x S, CB channels per
 // chunk, padded input width <= WP, per-tile slot span <= SL.
@@ -756,6 +785,157 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
     return pl;
 }
 
+// ---------------------------------------------------------------- batch-reduce GEMM
+
+// Highest element offset of an operand with the given extents and strides
+// (all >= 0), or -1 when a stride is negative.
+int64_t operand_extent(int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t n2, int64_t s2)
+{
+    if (s0 < 0 || s1 < 0 || s2 < 0) return -1;
+    return (n0 - 1) * s0 + (n1 - 1) * s1 + (n2 - 1) * s2;
+}
+
+// C[m, n] <- alpha sum_i A_i B_i + beta C (single-building-block page,
+// "Proposed Method"): rows m map to the kernel's M, columns n to its K,
+// the per-block reduction k to Kred and the batch to N.
+Plan make_brgemm_plan(const mic_handle_st* h, mic_dtype dtype, int m, int n, int k, int batch, double alpha,
+                      const void* a, int64_t sa_i, int64_t sa_m, int64_t sa_k, const void* b, int64_t sb_i,
+                      int64_t sb_k, int64_t sb_n, double beta, const void* c, int64_t sc_m, int64_t sc_n,
+                      bool need_pointers)
+{
+    Plan pl;
+    memset(&pl, 0, sizeof(pl));
+    pl.status = MIC_STATUS_BAD_PARAM;
+    if (m < 0 || n < 0 || k < 0 || batch < 0) return pl;
+    if (sa_i < 0 || sa_m < 0 || sa_k < 0 || sb_i < 0 || sb_k < 0 || sb_n < 0 || sc_m < 0 || sc_n < 0) return pl;
+    if (!valid_dtype(dtype)) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;
+        return pl;
+    }
+    pl.dt = dtype == MIC_DTYPE_F32 ? DType::F32 : dtype == MIC_DTYPE_F64 ? DType::F64 : DType::BF16;
+    const bool empty_c = m == 0 || n == 0;
+    const bool empty_red = k == 0 || batch == 0;
+    if (need_pointers && !empty_c && (!c || (!empty_red && (!a || !b)))) return pl;
+    // C's elements must not alias: distinct (m, n) need distinct offsets
+    if (!empty_c && ((m > 1 && sc_m == 0) || (n > 1 && sc_n == 0))) return pl;
+    const int64_t ea = empty_c || empty_red ? 0 : operand_extent(batch, sa_i, m, sa_m, k, sa_k);
+    const int64_t eb = empty_c || empty_red ? 0 : operand_extent(batch, sb_i, k, sb_k, n, sb_n);
+    const int64_t ec = empty_c ? 0 : operand_extent(1, 0, m, sc_m, n, sc_n);
+    if (ea >= kMaxOffset || eb >= kMaxOffset || ec >= kMaxOffset || (int64_t)batch * k >= kMaxOffset) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;
+        return pl;
+    }
+    if (need_pointers && !empty_c) {
+        const size_t ie = dtype_size(dtype), oe = pl.dt == DType::F64 ? 8 : 4;
+        if ((uintptr_t)c % oe) return pl;
+        if (!empty_red && ((uintptr_t)a % ie || (uintptr_t)b % ie)) return pl;
+    }
+    ConvParams& p = pl.p;
+    p.x = a;
+    p.w = b;
+    p.y = const_cast<void*>(c);
+    p.N = batch;
+    p.M = m;
+    p.K = n;
+    p.Kred = k;
+    p.sxn = (int)sa_i;
+    p.sxh = (int)sa_m;
+    p.sxw = (int)sa_k;
+    p.sdn = (int)sb_i;
+    p.sdk = (int)sb_k;
+    p.sdq = (int)sb_n;
+    p.syn = (int)sc_m;
+    p.syk = (int)sc_n;
+    p.div_pq = FastDiv(1);
+    p.div_q = FastDiv(1);
+    p.div_rs = FastDiv((uint32_t)(k > 0 ? k : 1));
+    p.alpha = alpha;
+    p.beta = beta;
+
+    const Candidate* list = kBrF32;
+    int count = (int)(sizeof(kBrF32) / sizeof(kBrF32[0]));
+    const Candidate* ws = kWsF32;
+    int ws_count = (int)(sizeof(kWsF32) / sizeof(kWsF32[0]));
+    if (pl.dt == DType::F64) {
+        list = kBrF64;
+        count = (int)(sizeof(kBrF64) / sizeof(kBrF64[0]));
+        ws = kWsF64;
+        ws_count = (int)(sizeof(kWsF64) / sizeof(kWsF64[0]));
+    } else if (pl.dt == DType::BF16) {
+        list = kBrBF16;
+        count = (int)(sizeof(kBrBF16) / sizeof(kBrBF16[0]));
+        ws = kWsBF16;
+        ws_count = (int)(sizeof(kWsBF16) / sizeof(kWsBF16[0]));
+    }
+    // the wave-split kernel reads the reduction with 16-byte loads: A and B
+    // contiguous along k, k a multiple of a load's elements, every load
+    // 16-byte aligned (pointer alignment is known only at a call)
+    const int ve = 16 / (int)dtype_size(dtype);
+    auto ws_ok = [&](const Candidate& cd) {
+        const int run = brgemm_ws_run(cd.v);
+        if (run == 0 || k == 0 || batch == 0 || sa_k != 1 || sb_k != 1 || k % run) return false;
+        if (batch > 1 && (sa_i % ve || sb_i % ve)) return false;
+        if ((m > 1 && sa_m % ve) || (n > 1 && sb_n % ve)) return false;
+        return !need_pointers || ((uintptr_t)a % 16 == 0 && (uintptr_t)b % 16 == 0);
+    };
+    const int num_cu = h ? h->num_cu : kDefaultCUs;
+    const char* force = getenv("MIC_FORCE_BRGEMM_VARIANT");
+    if (force && !force[0]) force = nullptr;
+    bool found = false;
+    if (force) {
+        for (int i = 0; i < count && !found; ++i)
+            if (strcmp(force, list[i].name) == 0) {
+                pl.cand = list[i];
+                found = true;
+            }
+        for (int i = 0; i < ws_count && !found; ++i)
+            if (strcmp(force, ws[i].name) == 0) {
+                if (!ws_ok(ws[i])) {
+                    pl.status = MIC_STATUS_NOT_SUPPORTED;   // forced onto operands it cannot read
+                    return pl;
+                }
+                pl.cand = ws[i];
+                found = true;
+            }
+    } else {
+        // Products whose 128 x 128 tiles cannot fill the chip go to the
+        // wave-split kernel (measured on MI355X: faster there, the shared-LDS
+        // tiles faster once 128 x 128 tiles fill every compute unit): its
+        // largest tile that still gives every compute unit one, else its
+        // smallest.
+        const int64_t big = (int64_t)((m + 127) / 128) * ((n + 127) / 128);
+        if (big < num_cu) {
+            for (int i = 0; i < ws_count && !found; ++i) {
+                const int64_t tiles = (int64_t)((m + ws[i].tm - 1) / ws[i].tm) * ((n + ws[i].tn - 1) / ws[i].tn);
+                if (ws_ok(ws[i]) && (tiles >= num_cu || i == ws_count - 1)) {
+                    pl.cand = ws[i];
+                    found = true;
+                }
+            }
+        }
+        double best = 0;
+        for (int i = 0; i < count && !found; ++i) {
+            const int64_t tiles = (int64_t)((m + list[i].tm - 1) / list[i].tm) * ((n + list[i].tn - 1) / list[i].tn);
+            const int64_t rounds = (tiles + num_cu - 1) / num_cu;
+            const double reuse = (double)list[i].tm * list[i].tn / (list[i].tm + list[i].tn);
+            const double eff = reuse >= 48.0 ? 1.0 : reuse / 48.0;
+            const double cost = (double)rounds * list[i].tm * list[i].tn / eff;
+            if (i == 0 || cost < best) {
+                best = cost;
+                pl.cand = list[i];
+            }
+        }
+        found = true;
+    }
+    if (!found) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;   // a forced variant of another type
+        return pl;
+    }
+    snprintf(pl.name, sizeof(pl.name), "%s", pl.cand.name);
+    pl.status = MIC_STATUS_SUCCESS;
+    return pl;
+}
+
 // ---------------------------------------------------------------- pooling
 
 // Output dims of pooling: the convolution's floor rule over the window.
@@ -1204,6 +1384,36 @@ mic_status mic_pool_forward(mic_handle handle, double alpha, mic_pool_desc pool,
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
     const hipError_t err = miconv::launch_pool_forward(pl.dt, pl.p, handle->stream);
     return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
+}
+
+mic_status mic_brgemm(mic_handle handle, mic_dtype dtype, int m, int n, int k, int batch, double alpha,
+                      const void* a, int64_t a_stride_batch, int64_t a_stride_m, int64_t a_stride_k,
+                      const void* b, int64_t b_stride_batch, int64_t b_stride_k, int64_t b_stride_n,
+                      double beta, void* c, int64_t c_stride_m, int64_t c_stride_n)
+{
+    if (!handle) return MIC_STATUS_BAD_PARAM;
+    Plan pl = make_brgemm_plan(handle, dtype, m, n, k, batch, alpha, a, a_stride_batch, a_stride_m, a_stride_k,
+                               b, b_stride_batch, b_stride_k, b_stride_n, beta, c, c_stride_m, c_stride_n, true);
+    if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    if (m == 0 || n == 0) return MIC_STATUS_SUCCESS;
+    const hipError_t err = miconv::launch_brgemm(pl.cand.v, pl.p, handle->stream);
+    return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
+}
+
+mic_status mic_brgemm_kernel_name(mic_handle handle, mic_dtype dtype, int m, int n, int k, int batch,
+                                  int64_t a_stride_batch, int64_t a_stride_m, int64_t a_stride_k,
+                                  int64_t b_stride_batch, int64_t b_stride_k, int64_t b_stride_n,
+                                  int64_t c_stride_m, int64_t c_stride_n, char* buf, size_t buflen)
+{
+    if (!buf) return MIC_STATUS_BAD_PARAM;
+    Plan pl = make_brgemm_plan(handle, dtype, m, n, k, batch, 1.0, nullptr, a_stride_batch, a_stride_m, a_stride_k,
+                               nullptr, b_stride_batch, b_stride_k, b_stride_n, 0.0, nullptr, c_stride_m, c_stride_n,
+                               false);
+    if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    const size_t len = strlen(pl.name);
+    if (len + 1 > buflen) return MIC_STATUS_BAD_PARAM;
+    memcpy(buf, pl.name, len + 1);
+    return MIC_STATUS_SUCCESS;
 }
 
 mic_status mic_conv_forward_kernel_name(mic_handle handle, mic_tensor_desc x_desc,

@@ -112,6 +112,52 @@ POOLING = [
           tags=("pool", "max")),
 ]
 
+
+@dataclass(frozen=True)
+class FcLayer:
+    """A fully-connected layer as a batch-reduce GEMM: y[m, n] = sum_i x_i[m, :] . W_i[:, n].
+
+    The layer's input features are cut into ``batch`` blocks of ``k``; with
+    batch 1 it is one plain product.  Activations x are (m, batch*k) row-major,
+    weights W are (n, batch*k) row-major (one row of input weights per output).
+    """
+    name: str
+    config: int
+    layer: int
+    m: int                       # minibatch rows
+    n: int                       # output features
+    k: int                       # input features per block
+    batch: int                   # blocks reduced into one output
+    dtype: str
+    x_dist: tuple
+    w_dist: tuple
+
+    @property
+    def features(self):
+        return self.k * self.batch
+
+
+# AlexNet's fully-connected layers at minibatch 128: fc6 reads conv5's pooled
+# 256 x 6 x 6 = 9216 features, fc7 and fc8 4096; fc8's 1000 outputs leave a
+# ragged tile edge.  fc6 also as 36 blocks of 256 features (one block per
+# spatial position of the pooled map).
+FC = [
+    FcLayer("alexnet_fc6", 7, 6, 128, 4096, 9216, 1, "f32", U11, ("he_normal", 9216)),
+    FcLayer("alexnet_fc7", 7, 7, 128, 4096, 4096, 1, "f32", U11, ("he_normal", 4096)),
+    FcLayer("alexnet_fc8", 7, 8, 128, 1000, 4096, 1, "f32", U11, ("he_normal", 4096)),
+    FcLayer("alexnet_fc6_blocked", 7, 16, 128, 4096, 256, 36, "f32", U11, ("he_normal", 9216)),
+    FcLayer("alexnet_fc6_f64", 7, 26, 128, 4096, 9216, 1, "f64", U11, ("he_normal", 9216)),
+    FcLayer("alexnet_fc6_bf16", 7, 36, 128, 4096, 9216, 1, "bf16", U11, ("he_normal", 9216)),
+]
+
+
+def fc_by_name(name):
+    for lay in FC:
+        if lay.name == name:
+            return lay
+    raise KeyError(name)
+
+
 CONFIGS = {1: TINY, 2: ALEXNET, 3: OVERFEAT, 4: SPEECH, 5: PRECISION}
 ALL_LAYERS = [l for c in sorted(CONFIGS) for l in CONFIGS[c]]
 

@@ -298,6 +298,46 @@ mic_status mic_pool_forward(mic_handle handle, double alpha, mic_pool_desc pool,
                             mic_tensor_desc x_desc, const void* x, double beta,
                             mic_tensor_desc y_desc, void* y);
 
+/* ------------------------------------------------------------------ batch-reduce GEMM
+ *
+ * Single-building-block page (Georganas et al.), "Proposed Method": the
+ * batch-reduce GEMM multiplies a batch of A blocks by a batch of B blocks
+ * and reduces all products into one C block:
+ *
+ *   C[i_m, i_n] <- alpha * sum_{i < batch} sum_{i_k < k} A_i[i_m, i_k] * B_i[i_k, i_n]
+ *                  + beta * C[i_m, i_n]
+ *
+ * with A_i[i_m, i_k] = a[i*a_stride_batch + i_m*a_stride_m + i_k*a_stride_k],
+ * B_i[i_k, i_n] = b[i*b_stride_batch + i_k*b_stride_k + i_n*b_stride_n] and
+ * C[i_m, i_n] = c[i_m*c_stride_m + i_n*c_stride_n], strides in elements.
+ * A fully-connected layer is one block product (batch 1, k = input
+ * features) or its input features cut into batch blocks.
+ *
+ * Element types: dtype MIC_DTYPE_F32 (A, B, C fp32), MIC_DTYPE_F64 (all
+ * fp64), MIC_DTYPE_BF16 (A, B bf16, C fp32, fp32 accumulation).  a, b, c are
+ * device pointers owned by the caller, aligned to their element size; the
+ * call is asynchronous on the handle's stream and keeps no reference.
+ * beta == 0 writes C without reading it (NaN-safe).  m == 0 or n == 0 is a
+ * no-op; k == 0 or batch == 0 gives C <- beta * C (a, b may then be null).
+ * C must not overlap A or B; distinct (i_m, i_n) must have distinct C
+ * offsets.  No workspace.  Errors: MIC_STATUS_BAD_PARAM (null handle or
+ * needed pointer, negative size or stride, misaligned pointer, aliased C
+ * elements), MIC_STATUS_NOT_SUPPORTED (unknown dtype, an operand's highest
+ * element offset or batch*k reaching 2^30), MIC_STATUS_LAUNCH_FAILED. */
+mic_status mic_brgemm(mic_handle handle, mic_dtype dtype, int m, int n, int k, int batch, double alpha,
+                      const void* a, int64_t a_stride_batch, int64_t a_stride_m, int64_t a_stride_k,
+                      const void* b, int64_t b_stride_batch, int64_t b_stride_k, int64_t b_stride_n,
+                      double beta, void* c, int64_t c_stride_m, int64_t c_stride_n);
+
+/* Name of the kernel variant mic_brgemm would launch for these sizes and
+ * strides (pointers taken as 16-byte aligned), host only, NUL-terminated
+ * into buf of buflen bytes; errors as mic_brgemm's size and stride checks,
+ * MIC_STATUS_BAD_PARAM if the name does not fit. */
+mic_status mic_brgemm_kernel_name(mic_handle handle, mic_dtype dtype, int m, int n, int k, int batch,
+                                  int64_t a_stride_batch, int64_t a_stride_m, int64_t a_stride_k,
+                                  int64_t b_stride_batch, int64_t b_stride_k, int64_t b_stride_n,
+                                  int64_t c_stride_m, int64_t c_stride_n, char* buf, size_t buflen);
+
 #ifdef __cplusplus
 }
 #endif

@@ -372,3 +372,63 @@ def test_pool_descriptor_and_output_dims():
         mic.pool_output_shape((1, 1, 3, 3), (5, 1), (1, 1), (0, 1, 0, 0))
     l = mic.lib()
     assert l.mic_pool_forward(None, 1.0, None, None, None, 0.0, None, None) == mic.MIC_STATUS_BAD_PARAM
+
+
+def test_brgemm_kernel_choice_host_only():
+    """Skinny products (the AlexNet fully-connected layers, weights contiguous along k) go to the
+    wave-split kernel; large ones, or B not contiguous along k, to the shared-LDS tiles."""
+    import torch
+    tdt = {"f32": torch.float32, "f64": torch.float64, "bf16": torch.bfloat16}
+    assert mic.brgemm_kernel_name(torch.float32, 128, 4096, 9216, b_strides=(0, 1, 9216)) == "ws_f32_32x64"
+    assert mic.brgemm_kernel_name(torch.float32, 256, 4096, 9216, b_strides=(0, 1, 9216)) == "ws_f32_64x64"
+    assert mic.brgemm_kernel_name(torch.float32, 128, 1000, 4096, b_strides=(0, 1, 4096)) == "ws_f32_16x32"
+    assert mic.brgemm_kernel_name(torch.bfloat16, 128, 4096, 9216, b_strides=(0, 1, 9216)) == "ws_bf16_32x64"
+    assert mic.brgemm_kernel_name(torch.float32, 128, 4096, 9216).startswith("br_f32_")      # B not k-contiguous
+    assert mic.brgemm_kernel_name(torch.float32, 4096, 4096, 4096, b_strides=(0, 1, 4096)) == "br_f32_128x128"
+    for lay in workloads.FC:
+        F = lay.features
+        name = mic.brgemm_kernel_name(tdt[lay.dtype], lay.m, lay.n, lay.k, lay.batch,
+                                      a_strides=(lay.k, F, 1), b_strides=(lay.k, 1, F))
+        assert name.startswith("ws_" + lay.dtype + "_"), (lay.name, name)
+
+
+def test_brgemm_argument_errors(monkeypatch):
+    import torch
+    l = mic.lib()
+    args = dict(m=4, n=4, k=4, batch=1)
+
+    def call(dtype=mic.MIC_DTYPE_F32, handle=1, a=16, b=16, c=16, sa=(16, 4, 1), sb=(16, 4, 1), sc=(4, 1), **kw):
+        d = dict(args, **kw)
+        return l.mic_brgemm(handle, dtype, d["m"], d["n"], d["k"], d["batch"], 1.0, a, *sa, b, *sb, 0.0, c, *sc)
+
+    # errors found before anything touches the device (handle 1 is never dereferenced on these paths)
+    assert l.mic_brgemm(None, mic.MIC_DTYPE_F32, 4, 4, 4, 1, 1.0, 16, 16, 4, 1, 16, 16, 4, 1, 0.0, 16, 4, 1) \
+        == mic.MIC_STATUS_BAD_PARAM
+    assert call(m=-1) == mic.MIC_STATUS_BAD_PARAM
+    assert call(batch=-1) == mic.MIC_STATUS_BAD_PARAM
+    assert call(sa=(16, -4, 1)) == mic.MIC_STATUS_BAD_PARAM
+    assert call(a=0) == mic.MIC_STATUS_BAD_PARAM                 # null A with work to do
+    assert call(c=0) == mic.MIC_STATUS_BAD_PARAM
+    assert call(a=18) == mic.MIC_STATUS_BAD_PARAM                # misaligned fp32 pointer
+    assert call(sc=(0, 1)) == mic.MIC_STATUS_BAD_PARAM           # rows of C alias
+    assert call(dtype=7) == mic.MIC_STATUS_NOT_SUPPORTED
+    assert call(sa=(0, 1 << 30, 1)) == mic.MIC_STATUS_NOT_SUPPORTED
+    assert call(k=1 << 16, batch=1 << 14, sa=(0, 0, 0), sb=(0, 0, 0)) == mic.MIC_STATUS_NOT_SUPPORTED
+    buf = ctypes.create_string_buffer(4)
+    assert l.mic_brgemm_kernel_name(None, mic.MIC_DTYPE_F32, 128, 128, 128, 1, 0, 128, 1, 0, 128, 1, 128, 1,
+                                    buf, 4) == mic.MIC_STATUS_BAD_PARAM
+    import torch
+    monkeypatch.setenv("MIC_FORCE_BRGEMM_VARIANT", "br_f64_64x64")
+    with pytest.raises(mic.MicError) as e:
+        mic.brgemm_kernel_name(torch.float32, 128, 128, 128)
+    assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+    monkeypatch.setenv("MIC_FORCE_BRGEMM_VARIANT", "br_f32_64x64")
+    assert mic.brgemm_kernel_name(torch.float32, 128, 128, 128) == "br_f32_64x64"
+    # the wave-split kernel needs A and B contiguous along k
+    monkeypatch.setenv("MIC_FORCE_BRGEMM_VARIANT", "ws_f32_32x64")
+    with pytest.raises(mic.MicError) as e:
+        mic.brgemm_kernel_name(torch.float32, 128, 128, 128)           # B packed (k, n): not contiguous in k
+    assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+    assert mic.brgemm_kernel_name(torch.float32, 128, 128, 128, b_strides=(0, 1, 128)) == "ws_f32_32x64"
+    with pytest.raises(mic.MicError):
+        mic.brgemm_kernel_name(torch.float32, 128, 128, 102, b_strides=(0, 1, 102))   # k % 4 != 0
