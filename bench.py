@@ -20,7 +20,8 @@ few images of every layer).  ``--op dgrad`` / ``--op wgrad`` time the data /
 filter gradient of the same layers instead (dy seeded uniform [-1, 1]; the
 same FLOP count).  ``--workload alexnet_pool`` times AlexNet's two max-pooling
 layers (after conv2 and conv5) and reports bandwidth (|x| + |y| per second)
-against the HBM roofline.  ``--workload alexnet_fc`` times AlexNet's
+against the HBM roofline.  ``--block B`` runs the forward pass on
+channel-blocked x, filters and y (blocks of B channels).  ``--workload alexnet_fc`` times AlexNet's
 fully-connected layers fc6-fc8 at minibatch 128 as batch-reduce GEMMs
 (``_f64`` / ``_bf16``: fc6 in that type), 2*m*n*k*batch FLOP per layer.
 """
@@ -50,6 +51,10 @@ def parse():
     ap.add_argument("--workload", default="alexnet", choices=WORKLOADS)
     ap.add_argument("--op", default="fprop", choices=("fprop", "dgrad", "wgrad"),
                     help="forward pass (default), data gradient or filter gradient of the layers")
+    ap.add_argument("--block", type=int, default=0,
+                    help="forward pass on channel-blocked x, filters and y with this block "
+                         "(x [N][C/b][H][W][b], filters [K/b][C/b][R][S][b][b], y [N][K/b][P][Q][b]); "
+                         "a tensor whose channel count b does not divide stays unblocked")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -159,7 +164,18 @@ def main():
         N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
         wt = torch.from_numpy(w).to({"f32": torch.float32, "f64": torch.float64,
                                      "bf16": torch.bfloat16}[dtype]).to(dev)
-        if args.op == "fprop":
+        if args.op == "fprop" and args.block:
+            # block every tensor whose channel count the block divides (exact
+            # blocks); the others stay NCHW / packed KCRS
+            b = args.block
+            C = lay.C
+            xt = torch.from_numpy(x).to(wt.dtype).to(dev)
+            xt = mic.to_blocked(xt, b) if C % b == 0 else xt
+            wb = mic.filters_to_blocked(wt, b, b) if C % b == 0 and K % b == 0 else wt
+            yt = (torch.zeros((N, K // b, P, Q, b), dtype=out_dt, device=dev) if K % b == 0
+                  else torch.zeros((N, K, P, Q), dtype=out_dt, device=dev))
+            plans.append((lay, mic.BlockedConvPlan(xt, wb, yt, lay.stride, lay.padding), (x, w)))
+        elif args.op == "fprop":
             xt = upload(x, dtype, lay.layout, lay.row_pitch, dev)
             yst = workloads.padded_strides(N, K, P, Q, lay.layout, lay.row_pitch)
             yt = torch.zeros(workloads.storage_elems(N, K, P, Q, yst), dtype=out_dt,
@@ -218,9 +234,12 @@ def main():
         ev1.synchronize()
         ms = ev0.elapsed_time(ev1) / reps
         tf = plan.flops / (ms * 1e-3) / 1e12
-        per_layer.append({"layer": lay.name, "kernel": plan.kernel_name(), "us": round(ms * 1e3, 2),
-                          "gflop": round(plan.flops / 1e9, 3), "tflops": round(tf, 2),
-                          "pct_mfma_peak": round(100 * tf / peak, 1)})
+        rec = {"layer": lay.name, "kernel": plan.kernel_name(), "us": round(ms * 1e3, 2),
+               "gflop": round(plan.flops / 1e9, 3), "tflops": round(tf, 2),
+               "pct_mfma_peak": round(100 * tf / peak, 1)}
+        if isinstance(plan, mic.BlockedConvPlan):
+            rec["blocked"] = {"x": plan.x.dim() == 5, "w": plan.w.dim() == 6, "y": plan.y.dim() == 5}
+        per_layer.append(rec)
 
     # dominant kernel: most time per step, launches grouped by kernel variant
     groups = {}
@@ -232,7 +251,7 @@ def main():
     dom = max(groups, key=lambda k: groups[k]["us"])
     g = groups[dom]
     achieved = (g["flops"] / g["launches"]) / (g["us"] / g["launches"] * 1e-6) / 1e12
-    traffic = stored_traffic(dom) if (args.workload == "alexnet" and args.op == "fprop") else None
+    traffic = stored_traffic(dom) if (args.workload == "alexnet" and args.op == "fprop" and not args.block) else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "kernel": dom, "launches_per_step": g["launches"],
@@ -255,7 +274,8 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded inputs with the workload's value distributions)",
-        "config": {"workload": wl_name if args.op == "fprop" else wl_name + "_" + args.op, "op": args.op,
+        "config": {"workload": (wl_name if args.op == "fprop" else wl_name + "_" + args.op) +
+                               ("_blocked%d" % args.block if args.block else ""), "op": args.op,
                    "global_batch": layers[0].N,
                    "layers": [l.name for l in layers], "gflop_per_step": round(flops_step / 1e9, 3),
                    "pct_mfma_peak": round(100 * value / peak, 1)},

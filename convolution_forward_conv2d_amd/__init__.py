@@ -74,10 +74,14 @@ _SIGS = {
     "mic_tensor_desc_set": ([_vp, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64], _i),
     "mic_tensor_desc_set_packed": ([_vp, _i, _i, _i, _i, _i, _i], _i),
     "mic_tensor_desc_get": ([_vp, _ip, _ip, _ip, _ip, _ip, _i64p], _i),
+    "mic_tensor_desc_set_blocked": ([_vp, _i, _i, _i, _i, _i, _i], _i),
+    "mic_tensor_desc_get_block": ([_vp, _ip, _i64p], _i),
     "mic_filter_desc_create": ([ctypes.POINTER(_vp)], _i),
     "mic_filter_desc_destroy": ([_vp], _i),
     "mic_filter_desc_set": ([_vp, _i, _i, _i, _i, _i], _i),
     "mic_filter_desc_get": ([_vp, _ip, _ip, _ip, _ip, _ip], _i),
+    "mic_filter_desc_set_blocked": ([_vp, _i, _i, _i, _i, _i, _i, _i], _i),
+    "mic_filter_desc_get_block": ([_vp, _ip, _ip], _i),
     "mic_conv_desc_create": ([ctypes.POINTER(_vp)], _i),
     "mic_conv_desc_destroy": ([_vp], _i),
     "mic_conv_desc_set": ([_vp, _i, _i, _i, _i, _i, _i], _i),
@@ -203,6 +207,16 @@ def mic_tensor_desc_get(d):
     return dt.value, (n.value, c.value, h.value, w.value), tuple(st)
 
 
+def mic_tensor_desc_set_blocked(d, dtype, n, c, h, w, cb):
+    _check(lib().mic_tensor_desc_set_blocked(d, dtype, n, c, h, w, cb), "mic_tensor_desc_set_blocked")
+
+
+def mic_tensor_desc_get_block(d):
+    cb, sb = _i(), _i64()
+    _check(lib().mic_tensor_desc_get_block(d, ctypes.byref(cb), ctypes.byref(sb)), "mic_tensor_desc_get_block")
+    return cb.value, sb.value
+
+
 def mic_filter_desc_create():
     return _create(lib().mic_filter_desc_create, "mic_filter_desc_create")
 
@@ -213,6 +227,16 @@ def mic_filter_desc_destroy(d):
 
 def mic_filter_desc_set(d, dtype, k, c, r, s):
     _check(lib().mic_filter_desc_set(d, dtype, k, c, r, s), "mic_filter_desc_set")
+
+
+def mic_filter_desc_set_blocked(d, dtype, k, c, r, s, kb, cb):
+    _check(lib().mic_filter_desc_set_blocked(d, dtype, k, c, r, s, kb, cb), "mic_filter_desc_set_blocked")
+
+
+def mic_filter_desc_get_block(d):
+    kb, cb = _i(), _i()
+    _check(lib().mic_filter_desc_get_block(d, ctypes.byref(kb), ctypes.byref(cb)), "mic_filter_desc_get_block")
+    return kb.value, cb.value
 
 
 def mic_filter_desc_get(d):
@@ -697,3 +721,80 @@ def brgemm_kernel_name_for(a, b, c):
     """Kernel variant mic_brgemm picks for these tensors (as brgemm() would pass them)."""
     batch, m, k = a.shape
     return brgemm_kernel_name(a.dtype, m, b.shape[2], k, batch, a.stride(), b.stride(), c.stride())
+
+
+# ---------------------------------------------------------------- channel-blocked layouts
+
+def to_blocked(t, cb):
+    """(N, C, H, W) -> packed channel-blocked (N, C/cb, H, W, cb) (a copy; C % cb == 0)."""
+    n, c, h, w = t.shape
+    if c % cb:
+        raise ValueError("C = %d is not a multiple of the block %d" % (c, cb))
+    return t.reshape(n, c // cb, cb, h, w).permute(0, 1, 3, 4, 2).contiguous()
+
+
+def from_blocked(tb):
+    """(N, C/cb, H, W, cb) -> logical (N, C, H, W) view."""
+    n, nb, h, w, cb = tb.shape
+    return tb.permute(0, 1, 4, 2, 3).reshape(n, nb * cb, h, w)
+
+
+def filters_to_blocked(f, kb, cb):
+    """(K, C, R, S) -> packed blocked filters (K/kb, C/cb, R, S, cb, kb) (a copy)."""
+    k, c, r, s = f.shape
+    if k % kb or c % cb:
+        raise ValueError("K, C = %d, %d are not multiples of the blocks %d, %d" % (k, c, kb, cb))
+    return f.reshape(k // kb, kb, c // cb, cb, r, s).permute(0, 2, 4, 5, 3, 1).contiguous()
+
+
+def filters_from_blocked(fb):
+    """(K/kb, C/cb, R, S, cb, kb) -> logical (K, C, R, S) view."""
+    nk, nc, r, s, cb, kb = fb.shape
+    return fb.permute(0, 5, 1, 4, 2, 3).reshape(nk * kb, nc * cb, r, s)
+
+
+class BlockedConvPlan(ConvPlan):
+    """ConvPlan for channel-blocked operands.
+
+    x: (N, C, H, W) of any strides, or channel-blocked (N, C/cb, H, W, cb)
+    contiguous; y likewise with the output channels; w: packed (K, C, R, S)
+    or blocked (K/kb, C/cb, R, S, cb, kb) contiguous.  Logical shapes follow
+    from the blocked ones.
+    """
+
+    def __init__(self, x, w, y, stride=(1, 1), padding=(0, 0, 0, 0), handle=None):
+        for t in (x, w, y):
+            if t.dtype not in _TORCH_DTYPE:
+                raise TypeError("unsupported dtype %s" % t.dtype)
+        if x.dim() not in (4, 5) or y.dim() not in (4, 5) or w.dim() not in (4, 6):
+            raise ValueError("x, y must be 4-D or blocked 5-D, w 4-D or blocked 6-D")
+        for t in (x, w, y):
+            if t.dim() > 4 and not t.is_contiguous():
+                raise ValueError("blocked operands must be contiguous")
+        if w.dim() == 4 and not w.is_contiguous():
+            raise ValueError("w must be packed K,C,R,S (contiguous)")
+        self.x, self.w, self.y = x, w, y
+        self.handle = handle if handle is not None else handle_for(x.device)
+        self.xd, self.wd, self.yd = mic_tensor_desc_create(), mic_filter_desc_create(), mic_tensor_desc_create()
+        self.cd = mic_conv_desc_create()
+
+        def set_act(d, t):
+            if t.dim() == 5:
+                n, nb, h, w_, cb = t.shape
+                mic_tensor_desc_set_blocked(d, _TORCH_DTYPE[t.dtype], n, nb * cb, h, w_, cb)
+                return (n, nb * cb, h, w_)
+            mic_tensor_desc_set(d, _TORCH_DTYPE[t.dtype], *t.shape, *_element_strides(t))
+            return tuple(t.shape)
+
+        xs = set_act(self.xd, x)
+        ys = set_act(self.yd, y)
+        if w.dim() == 6:
+            nk, nc, r, s_, cb, kb = w.shape
+            mic_filter_desc_set_blocked(self.wd, _TORCH_DTYPE[w.dtype], nk * kb, nc * cb, r, s_, kb, cb)
+            ws = (nk * kb, nc * cb, r, s_)
+        else:
+            mic_filter_desc_set(self.wd, _TORCH_DTYPE[w.dtype], *w.shape)
+            ws = tuple(w.shape)
+        mic_conv_desc_set(self.cd, *padding, *stride)
+        self.shapes = (xs, ws, ys)
+        self.flops = 2.0 * ys[0] * ys[1] * ys[2] * ys[3] * ws[1] * ws[2] * ws[3]

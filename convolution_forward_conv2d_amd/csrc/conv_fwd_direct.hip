@@ -35,23 +35,29 @@ __global__ void __launch_bounds__(256) conv_fwd_direct_kernel(const ConvParams p
     const int hb = (int)pp * p.u - p.pad_top;
     const int wb = (int)q * p.v - p.pad_left;
     const In* x = static_cast<const In*>(p.x);
-    const In* w = static_cast<const In*>(p.w) + (size_t)k * p.Kred;
+    const In* w = static_cast<const In*>(p.w);
+    const int rs = p.R * p.S;
+    // filter F[k, c, tap] at wc + tap * wt: packed KCRS, or blocked
+    // [K/kb][C/cb][R][S][cb][kb] (taps cb*kb apart)
+    const int wt = p.wkb > 0 ? p.wcb * p.wkb : 1;
     Acc acc = 0;
     for (int c = 0; c < p.C; ++c) {
+        const int xc = (int)n * p.sxn + blk_off(p.div_xcb, p.sxcb, p.sxc, c);
+        const int wc = p.wkb > 0 ? wblk_off(k, c, 0, p.C, rs, p.wkb, p.wcb) : k * p.Kred + c * rs;
         for (int r = 0; r < p.R; ++r) {
             const int h = hb + r;
             if ((unsigned)h >= (unsigned)p.H) continue;
             for (int s = 0; s < p.S; ++s) {
                 const int ww = wb + s;
                 if ((unsigned)ww >= (unsigned)p.W) continue;
-                const Acc xv = widen(x[(int)n * p.sxn + c * p.sxc + h * p.sxh + ww * p.sxw]);
-                const Acc fv = widen(w[(c * p.R + r) * p.S + s]);
+                const Acc xv = widen(x[xc + h * p.sxh + ww * p.sxw]);
+                const Acc fv = widen(w[wc + (r * p.S + s) * wt]);
                 acc += xv * fv;
             }
         }
     }
     Out* y = static_cast<Out*>(p.y);
-    const int off = (int)n * p.syn + k * p.syk + (int)pp * p.syp + (int)q * p.syq;
+    const int off = (int)n * p.syn + blk_off(p.div_ycb, p.sycb, p.syk, k) + (int)pp * p.syp + (int)q * p.syq;
     const Acc alpha = (Acc)p.alpha;
     const Acc beta = (Acc)p.beta;
     Acc val = alpha * acc;

@@ -47,7 +47,7 @@
 namespace miconv {
 
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS,
-          bool DG>
+          bool DG, bool WB>
 __global__ void __launch_bounds__(256 * KS)
 conv_fwd_halo_kernel(const ConvParams p)
 {
@@ -77,6 +77,15 @@ conv_fwd_halo_kernel(const ConvParams p)
     constexpr int VPR = TK * ES / VB;                   // vectors per filter row
     constexpr int NVB = (TN * VPR + NT - 1) / NT;       // slab vectors per thread per chunk
     constexpr int BUF_BYTES = ((HALO_BYTES + B_BYTES) + 15) / 16 * 16;
+    // WB (blocked filters [K/kb][C/cb][R][S][cb][kb]): a 16-byte load takes VK
+    // consecutive filters of one (channel, tap) slab column; units are
+    // (column e, filter quad kq) with 8 consecutive quads on 8 consecutive lanes
+    constexpr int VK = 16 / ES;
+    constexpr int QT = (TN + VK - 1) / VK;              // filter quads per slab
+    constexpr int QG = (QT + 7) / 8;                    // groups of 8 quads
+    constexpr int NWU = QG * 8 * TK;                    // units (some past QT)
+    constexpr int NWB = WB ? (NWU + NT - 1) / NT : 1;   // units per thread per chunk
+    static_assert(!(DG && WB), "blocked filters in the forward pass only");
     static_assert(Pol::V == 1, "scalar-operand MFMA policies only");
     static_assert(CB % Pol::G == 0, "whole channels per lane group");
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
@@ -156,24 +165,45 @@ conv_fwd_halo_kernel(const ConvParams p)
             d_ok |= (ok ? 1u : 0u) << i;
         }
     }
-    int b_off[NVB];
+    int b_off[WB ? 1 : NVB];
     uint32_t b_ok = 0;
+    if constexpr (!WB) {
 #pragma unroll
-    for (int i = 0; i < NVB; ++i) {
-        const int e = tid + NT * i;
-        const int row = e / VPR;
-        const int vec = e - row * VPR;
-        const bool ok = e < TN * VPR && n0 + row < p.K;
-        b_off[i] = ok ? (n0 + row) * p.Kred + vec * (VB / ES) : 0;   // elements
-        b_ok |= (ok ? 1u : 0u) << i;
+        for (int i = 0; i < NVB; ++i) {
+            const int e = tid + NT * i;
+            const int row = e / VPR;
+            const int vec = e - row * VPR;
+            const bool ok = e < TN * VPR && n0 + row < p.K;
+            b_off[i] = ok ? (n0 + row) * p.Kred + vec * (VB / ES) : 0;   // elements
+            b_ok |= (ok ? 1u : 0u) << i;
+        }
+    }
+    // WB: unit u -> slab column e = (channel cl, tap t), quad kq; its element
+    // offset is w_off[i] plus the chunk's (c0 / cb) * R*S*cb*kb + (c0 % cb) * kb
+    // (a chunk lies in one channel block; K is a multiple of kb, kb of VK)
+    int w_off[WB ? NWB : 1];
+    uint32_t w_ok = 0;
+    if constexpr (WB) {
+        const int blk = RS * p.wcb * p.wkb;
+#pragma unroll
+        for (int i = 0; i < NWB; ++i) {
+            const int u = tid + NT * i;
+            const int kq = (u / (8 * TK)) * 8 + (u & 7);
+            const int e = (u >> 3) % TK;
+            const int k = n0 + kq * VK;
+            const bool ok = u < NWU && kq < QT && k < p.K;
+            const int cl = e / RS, t = e - cl * RS;
+            w_off[i] = ok ? (k / p.wkb) * (p.C / p.wcb) * blk + (t * p.wcb + cl) * p.wkb + k % p.wkb : 0;
+            w_ok |= (ok ? 1u : 0u) << i;
+        }
     }
 
     In h_val[HE];
-    u32x4 b_val[DG ? 1 : NVB];
+    u32x4 b_val[DG ? 1 : (WB ? NWB : NVB)];
     In d_val[NDU][DG ? RS : 1];
 
     auto load_chunk = [&](int c0) {
-        const int xo = c0 * p.sxc;
+        const int xo = blk_off(p.div_xcb, p.sxcb, p.sxc, c0);
 #pragma unroll
         for (int i = 0; i < HE; ++i) h_val[i] = ((h_ok >> i) & 1) ? load_elem(x + h_off[i] + xo) : In(0);
         if constexpr (DG) {
@@ -184,6 +214,10 @@ conv_fwd_halo_kernel(const ConvParams p)
 #pragma unroll
                 for (int t = 0; t < RS; ++t) d_val[i][t] = ok ? load_elem(w + d_off[i] + wo + t) : In(0);
             }
+        } else if constexpr (WB) {
+            const int wo = (c0 / p.wcb) * (RS * p.wcb * p.wkb) + (c0 % p.wcb) * p.wkb;
+#pragma unroll
+            for (int i = 0; i < NWB; ++i) b_val[i] = *reinterpret_cast<const u32x4*>(w + w_off[i] + wo);
         } else {
             const int wo = c0 * RS;
 #pragma unroll
@@ -222,6 +256,25 @@ conv_fwd_halo_kernel(const ConvParams p)
                     In* dst = reinterpret_cast<In*>(bb + row * BROW) + cl * RS;
 #pragma unroll
                     for (int t = 0; t < RS; ++t) dst[RS - 1 - t] = d_val[i][t];
+                }
+            }
+        } else if constexpr (WB) {
+            // a quad's VK filters are VK slab rows of column e (zeros outside)
+#pragma unroll
+            for (int i = 0; i < NWB; ++i) {
+                const int u = tid + NT * i;
+                const int kq = (u / (8 * TK)) * 8 + (u & 7);
+                const int e = (u >> 3) % TK;
+                if (NWU % NT == 0 || u < NWU) {
+                    if (kq < QT) {
+                        const bool ok = (w_ok >> i) & 1;
+                        In v[VK];
+                        __builtin_memcpy(v, &b_val[i], 16);
+#pragma unroll
+                        for (int j = 0; j < VK; ++j)
+                            if (kq * VK + j < TN)
+                                *reinterpret_cast<In*>(bb + (kq * VK + j) * BROW + e * ES) = ok ? v[j] : In(0);
+                    }
                 }
             }
         } else {
@@ -351,12 +404,22 @@ static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStrea
     p.m_tiles = (p.M + p.m_step - 1) / p.m_step;
     p.n_tiles = (p.K + TN - 1) / TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
-    if (dgrad)
-        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, true>),
+    constexpr int VK = 16 / (int)sizeof(typename Pol::In);
+    if (p.wkb > 0) {
+        // blocked filters: the host checked cb % CB == 0, kb % VK == 0, K % kb == 0,
+        // C % cb == 0 and a 16-byte aligned w
+        if (dgrad || p.wcb % CB != 0 || p.wkb % VK != 0 || p.K % p.wkb != 0 || p.C % p.wcb != 0 ||
+            (uintptr_t)p.w % 16 != 0)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, true>),
                            grid, dim3(256 * KS), 0, stream, p);
-    else
-        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false>),
+    } else if (dgrad) {
+        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, true, false>),
                            grid, dim3(256 * KS), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, false>),
+                           grid, dim3(256 * KS), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -150,13 +150,15 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
     // Loads are unconditional (a unit outside the input or past K reads the
     // chunk's first element of x or w instead, which exists) and their
     // values are replaced by zeros at the store, so no load sits in a branch.
+    // x offset of a chunk's first channel (channel-blocked x: the chunk lies in one block)
+    auto x_chunk = [&](int c0) { return blk_off(p.div_xcb, p.sxcb, p.sxc, c0); };
     auto load_piece = [&](int q, int c0) {
         if (q < NLH) {
             if constexpr (CVEC) {
-                h_vec[q] = *reinterpret_cast<const u32x4*>(x + h_off[q] + c0);
+                h_vec[q] = *reinterpret_cast<const u32x4*>(x + h_off[q] + x_chunk(c0));
             } else {
                 const int i = q / 8, j = q % 8;
-                h_raw[i][j] = x[h_off[i] + (c0 + j) * p.sxc];
+                h_raw[i][j] = x[h_off[i] + x_chunk(c0) + j * p.sxc];
             }
         } else {
             const int i = (q - NLH) / NV, v = (q - NLH) % NV;
@@ -323,6 +325,7 @@ template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL
 static hipError_t launch_halo_bf16_variant(const ConvParams& p0, hipStream_t stream)
 {
     ConvParams p = p0;
+    if (p.wkb > 0) return hipErrorInvalidValue;          // packed KCRS filters only
     if (p.m_step <= 0 || p.m_step > TM) p.m_step = TM;   // the host sets P*Q for image tiles
     p.m_tiles = (p.M + p.m_step - 1) / p.m_step;
     p.n_tiles = (p.K + TN - 1) / TN;
@@ -330,7 +333,7 @@ static hipError_t launch_halo_bf16_variant(const ConvParams& p0, hipStream_t str
     // 16-byte input loads when the 8 channels of a group are contiguous and
     // every group starts on a 16-byte boundary
     const bool cvec = p.sxc == 1 && (uintptr_t)p.x % 16 == 0 && p.sxn % 8 == 0 && p.sxh % 8 == 0 &&
-                      p.sxw % 8 == 0;
+                      p.sxw % 8 == 0 && p.sxcb % 8 == 0;
     if (cvec)
         hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, true>), grid,
                            dim3(256), 0, stream, p);

@@ -9,7 +9,7 @@
 //   columns  k = filter               K
 //   reduce   kappa = (c, r, s)        Kred = C * R * S
 //   A[m, kappa] = X(n, c, p*u + r - pad_top, q*v + s - pad_left)   (0 outside)
-//   B[kappa, k] = F[k, c, r, s]                                     (packed KCRS)
+//   B[kappa, k] = F[k, c, r, s]                 (packed KCRS; WB: blocked filters)
 //
 // A workgroup of 4 waves owns a TM x TN output tile.  The reduction runs in
 // chunks of TK: each chunk of A (input receptive fields, gathered straight
@@ -44,7 +44,7 @@ namespace miconv {
 
 // ------------------------------------------------------------------ the kernel
 
-template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int TK, bool BVEC, bool TAP, bool DG>
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int TK, bool BVEC, bool TAP, bool DG, bool WB>
 __global__ void __launch_bounds__(256)
 conv_fwd_mfma_kernel(const ConvParams p)
 {
@@ -168,7 +168,8 @@ conv_fwd_mfma_kernel(const ConvParams p)
             tap_of(ch, c0, r, s);
             c0 += a_seg * A_EPT;                     // wave-uniform
             const bool tap_ok = ((unsigned)(hb + r) < (unsigned)p.H) && ((unsigned)(wb + s) < (unsigned)p.W);
-            const In* src = x + (abase + c0 * p.sxc + r * p.sxh + s * p.sxw);
+            // (channel-blocked x: the chunk's channels lie in one block)
+            const In* src = x + (abase + blk_off(p.div_xcb, p.sxcb, p.sxc, c0) + r * p.sxh + s * p.sxw);
 #pragma unroll
             for (int j = 0; j < A_EPT; ++j)
                 a_val[j] = (tap_ok && c0 + j < p.C) ? load_elem(src + j * p.sxc) : In(0);
@@ -183,7 +184,7 @@ conv_fwd_mfma_kernel(const ConvParams p)
             const bool ok = (kap + j < p.Kred) &&
                             ((unsigned)(hb + (int)r) < (unsigned)p.H) &&
                             ((unsigned)(wb + (int)s) < (unsigned)p.W);
-            const int off = abase + (int)c * p.sxc + (int)r * p.sxh + (int)s * p.sxw;
+            const int off = abase + blk_off(p.div_xcb, p.sxcb, p.sxc, (int)c) + (int)r * p.sxh + (int)s * p.sxw;
             a_val[j] = ok ? load_elem(x + off) : In(0);
             if (++s == (uint32_t)p.S) {
                 s = 0;
@@ -208,8 +209,18 @@ conv_fwd_mfma_kernel(const ConvParams p)
             int c0, r, s;
             tap_of(ch, c0, r, s);
             c0 += b_seg * B_EPT;
-            const In* src = wrow + (c0 * p.R + r) * p.S + s;
             const int rs = p.R * p.S;
+            if constexpr (WB) {
+                // blocked filters [K/kb][C/cb][R][S][cb][kb]: consecutive channels
+                // of one block kb apart, consecutive filters (lanes) adjacent
+                const int k = b_ok ? n0 + b_row : 0;
+                const In* src = w + wblk_off(k, c0, r * p.S + s, p.C, rs, p.wkb, p.wcb);
+#pragma unroll
+                for (int j = 0; j < B_EPT; ++j)
+                    b_val[j] = (b_ok && c0 + j < p.C) ? load_elem(src + j * p.wkb) : In(0);
+                return;
+            }
+            const In* src = wrow + (c0 * p.R + r) * p.S + s;
 #pragma unroll
             for (int j = 0; j < B_EPT; ++j)
                 b_val[j] = (b_ok && c0 + j < p.C) ? load_elem(src + j * rs) : In(0);
@@ -321,17 +332,22 @@ static hipError_t launch_variant(const ConvParams& p0, bool bvec, bool tap, bool
     constexpr int B_EPT = TK * TN / 256;
     constexpr bool CAN_VEC = (B_EPT * (int)sizeof(typename Pol::In)) % 16 == 0;
     if constexpr (!CAN_VEC) bvec = false;
-    if (dgrad)
-        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, true, true>),
+    if (p.wkb > 0) {
+        // blocked filters: tap order only, a chunk's TK channels in one block
+        if (dgrad || !tap || p.wcb % TK != 0 || p.K % p.wkb != 0 || p.C % p.wcb != 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, true, false, true>),
+                           grid, dim3(256), 0, stream, p);
+    } else if (dgrad)
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, true, true, false>),
                            grid, dim3(256), 0, stream, p);
     else if (tap)
-        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, true, false>),
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, true, false, false>),
                            grid, dim3(256), 0, stream, p);
     else if (bvec)
-        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, CAN_VEC, false, false>),
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, CAN_VEC, false, false, false>),
                            grid, dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, false, false>),
+        hipLaunchKernelGGL((conv_fwd_mfma_kernel<Pol, TM, TN, WAVES_M, WAVES_N, TK, false, false, false, false>),
                            grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }

@@ -61,7 +61,31 @@ struct ConvParams {
     // filter gradient: dy's element strides and division by P*Q and by Q
     int sdn, sdk, sdp, sdq;
     FastDiv div_opq, div_oq;
+    // Channel-blocked layouts: channel c of x lies at (c / xcb) * sxcb +
+    // (c % xcb) * sxc, output channel k of y at (k / ycb) * sycb + (k % ycb) * syk
+    // (blk_off); an unblocked tensor is one block of 2^30 channels.  Filters
+    // are packed KCRS when wkb == 0, else blocked [K/wkb][C/wcb][R][S][wcb][wkb].
+    FastDiv div_xcb, div_ycb;
+    int sxcb, sycb;
+    int wkb, wcb;
     double alpha, beta;  // converted to the accumulation type inside the kernel
 };
+
+// Element offset of channel c in a channel-blocked dimension (block size
+// d.d, block stride sblk, stride inside a block sc).
+__host__ __device__ __forceinline__ int blk_off(const FastDiv& d, int sblk, int sc, int c)
+{
+    uint32_t b, i;
+    d.divmod((uint32_t)c, b, i);
+    return (int)b * sblk + (int)i * sc;
+}
+
+// Element offset of F[k, c, r*S + s] in blocked filters [K/kb][C/cb][R][S][cb][kb].
+__host__ __device__ __forceinline__ int wblk_off(int k, int c, int tap, int C, int RS, int kb, int cb)
+{
+    return ((k / kb) * (C / cb) + c / cb) * (RS * cb * kb) + (tap * cb + c % cb) * kb + k % kb;
+}
+
+constexpr uint32_t kOneBlock = 1u << 30;   // block size of an unblocked channel dimension
 
 }  // namespace miconv

@@ -208,7 +208,7 @@ __device__ __forceinline__ void store_acc_tile(const ConvParams& p, unsigned cha
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     const int gk = nw0 + j * BM + Pol::col(e, lane);
-                    if (gk < p.K) put(moff + gk, acc[i][j][e]);
+                    if (gk < p.K) put(moff + blk_off(p.div_ycb, p.sycb, 1, gk), acc[i][j][e]);
                 }
             }
         }
@@ -232,7 +232,8 @@ __device__ __forceinline__ void store_acc_tile(const ConvParams& p, unsigned cha
             for (int t = 0; t < BM / LG; ++t) {
                 const int kl = lane / BM + LG * t;
                 const int gk = bk0 + kl;
-                if (row_ok && gk < p.K) put(moff + gk * p.syk, stage[kl * STAGE_PITCH + lane % BM]);
+                if (row_ok && gk < p.K)
+                    put(moff + blk_off(p.div_ycb, p.sycb, p.syk, gk), stage[kl * STAGE_PITCH + lane % BM]);
             }
         }
     }

@@ -30,12 +30,15 @@ struct mic_tensor_desc_st {
     mic_dtype dtype;
     int n, c, h, w;
     int64_t sn, sc, sh, sw;
+    int cb;          // channel block (0: unblocked); channel c at (c / cb) * scb + (c % cb) * sc
+    int64_t scb;
 };
 
 struct mic_filter_desc_st {
     bool set;
     mic_dtype dtype;
     int k, c, r, s;
+    int kb, cb;      // 0, 0: packed KCRS; else blocked [K/kb][C/cb][R][S][cb][kb]
 };
 
 struct mic_conv_desc_st {
@@ -77,8 +80,25 @@ size_t dtype_size(mic_dtype d)
 // Highest element offset a strided N,C,H,W tensor reaches, plus one.
 int64_t extent(const mic_tensor_desc_st& d)
 {
-    return (int64_t)(d.n - 1) * d.sn + (int64_t)(d.c - 1) * d.sc + (int64_t)(d.h - 1) * d.sh +
-           (int64_t)(d.w - 1) * d.sw + 1;
+    const int64_t chan = d.cb > 0 ? (int64_t)(d.c / d.cb - 1) * d.scb + (int64_t)(d.cb - 1) * d.sc
+                                  : (int64_t)(d.c - 1) * d.sc;
+    return (int64_t)(d.n - 1) * d.sn + chan + (int64_t)(d.h - 1) * d.sh + (int64_t)(d.w - 1) * d.sw + 1;
+}
+
+bool blocked(const mic_tensor_desc_st* d) { return d && d->cb > 0; }
+bool blocked(const mic_filter_desc_st* d) { return d && d->kb > 0; }
+
+// Channel blocking of x, y and the filters into the kernel parameters
+// (unblocked: one block of 2^30 channels, packed KCRS filters).
+void set_blocks(ConvParams& p, const mic_tensor_desc_st* xd, const mic_tensor_desc_st* yd,
+                const mic_filter_desc_st* wd)
+{
+    p.div_xcb = FastDiv(blocked(xd) ? (uint32_t)xd->cb : miconv::kOneBlock);
+    p.sxcb = blocked(xd) ? (int)xd->scb : 0;
+    p.div_ycb = FastDiv(blocked(yd) ? (uint32_t)yd->cb : miconv::kOneBlock);
+    p.sycb = blocked(yd) ? (int)yd->scb : 0;
+    p.wkb = blocked(wd) ? wd->kb : 0;
+    p.wcb = blocked(wd) ? wd->cb : 0;
 }
 
 mic_status output_dims(const mic_conv_desc_st* cd, const mic_tensor_desc_st* xd,
@@ -315,7 +335,14 @@ bool halo_eligible(const HaloCandidate& h, DType dt, const ConvParams& p, const 
 {
     if (h.dt != dt || h.r != p.R || h.s != p.S) return false;
     if (p.C % h.cb != 0) return false;
+    // channel-blocked x: a chunk of h.cb channels must lie in one block
+    if (p.div_xcb.d != miconv::kOneBlock && p.div_xcb.d % h.cb != 0) return false;
     if (dgrad) return dt != DType::BF16;     // scalar filter loads: no alignment needed
+    if (p.wkb > 0) {
+        // blocked filters: 16-byte loads of kb-contiguous filters (fp32/fp64 kernel only)
+        const int vk = dt == DType::F64 ? 2 : 4;
+        if (dt == DType::BF16 || p.wcb % h.cb != 0 || p.wkb % vk != 0) return false;
+    }
     if (check_ptr && (uintptr_t)w % 16 != 0) return false;
     return true;
 }
@@ -403,6 +430,7 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
     p.div_hp = FastDiv((uint32_t)p.Hp);
     p.div_u = FastDiv((uint32_t)p.u);
     p.div_v = FastDiv((uint32_t)p.v);
+    set_blocks(p, xd, yd, wd);
     p.alpha = alpha;
     p.beta = beta;
     const int Wp = xd->w + cd->pad_left + cd->pad_right;
@@ -477,11 +505,34 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
             }
         }
     }
-    (void)forced_gather;
     const size_t ie = dtype_size(xd->dtype);
-    pl.bvec = ((Kred * (int64_t)ie) % 16 == 0) && ((uintptr_t)w % 16 == 0);
+    pl.bvec = ((Kred * (int64_t)ie) % 16 == 0) && ((uintptr_t)w % 16 == 0) && !blocked(wd);
     const bool gather = pl.cand.v != Variant::DIRECT && !is_halo(pl.cand.v);
     if (!gather) pl.tap = false;
+    if (gather && (blocked(xd) || blocked(wd))) {
+        // Tap order reads a chunk of TK channels at one tap: with blocked x or
+        // filters the chunk must lie in one block.  Blocked filters need tap
+        // order; blocked x alone can also go through the flat order.
+        const int tk = gather_tk(pl.dt);
+        const bool tap_ok = (!blocked(xd) || xd->cb % tk == 0) && (!blocked(wd) || wd->cb % tk == 0);
+        if (forced_gather && pl.tap && !tap_ok) {
+            pl.status = MIC_STATUS_NOT_SUPPORTED;
+            return pl;
+        }
+        if (blocked(wd)) {
+            if (forced_gather && !pl.tap) {
+                pl.status = MIC_STATUS_NOT_SUPPORTED;
+                return pl;
+            }
+            if (tap_ok)
+                pl.tap = true;
+            else
+                pl.cand = kDirect;       // any blocking, one output per thread
+        } else if (!tap_ok) {
+            pl.tap = false;
+        }
+        if (pl.cand.v == Variant::DIRECT) pl.tap = false;
+    }
     snprintf(pl.name, sizeof(pl.name), "%s%s", pl.cand.name, pl.tap ? "_tap" : "");
     pl.status = MIC_STATUS_SUCCESS;
     return pl;
@@ -504,6 +555,10 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
     pl.status = MIC_STATUS_BAD_PARAM;
     if (!dyd || !wd || !cd || !dxd) return pl;
     if (!dyd->set || !wd->set || !cd->set || !dxd->set) return pl;
+    if (blocked(dyd) || blocked(wd) || blocked(dxd)) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;     // channel-blocked layouts: forward pass only
+        return pl;
+    }
     if (need_pointers && (!dy || !w || !dx)) return pl;
     int n, k, P, Q;
     mic_status st = output_dims(cd, dxd, wd, &n, &k, &P, &Q);
@@ -542,6 +597,7 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
     const int R = wd->r, S = wd->s, C = dxd->c, H = dxd->h, W = dxd->w;
     const int pt = cd->pad_top, pl_ = cd->pad_left;
     ConvParams& p = pl.p;
+    set_blocks(p, nullptr, nullptr, nullptr);
     p.x = dy;
     p.w = w;
     p.y = const_cast<void*>(dx);
@@ -678,6 +734,10 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
     pl.status = MIC_STATUS_BAD_PARAM;
     if (!xd || !dyd || !cd || !wd) return pl;
     if (!xd->set || !dyd->set || !cd->set || !wd->set) return pl;
+    if (blocked(xd) || blocked(dyd) || blocked(wd)) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;     // channel-blocked layouts: forward pass only
+        return pl;
+    }
     if (need_pointers && (!x || !dy || !dw)) return pl;
     int n, k, P, Q;
     mic_status st = output_dims(cd, xd, wd, &n, &k, &P, &Q);
@@ -710,6 +770,7 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
         if ((uintptr_t)x % ie || (uintptr_t)dy % ie || (uintptr_t)dw % oe) return pl;
     }
     ConvParams& p = pl.p;
+    set_blocks(p, nullptr, nullptr, nullptr);
     p.x = x;
     p.w = dy;
     p.y = const_cast<void*>(dw);
@@ -831,6 +892,7 @@ Plan make_brgemm_plan(const mic_handle_st* h, mic_dtype dtype, int m, int n, int
         if (!empty_red && ((uintptr_t)a % ie || (uintptr_t)b % ie)) return pl;
     }
     ConvParams& p = pl.p;
+    set_blocks(p, nullptr, nullptr, nullptr);
     p.x = a;
     p.w = b;
     p.y = const_cast<void*>(c);
@@ -960,6 +1022,10 @@ Plan make_pool_plan(const mic_pool_desc_st* pd, const mic_tensor_desc_st* xd, co
     memset(&pl, 0, sizeof(pl));
     pl.status = MIC_STATUS_BAD_PARAM;
     if (!yd || !yd->set) return pl;
+    if (blocked(xd) || blocked(yd)) {
+        pl.status = MIC_STATUS_NOT_SUPPORTED;     // channel-blocked layouts: forward pass only
+        return pl;
+    }
     if (need_pointers && (!x || !y)) return pl;
     int n, c, P, Q;
     mic_status st = pool_output_dims(pd, xd, &n, &c, &P, &Q);
@@ -990,6 +1056,7 @@ Plan make_pool_plan(const mic_pool_desc_st* pd, const mic_tensor_desc_st* xd, co
         if ((uintptr_t)x % ie || (uintptr_t)y % oe) return pl;
     }
     ConvParams& p = pl.p;
+    set_blocks(p, nullptr, nullptr, nullptr);
     p.x = x;
     p.y = const_cast<void*>(y);
     p.N = n;
@@ -1121,6 +1188,28 @@ mic_status mic_tensor_desc_set(mic_tensor_desc desc, mic_dtype dtype, int n, int
     desc->sc = sc;
     desc->sh = sh;
     desc->sw = sw;
+    desc->cb = 0;
+    desc->scb = 0;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_tensor_desc_set_blocked(mic_tensor_desc desc, mic_dtype dtype, int n, int c, int h, int w, int cb)
+{
+    if (!desc || !valid_dtype(dtype)) return MIC_STATUS_BAD_PARAM;
+    if (n < 1 || c < 1 || h < 1 || w < 1 || cb < 1 || c % cb != 0) return MIC_STATUS_BAD_PARAM;
+    const int64_t H = h, W = w, CB = cb;
+    mic_status st = mic_tensor_desc_set(desc, dtype, n, c, h, w, (int64_t)c * H * W, 1, W * CB, CB);
+    if (st != MIC_STATUS_SUCCESS) return st;
+    desc->cb = cb;
+    desc->scb = H * W * CB;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_tensor_desc_get_block(mic_tensor_desc desc, int* cb, int64_t* block_stride)
+{
+    if (!desc || !desc->set) return MIC_STATUS_BAD_PARAM;
+    if (cb) *cb = desc->cb;
+    if (block_stride) *block_stride = desc->scb;
     return MIC_STATUS_SUCCESS;
 }
 
@@ -1180,6 +1269,27 @@ mic_status mic_filter_desc_set(mic_filter_desc desc, mic_dtype dtype, int k, int
     desc->c = c;
     desc->r = r;
     desc->s = s;
+    desc->kb = 0;
+    desc->cb = 0;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_filter_desc_set_blocked(mic_filter_desc desc, mic_dtype dtype, int k, int c, int r, int s, int kb,
+                                       int cb)
+{
+    if (!desc || kb < 1 || cb < 1 || k % kb != 0 || c % cb != 0) return MIC_STATUS_BAD_PARAM;
+    mic_status st = mic_filter_desc_set(desc, dtype, k, c, r, s);
+    if (st != MIC_STATUS_SUCCESS) return st;
+    desc->kb = kb;
+    desc->cb = cb;
+    return MIC_STATUS_SUCCESS;
+}
+
+mic_status mic_filter_desc_get_block(mic_filter_desc desc, int* kb, int* cb)
+{
+    if (!desc || !desc->set) return MIC_STATUS_BAD_PARAM;
+    if (kb) *kb = desc->kb;
+    if (cb) *cb = desc->cb;
     return MIC_STATUS_SUCCESS;
 }
 

@@ -116,6 +116,27 @@ mic_status mic_tensor_desc_set_packed(mic_tensor_desc desc, mic_dtype dtype, mic
 mic_status mic_tensor_desc_get(mic_tensor_desc desc, mic_dtype* dtype,
                                int* n, int* c, int* h, int* w, int64_t* strides);
 
+/* Channel-blocked tensor (zero-memory direct-convolution page, "Proposed
+ * Method": input and output feature maps in a blocked layout that takes
+ * exactly the memory of standard storage): packed [N][C/cb][H][W][cb], so
+ * element (n, c, h, w) sits at
+ *   n*C*H*W + (c / cb)*H*W*cb + h*W*cb + w*cb + (c % cb).
+ * c must be a multiple of cb (no padding channels), cb >= 1, else
+ * MIC_STATUS_BAD_PARAM.  Accepted by mic_conv_forward for x and y, any cb:
+ * the tap-batched kernels read blocked x when cb is a multiple of their
+ * channel chunk (2 or 4 channels fp32/fp64, 16 bf16), the gather kernel's
+ * tap order when it is a multiple of 16 (32 bf16); other blockings run the
+ * gather kernel's flat order or the direct kernel.  The other operations
+ * return MIC_STATUS_NOT_SUPPORTED for blocked descriptors.
+ * mic_tensor_desc_set / _set_packed reset a descriptor to unblocked. */
+mic_status mic_tensor_desc_set_blocked(mic_tensor_desc desc, mic_dtype dtype, int n, int c, int h, int w,
+                                       int cb);
+
+/* Channel block cb (0 for an unblocked descriptor) and the element stride
+ * between channel blocks; either pointer may be null.  MIC_STATUS_BAD_PARAM
+ * if the descriptor was never set. */
+mic_status mic_tensor_desc_get_block(mic_tensor_desc desc, int* cb, int64_t* block_stride);
+
 /* ---------------------------------------------------------------- filter descriptor */
 
 mic_status mic_filter_desc_create(mic_filter_desc* desc);
@@ -125,6 +146,23 @@ mic_status mic_filter_desc_destroy(mic_filter_desc desc);
  * Dimensions must be >= 1. */
 mic_status mic_filter_desc_set(mic_filter_desc desc, mic_dtype dtype, int k, int c, int r, int s);
 mic_status mic_filter_desc_get(mic_filter_desc desc, mic_dtype* dtype, int* k, int* c, int* r, int* s);
+
+/* Blocked filters (zero-memory direct-convolution page, "Proposed Method":
+ * kernel weights in a blocked layout of the same size as standard storage):
+ * [K/kb][C/cb][R][S][cb][kb], so F[k, c, r, s] sits at
+ *   ((k/kb)*(C/cb) + c/cb)*R*S*cb*kb + ((r*S + s)*cb + c%cb)*kb + k%kb.
+ * k must be a multiple of kb and c of cb (kb, cb >= 1), else
+ * MIC_STATUS_BAD_PARAM.  Forward pass only, as for blocked tensors: the
+ * fp32/fp64 tap-batched kernels read them when cb is a multiple of their
+ * channel chunk and kb of 4 (fp32) or 2 (fp64) with w 16-byte aligned, the
+ * gather kernel when cb is a multiple of 16 (32 bf16), else the direct
+ * kernel runs.  mic_filter_desc_set resets a descriptor to packed KCRS. */
+mic_status mic_filter_desc_set_blocked(mic_filter_desc desc, mic_dtype dtype, int k, int c, int r, int s,
+                                       int kb, int cb);
+
+/* Filter blocks kb, cb (0, 0 for packed KCRS); either pointer may be null.
+ * MIC_STATUS_BAD_PARAM if the descriptor was never set. */
+mic_status mic_filter_desc_get_block(mic_filter_desc desc, int* kb, int* cb);
 
 /* ---------------------------------------------------------------- convolution descriptor */
 

@@ -1,0 +1,167 @@
+"""GPU parity of the forward pass on channel-blocked layouts against the oracle.
+
+x as [N][C/cb][H][W][cb], y as [N][K/kb][P][Q][kb], filters as
+[K/kb][C/cb][R][S][cb][kb] (zero-memory direct-convolution page, "Proposed
+Method": blocked layouts of the same size as standard storage).  The oracle
+runs on the logical tensors; the blocked copies are made with the layout
+conversions pinned in test_blocked_host.py.  Small shapes run every kernel
+variant that accepts the blocking in full; AlexNet conv3 (fp32) and conv4
+(bf16 inputs) run fully blocked at full size on sampled outputs, with
+integer inputs bit-exact and reruns bit-identical.  Tolerances are the
+forward pass's (gpu_harness).
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_forward_conv2d_amd as mic
+import gen
+import oracle
+from gen import workloads
+from gen.workloads import Layer
+
+import gpu_harness as H
+from test_parity_gpu import VARIANTS, U
+
+pytestmark = pytest.mark.gpu
+
+# (name, N, C, H, W, K, R, S, stride, pads, dtypes, x block, filter blocks (kb, cb), y block)
+CASES = [
+    ("halo3_all_blocked", 2, 32, 13, 13, 64, 3, 3, (1, 1), (1, 1, 1, 1), ("f32", "f64"), 16, (16, 16), 16),
+    ("halo5_all_blocked", 2, 16, 20, 20, 48, 5, 5, (1, 1), (2, 2, 2, 2), ("f32",), 8, (8, 8), 8),
+    ("x_y_blocked_packed_w", 2, 32, 13, 11, 40, 3, 3, (1, 1), (1, 1, 1, 1), ("f32", "f64", "bf16"), 16, None, 8),
+    ("tap_all_blocked", 2, 64, 9, 10, 64, 3, 3, (1, 1), (1, 1, 1, 1), ("f32", "bf16"), 32, (32, 32), 32),
+    ("strided_all_blocked", 2, 32, 15, 12, 32, 3, 2, (2, 1), (1, 0, 0, 1), ("f32", "f64"), 16, (16, 16), 8),
+    ("flat_x_by_2", 2, 6, 11, 9, 8, 5, 3, (2, 2), (2, 1, 1, 0), ("f32", "f64", "bf16"), 2, None, 4),
+    ("direct_filters_by_2", 2, 8, 7, 7, 8, 3, 3, (1, 1), (1, 1, 1, 1), ("f32", "bf16"), 8, (2, 8), 8),
+    ("y_only", 2, 20, 9, 9, 24, 3, 3, (1, 1), (1, 1, 1, 1), ("f32",), None, None, 12),
+]
+_ran = {}
+
+
+def _place(case, dtype, x64, w64, y_shape, fill=float("nan")):
+    _, N, C, Hh, Ww, K, R, S, stride, pads, _, xcb, wblk, ykb = case
+    dev = H.dev()
+    xt = torch.from_numpy(x64).to(H.TORCH_DT[dtype]).to(dev)
+    x = mic.to_blocked(xt, xcb) if xcb else xt
+    wt = torch.from_numpy(w64).to(H.TORCH_DT[dtype]).to(dev)
+    w = mic.filters_to_blocked(wt, *wblk) if wblk else wt
+    n, k, p, q = y_shape
+    ydt = H.OUT_DT[dtype]
+    if ykb:
+        y = torch.full((n, k // ykb, p, q, ykb), fill, dtype=ydt, device=dev)
+    else:
+        y = torch.full((n, k, p, q), fill, dtype=ydt, device=dev)
+    return x, w, y
+
+
+def _logical(y):
+    return mic.from_blocked(y) if y.dim() == 5 else y
+
+
+def _run(x, w, y, stride, pads, alpha=1.0, beta=0.0):
+    plan = mic.BlockedConvPlan(x, w, y, stride, pads)
+    try:
+        name = plan.kernel_name()
+        plan(alpha, beta)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    return name
+
+
+def _params():
+    return [(c, dt) for c in CASES for dt in c[10]]
+
+
+@pytest.mark.parametrize("case,dtype", _params(), ids=lambda v: v if isinstance(v, str) else v[0])
+def test_small_full_parity_every_accepting_variant(case, dtype, monkeypatch):
+    name, N, C, Hh, Ww, K, R, S, stride, pads = case[:10]
+    lay = Layer(name, 9, 2, N, C, Hh, Ww, K, R, S, stride, pads, dtype, U, U)
+    x64, w64 = H.inputs(lay)
+    ref, bound = oracle.conv2d_fprop(x64, w64, stride, pads)
+    x, w, _ = _place(case, dtype, x64, w64, ref.shape)
+    monkeypatch.delenv("MIC_FORCE_VARIANT", raising=False)
+    ran = 0
+    for var in [None] + VARIANTS[dtype]:
+        if var:
+            monkeypatch.setenv("MIC_FORCE_VARIANT", var)
+        _, _, y = _place(case, dtype, x64, w64, ref.shape)
+        try:
+            kname = _run(x, w, y, stride, pads)
+        except mic.MicError as e:
+            assert e.status == mic.MIC_STATUS_NOT_SUPPORTED and var is not None, (var, e)
+            continue
+        print("case", name, dtype, var or "default", "->", kname, flush=True)
+        H.check(dtype, _logical(y).double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (name, dtype, kname))
+        _ran.setdefault(dtype, set()).add(kname)
+        ran += 1
+    assert ran >= 2
+
+
+def test_blocked_filter_kernels_were_exercised():
+    """Every fp32/fp64 tap-batched kernel, a tap-order gather and the direct kernel ran on blocked inputs."""
+    want = {v for dt in ("f32", "f64") for v in VARIANTS[dt] if v.startswith("halo_")}
+    got = _ran.get("f32", set()) | _ran.get("f64", set())
+    assert want <= got, "halo variants never run on blocked layouts: %s" % sorted(want - got)
+    assert any(k.endswith("_tap") for k in _ran.get("bf16", set()))
+    assert "direct" in got and any(k.startswith("halo_bf16") for k in _ran.get("bf16", set()))
+
+
+def _full(lay, cb, integer=False):
+    dist = ("integers", -4, 4) if integer else None
+    x64, w64 = H.inputs(lay, dist, dist)
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    case = (lay.name, lay.N, lay.C, lay.H, lay.W, lay.K, lay.R, lay.S, lay.stride, lay.padding, None,
+            cb, (cb, cb), cb)
+    return x64, w64, case, (N, K, P, Q)
+
+
+FULL = [(workloads.ALEXNET[1], 16), (workloads.ALEXNET[1], 32),
+        ([l for l in workloads.PRECISION if l.name == "prec_conv4_bf16_nchw"][0], 32)]
+
+
+@pytest.mark.parametrize("lay,cb", FULL, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_workload_layer_blocked_sampled(lay, cb):
+    """Full-size layer, x, filters and y blocked: sampled parity, NaN-safe beta = 0, rerun bit-identity."""
+    x64, w64, case, yshape = _full(lay, cb)
+    x, w, y = _place(case, lay.dtype, x64, w64, yshape)
+    kname = _run(x, w, y, lay.stride, lay.padding)
+    print("layer", lay.name, "cb", cb, "->", kname, flush=True)
+    yl = _logical(y)
+    assert bool(torch.isfinite(yl).all()), "unwritten or non-finite outputs"
+    rng = np.random.default_rng(lay.config * 1000 + lay.layer + 17)
+    idx = H.sample_coords(rng, *yshape, 3000)
+    ref, bound = oracle.conv2d_fprop_at(x64, w64, idx, lay.stride, lay.padding)
+    rel, worst = H.check(lay.dtype, H.gather(yl, idx), ref, bound, what=lay.name)
+    print("  sampled rel-L2 %.3e, worst |err|/B %.3e" % (rel, worst), flush=True)
+    _, _, y2 = _place(case, lay.dtype, x64, w64, yshape, fill=0.0)
+    _run(x, w, y2, lay.stride, lay.padding)
+    assert torch.equal(y, y2), "rerun not bit-identical"
+
+
+@pytest.mark.parametrize("lay,cb", FULL[:1] + FULL[2:], ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_workload_layer_blocked_integer_exact(lay, cb):
+    x64, w64, case, yshape = _full(lay, cb, integer=True)
+    x, w, y = _place(case, lay.dtype, x64, w64, yshape)
+    _run(x, w, y, lay.stride, lay.padding)
+    rng = np.random.default_rng(lay.config * 1000 + lay.layer + 23)
+    idx = H.sample_coords(rng, *yshape, 3000)
+    ref, _ = oracle.conv2d_fprop_at(x64, w64, idx, lay.stride, lay.padding)
+    got = H.gather(_logical(y), idx)
+    assert np.array_equal(got, ref), "%s: %d mismatches" % (lay.name, int((got != ref).sum()))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
+def test_blocked_alpha_beta(dtype):
+    case = CASES[2] if dtype == "bf16" else CASES[0]
+    name, N, C, Hh, Ww, K, R, S, stride, pads = case[:10]
+    lay = Layer(name, 9, 4, N, C, Hh, Ww, K, R, S, stride, pads, dtype, U, U)
+    xi, wi = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
+    acc, _ = oracle.conv2d_fprop(xi, wi, stride, pads)
+    y_old = gen.integers(98, acc.shape)
+    x, w, y = _place(case, dtype, xi, wi, acc.shape)
+    ykb = case[13]
+    y.copy_(mic.to_blocked(torch.from_numpy(y_old).to(y.dtype).to(H.dev()), ykb))
+    _run(x, w, y, stride, pads, alpha=0.5, beta=0.25)
+    assert np.array_equal(_logical(y).double().cpu().numpy(), 0.5 * acc + 0.25 * y_old)
