@@ -1,0 +1,304 @@
+// conv_bwd_filter_halo.hip -- filter gradient of a stride-1 convolution with
+// the receptive fields read from an LDS halo (gfx950 MFMA).
+//
+//   dw[k,c,r,s] = alpha * sum_{n,p,q} dy[n,k,p,q] * X(n, c, p + r - pad_top, q + s - pad_left)
+//               + beta * dw[k,c,r,s]
+//
+// (the adjoint of the forward sum in F; cuDNN page, "Proposed Method":
+// forward and backward routines; maxDNN page, Abstract and RQ4: the forward
+// techniques carry over to the backward pass).  The matrix product is the
+// one of conv_bwd_filter.hip -- rows k (TM per tile), columns j = (c, r, s)
+// (TN per tile), reduction over the positions (n, p, q) -- but the
+// reduction runs in chunks of PR output rows of one image n, and each chunk
+// is staged in LDS once:
+//
+//   DY[k][pos]           dy[n, k, p0 + pos / WPH, pos % WPH]   (0 for q >= Q or p >= P)
+//   HALO[c - c_lo][h][w] X(n, c, p0 + h - pad_top, w - pad_left)  (0 outside the plane)
+//
+// with the position index pos = (p - p0) * WPH + q over a compile-time row
+// pitch WPH >= Q + S - 1.  Then B[pos, (c, r, s)] = HALO[c - c_lo][p - p0 + r][q + s]
+// = HALO_flat[base(c, r, s) + pos]: both MFMA operands are LDS reads at a
+// per-lane base plus the compile-time step, and the MFMA loop carries no
+// address arithmetic (the same device the forward halo kernel uses for its
+// input operand, with the roles of positions and taps exchanged).  Padding
+// positions (q >= Q, p >= P) have dy = 0 and cost MFMA steps only: Q / WPH
+// of the work is useful.  Lane group g of an MFMA takes positions
+// [g * SEGP, (g + 1) * SEGP).
+//
+// No workspace: the reduction is not split across workgroups.  The
+// epilogue stores dw (packed K,C,R,S) along j as conv_bwd_filter.hip does.
+//
+// Parameters as for conv_bwd_filter.hip: x, strides sx*; w = dy, strides
+// sd*; y = dw with syn = C*R*S, syk = 1; M = K, K = C*R*S; div_pq = div_q = 1;
+// u = v = 1 (host-checked), Q + S - 1 <= WPH.
+#include <stdint.h>
+
+#include <type_traits>
+
+#include <hip/hip_runtime.h>
+
+#include "conv_params.h"
+#include "kernels.h"
+#include "mfma_common.h"
+#include "tile_map.h"
+
+namespace miconv {
+
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WPH, int PR, int PLANE, int KS>
+__global__ void __launch_bounds__(256 * KS)
+conv_bwd_filter_halo_kernel(const ConvParams p)
+{
+    using In = typename Pol::In;
+    using AccV = typename Pol::AccV;
+    constexpr int NT = 256;                          // threads per half
+    constexpr int NTT = NT * KS;                     // threads of the workgroup
+    constexpr int BM = Pol::BM;
+    constexpr int G = Pol::G;
+    constexpr int ES = (int)sizeof(In);
+    constexpr int RS = R * S;
+    constexpr int WM = TM / WAVES_M;
+    constexpr int WN = TN / WAVES_N;
+    constexpr int FM = WM / BM;
+    constexpr int FN = WN / BM;
+    constexpr int NPOS = PR * WPH;                   // positions per chunk
+    constexpr int SEGP = NPOS / G;                   // MFMA steps per chunk
+    constexpr int SEGH = SEGP / KS;                  // ... per half
+    constexpr int DYP = NPOS + 1;                    // DY row pitch (odd: rows fall on other banks)
+    constexpr int HROWS = PR + R - 1;
+    // A padding position's tap (q + s up to WPH + S - 2) reads up to S - 1
+    // elements past the plane's last row: PLANE >= HROWS * WPH + S - 1 leaves
+    // spare elements, zeroed once, so such reads see finite zeros.  Beyond
+    // that, WPH and PLANE are chosen so the 32 columns (c, r, s) a half-wave
+    // reads land on distinct LDS banks but for at most two-way conflicts.
+    static_assert(PLANE >= HROWS * WPH + S - 1, "plane spare");
+    constexpr int CH = (RS - 1 + TN - 1) / RS + 1;   // channels TN consecutive columns can touch
+    constexpr int DY_ELEMS = TM * DYP;
+    constexpr int BUF_BYTES = ((DY_ELEMS + CH * PLANE) * ES + 15) / 16 * 16;
+    // DY loader: in each half TPK threads per filter row; half h takes rows
+    // pr = h + KS * i, a thread positions q0 + TPK * j of them
+    constexpr int TPK = NT / TM;
+    constexpr int QPT = WPH / TPK;                   // q values a thread visits per row
+    constexpr int PRH = (PR + KS - 1) / KS;          // rows per half
+    constexpr int NDY = PRH * QPT;                   // DY elements per thread per chunk
+    // halo loader: units (channel, row, column), column fastest, over all threads
+    constexpr int HU = CH * HROWS * WPH;
+    constexpr int NH = (HU + NTT - 1) / NTT;
+    static_assert(Pol::V == 1, "scalar-operand MFMA policies only");
+    static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
+    static_assert(NPOS % G == 0 && NT % TM == 0 && WPH % TPK == 0, "loader shapes");
+    static_assert((KS == 1 || KS == 2) && SEGP % KS == 0, "one or two halves split the steps");
+    static_assert(NDY <= 64 && NH <= 32, "validity masks");
+    static_assert(2 * BUF_BYTES <= 160 * 1024, "two chunk buffers fit the LDS");
+    static_assert((SEGP + DYP) * ES < 65536, "LDS immediate offsets");
+    static_assert(4 * BM * (BM + 1) * (int)sizeof(typename Pol::Acc) <= 2 * BUF_BYTES, "epilogue stage fits");
+
+    static_assert(KS == 1 || 4 * FM * FN * Pol::NACC * 64 * (int)sizeof(typename Pol::Acc) <= 2 * BUF_BYTES,
+                  "partial sums fit in the chunk buffers");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF_BYTES];
+
+    const int half = KS == 2 ? (int)(threadIdx.x >> 8) : 0;
+    const int tid = threadIdx.x & 255;               // thread within its half
+    const int lane = tid & 63;
+    const int wave = tid >> 6;                       // wave within its half
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int mt = tile / p.n_tiles;
+    const int nt = tile - mt * p.n_tiles;
+    const int m0 = mt * TM;
+    const int n0 = nt * TN;
+    const int c_lo = n0 / RS;
+
+    const In* __restrict__ x = static_cast<const In*>(p.x);
+    const In* __restrict__ dy = static_cast<const In*>(p.w);
+    const int PB = (p.P + PR - 1) / PR;              // row blocks per image
+    const int nch = p.N * PB;
+
+    // both chunk buffers start zeroed (the planes' spare elements stay so)
+    for (int i = (int)threadIdx.x; i < 2 * BUF_BYTES / 16; i += NTT)
+        reinterpret_cast<u32x4*>(smem)[i] = u32x4{0, 0, 0, 0};
+    __syncthreads();
+
+    // ---- DY loader geometry: filter row kr, first position q0
+    const int kr = tid / TPK;
+    const int q0 = tid % TPK;
+    const bool k_ok = m0 + kr < p.M;
+    const int dy_thread = (m0 + (k_ok ? kr : 0)) * p.sdk + half * p.sdp + q0 * p.sdq;
+    uint32_t q_ok = 0;                               // bit j: q0 + TPK * j < Q
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) q_ok |= (q0 + TPK * j < p.Q ? 1u : 0u) << j;
+
+    In dy_val[NDY];
+    uint64_t dy_ok = 0;
+    In h_val[NH];
+    uint32_t h_ok = 0;
+
+    // chunk ch -> registers (loads unconditional at a valid address, masked at the LDS store)
+    auto load_chunk = [&](int ch) {
+        const int n = ch / PB;
+        const int p0 = (ch - n * PB) * PR;
+        const int dy_chunk = n * p.sdn + p0 * p.sdp;
+        uint64_t okb = 0;
+#pragma unroll
+        for (int i = 0; i < NDY; ++i) {
+            const int prs = KS * (i / QPT);          // compile-time row step (row half + prs)
+            const int qj = i % QPT;
+            const bool ok = k_ok && ((q_ok >> qj) & 1) && half + prs < PR && p0 + half + prs < p.P;
+            const int off = dy_chunk + dy_thread + prs * p.sdp + TPK * qj * p.sdq;
+            dy_val[i] = load_elem(dy + (ok ? off : 0));
+            okb |= (uint64_t)(ok ? 1u : 0u) << i;
+        }
+        dy_ok = okb;
+        uint32_t hb = 0;
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int e = (int)threadIdx.x + NTT * i;
+            const int hc = e % WPH;
+            const int rowi = e / WPH;
+            const int chl = rowi / HROWS;
+            const int hr = rowi - chl * HROWS;
+            const int c = c_lo + chl;
+            const int h = p0 + hr - p.pad_top;
+            const int w = hc - p.pad_left;
+            const bool ok = e < HU && c < p.C && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
+            h_val[i] = load_elem(x + (ok ? n * p.sxn + c * p.sxc + h * p.sxh + w * p.sxw : 0));
+            hb |= (ok ? 1u : 0u) << i;
+        }
+        h_ok = hb;
+    };
+
+    auto store_chunk = [&](int buf) {
+        In* dyl = reinterpret_cast<In*>(smem + buf * BUF_BYTES);
+        In* hal = dyl + DY_ELEMS;
+        In* dst = dyl + kr * DYP + half * WPH + q0;
+#pragma unroll
+        for (int i = 0; i < NDY; ++i) {
+            const int prs = KS * (i / QPT);
+            const int qj = i % QPT;
+            if (PR % KS == 0 || half + prs < PR)     // (an odd PR leaves half 1 one row short)
+                dst[prs * WPH + TPK * qj] = ((dy_ok >> i) & 1) ? dy_val[i] : In(0);
+        }
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int e = (int)threadIdx.x + NTT * i;
+            if (HU % NTT == 0 || e < HU) {
+                const int hc = e % WPH;
+                const int rowi = e / WPH;
+                const int chl = rowi / HROWS;
+                const int hr = rowi - chl * HROWS;
+                hal[chl * PLANE + hr * WPH + hc] = ((h_ok >> i) & 1) ? h_val[i] : In(0);
+            }
+        }
+    };
+
+    // ---- per-lane operand bases (elements): A = DY row, B = the halo tap of a column
+    const int wm = wave / WAVES_N;
+    const int wn = wave % WAVES_N;
+    const int lrow = lane % BM;
+    const int lgrp = lane / BM;
+    // half h takes steps [h * SEGH, (h + 1) * SEGH) of every lane group's segment
+    int a_base[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a_base[i] = (wm * WM + i * BM + lrow) * DYP + lgrp * SEGP + half * SEGH;
+    int b_base[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * WN + j * BM + lrow;        // past C*R*S: a zero region, masked at the store
+        uint32_t c, rs, r, s;
+        p.div_rs.divmod((uint32_t)col, c, rs);
+        p.div_s.divmod(rs, r, s);
+        b_base[j] = DY_ELEMS + ((int)c - c_lo) * PLANE + (int)r * WPH + (int)s + lgrp * SEGP + half * SEGH;
+    }
+
+    AccV acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = AccV{};
+
+    if (nch > 0) {
+        load_chunk(0);
+        store_chunk(0);
+        __syncthreads();
+    }
+    for (int ch = 0; ch < nch; ++ch) {
+        const int cur = ch & 1;
+        const bool more = ch + 1 < nch;
+        load_chunk(more ? ch + 1 : ch);              // unconditional: no load under a branch
+        __builtin_amdgcn_sched_barrier(0);
+        const In* buf = reinterpret_cast<const In*>(smem + cur * BUF_BYTES);
+#pragma unroll
+        for (int t = 0; t < SEGH; ++t) {
+            In a[FM], b[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a[i] = buf[a_base[i] + t];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b[j] = buf[b_base[j] + t];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Pol::mfma_s(a[i], b[j], acc[i][j]);
+        }
+        if (more) store_chunk(cur ^ 1);
+        __syncthreads();
+    }
+
+    if constexpr (KS == 2) {
+        // half 1's partial sums -> LDS -> added by half 0 in a fixed order
+        typename Pol::Acc* red = reinterpret_cast<typename Pol::Acc*>(smem);
+        auto red_at = [&](int i, int j, int e) { return ((((wave * FM + i) * FN + j) * Pol::NACC + e) << 6) + lane; };
+        if (half == 1) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int e = 0; e < Pol::NACC; ++e) red[red_at(i, j, e)] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (half == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int e = 0; e < Pol::NACC; ++e) acc[i][j][e] += red[red_at(i, j, e)];
+        }
+        __syncthreads();
+    }
+    store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, p.M, wave, lane, half == 0);
+}
+
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WPH, int PR, int PLANE, int KS>
+static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
+{
+    ConvParams p = p0;
+    if (p.u != 1 || p.v != 1 || p.R != R || p.S != S || p.Q + S - 1 > WPH) return hipErrorInvalidValue;
+    p.m_tiles = (p.M + TM - 1) / TM;
+    p.n_tiles = (p.K + TN - 1) / TN;
+    const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
+    hipLaunchKernelGGL((conv_bwd_filter_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, WPH, PR, PLANE, KS>), grid,
+                       dim3(256 * KS), 0, stream, p);
+    return hipGetLastError();
+}
+
+// row pitch WPH and plane pitch PLANE: the smallest with at most two-way
+// (fp64 three-way) bank conflicts on the halo reads, searched offline
+//        name                     policy   TM  TN  waves  R  S  WPH  PR  PLANE  KS
+#define MICONV_WGH_VARIANTS(X)                                           \
+    X(WGH_F32_3x3_W16, PolF32, 64, 64, 2, 2, 3, 3, 16, 13, 243, 2)       \
+    X(WGH_F32_5x5_W24, PolF32, 64, 64, 2, 2, 5, 5, 24, 7, 269, 2)        \
+    X(WGH_F32_5x5_W36, PolF32, 64, 64, 2, 2, 5, 5, 36, 7, 401, 2)        \
+    X(WGH_F64_3x3_W16, PolF64, 64, 64, 2, 2, 3, 3, 16, 7, 147, 2)
+
+hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream)
+{
+    switch (v) {
+#define X(name, pol, tm, tn, wmm, wnn, r, s, wph, pr, plane, ks) \
+    case Variant::name: return launch_wgh_variant<pol, tm, tn, wmm, wnn, r, s, wph, pr, plane, ks>(p, stream);
+        MICONV_WGH_VARIANTS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace miconv

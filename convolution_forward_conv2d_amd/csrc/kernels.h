@@ -43,6 +43,10 @@ enum class Variant : int {
     WG_F64_64x64,
     WG_BF16_128x128,
     WG_BF16_64x64,
+    WGH_F32_3x3_W16,        // filter gradient, stride 1, halo in LDS (conv_bwd_filter_halo.hip)
+    WGH_F32_5x5_W24,
+    WGH_F32_5x5_W36,
+    WGH_F64_3x3_W16,
     BR_F32_128x128,         // batch-reduce GEMM, shared-LDS tiles (brgemm.hip)
     BR_F32_64x64,
     BR_F32_32x64,
@@ -81,6 +85,9 @@ hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);
 
 // Filter gradient (implicit GEMM over the output positions); p laid out as
 // conv_bwd_filter.hip describes.
+// Filter gradient of a stride-1 layer through an LDS halo (R, S, dtype and
+// Q + S - 1 <= the variant's row pitch, host-checked).
+hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream);
 hipError_t launch_bwd_filter(Variant v, const ConvParams& p, hipStream_t stream);
 
 // Batch-reduce GEMM; p laid out as brgemm.hip describes.  16-byte operand

@@ -157,6 +157,26 @@ const Candidate kWgBF16[] = {
     {Variant::WG_BF16_128x128, 128, 128, "wg_bf16_128x128"},
     {Variant::WG_BF16_64x64, 64, 64, "wg_bf16_64x64"},
 };
+// filter gradient through an LDS halo (conv_bwd_filter_halo.hip): stride 1,
+// fixed R x S, Q + S - 1 <= the row pitch
+struct WghCandidate {
+    Candidate c;
+    DType dt;
+    int r, s, wph;
+};
+const WghCandidate kWgh[] = {
+    {{Variant::WGH_F32_3x3_W16, 64, 64, "wgh_f32_3x3_64x64"}, DType::F32, 3, 3, 16},
+    {{Variant::WGH_F32_5x5_W24, 64, 64, "wgh_f32_5x5_w24_64x64"}, DType::F32, 5, 5, 24},
+    {{Variant::WGH_F32_5x5_W36, 64, 64, "wgh_f32_5x5_w36_64x64"}, DType::F32, 5, 5, 36},
+    {{Variant::WGH_F64_3x3_W16, 64, 64, "wgh_f64_3x3_64x64"}, DType::F64, 3, 3, 16},
+};
+
+bool is_wgh(Variant v)
+{
+    return v == Variant::WGH_F32_3x3_W16 || v == Variant::WGH_F32_5x5_W24 || v == Variant::WGH_F32_5x5_W36 ||
+           v == Variant::WGH_F64_3x3_W16;
+}
+
 // batch-reduce GEMM (brgemm.hip): shared-LDS tiles for large products
 const Candidate kBrF32[] = {
     {Variant::BR_F32_128x128, 128, 128, "br_f32_128x128"},
@@ -824,7 +844,24 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
     if (force && !force[0]) force = nullptr;
     double best = 0;
     bool found = false;
-    for (int i = 0; i < count; ++i) {
+    // stride-1 layers whose rows fit a halo variant's pitch take the halo kernel
+    for (const WghCandidate& wc : kWgh) {
+        if (force && strcmp(force, wc.c.name) != 0) continue;
+        const bool ok = wc.dt == pl.dt && wc.r == wd->r && wc.s == wd->s && cd->u == 1 && cd->v == 1 &&
+                        Q + wc.s - 1 <= wc.wph;
+        if (!ok) {
+            if (force) {
+                pl.status = MIC_STATUS_NOT_SUPPORTED;   // forced onto a layer it cannot take
+                return pl;
+            }
+            continue;
+        }
+        pl.cand = wc.c;
+        found = true;
+        break;
+    }
+    const bool halo = found;
+    for (int i = 0; i < count && !halo; ++i) {
         if (force && strcmp(force, list[i].name) != 0) continue;
         const int64_t tiles = (int64_t)((p.M + list[i].tm - 1) / list[i].tm) * ((p.K + list[i].tn - 1) / list[i].tn);
         const int64_t rounds = (tiles + num_cu - 1) / num_cu;
@@ -1412,7 +1449,8 @@ mic_status mic_conv_backward_filter(mic_handle handle, double alpha, mic_tensor_
     if (!handle) return MIC_STATUS_BAD_PARAM;
     Plan pl = make_wgrad_plan(handle, x_desc, x, dy_desc, dy, conv, dw_desc, dw, alpha, beta, true);
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
-    const hipError_t err = miconv::launch_bwd_filter(pl.cand.v, pl.p, handle->stream);
+    const hipError_t err = is_wgh(pl.cand.v) ? miconv::launch_bwd_filter_halo(pl.cand.v, pl.p, handle->stream)
+                                             : miconv::launch_bwd_filter(pl.cand.v, pl.p, handle->stream);
     return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
 }
 

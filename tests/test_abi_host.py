@@ -319,8 +319,21 @@ def _wgrad_name(lay, dts=None):
 
 
 def test_wgrad_kernel_choice_host_only():
+    """Stride-1 3x3 / 5x5 fp32 and 3x3 fp64 layers whose rows fit the halo pitch take the halo
+    kernel; the rest (strided, other filters, bf16) the gather kernel."""
+    want_halo = {"alexnet_conv2": "wgh_f32_5x5_w36_64x64", "alexnet_conv3": "wgh_f32_3x3_64x64",
+                 "alexnet_conv4": "wgh_f32_3x3_64x64", "alexnet_conv5": "wgh_f32_3x3_64x64",
+                 "overfeat_l2": "wgh_f32_5x5_w24_64x64", "overfeat_l3": "wgh_f32_3x3_64x64",
+                 "overfeat_l4": "wgh_f32_3x3_64x64", "overfeat_l5": "wgh_f32_3x3_64x64",
+                 "tiny": "wgh_f32_3x3_64x64"}
     for lay in workloads.ALL_LAYERS:
-        assert _wgrad_name(lay).startswith("wg_%s_" % lay.dtype), lay.name
+        name = _wgrad_name(lay)
+        if lay.name in want_halo:
+            assert name == want_halo[lay.name], (lay.name, name)
+        elif lay.dtype == "f64":
+            assert name == "wgh_f64_3x3_64x64", (lay.name, name)
+        else:
+            assert name.startswith("wg_%s_" % lay.dtype), (lay.name, name)
 
 
 def test_wgrad_shape_and_type_errors(monkeypatch):

@@ -31,10 +31,13 @@ from test_parity_gpu import SMALL_SHAPES, U
 pytestmark = pytest.mark.gpu
 
 WG_VARIANTS = {
-    "f32": ["wg_f32_128x128", "wg_f32_64x128", "wg_f32_128x64", "wg_f32_64x64"],
-    "f64": ["wg_f64_128x64", "wg_f64_64x64"],
+    "f32": ["wg_f32_128x128", "wg_f32_64x128", "wg_f32_128x64", "wg_f32_64x64", "wgh_f32_3x3_64x64",
+            "wgh_f32_5x5_w24_64x64", "wgh_f32_5x5_w36_64x64"],
+    "f64": ["wg_f64_128x64", "wg_f64_64x64", "wgh_f64_3x3_64x64"],
     "bf16": ["wg_bf16_128x128", "wg_bf16_64x64"],
 }
+# the halo variants (wgh_) take stride-1 layers of their filter size whose rows fit their pitch; the
+# library answers NOT_SUPPORTED for other shapes, and every variant must run on at least one shape
 _ran = set()
 
 
@@ -77,7 +80,12 @@ def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
         monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", var)
         print("case", shape["name"], dtype, var, flush=True)
         dw = _out(lay)
-        _run(lay, x, dy, dw)
+        try:
+            _run(lay, x, dy, dw)
+        except mic.MicError as e:
+            if var.startswith("wgh_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+                continue
+            raise
         H.check(dtype, dw.double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (shape["name"], dtype, var),
                 rel_scale=H.rel_l2_scale(N * P * Q))
         _ran.add(var)
@@ -140,8 +148,9 @@ def test_workload_layer_integer_exact(lay):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
-def test_alpha_beta(dtype, monkeypatch):
-    lay = _small("wg_ab", 2, 20, 13, 11, 36, 3, 3, (1, 2), (1, 1, 1, 0), dtype)
+@pytest.mark.parametrize("geom", [((1, 2), (1, 1, 1, 0)), ((1, 1), (1, 1, 1, 1))], ids=["s12", "s11"])
+def test_alpha_beta(dtype, geom, monkeypatch):
+    lay = _small("wg_ab", 2, 20, 13, 11, 36, 3, 3, geom[0], geom[1], dtype)
     xi, _ = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
     N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
     dyi = _dy(lay, (N, K, P, Q), integer=True)
@@ -152,7 +161,12 @@ def test_alpha_beta(dtype, monkeypatch):
     for var in WG_VARIANTS[dtype]:
         monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", var)
         dw = torch.from_numpy(old).to(H.OUT_DT[dtype]).to(H.dev())
-        _run(lay, x, dy, dw, alpha=0.5, beta=0.25)
+        try:
+            _run(lay, x, dy, dw, alpha=0.5, beta=0.25)
+        except mic.MicError as e:
+            if var.startswith("wgh_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+                continue
+            raise
         assert np.array_equal(dw.double().cpu().numpy(), 0.5 * acc + 0.25 * old), var
 
 
