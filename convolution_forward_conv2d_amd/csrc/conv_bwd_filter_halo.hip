@@ -44,6 +44,17 @@
 
 namespace miconv {
 
+namespace {
+template <int B, int E, class F>
+__device__ __forceinline__ void unroll_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        unroll_for<B + 1, E>(f);
+    }
+}
+}  // namespace
+
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WPH, int PR, int PLANE, int KS>
 __global__ void __launch_bounds__(256 * KS)
 conv_bwd_filter_halo_kernel(const ConvParams p)
@@ -132,60 +143,60 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     In h_val[NH];
     uint32_t h_ok = 0;
 
-    // chunk ch -> registers (loads unconditional at a valid address, masked at the LDS store)
-    auto load_chunk = [&](int ch) {
-        const int n = ch / PB;
-        const int p0 = (ch - n * PB) * PR;
-        const int dy_chunk = n * p.sdn + p0 * p.sdp;
-        uint64_t okb = 0;
-#pragma unroll
-        for (int i = 0; i < NDY; ++i) {
-            const int prs = KS * (i / QPT);          // compile-time row step (row half + prs)
-            const int qj = i % QPT;
-            const bool ok = k_ok && ((q_ok >> qj) & 1) && half + prs < PR && p0 + half + prs < p.P;
-            const int off = dy_chunk + dy_thread + prs * p.sdp + TPK * qj * p.sdq;
-            dy_val[i] = load_elem(dy + (ok ? off : 0));
-            okb |= (uint64_t)(ok ? 1u : 0u) << i;
-        }
-        dy_ok = okb;
-        uint32_t hb = 0;
-#pragma unroll
-        for (int i = 0; i < NH; ++i) {
+    // The next chunk moves global -> registers -> LDS in NL pieces (one
+    // element each) spread over the current chunk's MFMA steps: loads over
+    // the first half, LDS stores over the second.  Loads are unconditional
+    // at a valid address; the validity bits zero the values at the store.
+    constexpr int NL = NDY + NH;
+    int cn = 0, cp0 = 0, cdy = 0;                    // the chunk the pieces in flight belong to
+    auto set_chunk = [&](int ch) {
+        cn = ch / PB;
+        cp0 = (ch - cn * PB) * PR;
+        cdy = cn * p.sdn + cp0 * p.sdp;
+        dy_ok = 0;
+        h_ok = 0;
+    };
+    auto load_piece = [&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (q < NDY) {
+            constexpr int prs = KS * (q / QPT);      // row half + prs, column q0 + TPK * qj
+            constexpr int qj = q % QPT;
+            const bool ok = k_ok && ((q_ok >> qj) & 1) && half + prs < PR && cp0 + half + prs < p.P;
+            const int off = cdy + dy_thread + prs * p.sdp + TPK * qj * p.sdq;
+            dy_val[q] = load_elem(dy + (ok ? off : 0));
+            dy_ok |= (uint64_t)(ok ? 1u : 0u) << q;
+        } else {
+            constexpr int i = q - NDY;
             const int e = (int)threadIdx.x + NTT * i;
             const int hc = e % WPH;
             const int rowi = e / WPH;
             const int chl = rowi / HROWS;
             const int hr = rowi - chl * HROWS;
             const int c = c_lo + chl;
-            const int h = p0 + hr - p.pad_top;
+            const int h = cp0 + hr - p.pad_top;
             const int w = hc - p.pad_left;
             const bool ok = e < HU && c < p.C && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
-            h_val[i] = load_elem(x + (ok ? n * p.sxn + c * p.sxc + h * p.sxh + w * p.sxw : 0));
-            hb |= (ok ? 1u : 0u) << i;
+            h_val[i] = load_elem(x + (ok ? cn * p.sxn + c * p.sxc + h * p.sxh + w * p.sxw : 0));
+            h_ok |= (ok ? 1u : 0u) << i;
         }
-        h_ok = hb;
     };
-
-    auto store_chunk = [&](int buf) {
+    auto store_piece = [&](auto qc, int buf) {
+        constexpr int q = decltype(qc)::value;
         In* dyl = reinterpret_cast<In*>(smem + buf * BUF_BYTES);
-        In* hal = dyl + DY_ELEMS;
-        In* dst = dyl + kr * DYP + half * WPH + q0;
-#pragma unroll
-        for (int i = 0; i < NDY; ++i) {
-            const int prs = KS * (i / QPT);
-            const int qj = i % QPT;
+        if constexpr (q < NDY) {
+            constexpr int prs = KS * (q / QPT);
+            constexpr int qj = q % QPT;
             if (PR % KS == 0 || half + prs < PR)     // (an odd PR leaves half 1 one row short)
-                dst[prs * WPH + TPK * qj] = ((dy_ok >> i) & 1) ? dy_val[i] : In(0);
-        }
-#pragma unroll
-        for (int i = 0; i < NH; ++i) {
+                dyl[kr * DYP + half * WPH + q0 + prs * WPH + TPK * qj] = ((dy_ok >> q) & 1) ? dy_val[q] : In(0);
+        } else {
+            constexpr int i = q - NDY;
             const int e = (int)threadIdx.x + NTT * i;
             if (HU % NTT == 0 || e < HU) {
                 const int hc = e % WPH;
                 const int rowi = e / WPH;
                 const int chl = rowi / HROWS;
                 const int hr = rowi - chl * HROWS;
-                hal[chl * PLANE + hr * WPH + hc] = ((h_ok >> i) & 1) ? h_val[i] : In(0);
+                dyl[DY_ELEMS + chl * PLANE + hr * WPH + hc] = ((h_ok >> i) & 1) ? h_val[i] : In(0);
             }
         }
     };
@@ -216,29 +227,48 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         for (int j = 0; j < FN; ++j) acc[i][j] = AccV{};
 
     if (nch > 0) {
-        load_chunk(0);
-        store_chunk(0);
+        set_chunk(0);
+        unroll_for<0, NL>([&](auto qc) { load_piece(qc); });
+        unroll_for<0, NL>([&](auto qc) { store_piece(qc, 0); });
         __syncthreads();
     }
     for (int ch = 0; ch < nch; ++ch) {
         const int cur = ch & 1;
-        const bool more = ch + 1 < nch;
-        load_chunk(more ? ch + 1 : ch);              // unconditional: no load under a branch
-        __builtin_amdgcn_sched_barrier(0);
+        set_chunk(ch + 1 < nch ? ch + 1 : ch);       // past the end: reload, written where nothing reads
         const In* buf = reinterpret_cast<const In*>(smem + cur * BUF_BYTES);
+        // operands are read one step ahead of their MFMA
+        In a[FM], b[FN];
 #pragma unroll
-        for (int t = 0; t < SEGH; ++t) {
-            In a[FM], b[FN];
+        for (int i = 0; i < FM; ++i) a[i] = buf[a_base[i]];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) a[i] = buf[a_base[i] + t];
+        for (int j = 0; j < FN; ++j) b[j] = buf[b_base[j]];
+        unroll_for<0, SEGH>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            unroll_for<0, NL>([&](auto qc) {
+                if constexpr (decltype(qc)::value * (SEGH / 2) / NL == t) load_piece(qc);
+            });
+            In an[FM], bn[FN];
+            if constexpr (t + 1 < SEGH) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) b[j] = buf[b_base[j] + t];
+                for (int i = 0; i < FM; ++i) an[i] = buf[a_base[i] + t + 1];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bn[j] = buf[b_base[j] + t + 1];
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = Pol::mfma_s(a[i], b[j], acc[i][j]);
-        }
-        if (more) store_chunk(cur ^ 1);
+            unroll_for<0, NL>([&](auto qc) {
+                if constexpr (SEGH / 2 + decltype(qc)::value * (SEGH - SEGH / 2) / NL == t) store_piece(qc, cur ^ 1);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (t + 1 < SEGH) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) a[i] = an[i];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) b[j] = bn[j];
+            }
+        });
         __syncthreads();
     }
 
