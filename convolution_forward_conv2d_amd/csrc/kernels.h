@@ -47,6 +47,10 @@ enum class Variant : int {
     WGH_F32_5x5_W24,
     WGH_F32_5x5_W36,
     WGH_F64_3x3_W16,
+    WGS_F32_32x32,          // filter gradient, reduction split over waves (conv_bwd_filter_split.hip)
+    WGS_F32_16x16,
+    WGS_F64_32x32,
+    WGS_F64_16x16,
     BR_F32_128x128,         // batch-reduce GEMM, shared-LDS tiles (brgemm.hip)
     BR_F32_64x64,
     BR_F32_32x64,
@@ -89,6 +93,7 @@ hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);
 // Q + S - 1 <= the variant's row pitch, host-checked).
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream);
 hipError_t launch_bwd_filter(Variant v, const ConvParams& p, hipStream_t stream);
+hipError_t launch_bwd_filter_split(Variant v, const ConvParams& p, hipStream_t stream);
 
 // Batch-reduce GEMM; p laid out as brgemm.hip describes.  16-byte operand
 // loads are chosen inside when strides, k and alignment allow them.

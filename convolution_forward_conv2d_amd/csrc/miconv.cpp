@@ -142,39 +142,54 @@ const Candidate kBF16[] = {
     {Variant::MFMA_BF16_256x32, 256, 32, "mfma_bf16_256x32"},
 };
 const Candidate kDirect = {Variant::DIRECT, 0, 0, "direct"};
-// filter gradient (conv_bwd_filter.hip)
-const Candidate kWgF32[] = {
-    {Variant::WG_F32_128x128, 128, 128, "wg_f32_128x128"},
-    {Variant::WG_F32_64x128, 64, 128, "wg_f32_64x128"},
-    {Variant::WG_F32_128x64, 128, 64, "wg_f32_128x64"},
-    {Variant::WG_F32_64x64, 64, 64, "wg_f32_64x64"},
-};
-const Candidate kWgF64[] = {
-    {Variant::WG_F64_128x64, 128, 64, "wg_f64_128x64"},
-    {Variant::WG_F64_64x64, 64, 64, "wg_f64_64x64"},
-};
-const Candidate kWgBF16[] = {
-    {Variant::WG_BF16_128x128, 128, 128, "wg_bf16_128x128"},
-    {Variant::WG_BF16_64x64, 64, 64, "wg_bf16_64x64"},
-};
-// filter gradient through an LDS halo (conv_bwd_filter_halo.hip): stride 1,
-// fixed R x S, Q + S - 1 <= the row pitch
-struct WghCandidate {
+// Filter-gradient kernels: the gather kernel (conv_bwd_filter.hip, any
+// geometry), the LDS-halo kernel (conv_bwd_filter_halo.hip: stride 1, fixed
+// R x S, Q + S - 1 <= the row pitch wph) and the kernel that splits the
+// reduction over the waves of one workgroup (conv_bwd_filter_split.hip:
+// small tiles, tensors under 2 GiB).  ns is the measured time of one tile
+// per reduction position (N*P*Q) on MI355X with per_cu workgroups resident
+// on a compute unit; the plan picks the least rounds * ns.
+enum class WgKind { GATHER, HALO, SPLIT };
+struct WgCandidate {
     Candidate c;
     DType dt;
-    int r, s, wph;
+    WgKind kind;
+    int r, s, wph;      // halo kernel only
+    double ns;
+    int per_cu;
 };
-const WghCandidate kWgh[] = {
-    {{Variant::WGH_F32_3x3_W16, 64, 64, "wgh_f32_3x3_64x64"}, DType::F32, 3, 3, 16},
-    {{Variant::WGH_F32_5x5_W24, 64, 64, "wgh_f32_5x5_w24_64x64"}, DType::F32, 5, 5, 24},
-    {{Variant::WGH_F32_5x5_W36, 64, 64, "wgh_f32_5x5_w36_64x64"}, DType::F32, 5, 5, 36},
-    {{Variant::WGH_F64_3x3_W16, 64, 64, "wgh_f64_3x3_64x64"}, DType::F64, 3, 3, 16},
+const WgCandidate kWg[] = {
+    {{Variant::WG_F32_128x128, 128, 128, "wg_f32_128x128"}, DType::F32, WgKind::GATHER, 0, 0, 0, 170.0, 1},
+    {{Variant::WG_F32_64x128, 64, 128, "wg_f32_64x128"}, DType::F32, WgKind::GATHER, 0, 0, 0, 90.0, 1},
+    {{Variant::WG_F32_128x64, 128, 64, "wg_f32_128x64"}, DType::F32, WgKind::GATHER, 0, 0, 0, 90.0, 1},
+    {{Variant::WG_F32_64x64, 64, 64, "wg_f32_64x64"}, DType::F32, WgKind::GATHER, 0, 0, 0, 60.0, 1},
+    {{Variant::WG_F64_128x64, 128, 64, "wg_f64_128x64"}, DType::F64, WgKind::GATHER, 0, 0, 0, 157.0, 1},
+    {{Variant::WG_F64_64x64, 64, 64, "wg_f64_64x64"}, DType::F64, WgKind::GATHER, 0, 0, 0, 93.0, 1},
+    {{Variant::WG_BF16_128x128, 128, 128, "wg_bf16_128x128"}, DType::BF16, WgKind::GATHER, 0, 0, 0, 100.0, 1},
+    {{Variant::WG_BF16_64x64, 64, 64, "wg_bf16_64x64"}, DType::BF16, WgKind::GATHER, 0, 0, 0, 37.0, 1},
+    {{Variant::WGH_F32_3x3_W16, 64, 64, "wgh_f32_3x3_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 34.0, 1},
+    {{Variant::WGH_F32_5x5_W24, 64, 64, "wgh_f32_5x5_w24_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 32.0, 1},
+    {{Variant::WGH_F32_5x5_W36, 64, 64, "wgh_f32_5x5_w36_64x64"}, DType::F32, WgKind::HALO, 5, 5, 36, 39.0, 1},
+    {{Variant::WGH_F64_3x3_W16, 64, 64, "wgh_f64_3x3_64x64"}, DType::F64, WgKind::HALO, 3, 3, 16, 52.0, 1},
+    {{Variant::WGS_F32_32x32, 32, 32, "wgs_f32_32x32"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 12.5, 1},
+    {{Variant::WGS_F32_16x16, 16, 16, "wgs_f32_16x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 7.1, 2},
+    {{Variant::WGS_F64_32x32, 32, 32, "wgs_f64_32x32"}, DType::F64, WgKind::SPLIT, 0, 0, 0, 28.0, 1},
+    {{Variant::WGS_F64_16x16, 16, 16, "wgs_f64_16x16"}, DType::F64, WgKind::SPLIT, 0, 0, 0, 5.7, 1},
 };
+// the split kernel's loads run along the positions: with x or dy strided
+// along q (channels-last) they gather (measured 2.6x slower)
+constexpr double kSplitStridedPenalty = 2.6;
 
 bool is_wgh(Variant v)
 {
     return v == Variant::WGH_F32_3x3_W16 || v == Variant::WGH_F32_5x5_W24 || v == Variant::WGH_F32_5x5_W36 ||
            v == Variant::WGH_F64_3x3_W16;
+}
+
+bool is_wgs(Variant v)
+{
+    return v == Variant::WGS_F32_32x32 || v == Variant::WGS_F32_16x16 || v == Variant::WGS_F64_32x32 ||
+           v == Variant::WGS_F64_16x16;
 }
 
 // batch-reduce GEMM (brgemm.hip): shared-LDS tiles for large products
@@ -741,9 +756,12 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
 // ---------------------------------------------------------------- filter gradient
 
 // dw <- alpha * wgrad(x, dy) + beta * dw for the forward geometry (x, dw,
-// conv); dy must have the forward output's dims.  One kernel family
-// (conv_bwd_filter.hip); the tile shape by the quantisation cost model over
-// the dw tiles (the reduction over positions is not split: no workspace).
+// conv); dy must have the forward output's dims.  Stride-1 layers whose
+// rows fit a halo variant take conv_bwd_filter_halo.hip; the others the
+// gather kernel (conv_bwd_filter.hip) or, for a dw of few tiles, the kernel
+// that splits the reduction over the waves of one workgroup
+// (conv_bwd_filter_split.hip), by a quantisation cost model over the dw
+// tiles.  The reduction is never split across workgroups: no workspace.
 Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void* x,
                      const mic_tensor_desc_st* dyd, const void* dy, const mic_conv_desc_st* cd,
                      const mic_filter_desc_st* wd, const void* dw, double alpha, double beta,
@@ -830,25 +848,24 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
     p.alpha = alpha;
     p.beta = beta;
 
-    const Candidate* list = kWgF32;
-    int count = (int)(sizeof(kWgF32) / sizeof(kWgF32[0]));
-    if (pl.dt == DType::F64) {
-        list = kWgF64;
-        count = (int)(sizeof(kWgF64) / sizeof(kWgF64[0]));
-    } else if (pl.dt == DType::BF16) {
-        list = kWgBF16;
-        count = (int)(sizeof(kWgBF16) / sizeof(kWgBF16[0]));
-    }
     const int num_cu = h ? h->num_cu : kDefaultCUs;
     const char* force = getenv("MIC_FORCE_WGRAD_VARIANT");
     if (force && !force[0]) force = nullptr;
+    // the split kernel addresses x and dy with 32-bit byte offsets and reads
+    // zeros at offset 2^31 (range-checked buffer loads)
+    const int64_t es = (int64_t)dtype_size(xd->dtype);
+    const bool split_fits = extent(*xd) * es < INT32_MAX && extent(*dyd) * es < INT32_MAX;
+    const bool unit_q = xd->sw == 1 && dyd->sw == 1;
     double best = 0;
     bool found = false;
-    // stride-1 layers whose rows fit a halo variant's pitch take the halo kernel
-    for (const WghCandidate& wc : kWgh) {
+    for (const WgCandidate& wc : kWg) {
+        if (wc.dt != pl.dt) continue;
         if (force && strcmp(force, wc.c.name) != 0) continue;
-        const bool ok = wc.dt == pl.dt && wc.r == wd->r && wc.s == wd->s && cd->u == 1 && cd->v == 1 &&
-                        Q + wc.s - 1 <= wc.wph;
+        bool ok = true;
+        if (wc.kind == WgKind::HALO)
+            ok = wc.r == wd->r && wc.s == wd->s && cd->u == 1 && cd->v == 1 && Q + wc.s - 1 <= wc.wph;
+        else if (wc.kind == WgKind::SPLIT)
+            ok = split_fits;
         if (!ok) {
             if (force) {
                 pl.status = MIC_STATUS_NOT_SUPPORTED;   // forced onto a layer it cannot take
@@ -856,21 +873,14 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
             }
             continue;
         }
-        pl.cand = wc.c;
-        found = true;
-        break;
-    }
-    const bool halo = found;
-    for (int i = 0; i < count && !halo; ++i) {
-        if (force && strcmp(force, list[i].name) != 0) continue;
-        const int64_t tiles = (int64_t)((p.M + list[i].tm - 1) / list[i].tm) * ((p.K + list[i].tn - 1) / list[i].tn);
-        const int64_t rounds = (tiles + num_cu - 1) / num_cu;
-        const double reuse = (double)list[i].tm * list[i].tn / (list[i].tm + list[i].tn);
-        const double eff = reuse >= 48.0 ? 1.0 : reuse / 48.0;
-        const double cost = (double)rounds * list[i].tm * list[i].tn / eff;
+        const int64_t tiles = (int64_t)((p.M + wc.c.tm - 1) / wc.c.tm) * ((p.K + wc.c.tn - 1) / wc.c.tn);
+        const int64_t slots = (int64_t)num_cu * wc.per_cu;
+        const int64_t rounds = (tiles + slots - 1) / slots;
+        double cost = (double)rounds * wc.ns;
+        if (wc.kind == WgKind::SPLIT && !unit_q) cost *= kSplitStridedPenalty;
         if (!found || cost < best) {
             best = cost;
-            pl.cand = list[i];
+            pl.cand = wc.c;
             found = true;
         }
     }
@@ -1449,8 +1459,9 @@ mic_status mic_conv_backward_filter(mic_handle handle, double alpha, mic_tensor_
     if (!handle) return MIC_STATUS_BAD_PARAM;
     Plan pl = make_wgrad_plan(handle, x_desc, x, dy_desc, dy, conv, dw_desc, dw, alpha, beta, true);
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
-    const hipError_t err = is_wgh(pl.cand.v) ? miconv::launch_bwd_filter_halo(pl.cand.v, pl.p, handle->stream)
-                                             : miconv::launch_bwd_filter(pl.cand.v, pl.p, handle->stream);
+    const hipError_t err = is_wgh(pl.cand.v)   ? miconv::launch_bwd_filter_halo(pl.cand.v, pl.p, handle->stream)
+                           : is_wgs(pl.cand.v) ? miconv::launch_bwd_filter_split(pl.cand.v, pl.p, handle->stream)
+                                               : miconv::launch_bwd_filter(pl.cand.v, pl.p, handle->stream);
     return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
 }
 

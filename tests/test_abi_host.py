@@ -12,6 +12,7 @@ import pytest
 import convolution_forward_conv2d_amd as mic
 import oracle
 from gen import workloads
+from gen.workloads import Layer
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "convolution_forward_conv2d_amd", "csrc")
@@ -319,21 +320,41 @@ def _wgrad_name(lay, dts=None):
 
 
 def test_wgrad_kernel_choice_host_only():
-    """Stride-1 3x3 / 5x5 fp32 and 3x3 fp64 layers whose rows fit the halo pitch take the halo
-    kernel; the rest (strided, other filters, bf16) the gather kernel."""
-    want_halo = {"alexnet_conv2": "wgh_f32_5x5_w36_64x64", "alexnet_conv3": "wgh_f32_3x3_64x64",
-                 "alexnet_conv4": "wgh_f32_3x3_64x64", "alexnet_conv5": "wgh_f32_3x3_64x64",
-                 "overfeat_l2": "wgh_f32_5x5_w24_64x64", "overfeat_l3": "wgh_f32_3x3_64x64",
-                 "overfeat_l4": "wgh_f32_3x3_64x64", "overfeat_l5": "wgh_f32_3x3_64x64",
-                 "tiny": "wgh_f32_3x3_64x64"}
+    """The plan's cost model (rounds of tiles x measured time per tile) on the workload layers:
+    the halo kernel for stride-1 3x3 layers with enough 64x64 tiles, the split-reduction kernel
+    where dw has few tiles (first layers) or where its finer tiles round better (AlexNet conv2,
+    Overfeat L3), the gather kernel for bf16."""
+    want = {"tiny": "wgs_f32_16x16",
+            "alexnet_conv2": "wgs_f32_16x16", "alexnet_conv3": "wgh_f32_3x3_64x64",
+            "alexnet_conv4": "wgh_f32_3x3_64x64", "alexnet_conv5": "wgh_f32_3x3_64x64",
+            "overfeat_l1": "wgs_f32_16x16", "overfeat_l2": "wgh_f32_5x5_w24_64x64",
+            "overfeat_l3": "wgs_f32_32x32", "overfeat_l4": "wgh_f32_3x3_64x64",
+            "overfeat_l5": "wgh_f32_3x3_64x64",
+            "speech_l1": "wgs_f32_16x16", "speech_l2": "wgs_f32_32x32"}
     for lay in workloads.ALL_LAYERS:
         name = _wgrad_name(lay)
-        if lay.name in want_halo:
-            assert name == want_halo[lay.name], (lay.name, name)
+        if lay.name in want:
+            assert name == want[lay.name], (lay.name, name)
         elif lay.dtype == "f64":
             assert name == "wgh_f64_3x3_64x64", (lay.name, name)
         else:
             assert name.startswith("wg_%s_" % lay.dtype), (lay.name, name)
+
+
+def test_wgrad_split_kernel_needs_small_tensors(monkeypatch):
+    """The split-reduction kernel addresses x and dy with 32-bit byte offsets: forced onto a
+    tensor of 2 GiB or more it answers NOT_SUPPORTED, and the plan never picks it there."""
+    lay = workloads.TINY[0]
+    monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", "wgs_f32_16x16")
+    assert _wgrad_name(lay) == "wgs_f32_16x16"
+    # dy: 4 filters x 16384 x 8192 fp32 = 2 GiB (x: 512 MiB)
+    big = Layer("big", 9, 1, 1, 1, 1 << 14, 1 << 13, 4, 3, 3, (1, 1), (1, 1, 1, 1), "f32",
+                workloads.U11, workloads.U11)
+    with pytest.raises(mic.MicError) as e:
+        _wgrad_name(big)
+    assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+    monkeypatch.delenv("MIC_FORCE_WGRAD_VARIANT")
+    assert not _wgrad_name(big).startswith("wgs_")
 
 
 def test_wgrad_shape_and_type_errors(monkeypatch):

@@ -32,8 +32,8 @@ pytestmark = pytest.mark.gpu
 
 WG_VARIANTS = {
     "f32": ["wg_f32_128x128", "wg_f32_64x128", "wg_f32_128x64", "wg_f32_64x64", "wgh_f32_3x3_64x64",
-            "wgh_f32_5x5_w24_64x64", "wgh_f32_5x5_w36_64x64"],
-    "f64": ["wg_f64_128x64", "wg_f64_64x64", "wgh_f64_3x3_64x64"],
+            "wgh_f32_5x5_w24_64x64", "wgh_f32_5x5_w36_64x64", "wgs_f32_32x32", "wgs_f32_16x16"],
+    "f64": ["wg_f64_128x64", "wg_f64_64x64", "wgh_f64_3x3_64x64", "wgs_f64_32x32", "wgs_f64_16x16"],
     "bf16": ["wg_bf16_128x128", "wg_bf16_64x64"],
 }
 # the halo variants (wgh_) take stride-1 layers of their filter size whose rows fit their pitch; the
@@ -66,8 +66,16 @@ def _out(lay, fill=float("nan")):
     return torch.full(lay.w_shape, fill, dtype=H.OUT_DT[lay.dtype], device=H.dev())
 
 
+# a speech-like layer: one channel, 21x11 filters, stride (2, 1), asymmetric padding; its
+# N*P*Q = 2520 positions run through ten chunks of the split-reduction kernels, and dw
+# (32 x 231) is ragged against their 16- and 32-column tiles
+WG_SHAPES = SMALL_SHAPES + [
+    dict(name="speech_like", N=2, C=1, Hh=41, Ww=60, K=32, R=21, S=11, stride=(2, 1), pads=(10, 10, 0, 10)),
+]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
-@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: s["name"])
+@pytest.mark.parametrize("shape", WG_SHAPES, ids=lambda s: s["name"])
 def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
     lay = _small(dtype=dtype, **{k: v for k, v in shape.items()})
     x64, _ = H.inputs(lay)
