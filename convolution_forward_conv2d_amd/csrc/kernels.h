@@ -9,6 +9,7 @@ namespace miconv {
 
 enum class Variant : int {
     DIRECT = 0,          // one thread per output, any dtype/layout (plain loop, no MFMA)
+    DG_PHASE,            // data gradient onto 1-4 channels by stride phase (conv_bwd_data_phase.hip)
     MFMA_F32_128x128,
     MFMA_F32_128x64,
     MFMA_F32_256x32,
@@ -109,5 +110,6 @@ hipError_t launch_pool_forward(DType dt, const ConvParams& p, hipStream_t stream
 // Data gradient, plain direct kernel (one thread per dx element); p is laid
 // out as conv_bwd_data.hip describes.
 hipError_t launch_bwd_data_direct(DType dt, const ConvParams& p, hipStream_t stream);
+hipError_t launch_bwd_data_phase(DType dt, const ConvParams& p, hipStream_t stream);
 
 }  // namespace miconv

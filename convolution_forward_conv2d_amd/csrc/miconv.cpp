@@ -142,6 +142,7 @@ const Candidate kBF16[] = {
     {Variant::MFMA_BF16_256x32, 256, 32, "mfma_bf16_256x32"},
 };
 const Candidate kDirect = {Variant::DIRECT, 0, 0, "direct"};
+const Candidate kDgPhase = {Variant::DG_PHASE, 0, 0, "phase"};
 // Filter-gradient kernels: the gather kernel (conv_bwd_filter.hip, any
 // geometry), the LDS-halo kernel (conv_bwd_filter_halo.hip: stride 1, fixed
 // R x S, Q + S - 1 <= the row pitch wph) and the kernel that splits the
@@ -701,11 +702,23 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
     }
     if (pl.cand.v == Variant::DIRECT) {
         // no halo instance: the gather kernel in data-gradient mode (any
-        // stride), laid out as conv_fwd_mfma.hip describes; the direct kernel
-        // (conv_bwd_data.hip) when forced, or onto fewer than 16 channels,
-        // where the gather kernel's tiles would be almost empty (measured on
-        // MI355X: 1 channel 5.2 ms direct vs 36 ms gathered, 3 channels 8 vs 53)
-        const bool direct = forced_dgrad_name ? strcmp(forced_dgrad_name, kDirect.name) == 0 : C < 16;
+        // stride), laid out as conv_fwd_mfma.hip describes; onto fewer than 16
+        // channels, where the gather kernel's tiles would be almost empty
+        // (measured on MI355X: 1 channel 5.2 ms direct vs 36 ms gathered,
+        // 3 channels 8 vs 53), a vector-ALU kernel in the direct layout: the
+        // stride-phase kernel (conv_bwd_data_phase.hip) onto 2-4 channels with
+        // at most 6 column taps per phase and dy under 1 GiB (fp32, fp64),
+        // else the one-thread-per-element kernel (conv_bwd_data.hip).  Onto
+        // one channel the phase kernel's dy window yields too few
+        // multiply-adds per load (measured on MI355X, speech layer 1: 6.6 ms
+        // against 5.2 direct; Overfeat layer 1, 3 channels: 2.1 against 8.2);
+        // it runs there only when forced.
+        const bool phase_ok = C <= 4 && (S + cd->v - 1) / cd->v <= 6 && pl.dt != DType::BF16 &&
+                              extent(*dyd) * (int64_t)dtype_size(dyd->dtype) <= (int64_t(1) << 30);
+        const bool phase = forced_dgrad_name ? strcmp(forced_dgrad_name, kDgPhase.name) == 0 && phase_ok
+                                             : C >= 2 && phase_ok;
+        const bool direct = forced_dgrad_name ? strcmp(forced_dgrad_name, kDirect.name) == 0 || phase
+                                              : C < 16;
         if (!direct) {
             p.C = k;
             p.K = C;
@@ -730,7 +743,8 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
                     if (strcmp(forced_dgrad_name, list[i].name) == 0) pl.cand = list[i];
             }
         } else {
-            // direct kernel layout (conv_bwd_data.hip)
+            // direct kernel layout (conv_bwd_data.hip, conv_bwd_data_phase.hip)
+            if (phase) pl.cand = kDgPhase;
             p.C = C;
             p.H = H;
             p.W = W;
@@ -1432,6 +1446,8 @@ mic_status mic_conv_backward_data(mic_handle handle, double alpha, mic_filter_de
     hipError_t err;
     if (pl.cand.v == Variant::DIRECT)
         err = miconv::launch_bwd_data_direct(pl.dt, pl.p, handle->stream);
+    else if (pl.cand.v == Variant::DG_PHASE)
+        err = miconv::launch_bwd_data_phase(pl.dt, pl.p, handle->stream);
     else if (is_halo(pl.cand.v))
         err = miconv::launch_halo(pl.cand.v, pl.p, true, handle->stream);
     else

@@ -262,12 +262,29 @@ def test_dgrad_kernel_choice_host_only():
         assert names[name].startswith("dgrad_halo_f"), (name, names[name])
     # onto 96 channels: the 96-wide tiles
     assert names["alexnet_conv2"] == "dgrad_halo_f32x16_5x5_128x96"
-    # strided layers and bf16 take the gather kernel in data-gradient mode,
-    # gradients onto 1 or 3 channels the direct kernel
+    # strided layers and bf16 take the gather kernel in data-gradient mode; onto 3 channels
+    # the stride-phase kernel, onto 1 channel the direct kernel
     for name in ("speech_l2", "prec_conv3_bf16_nchw", "prec_conv5_bf16_nhwc"):
         assert names[name].startswith("dgrad_mfma_"), (name, names[name])
-    for name in ("overfeat_l1", "speech_l1"):
-        assert names[name] == "dgrad_direct", (name, names[name])
+    assert names["overfeat_l1"] == "dgrad_phase"
+    assert names["speech_l1"] == "dgrad_direct"
+
+
+def test_dgrad_phase_kernel_limits(monkeypatch):
+    """The stride-phase kernel takes 1-4 output channels and at most 6 column taps per phase,
+    fp32/fp64: forced onto anything else it answers NOT_SUPPORTED."""
+    def lay(C, S, v, dt="f32"):
+        return Layer("ph", 9, 1, 2, C, 20, 24, 8, 5, S, (2, v), (1, 1, 1, 1), dt,
+                     workloads.U11, workloads.U11)
+    monkeypatch.setenv("MIC_FORCE_DGRAD_VARIANT", "phase")
+    for C in (1, 2, 3, 4):
+        assert _dgrad_name(lay(C, 5, 2)) == "dgrad_phase"
+    assert _dgrad_name(lay(3, 12, 2)) == "dgrad_phase"        # 6 column taps
+    assert _dgrad_name(lay(3, 3, 1, "f64")) == "dgrad_phase"
+    for bad in (lay(5, 5, 2), lay(3, 13, 2), lay(3, 5, 2, "bf16")):
+        with pytest.raises(mic.MicError) as e:
+            _dgrad_name(bad)
+        assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
 
 
 def test_dgrad_shape_and_type_errors():

@@ -31,6 +31,10 @@ DG_VARIANTS = {
     "f64": ["direct", "halo_f64_3x3_128x128", "halo_f64_3x3_64x64"],
     "bf16": ["direct"],
 }
+# the stride-phase kernel onto 1-4 channels (fp32, fp64); NOT_SUPPORTED on other shapes
+DG_VARIANTS["f32"] += ["phase"]
+DG_VARIANTS["f64"] += ["phase"]
+_MAY_REFUSE = ("halo_", "phase")
 # the gather kernel in data-gradient mode (any stride)
 DG_VARIANTS["f32"] += ["mfma_f32_128x128", "mfma_f32_128x64", "mfma_f32_64x128", "mfma_f32_256x32"]
 DG_VARIANTS["f64"] += ["mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64"]
@@ -41,6 +45,16 @@ _ran = set()
 # reduction channels) is a multiple of 4
 SHAPES = SMALL_SHAPES + [
     dict(name="dg_halo5_k72", N=2, C=12, Hh=20, Ww=20, K=72, R=5, S=5, stride=(1, 1), pads=(2, 2, 2, 2)),
+    # stride-phase kernel: every channel count 1-4 and both column-tap bounds (<= 3, <= 6),
+    # phases with fewer taps than others, padding rows and columns on every side, and rows
+    # whose last window reaches past Q
+    dict(name="dg_phase_c1_41x11", N=2, C=1, Hh=47, Ww=61, K=8, R=21, S=11, stride=(2, 2),
+         pads=(10, 10, 0, 10)),
+    dict(name="dg_phase_c2", N=3, C=2, Hh=23, Ww=29, K=20, R=7, S=9, stride=(3, 2), pads=(2, 1, 3, 0)),
+    dict(name="dg_phase_c4", N=2, C=4, Hh=19, Ww=17, K=36, R=5, S=5, stride=(2, 2), pads=(1, 1, 1, 1)),
+    dict(name="dg_phase_c3_s4", N=2, C=3, Hh=39, Ww=43, K=24, R=11, S=11, stride=(4, 4), pads=(2, 0, 1, 3)),
+    # filter narrower than the stride: phases with no tap at all leave beta * dx
+    dict(name="dg_phase_c1_narrow", N=2, C=1, Hh=14, Ww=15, K=6, R=2, S=2, stride=(3, 3), pads=(0, 0, 0, 0)),
 ]
 
 
@@ -86,7 +100,7 @@ def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
         try:
             _run(lay, dy, w, dx)
         except mic.MicError as e:
-            if var.startswith("halo_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+            if var.startswith(_MAY_REFUSE) and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
                 continue
             raise
         H.check(dtype, dx.double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (shape["name"], dtype, var))
@@ -145,8 +159,11 @@ def test_workload_layer_integer_exact(lay):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
-def test_alpha_beta(dtype, monkeypatch):
-    lay = _small("dg_ab", 2, 20, 13, 11, 36, 3, 3, (1, 1), (1, 1, 1, 0), dtype)
+@pytest.mark.parametrize("geom", [(20, 3, 3, (1, 1), (1, 1, 1, 0)), (3, 7, 5, (3, 2), (2, 1, 0, 2))],
+                         ids=["c20", "c3_strided"])
+def test_alpha_beta(dtype, geom, monkeypatch):
+    C, R, S, stride, pads = geom
+    lay = _small("dg_ab", 2, C, 13, 11, 36, R, S, stride, pads, dtype)
     _, wi = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
     N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
     dyi = _dy(lay, (N, K, P, Q), integer=True)
@@ -160,7 +177,7 @@ def test_alpha_beta(dtype, monkeypatch):
         try:
             _run(lay, dy, w, dx, alpha=0.5, beta=0.25)
         except mic.MicError as e:
-            if var.startswith("halo_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+            if var.startswith(_MAY_REFUSE) and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
                 continue
             raise
         assert np.array_equal(dx.double().cpu().numpy(), 0.5 * acc + 0.25 * old), var
