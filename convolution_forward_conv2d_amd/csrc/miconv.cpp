@@ -1144,6 +1144,8 @@ Plan make_pool_plan(const mic_pool_desc_st* pd, const mic_tensor_desc_st* xd, co
     p.Kred = (int)pd->mode;    // pool_fwd.hip reads the mode here
     p.div_pq = FastDiv((uint32_t)(P * Q));
     p.div_q = FastDiv((uint32_t)Q);
+    p.div_rs = FastDiv((uint32_t)c);      // pool_fwd.hip: the channel count
+    p.div_s = FastDiv((uint32_t)M);       // and N*P*Q
     p.alpha = alpha;
     p.beta = beta;
     snprintf(pl.name, sizeof(pl.name), "pool_direct");

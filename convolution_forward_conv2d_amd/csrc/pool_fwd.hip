@@ -12,10 +12,15 @@
 // and y written once.  Consecutive threads take consecutive outputs along
 // y's unit stride: along q, or along c for channels-innermost y.
 //
+// Index arithmetic is 32-bit (the plan keeps N*C*P*Q below 2^30) with
+// multiply-shift division.  A 3x3 window (AlexNet's) has an instance with
+// the window unrolled, so its nine loads (clamped to the plane's first
+// element where they fall outside it) issue together; other windows loop.
+//
 // Parameters: x, its strides sx*; y, its strides sy*; N, C, H, W; window
 // R x S; P, Q; u, v; pad_top, pad_left; M = N*P*Q; div_pq, div_q divide by
-// P*Q and Q; Kred = the mode (0 max, 1 average over R*S, 2 average over the
-// positions inside).
+// P*Q and Q, div_rs by C and div_s by M; Kred = the mode (0 max, 1 average
+// over R*S, 2 average over the positions inside).
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -35,37 +40,57 @@ __device__ __forceinline__ float widen_pool(Bf16Pool v) { return __uint_as_float
 
 }  // namespace
 
-template <class In, class Acc, class Out>
+template <class In, class Acc, class Out, int RT, int ST>
 __global__ void __launch_bounds__(256) pool_fwd_kernel(const ConvParams p)
 {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)p.M * p.C) return;
-    int c, m;
-    if (p.syk == 1) {
-        m = (int)(idx / p.C);
-        c = (int)(idx - (int64_t)m * p.C);
-    } else {
-        c = (int)(idx / p.M);
-        m = (int)(idx - (int64_t)c * p.M);
-    }
+    const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
+    if (idx >= (uint32_t)p.M * (uint32_t)p.C) return;
+    // consecutive threads take consecutive outputs along y's unit stride
+    uint32_t c, m;
+    if (p.syk == 1)
+        p.div_rs.divmod(idx, m, c);
+    else
+        p.div_s.divmod(idx, c, m);
     uint32_t n, pq, pp, q;
-    p.div_pq.divmod((uint32_t)m, n, pq);
+    p.div_pq.divmod(m, n, pq);
     p.div_q.divmod(pq, pp, q);
     const int h0 = (int)pp * p.u - p.pad_top;
     const int w0 = (int)q * p.v - p.pad_left;
-    const In* x = static_cast<const In*>(p.x) + (int)n * p.sxn + c * p.sxc;
+    const In* x = static_cast<const In*>(p.x) + (int)n * p.sxn + (int)c * p.sxc;
     Acc best = 0, sum = 0;
     int inside = 0;
-    for (int r = 0; r < p.R; ++r) {
-        const int h = h0 + r;
-        if ((unsigned)h >= (unsigned)p.H) continue;
-        for (int s = 0; s < p.S; ++s) {
-            const int w = w0 + s;
-            if ((unsigned)w >= (unsigned)p.W) continue;
-            const Acc v = widen_pool(x[h * p.sxh + w * p.sxw]);
-            best = (inside == 0 || v > best) ? v : best;
-            sum += v;
-            ++inside;
+    // positions in row order; padding never counts, and max takes the first
+    // inside value, then any larger one
+    auto take = [&](Acc v) {
+        best = (inside == 0 || v > best) ? v : best;
+        sum += v;
+        ++inside;
+    };
+    if constexpr (RT > 0) {
+        Acc vals[RT][ST];
+        bool ok[RT][ST];
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int s = 0; s < ST; ++s) {
+                const int h = h0 + r, w = w0 + s;
+                ok[r][s] = (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
+                vals[r][s] = widen_pool(x[ok[r][s] ? h * p.sxh + w * p.sxw : 0]);
+            }
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int s = 0; s < ST; ++s)
+                if (ok[r][s]) take(vals[r][s]);
+    } else {
+        for (int r = 0; r < p.R; ++r) {
+            const int h = h0 + r;
+            if ((unsigned)h >= (unsigned)p.H) continue;
+            for (int s = 0; s < p.S; ++s) {
+                const int w = w0 + s;
+                if ((unsigned)w >= (unsigned)p.W) continue;
+                take(widen_pool(x[h * p.sxh + w * p.sxw]));
+            }
         }
     }
     Acc acc;
@@ -76,7 +101,7 @@ __global__ void __launch_bounds__(256) pool_fwd_kernel(const ConvParams p)
     else
         acc = inside ? sum / (Acc)inside : Acc(0);
     Out* y = static_cast<Out*>(p.y);
-    const int off = (int)n * p.syn + c * p.syk + (int)pp * p.syp + (int)q * p.syq;
+    const int off = (int)n * p.syn + (int)c * p.syk + (int)pp * p.syp + (int)q * p.syq;
     const Acc alpha = (Acc)p.alpha;
     const Acc beta = (Acc)p.beta;
     Acc val = alpha * acc;
@@ -89,7 +114,10 @@ static hipError_t launch_pool_t(const ConvParams& p, hipStream_t stream)
 {
     const int64_t total = (int64_t)p.M * p.C;
     const dim3 grid((unsigned)((total + 255) / 256));
-    hipLaunchKernelGGL((pool_fwd_kernel<In, Acc, Out>), grid, dim3(256), 0, stream, p);
+    if (p.R == 3 && p.S == 3)
+        hipLaunchKernelGGL((pool_fwd_kernel<In, Acc, Out, 3, 3>), grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((pool_fwd_kernel<In, Acc, Out, 0, 0>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
