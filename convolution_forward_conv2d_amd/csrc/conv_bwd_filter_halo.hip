@@ -318,6 +318,9 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     X(WGH_F32_3x3_W16, PolF32, 64, 64, 2, 2, 3, 3, 16, 13, 243, 2)       \
     X(WGH_F32_5x5_W24, PolF32, 64, 64, 2, 2, 5, 5, 24, 7, 269, 2)        \
     X(WGH_F32_5x5_W36, PolF32, 64, 64, 2, 2, 5, 5, 36, 7, 401, 2)        \
+    X(WGH_F32_3x3_W16_64x96, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 13, 247, 2) \
+    X(WGH_F32X16_3x3_W16, PolF32x16, 64, 64, 2, 2, 3, 3, 16, 13, 247, 2)     \
+    X(WGH_F32X16_5x5_W24, PolF32x16, 64, 64, 2, 2, 5, 5, 24, 7, 269, 2)      \
     X(WGH_F64_3x3_W16, PolF64, 64, 64, 2, 2, 3, 3, 16, 7, 147, 2)
 
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream)

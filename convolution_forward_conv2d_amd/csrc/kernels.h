@@ -47,6 +47,9 @@ enum class Variant : int {
     WGH_F32_3x3_W16,        // filter gradient, stride 1, halo in LDS (conv_bwd_filter_halo.hip)
     WGH_F32_5x5_W24,
     WGH_F32_5x5_W36,
+    WGH_F32_3x3_W16_64x96,
+    WGH_F32X16_3x3_W16,
+    WGH_F32X16_5x5_W24,
     WGH_F64_3x3_W16,
     WGS_F32_32x32,          // filter gradient, reduction split over waves (conv_bwd_filter_split.hip)
     WGS_F32_16x16,
