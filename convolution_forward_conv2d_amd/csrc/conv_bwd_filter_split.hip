@@ -82,6 +82,10 @@ __device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, int voff, in
 {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
+__device__ __forceinline__ uint16_t buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint16_t)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
 __device__ __forceinline__ double buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, double)
 {
     typedef unsigned int u32x2_t __attribute__((__vector_size__(2 * sizeof(unsigned int))));
@@ -104,11 +108,12 @@ conv_bwd_filter_split_kernel(const ConvParams p)
     constexpr int FN = TN / BM;
     constexpr int SEG = 64 / Pol::G;            // positions per lane per segment
     constexpr int FRAG_VECS = SEG * ES / 16;
+    constexpr int STEPS = SEG / Pol::V;         // MFMA steps per segment
     constexpr int PITCH = 64 * ES + 16;         // one 64-position row, padded
     constexpr int WAVE_BYTES = (TM + TN) * PITCH;
     constexpr int RED_BYTES = (NW - 1) * FM * FN * Pol::NACC * 64 * (int)sizeof(Acc);
     constexpr int SMEM = NW * WAVE_BYTES > RED_BYTES ? NW * WAVE_BYTES : RED_BYTES;
-    static_assert(Pol::V == 1, "one element per lane and MFMA step");
+    static_assert(SEG % Pol::V == 0, "whole MFMA steps per segment");
     static_assert(TM % BM == 0 && TN % BM == 0, "tile must hold whole MFMA blocks");
     static_assert(SEG * ES % 16 == 0, "lane slice must be whole 16-byte vectors");
     static_assert(NSLOT == 1 || NSLOT == 2, "one or two register slots");
@@ -214,12 +219,16 @@ conv_bwd_filter_split_kernel(const ConvParams p)
     };
     auto mfma_seg = [&]() {
 #pragma unroll
-        for (int t = 0; t < SEG; ++t) {
+        for (int t = 0; t < STEPS; ++t) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = Pol::mfma_s(frag_elem(fa[i], t, In{}), frag_elem(fb[j], t, In{}), acc[i][j]);
+                for (int j = 0; j < FN; ++j) {
+                    if constexpr (Pol::V == 1)
+                        acc[i][j] = Pol::mfma_s(frag_elem(fa[i], t, In{}), frag_elem(fb[j], t, In{}), acc[i][j]);
+                    else   // V consecutive positions per lane: one 16-byte fragment vector
+                        acc[i][j] = Pol::mfma(fa[i], fb[j], t, acc[i][j]);
+                }
         }
     };
 
@@ -308,7 +317,8 @@ static hipError_t launch_wgs_variant(const ConvParams& p0, hipStream_t stream)
     X(WGS_F32_32x32, PolF32, 32, 32, 8, 1)             \
     X(WGS_F32_16x16, PolF32x16, 16, 16, 8, 2)          \
     X(WGS_F64_32x32, PolF64, 32, 32, 4, 1)             \
-    X(WGS_F64_16x16, PolF64, 16, 16, 8, 2)
+    X(WGS_F64_16x16, PolF64, 16, 16, 8, 2)             \
+    X(WGS_BF16_32x32, PolBF16, 32, 32, 8, 1)
 
 hipError_t launch_bwd_filter_split(Variant v, const ConvParams& p, hipStream_t stream)
 {

@@ -55,6 +55,7 @@ enum class Variant : int {
     WGS_F32_16x16,
     WGS_F64_32x32,
     WGS_F64_16x16,
+    WGS_BF16_32x32,
     BR_F32_128x128,         // batch-reduce GEMM, shared-LDS tiles (brgemm.hip)
     BR_F32_64x64,
     BR_F32_32x64,

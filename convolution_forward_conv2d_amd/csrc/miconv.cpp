@@ -166,8 +166,8 @@ const WgCandidate kWg[] = {
     {{Variant::WG_F32_64x64, 64, 64, "wg_f32_64x64"}, DType::F32, WgKind::GATHER, 0, 0, 0, 60.0, 1},
     {{Variant::WG_F64_128x64, 128, 64, "wg_f64_128x64"}, DType::F64, WgKind::GATHER, 0, 0, 0, 157.0, 1},
     {{Variant::WG_F64_64x64, 64, 64, "wg_f64_64x64"}, DType::F64, WgKind::GATHER, 0, 0, 0, 93.0, 1},
-    {{Variant::WG_BF16_128x128, 128, 128, "wg_bf16_128x128"}, DType::BF16, WgKind::GATHER, 0, 0, 0, 100.0, 1},
-    {{Variant::WG_BF16_64x64, 64, 64, "wg_bf16_64x64"}, DType::BF16, WgKind::GATHER, 0, 0, 0, 37.0, 1},
+    {{Variant::WG_BF16_128x128, 128, 128, "wg_bf16_128x128"}, DType::BF16, WgKind::GATHER, 0, 0, 0, 190.0, 1},
+    {{Variant::WG_BF16_64x64, 64, 64, "wg_bf16_64x64"}, DType::BF16, WgKind::GATHER, 0, 0, 0, 75.0, 1},
     {{Variant::WGH_F32_3x3_W16, 64, 64, "wgh_f32_3x3_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 34.0, 1},
     {{Variant::WGH_F32_5x5_W24, 64, 64, "wgh_f32_5x5_w24_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 32.0, 1},
     {{Variant::WGH_F32_5x5_W36, 64, 64, "wgh_f32_5x5_w36_64x64"}, DType::F32, WgKind::HALO, 5, 5, 36, 39.0, 1},
@@ -179,6 +179,7 @@ const WgCandidate kWg[] = {
     {{Variant::WGS_F32_16x16, 16, 16, "wgs_f32_16x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 7.1, 2},
     {{Variant::WGS_F64_32x32, 32, 32, "wgs_f64_32x32"}, DType::F64, WgKind::SPLIT, 0, 0, 0, 28.0, 1},
     {{Variant::WGS_F64_16x16, 16, 16, "wgs_f64_16x16"}, DType::F64, WgKind::SPLIT, 0, 0, 0, 5.7, 1},
+    {{Variant::WGS_BF16_32x32, 32, 32, "wgs_bf16_32x32"}, DType::BF16, WgKind::SPLIT, 0, 0, 0, 15.8, 2},
 };
 // the split kernel's loads run along the positions: with x or dy strided
 // along q (channels-last) they gather (measured 2.6x slower)
@@ -194,7 +195,7 @@ bool is_wgh(Variant v)
 bool is_wgs(Variant v)
 {
     return v == Variant::WGS_F32_32x32 || v == Variant::WGS_F32_16x16 || v == Variant::WGS_F64_32x32 ||
-           v == Variant::WGS_F64_16x16;
+           v == Variant::WGS_F64_16x16 || v == Variant::WGS_BF16_32x32;
 }
 
 // batch-reduce GEMM (brgemm.hip): shared-LDS tiles for large products

@@ -340,8 +340,8 @@ def test_wgrad_kernel_choice_host_only():
     """The plan's cost model (rounds of tiles x measured time per tile) on the workload layers:
     the halo kernel for the stride-1 3x3 and 5x5 (pitch 24) layers, with 64x96 tiles where they
     save a round (AlexNet conv4, Overfeat L3-L5), the split-reduction kernel where dw has few
-    tiles (first layers) or where its finer tiles round better (AlexNet conv2), the gather kernel
-    for bf16."""
+    tiles (first layers) or where its finer tiles round better (AlexNet conv2, the bf16 layers),
+    the gather kernel for channels-last bf16."""
     want = {"tiny": "wgs_f32_16x16",
             "alexnet_conv2": "wgs_f32_16x16", "alexnet_conv3": "wgh_f32x16_3x3_64x64",
             "alexnet_conv4": "wgh_f32_3x3_64x96", "alexnet_conv5": "wgh_f32x16_3x3_64x64",
@@ -355,8 +355,11 @@ def test_wgrad_kernel_choice_host_only():
             assert name == want[lay.name], (lay.name, name)
         elif lay.dtype == "f64":
             assert name == "wgh_f64_3x3_64x64", (lay.name, name)
-        else:
+        elif lay.name.endswith("nhwc"):
+            # channels-last: the split kernel's position-ordered loads would gather
             assert name.startswith("wg_%s_" % lay.dtype), (lay.name, name)
+        else:
+            assert name == "wgs_bf16_32x32", (lay.name, name)
 
 
 def test_wgrad_split_kernel_needs_small_tensors(monkeypatch):

@@ -35,7 +35,7 @@ WG_VARIANTS = {
             "wgh_f32_5x5_w24_64x64", "wgh_f32_5x5_w36_64x64", "wgh_f32_3x3_64x96", "wgh_f32x16_3x3_64x64",
             "wgh_f32x16_5x5_w24_64x64", "wgs_f32_32x32", "wgs_f32_16x16"],
     "f64": ["wg_f64_128x64", "wg_f64_64x64", "wgh_f64_3x3_64x64", "wgs_f64_32x32", "wgs_f64_16x16"],
-    "bf16": ["wg_bf16_128x128", "wg_bf16_64x64"],
+    "bf16": ["wg_bf16_128x128", "wg_bf16_64x64", "wgs_bf16_32x32"],
 }
 # the halo variants (wgh_) take stride-1 layers of their filter size whose rows fit their pitch; the
 # library answers NOT_SUPPORTED for other shapes, and every variant must run on at least one shape
