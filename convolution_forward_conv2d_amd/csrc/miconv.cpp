@@ -182,8 +182,9 @@ const WgCandidate kWg[] = {
     {{Variant::WGS_BF16_32x32, 32, 32, "wgs_bf16_32x32"}, DType::BF16, WgKind::SPLIT, 0, 0, 0, 15.8, 2},
 };
 // the split kernel's loads run along the positions: with x or dy strided
-// along q (channels-last) they gather (measured 2.6x slower)
-constexpr double kSplitStridedPenalty = 2.6;
+// along q (channels-last) they gather (measured 2.6x slower for fp64,
+// 4.1-4.6x for bf16, whose 2-byte gathers use less of each cache line)
+double split_strided_penalty(DType dt) { return dt == DType::BF16 ? 4.5 : 2.6; }
 
 bool is_wgh(Variant v)
 {
@@ -896,7 +897,7 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
         const int64_t slots = (int64_t)num_cu * wc.per_cu;
         const int64_t rounds = (tiles + slots - 1) / slots;
         double cost = (double)rounds * wc.ns;
-        if (wc.kind == WgKind::SPLIT && !unit_q) cost *= kSplitStridedPenalty;
+        if (wc.kind == WgKind::SPLIT && !unit_q) cost *= split_strided_penalty(pl.dt);
         if (!found || cost < best) {
             best = cost;
             pl.cand = wc.c;
