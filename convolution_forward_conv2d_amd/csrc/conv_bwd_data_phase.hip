@@ -166,6 +166,202 @@ __global__ void __launch_bounds__(256) conv_bwd_data_phase_kernel(const ConvPara
     }
 }
 
+// Row-staged form of the same phase decomposition, for one to four
+// channels under a tall filter (speech layer 1: 41 x 11, stride 2, onto one
+// channel), where per-lane windows from global memory would touch many
+// cache lines per load.  A workgroup takes one image, one phase pair and a
+// band of HB output rows of that phase; for each filter k it stages the dy
+// rows and columns the band reaches -- HB + nr - 1 rows of wph + NSM - 1
+// values, zero outside dy -- in LDS with coalesced loads, double-buffered:
+// filter k + 1's values are loaded into registers before filter k is
+// computed and stored to the other buffer after it.  A lane owns WT
+// consecutive phase columns of one row (the host checks that 256 / HB lanes
+// cover a row) and reads its window from LDS with 16-byte reads; window
+// values past the staged row feed only columns that are not stored, and
+// the allocation has room for them.  Filter values are the workgroup's and
+// come in as scalars, as above.
+template <int CT, int NSM, int WT, int HB, int PER>
+__global__ void __launch_bounds__(256) conv_bwd_data_rows_kernel(const ConvParams p, int buf_elems)
+{
+    constexpr int NT = 256;
+    constexpr int TPR = NT / HB;                       // lanes per output row
+    constexpr int NWIN = WT + NSM - 1;
+    constexpr int NWV = (NWIN + 3) / 4;                // 16-byte window reads
+    static_assert(WT % 4 == 0 && NT % HB == 0, "lane shapes");
+    const int u = p.u, v = p.v;
+    const int a = (int)blockIdx.y / v;
+    const int b = (int)blockIdx.y - a * v;
+    const int h0 = phase_first(a, p.pad_top, u);
+    const int w0 = phase_first(b, p.pad_left, v);
+    const int hph = h0 < p.H ? (p.H - h0 + u - 1) / u : 0;
+    const int wph = w0 < p.W ? (p.W - w0 + v - 1) / v : 0;
+    const int nbands = (hph + HB - 1) / HB;
+    if ((int)blockIdx.x >= p.N * nbands) return;      // whole workgroup: the grid covers the largest phase
+    const int n = (int)blockIdx.x / nbands;
+    const int band = (int)blockIdx.x - n * nbands;
+    const int ns = b < p.S ? (p.S - b + v - 1) / v : 0;
+    const int nr = a < p.R && ns > 0 ? (p.R - a + u - 1) / u : 0;
+
+    // output row h' = band*HB + hr reads dy rows P0(h') - i, P0(h') = P0f + h';
+    // staged row sr holds dy row prow0 + sr, staged column sc dy column qcol0 + sc
+    const int P0f = (h0 + p.pad_top - a) / u;
+    const int Q0f = (w0 + p.pad_left - b) / v;
+    const int hq0 = band * HB;
+    const int nrr = nr > 0 ? nr : 1;
+    const int prow0 = P0f + hq0 - (nrr - 1);
+    const int qcol0 = Q0f - (NSM - 1);
+    const int srows = HB + nrr - 1;
+    const int scols = wph + NSM - 1;
+    const int pitch = (scols + 3) & ~3;
+    const int selems = srows * pitch;                  // <= buf_elems (host-sized for every phase)
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char dsm[];
+    float* const stage = reinterpret_cast<float*>(dsm);
+
+    const float* __restrict__ dy = static_cast<const float*>(p.x);
+    const float* __restrict__ f = static_cast<const float*>(p.w);
+    const int tid = threadIdx.x;
+    const int hr = tid / TPR;
+    const int wq = (tid - hr * TPR) * WT;              // first phase column of the lane
+
+    // staging: element e = tid + 256*i of the band's window, column fastest;
+    // loads unconditional at a valid address, zeros chosen at the store
+    int soff[PER];
+    uint64_t sok = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = tid + NT * i;
+        const int r = e / pitch;
+        const int c = e - r * pitch;
+        const int pr = prow0 + r;
+        const int qc = qcol0 + c;
+        const bool ok = e < selems && c < scols && (unsigned)pr < (unsigned)p.P && (unsigned)qc < (unsigned)p.Q;
+        soff[i] = ok ? n * p.sxn + pr * p.sxh + qc * p.sxw : 0;
+        sok |= (uint64_t)(ok ? 1u : 0u) << i;
+    }
+    float sval[PER];
+    auto stage_load = [&](int k) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) sval[i] = dy[soff[i] + k * p.sxc];
+    };
+    auto stage_store = [&](int buf) {
+        float* dst = stage + buf * buf_elems;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + NT * i;
+            if (e < selems) dst[e] = (sok >> i) & 1 ? sval[i] : 0.0f;
+        }
+    };
+
+    float acc[CT][WT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int j = 0; j < WT; ++j) acc[c][j] = 0.0f;
+
+    const int rs = p.R * p.S;
+    if (nr > 0) {
+        stage_load(0);
+        stage_store(0);
+        __syncthreads();
+        for (int k = 0; k < p.K; ++k) {
+            const int cur = k & 1;
+            stage_load(k + 1 < p.K ? k + 1 : k);
+            const float* src = stage + cur * buf_elems;
+            if (wq < wph) {
+                for (int i = 0; i < nr; ++i) {
+                    const float* row = src + (hr + (nr - 1) - i) * pitch + wq;
+                    float win[NWV * 4];
+#pragma unroll
+                    for (int vv = 0; vv < NWV; ++vv) {
+                        const float4 q4 = *reinterpret_cast<const float4*>(row + 4 * vv);
+                        win[4 * vv] = q4.x;
+                        win[4 * vv + 1] = q4.y;
+                        win[4 * vv + 2] = q4.z;
+                        win[4 * vv + 3] = q4.w;
+                    }
+                    const float* fk = f + (k * p.C) * rs + (a + i * u) * p.S + b;
+                    float fv[CT][NSM];
+#pragma unroll
+                    for (int c = 0; c < CT; ++c)
+#pragma unroll
+                        for (int t = 0; t < NSM; ++t) {
+                            const float fval = fk[c * rs + min(t, ns - 1) * v];
+                            fv[c][t] = t < ns ? fval : 0.0f;
+                        }
+#pragma unroll
+                    for (int c = 0; c < CT; ++c)
+#pragma unroll
+                        for (int j = 0; j < WT; ++j)
+#pragma unroll
+                            for (int t = 0; t < NSM; ++t) acc[c][j] += win[NSM - 1 + j - t] * fv[c][t];
+                }
+            }
+            stage_store(cur ^ 1);
+            __syncthreads();
+        }
+    }
+
+    if (hq0 + hr >= hph) return;
+    const int h = h0 + u * (hq0 + hr);
+    float* __restrict__ dx = static_cast<float*>(p.y);
+    const float alpha = (float)p.alpha;
+    const float beta = (float)p.beta;
+#pragma unroll
+    for (int j = 0; j < WT; ++j) {
+        if (wq + j >= wph) break;
+        const int w = w0 + v * (wq + j);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            if (c >= p.C) break;
+            const int off = n * p.syn + c * p.syk + h * p.syp + w * p.syq;
+            float val = alpha * acc[c][j];
+            if (beta != 0.0f) val += beta * dx[off];
+            dx[off] = val;
+        }
+    }
+}
+
+// Row-staged instance onto one channel: 8-row bands, 12 columns per lane
+// (so 32 lanes cover 384 phase columns), up to 6 column taps per phase.
+constexpr int kRowsHB = 8, kRowsWT = 12, kRowsNSM = 6, kRowsPER = 48;
+
+bool bwd_data_rows_fits(const ConvParams& p, size_t* lds_bytes)
+{
+    if (p.C != 1 || (p.S + p.v - 1) / p.v > kRowsNSM) return false;
+    const int wph = (p.W + p.v - 1) / p.v;
+    if (wph > (256 / kRowsHB) * kRowsWT) return false;
+    const int nrmax = (p.R + p.u - 1) / p.u;
+    const int pitch = (wph + kRowsNSM - 1 + 3) & ~3;
+    const int64_t elems = (int64_t)(kRowsHB + nrmax - 1) * pitch;
+    if (elems > 256 * kRowsPER) return false;
+    // two buffers, and room for the last lane's window past the last row
+    const int64_t bytes = (2 * elems + 16) * 4;
+    if (bytes > 160 * 1024) return false;
+    if (lds_bytes) *lds_bytes = (size_t)bytes;
+    return true;
+}
+
+hipError_t launch_bwd_data_rows(const ConvParams& p, hipStream_t stream)
+{
+    size_t lds = 0;
+    if (!bwd_data_rows_fits(p, &lds)) return hipErrorInvalidValue;
+    const int wph = (p.W + p.v - 1) / p.v;
+    const int nrmax = (p.R + p.u - 1) / p.u;
+    const int pitch = (wph + kRowsNSM - 1 + 3) & ~3;
+    const int buf_elems = (kRowsHB + nrmax - 1) * pitch;
+    const int hph = (p.H + p.u - 1) / p.u;
+    const dim3 grid((unsigned)(p.N * ((hph + kRowsHB - 1) / kRowsHB)), (unsigned)(p.u * p.v));
+    auto kern = conv_bwd_data_rows_kernel<1, kRowsNSM, kRowsWT, kRowsHB, kRowsPER>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, p, buf_elems);
+    return hipGetLastError();
+}
+
 template <class T, int CT, int NSM, int WT>
 static hipError_t launch_phase_t(const ConvParams& p, hipStream_t stream)
 {

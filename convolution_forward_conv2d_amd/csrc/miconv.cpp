@@ -143,6 +143,7 @@ const Candidate kBF16[] = {
 };
 const Candidate kDirect = {Variant::DIRECT, 0, 0, "direct"};
 const Candidate kDgPhase = {Variant::DG_PHASE, 0, 0, "phase"};
+const Candidate kDgRows = {Variant::DG_ROWS, 0, 0, "rows"};
 // Filter-gradient kernels: the gather kernel (conv_bwd_filter.hip, any
 // geometry), the LDS-halo kernel (conv_bwd_filter_halo.hip: stride 1, fixed
 // R x S, Q + S - 1 <= the row pitch wph) and the kernel that splits the
@@ -723,7 +724,22 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
                               extent(*dyd) * (int64_t)dtype_size(dyd->dtype) <= (int64_t(1) << 30);
         const bool phase = forced_dgrad_name ? strcmp(forced_dgrad_name, kDgPhase.name) == 0 && phase_ok
                                              : C >= 2 && phase_ok;
-        const bool direct = forced_dgrad_name ? strcmp(forced_dgrad_name, kDirect.name) == 0 || phase
+        // onto one channel (fp32): the row-staged form of the phase kernel
+        // when its staged window fits (speech layer 1: 5.2 ms direct)
+        bool rows_ok = false;
+        if (C == 1 && pl.dt == DType::F32) {
+            ConvParams q = p;
+            q.C = C;
+            q.H = H;
+            q.W = W;
+            q.R = R;
+            q.S = S;
+            q.u = cd->u;
+            q.v = cd->v;
+            rows_ok = miconv::bwd_data_rows_fits(q, nullptr);
+        }
+        const bool rows = forced_dgrad_name ? strcmp(forced_dgrad_name, kDgRows.name) == 0 && rows_ok : rows_ok;
+        const bool direct = forced_dgrad_name ? strcmp(forced_dgrad_name, kDirect.name) == 0 || phase || rows
                                               : C < 16;
         if (!direct) {
             p.C = k;
@@ -751,6 +767,7 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
         } else {
             // direct kernel layout (conv_bwd_data.hip, conv_bwd_data_phase.hip)
             if (phase) pl.cand = kDgPhase;
+            if (rows) pl.cand = kDgRows;
             p.C = C;
             p.H = H;
             p.W = W;
@@ -1456,6 +1473,8 @@ mic_status mic_conv_backward_data(mic_handle handle, double alpha, mic_filter_de
         err = miconv::launch_bwd_data_direct(pl.dt, pl.p, handle->stream);
     else if (pl.cand.v == Variant::DG_PHASE)
         err = miconv::launch_bwd_data_phase(pl.dt, pl.p, handle->stream);
+    else if (pl.cand.v == Variant::DG_ROWS)
+        err = miconv::launch_bwd_data_rows(pl.p, handle->stream);
     else if (is_halo(pl.cand.v))
         err = miconv::launch_halo(pl.cand.v, pl.p, true, handle->stream);
     else

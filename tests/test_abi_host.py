@@ -263,11 +263,11 @@ def test_dgrad_kernel_choice_host_only():
     # onto 96 channels: the 96-wide tiles
     assert names["alexnet_conv2"] == "dgrad_halo_f32x16_5x5_128x96"
     # strided layers and bf16 take the gather kernel in data-gradient mode; onto 3 channels
-    # the stride-phase kernel, onto 1 channel the direct kernel
+    # the stride-phase kernel, onto 1 channel its row-staged form
     for name in ("speech_l2", "prec_conv3_bf16_nchw", "prec_conv5_bf16_nhwc"):
         assert names[name].startswith("dgrad_mfma_"), (name, names[name])
     assert names["overfeat_l1"] == "dgrad_phase"
-    assert names["speech_l1"] == "dgrad_direct"
+    assert names["speech_l1"] == "dgrad_rows"
 
 
 def test_dgrad_phase_kernel_limits(monkeypatch):

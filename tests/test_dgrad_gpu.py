@@ -34,7 +34,9 @@ DG_VARIANTS = {
 # the stride-phase kernel onto 1-4 channels (fp32, fp64); NOT_SUPPORTED on other shapes
 DG_VARIANTS["f32"] += ["phase"]
 DG_VARIANTS["f64"] += ["phase"]
-_MAY_REFUSE = ("halo_", "phase")
+# its row-staged form onto one channel (fp32); NOT_SUPPORTED on other shapes
+DG_VARIANTS["f32"] += ["rows"]
+_MAY_REFUSE = ("halo_", "phase", "rows")
 # the gather kernel in data-gradient mode (any stride)
 DG_VARIANTS["f32"] += ["mfma_f32_128x128", "mfma_f32_128x64", "mfma_f32_64x128", "mfma_f32_256x32"]
 DG_VARIANTS["f64"] += ["mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64"]
