@@ -95,10 +95,13 @@ __device__ __forceinline__ double buf_load(__amdgpu_buffer_rsrc_t r, int voff, i
 
 }  // namespace
 
-template <class Pol, int TM, int TN, int NW, int NSLOT>
+template <class Pol, int TM, int TN, int NW, int NSLOT, int TMV>
 __global__ void __launch_bounds__(64 * NW)
 conv_bwd_filter_split_kernel(const ConvParams p)
 {
+    // TMV <= TM filters per tile are loaded and stored; with TMV < TM the
+    // MFMA block's other rows read the B rows that follow in LDS and their
+    // results are dropped (8-filter tiles: twice the tiles of a 16-row block)
     using In = typename Pol::In;
     using Acc = typename Pol::Acc;
     using AccV = typename Pol::AccV;
@@ -110,11 +113,12 @@ conv_bwd_filter_split_kernel(const ConvParams p)
     constexpr int FRAG_VECS = SEG * ES / 16;
     constexpr int STEPS = SEG / Pol::V;         // MFMA steps per segment
     constexpr int PITCH = 64 * ES + 16;         // one 64-position row, padded
-    constexpr int WAVE_BYTES = (TM + TN) * PITCH;
+    constexpr int WAVE_BYTES = (TMV + TN) * PITCH;
     constexpr int RED_BYTES = (NW - 1) * FM * FN * Pol::NACC * 64 * (int)sizeof(Acc);
     constexpr int SMEM = NW * WAVE_BYTES > RED_BYTES ? NW * WAVE_BYTES : RED_BYTES;
     static_assert(SEG % Pol::V == 0, "whole MFMA steps per segment");
     static_assert(TM % BM == 0 && TN % BM == 0, "tile must hold whole MFMA blocks");
+    static_assert(TMV <= TM && (TMV == TM || TMV + TN >= TM), "valid rows; the block's other rows stay in LDS");
     static_assert(SEG * ES % 16 == 0, "lane slice must be whole 16-byte vectors");
     static_assert(NSLOT == 1 || NSLOT == 2, "one or two register slots");
     static_assert(BM * (BM + 1) * (int)sizeof(Acc) <= SMEM, "epilogue stage fits");
@@ -128,7 +132,7 @@ conv_bwd_filter_split_kernel(const ConvParams p)
     const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
-    const int m0 = mt * TM;
+    const int m0 = mt * TMV;
     const int n0 = nt * TN;
     const int L = p.Kred;
 
@@ -140,9 +144,9 @@ conv_bwd_filter_split_kernel(const ConvParams p)
     // (c, r, s) and its tap.  Rows past the tile's edge are clamped to the
     // last: they feed only rows and columns of the MFMA block that are never
     // stored.
-    int a_off[TM];
+    int a_off[TMV];
 #pragma unroll
-    for (int e = 0; e < TM; ++e) a_off[e] = min(m0 + e, p.M - 1) * p.sdk * ES;
+    for (int e = 0; e < TMV; ++e) a_off[e] = min(m0 + e, p.M - 1) * p.sdk * ES;
     int b_off[TN], b_r[TN], b_s[TN];
 #pragma unroll
     for (int e = 0; e < TN; ++e) {
@@ -156,7 +160,7 @@ conv_bwd_filter_split_kernel(const ConvParams p)
     }
 
     struct Slot {
-        In a[TM];
+        In a[TMV];
         In b[TN];
     };
     // one 64-position segment: lane = position, every row of the tile
@@ -171,7 +175,7 @@ conv_bwd_filter_split_kernel(const ConvParams p)
         const int wq = (int)q * p.v - p.pad_left;
         const int xbase = ((int)n * p.sxn + hp * p.sxh + wq * p.sxw) * ES;
 #pragma unroll
-        for (int e = 0; e < TM; ++e) sl.a[e] = buf_load(dr, dvoff, a_off[e], In{});
+        for (int e = 0; e < TMV; ++e) sl.a[e] = buf_load(dr, dvoff, a_off[e], In{});
 #pragma unroll
         for (int e = 0; e < TN; ++e) {
             const bool ok = pos_ok && (unsigned)(hp + b_r[e]) < (unsigned)p.H &&
@@ -180,14 +184,14 @@ conv_bwd_filter_split_kernel(const ConvParams p)
         }
     };
 
-    // this wave's private transpose region: rows A 0..TM-1, then B
+    // this wave's private transpose region: rows A 0..TMV-1, then B
     unsigned char* const mine = smem + wave * WAVE_BYTES;
     auto store_seg = [&](const Slot& sl) {
         unsigned char* base = mine + lane * ES;
 #pragma unroll
-        for (int e = 0; e < TM; ++e) *reinterpret_cast<In*>(base + e * PITCH) = sl.a[e];
+        for (int e = 0; e < TMV; ++e) *reinterpret_cast<In*>(base + e * PITCH) = sl.a[e];
 #pragma unroll
-        for (int e = 0; e < TN; ++e) *reinterpret_cast<In*>(base + (TM + e) * PITCH) = sl.b[e];
+        for (int e = 0; e < TN; ++e) *reinterpret_cast<In*>(base + (TMV + e) * PITCH) = sl.b[e];
     };
 
     const int lrow = lane % BM;
@@ -212,7 +216,7 @@ conv_bwd_filter_split_kernel(const ConvParams p)
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(mine + (TM + j * BM + lrow) * PITCH + lgrp * SEG * ES);
+            const u32x4* src = reinterpret_cast<const u32x4*>(mine + (TMV + j * BM + lrow) * PITCH + lgrp * SEG * ES);
 #pragma unroll
             for (int v = 0; v < FRAG_VECS; ++v) fb[j][v] = src[v];
         }
@@ -298,33 +302,34 @@ conv_bwd_filter_split_kernel(const ConvParams p)
         }
     }
     __syncthreads();
-    store_acc_tile<Pol, FM, FN>(p, smem, acc, m0, n0, p.M, 0, lane, wave == 0);
+    store_acc_tile<Pol, FM, FN>(p, smem, acc, m0, n0, min(m0 + TMV, p.M), 0, lane, wave == 0);
 }
 
-template <class Pol, int TM, int TN, int NW, int NSLOT>
+template <class Pol, int TM, int TN, int NW, int NSLOT, int TMV>
 static hipError_t launch_wgs_variant(const ConvParams& p0, hipStream_t stream)
 {
     ConvParams p = p0;
-    p.m_tiles = (p.M + TM - 1) / TM;
+    p.m_tiles = (p.M + TMV - 1) / TMV;
     p.n_tiles = (p.K + TN - 1) / TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
-    hipLaunchKernelGGL((conv_bwd_filter_split_kernel<Pol, TM, TN, NW, NSLOT>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((conv_bwd_filter_split_kernel<Pol, TM, TN, NW, NSLOT, TMV>), grid, dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
-//        name              policy     TM  TN  waves slots
+//        name              policy     TM  TN  waves slots valid rows
 #define MICONV_WGS_VARIANTS(X)                         \
-    X(WGS_F32_32x32, PolF32, 32, 32, 8, 1)             \
-    X(WGS_F32_16x16, PolF32x16, 16, 16, 8, 2)          \
-    X(WGS_F64_32x32, PolF64, 32, 32, 4, 1)             \
-    X(WGS_F64_16x16, PolF64, 16, 16, 8, 2)             \
-    X(WGS_BF16_32x32, PolBF16, 32, 32, 8, 1)
+    X(WGS_F32_32x32, PolF32, 32, 32, 8, 1, 32)         \
+    X(WGS_F32_16x16, PolF32x16, 16, 16, 8, 2, 16)      \
+    X(WGS_F32_8x16, PolF32x16, 16, 16, 8, 2, 8)        \
+    X(WGS_F64_32x32, PolF64, 32, 32, 4, 1, 32)         \
+    X(WGS_F64_16x16, PolF64, 16, 16, 8, 2, 16)         \
+    X(WGS_BF16_32x32, PolBF16, 32, 32, 8, 1, 32)
 
 hipError_t launch_bwd_filter_split(Variant v, const ConvParams& p, hipStream_t stream)
 {
     switch (v) {
-#define X(name, pol, tm, tn, nw, ns) \
-    case Variant::name: return launch_wgs_variant<pol, tm, tn, nw, ns>(p, stream);
+#define X(name, pol, tm, tn, nw, ns, tmv) \
+    case Variant::name: return launch_wgs_variant<pol, tm, tn, nw, ns, tmv>(p, stream);
         MICONV_WGS_VARIANTS(X)
 #undef X
     default: return hipErrorInvalidValue;

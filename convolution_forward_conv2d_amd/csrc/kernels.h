@@ -54,6 +54,7 @@ enum class Variant : int {
     WGH_F64_3x3_W16,
     WGS_F32_32x32,          // filter gradient, reduction split over waves (conv_bwd_filter_split.hip)
     WGS_F32_16x16,
+    WGS_F32_8x16,
     WGS_F64_32x32,
     WGS_F64_16x16,
     WGS_BF16_32x32,

@@ -342,13 +342,13 @@ def test_wgrad_kernel_choice_host_only():
     save a round (AlexNet conv4, Overfeat L3-L5), the split-reduction kernel where dw has few
     tiles (first layers) or where its finer tiles round better (AlexNet conv2, the bf16 layers),
     the gather kernel for channels-last bf16."""
-    want = {"tiny": "wgs_f32_16x16",
+    want = {"tiny": "wgs_f32_8x16",
             "alexnet_conv2": "wgs_f32_16x16", "alexnet_conv3": "wgh_f32x16_3x3_64x64",
             "alexnet_conv4": "wgh_f32_3x3_64x96", "alexnet_conv5": "wgh_f32x16_3x3_64x64",
             "overfeat_l1": "wgs_f32_16x16", "overfeat_l2": "wgh_f32x16_5x5_w24_64x64",
             "overfeat_l3": "wgh_f32_3x3_64x96", "overfeat_l4": "wgh_f32_3x3_64x96",
             "overfeat_l5": "wgh_f32_3x3_64x96",
-            "speech_l1": "wgs_f32_16x16", "speech_l2": "wgs_f32_32x32"}
+            "speech_l1": "wgs_f32_8x16", "speech_l2": "wgs_f32_32x32"}
     for lay in workloads.ALL_LAYERS:
         name = _wgrad_name(lay)
         if lay.name in want:
