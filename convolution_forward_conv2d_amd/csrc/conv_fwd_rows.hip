@@ -1,0 +1,273 @@
+// conv_fwd_rows.hip -- fp32 convolution forward pass for tall filter banks
+// with few filters (the speech network's second layer: 32 filters of
+// 32 x 21 x 11, stride (2, 1), on 81 x 350 inputs), as an implicit GEMM whose
+// reduction is streamed one filter row at a time.
+//
+//   y[n,k,p,q] = alpha * sum_{c,r,s} x[n,c,p*u+r-pad_top,q*v+s-pad_left] * F[k,c,r,s] + beta * y
+//
+// (the convolution of the cuDNN page, "Proposed Method"; batch-reduce GEMM
+// over the filter taps as on the single-building-block page, read from x
+// with no packed copy as on the zero-memory direct-convolution page).
+//
+// The tap-batched halo kernel stages, per channel block, every input row a
+// tile touches and the whole R x S filter slab; with R = 21 and only 32
+// filters that slab and halo outgrow LDS, and the gather kernel's
+// per-element receptive-field loads then bound the layer.  Here a chunk of
+// the reduction is (8-channel block, filter row r): a tile of TM output
+// positions spans at most NSL output rows (the host checks Q >= TM for
+// NSL = 2), so the chunk stages NSL input rows -- row p*u + r - pad_top of
+// each output row p -- of WP columns for 8 channels, zero-padded, plus the
+// S taps x 8 channels x TN filters of row r.  The MFMA operand of position
+// (slot, q) at tap s and channel c is then halo[c][slot][q*v + s]: a per-lane
+// base plus a tap offset, no per-element gather.  v_mfma_f32_32x32x2_f32
+// takes two channels per step (one per lane group), so a chunk is S * 4
+// steps; operands are read from LDS one step ahead, and chunk ch + 1 moves
+// global -> registers during chunk ch and registers -> the other LDS buffer
+// after its steps (one barrier per chunk).
+//
+// Parameters as for the forward kernels (conv_params.h): x, w, y and their
+// strides; M = N*P*Q; div_pq, div_q divide by P*Q and Q.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "conv_params.h"
+#include "kernels.h"
+#include "mfma_common.h"
+#include "tile_map.h"
+
+namespace miconv {
+
+template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP>
+__global__ void __launch_bounds__(256)
+conv_fwd_rows_kernel(const ConvParams p)
+{
+    using Pol = PolF32;
+    using AccV = Pol::AccV;
+    constexpr int NT = 256;
+    constexpr int BM = Pol::BM;
+    constexpr int G = Pol::G;                       // channels per MFMA step (one per lane group)
+    constexpr int WM = TM / WAVES_M;
+    constexpr int WN = TN / WAVES_N;
+    constexpr int FM = WM / BM;
+    constexpr int FN = WN / BM;
+    constexpr int PLANE = NSL * WP;                 // one channel's staged rows
+    constexpr int HALO = CB * PLANE;                // floats
+    constexpr int SLAB = S * CB * TN;               // floats: [s][c][k]
+    constexpr int BUF = HALO + SLAB;
+    constexpr int NH = (HALO + NT - 1) / NT;        // halo elements per thread per chunk
+    constexpr int STEPS = S * (CB / G);
+    static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
+    static_assert(CB % G == 0 && TN * CB == NT, "one (filter, channel) slab row per thread");
+    static_assert(NH <= 32, "halo validity mask");
+    static_assert(2 * BUF * 4 <= 160 * 1024, "two chunk buffers fit the LDS");
+    static_assert(4 * BM * (BM + 1) <= 2 * BUF, "epilogue stage fits");
+
+    __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int mt = tile / p.n_tiles;
+    const int nt = tile - mt * p.n_tiles;
+    const int m0 = mt * TM;
+    const int m_end = min(m0 + TM, p.M);
+    const int n0 = nt * TN;
+
+    const float* __restrict__ x = static_cast<const float*>(p.x);
+    const float* __restrict__ w = static_cast<const float*>(p.w);
+
+    // the tile's first output row (n * P + p) and the slot of a position
+    auto out_row = [&](int m) {
+        uint32_t n, pq, pp, q;
+        p.div_pq.divmod((uint32_t)m, n, pq);
+        p.div_q.divmod(pq, pp, q);
+        return (int)n * p.P + (int)pp;
+    };
+    const int row0 = out_row(m0);
+    const int nrows = p.N * p.P;
+
+    // ---- halo loader: element e = (channel, slot, column), column fastest
+    int h_base[NH];                                  // x offset of (n, slot row's p*u - pad_top, column), channel 0
+    int h_row[NH];                                   // input row p*u - pad_top (r added per chunk)
+    uint32_t h_ok = 0;
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+        const int e = tid + NT * i;
+        const int cl = e / PLANE;
+        const int rem = e - cl * PLANE;
+        const int sl = rem / WP;
+        const int col = rem - sl * WP;
+        const int orow = row0 + sl;
+        const int n = orow / p.P;
+        const int pp = orow - n * p.P;
+        const int wc = col - p.pad_left;
+        const bool ok = e < HALO && orow < nrows && (unsigned)wc < (unsigned)p.W;
+        h_row[i] = pp * p.u - p.pad_top;
+        h_base[i] = ok ? n * p.sxn + cl * p.sxc + wc * p.sxw : 0;
+        h_ok |= (ok ? 1u : 0u) << i;
+    }
+    // ---- slab loader: thread -> (filter k, channel c), the S taps of row r
+    const int sk = tid % TN;
+    const int sc = tid / TN;
+    const bool s_ok = n0 + sk < p.K;
+    const int s_base = (s_ok ? n0 + sk : 0) * p.Kred;    // packed KCRS: filter row length C*R*S
+
+    float hv[NH];
+    uint32_t hv_ok = 0;                              // validity of the chunk in registers
+    float sv[S];
+    const int ncb = p.C / CB;
+    const int nch = ncb * p.R;
+    auto load_chunk = [&](int ch) {
+        const int r = ch / ncb;
+        const int c0 = (ch - r * ncb) * CB;
+        // unconditional loads at a valid address; zeros are chosen at the store
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int h = h_row[i] + r;
+            const bool ok = ((h_ok >> i) & 1u) && (unsigned)h < (unsigned)p.H;
+            hv[i] = x[ok ? h_base[i] + c0 * p.sxc + h * p.sxh : 0];
+            m |= (ok ? 1u : 0u) << i;
+        }
+        hv_ok = m;
+        const int fo = s_base + ((c0 + sc) * p.R + r) * S;
+#pragma unroll
+        for (int s = 0; s < S; ++s) sv[s] = w[fo + s];
+    };
+    auto store_chunk = [&](int buf) {
+        float* dst = smem + buf * BUF;
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int e = tid + NT * i;
+            if (HALO % NT == 0 || e < HALO) dst[e] = (hv_ok >> i) & 1u ? hv[i] : 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < S; ++s) dst[HALO + (s * CB + sc) * TN + sk] = s_ok ? sv[s] : 0.0f;
+    };
+
+    // ---- per-lane operand bases (floats)
+    const int wm = wave / WAVES_N;
+    const int wn = wave % WAVES_N;
+    const int lrow = lane & 31;
+    const int lgrp = lane >> 5;                      // channel within a step's pair
+    int a_base[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = min(m0 + wm * WM + i * BM + lrow, p.M - 1);
+        uint32_t n, pq, pp, q;
+        p.div_pq.divmod((uint32_t)m, n, pq);
+        p.div_q.divmod(pq, pp, q);
+        const int sl = (int)n * p.P + (int)pp - row0;
+        a_base[i] = lgrp * PLANE + sl * WP + (int)q * p.v;
+    }
+    int b_base[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b_base[j] = HALO + lgrp * TN + wn * WN + j * BM + lrow;
+
+    AccV acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = AccV{};
+
+    // step t = (tap s, channel pair cp): A = halo[(2cp + g) PLANE + base + s],
+    // B = slab[(s CB + 2cp + g) TN + k]
+    auto a_off = [](int t) { const int s = t / (CB / G), cp = t % (CB / G); return G * cp * PLANE + s; };
+    auto b_off = [](int t) { const int s = t / (CB / G), cp = t % (CB / G); return (s * CB + G * cp) * TN; };
+
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+        const int cur = ch & 1;
+        const bool more = ch + 1 < nch;
+        load_chunk(more ? ch + 1 : ch);
+        __builtin_amdgcn_sched_barrier(0);
+        const float* buf = smem + cur * BUF;
+        float a[FM], b[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[i] = buf[a_base[i] + a_off(0)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[j] = buf[b_base[j] + b_off(0)];
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+            float an[FM], bn[FN];
+            if (t + 1 < STEPS) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) an[i] = buf[a_base[i] + a_off(t + 1)];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bn[j] = buf[b_base[j] + b_off(t + 1)];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Pol::mfma_s(a[i], b[j], acc[i][j]);
+            if (t + 1 < STEPS) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) a[i] = an[i];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) b[j] = bn[j];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) store_chunk(cur ^ 1);
+        __syncthreads();
+    }
+
+    store_acc_tile<Pol, FM, FN>(p, reinterpret_cast<unsigned char*>(smem), acc, m0 + wm * WM, n0 + wn * WN, m_end,
+                                wave, lane);
+}
+
+// Eligibility: fp32, S and the filter row length of the instance, C a
+// multiple of the channel block, every tile inside NSL output rows
+// (Q >= TM), the staged row width (Q - 1) * v + S <= WP.
+template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP>
+static bool rows_variant_fits(const ConvParams& p)
+{
+    static_assert(NSL >= 2, "a tile within two output rows");
+    return p.S == S && p.C % CB == 0 && p.Q >= TM && (int64_t)(p.Q - 1) * p.v + S <= WP;
+}
+
+template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP>
+static hipError_t launch_rows_variant(const ConvParams& p0, hipStream_t stream)
+{
+    ConvParams p = p0;
+    if (!rows_variant_fits<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP>(p)) return hipErrorInvalidValue;
+    p.m_tiles = (p.M + TM - 1) / TM;
+    p.n_tiles = (p.K + TN - 1) / TN;
+    const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
+    hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP>), grid, dim3(256), 0, stream,
+                       p);
+    return hipGetLastError();
+}
+
+//        name                policy TM  TN  waves  S  CB NSL WP
+#define MICONV_ROWS_VARIANTS(X)                        \
+    X(ROWS_F32_S11_256x32, 256, 32, 4, 1, 11, 8, 2, 368)
+
+bool rows_fits(Variant v, const ConvParams& p)
+{
+    switch (v) {
+#define X(name, tm, tn, wmm, wnn, s, cb, nsl, wp) \
+    case Variant::name: return rows_variant_fits<tm, tn, wmm, wnn, s, cb, nsl, wp>(p);
+        MICONV_ROWS_VARIANTS(X)
+#undef X
+    default: return false;
+    }
+}
+
+hipError_t launch_rows(Variant v, const ConvParams& p, hipStream_t stream)
+{
+    switch (v) {
+#define X(name, tm, tn, wmm, wnn, s, cb, nsl, wp) \
+    case Variant::name: return launch_rows_variant<tm, tn, wmm, wnn, s, cb, nsl, wp>(p, stream);
+        MICONV_ROWS_VARIANTS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace miconv

@@ -11,6 +11,7 @@ enum class Variant : int {
     DIRECT = 0,          // one thread per output, any dtype/layout (plain loop, no MFMA)
     DG_PHASE,            // data gradient onto 1-4 channels by stride phase (conv_bwd_data_phase.hip)
     DG_ROWS,             // ... onto one channel, dy rows staged in LDS (same file)
+    ROWS_F32_S11_256x32, // forward pass, reduction streamed by filter row (conv_fwd_rows.hip)
     MFMA_F32_128x128,
     MFMA_F32_128x64,
     MFMA_F32_256x32,
@@ -119,5 +120,7 @@ hipError_t launch_bwd_data_direct(DType dt, const ConvParams& p, hipStream_t str
 hipError_t launch_bwd_data_phase(DType dt, const ConvParams& p, hipStream_t stream);
 bool bwd_data_rows_fits(const ConvParams& p, size_t* lds_bytes);
 hipError_t launch_bwd_data_rows(const ConvParams& p, hipStream_t stream);
+bool rows_fits(Variant v, const ConvParams& p);
+hipError_t launch_rows(Variant v, const ConvParams& p, hipStream_t stream);
 
 }  // namespace miconv

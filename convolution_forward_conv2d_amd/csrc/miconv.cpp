@@ -144,6 +144,8 @@ const Candidate kBF16[] = {
 const Candidate kDirect = {Variant::DIRECT, 0, 0, "direct"};
 const Candidate kDgPhase = {Variant::DG_PHASE, 0, 0, "phase"};
 const Candidate kDgRows = {Variant::DG_ROWS, 0, 0, "rows"};
+// forward pass with the reduction streamed by filter row (conv_fwd_rows.hip)
+const Candidate kRowsF32 = {Variant::ROWS_F32_S11_256x32, 256, 32, "rows_f32_s11_256x32"};
 // Filter-gradient kernels: the gather kernel (conv_bwd_filter.hip, any
 // geometry), the LDS-halo kernel (conv_bwd_filter_halo.hip: stride 1, fixed
 // R x S, Q + S - 1 <= the row pitch wph) and the kernel that splits the
@@ -501,6 +503,12 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
         }
     }
 
+    // no halo instance: tall filter banks with few filters stream the
+    // reduction by filter row (speech layer 2: 2.9 ms through the gather kernel)
+    const bool rows_ok = pl.dt == DType::F32 && !blocked(xd) && !blocked(wd) && !blocked(yd) &&
+                         miconv::rows_fits(kRowsF32.v, p);
+    if (!is_halo(pl.cand.v) && rows_ok) pl.cand = kRowsF32;
+
     pl.tap = prefer_tap(pl.dt, p.C);
     bool forced_gather = false;
     // MIC_FORCE_VARIANT=<name> pins a variant (tests walk every variant with it)
@@ -524,6 +532,12 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
             if (halo_forced) {
             } else if (strcmp(force, kDirect.name) == 0) {
                 pl.cand = kDirect;
+            } else if (strcmp(force, kRowsF32.name) == 0) {
+                if (!rows_ok) {
+                    pl.status = MIC_STATUS_NOT_SUPPORTED;
+                    return pl;
+                }
+                pl.cand = kRowsF32;
             } else {
                 const Candidate* list;
                 int count;
@@ -552,7 +566,7 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
     }
     const size_t ie = dtype_size(xd->dtype);
     pl.bvec = ((Kred * (int64_t)ie) % 16 == 0) && ((uintptr_t)w % 16 == 0) && !blocked(wd);
-    const bool gather = pl.cand.v != Variant::DIRECT && !is_halo(pl.cand.v);
+    const bool gather = pl.cand.v != Variant::DIRECT && pl.cand.v != kRowsF32.v && !is_halo(pl.cand.v);
     if (!gather) pl.tap = false;
     if (gather && (blocked(xd) || blocked(wd))) {
         // Tap order reads a chunk of TK channels at one tap: with blocked x or
@@ -1462,6 +1476,8 @@ mic_status mic_conv_forward(mic_handle handle, double alpha, mic_tensor_desc x_d
     hipError_t err;
     if (pl.cand.v == Variant::DIRECT)
         err = miconv::launch_direct(pl.dt, pl.p, handle->stream);
+    else if (pl.cand.v == kRowsF32.v)
+        err = miconv::launch_rows(pl.cand.v, pl.p, handle->stream);
     else if (is_halo(pl.cand.v))
         err = miconv::launch_halo(pl.cand.v, pl.p, false, handle->stream);
     else

@@ -37,6 +37,9 @@ VARIANTS = {
 # the gather variants also run with the reduction in channel blocks per filter tap
 for _dt in VARIANTS:
     VARIANTS[_dt] += [v + "_tap" for v in VARIANTS[_dt] if v.startswith("mfma_")]
+# the reduction streamed by filter row: 11-wide filters, 8-channel blocks, Q >= 256
+VARIANTS["f32"] += ["rows_f32_s11_256x32"]
+_MAY_REFUSE = ("halo_", "rows_")
 # halo variants only take the shapes they were built for (the library answers
 # NOT_SUPPORTED otherwise); every one of them must run on at least one shape
 _ran = set()
@@ -92,8 +95,17 @@ def _run(lay, x, w, y, alpha=1.0, beta=0.0):
     return y
 
 
+# forward-only shapes for the row-streamed kernel: a 5x11 filter bank with a ragged second
+# filter tile (K = 40) and a ragged last position tile; a speech-like 21x11 bank, stride (2, 1),
+# padding on three sides, output rows 260 wide (a tile straddles two of them)
+FWD_SHAPES = SMALL_SHAPES + [
+    dict(name="rows_5x11", N=2, C=16, Hh=25, Ww=270, K=40, R=5, S=11, stride=(2, 1), pads=(2, 2, 0, 10)),
+    dict(name="rows_21x11", N=1, C=8, Hh=41, Ww=260, K=32, R=21, S=11, stride=(2, 1), pads=(10, 10, 0, 10)),
+]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
-@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: s["name"])
+@pytest.mark.parametrize("shape", FWD_SHAPES, ids=lambda s: s["name"])
 def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
     lay = _small(dtype=dtype, **{k: v for k, v in shape.items()})
     x64, w64 = H.inputs(lay)
@@ -107,7 +119,7 @@ def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
         try:
             _run(lay, x, w, y)
         except mic.MicError as e:
-            if var.startswith("halo_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+            if var.startswith(_MAY_REFUSE) and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
                 continue
             raise
         H.check(dtype, y.double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (shape["name"], dtype, var))
@@ -199,7 +211,7 @@ def test_alpha_beta(dtype, geom, monkeypatch):
         try:
             _run(lay, x, w, y, alpha=0.5, beta=0.25)
         except mic.MicError as e:
-            if var.startswith("halo_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+            if var.startswith(_MAY_REFUSE) and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
                 continue
             raise
         assert np.array_equal(y.double().cpu().numpy(), 0.5 * acc + 0.25 * y_old), var
