@@ -923,7 +923,8 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
         // position: worth it only when 16x16 tiles leave most CUs idle
         // (measured: speech L1, 58 tiles, 4.7 -> 4.1 ms; Overfeat L1, 138
         // tiles, 2.4 -> 3.0 ms)
-        if (wc.c.v == Variant::WGS_F32_8x16)
+        // (a preference of the automatic choice: forced, the kernel takes any shape)
+        if (wc.c.v == Variant::WGS_F32_8x16 && !force)
             ok = ok && (int64_t)((p.M + 15) / 16) * ((p.K + 15) / 16) * 4 <= num_cu;
         if (!ok) {
             if (force) {
