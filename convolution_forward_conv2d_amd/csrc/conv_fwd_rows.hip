@@ -221,6 +221,262 @@ conv_fwd_rows_kernel(const ConvParams p)
                                 wave, lane);
 }
 
+// ------------------------------------------------------------------ data gradient
+//
+// dx[n,c,h,w] = alpha * sum over k, r, s with h + pad_top - r = p*u
+// (0 <= p < P) and q = w + pad_left - s (0 <= q < Q; horizontal stride 1)
+// of dy[n,k,p,q] * F[k,c,r,s] + beta * dx.  For the rows of one phase
+// a = (h + pad_top) mod u the taps are r = a + u*i and p = P0(h) - i: a
+// stride-1 correlation of dy with filter rows a, a + u, ... and the columns
+// reversed.  One launch per phase (the host folds the phase's first row
+// into y and u into its row stride, so the epilogue is the forward one);
+// a chunk is (8 dy channels, tap row i), staging the dy rows P0 + h' - i of
+// the tile's two output rows, columns q = w + pad_left - (S - 1) ... ;
+// the operand of (w, s) is halo[k][slot][w + S - 1 - s] and the slab holds
+// F[k][c][a + u*i][s] with the output channel c as the MFMA column.
+//
+// Parameters (per launch): x = dy with sx* its (n, k, p, q) strides, w = F,
+// y = dx at row h0 of the phase, syp = u * dx's row stride; N, P, Q dy's
+// dims; H = the phase's row count h', W = dx's width; K = dx's channels
+// (the MFMA columns), C = dy's channels (the reduction), R = the phase's
+// tap rows; pad_top carries P0(h0), pad_left the column pad, u the filter
+// row step, Hp the phase a; M = N * h' * W, div_pq / div_q by h'*W and W.
+template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP>
+__global__ void __launch_bounds__(256)
+conv_bwd_data_rows_mfma_kernel(const ConvParams p)
+{
+    using Pol = PolF32;
+    using AccV = Pol::AccV;
+    constexpr int NT = 256;
+    constexpr int BM = Pol::BM;
+    constexpr int G = Pol::G;
+    constexpr int WM = TM / WAVES_M;
+    constexpr int WN = TN / WAVES_N;
+    constexpr int FM = WM / BM;
+    constexpr int FN = WN / BM;
+    constexpr int PLANE = NSL * WP;
+    constexpr int HALO = CB * PLANE;
+    constexpr int SLAB = S * CB * TN;
+    constexpr int BUF = HALO + SLAB;
+    constexpr int NH = (HALO + NT - 1) / NT;
+    constexpr int STEPS = S * (CB / G);
+    static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
+    static_assert(CB % G == 0 && TN * CB == NT, "one (output channel, dy channel) slab row per thread");
+    static_assert(NH <= 32, "halo validity mask");
+    static_assert(2 * BUF * 4 <= 160 * 1024, "two chunk buffers fit the LDS");
+    static_assert(4 * BM * (BM + 1) <= 2 * BUF, "epilogue stage fits");
+
+    __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int mt = tile / p.n_tiles;
+    const int nt = tile - mt * p.n_tiles;
+    const int m0 = mt * TM;
+    const int m_end = min(m0 + TM, p.M);
+    const int n0 = nt * TN;
+
+    const float* __restrict__ dy = static_cast<const float*>(p.x);
+    const float* __restrict__ f = static_cast<const float*>(p.w);
+    const int hq = p.H;                               // output rows of the phase
+    const int P0f = p.pad_top;                        // dy row of tap row 0 at h' = 0
+    const int a = p.Hp;                               // the phase: filter rows a + u*i
+    const int qoff = p.pad_left - (S - 1);            // dy column of halo column 0 at w = 0
+
+    auto out_row = [&](int m) {
+        uint32_t n, pq, pp, q;
+        p.div_pq.divmod((uint32_t)m, n, pq);
+        p.div_q.divmod(pq, pp, q);
+        return (int)n * hq + (int)pp;
+    };
+    const int row0 = out_row(m0);
+    const int nrows = p.N * hq;
+
+    // ---- halo loader: element e = (dy channel, slot, column), column fastest
+    int h_base[NH];
+    int h_row[NH];                                    // dy row of tap row 0 (i subtracted per chunk)
+    uint32_t h_ok = 0;
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+        const int e = tid + NT * i;
+        const int cl = e / PLANE;
+        const int rem = e - cl * PLANE;
+        const int sl = rem / WP;
+        const int col = rem - sl * WP;
+        const int orow = row0 + sl;
+        const int n = orow / hq;
+        const int hh = orow - n * hq;
+        const int qc = col + qoff;
+        const bool ok = e < HALO && orow < nrows && (unsigned)qc < (unsigned)p.Q;
+        h_row[i] = P0f + hh;
+        h_base[i] = ok ? n * p.sxn + cl * p.sxc + qc * p.sxw : 0;
+        h_ok |= (ok ? 1u : 0u) << i;
+    }
+    // ---- slab loader: thread -> (output channel c, dy channel k), the S taps of row a + u*i
+    const int sk = tid % TN;                          // output channel within the tile
+    const int sc = tid / TN;                          // dy channel within the block
+    const bool s_ok = n0 + sk < p.K;
+    const int RS = p.R * S;                           // p.R here: the filter's full row count
+
+    float hv[NH];
+    uint32_t hv_ok = 0;
+    float sv[S];
+    const int ncb = p.C / CB;
+    const int nri = p.Kred;                           // tap rows of the phase
+    const int nch = ncb * nri;
+    auto load_chunk = [&](int ch) {
+        const int i = ch / ncb;
+        const int k0 = (ch - i * ncb) * CB;
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < NH; ++e) {
+            const int pr = h_row[e] - i;
+            const bool ok = ((h_ok >> e) & 1u) && (unsigned)pr < (unsigned)p.P;
+            hv[e] = dy[ok ? h_base[e] + k0 * p.sxc + pr * p.sxh : 0];
+            m |= (ok ? 1u : 0u) << e;
+        }
+        hv_ok = m;
+        // F[k0 + sc][c][a + u*i][0 .. S-1], packed K,C,R,S
+        const int fo = ((k0 + sc) * p.K + (s_ok ? n0 + sk : 0)) * RS + (a + p.u * i) * S;
+#pragma unroll
+        for (int s = 0; s < S; ++s) sv[s] = f[fo + s];
+    };
+    auto store_chunk = [&](int buf) {
+        float* dst = smem + buf * BUF;
+#pragma unroll
+        for (int e = 0; e < NH; ++e) {
+            const int ee = tid + NT * e;
+            if (HALO % NT == 0 || ee < HALO) dst[ee] = (hv_ok >> e) & 1u ? hv[e] : 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < S; ++s) dst[HALO + (s * CB + sc) * TN + sk] = s_ok ? sv[s] : 0.0f;
+    };
+
+    const int wm = wave / WAVES_N;
+    const int wn = wave % WAVES_N;
+    const int lrow = lane & 31;
+    const int lgrp = lane >> 5;
+    int a_base[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = min(m0 + wm * WM + i * BM + lrow, p.M - 1);
+        uint32_t n, pq, pp, q;
+        p.div_pq.divmod((uint32_t)m, n, pq);
+        p.div_q.divmod(pq, pp, q);
+        const int sl = (int)n * hq + (int)pp - row0;
+        a_base[i] = lgrp * PLANE + sl * WP + (int)q + (S - 1);
+    }
+    int b_base[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b_base[j] = HALO + lgrp * TN + wn * WN + j * BM + lrow;
+
+    AccV acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = AccV{};
+
+    // step t = (tap s, dy channel pair cp): A = halo[(2cp + g) PLANE + base - s]
+    auto a_off = [](int t) { const int s = t / (CB / G), cp = t % (CB / G); return G * cp * PLANE - s; };
+    auto b_off = [](int t) { const int s = t / (CB / G), cp = t % (CB / G); return (s * CB + G * cp) * TN; };
+
+    if (nch > 0) {
+        load_chunk(0);
+        store_chunk(0);
+        __syncthreads();
+    }
+    for (int ch = 0; ch < nch; ++ch) {
+        const int cur = ch & 1;
+        const bool more = ch + 1 < nch;
+        load_chunk(more ? ch + 1 : ch);
+        __builtin_amdgcn_sched_barrier(0);
+        const float* buf = smem + cur * BUF;
+        float av[FM], bv[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) av[i] = buf[a_base[i] + a_off(0)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bv[j] = buf[b_base[j] + b_off(0)];
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+            float an[FM], bn[FN];
+            if (t + 1 < STEPS) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) an[i] = buf[a_base[i] + a_off(t + 1)];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bn[j] = buf[b_base[j] + b_off(t + 1)];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Pol::mfma_s(av[i], bv[j], acc[i][j]);
+            if (t + 1 < STEPS) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) av[i] = an[i];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bv[j] = bn[j];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) store_chunk(cur ^ 1);
+        __syncthreads();
+    }
+
+    store_acc_tile<Pol, FM, FN>(p, reinterpret_cast<unsigned char*>(smem), acc, m0 + wm * WM, n0 + wn * WN, m_end,
+                                wave, lane);
+}
+
+// The data gradient's instance: the forward geometry (dy = P x Q, filters
+// K x C x R x S, dx = N x C x H x W) with horizontal stride 1, S = 11, K a
+// multiple of 8, W >= 256 (a tile within two output rows of a phase) and
+// W + S - 1 <= 368.  Params in the direct kernel's layout.
+constexpr int kDgRowsTM = 256, kDgRowsTN = 32, kDgRowsS = 11, kDgRowsCB = 8, kDgRowsWP = 368;
+
+bool bwd_data_rows_mfma_fits(const ConvParams& p)
+{
+    return p.v == 1 && p.S == kDgRowsS && p.K % kDgRowsCB == 0 && p.W >= kDgRowsTM &&
+           p.W + kDgRowsS - 1 <= kDgRowsWP;
+}
+
+hipError_t launch_bwd_data_rows_mfma(const ConvParams& p0, hipStream_t stream)
+{
+    if (!bwd_data_rows_mfma_fits(p0)) return hipErrorInvalidValue;
+    const int u = p0.u;
+    for (int a = 0; a < u; ++a) {
+        // rows h with (h + pad_top) mod u == a: h = h0 + u*h'
+        const int h0 = ((a - p0.pad_top) % u + u) % u;
+        const int hq = h0 < p0.H ? (p0.H - h0 + u - 1) / u : 0;
+        if (hq == 0) continue;
+        const int nr = a < p0.R ? (p0.R - a + u - 1) / u : 0;
+        ConvParams p = p0;
+        p.y = static_cast<float*>(p0.y) + (int64_t)h0 * p0.syp;
+        p.syp = u * p0.syp;
+        p.H = hq;
+        p.K = p0.C;                                  // MFMA columns: dx's channels
+        p.C = p0.K;                                  // reduction: dy's channels (blocks of 8)
+        p.R = p0.R;                                  // the filter's rows (for its strides)
+        p.Kred = nr;                                 // tap rows a, a + u, ...
+        p.Hp = a;
+        p.pad_top = (h0 + p0.pad_top - a) / u;       // P0 at h' = 0
+        p.M = p0.N * hq * p0.W;
+        p.div_pq = FastDiv((uint32_t)(hq * p0.W));
+        p.div_q = FastDiv((uint32_t)p0.W);
+        p.Q = p0.Q;
+        p.m_tiles = (p.M + kDgRowsTM - 1) / kDgRowsTM;
+        p.n_tiles = (p.K + kDgRowsTN - 1) / kDgRowsTN;
+        const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
+        if (nr == 0 && p.beta == 1.0) continue;      // nothing to add (alpha * 0 + dx)
+        hipLaunchKernelGGL((conv_bwd_data_rows_mfma_kernel<kDgRowsTM, kDgRowsTN, 4, 1, kDgRowsS, kDgRowsCB, 2,
+                                                           kDgRowsWP>),
+                           grid, dim3(256), 0, stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // Eligibility: fp32, S and the filter row length of the instance, C a
 // multiple of the channel block, every tile inside NSL output rows
 // (Q >= TM), the staged row width (Q - 1) * v + S <= WP.

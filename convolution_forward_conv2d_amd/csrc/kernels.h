@@ -12,6 +12,7 @@ enum class Variant : int {
     DG_PHASE,            // data gradient onto 1-4 channels by stride phase (conv_bwd_data_phase.hip)
     DG_ROWS,             // ... onto one channel, dy rows staged in LDS (same file)
     ROWS_F32_S11_256x32, // forward pass, reduction streamed by filter row (conv_fwd_rows.hip)
+    DG_ROWS_MFMA,        // data gradient, the same streaming per stride phase (conv_fwd_rows.hip)
     MFMA_F32_128x128,
     MFMA_F32_128x64,
     MFMA_F32_256x32,
@@ -122,5 +123,7 @@ bool bwd_data_rows_fits(const ConvParams& p, size_t* lds_bytes);
 hipError_t launch_bwd_data_rows(const ConvParams& p, hipStream_t stream);
 bool rows_fits(Variant v, const ConvParams& p);
 hipError_t launch_rows(Variant v, const ConvParams& p, hipStream_t stream);
+bool bwd_data_rows_mfma_fits(const ConvParams& p);
+hipError_t launch_bwd_data_rows_mfma(const ConvParams& p, hipStream_t stream);
 
 }  // namespace miconv

@@ -146,6 +146,7 @@ const Candidate kDgPhase = {Variant::DG_PHASE, 0, 0, "phase"};
 const Candidate kDgRows = {Variant::DG_ROWS, 0, 0, "rows"};
 // forward pass with the reduction streamed by filter row (conv_fwd_rows.hip)
 const Candidate kRowsF32 = {Variant::ROWS_F32_S11_256x32, 256, 32, "rows_f32_s11_256x32"};
+const Candidate kDgRowsMfma = {Variant::DG_ROWS_MFMA, 256, 32, "rows_mfma_f32_s11_256x32"};
 // Filter-gradient kernels: the gather kernel (conv_bwd_filter.hip, any
 // geometry), the LDS-halo kernel (conv_bwd_filter_halo.hip: stride 1, fixed
 // R x S, Q + S - 1 <= the row pitch wph) and the kernel that splits the
@@ -755,8 +756,23 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
             rows_ok = miconv::bwd_data_rows_fits(q, nullptr);
         }
         const bool rows = forced_dgrad_name ? strcmp(forced_dgrad_name, kDgRows.name) == 0 && rows_ok : rows_ok;
-        const bool direct = forced_dgrad_name ? strcmp(forced_dgrad_name, kDirect.name) == 0 || phase || rows
-                                              : C < 16;
+        // horizontal stride 1 and an 11-wide filter onto wide rows: the
+        // forward pass's row-streamed kernel per stride phase (speech layer 2:
+        // 5.0 ms through the gather kernel)
+        bool rows_mfma_ok = false;
+        if (pl.dt == DType::F32 && C >= 16) {
+            ConvParams q = p;
+            q.K = k;
+            q.W = W;
+            q.S = S;
+            q.v = cd->v;
+            rows_mfma_ok = miconv::bwd_data_rows_mfma_fits(q);
+        }
+        const bool rows_mfma = forced_dgrad_name ? strcmp(forced_dgrad_name, kDgRowsMfma.name) == 0 && rows_mfma_ok
+                                                 : rows_mfma_ok;
+        const bool direct = forced_dgrad_name
+                                ? strcmp(forced_dgrad_name, kDirect.name) == 0 || phase || rows || rows_mfma
+                                : C < 16 || rows_mfma;
         if (!direct) {
             p.C = k;
             p.K = C;
@@ -784,6 +800,7 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
             // direct kernel layout (conv_bwd_data.hip, conv_bwd_data_phase.hip)
             if (phase) pl.cand = kDgPhase;
             if (rows) pl.cand = kDgRows;
+            if (rows_mfma) pl.cand = kDgRowsMfma;
             p.C = C;
             p.H = H;
             p.W = W;
@@ -1500,6 +1517,8 @@ mic_status mic_conv_backward_data(mic_handle handle, double alpha, mic_filter_de
         err = miconv::launch_bwd_data_phase(pl.dt, pl.p, handle->stream);
     else if (pl.cand.v == Variant::DG_ROWS)
         err = miconv::launch_bwd_data_rows(pl.p, handle->stream);
+    else if (pl.cand.v == Variant::DG_ROWS_MFMA)
+        err = miconv::launch_bwd_data_rows_mfma(pl.p, handle->stream);
     else if (is_halo(pl.cand.v))
         err = miconv::launch_halo(pl.cand.v, pl.p, true, handle->stream);
     else

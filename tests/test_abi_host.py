@@ -267,8 +267,10 @@ def test_dgrad_kernel_choice_host_only():
     assert names["alexnet_conv2"] == "dgrad_halo_f32x16_5x5_128x96"
     # strided layers and bf16 take the gather kernel in data-gradient mode; onto 3 channels
     # the stride-phase kernel, onto 1 channel its row-staged form
-    for name in ("speech_l2", "prec_conv3_bf16_nchw", "prec_conv5_bf16_nhwc"):
+    for name in ("prec_conv3_bf16_nchw", "prec_conv5_bf16_nhwc"):
         assert names[name].startswith("dgrad_mfma_"), (name, names[name])
+    # 21x11 / stride (2, 1) onto 32 channels: the row-streamed kernel per stride phase
+    assert names["speech_l2"] == "dgrad_rows_mfma_f32_s11_256x32"
     assert names["overfeat_l1"] == "dgrad_phase"
     assert names["speech_l1"] == "dgrad_rows"
 

@@ -36,6 +36,9 @@ DG_VARIANTS["f32"] += ["phase"]
 DG_VARIANTS["f64"] += ["phase"]
 # its row-staged form onto one channel (fp32); NOT_SUPPORTED on other shapes
 DG_VARIANTS["f32"] += ["rows"]
+# the forward pass's row-streamed kernel per stride phase: horizontal stride 1, 11-wide
+# filters, dy channels in blocks of 8, dx rows >= 256 wide
+DG_VARIANTS["f32"] += ["rows_mfma_f32_s11_256x32"]
 _MAY_REFUSE = ("halo_", "phase", "rows")
 # the gather kernel in data-gradient mode (any stride)
 DG_VARIANTS["f32"] += ["mfma_f32_128x128", "mfma_f32_128x64", "mfma_f32_64x128", "mfma_f32_256x32"]
@@ -57,6 +60,11 @@ SHAPES = SMALL_SHAPES + [
     dict(name="dg_phase_c3_s4", N=2, C=3, Hh=39, Ww=43, K=24, R=11, S=11, stride=(4, 4), pads=(2, 0, 1, 3)),
     # filter narrower than the stride: phases with no tap at all leave beta * dx
     dict(name="dg_phase_c1_narrow", N=2, C=1, Hh=14, Ww=15, K=6, R=2, S=2, stride=(3, 3), pads=(0, 0, 0, 0)),
+    # row-streamed per phase: speech-like 21x11 / (2, 1) onto 40 channels (a ragged second
+    # channel tile), and 7x11 / (3, 1) with padding on every side
+    dict(name="dg_rows_21x11", N=1, C=40, Hh=41, Ww=260, K=16, R=21, S=11, stride=(2, 1),
+         pads=(10, 10, 0, 10)),
+    dict(name="dg_rows_s3", N=2, C=16, Hh=20, Ww=270, K=8, R=7, S=11, stride=(3, 1), pads=(2, 1, 3, 7)),
 ]
 
 
