@@ -221,6 +221,211 @@ conv_fwd_rows_kernel(const ConvParams p)
                                 wave, lane);
 }
 
+// ------------------------------------------------------------------ one input channel
+//
+// The same streaming for a single input channel (the speech network's first
+// layer: 32 filters of 41 x 11, stride 2, on 161 x 700): with no channel
+// pair to give the MFMA's two lane groups, they take adjacent taps (s, s+1)
+// of a filter row (S rounded up to SP = S + 1, the extra tap zero), and a
+// chunk is RB filter rows, so that it holds RB * SP / 2 steps.  The chunk
+// stages, per filter row j and output-row slot, one input row of WP columns;
+// the operand of (slot, q) at (j, s) is halo[j][slot][q*v + s].
+template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int RB, int NSL, int WP>
+__global__ void __launch_bounds__(256)
+conv_fwd_rows1_kernel(const ConvParams p)
+{
+    using Pol = PolF32;
+    using AccV = Pol::AccV;
+    constexpr int NT = 256;
+    constexpr int BM = Pol::BM;
+    constexpr int G = Pol::G;
+    constexpr int SP = (S + G - 1) / G * G;         // taps rounded up to whole pairs
+    constexpr int WM = TM / WAVES_M;
+    constexpr int WN = TN / WAVES_N;
+    constexpr int FM = WM / BM;
+    constexpr int FN = WN / BM;
+    constexpr int ROWP = NSL * WP;                  // one filter row's staged input rows
+    constexpr int HALO = RB * ROWP;
+    constexpr int SLAB = RB * SP * TN;              // [j][s][k]
+    constexpr int BUF = HALO + SLAB;
+    constexpr int NH = (HALO + NT - 1) / NT;
+    constexpr int NS = (SLAB + NT - 1) / NT;
+    constexpr int STEPS = RB * (SP / G);
+    static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
+    static_assert(NH <= 32 && NS <= 32, "validity masks");
+    static_assert(2 * BUF * 4 <= 160 * 1024, "two chunk buffers fit the LDS");
+    static_assert(4 * BM * (BM + 1) <= 2 * BUF, "epilogue stage fits");
+
+    __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int mt = tile / p.n_tiles;
+    const int nt = tile - mt * p.n_tiles;
+    const int m0 = mt * TM;
+    const int m_end = min(m0 + TM, p.M);
+    const int n0 = nt * TN;
+
+    const float* __restrict__ x = static_cast<const float*>(p.x);
+    const float* __restrict__ w = static_cast<const float*>(p.w);
+
+    auto out_row = [&](int m) {
+        uint32_t n, pq, pp, q;
+        p.div_pq.divmod((uint32_t)m, n, pq);
+        p.div_q.divmod(pq, pp, q);
+        return (int)n * p.P + (int)pp;
+    };
+    const int row0 = out_row(m0);
+    const int nrows = p.N * p.P;
+
+    // ---- halo loader: element e = (filter row j, slot, column), column fastest
+    int h_base[NH];
+    int h_row[NH];                                   // input row of filter row j at chunk row 0
+    uint32_t h_ok = 0;
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+        const int e = tid + NT * i;
+        const int j = e / ROWP;
+        const int rem = e - j * ROWP;
+        const int sl = rem / WP;
+        const int col = rem - sl * WP;
+        const int orow = row0 + sl;
+        const int n = orow / p.P;
+        const int pp = orow - n * p.P;
+        const int wc = col - p.pad_left;
+        const bool ok = e < HALO && orow < nrows && (unsigned)wc < (unsigned)p.W;
+        h_row[i] = pp * p.u - p.pad_top + j;
+        h_base[i] = ok ? n * p.sxn + wc * p.sxw : 0;
+        h_ok |= (ok ? 1u : 0u) << i;
+    }
+    // ---- slab loader: element e = (filter row j, tap s, filter k), k fastest
+    int s_off[NS];
+    uint32_t s_ok0 = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int e = tid + NT * i;
+        const int j = e / (SP * TN);
+        const int rem = e - j * (SP * TN);
+        const int ss = rem / TN;
+        const int k = rem - ss * TN;
+        const bool ok = e < SLAB && ss < S && n0 + k < p.K;
+        s_off[i] = ok ? (n0 + k) * p.Kred + j * S + ss : 0;   // packed K,1,R,S; row r0 added per chunk
+        s_ok0 |= (ok ? 1u : 0u) << i;
+    }
+
+    float hv[NH], sv[NS];
+    uint32_t hv_ok = 0, sv_ok = 0;
+    const int nch = (p.R + RB - 1) / RB;
+    auto load_chunk = [&](int ch) {
+        const int r0 = ch * RB;
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int h = h_row[i] + r0;
+            const bool ok = ((h_ok >> i) & 1u) && (unsigned)h < (unsigned)p.H;
+            hv[i] = x[ok ? h_base[i] + h * p.sxh : 0];
+            m |= (ok ? 1u : 0u) << i;
+        }
+        hv_ok = m;
+        uint32_t ms = 0;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int e = tid + NT * i;
+            const int j = e / (SP * TN);
+            const bool ok = ((s_ok0 >> i) & 1u) && r0 + j < p.R;
+            sv[i] = w[ok ? s_off[i] + r0 * S : 0];
+            ms |= (ok ? 1u : 0u) << i;
+        }
+        sv_ok = ms;
+    };
+    auto store_chunk = [&](int buf) {
+        float* dst = smem + buf * BUF;
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int e = tid + NT * i;
+            if (HALO % NT == 0 || e < HALO) dst[e] = (hv_ok >> i) & 1u ? hv[i] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int e = tid + NT * i;
+            if (SLAB % NT == 0 || e < SLAB) dst[HALO + e] = (sv_ok >> i) & 1u ? sv[i] : 0.0f;
+        }
+    };
+
+    const int wm = wave / WAVES_N;
+    const int wn = wave % WAVES_N;
+    const int lrow = lane & 31;
+    const int lgrp = lane >> 5;                      // tap within a step's pair
+    int a_base[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = min(m0 + wm * WM + i * BM + lrow, p.M - 1);
+        uint32_t n, pq, pp, q;
+        p.div_pq.divmod((uint32_t)m, n, pq);
+        p.div_q.divmod(pq, pp, q);
+        const int sl = (int)n * p.P + (int)pp - row0;
+        a_base[i] = sl * WP + (int)q * p.v + lgrp;
+    }
+    int b_base[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b_base[j] = HALO + lgrp * TN + wn * WN + j * BM + lrow;
+
+    AccV acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = AccV{};
+
+    // step t = (filter row j, tap pair sp): A = halo[j ROWP + base + 2 sp], B = slab[(j SP + 2 sp + g) TN + k]
+    auto a_off = [](int t) { const int j = t / (SP / G), sp = t % (SP / G); return j * ROWP + G * sp; };
+    auto b_off = [](int t) { const int j = t / (SP / G), sp = t % (SP / G); return (j * SP + G * sp) * TN; };
+
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+        const int cur = ch & 1;
+        const bool more = ch + 1 < nch;
+        load_chunk(more ? ch + 1 : ch);
+        __builtin_amdgcn_sched_barrier(0);
+        const float* buf = smem + cur * BUF;
+        float av[FM], bv[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) av[i] = buf[a_base[i] + a_off(0)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bv[j] = buf[b_base[j] + b_off(0)];
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+            float an[FM], bn[FN];
+            if (t + 1 < STEPS) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) an[i] = buf[a_base[i] + a_off(t + 1)];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bn[j] = buf[b_base[j] + b_off(t + 1)];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Pol::mfma_s(av[i], bv[j], acc[i][j]);
+            if (t + 1 < STEPS) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) av[i] = an[i];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bv[j] = bn[j];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) store_chunk(cur ^ 1);
+        __syncthreads();
+    }
+
+    store_acc_tile<Pol, FM, FN>(p, reinterpret_cast<unsigned char*>(smem), acc, m0 + wm * WM, n0 + wn * WN, m_end,
+                                wave, lane);
+}
+
 // ------------------------------------------------------------------ data gradient
 //
 // dx[n,c,h,w] = alpha * sum over k, r, s with h + pad_top - r = p*u
@@ -504,8 +709,30 @@ static hipError_t launch_rows_variant(const ConvParams& p0, hipStream_t stream)
 #define MICONV_ROWS_VARIANTS(X)                        \
     X(ROWS_F32_S11_256x32, 256, 32, 4, 1, 11, 8, 2, 368)
 
+// one input channel: S = 11 taps as 6 pairs, 4 filter rows per chunk, two
+// output-row slots of 712 staged columns ((Q - 1) * v + 12 <= 712)
+constexpr int kRows1TM = 256, kRows1TN = 32, kRows1S = 11, kRows1RB = 4, kRows1WP = 712;
+
+static bool rows1_fits(const ConvParams& p)
+{
+    return p.C == 1 && p.S == kRows1S && p.Q >= kRows1TM && (int64_t)(p.Q - 1) * p.v + kRows1S + 1 <= kRows1WP;
+}
+
+static hipError_t launch_rows1(const ConvParams& p0, hipStream_t stream)
+{
+    if (!rows1_fits(p0)) return hipErrorInvalidValue;
+    ConvParams p = p0;
+    p.m_tiles = (p.M + kRows1TM - 1) / kRows1TM;
+    p.n_tiles = (p.K + kRows1TN - 1) / kRows1TN;
+    const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
+    hipLaunchKernelGGL((conv_fwd_rows1_kernel<kRows1TM, kRows1TN, 4, 1, kRows1S, kRows1RB, 2, kRows1WP>), grid,
+                       dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
 bool rows_fits(Variant v, const ConvParams& p)
 {
+    if (v == Variant::ROWS1_F32_S11_256x32) return rows1_fits(p);
     switch (v) {
 #define X(name, tm, tn, wmm, wnn, s, cb, nsl, wp) \
     case Variant::name: return rows_variant_fits<tm, tn, wmm, wnn, s, cb, nsl, wp>(p);
@@ -517,6 +744,7 @@ bool rows_fits(Variant v, const ConvParams& p)
 
 hipError_t launch_rows(Variant v, const ConvParams& p, hipStream_t stream)
 {
+    if (v == Variant::ROWS1_F32_S11_256x32) return launch_rows1(p, stream);
     switch (v) {
 #define X(name, tm, tn, wmm, wnn, s, cb, nsl, wp) \
     case Variant::name: return launch_rows_variant<tm, tn, wmm, wnn, s, cb, nsl, wp>(p, stream);

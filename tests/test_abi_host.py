@@ -140,7 +140,7 @@ def test_kernel_choice_host_only():
     assert names["overfeat_l1"].startswith("mfma_f32_")
     # 21x11 filters, 32 filters, Q = 350 >= the 256-position tile: reduction streamed by filter row
     assert names["speech_l2"] == "rows_f32_s11_256x32"
-    assert names["speech_l1"].startswith("mfma_f32_")          # one channel: no 8-channel block
+    assert names["speech_l1"] == "rows1_f32_s11_256x32"         # one channel: adjacent taps paired
     assert names["prec_conv3_f64_nchw"].startswith("halo_f64_3x3_")
     assert names["prec_conv3_bf16_nhwc"].startswith("halo_bf16_3x3_")
     assert names["prec_conv5_bf16_nchw"].startswith("halo_bf16_3x3_")

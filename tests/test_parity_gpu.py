@@ -38,8 +38,8 @@ VARIANTS = {
 for _dt in VARIANTS:
     VARIANTS[_dt] += [v + "_tap" for v in VARIANTS[_dt] if v.startswith("mfma_")]
 # the reduction streamed by filter row: 11-wide filters, 8-channel blocks, Q >= 256
-VARIANTS["f32"] += ["rows_f32_s11_256x32"]
-_MAY_REFUSE = ("halo_", "rows_")
+VARIANTS["f32"] += ["rows_f32_s11_256x32", "rows1_f32_s11_256x32"]
+_MAY_REFUSE = ("halo_", "rows_", "rows1_")
 # halo variants only take the shapes they were built for (the library answers
 # NOT_SUPPORTED otherwise); every one of them must run on at least one shape
 _ran = set()
@@ -101,6 +101,10 @@ def _run(lay, x, w, y, alpha=1.0, beta=0.0):
 FWD_SHAPES = SMALL_SHAPES + [
     dict(name="rows_5x11", N=2, C=16, Hh=25, Ww=270, K=40, R=5, S=11, stride=(2, 1), pads=(2, 2, 0, 10)),
     dict(name="rows_21x11", N=1, C=8, Hh=41, Ww=260, K=32, R=21, S=11, stride=(2, 1), pads=(10, 10, 0, 10)),
+    # one input channel (adjacent taps paired): speech-like 41x11 / (2, 2) with padding on three
+    # sides and K = 40 (a ragged filter tile); 7 filter rows (the last chunk of 4 half empty)
+    dict(name="rows1_41x11", N=1, C=1, Hh=61, Ww=530, K=40, R=41, S=11, stride=(2, 2), pads=(20, 20, 0, 10)),
+    dict(name="rows1_7x11", N=2, C=1, Hh=15, Ww=270, K=32, R=7, S=11, stride=(1, 1), pads=(3, 3, 5, 5)),
 ]
 
 
