@@ -13,17 +13,20 @@
 // tile touches and the whole R x S filter slab; with R = 21 and only 32
 // filters that slab and halo outgrow LDS, and the gather kernel's
 // per-element receptive-field loads then bound the layer.  Here a chunk of
-// the reduction is (8-channel block, filter row r): a tile of TM output
+// the reduction is (CB-channel block, filter row r): a tile of TM output
 // positions spans at most NSL output rows (the host checks Q >= TM for
 // NSL = 2), so the chunk stages NSL input rows -- row p*u + r - pad_top of
-// each output row p -- of WP columns for 8 channels, zero-padded, plus the
-// S taps x 8 channels x TN filters of row r.  The MFMA operand of position
+// each output row p -- of WP columns for CB channels, zero-padded, plus the
+// S taps x CB channels x TN filters of row r.  The MFMA operand of position
 // (slot, q) at tap s and channel c is then halo[c][slot][q*v + s]: a per-lane
 // base plus a tap offset, no per-element gather.  v_mfma_f32_32x32x2_f32
-// takes two channels per step (one per lane group), so a chunk is S * 4
+// takes two channels per step (one per lane group), so a chunk is S * CB / 2
 // steps; operands are read from LDS one step ahead, and chunk ch + 1 moves
 // global -> registers during chunk ch and registers -> the other LDS buffer
-// after its steps (one barrier per chunk).
+// after its steps (one barrier per chunk).  Small chunks are the point: at
+// CB = 4 a block holds 35 KB of LDS and 128 registers a lane, so four blocks
+// share a CU and cover each other's chunk-edge waits (CB = 8: two blocks,
+// 4% slower on the speech layer; CB = 2: 6% slower).
 //
 // Parameters as for the forward kernels (conv_params.h): x, w, y and their
 // strides; M = N*P*Q; div_pq, div_q divide by P*Q and Q.
@@ -58,7 +61,10 @@ conv_fwd_rows_kernel(const ConvParams p)
     constexpr int NH = (HALO + NT - 1) / NT;        // halo elements per thread per chunk
     constexpr int STEPS = S * (CB / G);
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
-    static_assert(CB % G == 0 && TN * CB == NT, "one (filter, channel) slab row per thread");
+    constexpr int SROWS = TN * CB;                  // slab rows (filter, channel) of S taps
+    constexpr int SPLIT = NT / SROWS;               // threads sharing a slab row
+    constexpr int SH = (S + SPLIT - 1) / SPLIT;     // taps per thread
+    static_assert(CB % G == 0 && NT % SROWS == 0, "whole slab rows per thread group");
     static_assert(NH <= 32, "halo validity mask");
     static_assert(2 * BUF * 4 <= 160 * 1024, "two chunk buffers fit the LDS");
     static_assert(4 * BM * (BM + 1) <= 2 * BUF, "epilogue stage fits");
@@ -109,15 +115,16 @@ conv_fwd_rows_kernel(const ConvParams p)
         h_base[i] = ok ? n * p.sxn + cl * p.sxc + wc * p.sxw : 0;
         h_ok |= (ok ? 1u : 0u) << i;
     }
-    // ---- slab loader: thread -> (filter k, channel c), the S taps of row r
+    // ---- slab loader: thread -> (filter k, channel c, taps sh*SH ... sh*SH + SH - 1) of row r
     const int sk = tid % TN;
-    const int sc = tid / TN;
+    const int sc = (tid / TN) % CB;
+    const int sh = tid / SROWS;
     const bool s_ok = n0 + sk < p.K;
     const int s_base = (s_ok ? n0 + sk : 0) * p.Kred;    // packed KCRS: filter row length C*R*S
 
     float hv[NH];
     uint32_t hv_ok = 0;                              // validity of the chunk in registers
-    float sv[S];
+    float sv[SH];
     const int ncb = p.C / CB;
     const int nch = ncb * p.R;
     auto load_chunk = [&](int ch) {
@@ -135,7 +142,7 @@ conv_fwd_rows_kernel(const ConvParams p)
         hv_ok = m;
         const int fo = s_base + ((c0 + sc) * p.R + r) * S;
 #pragma unroll
-        for (int s = 0; s < S; ++s) sv[s] = w[fo + s];
+        for (int i = 0; i < SH; ++i) sv[i] = w[fo + min(sh * SH + i, S - 1)];
     };
     auto store_chunk = [&](int buf) {
         float* dst = smem + buf * BUF;
@@ -145,7 +152,10 @@ conv_fwd_rows_kernel(const ConvParams p)
             if (HALO % NT == 0 || e < HALO) dst[e] = (hv_ok >> i) & 1u ? hv[i] : 0.0f;
         }
 #pragma unroll
-        for (int s = 0; s < S; ++s) dst[HALO + (s * CB + sc) * TN + sk] = s_ok ? sv[s] : 0.0f;
+        for (int i = 0; i < SH; ++i) {
+            const int s = sh * SH + i;
+            if (SPLIT * SH == S || s < S) dst[HALO + (s * CB + sc) * TN + sk] = s_ok ? sv[i] : 0.0f;
+        }
     };
 
     // ---- per-lane operand bases (floats)
@@ -223,13 +233,14 @@ conv_fwd_rows_kernel(const ConvParams p)
 
 // ------------------------------------------------------------------ one input channel
 //
-// The same streaming for a single input channel (the speech network's first
-// layer: 32 filters of 41 x 11, stride 2, on 161 x 700): with no channel
-// pair to give the MFMA's two lane groups, they take adjacent taps (s, s+1)
-// of a filter row (S rounded up to SP = S + 1, the extra tap zero), and a
-// chunk is RB filter rows, so that it holds RB * SP / 2 steps.  The chunk
-// stages, per filter row j and output-row slot, one input row of WP columns;
-// the operand of (slot, q) at (j, s) is halo[j][slot][q*v + s].
+// The same streaming for one to four input channels (the speech network's
+// first layer: 32 filters of 41 x 11, stride 2, on one channel; Overfeat's:
+// 96 filters of 3 x 11 x 11, stride 4): with no channel pair to give the
+// MFMA's two lane groups, they take adjacent taps (s, s+1) of a filter row
+// (S rounded up to SP = S + 1, the extra tap zero), and a chunk is one
+// channel and RB filter rows, so that it holds RB * SP / 2 steps.  The chunk
+// stages, per filter row j and output-row slot, one input row of WP
+// columns; the operand of (slot, q) at (j, s) is halo[j][slot][q*v + s].
 template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int RB, int NSL, int WP>
 __global__ void __launch_bounds__(256)
 conv_fwd_rows1_kernel(const ConvParams p)
@@ -254,9 +265,9 @@ conv_fwd_rows1_kernel(const ConvParams p)
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
     static_assert(NH <= 32 && NS <= 32, "validity masks");
     static_assert(2 * BUF * 4 <= 160 * 1024, "two chunk buffers fit the LDS");
-    static_assert(4 * BM * (BM + 1) <= 2 * BUF, "epilogue stage fits");
+    constexpr int SMEM = 2 * BUF > 4 * BM * (BM + 1) ? 2 * BUF : 4 * BM * (BM + 1);   // chunk buffers / epilogue stage
 
-    __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
+    __shared__ __attribute__((aligned(16))) float smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -298,7 +309,7 @@ conv_fwd_rows1_kernel(const ConvParams p)
         const int wc = col - p.pad_left;
         const bool ok = e < HALO && orow < nrows && (unsigned)wc < (unsigned)p.W;
         h_row[i] = pp * p.u - p.pad_top + j;
-        h_base[i] = ok ? n * p.sxn + wc * p.sxw : 0;
+        h_base[i] = ok ? n * p.sxn + wc * p.sxw : 0;     // channel added per chunk
         h_ok |= (ok ? 1u : 0u) << i;
     }
     // ---- slab loader: element e = (filter row j, tap s, filter k), k fastest
@@ -312,21 +323,24 @@ conv_fwd_rows1_kernel(const ConvParams p)
         const int ss = rem / TN;
         const int k = rem - ss * TN;
         const bool ok = e < SLAB && ss < S && n0 + k < p.K;
-        s_off[i] = ok ? (n0 + k) * p.Kred + j * S + ss : 0;   // packed K,1,R,S; row r0 added per chunk
+        s_off[i] = ok ? (n0 + k) * p.Kred + j * S + ss : 0;   // packed K,C,R,S; (c, r0) added per chunk
         s_ok0 |= (ok ? 1u : 0u) << i;
     }
 
     float hv[NH], sv[NS];
     uint32_t hv_ok = 0, sv_ok = 0;
-    const int nch = (p.R + RB - 1) / RB;
+    const int nrb = (p.R + RB - 1) / RB;
+    const int nch = p.C * nrb;                       // chunk = (filter row block, channel), channel fastest
     auto load_chunk = [&](int ch) {
-        const int r0 = ch * RB;
+        const int rb = ch / p.C;
+        const int c = ch - rb * p.C;
+        const int r0 = rb * RB;
         uint32_t m = 0;
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
             const int h = h_row[i] + r0;
             const bool ok = ((h_ok >> i) & 1u) && (unsigned)h < (unsigned)p.H;
-            hv[i] = x[ok ? h_base[i] + h * p.sxh : 0];
+            hv[i] = x[ok ? h_base[i] + c * p.sxc + h * p.sxh : 0];
             m |= (ok ? 1u : 0u) << i;
         }
         hv_ok = m;
@@ -336,7 +350,7 @@ conv_fwd_rows1_kernel(const ConvParams p)
             const int e = tid + NT * i;
             const int j = e / (SP * TN);
             const bool ok = ((s_ok0 >> i) & 1u) && r0 + j < p.R;
-            sv[i] = w[ok ? s_off[i] + r0 * S : 0];
+            sv[i] = w[ok ? s_off[i] + (c * p.R + r0) * S : 0];
             ms |= (ok ? 1u : 0u) << i;
         }
         sv_ok = ms;
@@ -466,7 +480,10 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
     constexpr int NH = (HALO + NT - 1) / NT;
     constexpr int STEPS = S * (CB / G);
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
-    static_assert(CB % G == 0 && TN * CB == NT, "one (output channel, dy channel) slab row per thread");
+    constexpr int SROWS = TN * CB;                   // slab rows (output channel, dy channel) of S taps
+    constexpr int SPLIT = NT / SROWS;                // threads sharing a slab row
+    constexpr int SH = (S + SPLIT - 1) / SPLIT;      // taps per thread
+    static_assert(CB % G == 0 && NT % SROWS == 0, "whole slab rows per thread group");
     static_assert(NH <= 32, "halo validity mask");
     static_assert(2 * BUF * 4 <= 160 * 1024, "two chunk buffers fit the LDS");
     static_assert(4 * BM * (BM + 1) <= 2 * BUF, "epilogue stage fits");
@@ -520,15 +537,16 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
         h_base[i] = ok ? n * p.sxn + cl * p.sxc + qc * p.sxw : 0;
         h_ok |= (ok ? 1u : 0u) << i;
     }
-    // ---- slab loader: thread -> (output channel c, dy channel k), the S taps of row a + u*i
+    // ---- slab loader: thread -> (output channel c, dy channel k, taps sh*SH ...) of row a + u*i
     const int sk = tid % TN;                          // output channel within the tile
-    const int sc = tid / TN;                          // dy channel within the block
+    const int sc = (tid / TN) % CB;                   // dy channel within the block
+    const int sh = tid / SROWS;
     const bool s_ok = n0 + sk < p.K;
     const int RS = p.R * S;                           // p.R here: the filter's full row count
 
     float hv[NH];
     uint32_t hv_ok = 0;
-    float sv[S];
+    float sv[SH];
     const int ncb = p.C / CB;
     const int nri = p.Kred;                           // tap rows of the phase
     const int nch = ncb * nri;
@@ -547,7 +565,7 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
         // F[k0 + sc][c][a + u*i][0 .. S-1], packed K,C,R,S
         const int fo = ((k0 + sc) * p.K + (s_ok ? n0 + sk : 0)) * RS + (a + p.u * i) * S;
 #pragma unroll
-        for (int s = 0; s < S; ++s) sv[s] = f[fo + s];
+        for (int j = 0; j < SH; ++j) sv[j] = f[fo + min(sh * SH + j, S - 1)];
     };
     auto store_chunk = [&](int buf) {
         float* dst = smem + buf * BUF;
@@ -557,7 +575,10 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
             if (HALO % NT == 0 || ee < HALO) dst[ee] = (hv_ok >> e) & 1u ? hv[e] : 0.0f;
         }
 #pragma unroll
-        for (int s = 0; s < S; ++s) dst[HALO + (s * CB + sc) * TN + sk] = s_ok ? sv[s] : 0.0f;
+        for (int j = 0; j < SH; ++j) {
+            const int s = sh * SH + j;
+            if (SPLIT * SH == S || s < S) dst[HALO + (s * CB + sc) * TN + sk] = s_ok ? sv[j] : 0.0f;
+        }
     };
 
     const int wm = wave / WAVES_N;
@@ -707,32 +728,41 @@ static hipError_t launch_rows_variant(const ConvParams& p0, hipStream_t stream)
 
 //        name                policy TM  TN  waves  S  CB NSL WP
 #define MICONV_ROWS_VARIANTS(X)                        \
-    X(ROWS_F32_S11_256x32, 256, 32, 4, 1, 11, 8, 2, 368)
+    X(ROWS_F32_S11_256x32, 256, 32, 4, 1, 11, 4, 2, 368)
 
-// one input channel: S = 11 taps as 6 pairs, 4 filter rows per chunk, two
-// output-row slots of 712 staged columns ((Q - 1) * v + 12 <= 712)
-constexpr int kRows1TM = 256, kRows1TN = 32, kRows1S = 11, kRows1RB = 4, kRows1WP = 712;
+// one to four input channels: S = 11 taps as 6 pairs, one filter row per
+// chunk (14-18 KB of LDS, at most 116 registers a lane: four or more
+// blocks a CU; four filter rows, two blocks a CU, took 1.3-1.4x as long);
+// two output-row slots of 712 staged columns (a 256-position tile
+// within two output rows: Q >= 256), or six of 232 (Q >= 51, as Overfeat
+// layer 1's 56); (Q - 1) * v + 12 <= the staged width
+constexpr int kRows1TM = 256, kRows1TN = 32, kRows1S = 11, kRows1RB = 1;
 
-static bool rows1_fits(const ConvParams& p)
+template <int NSL, int WP>
+static bool rows1_variant_fits(const ConvParams& p)
 {
-    return p.C == 1 && p.S == kRows1S && p.Q >= kRows1TM && (int64_t)(p.Q - 1) * p.v + kRows1S + 1 <= kRows1WP;
+    const int spanned = (kRows1TM - 1 + p.Q - 1) / p.Q + 1;    // output rows a tile can touch
+    return p.C >= 1 && p.C <= 4 && p.S == kRows1S && spanned <= NSL &&
+           (int64_t)(p.Q - 1) * p.v + kRows1S + 1 <= WP;
 }
 
-static hipError_t launch_rows1(const ConvParams& p0, hipStream_t stream)
+template <int NSL, int WP>
+static hipError_t launch_rows1_variant(const ConvParams& p0, hipStream_t stream)
 {
-    if (!rows1_fits(p0)) return hipErrorInvalidValue;
+    if (!rows1_variant_fits<NSL, WP>(p0)) return hipErrorInvalidValue;
     ConvParams p = p0;
     p.m_tiles = (p.M + kRows1TM - 1) / kRows1TM;
     p.n_tiles = (p.K + kRows1TN - 1) / kRows1TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
-    hipLaunchKernelGGL((conv_fwd_rows1_kernel<kRows1TM, kRows1TN, 4, 1, kRows1S, kRows1RB, 2, kRows1WP>), grid,
+    hipLaunchKernelGGL((conv_fwd_rows1_kernel<kRows1TM, kRows1TN, 4, 1, kRows1S, kRows1RB, NSL, WP>), grid,
                        dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 bool rows_fits(Variant v, const ConvParams& p)
 {
-    if (v == Variant::ROWS1_F32_S11_256x32) return rows1_fits(p);
+    if (v == Variant::ROWS1_F32_S11_256x32) return rows1_variant_fits<2, 712>(p);
+    if (v == Variant::ROWS1N6_F32_S11_256x32) return rows1_variant_fits<6, 232>(p);
     switch (v) {
 #define X(name, tm, tn, wmm, wnn, s, cb, nsl, wp) \
     case Variant::name: return rows_variant_fits<tm, tn, wmm, wnn, s, cb, nsl, wp>(p);
@@ -744,7 +774,8 @@ bool rows_fits(Variant v, const ConvParams& p)
 
 hipError_t launch_rows(Variant v, const ConvParams& p, hipStream_t stream)
 {
-    if (v == Variant::ROWS1_F32_S11_256x32) return launch_rows1(p, stream);
+    if (v == Variant::ROWS1_F32_S11_256x32) return launch_rows1_variant<2, 712>(p, stream);
+    if (v == Variant::ROWS1N6_F32_S11_256x32) return launch_rows1_variant<6, 232>(p, stream);
     switch (v) {
 #define X(name, tm, tn, wmm, wnn, s, cb, nsl, wp) \
     case Variant::name: return launch_rows_variant<tm, tn, wmm, wnn, s, cb, nsl, wp>(p, stream);

@@ -13,6 +13,7 @@ enum class Variant : int {
     DG_ROWS,             // ... onto one channel, dy rows staged in LDS (same file)
     ROWS_F32_S11_256x32, // forward pass, reduction streamed by filter row (conv_fwd_rows.hip)
     ROWS1_F32_S11_256x32, // ... onto one input channel, tap pairs (same file)
+    ROWS1N6_F32_S11_256x32, // ... six output-row slots (short output rows)
     DG_ROWS_MFMA,        // data gradient, the same streaming per stride phase (conv_fwd_rows.hip)
     MFMA_F32_128x128,
     MFMA_F32_128x64,

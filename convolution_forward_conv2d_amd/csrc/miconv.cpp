@@ -148,6 +148,7 @@ const Candidate kDgRows = {Variant::DG_ROWS, 0, 0, "rows"};
 const Candidate kRowsF32 = {Variant::ROWS_F32_S11_256x32, 256, 32, "rows_f32_s11_256x32"};
 const Candidate kDgRowsMfma = {Variant::DG_ROWS_MFMA, 256, 32, "rows_mfma_f32_s11_256x32"};
 const Candidate kRows1F32 = {Variant::ROWS1_F32_S11_256x32, 256, 32, "rows1_f32_s11_256x32"};
+const Candidate kRows1N6F32 = {Variant::ROWS1N6_F32_S11_256x32, 256, 32, "rows1n6_f32_s11_256x32"};
 // Filter-gradient kernels: the gather kernel (conv_bwd_filter.hip, any
 // geometry), the LDS-halo kernel (conv_bwd_filter_halo.hip: stride 1, fixed
 // R x S, Q + S - 1 <= the row pitch wph) and the kernel that splits the
@@ -509,9 +510,12 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
     // reduction by filter row (speech layer 2: 2.9 ms through the gather kernel)
     const bool unblocked = !blocked(xd) && !blocked(wd) && !blocked(yd);
     const bool rows_ok = pl.dt == DType::F32 && unblocked && miconv::rows_fits(kRowsF32.v, p);
-    // ... and onto one input channel with adjacent taps paired (speech layer 1)
+    // ... and onto 1-4 input channels with adjacent taps paired (speech
+    // layer 1: two output-row slots; Overfeat layer 1: six)
     const bool rows1_ok = pl.dt == DType::F32 && unblocked && miconv::rows_fits(kRows1F32.v, p);
+    const bool rows1n6_ok = pl.dt == DType::F32 && unblocked && miconv::rows_fits(kRows1N6F32.v, p);
     if (!is_halo(pl.cand.v) && rows_ok) pl.cand = kRowsF32;
+    if (!is_halo(pl.cand.v) && rows1n6_ok) pl.cand = kRows1N6F32;
     if (!is_halo(pl.cand.v) && rows1_ok) pl.cand = kRows1F32;
 
     pl.tap = prefer_tap(pl.dt, p.C);
@@ -537,13 +541,17 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
             if (halo_forced) {
             } else if (strcmp(force, kDirect.name) == 0) {
                 pl.cand = kDirect;
-            } else if (strcmp(force, kRowsF32.name) == 0 || strcmp(force, kRows1F32.name) == 0) {
-                const bool one = strcmp(force, kRows1F32.name) == 0;
-                if (!(one ? rows1_ok : rows_ok)) {
+            } else if (strcmp(force, kRowsF32.name) == 0 || strcmp(force, kRows1F32.name) == 0 ||
+                       strcmp(force, kRows1N6F32.name) == 0) {
+                const Candidate& c = strcmp(force, kRowsF32.name) == 0    ? kRowsF32
+                                     : strcmp(force, kRows1F32.name) == 0 ? kRows1F32
+                                                                          : kRows1N6F32;
+                const bool ok = c.v == kRowsF32.v ? rows_ok : c.v == kRows1F32.v ? rows1_ok : rows1n6_ok;
+                if (!ok) {
                     pl.status = MIC_STATUS_NOT_SUPPORTED;
                     return pl;
                 }
-                pl.cand = one ? kRows1F32 : kRowsF32;
+                pl.cand = c;
             } else {
                 const Candidate* list;
                 int count;
@@ -573,7 +581,7 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
     const size_t ie = dtype_size(xd->dtype);
     pl.bvec = ((Kred * (int64_t)ie) % 16 == 0) && ((uintptr_t)w % 16 == 0) && !blocked(wd);
     const bool gather = pl.cand.v != Variant::DIRECT && pl.cand.v != kRowsF32.v && pl.cand.v != kRows1F32.v &&
-                        !is_halo(pl.cand.v);
+                        pl.cand.v != kRows1N6F32.v && !is_halo(pl.cand.v);
     if (!gather) pl.tap = false;
     if (gather && (blocked(xd) || blocked(wd))) {
         // Tap order reads a chunk of TK channels at one tap: with blocked x or
@@ -1500,7 +1508,7 @@ mic_status mic_conv_forward(mic_handle handle, double alpha, mic_tensor_desc x_d
     hipError_t err;
     if (pl.cand.v == Variant::DIRECT)
         err = miconv::launch_direct(pl.dt, pl.p, handle->stream);
-    else if (pl.cand.v == kRowsF32.v || pl.cand.v == kRows1F32.v)
+    else if (pl.cand.v == kRowsF32.v || pl.cand.v == kRows1F32.v || pl.cand.v == kRows1N6F32.v)
         err = miconv::launch_rows(pl.cand.v, pl.p, handle->stream);
     else if (is_halo(pl.cand.v))
         err = miconv::launch_halo(pl.cand.v, pl.p, false, handle->stream);

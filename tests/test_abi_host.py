@@ -137,7 +137,7 @@ def test_kernel_choice_host_only():
         assert names[name].startswith(("halo_f32_3x3_", "halo_f32x16_3x3_")), (name, names[name])
     assert names["alexnet_conv2"].startswith("halo_f32_5x5_")
     assert names["overfeat_l2"].startswith("halo_f32_5x5_")
-    assert names["overfeat_l1"].startswith("mfma_f32_")
+    assert names["overfeat_l1"] == "rows1n6_f32_s11_256x32"      # 3 channels, 56-wide output rows
     # 21x11 filters, 32 filters, Q = 350 >= the 256-position tile: reduction streamed by filter row
     assert names["speech_l2"] == "rows_f32_s11_256x32"
     assert names["speech_l1"] == "rows1_f32_s11_256x32"         # one channel: adjacent taps paired

@@ -38,8 +38,8 @@ VARIANTS = {
 for _dt in VARIANTS:
     VARIANTS[_dt] += [v + "_tap" for v in VARIANTS[_dt] if v.startswith("mfma_")]
 # the reduction streamed by filter row: 11-wide filters, 8-channel blocks, Q >= 256
-VARIANTS["f32"] += ["rows_f32_s11_256x32", "rows1_f32_s11_256x32"]
-_MAY_REFUSE = ("halo_", "rows_", "rows1_")
+VARIANTS["f32"] += ["rows_f32_s11_256x32", "rows1_f32_s11_256x32", "rows1n6_f32_s11_256x32"]
+_MAY_REFUSE = ("halo_", "rows_", "rows1_", "rows1n6_")
 # halo variants only take the shapes they were built for (the library answers
 # NOT_SUPPORTED otherwise); every one of them must run on at least one shape
 _ran = set()
@@ -105,6 +105,12 @@ FWD_SHAPES = SMALL_SHAPES + [
     # sides and K = 40 (a ragged filter tile); 7 filter rows (the last chunk of 4 half empty)
     dict(name="rows1_41x11", N=1, C=1, Hh=61, Ww=530, K=40, R=41, S=11, stride=(2, 2), pads=(20, 20, 0, 10)),
     dict(name="rows1_7x11", N=2, C=1, Hh=15, Ww=270, K=32, R=7, S=11, stride=(1, 1), pads=(3, 3, 5, 5)),
+    # 1-4 channels, short output rows (six slots): Overfeat-like 11x11 / 4 on 3 channels with K = 96,
+    # and 2 channels, 9 filter rows, padding on every side
+    dict(name="rows1n6_c3_s4", N=2, C=3, Hh=71, Ww=231, K=96, R=11, S=11, stride=(4, 4), pads=(0, 0, 0, 0)),
+    dict(name="rows1n6_c2", N=2, C=2, Hh=20, Ww=60, K=40, R=9, S=11, stride=(1, 1), pads=(2, 3, 4, 1)),
+    # odd stride 3
+    dict(name="rows1n6_c3_s3", N=2, C=3, Hh=40, Ww=160, K=20, R=5, S=11, stride=(3, 3), pads=(1, 1, 2, 2)),
 ]
 
 
