@@ -16,7 +16,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["miconv.cpp", "conv_fwd_mfma.hip", "conv_fwd_halo.hip", "conv_fwd_halo_bf16.hip",
            "conv_fwd_direct.hip", "conv_bwd_data.hip", "conv_bwd_filter.hip",
            "pool_fwd.hip", "brgemm.hip", "conv_bwd_filter_halo.hip",
-           "conv_bwd_filter_split.hip", "conv_bwd_data_phase.hip", "conv_fwd_rows.hip"]
+           "conv_bwd_filter_split.hip", "conv_bwd_data_phase.hip", "conv_fwd_rows.hip",
+           "conv_bwd_data_subpixel.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -15,6 +15,7 @@ enum class Variant : int {
     ROWS1_F32_S11_256x32, // ... onto one input channel, tap pairs (same file)
     ROWS1N6_F32_S11_256x32, // ... six output-row slots (short output rows)
     DG_ROWS_MFMA,        // data gradient, the same streaming per stride phase (conv_fwd_rows.hip)
+    DG_SUBPIXEL,         // strided data gradient as a stride-1 GEMM onto the stride phases (conv_bwd_data_subpixel.hip)
     MFMA_F32_128x128,
     MFMA_F32_128x64,
     MFMA_F32_256x32,
@@ -127,5 +128,7 @@ bool rows_fits(Variant v, const ConvParams& p);
 hipError_t launch_rows(Variant v, const ConvParams& p, hipStream_t stream);
 bool bwd_data_rows_mfma_fits(const ConvParams& p);
 hipError_t launch_bwd_data_rows_mfma(const ConvParams& p, hipStream_t stream);
+bool bwd_data_subpixel_fits(const ConvParams& p);
+hipError_t launch_bwd_data_subpixel(DType dt, const ConvParams& p, hipStream_t stream);
 
 }  // namespace miconv

@@ -147,6 +147,7 @@ const Candidate kDgRows = {Variant::DG_ROWS, 0, 0, "rows"};
 // forward pass with the reduction streamed by filter row (conv_fwd_rows.hip)
 const Candidate kRowsF32 = {Variant::ROWS_F32_S11_256x32, 256, 32, "rows_f32_s11_256x32"};
 const Candidate kDgRowsMfma = {Variant::DG_ROWS_MFMA, 256, 32, "rows_mfma_f32_s11_256x32"};
+const Candidate kDgSubpixel = {Variant::DG_SUBPIXEL, 128, 64, "subpixel"};
 const Candidate kRows1F32 = {Variant::ROWS1_F32_S11_256x32, 256, 32, "rows1_f32_s11_256x32"};
 const Candidate kRows1N6F32 = {Variant::ROWS1N6_F32_S11_256x32, 256, 32, "rows1n6_f32_s11_256x32"};
 // Filter-gradient kernels: the gather kernel (conv_bwd_filter.hip, any
@@ -617,8 +618,10 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
 // dx <- alpha * dgrad(dy, w) + beta * dx.  The forward geometry is (dx, w,
 // conv); dy must have the forward output's dims.  Stride-1 problems of the
 // halo shapes (fp32, fp64) run as the forward pass of dy with the filter
-// transposed and flipped (conv_fwd_halo.hip, DG instances); everything else
-// takes the direct kernel (conv_bwd_data.hip).
+// transposed and flipped (conv_fwd_halo.hip, DG instances); strided ones as
+// a stride-1 GEMM over dy onto dx's stride phases (conv_bwd_data_subpixel.hip)
+// or one of the kernels below; the rest the gather kernel in data-gradient
+// mode or the direct kernel (conv_bwd_data.hip).
 Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, const void* dy,
                      const mic_filter_desc_st* wd, const void* w, const mic_conv_desc_st* cd,
                      const mic_tensor_desc_st* dxd, const void* dx, double alpha, double beta,
@@ -784,9 +787,32 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
         }
         const bool rows_mfma = forced_dgrad_name ? strcmp(forced_dgrad_name, kDgRowsMfma.name) == 0 && rows_mfma_ok
                                                  : rows_mfma_ok;
+        // a stride above 1 with at least 32 columns (channel, row phase,
+        // column phase): the stride-1 GEMM over dy onto dx's stride phases,
+        // which spends no multiply-adds off the stride grid (Overfeat layer 1,
+        // 3 channels at stride 4: 48 columns)
+        bool subpixel_ok = false;
+        if ((cd->u > 1 || cd->v > 1) && pl.dt != DType::BF16 && (int64_t)C * cd->u * cd->v >= 32) {
+            ConvParams q = p;
+            q.C = C;
+            q.H = H;
+            q.W = W;
+            q.K = k;
+            q.P = P;
+            q.Q = Q;
+            q.R = R;
+            q.S = S;
+            q.u = cd->u;
+            q.v = cd->v;
+            q.pad_top = pt;
+            q.pad_left = pl_;
+            subpixel_ok = miconv::bwd_data_subpixel_fits(q);
+        }
+        const bool subpixel = forced_dgrad_name ? strcmp(forced_dgrad_name, kDgSubpixel.name) == 0 && subpixel_ok
+                                                : subpixel_ok && !rows_mfma;
         const bool direct = forced_dgrad_name
-                                ? strcmp(forced_dgrad_name, kDirect.name) == 0 || phase || rows || rows_mfma
-                                : C < 16 || rows_mfma;
+                                ? strcmp(forced_dgrad_name, kDirect.name) == 0 || phase || rows || rows_mfma || subpixel
+                                : C < 16 || rows_mfma || subpixel;
         if (!direct) {
             p.C = k;
             p.K = C;
@@ -815,6 +841,7 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
             if (phase) pl.cand = kDgPhase;
             if (rows) pl.cand = kDgRows;
             if (rows_mfma) pl.cand = kDgRowsMfma;
+            if (subpixel) pl.cand = kDgSubpixel;
             p.C = C;
             p.H = H;
             p.W = W;
@@ -1533,6 +1560,8 @@ mic_status mic_conv_backward_data(mic_handle handle, double alpha, mic_filter_de
         err = miconv::launch_bwd_data_rows(pl.p, handle->stream);
     else if (pl.cand.v == Variant::DG_ROWS_MFMA)
         err = miconv::launch_bwd_data_rows_mfma(pl.p, handle->stream);
+    else if (pl.cand.v == Variant::DG_SUBPIXEL)
+        err = miconv::launch_bwd_data_subpixel(pl.dt, pl.p, handle->stream);
     else if (is_halo(pl.cand.v))
         err = miconv::launch_halo(pl.cand.v, pl.p, true, handle->stream);
     else

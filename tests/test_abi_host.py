@@ -265,14 +265,32 @@ def test_dgrad_kernel_choice_host_only():
         assert names[name].startswith("dgrad_halo_f"), (name, names[name])
     # onto 96 channels: the 96-wide tiles
     assert names["alexnet_conv2"] == "dgrad_halo_f32x16_5x5_128x96"
-    # strided layers and bf16 take the gather kernel in data-gradient mode; onto 3 channels
-    # the stride-phase kernel, onto 1 channel its row-staged form
+    # bf16 takes the gather kernel in data-gradient mode; strided onto 3 channels at stride 4
+    # (48 channel x phase columns) the stride-1 GEMM onto the stride phases, onto 1 channel
+    # (4 columns) the stride-phase kernel's row-staged form
     for name in ("prec_conv3_bf16_nchw", "prec_conv5_bf16_nhwc"):
         assert names[name].startswith("dgrad_mfma_"), (name, names[name])
     # 21x11 / stride (2, 1) onto 32 channels: the row-streamed kernel per stride phase
     assert names["speech_l2"] == "dgrad_rows_mfma_f32_s11_256x32"
-    assert names["overfeat_l1"] == "dgrad_phase"
+    assert names["overfeat_l1"] == "dgrad_subpixel"
     assert names["speech_l1"] == "dgrad_rows"
+
+
+def test_dgrad_subpixel_kernel_limits(monkeypatch):
+    """The stride-phase GEMM needs a stride above 1 and at least 32 (channel, row phase, column
+    phase) columns, fp32/fp64; automatic choice below the row-streamed kernel."""
+    def lay(C, u, v, dt="f32"):
+        return Layer("sp", 9, 1, 2, C, 20, 24, 8, 5, 5, (u, v), (1, 1, 1, 1), dt,
+                     workloads.U11, workloads.U11)
+    assert _dgrad_name(lay(8, 2, 2)) == "dgrad_subpixel"          # 32 columns
+    assert _dgrad_name(lay(3, 4, 4, "f64")) == "dgrad_subpixel"   # 48 columns
+    assert _dgrad_name(lay(16, 2, 1)) == "dgrad_subpixel"
+    assert _dgrad_name(lay(7, 2, 2)) != "dgrad_subpixel"          # 28 columns
+    monkeypatch.setenv("MIC_FORCE_DGRAD_VARIANT", "subpixel")
+    for bad in (lay(32, 1, 1), lay(7, 2, 2), lay(8, 2, 2, "bf16")):
+        with pytest.raises(mic.MicError) as e:
+            _dgrad_name(bad)
+        assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
 
 
 def test_dgrad_phase_kernel_limits(monkeypatch):

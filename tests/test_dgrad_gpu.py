@@ -39,7 +39,11 @@ DG_VARIANTS["f32"] += ["rows"]
 # the forward pass's row-streamed kernel per stride phase: horizontal stride 1, 11-wide
 # filters, dy channels in blocks of 8, dx rows >= 256 wide
 DG_VARIANTS["f32"] += ["rows_mfma_f32_s11_256x32"]
-_MAY_REFUSE = ("halo_", "phase", "rows")
+# the stride-1 GEMM over dy onto dx's stride phases: a stride above 1 and at least 32
+# (channel, row phase, column phase) columns (fp32, fp64)
+DG_VARIANTS["f32"] += ["subpixel"]
+DG_VARIANTS["f64"] += ["subpixel"]
+_MAY_REFUSE = ("halo_", "phase", "rows", "subpixel")
 # the gather kernel in data-gradient mode (any stride)
 DG_VARIANTS["f32"] += ["mfma_f32_128x128", "mfma_f32_128x64", "mfma_f32_64x128", "mfma_f32_256x32"]
 DG_VARIANTS["f64"] += ["mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64"]
@@ -65,6 +69,11 @@ SHAPES = SMALL_SHAPES + [
     dict(name="dg_rows_21x11", N=1, C=40, Hh=41, Ww=260, K=16, R=21, S=11, stride=(2, 1),
          pads=(10, 10, 0, 10)),
     dict(name="dg_rows_s3", N=2, C=16, Hh=20, Ww=270, K=8, R=7, S=11, stride=(3, 1), pads=(2, 1, 3, 7)),
+    # stride phases as GEMM columns: strides (2, 3) with 48 columns and uneven padding;
+    # strides (3, 2) with 120 columns (a ragged second column tile), 17 dy channels (a
+    # ragged channel block) and filters not a multiple of the stride
+    dict(name="dg_sub_c8_s2x3", N=2, C=8, Hh=21, Ww=19, K=40, R=5, S=3, stride=(2, 3), pads=(1, 2, 0, 2)),
+    dict(name="dg_sub_c20_s3x2", N=1, C=20, Hh=25, Ww=23, K=17, R=7, S=4, stride=(3, 2), pads=(3, 0, 1, 2)),
 ]
 
 
