@@ -157,7 +157,7 @@ const Candidate kRows1N6F32 = {Variant::ROWS1N6_F32_S11_256x32, 256, 32, "rows1n
 // small tiles, tensors under 2 GiB).  ns is the measured time of one tile
 // per reduction position (N*P*Q) on MI355X with per_cu workgroups resident
 // on a compute unit; the plan picks the least rounds * ns.
-enum class WgKind { GATHER, HALO, SPLIT };
+enum class WgKind { GATHER, HALO, SPLIT, ROWS };
 struct WgCandidate {
     Candidate c;
     DType dt;
@@ -188,6 +188,11 @@ const WgCandidate kWg[] = {
     {{Variant::WGS_F64_32x32, 32, 32, "wgs_f64_32x32"}, DType::F64, WgKind::SPLIT, 0, 0, 0, 28.0, 1},
     {{Variant::WGS_F64_16x16, 16, 16, "wgs_f64_16x16"}, DType::F64, WgKind::SPLIT, 0, 0, 0, 5.7, 1},
     {{Variant::WGS_BF16_32x32, 32, 32, "wgs_bf16_32x32"}, DType::BF16, WgKind::SPLIT, 0, 0, 0, 15.8, 2},
+    // first layers on the vector ALU: tiles of KT filters x S taps of one
+    // (c, r); ns here is the time of one output row per tile, the cost that
+    // time over Q (measured on MI355X: speech L1 770 us, Overfeat L1 855 us)
+    {{Variant::WGR_F32_S11_V2, 3, 11, "wgr_f32_s11_v2"}, DType::F32, WgKind::ROWS, 0, 0, 0, 298.0, 2},
+    {{Variant::WGR_F32_S11_V4, 7, 11, "wgr_f32_s11_v4"}, DType::F32, WgKind::ROWS, 0, 0, 0, 119.0, 2},
 };
 // the split kernel's loads run along the positions: with x or dy strided
 // along q (channels-last) they gather (measured 2.6x slower for fp64,
@@ -200,6 +205,8 @@ bool is_wgh(Variant v)
            v == Variant::WGH_F32_3x3_W16_64x96 || v == Variant::WGH_F32X16_3x3_W16 ||
            v == Variant::WGH_F32X16_5x5_W24 || v == Variant::WGH_F64_3x3_W16;
 }
+
+bool is_wgr(Variant v) { return v == Variant::WGR_F32_S11_V2 || v == Variant::WGR_F32_S11_V4; }
 
 bool is_wgs(Variant v)
 {
@@ -977,6 +984,8 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
             ok = wc.r == wd->r && wc.s == wd->s && cd->u == 1 && cd->v == 1 && Q + wc.s - 1 <= wc.wph;
         else if (wc.kind == WgKind::SPLIT)
             ok = split_fits;
+        else if (wc.kind == WgKind::ROWS)
+            ok = miconv::bwd_filter_rows_fits(wc.c.v, p);
         // 8-filter split tiles double the tile count at 1.5x the loads per
         // position: worth it only when 16x16 tiles leave most CUs idle
         // (measured: speech L1, 58 tiles, 4.7 -> 4.1 ms; Overfeat L1, 138
@@ -996,6 +1005,7 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
         const int64_t rounds = (tiles + slots - 1) / slots;
         double cost = (double)rounds * wc.ns;
         if (wc.kind == WgKind::SPLIT && !unit_q) cost *= split_strided_penalty(pl.dt);
+        if (wc.kind == WgKind::ROWS) cost /= Q;
         if (!found || cost < best) {
             best = cost;
             pl.cand = wc.c;
@@ -1591,6 +1601,7 @@ mic_status mic_conv_backward_filter(mic_handle handle, double alpha, mic_tensor_
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
     const hipError_t err = is_wgh(pl.cand.v)   ? miconv::launch_bwd_filter_halo(pl.cand.v, pl.p, handle->stream)
                            : is_wgs(pl.cand.v) ? miconv::launch_bwd_filter_split(pl.cand.v, pl.p, handle->stream)
+                           : is_wgr(pl.cand.v) ? miconv::launch_bwd_filter_rows(pl.cand.v, pl.p, handle->stream)
                                                : miconv::launch_bwd_filter(pl.cand.v, pl.p, handle->stream);
     return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
 }

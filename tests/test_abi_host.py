@@ -359,19 +359,39 @@ def _wgrad_name(lay, dts=None):
         _free(xd, wd, cd, yd)
 
 
+def test_wgrad_first_layer_kernel_limits(monkeypatch):
+    """The vector-ALU first-layer kernels take 11-wide fp32 filters at their column stride (2 or 4),
+    at most 384 (64) output columns, unit stride along w and q, left padding under 64; forced onto
+    anything else they answer NOT_SUPPORTED."""
+    def lay(S=11, v=2, W=150, layout="nchw", pl=0, dt="f32"):
+        return Layer("wr", 9, 1, 2, 2, 20, W, 6, 5, S, (2, v), (1, 1, pl, 0), dt,
+                     workloads.U11, workloads.U11, layout=layout)
+    monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", "wgr_f32_s11_v2")
+    assert _wgrad_name(lay()) == "wgr_f32_s11_v2"
+    assert _wgrad_name(lay(W=700, pl=63)) == "wgr_f32_s11_v2"          # Q = 377, pad 63
+    for bad in (lay(S=9), lay(v=4), lay(W=790), lay(layout="nhwc"), lay(pl=64), lay(dt="f64")):
+        with pytest.raises(mic.MicError) as e:
+            _wgrad_name(bad)
+        assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+    monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", "wgr_f32_s11_v4")
+    assert _wgrad_name(lay(v=4, W=260)) == "wgr_f32_s11_v4"            # Q = 63
+    with pytest.raises(mic.MicError):
+        _wgrad_name(lay(v=4, W=270))                                     # Q = 65
+
+
 def test_wgrad_kernel_choice_host_only():
     """The plan's cost model (rounds of tiles x measured time per tile) on the workload layers:
     the halo kernel for the stride-1 3x3 and 5x5 (pitch 24) layers, with 64x96 tiles where they
-    save a round (AlexNet conv4, Overfeat L3-L5), the split-reduction kernel where dw has few
-    tiles (first layers) or where its finer tiles round better (AlexNet conv2, the bf16 layers),
-    the gather kernel for channels-last bf16."""
+    save a round (AlexNet conv4, Overfeat L3-L5), the vector-ALU row-staged kernel for the strided
+    11-wide first layers, the split-reduction kernel where dw has few tiles or where its finer
+    tiles round better (AlexNet conv2, the bf16 layers), the gather kernel for channels-last bf16."""
     want = {"tiny": "wgs_f32_8x16",
             "alexnet_conv2": "wgs_f32_16x16", "alexnet_conv3": "wgh_f32x16_3x3_64x64",
             "alexnet_conv4": "wgh_f32_3x3_64x96", "alexnet_conv5": "wgh_f32x16_3x3_64x64",
-            "overfeat_l1": "wgs_f32_16x16", "overfeat_l2": "wgh_f32x16_5x5_w24_64x64",
+            "overfeat_l1": "wgr_f32_s11_v4", "overfeat_l2": "wgh_f32x16_5x5_w24_64x64",
             "overfeat_l3": "wgh_f32_3x3_64x96", "overfeat_l4": "wgh_f32_3x3_64x96",
             "overfeat_l5": "wgh_f32_3x3_64x96",
-            "speech_l1": "wgs_f32_8x16", "speech_l2": "wgs_f32_32x32"}
+            "speech_l1": "wgr_f32_s11_v2", "speech_l2": "wgs_f32_32x32"}
     for lay in workloads.ALL_LAYERS:
         name = _wgrad_name(lay)
         if lay.name in want:

@@ -37,8 +37,12 @@ WG_VARIANTS = {
     "f64": ["wg_f64_128x64", "wg_f64_64x64", "wgh_f64_3x3_64x64", "wgs_f64_32x32", "wgs_f64_16x16"],
     "bf16": ["wg_bf16_128x128", "wg_bf16_64x64", "wgs_bf16_32x32"],
 }
-# the halo variants (wgh_) take stride-1 layers of their filter size whose rows fit their pitch; the
-# library answers NOT_SUPPORTED for other shapes, and every variant must run on at least one shape
+# the first-layer kernels on the vector ALU (wgr_): 11-wide filter rows at column stride 2 or 4
+WG_VARIANTS["f32"] += ["wgr_f32_s11_v2", "wgr_f32_s11_v4"]
+# the halo variants (wgh_) take stride-1 layers of their filter size whose rows fit their pitch, the
+# wgr_ variants their stride and filter width; the library answers NOT_SUPPORTED for other shapes,
+# and every variant must run on at least one shape
+_MAY_REFUSE = ("wgh_", "wgr_")
 _ran = set()
 
 
@@ -72,6 +76,12 @@ def _out(lay, fill=float("nan")):
 # (32 x 231) is ragged against their 16- and 32-column tiles
 WG_SHAPES = SMALL_SHAPES + [
     dict(name="speech_like", N=2, C=1, Hh=41, Ww=60, K=32, R=21, S=11, stride=(2, 1), pads=(10, 10, 0, 10)),
+    # first layers at column stride 2 and 4 (11-wide filter rows): filter counts ragged against the
+    # 3- and 7-filter tiles, rows whose input row falls in the padding, a 367-wide output row
+    # spanning six 64-position groups
+    dict(name="wgr_s2", N=2, C=1, Hh=30, Ww=150, K=7, R=7, S=11, stride=(2, 2), pads=(3, 3, 0, 10)),
+    dict(name="wgr_s4_c3", N=2, C=3, Hh=31, Ww=70, K=10, R=5, S=11, stride=(4, 4), pads=(0, 1, 2, 0)),
+    dict(name="wgr_s2_wide", N=1, C=1, Hh=21, Ww=740, K=5, R=9, S=11, stride=(2, 2), pads=(4, 4, 1, 3)),
 ]
 
 
@@ -92,7 +102,7 @@ def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
         try:
             _run(lay, x, dy, dw)
         except mic.MicError as e:
-            if var.startswith("wgh_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+            if var.startswith(_MAY_REFUSE) and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
                 continue
             raise
         H.check(dtype, dw.double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (shape["name"], dtype, var),
@@ -173,10 +183,26 @@ def test_alpha_beta(dtype, geom, monkeypatch):
         try:
             _run(lay, x, dy, dw, alpha=0.5, beta=0.25)
         except mic.MicError as e:
-            if var.startswith("wgh_") and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
+            if var.startswith(_MAY_REFUSE) and e.status == mic.MIC_STATUS_NOT_SUPPORTED:
                 continue
             raise
         assert np.array_equal(dw.double().cpu().numpy(), 0.5 * acc + 0.25 * old), var
+
+
+@pytest.mark.parametrize("stride", [(2, 2), (1, 4)], ids=["s2", "s14"])
+def test_alpha_beta_first_layer_kernels(stride, monkeypatch):
+    """The vector-ALU first-layer kernels: y = alpha * sum + beta * y exactly on integer data."""
+    lay = _small("wgr_ab", 2, 2, 9, 80, 9, 3, 11, stride, (1, 1, 0, 3), "f32")
+    xi, _ = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    dyi = _dy(lay, (N, K, P, Q), integer=True)
+    acc, _ = oracle.conv2d_bwd_filter(xi, dyi, lay.w_shape, lay.stride, lay.padding)
+    old = gen.integers(97, acc.shape)
+    var = "wgr_f32_s11_v2" if stride[1] == 2 else "wgr_f32_s11_v4"
+    monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", var)
+    dw = torch.from_numpy(old).to(torch.float32).to(H.dev())
+    _run(lay, H.to_device(xi, "f32"), H.to_device(dyi, "f32"), dw, alpha=0.5, beta=0.25)
+    assert np.array_equal(dw.double().cpu().numpy(), 0.5 * acc + 0.25 * old), var
 
 
 def test_wgrad_error_statuses_on_device():
