@@ -25,6 +25,14 @@
 // of the work is useful.  Lane group g of an MFMA takes positions
 // [g * SEGP, (g + 1) * SEGP).
 //
+// QD > 0 (instances for a compile-time output width Q = QD, with PR a
+// multiple of G): lane group g takes the output rows g, g + G, ... of the
+// chunk and steps along their QD real columns only, so no step lands on a
+// padding column; step u of the group is row G * (u / QD) + g, column
+// u % QD, at the compile-time offset G * WPH * (u / QD) + u % QD from the
+// group's base g * WPH.  Half h takes steps [h * SEGH, (h + 1) * SEGH) and
+// runs its own unrolled copy of the steps.
+//
 // No workspace: the reduction is not split across workgroups.  The
 // epilogue stores dw (packed K,C,R,S) along j as conv_bwd_filter.hip does.
 //
@@ -55,7 +63,8 @@ __device__ __forceinline__ void unroll_for(F&& f)
 }
 }  // namespace
 
-template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WPH, int PR, int PLANE, int KS>
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WPH, int PR, int PLANE, int KS,
+          int QD>
 __global__ void __launch_bounds__(256 * KS)
 conv_bwd_filter_halo_kernel(const ConvParams p)
 {
@@ -72,8 +81,9 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     constexpr int FM = WM / BM;
     constexpr int FN = WN / BM;
     constexpr int NPOS = PR * WPH;                   // positions per chunk
-    constexpr int SEGP = NPOS / G;                   // MFMA steps per chunk
+    constexpr int SEGP = QD > 0 ? PR / G * QD : NPOS / G;   // MFMA steps per chunk
     constexpr int SEGH = SEGP / KS;                  // ... per half
+    static_assert(QD == 0 || (PR % G == 0 && QD + S - 1 <= WPH), "whole rows per lane group");
     constexpr int DYP = NPOS + 1;                    // DY row pitch (odd: rows fall on other banks)
     constexpr int HROWS = PR + R - 1;
     // A padding position's tap (q + s up to WPH + S - 2) reads up to S - 1
@@ -207,9 +217,11 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     const int lrow = lane % BM;
     const int lgrp = lane / BM;
     // half h takes steps [h * SEGH, (h + 1) * SEGH) of every lane group's segment
+    // (QD > 0: the group's first row; the half's steps are compile-time offsets)
+    const int pos_base = QD > 0 ? lgrp * WPH : lgrp * SEGP + half * SEGH;
     int a_base[FM];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) a_base[i] = (wm * WM + i * BM + lrow) * DYP + lgrp * SEGP + half * SEGH;
+    for (int i = 0; i < FM; ++i) a_base[i] = (wm * WM + i * BM + lrow) * DYP + pos_base;
     int b_base[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -217,7 +229,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         uint32_t c, rs, r, s;
         p.div_rs.divmod((uint32_t)col, c, rs);
         p.div_s.divmod(rs, r, s);
-        b_base[j] = DY_ELEMS + ((int)c - c_lo) * PLANE + (int)r * WPH + (int)s + lgrp * SEGP + half * SEGH;
+        b_base[j] = DY_ELEMS + ((int)c - c_lo) * PLANE + (int)r * WPH + (int)s + pos_base;
     }
 
     AccV acc[FM][FN];
@@ -232,16 +244,23 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         unroll_for<0, NL>([&](auto qc) { store_piece(qc, 0); });
         __syncthreads();
     }
-    for (int ch = 0; ch < nch; ++ch) {
-        const int cur = ch & 1;
-        set_chunk(ch + 1 < nch ? ch + 1 : ch);       // past the end: reload, written where nothing reads
-        const In* buf = reinterpret_cast<const In*>(smem + cur * BUF_BYTES);
+    // offset of step t of half H from the lane's base
+    auto step_off = [](auto hc, int t) constexpr {
+        constexpr int H = decltype(hc)::value;
+        if constexpr (QD > 0) {
+            const int u = H * SEGH + t;
+            return G * WPH * (u / QD) + u % QD;
+        } else {
+            return t;
+        }
+    };
+    auto run_steps = [&](auto hc, const In* buf, int cur) {
         // operands are read one step ahead of their MFMA
         In a[FM], b[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) a[i] = buf[a_base[i]];
+        for (int i = 0; i < FM; ++i) a[i] = buf[a_base[i] + step_off(hc, 0)];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) b[j] = buf[b_base[j]];
+        for (int j = 0; j < FN; ++j) b[j] = buf[b_base[j] + step_off(hc, 0)];
         unroll_for<0, SEGH>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             unroll_for<0, NL>([&](auto qc) {
@@ -250,9 +269,9 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
             In an[FM], bn[FN];
             if constexpr (t + 1 < SEGH) {
 #pragma unroll
-                for (int i = 0; i < FM; ++i) an[i] = buf[a_base[i] + t + 1];
+                for (int i = 0; i < FM; ++i) an[i] = buf[a_base[i] + step_off(hc, t + 1)];
 #pragma unroll
-                for (int j = 0; j < FN; ++j) bn[j] = buf[b_base[j] + t + 1];
+                for (int j = 0; j < FN; ++j) bn[j] = buf[b_base[j] + step_off(hc, t + 1)];
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -269,6 +288,15 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
                 for (int j = 0; j < FN; ++j) b[j] = bn[j];
             }
         });
+    };
+    for (int ch = 0; ch < nch; ++ch) {
+        const int cur = ch & 1;
+        set_chunk(ch + 1 < nch ? ch + 1 : ch);       // past the end: reload, written where nothing reads
+        const In* buf = reinterpret_cast<const In*>(smem + cur * BUF_BYTES);
+        if (QD == 0 || half == 0)
+            run_steps(std::integral_constant<int, 0>{}, buf, cur);
+        else
+            run_steps(std::integral_constant<int, 1>{}, buf, cur);
         __syncthreads();
     }
 
@@ -298,36 +326,40 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, p.M, wave, lane, half == 0);
 }
 
-template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WPH, int PR, int PLANE, int KS>
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WPH, int PR, int PLANE, int KS,
+          int QD>
 static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
 {
     ConvParams p = p0;
-    if (p.u != 1 || p.v != 1 || p.R != R || p.S != S || p.Q + S - 1 > WPH) return hipErrorInvalidValue;
+    if (p.u != 1 || p.v != 1 || p.R != R || p.S != S || p.Q + S - 1 > WPH || (QD > 0 && p.Q != QD))
+        return hipErrorInvalidValue;
     p.m_tiles = (p.M + TM - 1) / TM;
     p.n_tiles = (p.K + TN - 1) / TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
-    hipLaunchKernelGGL((conv_bwd_filter_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, WPH, PR, PLANE, KS>), grid,
-                       dim3(256 * KS), 0, stream, p);
+    hipLaunchKernelGGL((conv_bwd_filter_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, WPH, PR, PLANE, KS, QD>),
+                       grid, dim3(256 * KS), 0, stream, p);
     return hipGetLastError();
 }
 
 // row pitch WPH and plane pitch PLANE: the smallest with at most two-way
 // (fp64 three-way) bank conflicts on the halo reads, searched offline
-//        name                     policy   TM  TN  waves  R  S  WPH  PR  PLANE  KS
-#define MICONV_WGH_VARIANTS(X)                                           \
-    X(WGH_F32_3x3_W16, PolF32, 64, 64, 2, 2, 3, 3, 16, 13, 243, 2)       \
-    X(WGH_F32_5x5_W24, PolF32, 64, 64, 2, 2, 5, 5, 24, 7, 269, 2)        \
-    X(WGH_F32_5x5_W36, PolF32, 64, 64, 2, 2, 5, 5, 36, 7, 401, 2)        \
-    X(WGH_F32_3x3_W16_64x96, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 13, 247, 2) \
-    X(WGH_F32X16_3x3_W16, PolF32x16, 64, 64, 2, 2, 3, 3, 16, 13, 247, 2)     \
-    X(WGH_F32X16_5x5_W24, PolF32x16, 64, 64, 2, 2, 5, 5, 24, 7, 269, 2)      \
-    X(WGH_F64_3x3_W16, PolF64, 64, 64, 2, 2, 3, 3, 16, 7, 147, 2)
+// (QD: output rows of exactly QD columns, the steps along them only)
+//        name                     policy   TM  TN  waves  R  S  WPH  PR  PLANE  KS  QD
+#define MICONV_WGH_VARIANTS(X)                                              \
+    X(WGH_F32_3x3_W16, PolF32, 64, 64, 2, 2, 3, 3, 16, 13, 243, 2, 0)       \
+    X(WGH_F32_5x5_W24, PolF32, 64, 64, 2, 2, 5, 5, 24, 7, 269, 2, 0)        \
+    X(WGH_F32_5x5_W36, PolF32, 64, 64, 2, 2, 5, 5, 36, 7, 401, 2, 0)        \
+    X(WGH_F32_3x3_W16_64x96, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 13, 247, 2, 0) \
+    X(WGH_F32X16_3x3_W16, PolF32x16, 64, 64, 2, 2, 3, 3, 16, 13, 247, 2, 0)     \
+    X(WGH_F32X16_5x5_W24, PolF32x16, 64, 64, 2, 2, 5, 5, 24, 7, 269, 2, 0)      \
+    X(WGH_F64_3x3_W16, PolF64, 64, 64, 2, 2, 3, 3, 16, 7, 147, 2, 0)            \
+    X(WGH_F32_3x3_Q12_64x96, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 12, 247, 2, 12)
 
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream)
 {
     switch (v) {
-#define X(name, pol, tm, tn, wmm, wnn, r, s, wph, pr, plane, ks) \
-    case Variant::name: return launch_wgh_variant<pol, tm, tn, wmm, wnn, r, s, wph, pr, plane, ks>(p, stream);
+#define X(name, pol, tm, tn, wmm, wnn, r, s, wph, pr, plane, ks, qd) \
+    case Variant::name: return launch_wgh_variant<pol, tm, tn, wmm, wnn, r, s, wph, pr, plane, ks, qd>(p, stream);
         MICONV_WGH_VARIANTS(X)
 #undef X
     default: return hipErrorInvalidValue;

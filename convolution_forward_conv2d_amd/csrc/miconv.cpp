@@ -165,6 +165,7 @@ struct WgCandidate {
     int r, s, wph;      // halo kernel only
     double ns;
     int per_cu;
+    int qd;             // halo kernel: output rows of exactly qd columns (0: any width)
 };
 const WgCandidate kWg[] = {
     {{Variant::WG_F32_128x128, 128, 128, "wg_f32_128x128"}, DType::F32, WgKind::GATHER, 0, 0, 0, 170.0, 1},
@@ -182,6 +183,7 @@ const WgCandidate kWg[] = {
     {{Variant::WGH_F32X16_3x3_W16, 64, 64, "wgh_f32x16_3x3_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 33.0, 1},
     {{Variant::WGH_F32X16_5x5_W24, 64, 64, "wgh_f32x16_5x5_w24_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 30.8, 1},
     {{Variant::WGH_F64_3x3_W16, 64, 64, "wgh_f64_3x3_64x64"}, DType::F64, WgKind::HALO, 3, 3, 16, 52.0, 1},
+    {{Variant::WGH_F32_3x3_Q12_64x96, 64, 96, "wgh_f32_3x3_q12_64x96"}, DType::F32, WgKind::HALO, 3, 3, 16, 30.5, 1, 12},
     {{Variant::WGS_F32_32x32, 32, 32, "wgs_f32_32x32"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 12.5, 1},
     {{Variant::WGS_F32_16x16, 16, 16, "wgs_f32_16x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 7.1, 2},
     {{Variant::WGS_F32_8x16, 8, 16, "wgs_f32_8x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 4.5, 2},
@@ -203,7 +205,7 @@ bool is_wgh(Variant v)
 {
     return v == Variant::WGH_F32_3x3_W16 || v == Variant::WGH_F32_5x5_W24 || v == Variant::WGH_F32_5x5_W36 ||
            v == Variant::WGH_F32_3x3_W16_64x96 || v == Variant::WGH_F32X16_3x3_W16 ||
-           v == Variant::WGH_F32X16_5x5_W24 || v == Variant::WGH_F64_3x3_W16;
+           v == Variant::WGH_F32X16_5x5_W24 || v == Variant::WGH_F64_3x3_W16 || v == Variant::WGH_F32_3x3_Q12_64x96;
 }
 
 bool is_wgr(Variant v) { return v == Variant::WGR_F32_S11_V2 || v == Variant::WGR_F32_S11_V4; }
@@ -981,7 +983,8 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
         if (force && strcmp(force, wc.c.name) != 0) continue;
         bool ok = true;
         if (wc.kind == WgKind::HALO)
-            ok = wc.r == wd->r && wc.s == wd->s && cd->u == 1 && cd->v == 1 && Q + wc.s - 1 <= wc.wph;
+            ok = wc.r == wd->r && wc.s == wd->s && cd->u == 1 && cd->v == 1 && Q + wc.s - 1 <= wc.wph &&
+                 (wc.qd == 0 || Q == wc.qd);
         else if (wc.kind == WgKind::SPLIT)
             ok = split_fits;
         else if (wc.kind == WgKind::ROWS)

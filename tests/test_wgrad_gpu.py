@@ -37,6 +37,8 @@ WG_VARIANTS = {
     "f64": ["wg_f64_128x64", "wg_f64_64x64", "wgh_f64_3x3_64x64", "wgs_f64_32x32", "wgs_f64_16x16"],
     "bf16": ["wg_bf16_128x128", "wg_bf16_64x64", "wgs_bf16_32x32"],
 }
+# the 3x3 halo kernel that steps along output rows of exactly 12 columns (no padding positions)
+WG_VARIANTS["f32"] += ["wgh_f32_3x3_q12_64x96"]
 # the first-layer kernels on the vector ALU (wgr_): 11-wide filter rows at column stride 2 or 4
 WG_VARIANTS["f32"] += ["wgr_f32_s11_v2", "wgr_f32_s11_v4"]
 # the halo variants (wgh_) take stride-1 layers of their filter size whose rows fit their pitch, the
@@ -82,6 +84,9 @@ WG_SHAPES = SMALL_SHAPES + [
     dict(name="wgr_s2", N=2, C=1, Hh=30, Ww=150, K=7, R=7, S=11, stride=(2, 2), pads=(3, 3, 0, 10)),
     dict(name="wgr_s4_c3", N=2, C=3, Hh=31, Ww=70, K=10, R=5, S=11, stride=(4, 4), pads=(0, 1, 2, 0)),
     dict(name="wgr_s2_wide", N=1, C=1, Hh=21, Ww=740, K=5, R=9, S=11, stride=(2, 2), pads=(4, 4, 1, 3)),
+    # 12-column output rows, 17 of them (a second, short row chunk per image), tiles ragged in k and in
+    # (c, r, s), for the 12-column halo instance
+    dict(name="wgh_q12_p17", N=2, C=20, Hh=17, Ww=12, K=70, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
 ]
 
 
