@@ -30,8 +30,8 @@
 // chunk and steps along their QD real columns only, so no step lands on a
 // padding column; step u of the group is row G * (u / QD) + g, column
 // u % QD, at the compile-time offset G * WPH * (u / QD) + u % QD from the
-// group's base g * WPH.  Half h takes steps [h * SEGH, (h + 1) * SEGH) and
-// runs its own unrolled copy of the steps.
+// group's base g * WPH.  Half 0 takes steps [0, SEGH), half 1 the rest
+// (one fewer when SEGP is odd), each in its own unrolled copy of the steps.
 //
 // No workspace: the reduction is not split across workgroups.  The
 // epilogue stores dw (packed K,C,R,S) along j as conv_bwd_filter.hip does.
@@ -82,7 +82,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     constexpr int FN = WN / BM;
     constexpr int NPOS = PR * WPH;                   // positions per chunk
     constexpr int SEGP = QD > 0 ? PR / G * QD : NPOS / G;   // MFMA steps per chunk
-    constexpr int SEGH = SEGP / KS;                  // ... per half
+    constexpr int SEGH = (SEGP + KS - 1) / KS;       // ... of half 0 (QD > 0: half 1 may take one fewer)
     static_assert(QD == 0 || (PR % G == 0 && QD + S - 1 <= WPH), "whole rows per lane group");
     constexpr int DYP = NPOS + 1;                    // DY row pitch (odd: rows fall on other banks)
     constexpr int HROWS = PR + R - 1;
@@ -107,7 +107,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     static_assert(Pol::V == 1, "scalar-operand MFMA policies only");
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
     static_assert(NPOS % G == 0 && NT % TM == 0 && WPH % TPK == 0, "loader shapes");
-    static_assert((KS == 1 || KS == 2) && SEGP % KS == 0, "one or two halves split the steps");
+    static_assert((KS == 1 || KS == 2) && (QD > 0 || SEGP % KS == 0), "one or two halves split the steps");
     static_assert(NDY <= 64 && NH <= 32, "validity masks");
     static_assert(2 * BUF_BYTES <= 160 * 1024, "two chunk buffers fit the LDS");
     static_assert((SEGP + DYP) * ES < 65536, "LDS immediate offsets");
@@ -255,19 +255,20 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         }
     };
     auto run_steps = [&](auto hc, const In* buf, int cur) {
+        constexpr int NSTEP = decltype(hc)::value == 0 ? SEGH : SEGP - SEGH;   // this half's steps
         // operands are read one step ahead of their MFMA
         In a[FM], b[FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) a[i] = buf[a_base[i] + step_off(hc, 0)];
 #pragma unroll
         for (int j = 0; j < FN; ++j) b[j] = buf[b_base[j] + step_off(hc, 0)];
-        unroll_for<0, SEGH>([&](auto tc) {
+        unroll_for<0, NSTEP>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             unroll_for<0, NL>([&](auto qc) {
-                if constexpr (decltype(qc)::value * (SEGH / 2) / NL == t) load_piece(qc);
+                if constexpr (decltype(qc)::value * (NSTEP / 2) / NL == t) load_piece(qc);
             });
             In an[FM], bn[FN];
-            if constexpr (t + 1 < SEGH) {
+            if constexpr (t + 1 < NSTEP) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i) an[i] = buf[a_base[i] + step_off(hc, t + 1)];
 #pragma unroll
@@ -278,10 +279,10 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = Pol::mfma_s(a[i], b[j], acc[i][j]);
             unroll_for<0, NL>([&](auto qc) {
-                if constexpr (SEGH / 2 + decltype(qc)::value * (SEGH - SEGH / 2) / NL == t) store_piece(qc, cur ^ 1);
+                if constexpr (NSTEP / 2 + decltype(qc)::value * (NSTEP - NSTEP / 2) / NL == t) store_piece(qc, cur ^ 1);
             });
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (t + 1 < SEGH) {
+            if constexpr (t + 1 < NSTEP) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i) a[i] = an[i];
 #pragma unroll
@@ -353,7 +354,9 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     X(WGH_F32X16_3x3_W16, PolF32x16, 64, 64, 2, 2, 3, 3, 16, 13, 247, 2, 0)     \
     X(WGH_F32X16_5x5_W24, PolF32x16, 64, 64, 2, 2, 5, 5, 24, 7, 269, 2, 0)      \
     X(WGH_F64_3x3_W16, PolF64, 64, 64, 2, 2, 3, 3, 16, 7, 147, 2, 0)            \
-    X(WGH_F32_3x3_Q12_64x96, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 12, 247, 2, 12)
+    X(WGH_F32_3x3_Q12_64x96, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 12, 247, 2, 12)     \
+    X(WGH_F32_3x3_Q13, PolF32, 64, 64, 2, 2, 3, 3, 16, 14, 259, 2, 13)                \
+    X(WGH_F32X16_5x5_Q20, PolF32x16, 64, 64, 2, 2, 5, 5, 24, 4, 197, 2, 20)
 
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream)
 {

@@ -60,6 +60,8 @@ enum class Variant : int {
     WGH_F32X16_5x5_W24,
     WGH_F64_3x3_W16,
     WGH_F32_3x3_Q12_64x96,   // ... stepping along output rows of exactly 12 columns
+    WGH_F32_3x3_Q13,         // ... 13 columns (32x32 blocks)
+    WGH_F32X16_5x5_Q20,      // ... 5x5, 20 columns
     WGS_F32_32x32,          // filter gradient, reduction split over waves (conv_bwd_filter_split.hip)
     WGS_F32_16x16,
     WGS_F32_8x16,
