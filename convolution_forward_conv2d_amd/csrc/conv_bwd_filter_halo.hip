@@ -356,7 +356,8 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     X(WGH_F64_3x3_W16, PolF64, 64, 64, 2, 2, 3, 3, 16, 7, 147, 2, 0)            \
     X(WGH_F32_3x3_Q12_64x96, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 12, 247, 2, 12)     \
     X(WGH_F32_3x3_Q13, PolF32, 64, 64, 2, 2, 3, 3, 16, 14, 259, 2, 13)                \
-    X(WGH_F32X16_5x5_Q20, PolF32x16, 64, 64, 2, 2, 5, 5, 24, 4, 197, 2, 20)
+    X(WGH_F32X16_5x5_Q20, PolF32x16, 64, 64, 2, 2, 5, 5, 24, 4, 197, 2, 20)          \
+    X(WGH_F32X16_5x5_Q27, PolF32x16, 64, 64, 2, 2, 5, 5, 32, 4, 261, 2, 27)
 
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream)
 {

@@ -62,6 +62,7 @@ enum class Variant : int {
     WGH_F32_3x3_Q12_64x96,   // ... stepping along output rows of exactly 12 columns
     WGH_F32_3x3_Q13,         // ... 13 columns (32x32 blocks)
     WGH_F32X16_5x5_Q20,      // ... 5x5, 20 columns
+    WGH_F32X16_5x5_Q27,      // ... 5x5, 27 columns
     WGS_F32_32x32,          // filter gradient, reduction split over waves (conv_bwd_filter_split.hip)
     WGS_F32_16x16,
     WGS_F32_8x16,

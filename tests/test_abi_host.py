@@ -383,12 +383,12 @@ def test_wgrad_kernel_choice_host_only():
     """The plan's cost model (rounds of tiles x measured time per tile) on the workload layers:
     the halo kernel for the stride-1 3x3 and 5x5 (pitch 24) layers, with 64x96 tiles where they
     save a round (AlexNet conv4; Overfeat L3-L5 in the form that steps along their 12-column output
-    rows only, as AlexNet conv3/conv5 and Overfeat L2 along 13 and 20), the vector-ALU row-staged
-    kernel for the strided
+    rows only, as AlexNet conv2/conv3/conv5 and Overfeat L2 along 27, 13 and 20), the vector-ALU
+    row-staged kernel for the strided
     11-wide first layers, the split-reduction kernel where dw has few tiles or where its finer
     tiles round better (AlexNet conv2, the bf16 layers), the gather kernel for channels-last bf16."""
     want = {"tiny": "wgs_f32_8x16",
-            "alexnet_conv2": "wgs_f32_16x16", "alexnet_conv3": "wgh_f32_3x3_q13_64x64",
+            "alexnet_conv2": "wgh_f32x16_5x5_q27_64x64", "alexnet_conv3": "wgh_f32_3x3_q13_64x64",
             "alexnet_conv4": "wgh_f32_3x3_64x96", "alexnet_conv5": "wgh_f32_3x3_q13_64x64",
             "overfeat_l1": "wgr_f32_s11_v4", "overfeat_l2": "wgh_f32x16_5x5_q20_64x64",
             "overfeat_l3": "wgh_f32_3x3_q12_64x96", "overfeat_l4": "wgh_f32_3x3_q12_64x96",

@@ -38,7 +38,8 @@ WG_VARIANTS = {
     "bf16": ["wg_bf16_128x128", "wg_bf16_64x64", "wgs_bf16_32x32"],
 }
 # the 3x3 halo kernel that steps along output rows of exactly 12 columns (no padding positions)
-WG_VARIANTS["f32"] += ["wgh_f32_3x3_q12_64x96", "wgh_f32_3x3_q13_64x64", "wgh_f32x16_5x5_q20_64x64"]
+WG_VARIANTS["f32"] += ["wgh_f32_3x3_q12_64x96", "wgh_f32_3x3_q13_64x64", "wgh_f32x16_5x5_q20_64x64",
+                       "wgh_f32x16_5x5_q27_64x64"]
 # the first-layer kernels on the vector ALU (wgr_): 11-wide filter rows at column stride 2 or 4
 WG_VARIANTS["f32"] += ["wgr_f32_s11_v2", "wgr_f32_s11_v4"]
 # the halo variants (wgh_) take stride-1 layers of their filter size whose rows fit their pitch, the
@@ -90,6 +91,7 @@ WG_SHAPES = SMALL_SHAPES + [
     # 13-column rows (14-row chunks: one row past P), and 5x5 filters on 20-column rows (4-row chunks)
     dict(name="wgh_q13", N=2, C=12, Hh=13, Ww=13, K=70, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
     dict(name="wgh_q20_5x5", N=2, C=7, Hh=22, Ww=24, K=40, R=5, S=5, stride=(1, 1), pads=(1, 1, 0, 0)),
+    dict(name="wgh_q27_5x5", N=2, C=5, Hh=10, Ww=27, K=70, R=5, S=5, stride=(1, 1), pads=(2, 2, 2, 2)),
 ]
 
 
