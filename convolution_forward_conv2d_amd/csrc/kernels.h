@@ -37,6 +37,7 @@ enum class Variant : int {
     HALO_F32x16_3x3_176x128,
     HALO_F32x16_3x3_144x128,
     HALO_F32x16_5x5_128x96,        // 96 filters per tile (K = 96, e.g. a data gradient onto 96 channels)
+    HALO_F32_5x5_128x96_C2,        // ... on 32x32 blocks, 2-channel chunks, four waves of 32 rows x 96
     HALO_F32x16_3x3_176x128_KS2,   // two halves split the reduction of one tile
     HALO_F32_3x3_128x128_KS2,
     HALO_F64_3x3_128x128,

@@ -272,6 +272,7 @@ const HaloCandidate kHalo[] = {
     {{Variant::HALO_F32x16_3x3_176x128, 176, 128, "halo_f32x16_3x3_176x128"}, DType::F32, 3, 3, 4, 16, 16, 0.9, 1},
     {{Variant::HALO_F32x16_3x3_144x128, 144, 128, "halo_f32x16_3x3_144x128"}, DType::F32, 3, 3, 4, 16, 16, 0.95, 1},
     {{Variant::HALO_F32x16_5x5_128x96, 128, 96, "halo_f32x16_5x5_128x96"}, DType::F32, 5, 5, 4, 32, 16, 0.85, 1},
+    {{Variant::HALO_F32_5x5_128x96_C2, 128, 96, "halo_f32_5x5_128x96_c2"}, DType::F32, 5, 5, 2, 32, 16, 0.98, 1},
     {{Variant::HALO_F32x16_3x3_176x128_KS2, 176, 128, "halo_f32x16_3x3_176x128_ks2"}, DType::F32, 3, 3, 4, 16, 16, 0.95, 2},
     {{Variant::HALO_F32_3x3_128x128_KS2, 128, 128, "halo_f32_3x3_128x128_ks2"}, DType::F32, 3, 3, 4, 16, 16, 0.9, 2},
     {{Variant::HALO_F64_3x3_128x128, 128, 128, "halo_f64_3x3_128x128"}, DType::F64, 3, 3, 4, 16, 16, 1.0, 1},

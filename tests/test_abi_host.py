@@ -264,7 +264,7 @@ def test_dgrad_kernel_choice_host_only():
                  "overfeat_l4", "overfeat_l5", "prec_conv3_f64_nchw", "prec_conv4_f64_nhwc"):
         assert names[name].startswith("dgrad_halo_f"), (name, names[name])
     # onto 96 channels: the 96-wide tiles
-    assert names["alexnet_conv2"] == "dgrad_halo_f32x16_5x5_128x96"
+    assert names["alexnet_conv2"] == "dgrad_halo_f32_5x5_128x96_c2"
     # bf16 takes the gather kernel in data-gradient mode; strided onto 3 channels at stride 4
     # (48 channel x phase columns) the stride-1 GEMM onto the stride phases, onto 1 channel
     # (4 columns) the stride-phase kernel's row-staged form
