@@ -42,6 +42,7 @@ enum class Variant : int {
     HALO_F32_3x3_128x128_KS2,
     HALO_F64_3x3_128x128,
     HALO_F64_3x3_64x64,
+    HALO_F64_3x3_128x64,           // fp64, 64 filters: two or three workgroups per CU
     HALO_BF16_3x3_128x128,  // bf16 halo kernel, channel-innermost LDS (conv_fwd_halo_bf16.hip)
     HALO_BF16_3x3_128x64,
     HALO_BF16_3x3_192x128,
