@@ -29,9 +29,19 @@
 // page, "Proposed Method"), double-buffered through LDS (maxDNN page,
 // "Proposed Method").
 //
+// DG = true computes the data gradient of a stride-1 convolution as the
+// forward pass of dy with the filter transposed (K <-> C) and flipped, as
+// the fp32 halo kernel does (the host passes that forward problem: x = dy,
+// y = dx, C and K exchanged).  Only the slab differs: a unit (dx channel n,
+// 8-channel group g) needs, per tap, the 8 values F[c0 + 8g + j, n, tap]
+// of 8 filters of the real problem, which lie C*R*S apart.  A thread loads
+// the 8 runs F[c0 + 8g + j, n, 0 .. RS-1] with 2-byte loads (consecutive
+// lanes take consecutive n, whose runs are adjacent in memory) and packs
+// tap RS-1-t of the 8 runs into slab tap t.
+//
 // Eligibility (checked by the host): R and S equal to the instance's; C a
 // multiple of 16; W + pad_left + pad_right <= WP; every tile's slot span
-// <= SL; w 16-byte aligned.
+// <= SL; w 16-byte aligned (the forward pass).
 #include <stdint.h>
 
 #include <type_traits>
@@ -48,7 +58,7 @@ namespace miconv {
 // filter n of a tile keeps group g of a tap at 16-byte unit 2n + (g ^ swz(n))
 __device__ __forceinline__ int slab_swz(int n) { return ((n >> 2) ^ (n >> 3)) & 1; }
 
-template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL, bool CVEC>
+template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL, bool CVEC, bool DG>
 __global__ void __launch_bounds__(256)
 conv_fwd_halo_bf16_kernel(const ConvParams p)
 {
@@ -70,6 +80,7 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
     constexpr int SU = 2 * TN;                    // slab units (filter, 8-channel group) per chunk
     constexpr int SUT = (SU + NT - 1) / NT;
     constexpr int NV = RS;                        // 16-byte vectors per slab unit: 8 channels x RS taps
+    constexpr int ND = DG ? 8 * RS : 1;           // DG: 2-byte loads per slab unit (8 runs of RS taps)
     constexpr int BUF_BYTES = HALO_BYTES + SLAB_BYTES;
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
     static_assert(BUF_BYTES % 16 == 0, "16-byte aligned buffers");
@@ -131,20 +142,26 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
         const int row = e >> 1;
         const int g = e & 1;
         const bool ok = e < SU && n0 + row < p.K;
-        s_off[i] = ok ? (n0 + row) * p.Kred + 8 * g * RS : 0;
+        // DG: F[c0 + 8g + j, n, t] at ((c0 + 8g + j) * K + n) * RS + t, K the
+        // channel count of dx here
+        if constexpr (DG)
+            s_off[i] = ok ? (8 * g * p.K + n0 + row) * RS : 0;
+        else
+            s_off[i] = ok ? (n0 + row) * p.Kred + 8 * g * RS : 0;
         s_ok |= (ok ? 1u : 0u) << i;
     }
 
     // registers of the chunk in flight
     uint32_t h_raw[CVEC ? 1 : HUT][8];
     u32x4 h_vec[CVEC ? HUT : 1];
-    u32x4 s_val[SUT][NV];
+    u32x4 s_val[SUT][DG ? 1 : NV];
+    uint16_t s_raw[SUT][ND];
 
     // A chunk moves global -> registers -> LDS in pieces: load piece q is
     // one global load (a 2-byte channel value or a 16-byte vector), store
     // piece q one 16-byte LDS write (a halo unit, or one tap of a slab unit).
     constexpr int NLH = CVEC ? HUT : 8 * HUT;    // halo load pieces
-    constexpr int NL = NLH + SUT * NV;           // load pieces per chunk
+    constexpr int NL = NLH + SUT * (DG ? ND : NV);   // load pieces per chunk
     constexpr int NS = HUT + SUT * RS;           // store pieces per chunk
 
     // Loads are unconditional (a unit outside the input or past K reads the
@@ -160,6 +177,10 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
                 const int i = q / 8, j = q % 8;
                 h_raw[i][j] = x[h_off[i] + x_chunk(c0) + j * p.sxc];
             }
+        } else if constexpr (DG) {
+            const int i = (q - NLH) / ND, v = (q - NLH) % ND;
+            const int j = v / RS, t = v % RS;
+            s_raw[i][v] = w[s_off[i] + (c0 + j) * p.K * RS + t];
         } else {
             const int i = (q - NLH) / NV, v = (q - NLH) % NV;
             s_val[i][v] = *reinterpret_cast<const u32x4*>(w + s_off[i] + c0 * RS + 8 * v);
@@ -198,19 +219,30 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
                 const int g = e & 1;
                 const bool ok = (s_ok >> i) & 1;
                 unsigned char* dst = hb + HALO_BYTES + 16 * (2 * row + (g ^ slab_swz(row)));
-                // element k of the unit's run is channel k / RS at tap k % RS:
-                // dword d of tap t holds channels 2d and 2d+1 of that tap
-                const uint32_t* words = reinterpret_cast<const uint32_t*>(&s_val[i][0]);
                 u32x4 out;
+                if constexpr (DG) {
+                    // slab tap t is tap RS-1-t of the runs (the filter flipped);
+                    // dword d holds runs 2d and 2d+1
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const int klo = (2 * d) * RS + t;
-                    const int khi = (2 * d + 1) * RS + t;
-                    const uint32_t wlo = words[klo >> 1];
-                    const uint32_t whi = words[khi >> 1];
-                    const uint32_t lo = (klo & 1) ? (wlo >> 16) : (wlo & 0xffffu);
-                    const uint32_t hi = (khi & 1) ? (whi & 0xffff0000u) : (whi << 16);
-                    out[d] = ok ? (lo | hi) : 0u;
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t lo = s_raw[i][(2 * d) * RS + RS - 1 - t];
+                        const uint32_t hi = s_raw[i][(2 * d + 1) * RS + RS - 1 - t];
+                        out[d] = ok ? (lo | (hi << 16)) : 0u;
+                    }
+                } else {
+                    // element k of the unit's run is channel k / RS at tap k % RS:
+                    // dword d of tap t holds channels 2d and 2d+1 of that tap
+                    const uint32_t* words = reinterpret_cast<const uint32_t*>(&s_val[i][0]);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const int klo = (2 * d) * RS + t;
+                        const int khi = (2 * d + 1) * RS + t;
+                        const uint32_t wlo = words[klo >> 1];
+                        const uint32_t whi = words[khi >> 1];
+                        const uint32_t lo = (klo & 1) ? (wlo >> 16) : (wlo & 0xffffu);
+                        const uint32_t hi = (khi & 1) ? (whi & 0xffff0000u) : (whi << 16);
+                        out[d] = ok ? (lo | hi) : 0u;
+                    }
                 }
                 *reinterpret_cast<u32x4*>(dst + t * TAP_BYTES) = out;
             }
@@ -321,8 +353,8 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
 
 // ------------------------------------------------------------------ instances and launch
 
-template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL>
-static hipError_t launch_halo_bf16_variant(const ConvParams& p0, hipStream_t stream)
+template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL, bool DGOK>
+static hipError_t launch_halo_bf16_variant(const ConvParams& p0, bool dgrad, hipStream_t stream)
 {
     ConvParams p = p0;
     if (p.wkb > 0) return hipErrorInvalidValue;          // packed KCRS filters only
@@ -334,30 +366,53 @@ static hipError_t launch_halo_bf16_variant(const ConvParams& p0, hipStream_t str
     // every group starts on a 16-byte boundary
     const bool cvec = p.sxc == 1 && (uintptr_t)p.x % 16 == 0 && p.sxn % 8 == 0 && p.sxh % 8 == 0 &&
                       p.sxw % 8 == 0 && p.sxcb % 8 == 0;
+    if (dgrad) {
+        if constexpr (DGOK) {
+            if (cvec)
+                hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, true, true>),
+                                   grid, dim3(256), 0, stream, p);
+            else
+                hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, false, true>),
+                                   grid, dim3(256), 0, stream, p);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     if (cvec)
-        hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, true>), grid,
+        hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, true, false>), grid,
                            dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, false>), grid,
+        hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, false, false>), grid,
                            dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-//        name                     TM   TN  waves  R  S  WP  SL
-#define MICONV_HALO_BF16_VARIANTS(X)                      \
-    X(HALO_BF16_3x3_128x128, 128, 128, 2, 2, 3, 3, 16, 16) \
-    X(HALO_BF16_3x3_128x64, 128, 64, 2, 2, 3, 3, 16, 16)   \
-    X(HALO_BF16_3x3_192x128, 192, 128, 2, 2, 3, 3, 16, 16)
+// (DG: the data-gradient slab holds 72 more registers: 64-filter tiles only)
+//        name                     TM   TN  waves  R  S  WP  SL  DG
+#define MICONV_HALO_BF16_VARIANTS(X)                              \
+    X(HALO_BF16_3x3_128x128, 128, 128, 2, 2, 3, 3, 16, 16, false)  \
+    X(HALO_BF16_3x3_128x64, 128, 64, 2, 2, 3, 3, 16, 16, true)     \
+    X(HALO_BF16_3x3_192x128, 192, 128, 2, 2, 3, 3, 16, 16, false)
 
-hipError_t launch_halo_bf16(Variant v, const ConvParams& p, hipStream_t stream)
+static hipError_t launch_halo_bf16_any(Variant v, const ConvParams& p, bool dgrad, hipStream_t stream)
 {
     switch (v) {
-#define X(name, tm, tn, wmm, wnn, r, s, wp, sl) \
-    case Variant::name: return launch_halo_bf16_variant<tm, tn, wmm, wnn, r, s, wp, sl>(p, stream);
+#define X(name, tm, tn, wmm, wnn, r, s, wp, sl, dg) \
+    case Variant::name: return launch_halo_bf16_variant<tm, tn, wmm, wnn, r, s, wp, sl, dg>(p, dgrad, stream);
         MICONV_HALO_BF16_VARIANTS(X)
 #undef X
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_halo_bf16(Variant v, const ConvParams& p, hipStream_t stream)
+{
+    return launch_halo_bf16_any(v, p, false, stream);
+}
+
+hipError_t launch_halo_bf16_dgrad(Variant v, const ConvParams& p, hipStream_t stream)
+{
+    return launch_halo_bf16_any(v, p, true, stream);
 }
 
 }  // namespace miconv

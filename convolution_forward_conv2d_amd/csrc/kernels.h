@@ -103,6 +103,7 @@ hipError_t launch_mfma(Variant v, const ConvParams& p, bool bvec, bool tap, bool
 // gradient (conv_fwd_halo.hip); fp32 and fp64 instances only.
 hipError_t launch_halo(Variant v, const ConvParams& p, bool dgrad, hipStream_t stream);
 hipError_t launch_halo_bf16(Variant v, const ConvParams& p, hipStream_t stream);
+hipError_t launch_halo_bf16_dgrad(Variant v, const ConvParams& p, hipStream_t stream);
 
 // Launch the plain direct kernel (one thread per output element).
 hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);

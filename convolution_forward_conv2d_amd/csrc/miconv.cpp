@@ -406,7 +406,9 @@ bool halo_eligible(const HaloCandidate& h, DType dt, const ConvParams& p, const 
     if (p.C % h.cb != 0) return false;
     // channel-blocked x: a chunk of h.cb channels must lie in one block
     if (p.div_xcb.d != miconv::kOneBlock && p.div_xcb.d % h.cb != 0) return false;
-    if (dgrad) return dt != DType::BF16;     // scalar filter loads: no alignment needed
+    // scalar filter loads: no alignment needed; bf16 only in the 64-filter
+    // instance and with packed KCRS filters
+    if (dgrad) return dt != DType::BF16 || (h.c.v == Variant::HALO_BF16_3x3_128x64 && p.wkb == 0);
     if (p.wkb > 0) {
         // blocked filters: 16-byte loads of kb-contiguous filters (fp32/fp64 kernel only)
         const int vk = dt == DType::F64 ? 2 : 4;
@@ -723,8 +725,7 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
     // on top and H-P+pad_top below (S-1-pad_left, W-Q+pad_left across), output
     // H x W
     const int pb2 = H - P + pt, pr2 = W - Q + pl_;
-    const bool halo_ok = cd->u == 1 && cd->v == 1 && pt <= R - 1 && pl_ <= S - 1 && pb2 >= 0 && pr2 >= 0 &&
-                         pl.dt != DType::BF16;
+    const bool halo_ok = cd->u == 1 && cd->v == 1 && pt <= R - 1 && pl_ <= S - 1 && pb2 >= 0 && pr2 >= 0;
     if (halo_ok) {
         ConvParams v = p;
         v.C = k;
@@ -1584,6 +1585,8 @@ mic_status mic_conv_backward_data(mic_handle handle, double alpha, mic_filter_de
         err = miconv::launch_bwd_data_rows_mfma(pl.p, handle->stream);
     else if (pl.cand.v == Variant::DG_SUBPIXEL)
         err = miconv::launch_bwd_data_subpixel(pl.dt, pl.p, handle->stream);
+    else if (is_halo(pl.cand.v) && pl.dt == DType::BF16)
+        err = miconv::launch_halo_bf16_dgrad(pl.cand.v, pl.p, handle->stream);
     else if (is_halo(pl.cand.v))
         err = miconv::launch_halo(pl.cand.v, pl.p, true, handle->stream);
     else
