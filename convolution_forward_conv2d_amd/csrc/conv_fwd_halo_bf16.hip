@@ -34,10 +34,11 @@
 // the fp32 halo kernel does (the host passes that forward problem: x = dy,
 // y = dx, C and K exchanged).  Only the slab differs: a unit (dx channel n,
 // 8-channel group g) needs, per tap, the 8 values F[c0 + 8g + j, n, tap]
-// of 8 filters of the real problem, which lie C*R*S apart.  A thread loads
-// the 8 runs F[c0 + 8g + j, n, 0 .. RS-1] with 2-byte loads (consecutive
-// lanes take consecutive n, whose runs are adjacent in memory) and packs
-// tap RS-1-t of the 8 runs into slab tap t.
+// of 8 filters of the real problem, which lie C*R*S apart.  Two threads
+// share a unit: each loads 4 of the runs F[c0 + 8g + j, n, 0 .. RS-1] with
+// 2-byte loads (consecutive lanes take consecutive n, whose runs are
+// adjacent in memory) and packs tap RS-1-t of its runs into 8 bytes of slab
+// tap t.
 //
 // Eligibility (checked by the host): R and S equal to the instance's; C a
 // multiple of 16; W + pad_left + pad_right <= WP; every tile's slot span
@@ -78,9 +79,10 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
     constexpr int TAP_BYTES = TN * 32;            // one tap of the slab: TN filters x 16 channels
     constexpr int SLAB_BYTES = RS * TAP_BYTES;
     constexpr int SU = 2 * TN;                    // slab units (filter, 8-channel group) per chunk
-    constexpr int SUT = (SU + NT - 1) / NT;
+    constexpr int SUD = DG ? 2 * SU : SU;         // DG: two threads per unit, 4 filter runs each
+    constexpr int SUT = (SUD + NT - 1) / NT;
     constexpr int NV = RS;                        // 16-byte vectors per slab unit: 8 channels x RS taps
-    constexpr int ND = DG ? 8 * RS : 1;           // DG: 2-byte loads per slab unit (8 runs of RS taps)
+    constexpr int ND = DG ? 4 * RS : 1;           // DG: 2-byte loads per half unit (4 runs of RS taps)
     constexpr int BUF_BYTES = HALO_BYTES + SLAB_BYTES;
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
     static_assert(BUF_BYTES % 16 == 0, "16-byte aligned buffers");
@@ -139,13 +141,15 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
 #pragma unroll
     for (int i = 0; i < SUT; ++i) {
         const int e = tid + NT * i;
-        const int row = e >> 1;
-        const int g = e & 1;
-        const bool ok = e < SU && n0 + row < p.K;
-        // DG: F[c0 + 8g + j, n, t] at ((c0 + 8g + j) * K + n) * RS + t, K the
-        // channel count of dx here
+        const int half = DG ? e / SU : 0;
+        const int ue = DG ? e % SU : e;
+        const int row = ue >> 1;
+        const int g = ue & 1;
+        const bool ok = e < SUD && n0 + row < p.K;
+        // DG: F[c0 + 8g + 4half + j, n, t] at ((c0 + 8g + 4half + j) * K + n) * RS + t,
+        // K the channel count of dx here
         if constexpr (DG)
-            s_off[i] = ok ? (8 * g * p.K + n0 + row) * RS : 0;
+            s_off[i] = ok ? ((8 * g + 4 * half) * p.K + n0 + row) * RS : 0;
         else
             s_off[i] = ok ? (n0 + row) * p.Kred + 8 * g * RS : 0;
         s_ok |= (ok ? 1u : 0u) << i;
@@ -214,25 +218,29 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
         } else {
             const int i = (q - HUT) / RS, t = (q - HUT) % RS;
             const int e = tid + NT * i;
-            if (SU % NT == 0 || e < SU) {
-                const int row = e >> 1;
-                const int g = e & 1;
+            if (SUD % NT == 0 || e < SUD) {
+                const int half = DG ? e / SU : 0;
+                const int ue = DG ? e % SU : e;
+                const int row = ue >> 1;
+                const int g = ue & 1;
                 const bool ok = (s_ok >> i) & 1;
                 unsigned char* dst = hb + HALO_BYTES + 16 * (2 * row + (g ^ slab_swz(row)));
-                u32x4 out;
                 if constexpr (DG) {
                     // slab tap t is tap RS-1-t of the runs (the filter flipped);
-                    // dword d holds runs 2d and 2d+1
+                    // dword 2half + d holds runs 4half + 2d and 4half + 2d + 1
+                    u32x2 o2;
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
+                    for (int d = 0; d < 2; ++d) {
                         const uint32_t lo = s_raw[i][(2 * d) * RS + RS - 1 - t];
                         const uint32_t hi = s_raw[i][(2 * d + 1) * RS + RS - 1 - t];
-                        out[d] = ok ? (lo | (hi << 16)) : 0u;
+                        o2[d] = ok ? (lo | (hi << 16)) : 0u;
                     }
+                    *reinterpret_cast<u32x2*>(dst + 8 * half + t * TAP_BYTES) = o2;
                 } else {
                     // element k of the unit's run is channel k / RS at tap k % RS:
                     // dword d of tap t holds channels 2d and 2d+1 of that tap
                     const uint32_t* words = reinterpret_cast<const uint32_t*>(&s_val[i][0]);
+                    u32x4 out;
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
                         const int klo = (2 * d) * RS + t;
@@ -243,8 +251,8 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
                         const uint32_t hi = (khi & 1) ? (whi & 0xffff0000u) : (whi << 16);
                         out[d] = ok ? (lo | hi) : 0u;
                     }
+                    *reinterpret_cast<u32x4*>(dst + t * TAP_BYTES) = out;
                 }
-                *reinterpret_cast<u32x4*>(dst + t * TAP_BYTES) = out;
             }
         }
     };
