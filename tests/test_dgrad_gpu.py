@@ -54,6 +54,11 @@ _ran = set()
 # the forward shapes, plus a 5x5 one whose filter count (the data gradient's
 # reduction channels) is a multiple of 4
 SHAPES = SMALL_SHAPES + [
+    # 3x3 stride 1 onto 70 channels (a ragged 64-channel tile) from 48 (three
+    # 16-channel chunks), padding unequal on every side, 10x12 images (one
+    # 120-position tile each, 12 halo rows, 14 padded columns): the bf16 halo
+    # kernel's data-gradient mode
+    dict(name="dg_halo3_c70_k48", N=3, C=70, Hh=10, Ww=12, K=48, R=3, S=3, stride=(1, 1), pads=(2, 0, 1, 2)),
     dict(name="dg_halo5_k72", N=2, C=12, Hh=20, Ww=20, K=72, R=5, S=5, stride=(1, 1), pads=(2, 2, 2, 2)),
     # stride-phase kernel: every channel count 1-4 and both column-tap bounds (<= 3, <= 6),
     # phases with fewer taps than others, padding rows and columns on every side, and rows
@@ -179,11 +184,16 @@ def test_workload_layer_integer_exact(lay):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
-@pytest.mark.parametrize("geom", [(20, 3, 3, (1, 1), (1, 1, 1, 0)), (3, 7, 5, (3, 2), (2, 1, 0, 2))],
-                         ids=["c20", "c3_strided"])
+@pytest.mark.parametrize("geom", [(20, 3, 3, (1, 1), (1, 1, 1, 0), 36, 13, 11),
+                                  (3, 7, 5, (3, 2), (2, 1, 0, 2), 36, 13, 11),
+                                  (70, 3, 3, (1, 1), (2, 0, 1, 2), 32, 10, 12)],
+                         ids=["c20", "c3_strided", "c70_k32"])
 def test_alpha_beta(dtype, geom, monkeypatch):
-    C, R, S, stride, pads = geom
-    lay = _small("dg_ab", 2, C, 13, 11, 36, R, S, stride, pads, dtype)
+    """c70_k32: 32 dy channels (two 16-channel chunks) onto 70 dx channels (a
+    64-channel tile and a ragged one) of 10x12 images (one 120-position tile
+    each), so the bf16 halo kernel takes it too."""
+    C, R, S, stride, pads, K, Hh, Ww = geom
+    lay = _small("dg_ab", 2, C, Hh, Ww, K, R, S, stride, pads, dtype)
     _, wi = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
     N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
     dyi = _dy(lay, (N, K, P, Q), integer=True)
