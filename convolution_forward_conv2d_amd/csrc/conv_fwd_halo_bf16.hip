@@ -395,10 +395,10 @@ static hipError_t launch_halo_bf16_variant(const ConvParams& p0, bool dgrad, hip
     return hipGetLastError();
 }
 
-// (DG: the data-gradient slab holds 72 more registers: 64-filter tiles only)
+// (DG: the data-gradient slab holds 36 more registers per 256 slab half units)
 //        name                     TM   TN  waves  R  S  WP  SL  DG
 #define MICONV_HALO_BF16_VARIANTS(X)                              \
-    X(HALO_BF16_3x3_128x128, 128, 128, 2, 2, 3, 3, 16, 16, false)  \
+    X(HALO_BF16_3x3_128x128, 128, 128, 2, 2, 3, 3, 16, 16, true)   \
     X(HALO_BF16_3x3_128x64, 128, 64, 2, 2, 3, 3, 16, 16, true)     \
     X(HALO_BF16_3x3_192x128, 192, 128, 2, 2, 3, 3, 16, 16, false)
 

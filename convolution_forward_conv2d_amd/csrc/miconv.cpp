@@ -406,9 +406,13 @@ bool halo_eligible(const HaloCandidate& h, DType dt, const ConvParams& p, const 
     if (p.C % h.cb != 0) return false;
     // channel-blocked x: a chunk of h.cb channels must lie in one block
     if (p.div_xcb.d != miconv::kOneBlock && p.div_xcb.d % h.cb != 0) return false;
-    // scalar filter loads: no alignment needed; bf16 only in the 64-filter
-    // instance and with packed KCRS filters
-    if (dgrad) return dt != DType::BF16 || (h.c.v == Variant::HALO_BF16_3x3_128x64 && p.wkb == 0);
+    // scalar filter loads: no alignment needed.  bf16 with packed KCRS
+    // filters: 64-filter tiles, 128-filter ones where dy is read 2 bytes at a
+    // time (channels not innermost; with 16-byte dy loads they run slower)
+    if (dgrad)
+        return dt != DType::BF16 ||
+               (p.wkb == 0 && (h.c.v == Variant::HALO_BF16_3x3_128x64 ||
+                               (h.c.v == Variant::HALO_BF16_3x3_128x128 && p.sxc != 1)));
     if (p.wkb > 0) {
         // blocked filters: 16-byte loads of kb-contiguous filters (fp32/fp64 kernel only)
         const int vk = dt == DType::F64 ? 2 : 4;

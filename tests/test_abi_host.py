@@ -265,11 +265,19 @@ def test_dgrad_kernel_choice_host_only():
         assert names[name].startswith("dgrad_halo_f"), (name, names[name])
     # onto 96 channels: the 96-wide tiles
     assert names["alexnet_conv2"] == "dgrad_halo_f32_5x5_128x96_c2"
-    # bf16 takes the halo kernel's 64-filter instance in data-gradient mode; strided onto 3
-    # channels at stride 4 (48 channel x phase columns) the stride-1 GEMM onto the stride
-    # phases, onto 1 channel (4 columns) the stride-phase kernel's row-staged form
+    # bf16 takes the halo kernel in data-gradient mode: 128 filters per tile onto NCHW dy
+    # (the descriptors here), 64 onto channels-last dy; strided onto 3 channels at stride 4
+    # (48 channel x phase columns) the stride-1 GEMM onto the stride phases, onto 1 channel
+    # (4 columns) the stride-phase kernel's row-staged form
     for name in ("prec_conv3_bf16_nchw", "prec_conv4_bf16_nhwc", "prec_conv5_bf16_nhwc"):
-        assert names[name] == "dgrad_halo_bf16_3x3_128x64", (name, names[name])
+        assert names[name] == "dgrad_halo_bf16_3x3_128x128", (name, names[name])
+    lay = workloads.by_name("prec_conv4_bf16_nhwc")
+    xd, wd, cd, yd = _descs(lay, mic.MIC_DTYPE_F32, 2, 2)
+    try:
+        mic.mic_tensor_desc_set_packed(yd, 2, mic.MIC_LAYOUT_NHWC, *mic.mic_conv_forward_output_dim(cd, xd, wd))
+        assert mic.mic_conv_backward_data_kernel_name(None, wd, yd, cd, xd) == "dgrad_halo_bf16_3x3_128x64"
+    finally:
+        _free(xd, wd, cd, yd)
     # 21x11 / stride (2, 1) onto 32 channels: the row-streamed kernel per stride phase
     assert names["speech_l2"] == "dgrad_rows_mfma_f32_s11_256x32"
     assert names["overfeat_l1"] == "dgrad_subpixel"
