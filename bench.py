@@ -1,19 +1,26 @@
 """Benchmark: effective convolution TFLOP/s on one MI355X.
 
-Default workload: the AlexNet-style fp32 NCHW stack at batch 128 (conv2:
-96->256, 27x27, 5x5/s1/pad2; conv3: 256->384, conv4: 384->384, conv5:
-384->256, all 13x13, 3x3/s1/pad1), synthetic seeded inputs (uniform[-1,1]
-data, He-normal weights).  One step = the workload's forward passes, each
-one kernel launch of libmiconv through the C ABI.
+Default workload: the largest configuration, the Overfeat-fast-style fp32
+NCHW stack at batch 128 (L1: 3->96, 231x231, 11x11/s4; L2: 96->256, 24x24,
+5x5/s1; L3-L5: 256->512->1024->1024, 12x12, 3x3/s1/pad1; 656.2 GFLOP per
+step), synthetic seeded inputs (uniform[-1,1] data, N(0, 0.01) weights).
+One step = the workload's forward passes, each one kernel launch of
+libmiconv through the C ABI.
+
+Timing: W warm-up steps, then five timed regions of exactly K steps each,
+every region bracketed by torch.cuda.synchronize() on both sides;
+``ms_per_step`` and ``value`` come from the median region (all five are
+reported).  Per-layer kernel times: HIP events on the launch stream around
+back-to-back launches, regions of at least 100 ms, median of five.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                    [--workload alexnet|overfeat|speech|tiny|prec_f64|prec_bf16|alexnet_pool|
+                    [--workload overfeat|alexnet|speech|tiny|prec_f64|prec_bf16|alexnet_pool|
                                 alexnet_fc|alexnet_fc_f64|alexnet_fc_bf16]
                     [--op fprop|dgrad|wgrad]
 
 Prints one JSON line.  ``value`` = 2*N*K*C*R*S*P*Q summed over the step's
-layers / mean step time (inputs resident in HBM, no host traffic inside
-the timed region).  ``roofline`` covers the kernel with the most time per
+layers / median-region step time (inputs resident in HBM, no host traffic
+inside the timed region).  ``roofline`` covers the kernel with the most time per
 step, timed with HIP events on the stream it runs on.  ``cpu_baseline``
 times the CPU oracle on a bounded sample of the same workload (the first
 few images of every layer).  ``--op dgrad`` / ``--op wgrad`` time the data /
@@ -37,7 +44,9 @@ sys.path.insert(0, ROOT)
 
 # MI355X dense MFMA peaks (256 CU x 2.4 GHz): fp32 256, fp64 128, bf16 4096 FLOP/clk/CU
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "bf16": 2516.6}
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_alexnet_fp32.md")
+# committed rocprofv3 counter summaries, per workload (HBM bytes per launch of the dominant kernel)
+PROFILE_TRAFFIC = {"overfeat": os.path.join(ROOT, "profiles", "traffic_overfeat_fp32.md"),
+                   "alexnet": os.path.join(ROOT, "profiles", "traffic_alexnet_fp32.md")}
 WORKLOADS = ("alexnet", "overfeat", "speech", "tiny", "prec_f64", "prec_bf16", "alexnet_pool", "alexnet_fc",
              "alexnet_fc_f64", "alexnet_fc_bf16")
 HBM_PEAK_GBS = 8000.0
@@ -46,9 +55,9 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20, help="steps per timed region (five regions)")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="alexnet", choices=WORKLOADS)
+    ap.add_argument("--workload", default="overfeat", choices=WORKLOADS)
     ap.add_argument("--op", default="fprop", choices=("fprop", "dgrad", "wgrad"),
                     help="forward pass (default), data gradient or filter gradient of the layers")
     ap.add_argument("--block", type=int, default=0,
@@ -59,7 +68,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="before the steps, run one plain device copy of this many MiB "
+                    help="before the steps, run one plain device copy of this many MiB, its "
+                         "source first pushed out of the caches by a write of as many MiB "
                          "(a known-size kernel to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
 
@@ -96,13 +106,14 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on this exact source and kernel; else None."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def stored_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of the
+    workload, if it was taken on this exact source and kernel; else None."""
+    path = PROFILE_TRAFFIC.get(workload)
+    if not path or not os.path.exists(path):
         return None
     vals = {}
-    with open(PROFILE_TRAFFIC) as fh:
+    with open(path) as fh:
         for line in fh:
             if line.startswith("traffic:"):
                 for kv in line[len("traffic:"):].split():
@@ -114,6 +125,63 @@ def stored_traffic(kernel):
         return float(vals["bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+REGIONS = 5
+MIN_REGION_S = 0.1
+
+
+def timed_regions(torch, step, steps):
+    """Wall time (s) of REGIONS regions of exactly `steps` steps, each bracketed by
+    torch.cuda.synchronize() on both sides."""
+    out = []
+    for _ in range(REGIONS):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        out.append(time.perf_counter() - t0)
+    return out
+
+
+def event_ms(torch, stream, launch):
+    """Median over REGIONS of one launch's mean duration (ms), from HIP events
+    recorded on the launch stream around back-to-back launches; each region
+    runs at least MIN_REGION_S."""
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    launch()
+    ev0.record(stream)
+    launch()
+    ev1.record(stream)
+    ev1.synchronize()
+    one = max(ev0.elapsed_time(ev1), 1e-3)
+    reps = max(5, int(MIN_REGION_S * 1e3 / one) + 1)
+    res = []
+    for _ in range(REGIONS):
+        ev0.record(stream)
+        for _ in range(reps):
+            launch()
+        ev1.record(stream)
+        ev1.synchronize()
+        res.append(ev0.elapsed_time(ev1) / reps)
+    return sorted(res)[len(res) // 2]
+
+
+def copy_probe(torch, dev, mib):
+    """One plain device copy of `mib` MiB whose source has been pushed out of the
+    L2 and the 256 MB last-level cache by a write of another `mib` MiB: the
+    known-size reference that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    evict = torch.empty_like(src)
+    evict.fill_(2.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst, evict
 
 
 def upload(a64, dtype, layout, row_pitch, dev):
@@ -197,13 +265,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     flops_step = sum(p.flops for _, p, _ in plans)
     if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(torch, dev, args.copy_probe_mib)
 
     def step():
         for _, plan, _ in plans:
@@ -211,28 +273,15 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    regions = timed_regions(torch, step, args.steps)
+    elapsed = sorted(regions)[len(regions) // 2]
     ms_per_step = 1e3 * elapsed / args.steps
     value = flops_step / (elapsed / args.steps) / 1e12
 
     # per-layer kernel durations with HIP events on the launch stream
     per_layer = []
-    reps = max(5, args.steps)
     for lay, plan, _ in plans:
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        plan(1.0, 0.0, stream)
-        ev0.record(stream)
-        for _ in range(reps):
-            plan(1.0, 0.0, stream)
-        ev1.record(stream)
-        ev1.synchronize()
-        ms = ev0.elapsed_time(ev1) / reps
+        ms = event_ms(torch, stream, lambda: plan(1.0, 0.0, stream))
         tf = plan.flops / (ms * 1e-3) / 1e12
         rec = {"layer": lay.name, "kernel": plan.kernel_name(), "us": round(ms * 1e3, 2),
                "gflop": round(plan.flops / 1e9, 3), "tflops": round(tf, 2),
@@ -251,7 +300,7 @@ def main():
     dom = max(groups, key=lambda k: groups[k]["us"])
     g = groups[dom]
     achieved = (g["flops"] / g["launches"]) / (g["us"] / g["launches"] * 1e-6) / 1e12
-    traffic = stored_traffic(dom) if (args.workload == "alexnet" and args.op == "fprop" and not args.block) else None
+    traffic = stored_traffic(args.workload, dom) if (args.op == "fprop" and not args.block) else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "kernel": dom, "launches_per_step": g["launches"],
@@ -269,6 +318,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "regions_ms": [round(1e3 * r, 3) for r in regions],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -306,24 +356,11 @@ def bench_pool(args, torch, mic, gen, workloads, dev):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    regions = timed_regions(torch, step, args.steps)
+    elapsed = sorted(regions)[len(regions) // 2]
     per_layer = []
-    reps = max(5, args.steps)
     for lay, plan, _ in plans:
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        plan(1.0, 0.0, stream)
-        ev0.record(stream)
-        for _ in range(reps):
-            plan(1.0, 0.0, stream)
-        ev1.record(stream)
-        ev1.synchronize()
-        us = ev0.elapsed_time(ev1) / reps * 1e3
+        us = event_ms(torch, stream, lambda: plan(1.0, 0.0, stream)) * 1e3
         per_layer.append({"layer": lay.name, "kernel": plan.kernel_name(), "us": round(us, 2),
                           "mb": round(plan.bytes / 1e6, 2), "gbs": round(plan.bytes / (us * 1e-6) / 1e9, 1)})
     dom = max(per_layer, key=lambda r: r["us"])
@@ -395,24 +432,11 @@ def bench_fc(args, torch, mic, gen, workloads, dev):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    regions = timed_regions(torch, step, args.steps)
+    elapsed = sorted(regions)[len(regions) // 2]
     per_layer = []
-    reps = max(5, args.steps)
     for lay, a, b, c, flops, _, _ in runs:
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        mic.brgemm(a, b, c)
-        ev0.record(stream)
-        for _ in range(reps):
-            mic.brgemm(a, b, c)
-        ev1.record(stream)
-        ev1.synchronize()
-        us = ev0.elapsed_time(ev1) / reps * 1e3
+        us = event_ms(torch, stream, lambda: mic.brgemm(a, b, c)) * 1e3
         per_layer.append({"layer": lay.name, "kernel": mic.brgemm_kernel_name_for(a, b, c),
                           "us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 2),
                           "gbs": round(hbm_bytes[lay.name] / (us * 1e-6) / 1e9, 1),

@@ -76,9 +76,9 @@ struct TileMN {
     int mt, nt;
 };
 
-__device__ __forceinline__ TileMN tile_coords(int m_tiles, int n_tiles)
+__device__ __forceinline__ TileMN tile_coords(int m_tiles, int n_tiles, int rev)
 {
-    const int tile = xcd_logical_tile((int)blockIdx.x, m_tiles * n_tiles);
+    const int tile = xcd_logical_tile((int)blockIdx.x, m_tiles * n_tiles, rev);
     TileMN t;
     if (m_tiles <= n_tiles) {
         t.nt = tile / m_tiles;
@@ -146,7 +146,7 @@ brgemm_kernel(const ConvParams p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const TileMN tc = tile_coords(p.m_tiles, p.n_tiles);
+    const TileMN tc = tile_coords(p.m_tiles, p.n_tiles, p.tile_rev);
     const int m0 = tc.mt * TM;
     const int n0 = tc.nt * TN;
 
@@ -392,7 +392,7 @@ brgemm_ws_kernel(const ConvParams p)
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const TileMN tc = tile_coords(p.m_tiles, p.n_tiles);
+    const TileMN tc = tile_coords(p.m_tiles, p.n_tiles, p.tile_rev);
     const int m0 = tc.mt * TM;
     const int n0 = tc.nt * TN;
 

@@ -93,6 +93,7 @@ struct SubpixelArgs {
     FastDiv div_de, div_e;      // by D * E and by E (tap decode)
     FastDiv div_uv, div_v;      // column z -> (c, a, b)
     double alpha, beta;
+    int tile_rev;               // tiles in reverse order (xcd_logical_tile)
 };
 
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int TK>
@@ -136,7 +137,7 @@ conv_bwd_data_subpixel_kernel(const SubpixelArgs p)
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
     const int m0 = mt * TM;
@@ -382,6 +383,7 @@ bool subpixel_args(const ConvParams& p, SubpixelArgs& a, int tn)
     a.alpha = p.alpha;
     a.beta = p.beta;
     a.m_tiles = (a.M + kSpTM - 1) / kSpTM;
+    a.tile_rev = p.tile_rev;
     a.n_tiles = (a.Z + tn - 1) / tn;
     return true;
 }

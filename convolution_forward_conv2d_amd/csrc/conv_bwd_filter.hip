@@ -80,7 +80,7 @@ conv_bwd_filter_kernel(const ConvParams p)
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
     const int m0 = mt * TM;

@@ -122,7 +122,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     const int tid = threadIdx.x & 255;               // thread within its half
     const int lane = tid & 63;
     const int wave = tid >> 6;                       // wave within its half
-    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
     const int m0 = mt * TM;

@@ -129,7 +129,7 @@ conv_bwd_filter_split_kernel(const ConvParams p)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
     const int m0 = mt * TMV;

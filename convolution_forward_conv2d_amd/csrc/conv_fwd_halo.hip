@@ -108,7 +108,7 @@ conv_fwd_halo_kernel(const ConvParams p)
     const int wave = tid >> 6;                   // wave within its half
     unsigned char* smem = smem_all + half * 2 * BUF_BYTES;
 
-    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
     // a tile covers rows m0 .. m_end-1: TM consecutive rows, or one output

@@ -75,7 +75,7 @@ conv_fwd_rows_kernel(const ConvParams p)
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
     const int m0 = mt * TM;
@@ -273,7 +273,7 @@ conv_fwd_rows1_kernel(const ConvParams p)
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
     const int m0 = mt * TM;
@@ -494,7 +494,7 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles);
+    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
     const int m0 = mt * TM;

@@ -69,6 +69,7 @@ struct ConvParams {
     int sxcb, sycb;
     int wkb, wcb;
     double alpha, beta;  // converted to the accumulation type inside the kernel
+    int tile_rev;        // 1: tiles run in reverse order (xcd_logical_tile); tests only
 };
 
 // Element offset of channel c in a channel-blocked dimension (block size

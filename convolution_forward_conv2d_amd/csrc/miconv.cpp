@@ -285,6 +285,15 @@ const HaloCandidate kHalo[] = {
     {{Variant::HALO_BF16_3x3_192x128, 192, 128, "halo_bf16_3x3_192x128"}, DType::BF16, 3, 3, 16, 16, 16, 1.0, 1},
 };
 
+// MIC_TILE_ORDER=reverse (environment) makes every tiled kernel run its
+// output tiles in the opposite order; the result must not change (the tests
+// compare both orders bit for bit).
+int tile_order_reversed()
+{
+    const char* e = getenv("MIC_TILE_ORDER");
+    return e && strcmp(e, "reverse") == 0 ? 1 : 0;
+}
+
 struct Plan {
     mic_status status;
     DType dt;
@@ -1200,10 +1209,13 @@ mic_status pool_output_dims(const mic_pool_desc_st* pd, const mic_tensor_desc_st
     const int64_t hspan = (int64_t)xd->h + pd->pad_top + pd->pad_bottom - pd->r;
     const int64_t wspan = (int64_t)xd->w + pd->pad_left + pd->pad_right - pd->s;
     if (hspan < 0 || wspan < 0) return MIC_STATUS_BAD_PARAM;
+    const int64_t P = hspan / pd->u + 1;
+    const int64_t Q = wspan / pd->v + 1;
+    if (P > INT32_MAX || Q > INT32_MAX) return MIC_STATUS_NOT_SUPPORTED;
     *n = xd->n;
     *c = xd->c;
-    *p = (int)(hspan / pd->u + 1);
-    *q = (int)(wspan / pd->v + 1);
+    *p = (int)P;
+    *q = (int)Q;
     return MIC_STATUS_SUCCESS;
 }
 
@@ -1237,7 +1249,10 @@ Plan make_pool_plan(const mic_pool_desc_st* pd, const mic_tensor_desc_st* xd, co
         return pl;
     }
     const int64_t M = (int64_t)n * P * Q;
-    if (extent(*xd) >= kMaxOffset || extent(*yd) >= kMaxOffset || M * c >= kMaxOffset ||
+    // the kernel visits the R*S window positions of every output with int
+    // arithmetic: the window stays below the offset limit too
+    if ((int64_t)pd->r * pd->s >= kMaxOffset || extent(*xd) >= kMaxOffset || extent(*yd) >= kMaxOffset ||
+        M * c >= kMaxOffset ||
         xd->sn >= kMaxOffset || xd->sc >= kMaxOffset || xd->sh >= kMaxOffset || xd->sw >= kMaxOffset ||
         yd->sn >= kMaxOffset || yd->sc >= kMaxOffset || yd->sh >= kMaxOffset || yd->sw >= kMaxOffset) {
         pl.status = MIC_STATUS_NOT_SUPPORTED;
@@ -1559,6 +1574,7 @@ mic_status mic_conv_forward(mic_handle handle, double alpha, mic_tensor_desc x_d
     if (!handle) return MIC_STATUS_BAD_PARAM;
     Plan pl = make_plan(handle, x_desc, x, w_desc, w, conv, y_desc, y, alpha, beta, true);
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    pl.p.tile_rev = tile_order_reversed();
     hipError_t err;
     if (pl.cand.v == Variant::DIRECT)
         err = miconv::launch_direct(pl.dt, pl.p, handle->stream);
@@ -1578,6 +1594,7 @@ mic_status mic_conv_backward_data(mic_handle handle, double alpha, mic_filter_de
     if (!handle) return MIC_STATUS_BAD_PARAM;
     Plan pl = make_dgrad_plan(handle, dy_desc, dy, w_desc, w, conv, dx_desc, dx, alpha, beta, true);
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    pl.p.tile_rev = tile_order_reversed();
     hipError_t err;
     if (pl.cand.v == Variant::DIRECT)
         err = miconv::launch_bwd_data_direct(pl.dt, pl.p, handle->stream);
@@ -1618,6 +1635,7 @@ mic_status mic_conv_backward_filter(mic_handle handle, double alpha, mic_tensor_
     if (!handle) return MIC_STATUS_BAD_PARAM;
     Plan pl = make_wgrad_plan(handle, x_desc, x, dy_desc, dy, conv, dw_desc, dw, alpha, beta, true);
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
+    pl.p.tile_rev = tile_order_reversed();
     const hipError_t err = is_wgh(pl.cand.v)   ? miconv::launch_bwd_filter_halo(pl.cand.v, pl.p, handle->stream)
                            : is_wgs(pl.cand.v) ? miconv::launch_bwd_filter_split(pl.cand.v, pl.p, handle->stream)
                            : is_wgr(pl.cand.v) ? miconv::launch_bwd_filter_rows(pl.cand.v, pl.p, handle->stream)
@@ -1715,6 +1733,7 @@ mic_status mic_brgemm(mic_handle handle, mic_dtype dtype, int m, int n, int k, i
                                b, b_stride_batch, b_stride_k, b_stride_n, beta, c, c_stride_m, c_stride_n, true);
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
     if (m == 0 || n == 0) return MIC_STATUS_SUCCESS;
+    pl.p.tile_rev = tile_order_reversed();
     const hipError_t err = miconv::launch_brgemm(pl.cand.v, pl.p, handle->stream);
     return err == hipSuccess ? MIC_STATUS_SUCCESS : MIC_STATUS_LAUNCH_FAILED;
 }

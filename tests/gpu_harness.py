@@ -11,6 +11,10 @@ Tolerances (per element type, fixed in the tests, not tuned to results):
         does not change.
   f64 : relative L2 error <= 1e-12.
   bf16: relative L2 error <= 1e-2 (bf16 inputs, fp32 accumulation and output).
+        The oracle reads the same bf16-rounded inputs and the kernels
+        accumulate in fp32, so the fp32 per-element bound 2e-6 * B is
+        asserted as well: a packing slip that touches a few outputs breaks it
+        long before it moves the relative L2 error past 1e-2.
 """
 import numpy as np
 import torch
@@ -22,7 +26,7 @@ from gen import workloads
 TORCH_DT = {"f32": torch.float32, "f64": torch.float64, "bf16": torch.bfloat16}
 OUT_DT = {"f32": torch.float32, "f64": torch.float64, "bf16": torch.float32}
 RELL2 = {"f32": 1e-5, "f64": 1e-12, "bf16": 1e-2}
-ELEM_BOUND = {"f32": 2e-6}
+ELEM_BOUND = {"f32": 2e-6, "bf16": 2e-6}
 
 
 def dev():
@@ -45,6 +49,29 @@ def strided_empty(shape, strides, dtype, device, fill=float("nan")):
     return base.as_strided(shape, strides)
 
 
+# NaN canary cells placed directly before and after an output's storage
+GUARD = 4096
+
+
+def guarded_empty(shape, strides, dtype, device=None):
+    """A NaN-filled strided tensor inside one allocation that also holds GUARD
+    NaN cells before and after it (and, for padded strides, the pad cells
+    between its rows).  Returns (tensor, whole allocation)."""
+    device = device or dev()
+    n = workloads.storage_elems(*shape, strides)
+    base = torch.full((n + 2 * GUARD,), float("nan"), dtype=dtype, device=device)
+    return base.as_strided(shape, strides, GUARD), base
+
+
+def assert_only_tensor_written(t, base, what=""):
+    """Every cell of the allocation that is not an element of t still holds NaN."""
+    mask = torch.zeros(base.numel(), dtype=torch.bool, device=base.device)
+    mask.as_strided(t.shape, t.stride(), t.storage_offset()).fill_(True)
+    outside = base[~mask]
+    bad = int((~torch.isnan(outside)).sum())
+    assert bad == 0, "%s: %d cells outside the output were written" % (what, bad)
+
+
 def to_device(a64, dtype_key, layout="nchw", row_pitch=0, device=None):
     """Upload logical N,C,H,W float64 data into a tensor of the given layout."""
     device = device or dev()
@@ -59,6 +86,24 @@ def out_tensor(lay, shape, device=None, fill=float("nan")):
     device = device or dev()
     st = workloads.padded_strides(*shape, lay.layout, lay.row_pitch)
     return strided_empty(shape, st, OUT_DT[lay.dtype], device, fill)
+
+
+def guarded_out(lay, shape):
+    """out_tensor's layout, NaN-filled, with canary cells around it: (tensor, allocation)."""
+    st = workloads.padded_strides(*shape, lay.layout, lay.row_pitch)
+    return guarded_empty(shape, st, OUT_DT[lay.dtype])
+
+
+def full_order(layers):
+    """Layers ordered so that the layouts of one logical layer (same config,
+    layer and element type: the same generated values) run one after another
+    and share one oracle result."""
+    return sorted(layers, key=lambda l: (l.config, l.dtype, l.layer, l.layout))
+
+
+def to_host(t):
+    """Device tensor -> float64 numpy in logical N,C,H,W order."""
+    return t.double().cpu().numpy()
 
 
 def sample_coords(rng, N, K, P, Q, count):

@@ -225,6 +225,8 @@ int main() {
             if (t < 0 || t >= tiles || seen[t]++) { printf("map %d %d\n", tiles, b); return 1; }
             // ids on one XCD form one contiguous run
             if (b >= 8 && xcd_logical_tile(b - 8, tiles) != t - 1) { printf("run %d %d\n", tiles, b); return 1; }
+            // the reversed order is the mirror image of the same bijection
+            if (xcd_logical_tile(b, tiles, 1) != tiles - 1 - t) { printf("rev %d %d\n", tiles, b); return 1; }
         }
     }
     printf("ok\n");
@@ -480,6 +482,34 @@ def test_pool_descriptor_and_output_dims():
         mic.pool_output_shape((1, 1, 3, 3), (5, 1), (1, 1), (0, 1, 0, 0))
     l = mic.lib()
     assert l.mic_pool_forward(None, 1.0, None, None, None, 0.0, None, None) == mic.MIC_STATUS_BAD_PARAM
+
+
+def test_pool_size_limits_host_only():
+    """Output sizes past INT32_MAX and windows of 2^30 positions or more are refused
+    before anything is launched (the kernel indexes them with 32-bit ints)."""
+    big = (1 << 31) - 1
+    with pytest.raises(mic.MicError) as e:                 # P = 2^31 - 1 + 2^30 rows
+        mic.pool_output_shape((1, 1, big, 1), (1, 1), (1, 1), (1 << 30, 0, 0, 0))
+    assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+    assert mic.pool_output_shape((1, 1, big, 1), (1, 1), (1, 1), (0, 0, 0, 0)) == (1, 1, big, 1)
+    # a 32768 x 32768 window over a 1 x 1 input padded to the window: one output of
+    # 2^30 window positions.  Fake non-null handle and pointers: the call must fail
+    # in validation, before anything dereferences them.
+    xd, yd, pd = mic.mic_tensor_desc_create(), mic.mic_tensor_desc_create(), mic.mic_pool_desc_create()
+    try:
+        mic.mic_tensor_desc_set_packed(xd, mic.MIC_DTYPE_F32, mic.MIC_LAYOUT_NCHW, 1, 1, 1, 1)
+        mic.mic_tensor_desc_set_packed(yd, mic.MIC_DTYPE_F32, mic.MIC_LAYOUT_NCHW, 1, 1, 1, 1)
+        l = mic.lib()
+        for win, status in [(32768, mic.MIC_STATUS_NOT_SUPPORTED), (32767, None)]:
+            pad = win - 1
+            mic.mic_pool_desc_set(pd, mic.MIC_POOL_MAX, win, win, pad, 0, pad, 0, 1, 1)
+            assert mic.mic_pool_forward_output_dim(pd, xd) == (1, 1, 1, 1)
+            if status is not None:
+                assert l.mic_pool_forward(1, 1.0, pd, xd, 16, 0.0, yd, 16) == status
+    finally:
+        mic.mic_tensor_desc_destroy(xd)
+        mic.mic_tensor_desc_destroy(yd)
+        mic.mic_pool_desc_destroy(pd)
 
 
 def test_brgemm_kernel_choice_host_only():

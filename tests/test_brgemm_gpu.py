@@ -139,6 +139,14 @@ def test_small_full_parity_every_variant(dtype, case, monkeypatch):
         if case["c"] == "pitch":         # the row padding stays untouched
             pad = base.view(case["m"], case["n"] + 7)[:, case["n"]:]
             assert bool(torch.isnan(pad).all()), "write outside C"
+        # the same tiles in reverse order give the same bits
+        monkeypatch.setenv("MIC_TILE_ORDER", "reverse")
+        c_rev, _ = _c_view(case["m"], case["n"], case["c"], dtype)
+        mic.brgemm(a, b, c_rev)
+        torch.cuda.synchronize()
+        monkeypatch.delenv("MIC_TILE_ORDER")
+        assert torch.equal(c, c_rev), "%s/%s/%s: reversed tile order changed the result" % (
+            case["name"], dtype, var)
         _ran.add(var)
 
 

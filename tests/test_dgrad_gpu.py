@@ -1,12 +1,17 @@
 """GPU parity of the data gradient (mic_conv_backward_data) against the oracle.
 
 Small shapes spanning several tiles with ragged tails are compared in full
-for every kernel variant; every workload layer's data gradient is run at
-full size and compared on sampled coordinates, with integer-valued inputs
-bit-exact, NaN-prefilled dx fully overwritten and reruns bit-identical.
+for every kernel variant, also with the tiles run in reverse order (bit for
+bit the same result); every workload layer's data gradient is run at full
+size and its whole dx compared with the whole oracle output, with
+NaN-prefilled dx fully overwritten, canary cells around dx untouched and
+reruns bit-identical; integer-valued inputs are bit-exact on sampled
+coordinates in every layout.
 dy is seeded uniform [-1, 1] (tensor id 3 of the layer's seed), rounded to
 the layer's storage type.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -129,6 +134,12 @@ def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
                 continue
             raise
         H.check(dtype, dx.double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (shape["name"], dtype, var))
+        monkeypatch.setenv("MIC_TILE_ORDER", "reverse")
+        dx_rev = _out(lay)
+        _run(lay, dy, w, dx_rev)
+        monkeypatch.delenv("MIC_TILE_ORDER")
+        assert torch.equal(dx, dx_rev), "%s/%s/%s: reversed tile order changed the result" % (
+            shape["name"], dtype, var)
         _ran.add(var)
 
 
@@ -142,32 +153,46 @@ def _sample(rng, shape, count):
     return H.sample_coords(rng, N, C, Hh, Ww, count)
 
 
-@pytest.mark.parametrize("lay", workloads.ALL_LAYERS, ids=lambda l: l.name)
-def test_workload_layer_sampled(lay):
-    """Full-size data gradient, default variant: sampled parity, NaN-safe beta=0, rerun bit-identity."""
+_cache = {}
+
+
+def _layer_case(lay):
+    """dy, w and the whole-tensor oracle dx (and bound); layouts of one logical layer share them."""
+    key = (lay.config, lay.layer, lay.dtype)
+    if key not in _cache:
+        _cache.clear()
+        _, w64 = H.inputs(lay)
+        N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+        dy64 = _dy(lay, (N, K, P, Q))
+        t0 = time.perf_counter()
+        ref, bound = oracle.conv2d_bwd_data(dy64, w64, lay.x_shape, lay.stride, lay.padding)
+        print("  oracle %.1f s" % (time.perf_counter() - t0), flush=True)
+        _cache[key] = (dy64, w64, ref, bound)
+    return _cache[key]
+
+
+@pytest.mark.parametrize("lay", H.full_order(workloads.ALL_LAYERS), ids=lambda l: l.name)
+def test_workload_layer_full(lay):
+    """Full-size data gradient, default variant: the whole dx against the whole
+    oracle output, NaN-safe beta = 0, canaries around dx, rerun bit-identity."""
     print("layer", lay.name, flush=True)
-    _, w64 = H.inputs(lay)
-    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
-    dy64 = _dy(lay, (N, K, P, Q))
+    dy64, w64, ref, bound = _layer_case(lay)
     dy = H.to_device(dy64, lay.dtype, lay.layout, lay.row_pitch)
     w = torch.from_numpy(w64).to(H.TORCH_DT[lay.dtype]).to(H.dev())
-    dx = _out(lay)
+    dx, base = H.guarded_out(lay, lay.x_shape)
     _run(lay, dy, w, dx)
-    assert bool(torch.isfinite(dx).all()), "unwritten or non-finite dx"
-    rng = np.random.default_rng(lay.config * 1000 + lay.layer + 17)
-    idx = _sample(rng, lay.x_shape, 3000)
-    ref, bound = oracle.conv2d_bwd_data_at(dy64, w64, lay.x_shape, idx, lay.stride, lay.padding)
-    rel, worst = H.check(lay.dtype, H.gather(dx, idx), ref, bound, what=lay.name)
-    print("  sampled rel-L2 %.3e, worst |err|/B %.3e" % (rel, worst), flush=True)
+    H.assert_only_tensor_written(dx, base, lay.name)
+    rel, worst = H.check(lay.dtype, H.to_host(dx), ref, bound, what=lay.name)
+    print("  whole tensor (%d outputs): rel-L2 %.3e, worst |err|/B %.3e" % (ref.size, rel, worst), flush=True)
     dx2 = _out(lay, fill=0.0)
     _run(lay, dy, w, dx2)
     assert torch.equal(dx, dx2), "rerun not bit-identical"
 
 
-@pytest.mark.parametrize("lay", [l for l in workloads.ALL_LAYERS if not l.name.endswith("nhwc")],
-                         ids=lambda l: l.name)
+@pytest.mark.parametrize("lay", workloads.ALL_LAYERS, ids=lambda l: l.name)
 def test_workload_layer_integer_exact(lay):
-    """Integer dy and filter in [-4, 4]: every partial sum is an exact integer below 2^24."""
+    """Integer dy and filter in [-4, 4]: every partial sum is an exact integer below 2^24
+    (every layout, NHWC included)."""
     print("layer", lay.name, flush=True)
     _, w64 = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
     N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)

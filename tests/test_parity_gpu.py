@@ -1,12 +1,17 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
 Small shapes that span several tiles with ragged tails are compared element
-by element in full, for every kernel variant; every workload layer is run at
-its full size and compared on sampled outputs (corners, edge midpoints and
-random coordinates), plus properties that hold at any size: integer-valued
-inputs give bit-exact results, reruns are bit-identical, NaN in y never
-leaks when beta = 0, and nothing outside y is written.
+by element in full, for every kernel variant, in the normal tile order and
+with the tiles run in reverse (the result must not change by a bit); every
+workload layer is run at its full size and its whole output is compared with
+the whole oracle output (relative L2 over the tensor and the per-element
+bound on every element), plus properties that hold at any size:
+integer-valued inputs give bit-exact results over the whole tensor, reruns
+are bit-identical, NaN in y never leaks when beta = 0, and nothing outside y
+is written (canary cells directly before and after y, and the pad cells of
+padded rows, stay untouched).
 """
+import time
 import os
 
 import numpy as np
@@ -134,6 +139,14 @@ def test_small_full_parity_every_variant(dtype, shape, monkeypatch):
                 continue
             raise
         H.check(dtype, y.double().cpu().numpy(), ref, bound, what="%s/%s/%s" % (shape["name"], dtype, var))
+        # the same tiles in reverse order: any dependence between workgroups
+        # or race on LDS shows as a changed bit
+        monkeypatch.setenv("MIC_TILE_ORDER", "reverse")
+        y_rev = H.out_tensor(lay, ref.shape)
+        _run(lay, x, w, y_rev)
+        monkeypatch.delenv("MIC_TILE_ORDER")
+        assert torch.equal(y, y_rev), "%s/%s/%s: reversed tile order changed the result" % (
+            shape["name"], dtype, var)
         _ran.add(var)
 
 
@@ -157,51 +170,54 @@ def test_tiny_workload_full_and_deterministic():
 _cache = {}
 
 
-def _layer_inputs(lay, integer=False):
+def _layer_case(lay, integer=False):
+    """Inputs and the whole-tensor oracle output (y, bound) of a workload layer.
+    The layouts of one logical layer share them (same generated values)."""
     key = (lay.config, lay.layer, lay.dtype, integer)
     if key not in _cache:
         _cache.clear()
         dist = ("integers", -4, 4) if integer else None
-        _cache[key] = H.inputs(lay, dist, dist)
+        x64, w64 = H.inputs(lay, dist, dist)
+        t0 = time.perf_counter()
+        ref, bound = oracle.conv2d_fprop(x64, w64, lay.stride, lay.padding)
+        print("  oracle %.1f s" % (time.perf_counter() - t0), flush=True)
+        _cache[key] = (x64, w64, ref, bound)
     return _cache[key]
 
 
-@pytest.mark.parametrize("lay", workloads.ALL_LAYERS, ids=lambda l: l.name)
-def test_workload_layer_sampled(lay):
-    """Full-size layer, default variant: sampled parity, rerun bit-identity, NaN-safe beta=0."""
+FULL_LAYERS = H.full_order(workloads.ALL_LAYERS)
+
+
+@pytest.mark.parametrize("lay", FULL_LAYERS, ids=lambda l: l.name)
+def test_workload_layer_full(lay):
+    """Full-size layer, default variant, whole output against the whole oracle
+    output; NaN-prefilled y fully overwritten (beta = 0), canaries around y
+    untouched, rerun bit-identical."""
     print("layer", lay.name, flush=True)
-    x64, w64 = _layer_inputs(lay)
+    x64, w64, ref, bound = _layer_case(lay)
     x = H.to_device(x64, lay.dtype, lay.layout, lay.row_pitch)
     w = torch.from_numpy(w64).to(H.TORCH_DT[lay.dtype]).to(H.dev())
-    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
-    y = H.out_tensor(lay, (N, K, P, Q))                # NaN-filled: beta = 0 must overwrite all
+    y, base = H.guarded_out(lay, ref.shape)
     _run(lay, x, w, y)
-    assert bool(torch.isfinite(y).all()), "unwritten or non-finite outputs"
-    rng = np.random.default_rng(lay.config * 1000 + lay.layer)
-    idx = H.sample_coords(rng, N, K, P, Q, 3000)
-    ref, bound = oracle.conv2d_fprop_at(x64, w64, idx, lay.stride, lay.padding)
-    rel, worst = H.check(lay.dtype, H.gather(y, idx), ref, bound, what=lay.name)
-    print("  sampled rel-L2 %.3e, worst |err|/B %.3e" % (rel, worst), flush=True)
-    y2 = H.out_tensor(lay, (N, K, P, Q), fill=0.0)
+    H.assert_only_tensor_written(y, base, lay.name)
+    rel, worst = H.check(lay.dtype, H.to_host(y), ref, bound, what=lay.name)
+    print("  whole tensor (%d outputs): rel-L2 %.3e, worst |err|/B %.3e" % (ref.size, rel, worst), flush=True)
+    y2 = H.out_tensor(lay, ref.shape, fill=0.0)
     _run(lay, x, w, y2)
     assert torch.equal(y, y2), "rerun not bit-identical"
 
 
-@pytest.mark.parametrize("lay", [l for l in workloads.ALL_LAYERS if not l.name.endswith("nhwc")],
-                         ids=lambda l: l.name)
+@pytest.mark.parametrize("lay", FULL_LAYERS, ids=lambda l: l.name)
 def test_workload_layer_integer_exact(lay):
-    """Integer inputs in [-4, 4]: every partial sum is an exact integer below 2^24."""
+    """Integer inputs in [-4, 4]: every partial sum is an exact integer below 2^24,
+    so the whole output must equal the oracle's bit for bit, in every layout."""
     print("layer", lay.name, flush=True)
-    x64, w64 = _layer_inputs(lay, integer=True)
+    x64, w64, ref, _ = _layer_case(lay, integer=True)
     x = H.to_device(x64, lay.dtype, lay.layout, lay.row_pitch)
     w = torch.from_numpy(w64).to(H.TORCH_DT[lay.dtype]).to(H.dev())
-    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
-    y = H.out_tensor(lay, (N, K, P, Q))
+    y = H.out_tensor(lay, ref.shape)
     _run(lay, x, w, y)
-    rng = np.random.default_rng(7 + lay.config * 1000 + lay.layer)
-    idx = H.sample_coords(rng, N, K, P, Q, 3000)
-    ref, _ = oracle.conv2d_fprop_at(x64, w64, idx, lay.stride, lay.padding)
-    got = H.gather(y, idx)
+    got = H.to_host(y)
     assert np.array_equal(got, ref), "%s: %d mismatches" % (lay.name, int((got != ref).sum()))
 
 
@@ -247,17 +263,17 @@ def test_subtensor_output_and_canaries(layout):
     x64, w64 = H.inputs(lay)
     ref, bound = oracle.conv2d_fprop(x64, w64, lay.stride, lay.padding)
     N, K, P, Q = ref.shape
-    big = torch.full((N, K + 9, P, Q), 7.25, dtype=torch.float32, device=H.dev())
-    if layout == "nhwc":
-        big = big.contiguous(memory_format=torch.channels_last)
-    guard = torch.full((4096,), -3.5, dtype=torch.float32, device=H.dev())
+    # the parent tensor (K + 9 channels) sits in one allocation between canary cells
+    st = workloads.padded_strides(N, K + 9, P, Q, layout, 0)
+    big, base = H.guarded_empty((N, K + 9, P, Q), st, torch.float32)
+    big.fill_(7.25)
     y = big[:, 4:4 + K]
     x = H.to_device(x64, "f32", layout)
     w = torch.from_numpy(w64).float().to(H.dev())
     _run(lay, x, w, y)
     H.check("f32", y.double().cpu().numpy(), ref, bound, what="subtensor")
     assert bool((big[:, :4] == 7.25).all()) and bool((big[:, 4 + K:] == 7.25).all())
-    assert bool((guard == -3.5).all())
+    assert bool(torch.isnan(base[:H.GUARD]).all()) and bool(torch.isnan(base[-H.GUARD:]).all())
 
 
 def test_nondefault_stream():
