@@ -11,7 +11,8 @@ Timing: W warm-up steps, then five timed regions of exactly K steps each,
 every region bracketed by torch.cuda.synchronize() on both sides;
 ``ms_per_step`` and ``value`` come from the median region (all five are
 reported).  Per-layer kernel times: HIP events on the launch stream around
-back-to-back launches, regions of at least 100 ms, median of five.
+back-to-back launches, median of five regions; every layer gets the same
+launch count, which makes its shortest region at least 100 ms.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
                     [--workload overfeat|alexnet|speech|tiny|prec_f64|prec_bf16|alexnet_pool|
@@ -64,6 +65,9 @@ def parse():
                     help="forward pass on channel-blocked x, filters and y with this block "
                          "(x [N][C/b][H][W][b], filters [K/b][C/b][R][S][b][b], y [N][K/b][P][Q][b]); "
                          "a tensor whose channel count b does not divide stays unblocked")
+    ap.add_argument("--layer-reps", type=int, default=0,
+                    help="launches per region of the per-layer timing (default 0: enough for the "
+                         "shortest layer's region to last 100 ms; counter runs use a few)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -145,19 +149,31 @@ def timed_regions(torch, step, steps):
     return out
 
 
-def event_ms(torch, stream, launch):
+def region_reps(torch, stream, launches):
+    """Back-to-back launches per timed region such that the region of the
+    shortest launch lasts at least MIN_REGION_S.  Every launch of the step
+    gets the same count, so a profiler's per-kernel average over the whole
+    run weights the layers alike, as the per-launch averages here do."""
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    shortest = None
+    for launch in launches:
+        launch()
+        ev0.record(stream)
+        launch()
+        ev1.record(stream)
+        ev1.synchronize()
+        one = max(ev0.elapsed_time(ev1), 1e-3)
+        shortest = one if shortest is None else min(shortest, one)
+    return max(5, int(MIN_REGION_S * 1e3 / shortest) + 1)
+
+
+def event_ms(torch, stream, launch, reps):
     """Median over REGIONS of one launch's mean duration (ms), from HIP events
-    recorded on the launch stream around back-to-back launches; each region
-    runs at least MIN_REGION_S."""
+    recorded on the launch stream around `reps` back-to-back launches."""
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     launch()
-    ev0.record(stream)
-    launch()
-    ev1.record(stream)
-    ev1.synchronize()
-    one = max(ev0.elapsed_time(ev1), 1e-3)
-    reps = max(5, int(MIN_REGION_S * 1e3 / one) + 1)
     res = []
     for _ in range(REGIONS):
         ev0.record(stream)
@@ -280,8 +296,9 @@ def main():
 
     # per-layer kernel durations with HIP events on the launch stream
     per_layer = []
+    reps = args.layer_reps or region_reps(torch, stream, [lambda plan=plan: plan(1.0, 0.0, stream) for _, plan, _ in plans])
     for lay, plan, _ in plans:
-        ms = event_ms(torch, stream, lambda: plan(1.0, 0.0, stream))
+        ms = event_ms(torch, stream, lambda: plan(1.0, 0.0, stream), reps)
         tf = plan.flops / (ms * 1e-3) / 1e12
         rec = {"layer": lay.name, "kernel": plan.kernel_name(), "us": round(ms * 1e3, 2),
                "gflop": round(plan.flops / 1e9, 3), "tflops": round(tf, 2),
@@ -359,8 +376,9 @@ def bench_pool(args, torch, mic, gen, workloads, dev):
     regions = timed_regions(torch, step, args.steps)
     elapsed = sorted(regions)[len(regions) // 2]
     per_layer = []
+    reps = args.layer_reps or region_reps(torch, stream, [lambda plan=plan: plan(1.0, 0.0, stream) for _, plan, _ in plans])
     for lay, plan, _ in plans:
-        us = event_ms(torch, stream, lambda: plan(1.0, 0.0, stream)) * 1e3
+        us = event_ms(torch, stream, lambda: plan(1.0, 0.0, stream), reps) * 1e3
         per_layer.append({"layer": lay.name, "kernel": plan.kernel_name(), "us": round(us, 2),
                           "mb": round(plan.bytes / 1e6, 2), "gbs": round(plan.bytes / (us * 1e-6) / 1e9, 1)})
     dom = max(per_layer, key=lambda r: r["us"])
@@ -435,8 +453,9 @@ def bench_fc(args, torch, mic, gen, workloads, dev):
     regions = timed_regions(torch, step, args.steps)
     elapsed = sorted(regions)[len(regions) // 2]
     per_layer = []
+    reps = args.layer_reps or region_reps(torch, stream, [lambda r=r: mic.brgemm(r[1], r[2], r[3]) for r in runs])
     for lay, a, b, c, flops, _, _ in runs:
-        us = event_ms(torch, stream, lambda: mic.brgemm(a, b, c)) * 1e3
+        us = event_ms(torch, stream, lambda: mic.brgemm(a, b, c), reps) * 1e3
         per_layer.append({"layer": lay.name, "kernel": mic.brgemm_kernel_name_for(a, b, c),
                           "us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 2),
                           "gbs": round(hbm_bytes[lay.name] / (us * 1e-6) / 1e9, 1),

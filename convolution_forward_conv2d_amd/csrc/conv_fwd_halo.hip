@@ -109,8 +109,9 @@ conv_fwd_halo_kernel(const ConvParams p)
     unsigned char* smem = smem_all + half * 2 * BUF_BYTES;
 
     const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
-    const int mt = tile / p.n_tiles;
-    const int nt = tile - mt * p.n_tiles;
+    const TileRC rc = grouped_tile(tile, p.m_tiles, p.n_tiles, p.n_group);
+    const int mt = rc.mt;
+    const int nt = rc.nt;
     // a tile covers rows m0 .. m_end-1: TM consecutive rows, or one output
     // image (m_step = P*Q <= TM, the rest of the tile idle)
     const int m0 = mt * p.m_step;
@@ -403,6 +404,16 @@ static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStrea
     if (p.m_step <= 0 || p.m_step > TM) p.m_step = TM;   // the host sets P*Q for image tiles
     p.m_tiles = (p.M + p.m_step - 1) / p.m_step;
     p.n_tiles = (p.K + TN - 1) / TN;
+    {
+        // workgroups per CU as the LDS allows (the chunk buffers of every half)
+        constexpr int ES = (int)sizeof(typename Pol::In);
+        constexpr int TK = CB * R * S;
+        constexpr int ROW8 = (TK * ES + 7) / 8;
+        constexpr int BROW = 8 * (ROW8 % 2 ? ROW8 : ROW8 + 1);
+        constexpr int BUF = ((CB * (SL * WP + 16) * ES + TN * BROW) + 15) / 16 * 16;
+        constexpr int WG_PER_CU = (160 * 1024) / (KS * 2 * BUF) > 0 ? (160 * 1024) / (KS * 2 * BUF) : 1;
+        p.n_group = choose_n_group(p, (int64_t)p.N * p.C * p.H * p.W * ES, (int64_t)p.K * p.Kred * ES, WG_PER_CU);
+    }
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
     constexpr int VK = 16 / (int)sizeof(typename Pol::In);
     if (p.wkb > 0) {

@@ -70,6 +70,7 @@ struct ConvParams {
     int wkb, wcb;
     double alpha, beta;  // converted to the accumulation type inside the kernel
     int tile_rev;        // 1: tiles run in reverse order (xcd_logical_tile); tests only
+    int n_group;         // n tiles per group of the logical tile order (grouped_tile); 0: one group
 };
 
 // Element offset of channel c in a channel-blocked dimension (block size

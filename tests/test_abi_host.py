@@ -229,6 +229,20 @@ int main() {
             if (xcd_logical_tile(b, tiles, 1) != tiles - 1 - t) { printf("rev %d %d\n", tiles, b); return 1; }
         }
     }
+    // grouped (m tile, n tile) order: a bijection onto the m_tiles x n_tiles grid for every group width
+    for (int mt = 1; mt <= 40; ++mt)
+        for (int nt = 1; nt <= 12; ++nt)
+            for (int ng = 0; ng <= nt + 1; ++ng) {
+                std::vector<int> seen(mt * nt, 0);
+                for (int t = 0; t < mt * nt; ++t) {
+                    TileRC rc = grouped_tile(t, mt, nt, ng);
+                    if (rc.mt < 0 || rc.mt >= mt || rc.nt < 0 || rc.nt >= nt || seen[rc.mt * nt + rc.nt]++) {
+                        printf("group %d %d %d %d\n", mt, nt, ng, t); return 1;
+                    }
+                    // within a group the n tiles of one m tile are consecutive
+                    if (ng > 0 && ng < nt && rc.nt / ng != (t / (mt * ng))) { printf("grp %d %d %d %d\n", mt, nt, ng, t); return 1; }
+                }
+            }
     printf("ok\n");
     return 0;
 }
