@@ -450,7 +450,8 @@ static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStrea
     X(HALO_F32_3x3_128x128_KS2, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 2)      \
     X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1)          \
     X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16, 1)               \
-    X(HALO_F64_3x3_128x64, PolF64, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1)
+    X(HALO_F64_3x3_128x64, PolF64, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1)            \
+    X(HALO_F64_3x3_176x64_KS2, PolF64, 176, 64, 1, 4, 3, 3, 4, 16, 16, 2)
 
 hipError_t launch_halo(Variant v, const ConvParams& p, bool dgrad, hipStream_t stream)
 {

@@ -43,6 +43,7 @@ enum class Variant : int {
     HALO_F64_3x3_128x128,
     HALO_F64_3x3_64x64,
     HALO_F64_3x3_128x64,           // fp64, 64 filters: two or three workgroups per CU
+    HALO_F64_3x3_176x64_KS2,       // fp64, one output image per tile, the reduction split over two halves
     HALO_BF16_3x3_128x128,  // bf16 halo kernel, channel-innermost LDS (conv_fwd_halo_bf16.hip)
     HALO_BF16_3x3_128x64,
     HALO_BF16_3x3_192x128,

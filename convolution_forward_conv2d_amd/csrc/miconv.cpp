@@ -280,6 +280,9 @@ const HaloCandidate kHalo[] = {
     // (1.03: ahead of 128x128 on one tile per CU, measured 1.11-1.13x; behind
     // 64x64 on conv5's 170 tiles, measured 0.92x)
     {{Variant::HALO_F64_3x3_128x64, 128, 64, "halo_f64_3x3_128x64"}, DType::F64, 3, 3, 4, 16, 16, 1.03, 1},
+    // one 13x13 output image (169 of 176 rows) x 64 filters, two halves per tile:
+    // K = 256 at N = 64 gives exactly one tile per CU
+    {{Variant::HALO_F64_3x3_176x64_KS2, 176, 64, "halo_f64_3x3_176x64_ks2"}, DType::F64, 3, 3, 4, 16, 16, 0.95, 2},
     {{Variant::HALO_BF16_3x3_128x128, 128, 128, "halo_bf16_3x3_128x128"}, DType::BF16, 3, 3, 16, 16, 16, 1.0, 1},
     {{Variant::HALO_BF16_3x3_128x64, 128, 64, "halo_bf16_3x3_128x64"}, DType::BF16, 3, 3, 16, 16, 16, 0.8, 1},
     {{Variant::HALO_BF16_3x3_192x128, 192, 128, "halo_bf16_3x3_192x128"}, DType::BF16, 3, 3, 16, 16, 16, 1.0, 1},

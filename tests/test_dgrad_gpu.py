@@ -34,7 +34,8 @@ DG_VARIANTS = {
             "halo_f32_5x5_128x96_c2",
             "halo_f32x16_3x3_176x128_ks2",
             "halo_f32_3x3_128x128_ks2"],
-    "f64": ["direct", "halo_f64_3x3_128x128", "halo_f64_3x3_64x64", "halo_f64_3x3_128x64"],
+    "f64": ["direct", "halo_f64_3x3_128x128", "halo_f64_3x3_64x64", "halo_f64_3x3_128x64",
+            "halo_f64_3x3_176x64_ks2"],
     "bf16": ["direct", "halo_bf16_3x3_128x64", "halo_bf16_3x3_128x128"],
 }
 # the stride-phase kernel onto 1-4 channels (fp32, fp64); NOT_SUPPORTED on other shapes

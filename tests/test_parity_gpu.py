@@ -36,7 +36,8 @@ VARIANTS = {
             "halo_f32x16_3x3_176x128_ks2",
             "halo_f32_3x3_128x128_ks2"],
     "f64": ["direct", "mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64",
-            "halo_f64_3x3_128x128", "halo_f64_3x3_64x64", "halo_f64_3x3_128x64"],
+            "halo_f64_3x3_128x128", "halo_f64_3x3_64x64", "halo_f64_3x3_128x64",
+            "halo_f64_3x3_176x64_ks2"],
     "bf16": ["direct", "mfma_bf16_128x128", "mfma_bf16_128x64", "mfma_bf16_256x32",
              "halo_bf16_3x3_128x128", "halo_bf16_3x3_128x64", "halo_bf16_3x3_192x128"],
 }
