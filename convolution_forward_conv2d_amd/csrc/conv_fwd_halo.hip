@@ -443,6 +443,7 @@ static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStrea
     X(HALO_F32_5x5_128x128, PolF32, 128, 128, 2, 2, 5, 5, 4, 32, 16, 1)          \
     X(HALO_F32_5x5_128x128_C2, PolF32, 128, 128, 2, 2, 5, 5, 2, 32, 16, 1)       \
     X(HALO_F32_5x5_128x96_C2, PolF32, 128, 96, 4, 1, 5, 5, 2, 32, 16, 1)         \
+    X(HALO_F32x16_5x5_208x64, PolF32x16, 208, 64, 1, 4, 5, 5, 4, 32, 24, 1)      \
     X(HALO_F32x16_3x3_176x128, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 1)    \
     X(HALO_F32x16_3x3_144x128, PolF32x16, 144, 128, 1, 4, 3, 3, 4, 16, 16, 1)    \
     X(HALO_F32x16_5x5_128x96, PolF32x16, 128, 96, 2, 2, 5, 5, 4, 32, 16, 1)      \

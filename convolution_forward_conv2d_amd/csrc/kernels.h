@@ -38,6 +38,7 @@ enum class Variant : int {
     HALO_F32x16_3x3_144x128,
     HALO_F32x16_5x5_128x96,        // 96 filters per tile (K = 96, e.g. a data gradient onto 96 channels)
     HALO_F32_5x5_128x96_C2,        // ... on 32x32 blocks, 2-channel chunks, four waves of 32 rows x 96
+    HALO_F32x16_5x5_208x64,        // 208 rows x 64 filters on 16x16 blocks, 1x4 waves (two workgroups per CU)
     HALO_F32x16_3x3_176x128_KS2,   // two halves split the reduction of one tile
     HALO_F32_3x3_128x128_KS2,
     HALO_F64_3x3_128x128,
@@ -66,6 +67,9 @@ enum class Variant : int {
     WGH_F32_3x3_Q13,         // ... 13 columns (32x32 blocks)
     WGH_F32X16_5x5_Q20,      // ... 5x5, 20 columns
     WGH_F32X16_5x5_Q27,      // ... 5x5, 27 columns
+    WGC_BF16_64x64,         // filter gradient, bf16, channels-last x and dy (conv_bwd_filter_cl.hip)
+    WGC_BF16_64x64_KS2,     // ... two groups of waves split the reduction
+    WGC_BF16_64x64_KS3,     // ... three groups
     WGS_F32_32x32,          // filter gradient, reduction split over waves (conv_bwd_filter_split.hip)
     WGS_F32_16x16,
     WGS_F32_8x16,
@@ -116,6 +120,7 @@ hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream);
 hipError_t launch_bwd_filter(Variant v, const ConvParams& p, hipStream_t stream);
 hipError_t launch_bwd_filter_split(Variant v, const ConvParams& p, hipStream_t stream);
+hipError_t launch_bwd_filter_cl(Variant v, const ConvParams& p, hipStream_t stream);
 
 // Batch-reduce GEMM; p laid out as brgemm.hip describes.  16-byte operand
 // loads are chosen inside when strides, k and alignment allow them.

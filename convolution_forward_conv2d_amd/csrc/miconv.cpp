@@ -157,7 +157,7 @@ const Candidate kRows1N6F32 = {Variant::ROWS1N6_F32_S11_256x32, 256, 32, "rows1n
 // small tiles, tensors under 2 GiB).  ns is the measured time of one tile
 // per reduction position (N*P*Q) on MI355X with per_cu workgroups resident
 // on a compute unit; the plan picks the least rounds * ns.
-enum class WgKind { GATHER, HALO, SPLIT, ROWS };
+enum class WgKind { GATHER, HALO, SPLIT, ROWS, CL };
 struct WgCandidate {
     Candidate c;
     DType dt;
@@ -193,6 +193,11 @@ const WgCandidate kWg[] = {
     {{Variant::WGS_F64_32x32, 32, 32, "wgs_f64_32x32"}, DType::F64, WgKind::SPLIT, 0, 0, 0, 28.0, 1},
     {{Variant::WGS_F64_16x16, 16, 16, "wgs_f64_16x16"}, DType::F64, WgKind::SPLIT, 0, 0, 0, 5.7, 1},
     {{Variant::WGS_BF16_32x32, 32, 32, "wgs_bf16_32x32"}, DType::BF16, WgKind::SPLIT, 0, 0, 0, 15.8, 2},
+    // bf16 with channels-last x and dy: 64 filters x 64 channels of one tap,
+    // operands transposed on their way out of LDS
+    {{Variant::WGC_BF16_64x64, 64, 64, "wgc_bf16_64x64"}, DType::BF16, WgKind::CL, 0, 0, 0, 15.0, 2},
+    {{Variant::WGC_BF16_64x64_KS3, 64, 64, "wgc_bf16_64x64_ks3"}, DType::BF16, WgKind::CL, 0, 0, 0, 6.0, 1},
+    {{Variant::WGC_BF16_64x64_KS2, 64, 64, "wgc_bf16_64x64_ks2"}, DType::BF16, WgKind::CL, 0, 0, 0, 8.0, 2},
     // first layers on the vector ALU: tiles of KT filters x S taps of one
     // (c, r); ns here is the time of one output row per tile, the cost that
     // time over Q (measured on MI355X: speech L1 770 us, Overfeat L1 855 us)
@@ -214,6 +219,11 @@ bool is_wgh(Variant v)
 }
 
 bool is_wgr(Variant v) { return v == Variant::WGR_F32_S11_V2 || v == Variant::WGR_F32_S11_V4; }
+
+bool is_wgc(Variant v)
+{
+    return v == Variant::WGC_BF16_64x64 || v == Variant::WGC_BF16_64x64_KS2 || v == Variant::WGC_BF16_64x64_KS3;
+}
 
 bool is_wgs(Variant v)
 {
@@ -273,6 +283,7 @@ const HaloCandidate kHalo[] = {
     {{Variant::HALO_F32x16_3x3_144x128, 144, 128, "halo_f32x16_3x3_144x128"}, DType::F32, 3, 3, 4, 16, 16, 0.95, 1},
     {{Variant::HALO_F32x16_5x5_128x96, 128, 96, "halo_f32x16_5x5_128x96"}, DType::F32, 5, 5, 4, 32, 16, 0.85, 1},
     {{Variant::HALO_F32_5x5_128x96_C2, 128, 96, "halo_f32_5x5_128x96_c2"}, DType::F32, 5, 5, 2, 32, 16, 0.98, 1},
+    {{Variant::HALO_F32x16_5x5_208x64, 208, 64, "halo_f32x16_5x5_208x64"}, DType::F32, 5, 5, 4, 32, 24, 0.9, 1},
     {{Variant::HALO_F32x16_3x3_176x128_KS2, 176, 128, "halo_f32x16_3x3_176x128_ks2"}, DType::F32, 3, 3, 4, 16, 16, 0.95, 2},
     {{Variant::HALO_F32_3x3_128x128_KS2, 128, 128, "halo_f32_3x3_128x128_ks2"}, DType::F32, 3, 3, 4, 16, 16, 0.9, 2},
     {{Variant::HALO_F64_3x3_128x128, 128, 128, "halo_f64_3x3_128x128"}, DType::F64, 3, 3, 4, 16, 16, 1.0, 1},
@@ -1015,6 +1026,11 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
             ok = split_fits;
         else if (wc.kind == WgKind::ROWS)
             ok = miconv::bwd_filter_rows_fits(wc.c.v, p);
+        else if (wc.kind == WgKind::CL)
+            // 16-byte loads of 8 consecutive filters / channels at every position
+            ok = xd->sc == 1 && dyd->sc == 1 && wd->k % 8 == 0 && wd->c % 8 == 0 && xd->sn % 8 == 0 &&
+                 xd->sh % 8 == 0 && xd->sw % 8 == 0 && dyd->sn % 8 == 0 && dyd->sh % 8 == 0 &&
+                 dyd->sw % 8 == 0 && (!need_pointers || ((uintptr_t)x % 16 == 0 && (uintptr_t)dy % 16 == 0));
         // 8-filter split tiles double the tile count at 1.5x the loads per
         // position: worth it only when 16x16 tiles leave most CUs idle
         // (measured: speech L1, 58 tiles, 4.7 -> 4.1 ms; Overfeat L1, 138
@@ -1640,6 +1656,7 @@ mic_status mic_conv_backward_filter(mic_handle handle, double alpha, mic_tensor_
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
     pl.p.tile_rev = tile_order_reversed();
     const hipError_t err = is_wgh(pl.cand.v)   ? miconv::launch_bwd_filter_halo(pl.cand.v, pl.p, handle->stream)
+                           : is_wgc(pl.cand.v) ? miconv::launch_bwd_filter_cl(pl.cand.v, pl.p, handle->stream)
                            : is_wgs(pl.cand.v) ? miconv::launch_bwd_filter_split(pl.cand.v, pl.p, handle->stream)
                            : is_wgr(pl.cand.v) ? miconv::launch_bwd_filter_rows(pl.cand.v, pl.p, handle->stream)
                                                : miconv::launch_bwd_filter(pl.cand.v, pl.p, handle->stream);

@@ -136,7 +136,8 @@ def test_kernel_choice_host_only():
                  "overfeat_l5"):
         assert names[name].startswith(("halo_f32_3x3_", "halo_f32x16_3x3_")), (name, names[name])
     assert names["alexnet_conv2"].startswith("halo_f32_5x5_")
-    assert names["overfeat_l2"].startswith("halo_f32_5x5_")
+    # 20x20 outputs, 256 filters: 208-row x 64-filter tiles on 16x16 blocks (988 tiles, about four per CU)
+    assert names["overfeat_l2"] == "halo_f32x16_5x5_208x64"
     assert names["overfeat_l1"] == "rows1n6_f32_s11_256x32"      # 3 channels, 56-wide output rows
     # 21x11 filters, 32 filters, Q = 350 >= the 256-position tile: reduction streamed by filter row
     assert names["speech_l2"] == "rows_f32_s11_256x32"
@@ -381,6 +382,41 @@ def _wgrad_name(lay, dts=None):
         return mic.mic_conv_backward_filter_kernel_name(None, xd, yd, cd, wd)
     finally:
         _free(xd, wd, cd, yd)
+
+
+def _wgrad_name_same_layout(lay, k=None):
+    """Like _wgrad_name, with dy in the layer's own layout (and row pitch)."""
+    xd, wd, yd, cd = (mic.mic_tensor_desc_create(), mic.mic_filter_desc_create(),
+                      mic.mic_tensor_desc_create(), mic.mic_conv_desc_create())
+    try:
+        dt = {"f32": 0, "f64": 1, "bf16": 2}[lay.dtype]
+        K = lay.K if k is None else k
+        xs = workloads.padded_strides(lay.N, lay.C, lay.H, lay.W, lay.layout, lay.row_pitch)
+        mic.mic_tensor_desc_set(xd, dt, *lay.x_shape, *xs)
+        mic.mic_filter_desc_set(wd, 1 if dt == 1 else 0, K, lay.C, lay.R, lay.S)
+        mic.mic_conv_desc_set(cd, *lay.padding, *lay.stride)
+        N, K, P, Q = mic.mic_conv_forward_output_dim(cd, xd, wd)
+        ys = workloads.padded_strides(N, K, P, Q, lay.layout, lay.row_pitch)
+        mic.mic_tensor_desc_set(yd, dt, N, K, P, Q, *ys)
+        return mic.mic_conv_backward_filter_kernel_name(None, xd, yd, cd, wd)
+    finally:
+        _free(xd, wd, cd, yd)
+
+
+def test_wgrad_channels_last_bf16_choice_host_only():
+    """bf16 with channels-last x and dy goes to the transposing-read kernel: three wave groups
+    where the tiles fit one per compute unit (conv3, conv5: 216 tiles), two where two workgroups
+    share a unit (conv4: 324 tiles); channel counts that are not multiples of 8 cannot take it."""
+    want = {"prec_conv3_bf16_nhwc": "wgc_bf16_64x64_ks3", "prec_conv4_bf16_nhwc": "wgc_bf16_64x64_ks2",
+            "prec_conv5_bf16_nhwc": "wgc_bf16_64x64_ks3"}
+    for lay in workloads.PRECISION:
+        name = _wgrad_name_same_layout(lay)
+        if lay.name in want:
+            assert name == want[lay.name], (lay.name, name)
+        else:
+            assert not name.startswith("wgc_"), (lay.name, name)
+    lay = workloads.by_name("prec_conv3_bf16_nhwc")
+    assert not _wgrad_name_same_layout(lay, k=100).startswith("wgc_")      # K % 8 != 0
 
 
 def test_wgrad_first_layer_kernel_limits(monkeypatch):

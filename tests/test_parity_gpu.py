@@ -33,6 +33,7 @@ VARIANTS = {
             "halo_f32_3x3_128x128", "halo_f32_3x3_128x64", "halo_f32_3x3_64x128", "halo_f32_3x3_96x128",
             "halo_f32_5x5_128x128", "halo_f32_5x5_128x128_c2", "halo_f32x16_3x3_176x128",
             "halo_f32x16_3x3_144x128", "halo_f32x16_5x5_128x96", "halo_f32_5x5_128x96_c2",
+            "halo_f32x16_5x5_208x64",
             "halo_f32x16_3x3_176x128_ks2",
             "halo_f32_3x3_128x128_ks2"],
     "f64": ["direct", "mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64",

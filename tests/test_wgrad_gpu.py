@@ -49,7 +49,10 @@ WG_VARIANTS["f32"] += ["wgr_f32_s11_v2", "wgr_f32_s11_v4"]
 # the halo variants (wgh_) take stride-1 layers of their filter size whose rows fit their pitch, the
 # wgr_ variants their stride and filter width; the library answers NOT_SUPPORTED for other shapes,
 # and every variant must run on at least one shape
-_MAY_REFUSE = ("wgh_", "wgr_")
+# the channels-last bf16 kernel (wgc_) takes x and dy with channel stride 1 and
+# 8-aligned strides and channel counts
+WG_VARIANTS["bf16"] += ["wgc_bf16_64x64", "wgc_bf16_64x64_ks2", "wgc_bf16_64x64_ks3"]
+_MAY_REFUSE = ("wgh_", "wgr_", "wgc_")
 _ran = set()
 
 
