@@ -46,9 +46,14 @@
 
 namespace miconv {
 
+// WPE: the fewest waves per SIMD the register allocation must leave room for
+// (1: no constraint).  Two for instances whose LDS admits two workgroups per
+// CU but whose unconstrained allocation would not (Overfeat L2 on 208 x 64
+// tiles: 603 -> 520 us; AlexNet conv2-conv4 and the fp64 128 x 64 tiles
+// 1-2% faster); a cap would hurt the instances that run three.
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS,
-          bool DG, bool WB>
-__global__ void __launch_bounds__(256 * KS)
+          bool DG, bool WB, int WPE>
+__global__ void __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(WPE)))
 conv_fwd_halo_kernel(const ConvParams p)
 {
     using In = typename Pol::In;
@@ -397,7 +402,7 @@ conv_fwd_halo_kernel(const ConvParams p)
 
 // ------------------------------------------------------------------ instances and launch
 
-template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS>
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS, int WPE>
 static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStream_t stream)
 {
     ConvParams p = p0;
@@ -422,43 +427,43 @@ static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStrea
         if (dgrad || p.wcb % CB != 0 || p.wkb % VK != 0 || p.K % p.wkb != 0 || p.C % p.wcb != 0 ||
             (uintptr_t)p.w % 16 != 0)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, true>),
+        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, true, WPE>),
                            grid, dim3(256 * KS), 0, stream, p);
     } else if (dgrad) {
-        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, true, false>),
+        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, true, false, WPE>),
                            grid, dim3(256 * KS), 0, stream, p);
     } else {
-        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, false>),
+        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, false, WPE>),
                            grid, dim3(256 * KS), 0, stream, p);
     }
     return hipGetLastError();
 }
 
-//        name                     policy     TM   TN  waves  R  S  CB  WP  SL  KS
+//        name                     policy     TM   TN  waves  R  S  CB  WP  SL  KS  WPE
 #define MICONV_HALO_VARIANTS(X)                                                 \
-    X(HALO_F32_3x3_128x128, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1)          \
-    X(HALO_F32_3x3_128x64, PolF32, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1)            \
-    X(HALO_F32_3x3_64x128, PolF32, 64, 128, 2, 2, 3, 3, 4, 16, 16, 1)            \
-    X(HALO_F32_3x3_96x128, PolF32, 96, 128, 1, 4, 3, 3, 4, 16, 16, 1)            \
-    X(HALO_F32_5x5_128x128, PolF32, 128, 128, 2, 2, 5, 5, 4, 32, 16, 1)          \
-    X(HALO_F32_5x5_128x128_C2, PolF32, 128, 128, 2, 2, 5, 5, 2, 32, 16, 1)       \
-    X(HALO_F32_5x5_128x96_C2, PolF32, 128, 96, 4, 1, 5, 5, 2, 32, 16, 1)         \
-    X(HALO_F32x16_5x5_208x64, PolF32x16, 208, 64, 1, 4, 5, 5, 4, 32, 24, 1)      \
-    X(HALO_F32x16_3x3_176x128, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 1)    \
-    X(HALO_F32x16_3x3_144x128, PolF32x16, 144, 128, 1, 4, 3, 3, 4, 16, 16, 1)    \
-    X(HALO_F32x16_5x5_128x96, PolF32x16, 128, 96, 2, 2, 5, 5, 4, 32, 16, 1)      \
-    X(HALO_F32x16_3x3_176x128_KS2, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 2) \
-    X(HALO_F32_3x3_128x128_KS2, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 2)      \
-    X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1)          \
-    X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16, 1)               \
-    X(HALO_F64_3x3_128x64, PolF64, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1)            \
-    X(HALO_F64_3x3_176x64_KS2, PolF64, 176, 64, 1, 4, 3, 3, 4, 16, 16, 2)
+    X(HALO_F32_3x3_128x128, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1, 2)          \
+    X(HALO_F32_3x3_128x64, PolF32, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1, 1)            \
+    X(HALO_F32_3x3_64x128, PolF32, 64, 128, 2, 2, 3, 3, 4, 16, 16, 1, 1)            \
+    X(HALO_F32_3x3_96x128, PolF32, 96, 128, 1, 4, 3, 3, 4, 16, 16, 1, 1)            \
+    X(HALO_F32_5x5_128x128, PolF32, 128, 128, 2, 2, 5, 5, 4, 32, 16, 1, 1)          \
+    X(HALO_F32_5x5_128x128_C2, PolF32, 128, 128, 2, 2, 5, 5, 2, 32, 16, 1, 2)       \
+    X(HALO_F32_5x5_128x96_C2, PolF32, 128, 96, 4, 1, 5, 5, 2, 32, 16, 1, 1)         \
+    X(HALO_F32x16_5x5_208x64, PolF32x16, 208, 64, 1, 4, 5, 5, 4, 32, 24, 1, 2)      \
+    X(HALO_F32x16_3x3_176x128, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 1, 1)    \
+    X(HALO_F32x16_3x3_144x128, PolF32x16, 144, 128, 1, 4, 3, 3, 4, 16, 16, 1, 1)    \
+    X(HALO_F32x16_5x5_128x96, PolF32x16, 128, 96, 2, 2, 5, 5, 4, 32, 16, 1, 1)      \
+    X(HALO_F32x16_3x3_176x128_KS2, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 2, 1) \
+    X(HALO_F32_3x3_128x128_KS2, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 2, 1)      \
+    X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1, 1)          \
+    X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16, 1, 1)               \
+    X(HALO_F64_3x3_128x64, PolF64, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1, 2)            \
+    X(HALO_F64_3x3_176x64_KS2, PolF64, 176, 64, 1, 4, 3, 3, 4, 16, 16, 2, 1)
 
 hipError_t launch_halo(Variant v, const ConvParams& p, bool dgrad, hipStream_t stream)
 {
     switch (v) {
-#define X(name, pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks) \
-    case Variant::name: return launch_halo_variant<pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks>(p, dgrad, stream);
+#define X(name, pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks, wpe) \
+    case Variant::name: return launch_halo_variant<pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks, wpe>(p, dgrad, stream);
         MICONV_HALO_VARIANTS(X)
 #undef X
     default: return dgrad ? hipErrorInvalidValue : launch_halo_bf16(v, p, stream);
