@@ -17,7 +17,8 @@ SOURCES = ["miconv.cpp", "conv_fwd_mfma.hip", "conv_fwd_halo.hip", "conv_fwd_hal
            "conv_fwd_direct.hip", "conv_bwd_data.hip", "conv_bwd_filter.hip",
            "pool_fwd.hip", "brgemm.hip", "conv_bwd_filter_halo.hip",
            "conv_bwd_filter_split.hip", "conv_bwd_data_phase.hip", "conv_fwd_rows.hip",
-           "conv_bwd_data_subpixel.hip", "conv_bwd_filter_rows.hip", "conv_bwd_filter_cl.hip"]
+           "conv_bwd_data_subpixel.hip", "conv_bwd_filter_rows.hip", "conv_bwd_filter_cl.hip",
+           "conv_bwd_data_taps.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

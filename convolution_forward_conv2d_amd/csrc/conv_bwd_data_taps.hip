@@ -1,0 +1,248 @@
+// conv_bwd_data_taps.hip -- data gradient of a strided layer onto few input
+// channels (a first layer: the speech network's 41 x 11 bank at stride 2 onto
+// one channel) on gfx950 MFMA, with the filter's column taps as the GEMM's
+// columns.
+//
+//   dx[n,c,h,w] = alpha * sum_{k,r,s: h + pt - r = u p, w + pl - s = v q} dy[n,k,p,q] * F[k,c,r,s] + beta * dx
+//
+// (the backward routine in x that the cuDNN page, "Proposed Method", lists
+// beside the forward one; the maxDNN page, Abstract and RQ4, expects the
+// forward techniques to carry over to it).  Onto one channel the usual
+// implicit GEMM has a single column; here the columns are the S taps of a
+// filter row instead.  For the row phase a = (h + pt) mod u, with
+// h + pt = u P' + a, the rows reaching h are r = a + u i at p = P' - i, so
+//
+//   Z[P', q, s] = sum_k sum_i dy[n, k, P' - i, q] * F[k, c, a + u i, s]
+//   dx[n, c, h, w] = sum over s with (w + pl - s) = v q, 0 <= q < Q, of Z[P', q, s]
+//
+// Z is an implicit GEMM -- rows (P', q), columns s, reduction (k, i) -- whose
+// operands are plain dy rows and filter taps; the second sum, a handful of
+// terms per output, runs from LDS in the epilogue.  No multiply-add falls off
+// the stride grid; the waste is the column padding (S of 16) and the rows'
+// q padding to whole 16-blocks.
+//
+// A workgroup takes one image n, channel c, phase a and a band of TB
+// consecutive phase rows P'.  The reduction runs channel by channel of dy:
+// a chunk stages the TB + 4*IS - 1 dy rows P'_0 + TB - 1 - i (zeros outside
+// dy) of QP = 16*QB columns in LDS, double-buffered; 16x16x4 fp32 MFMA blocks
+// (PolF32x16), the four lane groups taking four consecutive i, each lane's
+// filter tap F[k, c, a + u i, s] read straight from memory (zero for i past
+// the phase's taps or s past S).  The 4 waves split the TB * QB row blocks.
+//
+// Parameters (direct layout, as conv_bwd_data_phase.hip): x = dy and its
+// strides sx*, w = F (packed K,C,R,S), y = dx and its strides sy*; N, C, H, W
+// dx's dims; K, P, Q dy's; R, S, u, v, pad_top, pad_left the forward
+// geometry.  The host checks: fp32, S <= 16, Q <= QP, ceil(R/u) <= 4*IS.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "conv_params.h"
+#include "kernels.h"
+#include "mfma_common.h"
+
+namespace miconv {
+
+template <int TB, int QB, int IS>
+__global__ void __launch_bounds__(256)
+conv_bwd_data_taps_kernel(const ConvParams p, int bands)
+{
+    using Pol = PolF32x16;
+    using AccV = Pol::AccV;
+    constexpr int NT = 256;
+    constexpr int QP = 16 * QB;                  // staged columns per dy row
+    constexpr int NI = 4 * IS;                   // taps i per chunk (zero past the phase's)
+    constexpr int ROWS = TB + NI - 1;            // staged dy rows per chunk
+    constexpr int BUF = ROWS * QP;               // floats
+    constexpr int NBLK = TB * QB;                // 16-row blocks of the tile
+    constexpr int FM = (NBLK + 3) / 4;           // blocks per wave
+    constexpr int NL = (BUF + NT - 1) / NT;      // staged values per thread per chunk
+    constexpr int ZP = 17;                       // epilogue: floats per (P', q) row of Z (16 taps + pad)
+    static_assert(TB * QP * ZP <= 2 * BUF, "the epilogue's Z fits in the chunk buffers");
+    static_assert(NL <= 64, "staging mask");
+
+    __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    // blockIdx.x -> (band, phase a, channel c, image n), band fastest
+    int bid = (int)blockIdx.x;
+    const int band = bid % bands;
+    bid /= bands;
+    const int a = bid % p.u;
+    bid /= p.u;
+    const int c = bid % p.C;
+    const int n = bid / p.C;
+    // phase rows P' of dx rows h = u P' + a - pt inside [0, H)
+    const int h_first = ((a - p.pad_top) % p.u + p.u) % p.u;     // smallest h >= 0 of the phase
+    if (h_first >= p.H) return;
+    const int P_lo = (h_first + p.pad_top - a) / p.u;
+    const int P_hi = (p.H - 1 - ((p.H - 1 - h_first) % p.u) + p.pad_top - a) / p.u;
+    const int P0 = P_lo + band * TB;
+    if (P0 > P_hi) return;                        // uniform: the band lies past the phase's rows
+    const int Ia = (p.R - a + p.u - 1) / p.u;     // taps i of the phase (a + u i < R)
+
+    const float* __restrict__ dy = static_cast<const float*>(p.x);
+    const float* __restrict__ F = static_cast<const float*>(p.w);
+    const float* __restrict__ dyn = dy + (int64_t)n * p.sxn;
+
+    // ---- staging: value e = (staged row j, column q): dy row P0 + TB - 1 - j
+    int st_off[NL];
+    uint64_t st_ok = 0;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int e = tid + NT * i;
+        const int j = e / QP;
+        const int q = e - j * QP;
+        const int prow = P0 + TB - 1 - j;
+        const bool ok = e < BUF && q < p.Q && prow >= 0 && prow < p.P;
+        st_off[i] = ok ? prow * p.sxh + q * p.sxw : 0;
+        st_ok |= (ok ? uint64_t(1) : uint64_t(0)) << i;
+    }
+    float sv[NL];
+    auto load_chunk = [&](int k) {
+        const float* src = dyn + k * p.sxc;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) sv[i] = src[st_off[i]];
+    };
+    auto store_chunk = [&](int buf) {
+        float* dst = smem + buf * BUF;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int e = tid + NT * i;
+            if (BUF % NT == 0 || e < BUF) dst[e] = ((st_ok >> i) & 1) ? sv[i] : 0.0f;
+        }
+    };
+
+    // ---- MFMA geometry: wave w takes blocks w, w + 4, ... of the TB x QB grid;
+    // lane l: A row (position) l % 16 of the block, lane group g = l / 16 takes tap i = 4t + g
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    int a_base[FM];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+        const int b = wave + 4 * f;
+        const int pb = b / QB;                    // phase row within the band
+        const int qb = b - pb * QB;
+        // staged row of (P0 + pb) - i is TB - 1 - pb + i
+        a_base[f] = (b < NBLK ? (TB - 1 - pb + g) * QP + qb * 16 + l16 : 0);
+    }
+    // B: F[k, c, a + u i, s] with i = 4t + g and s = l16 (zero past the taps)
+    const bool s_ok = l16 < p.S;
+    int b_off[IS];
+    uint32_t b_ok = 0;
+#pragma unroll
+    for (int t = 0; t < IS; ++t) {
+        const int i = 4 * t + g;
+        const int r = a + p.u * i;
+        const bool ok = s_ok && i < Ia && r < p.R;
+        b_off[t] = ok ? (c * p.R + r) * p.S + l16 : 0;
+        b_ok |= (ok ? 1u : 0u) << t;
+    }
+    const int fk = p.C * p.R * p.S;               // filter stride between k
+
+    AccV acc[FM];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) acc[f] = AccV{};
+
+    float bv[IS];
+    auto load_b = [&](int k) {
+#pragma unroll
+        for (int t = 0; t < IS; ++t) bv[t] = ((b_ok >> t) & 1) ? F[k * fk + b_off[t]] : 0.0f;
+    };
+
+    load_chunk(0);
+    store_chunk(0);
+    load_b(0);
+    __syncthreads();
+    for (int k = 0; k < p.K; ++k) {
+        const int cur = k & 1;
+        const bool more = k + 1 < p.K;
+        if (more) load_chunk(k + 1);
+        const float* buf = smem + cur * BUF;
+        float bcur[IS];
+#pragma unroll
+        for (int t = 0; t < IS; ++t) bcur[t] = bv[t];
+        if (more) load_b(k + 1);
+#pragma unroll
+        for (int t = 0; t < IS; ++t) {
+#pragma unroll
+            for (int f = 0; f < FM; ++f) {
+                if (wave + 4 * f < NBLK) {
+                    const float av = buf[a_base[f] + 4 * t * QP];
+                    acc[f] = Pol::mfma_s(av, bcur[t], acc[f]);
+                }
+            }
+        }
+        if (more) store_chunk(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: Z -> LDS as [pb][q][s] (17 floats per (pb, q)), then each
+    // output of the band sums its taps
+    float* Z = smem;
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+        const int b = wave + 4 * f;
+        if (b < NBLK) {
+            const int pb = b / QB;
+            const int qb = b - pb * QB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = Pol::row(e, lane);          // position within the block
+                const int s = Pol::col(e, lane);          // tap
+                Z[(pb * QP + qb * 16 + m) * ZP + s] = acc[f][e];
+            }
+        }
+    }
+    __syncthreads();
+    float* dx = static_cast<float*>(p.y);
+    const float alpha = (float)p.alpha;
+    const float beta = (float)p.beta;
+    for (int e = tid; e < TB * p.W; e += NT) {
+        const int pb = e / p.W;
+        const int w = e - pb * p.W;
+        const int Pp = P0 + pb;
+        const int h = p.u * Pp + a - p.pad_top;
+        if (Pp > P_hi || h < 0 || h >= p.H) continue;
+        const int wp = w + p.pad_left;
+        float sum = 0.0f;
+        // taps s = wp - v q for q = floor(wp / v) down to the first with s >= S
+        for (int q = wp / p.v; q >= 0; --q) {
+            const int s = wp - p.v * q;
+            if (s >= p.S) break;
+            if (q < p.Q) sum += Z[(pb * QP + q) * ZP + s];
+        }
+        float* o = dx + (int64_t)n * p.syn + (int64_t)c * p.syk + (int64_t)h * p.syp + (int64_t)w * p.syq;
+        *o = beta != 0.0f ? alpha * sum + beta * *o : alpha * sum;
+    }
+}
+
+// phase rows of the phase with the most rows (bands per phase)
+static int taps_rows_per_phase(const ConvParams& p)
+{
+    return (p.H + p.u - 1) / p.u;
+}
+
+constexpr int kTapsTB = 2, kTapsQB = 22, kTapsIS = 6;
+
+bool bwd_data_taps_fits(const ConvParams& p)
+{
+    return p.S <= 16 && p.Q <= 16 * kTapsQB && (p.R + p.u - 1) / p.u <= 4 * kTapsIS && p.K >= 1 && p.v >= 1 &&
+           p.u >= 1;
+}
+
+hipError_t launch_bwd_data_taps(const ConvParams& p, hipStream_t stream)
+{
+    if (!bwd_data_taps_fits(p)) return hipErrorInvalidValue;
+    const int bands = (taps_rows_per_phase(p) + kTapsTB - 1) / kTapsTB;
+    const int64_t grid = (int64_t)p.N * p.C * p.u * bands;
+    if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((conv_bwd_data_taps_kernel<kTapsTB, kTapsQB, kTapsIS>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p, bands);
+    return hipGetLastError();
+}
+
+}  // namespace miconv

@@ -40,6 +40,13 @@
 // adjacent in memory) and packs tap RS-1-t of its runs into 8 bytes of slab
 // tap t.
 //
+// WB = true reads blocked filters [K/kb][C/cb][R][S][cb][kb] (the forward
+// pass; kb a multiple of 8, cb of 16): there 8 consecutive filters of one
+// (channel, tap) are one 16-byte load.  A thread takes blocks of (tap, 8-channel
+// group, 8 filters): 8 loads, one per channel, and an 8 x 8 transpose of the
+// 16-bit values in registers (byte permutes) gives each filter's 8 channels,
+// stored as the same slab units the KCRS loader writes.
+//
 // Eligibility (checked by the host): R and S equal to the instance's; C a
 // multiple of 16; W + pad_left + pad_right <= WP; every tile's slot span
 // <= SL; w 16-byte aligned (the forward pass).
@@ -59,7 +66,7 @@ namespace miconv {
 // filter n of a tile keeps group g of a tap at 16-byte unit 2n + (g ^ swz(n))
 __device__ __forceinline__ int slab_swz(int n) { return ((n >> 2) ^ (n >> 3)) & 1; }
 
-template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL, bool CVEC, bool DG>
+template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL, bool CVEC, bool DG, bool WB>
 __global__ void __launch_bounds__(256)
 conv_fwd_halo_bf16_kernel(const ConvParams p)
 {
@@ -84,6 +91,12 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
     constexpr int NV = RS;                        // 16-byte vectors per slab unit: 8 channels x RS taps
     constexpr int ND = DG ? 4 * RS : 1;           // DG: 2-byte loads per half unit (4 runs of RS taps)
     constexpr int BUF_BYTES = HALO_BYTES + SLAB_BYTES;
+    // WB: transpose blocks (tap, group, filter octet) per chunk, per thread
+    constexpr int OCT = TN / 8;
+    constexpr int NB = RS * 2 * OCT;
+    constexpr int WBT = WB ? (NB + NT - 1) / NT : 0;
+    static_assert(!(WB && DG), "blocked filters in the forward pass only");
+    static_assert(TN % 8 == 0, "whole filter octets");
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
     static_assert(BUF_BYTES % 16 == 0, "16-byte aligned buffers");
     static_assert(4 * BM * (BM + 1) * 4 <= 2 * BUF_BYTES, "epilogue stage fits");
@@ -155,6 +168,27 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
         s_ok |= (ok ? 1u : 0u) << i;
     }
 
+    // WB: block b = (tap t, group g, octet o), octet fastest (consecutive lanes
+    // read consecutive 16-byte pieces of one (channel, tap) filter row)
+    int wb_off[WB ? WBT : 1];
+    uint32_t wb_ok = 0;
+    if constexpr (WB) {
+        const int cblk = RS * p.wcb * p.wkb;             // elements of one (filter block, channel block)
+#pragma unroll
+        for (int i = 0; i < WBT; ++i) {
+            const int b = tid + NT * i;
+            const int o = b % OCT;
+            const int tg = b / OCT;
+            const int g = tg & 1;
+            const int t = tg >> 1;
+            const int k = n0 + 8 * o;
+            const bool ok = b < NB && k < p.K;
+            wb_off[i] = ok ? (k / p.wkb) * (p.C / p.wcb) * cblk + (t * p.wcb + 8 * g) * p.wkb + k % p.wkb : 0;
+            wb_ok |= (ok ? 1u : 0u) << i;
+        }
+    }
+    u32x4 wb_val[WB ? WBT : 1][8];
+
     // registers of the chunk in flight
     uint32_t h_raw[CVEC ? 1 : HUT][8];
     u32x4 h_vec[CVEC ? HUT : 1];
@@ -165,8 +199,8 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
     // one global load (a 2-byte channel value or a 16-byte vector), store
     // piece q one 16-byte LDS write (a halo unit, or one tap of a slab unit).
     constexpr int NLH = CVEC ? HUT : 8 * HUT;    // halo load pieces
-    constexpr int NL = NLH + SUT * (DG ? ND : NV);   // load pieces per chunk
-    constexpr int NS = HUT + SUT * RS;           // store pieces per chunk
+    constexpr int NL = NLH + (WB ? 8 * WBT : SUT * (DG ? ND : NV));   // load pieces per chunk
+    constexpr int NS = HUT + (WB ? 8 * WBT : SUT * RS);              // store pieces per chunk
 
     // Loads are unconditional (a unit outside the input or past K reads the
     // chunk's first element of x or w instead, which exists) and their
@@ -181,6 +215,11 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
                 const int i = q / 8, j = q % 8;
                 h_raw[i][j] = x[h_off[i] + x_chunk(c0) + j * p.sxc];
             }
+        } else if constexpr (WB) {
+            // the chunk's 16 channels lie in one channel block
+            const int i = (q - NLH) / 8, j = (q - NLH) % 8;
+            const int co = (c0 / p.wcb) * (RS * p.wcb * p.wkb) + (c0 % p.wcb) * p.wkb;
+            wb_val[i][j] = *reinterpret_cast<const u32x4*>(w + wb_off[i] + co + j * p.wkb);
         } else if constexpr (DG) {
             const int i = (q - NLH) / ND, v = (q - NLH) % ND;
             const int j = v / RS, t = v % RS;
@@ -214,6 +253,28 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
 #pragma unroll
                 for (int d = 0; d < 4; ++d) val[d] = ok ? val[d] : 0u;
                 *reinterpret_cast<u32x4*>(hb + pix * PIX + 16 * g) = val;
+            }
+        } else if constexpr (WB) {
+            // filter f of block i: dword d holds channels 2d, 2d+1, i.e. the
+            // 16-bit half f%2 of word f/2 of channel rows 2d and 2d+1
+            const int i = (q - HUT) / 8, f = (q - HUT) % 8;
+            const int b = tid + NT * i;
+            if (NB % NT == 0 || b < NB) {
+                const int o = b % OCT;
+                const int tg = b / OCT;
+                const int g = tg & 1;
+                const int t = tg >> 1;
+                const int row = 8 * o + f;
+                const bool ok = (wb_ok >> i) & 1;
+                u32x4 out;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t lo = wb_val[i][2 * d][f >> 1];
+                    const uint32_t hi = wb_val[i][2 * d + 1][f >> 1];
+                    const uint32_t v = (f & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+                    out[d] = ok ? v : 0u;
+                }
+                *reinterpret_cast<u32x4*>(hb + HALO_BYTES + t * TAP_BYTES + 16 * (2 * row + (g ^ slab_swz(row)))) = out;
             }
         } else {
             const int i = (q - HUT) / RS, t = (q - HUT) % RS;
@@ -365,7 +426,11 @@ template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL
 static hipError_t launch_halo_bf16_variant(const ConvParams& p0, bool dgrad, hipStream_t stream)
 {
     ConvParams p = p0;
-    if (p.wkb > 0) return hipErrorInvalidValue;          // packed KCRS filters only
+    // blocked filters: the host checked kb % 8 == 0, cb % 16 == 0, K % kb == 0,
+    // C % cb == 0 and a 16-byte aligned w (forward pass only)
+    if (p.wkb > 0 && (dgrad || p.wkb % 8 != 0 || p.wcb % 16 != 0 || p.K % p.wkb != 0 || p.C % p.wcb != 0 ||
+                      (uintptr_t)p.w % 16 != 0))
+        return hipErrorInvalidValue;
     if (p.m_step <= 0 || p.m_step > TM) p.m_step = TM;   // the host sets P*Q for image tiles
     p.m_tiles = (p.M + p.m_step - 1) / p.m_step;
     p.n_tiles = (p.K + TN - 1) / TN;
@@ -377,21 +442,29 @@ static hipError_t launch_halo_bf16_variant(const ConvParams& p0, bool dgrad, hip
     if (dgrad) {
         if constexpr (DGOK) {
             if (cvec)
-                hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, true, true>),
+                hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, true, true, false>),
                                    grid, dim3(256), 0, stream, p);
             else
-                hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, false, true>),
+                hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, false, true, false>),
                                    grid, dim3(256), 0, stream, p);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
     }
-    if (cvec)
-        hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, true, false>), grid,
+    if (p.wkb > 0) {
+        if (cvec)
+            hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, true, false, true>),
+                               grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, false, false, true>),
+                               grid, dim3(256), 0, stream, p);
+    } else if (cvec) {
+        hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, true, false, false>), grid,
                            dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, false, false>), grid,
+    } else {
+        hipLaunchKernelGGL((conv_fwd_halo_bf16_kernel<TM, TN, WAVES_M, WAVES_N, R, S, WP, SL, false, false, false>), grid,
                            dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -32,6 +32,8 @@
 // strides; M = N*P*Q; div_pq, div_q divide by P*Q and Q.
 #include <stdint.h>
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include "conv_params.h"
@@ -41,7 +43,11 @@
 
 namespace miconv {
 
-template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP>
+// XB: x channel-blocked ([N][C/cb][H][W][cb], cb a multiple of CB, 16-byte
+// aligned): a chunk's CB = 4 channels lie side by side, so the halo moves as
+// one 16-byte load per (slot, column).  WB: blocked filters
+// ([K/kb][C/cb][R][S][cb][kb]).  Both false: NCHW x and packed KCRS filters.
+template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP, bool XB, bool WB>
 __global__ void __launch_bounds__(256)
 conv_fwd_rows_kernel(const ConvParams p)
 {
@@ -58,9 +64,11 @@ conv_fwd_rows_kernel(const ConvParams p)
     constexpr int HALO = CB * PLANE;                // floats
     constexpr int SLAB = S * CB * TN;               // floats: [s][c][k]
     constexpr int BUF = HALO + SLAB;
-    constexpr int NH = (HALO + NT - 1) / NT;        // halo elements per thread per chunk
+    // halo elements (XB: 4-channel groups) per thread per chunk
+    constexpr int NH = XB ? (PLANE + NT - 1) / NT : (HALO + NT - 1) / NT;
     constexpr int STEPS = S * (CB / G);
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
+    static_assert(!XB || CB == 4, "blocked x: one 16-byte load per chunk column");
     constexpr int SROWS = TN * CB;                  // slab rows (filter, channel) of S taps
     constexpr int SPLIT = NT / SROWS;               // threads sharing a slab row
     constexpr int SH = (S + SPLIT - 1) / SPLIT;     // taps per thread
@@ -96,6 +104,8 @@ conv_fwd_rows_kernel(const ConvParams p)
     const int nrows = p.N * p.P;
 
     // ---- halo loader: element e = (channel, slot, column), column fastest
+    // (XB: e = (slot, column) carrying the chunk's four channels)
+    constexpr int HE = XB ? PLANE : HALO;
     int h_base[NH];                                  // x offset of (n, slot row's p*u - pad_top, column), channel 0
     int h_row[NH];                                   // input row p*u - pad_top (r added per chunk)
     uint32_t h_ok = 0;
@@ -110,7 +120,7 @@ conv_fwd_rows_kernel(const ConvParams p)
         const int n = orow / p.P;
         const int pp = orow - n * p.P;
         const int wc = col - p.pad_left;
-        const bool ok = e < HALO && orow < nrows && (unsigned)wc < (unsigned)p.W;
+        const bool ok = e < HE && orow < nrows && (unsigned)wc < (unsigned)p.W;
         h_row[i] = pp * p.u - p.pad_top;
         h_base[i] = ok ? n * p.sxn + cl * p.sxc + wc * p.sxw : 0;
         h_ok |= (ok ? 1u : 0u) << i;
@@ -120,9 +130,12 @@ conv_fwd_rows_kernel(const ConvParams p)
     const int sc = (tid / TN) % CB;
     const int sh = tid / SROWS;
     const bool s_ok = n0 + sk < p.K;
-    const int s_base = (s_ok ? n0 + sk : 0) * p.Kred;    // packed KCRS: filter row length C*R*S
+    // packed KCRS: filter k's row of C*R*S; blocked: its block row and place in the block
+    const int kk = s_ok ? n0 + sk : 0;
+    const int s_base = WB ? (kk / p.wkb) * (p.C / p.wcb) * (p.R * S * p.wcb * p.wkb) + kk % p.wkb : kk * p.Kred;
 
-    float hv[NH];
+    using HV = typename std::conditional<XB, float4, float>::type;
+    HV hv[NH];
     uint32_t hv_ok = 0;                              // validity of the chunk in registers
     float sv[SH];
     const int ncb = p.C / CB;
@@ -130,26 +143,48 @@ conv_fwd_rows_kernel(const ConvParams p)
     auto load_chunk = [&](int ch) {
         const int r = ch / ncb;
         const int c0 = (ch - r * ncb) * CB;
+        // x offset of the chunk's first channel (blocked x: the chunk lies in one block)
+        const int xo = XB ? blk_off(p.div_xcb, p.sxcb, p.sxc, c0) : c0 * p.sxc;
         // unconditional loads at a valid address; zeros are chosen at the store
         uint32_t m = 0;
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
             const int h = h_row[i] + r;
             const bool ok = ((h_ok >> i) & 1u) && (unsigned)h < (unsigned)p.H;
-            hv[i] = x[ok ? h_base[i] + c0 * p.sxc + h * p.sxh : 0];
+            hv[i] = *reinterpret_cast<const HV*>(x + (ok ? h_base[i] + xo + h * p.sxh : 0));
             m |= (ok ? 1u : 0u) << i;
         }
         hv_ok = m;
-        const int fo = s_base + ((c0 + sc) * p.R + r) * S;
+        if (WB) {
+            // the channel's block once per chunk, then the taps at a stride of cb*kb
+            const int c = c0 + sc;
+            const int wo = s_base + (c / p.wcb) * (p.R * S * p.wcb * p.wkb) + (c % p.wcb) * p.wkb +
+                           r * S * p.wcb * p.wkb;
 #pragma unroll
-        for (int i = 0; i < SH; ++i) sv[i] = w[fo + min(sh * SH + i, S - 1)];
+            for (int i = 0; i < SH; ++i) sv[i] = w[wo + min(sh * SH + i, S - 1) * p.wcb * p.wkb];
+        } else {
+            const int fo = s_base + ((c0 + sc) * p.R + r) * S;
+#pragma unroll
+            for (int i = 0; i < SH; ++i) sv[i] = w[fo + min(sh * SH + i, S - 1)];
+        }
     };
     auto store_chunk = [&](int buf) {
         float* dst = smem + buf * BUF;
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
             const int e = tid + NT * i;
-            if (HALO % NT == 0 || e < HALO) dst[e] = (hv_ok >> i) & 1u ? hv[i] : 0.0f;
+            if constexpr (XB) {
+                if (PLANE % NT == 0 || e < PLANE) {
+                    const bool ok = (hv_ok >> i) & 1u;
+                    const float4 v = hv[i];
+                    dst[e] = ok ? v.x : 0.0f;
+                    dst[PLANE + e] = ok ? v.y : 0.0f;
+                    dst[2 * PLANE + e] = ok ? v.z : 0.0f;
+                    dst[3 * PLANE + e] = ok ? v.w : 0.0f;
+                }
+            } else {
+                if (HALO % NT == 0 || e < HALO) dst[e] = (hv_ok >> i) & 1u ? hv[i] : 0.0f;
+            }
         }
 #pragma unroll
         for (int i = 0; i < SH; ++i) {
@@ -718,11 +753,32 @@ static hipError_t launch_rows_variant(const ConvParams& p0, hipStream_t stream)
 {
     ConvParams p = p0;
     if (!rows_variant_fits<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP>(p)) return hipErrorInvalidValue;
+    const bool xb = p.div_xcb.d != kOneBlock;
+    const bool wb = p.wkb > 0;
+    if (xb) {
+        // the chunk's channels side by side, 16-byte aligned: packed blocks of
+        // a multiple of CB channels, strides in whole 16-byte units
+        const int cb = (int)p.div_xcb.d;
+        if (cb % CB || p.sxc != 1 || p.sxw % 4 || p.sxh % 4 || p.sxn % 4 || p.sxcb % 4 ||
+            reinterpret_cast<uintptr_t>(p.x) % 16)
+            return hipErrorInvalidValue;
+    }
+    if (wb && (p.C % p.wcb || p.K % p.wkb)) return hipErrorInvalidValue;
     p.m_tiles = (p.M + TM - 1) / TM;
     p.n_tiles = (p.K + TN - 1) / TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
-    hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP>), grid, dim3(256), 0, stream,
-                       p);
+    if (xb && wb)
+        hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP, true, true>), grid,
+                           dim3(256), 0, stream, p);
+    else if (xb)
+        hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP, true, false>), grid,
+                           dim3(256), 0, stream, p);
+    else if (wb)
+        hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP, false, true>), grid,
+                           dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP, false, false>), grid,
+                           dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

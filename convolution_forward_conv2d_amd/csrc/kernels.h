@@ -16,6 +16,7 @@ enum class Variant : int {
     ROWS1N6_F32_S11_256x32, // ... six output-row slots (short output rows)
     DG_ROWS_MFMA,        // data gradient, the same streaming per stride phase (conv_fwd_rows.hip)
     DG_SUBPIXEL,         // strided data gradient as a stride-1 GEMM onto the stride phases (conv_bwd_data_subpixel.hip)
+    DG_TAPS,             // strided data gradient onto few channels, filter column taps as GEMM columns (conv_bwd_data_taps.hip)
     WGR_F32_S11_V2,      // filter gradient of a first layer on the vector ALU, staged output rows (conv_bwd_filter_rows.hip)
     WGR_F32_S11_V4,
     MFMA_F32_128x128,
@@ -144,6 +145,8 @@ hipError_t launch_rows(Variant v, const ConvParams& p, hipStream_t stream);
 bool bwd_data_rows_mfma_fits(const ConvParams& p);
 hipError_t launch_bwd_data_rows_mfma(const ConvParams& p, hipStream_t stream);
 bool bwd_data_subpixel_fits(const ConvParams& p);
+bool bwd_data_taps_fits(const ConvParams& p);
+hipError_t launch_bwd_data_taps(const ConvParams& p, hipStream_t stream);
 hipError_t launch_bwd_data_subpixel(DType dt, const ConvParams& p, hipStream_t stream);
 bool bwd_filter_rows_fits(Variant v, const ConvParams& p);
 hipError_t launch_bwd_filter_rows(Variant v, const ConvParams& p, hipStream_t stream);

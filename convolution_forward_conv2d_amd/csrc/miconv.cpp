@@ -148,6 +148,7 @@ const Candidate kDgRows = {Variant::DG_ROWS, 0, 0, "rows"};
 const Candidate kRowsF32 = {Variant::ROWS_F32_S11_256x32, 256, 32, "rows_f32_s11_256x32"};
 const Candidate kDgRowsMfma = {Variant::DG_ROWS_MFMA, 256, 32, "rows_mfma_f32_s11_256x32"};
 const Candidate kDgSubpixel = {Variant::DG_SUBPIXEL, 128, 64, "subpixel"};
+const Candidate kDgTaps = {Variant::DG_TAPS, 0, 0, "taps"};
 const Candidate kRows1F32 = {Variant::ROWS1_F32_S11_256x32, 256, 32, "rows1_f32_s11_256x32"};
 const Candidate kRows1N6F32 = {Variant::ROWS1N6_F32_S11_256x32, 256, 32, "rows1n6_f32_s11_256x32"};
 // Filter-gradient kernels: the gather kernel (conv_bwd_filter.hip, any
@@ -437,9 +438,10 @@ bool halo_eligible(const HaloCandidate& h, DType dt, const ConvParams& p, const 
                (p.wkb == 0 && (h.c.v == Variant::HALO_BF16_3x3_128x64 ||
                                (h.c.v == Variant::HALO_BF16_3x3_128x128 && p.sxc != 1)));
     if (p.wkb > 0) {
-        // blocked filters: 16-byte loads of kb-contiguous filters (fp32/fp64 kernel only)
-        const int vk = dt == DType::F64 ? 2 : 4;
-        if (dt == DType::BF16 || p.wcb % h.cb != 0 || p.wkb % vk != 0) return false;
+        // blocked filters: 16-byte loads of kb-contiguous filters (4 fp32, 2 fp64
+        // or 8 bf16 filters; bf16 transposes 8 x 8 blocks, a chunk's 16 channels in one block)
+        const int vk = dt == DType::F64 ? 2 : dt == DType::BF16 ? 8 : 4;
+        if (p.wcb % h.cb != 0 || p.wkb % vk != 0) return false;
     }
     if (check_ptr && (uintptr_t)w % 16 != 0) return false;
     return true;
@@ -556,12 +558,18 @@ Plan make_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const void*
 
     // no halo instance: tall filter banks with few filters stream the
     // reduction by filter row (speech layer 2: 2.9 ms through the gather kernel)
-    const bool unblocked = !blocked(xd) && !blocked(wd) && !blocked(yd);
-    const bool rows_ok = pl.dt == DType::F32 && unblocked && miconv::rows_fits(kRowsF32.v, p);
+    // the row-streamed kernel reads channel-blocked x when a block holds its
+    // 4-channel chunks (one 16-byte load per chunk column: x 16-byte aligned),
+    // blocked filters tap by tap, blocked y in the epilogue
+    const bool rows_blocks_ok =
+        !blocked(xd) || (xd->cb % 4 == 0 && (!need_pointers || (uintptr_t)x % 16 == 0));
+    const bool rows_ok = pl.dt == DType::F32 && rows_blocks_ok && miconv::rows_fits(kRowsF32.v, p);
     // ... and onto 1-4 input channels with adjacent taps paired (speech
     // layer 1: two output-row slots; Overfeat layer 1: six)
-    const bool rows1_ok = pl.dt == DType::F32 && unblocked && miconv::rows_fits(kRows1F32.v, p);
-    const bool rows1n6_ok = pl.dt == DType::F32 && unblocked && miconv::rows_fits(kRows1N6F32.v, p);
+    // ... and the one-channel forms blocked y (their x and filter loaders read plain layouts)
+    const bool rows1_layout_ok = !blocked(xd) && !blocked(wd);
+    const bool rows1_ok = pl.dt == DType::F32 && rows1_layout_ok && miconv::rows_fits(kRows1F32.v, p);
+    const bool rows1n6_ok = pl.dt == DType::F32 && rows1_layout_ok && miconv::rows_fits(kRows1N6F32.v, p);
     if (!is_halo(pl.cand.v) && rows_ok) pl.cand = kRowsF32;
     if (!is_halo(pl.cand.v) && rows1n6_ok) pl.cand = kRows1N6F32;
     if (!is_halo(pl.cand.v) && rows1_ok) pl.cand = kRows1F32;
@@ -856,9 +864,32 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
         }
         const bool subpixel = forced_dgrad_name ? strcmp(forced_dgrad_name, kDgSubpixel.name) == 0 && subpixel_ok
                                                 : subpixel_ok && !rows_mfma;
+        // a strided layer onto 1-4 channels with too few (channel, phase)
+        // columns for the stride-phase GEMM and filter rows of at most 16
+        // taps: the GEMM whose columns are the taps of a filter row, the
+        // stride grid's column sum done from LDS (conv_bwd_data_taps.hip;
+        // speech layer 1 onto one channel)
+        bool taps_ok = false;
+        if ((cd->u > 1 || cd->v > 1) && pl.dt == DType::F32 && C <= 4) {
+            ConvParams q = p;
+            q.C = C;
+            q.H = H;
+            q.W = W;
+            q.K = k;
+            q.P = P;
+            q.Q = Q;
+            q.R = R;
+            q.S = S;
+            q.u = cd->u;
+            q.v = cd->v;
+            taps_ok = miconv::bwd_data_taps_fits(q);
+        }
+        const bool taps = forced_dgrad_name ? strcmp(forced_dgrad_name, kDgTaps.name) == 0 && taps_ok
+                                            : taps_ok && !subpixel && !rows_mfma;
         const bool direct = forced_dgrad_name
-                                ? strcmp(forced_dgrad_name, kDirect.name) == 0 || phase || rows || rows_mfma || subpixel
-                                : C < 16 || rows_mfma || subpixel;
+                                ? strcmp(forced_dgrad_name, kDirect.name) == 0 || phase || rows || rows_mfma || subpixel ||
+                                      taps
+                                : C < 16 || rows_mfma || subpixel || taps;
         if (!direct) {
             p.C = k;
             p.K = C;
@@ -888,6 +919,7 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
             if (rows) pl.cand = kDgRows;
             if (rows_mfma) pl.cand = kDgRowsMfma;
             if (subpixel) pl.cand = kDgSubpixel;
+            if (taps) pl.cand = kDgTaps;
             p.C = C;
             p.H = H;
             p.W = W;
@@ -1623,6 +1655,8 @@ mic_status mic_conv_backward_data(mic_handle handle, double alpha, mic_filter_de
         err = miconv::launch_bwd_data_rows(pl.p, handle->stream);
     else if (pl.cand.v == Variant::DG_ROWS_MFMA)
         err = miconv::launch_bwd_data_rows_mfma(pl.p, handle->stream);
+    else if (pl.cand.v == Variant::DG_TAPS)
+        err = miconv::launch_bwd_data_taps(pl.p, handle->stream);
     else if (pl.cand.v == Variant::DG_SUBPIXEL)
         err = miconv::launch_bwd_data_subpixel(pl.dt, pl.p, handle->stream);
     else if (is_halo(pl.cand.v) && pl.dt == DType::BF16)

@@ -298,7 +298,7 @@ def test_dgrad_kernel_choice_host_only():
     # 21x11 / stride (2, 1) onto 32 channels: the row-streamed kernel per stride phase
     assert names["speech_l2"] == "dgrad_rows_mfma_f32_s11_256x32"
     assert names["overfeat_l1"] == "dgrad_subpixel"
-    assert names["speech_l1"] == "dgrad_rows"
+    assert names["speech_l1"] == "dgrad_taps"
 
 
 def test_dgrad_subpixel_kernel_limits(monkeypatch):
@@ -313,6 +313,28 @@ def test_dgrad_subpixel_kernel_limits(monkeypatch):
     assert _dgrad_name(lay(7, 2, 2)) != "dgrad_subpixel"          # 28 columns
     monkeypatch.setenv("MIC_FORCE_DGRAD_VARIANT", "subpixel")
     for bad in (lay(32, 1, 1), lay(7, 2, 2), lay(8, 2, 2, "bf16")):
+        with pytest.raises(mic.MicError) as e:
+            _dgrad_name(bad)
+        assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED
+
+
+def test_dgrad_taps_kernel_limits(monkeypatch):
+    """The taps kernel takes 1-4 output channels at a stride above 1, fp32, filter rows of at
+    most 16 taps, dy rows of at most 352 columns and at most 24 filter rows per row phase;
+    chosen below the stride-phase GEMM (speech layer 1), NOT_SUPPORTED when forced elsewhere."""
+    def lay(C, S, u, Ww=40, R=5, dt="f32", v=2):
+        return Layer("tp", 9, 1, 2, C, R + 25, Ww, 8, R, S, (u, v), (1, 1, 1, 1), dt,
+                     workloads.U11, workloads.U11)
+    assert _dgrad_name(lay(1, 11, 2)) == "dgrad_taps"
+    assert _dgrad_name(lay(8, 5, 2)) == "dgrad_subpixel"        # 32 columns
+    monkeypatch.setenv("MIC_FORCE_DGRAD_VARIANT", "taps")
+    for C in (1, 2, 3, 4):
+        assert _dgrad_name(lay(C, 16, 2)) == "dgrad_taps"
+    assert _dgrad_name(lay(1, 5, 2, Ww=703)) == "dgrad_taps"    # Q = 351
+    assert _dgrad_name(lay(1, 5, 2, R=48)) == "dgrad_taps"      # 24 rows per phase
+    assert _dgrad_name(lay(1, 5, 1)) == "dgrad_taps"            # stride (1, 2)
+    for bad in (lay(5, 5, 2), lay(1, 17, 2), lay(1, 5, 1, v=1), lay(1, 5, 2, Ww=707),
+                lay(1, 5, 2, R=49), lay(1, 5, 2, dt="f64")):
         with pytest.raises(mic.MicError) as e:
             _dgrad_name(bad)
         assert e.value.status == mic.MIC_STATUS_NOT_SUPPORTED

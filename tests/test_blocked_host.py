@@ -111,9 +111,13 @@ def test_blocked_kernel_choice():
     assert _choice(F64, 16, (16, 16), 16).startswith("halo_f64_3x3_")
     assert _choice(F32, 32, None, 32).startswith("halo_f32_3x3_")
     assert _choice(BF16, 16, None, 16).startswith("halo_bf16_3x3_")
-    # bf16 blocked filters: gather kernel in tap order (cb a multiple of 32), else direct
-    assert _choice(BF16, 32, (32, 32), 32).endswith("_tap")
-    assert _choice(BF16, 16, (16, 16), 16) == "direct"
+    # bf16 blocked filters: the tap-batched kernel's transposing loader when blocks of
+    # 8 filters and 16 channels fit (kb % 8, cb % 16), else the gather kernel in tap
+    # order (cb a multiple of 32), else direct
+    assert _choice(BF16, 32, (32, 32), 32).startswith("halo_bf16_3x3_")
+    assert _choice(BF16, 16, (16, 16), 16).startswith("halo_bf16_3x3_")
+    assert _choice(BF16, 32, (4, 32), 32).endswith("_tap")
+    assert _choice(BF16, 16, (4, 16), 16) == "direct"
     # x blocked by 2 (not a multiple of the 4-channel chunk): flat gather order
     name = _choice(F32, 2, None, 8)
     assert name.startswith("mfma_f32_") and not name.endswith("_tap")
@@ -131,8 +135,9 @@ def test_blocked_forced_variants(monkeypatch):
     with pytest.raises(mic.MicError):
         _choice(F32, 8, None, 8)                                      # tap order needs cb % 16 == 0
     monkeypatch.setenv("MIC_FORCE_VARIANT", "halo_bf16_3x3_128x128")
+    assert _choice(mic.MIC_DTYPE_BF16, 32, (32, 32), 32) == "halo_bf16_3x3_128x128"
     with pytest.raises(mic.MicError):
-        _choice(mic.MIC_DTYPE_BF16, 32, (32, 32), 32)                 # bf16 halo: packed filters only
+        _choice(mic.MIC_DTYPE_BF16, 32, (4, 32), 32)                  # bf16 halo: blocks of 8 filters or more
 
 
 def test_other_operations_refuse_blocked_descriptors():

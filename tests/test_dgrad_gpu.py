@@ -50,7 +50,10 @@ DG_VARIANTS["f32"] += ["rows_mfma_f32_s11_256x32"]
 # (channel, row phase, column phase) columns (fp32, fp64)
 DG_VARIANTS["f32"] += ["subpixel"]
 DG_VARIANTS["f64"] += ["subpixel"]
-_MAY_REFUSE = ("halo_", "phase", "rows", "subpixel")
+# the GEMM whose columns are a filter row's taps, onto 1-4 channels at a stride above 1
+# (fp32): filter rows of at most 16 taps, dy rows of at most 352 columns
+DG_VARIANTS["f32"] += ["taps"]
+_MAY_REFUSE = ("halo_", "phase", "rows", "subpixel", "taps")
 # the gather kernel in data-gradient mode (any stride)
 DG_VARIANTS["f32"] += ["mfma_f32_128x128", "mfma_f32_128x64", "mfma_f32_64x128", "mfma_f32_256x32"]
 DG_VARIANTS["f64"] += ["mfma_f64_128x128", "mfma_f64_128x64", "mfma_f64_64x64"]
@@ -76,6 +79,11 @@ SHAPES = SMALL_SHAPES + [
     dict(name="dg_phase_c3_s4", N=2, C=3, Hh=39, Ww=43, K=24, R=11, S=11, stride=(4, 4), pads=(2, 0, 1, 3)),
     # filter narrower than the stride: phases with no tap at all leave beta * dx
     dict(name="dg_phase_c1_narrow", N=2, C=1, Hh=14, Ww=15, K=6, R=2, S=2, stride=(3, 3), pads=(0, 0, 0, 0)),
+    # filter-row taps as GEMM columns: a speech-like 41 x 11 bank at stride 2 onto one
+    # channel, dy rows of 350 columns (the staged width is 352), 21 taps per row phase
+    # (six groups of four, the last partly zero) and an odd number of phase rows
+    dict(name="dg_taps_41x11_wide", N=1, C=1, Hh=31, Ww=699, K=12, R=41, S=11, stride=(2, 2),
+         pads=(20, 19, 5, 5)),
     # row-streamed per phase: speech-like 21x11 / (2, 1) onto 40 channels (a ragged second
     # channel tile), and 7x11 / (3, 1) with padding on every side
     dict(name="dg_rows_21x11", N=1, C=40, Hh=41, Ww=260, K=16, R=21, S=11, stride=(2, 1),
