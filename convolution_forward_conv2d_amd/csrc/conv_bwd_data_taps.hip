@@ -35,15 +35,21 @@
 // geometry.  The host checks: fp32, S <= 16, Q <= QP, ceil(R/u) <= 4*IS.
 #include <stdint.h>
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include "conv_params.h"
 #include "kernels.h"
 #include "mfma_common.h"
+#include "tile_map.h"
 
 namespace miconv {
 
-template <int TB, int QB, int IS>
+// V: dy values per staging load (1, 2 or 4 consecutive columns; V > 1 needs
+// unit column stride, Q and the row, channel and image strides multiples of
+// V and dy's address aligned to V values)
+template <int TB, int QB, int IS, int V>
 __global__ void __launch_bounds__(256)
 conv_bwd_data_taps_kernel(const ConvParams p, int bands)
 {
@@ -56,9 +62,13 @@ conv_bwd_data_taps_kernel(const ConvParams p, int bands)
     constexpr int BUF = ROWS * QP;               // floats
     constexpr int NBLK = TB * QB;                // 16-row blocks of the tile
     constexpr int FM = (NBLK + 3) / 4;           // blocks per wave
-    constexpr int NL = (BUF + NT - 1) / NT;      // staged values per thread per chunk
+    constexpr int NU = BUF / V;                  // staging units of V columns per chunk
+    constexpr int NL = (NU + NT - 1) / NT;       // staging units per thread per chunk
+    static_assert(QP % V == 0, "whole units per staged row");
     constexpr int ZP = 17;                       // epilogue: floats per (P', q) row of Z (16 taps + pad)
-    static_assert(TB * QP * ZP <= 2 * BUF, "the epilogue's Z fits in the chunk buffers");
+    constexpr int ZR0 = 2 * BUF / (QP * ZP);     // phase rows of Z the chunk buffers hold
+    constexpr int ZR = ZR0 < TB ? ZR0 : TB;
+    static_assert(ZR >= 1, "one phase row of Z fits in the chunk buffers");
     static_assert(NL <= 64, "staging mask");
 
     __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
@@ -67,8 +77,10 @@ conv_bwd_data_taps_kernel(const ConvParams p, int bands)
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // blockIdx.x -> (band, phase a, channel c, image n), band fastest
-    int bid = (int)blockIdx.x;
+    // workgroup -> (band, phase a, channel c, image n), band fastest, in runs
+    // of consecutive ids per XCD: the bands of one phase, which stage
+    // overlapping dy rows, share an L2
+    int bid = xcd_logical_tile((int)blockIdx.x, (int)gridDim.x, p.tile_rev);
     const int band = bid % bands;
     bid /= bands;
     const int a = bid % p.u;
@@ -88,31 +100,34 @@ conv_bwd_data_taps_kernel(const ConvParams p, int bands)
     const float* __restrict__ F = static_cast<const float*>(p.w);
     const float* __restrict__ dyn = dy + (int64_t)n * p.sxn;
 
-    // ---- staging: value e = (staged row j, column q): dy row P0 + TB - 1 - j
+    // ---- staging: unit e = (staged row j, columns q ... q + V - 1): dy row
+    // P0 + TB - 1 - j (the host keeps Q a multiple of V: a unit lies in one row)
+    using VT = typename std::conditional<V == 4, float4, typename std::conditional<V == 2, float2, float>::type>::type;
     int st_off[NL];
     uint64_t st_ok = 0;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
         const int e = tid + NT * i;
-        const int j = e / QP;
-        const int q = e - j * QP;
+        const int j = e / (QP / V);
+        const int q = V * (e - j * (QP / V));
         const int prow = P0 + TB - 1 - j;
-        const bool ok = e < BUF && q < p.Q && prow >= 0 && prow < p.P;
+        const bool ok = e < NU && prow >= 0 && prow < p.P && q < p.Q;
         st_off[i] = ok ? prow * p.sxh + q * p.sxw : 0;
         st_ok |= (ok ? uint64_t(1) : uint64_t(0)) << i;
     }
-    float sv[NL];
+    VT sv[NL];
+    // unconditional loads at a valid address; zeros are chosen at the store
     auto load_chunk = [&](int k) {
         const float* src = dyn + k * p.sxc;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) sv[i] = src[st_off[i]];
+        for (int i = 0; i < NL; ++i) sv[i] = *reinterpret_cast<const VT*>(src + st_off[i]);
     };
     auto store_chunk = [&](int buf) {
-        float* dst = smem + buf * BUF;
+        VT* dst = reinterpret_cast<VT*>(smem + buf * BUF);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int e = tid + NT * i;
-            if (BUF % NT == 0 || e < BUF) dst[e] = ((st_ok >> i) & 1) ? sv[i] : 0.0f;
+            if (NU % NT == 0 || e < NU) dst[e] = (st_ok >> i) & 1 ? sv[i] : VT{};
         }
     };
 
@@ -147,11 +162,13 @@ conv_bwd_data_taps_kernel(const ConvParams p, int bands)
 #pragma unroll
     for (int f = 0; f < FM; ++f) acc[f] = AccV{};
 
+    // filter taps: unconditional loads at a valid address, zeros chosen after
     float bv[IS];
     auto load_b = [&](int k) {
 #pragma unroll
-        for (int t = 0; t < IS; ++t) bv[t] = ((b_ok >> t) & 1) ? F[k * fk + b_off[t]] : 0.0f;
+        for (int t = 0; t < IS; ++t) bv[t] = F[k * fk + b_off[t]];
     };
+    auto blk_ok = [&](int f) { return NBLK % 4 == 0 || wave + 4 * f < NBLK; };
 
     load_chunk(0);
     store_chunk(0);
@@ -160,63 +177,79 @@ conv_bwd_data_taps_kernel(const ConvParams p, int bands)
     for (int k = 0; k < p.K; ++k) {
         const int cur = k & 1;
         const bool more = k + 1 < p.K;
-        if (more) load_chunk(k + 1);
+        load_chunk(more ? k + 1 : k);
         const float* buf = smem + cur * BUF;
         float bcur[IS];
 #pragma unroll
-        for (int t = 0; t < IS; ++t) bcur[t] = bv[t];
-        if (more) load_b(k + 1);
+        for (int t = 0; t < IS; ++t) bcur[t] = (b_ok >> t) & 1u ? bv[t] : 0.0f;
+        load_b(more ? k + 1 : k);
+        // keep the next chunk's loads ahead of this chunk's products
+        __builtin_amdgcn_sched_barrier(0);
+        // operands of step t + 1 read from LDS while step t's products issue
+        float av[FM], an[FM];
+#pragma unroll
+        for (int f = 0; f < FM; ++f) av[f] = blk_ok(f) ? buf[a_base[f]] : 0.0f;
 #pragma unroll
         for (int t = 0; t < IS; ++t) {
+            if (t + 1 < IS) {
 #pragma unroll
-            for (int f = 0; f < FM; ++f) {
-                if (wave + 4 * f < NBLK) {
-                    const float av = buf[a_base[f] + 4 * t * QP];
-                    acc[f] = Pol::mfma_s(av, bcur[t], acc[f]);
-                }
+                for (int f = 0; f < FM; ++f) an[f] = blk_ok(f) ? buf[a_base[f] + 4 * (t + 1) * QP] : 0.0f;
+            }
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+                if (blk_ok(f)) acc[f] = Pol::mfma_s(av[f], bcur[t], acc[f]);
+            if (t + 1 < IS) {
+#pragma unroll
+                for (int f = 0; f < FM; ++f) av[f] = an[f];
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
         if (more) store_chunk(cur ^ 1);
         __syncthreads();
     }
 
-    // ---- epilogue: Z -> LDS as [pb][q][s] (17 floats per (pb, q)), then each
-    // output of the band sums its taps
+    // ---- epilogue: Z -> LDS as [pb][q][s] (17 floats per (pb, q)), ZR phase
+    // rows at a time, then each output of those rows sums its taps
     float* Z = smem;
-#pragma unroll
-    for (int f = 0; f < FM; ++f) {
-        const int b = wave + 4 * f;
-        if (b < NBLK) {
-            const int pb = b / QB;
-            const int qb = b - pb * QB;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = Pol::row(e, lane);          // position within the block
-                const int s = Pol::col(e, lane);          // tap
-                Z[(pb * QP + qb * 16 + m) * ZP + s] = acc[f][e];
-            }
-        }
-    }
-    __syncthreads();
     float* dx = static_cast<float*>(p.y);
     const float alpha = (float)p.alpha;
     const float beta = (float)p.beta;
-    for (int e = tid; e < TB * p.W; e += NT) {
-        const int pb = e / p.W;
-        const int w = e - pb * p.W;
-        const int Pp = P0 + pb;
-        const int h = p.u * Pp + a - p.pad_top;
-        if (Pp > P_hi || h < 0 || h >= p.H) continue;
-        const int wp = w + p.pad_left;
-        float sum = 0.0f;
-        // taps s = wp - v q for q = floor(wp / v) down to the first with s >= S
-        for (int q = wp / p.v; q >= 0; --q) {
-            const int s = wp - p.v * q;
-            if (s >= p.S) break;
-            if (q < p.Q) sum += Z[(pb * QP + q) * ZP + s];
+#pragma unroll
+    for (int pb0 = 0; pb0 < TB; pb0 += ZR) {
+        if (pb0 > 0) __syncthreads();             // the previous rows' sums are read
+#pragma unroll
+        for (int f = 0; f < FM; ++f) {
+            const int b = wave + 4 * f;
+            const int pb = b / QB;
+            if (b < NBLK && pb >= pb0 && pb < pb0 + ZR) {
+                const int qb = b - pb * QB;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = Pol::row(e, lane);          // position within the block
+                    const int s = Pol::col(e, lane);          // tap
+                    Z[((pb - pb0) * QP + qb * 16 + m) * ZP + s] = acc[f][e];
+                }
+            }
         }
-        float* o = dx + (int64_t)n * p.syn + (int64_t)c * p.syk + (int64_t)h * p.syp + (int64_t)w * p.syq;
-        *o = beta != 0.0f ? alpha * sum + beta * *o : alpha * sum;
+        __syncthreads();
+        const int nr = min(ZR, TB - pb0);
+        for (int e = tid; e < nr * p.W; e += NT) {
+            const int zr = e / p.W;
+            const int w = e - zr * p.W;
+            const int Pp = P0 + pb0 + zr;
+            const int h = p.u * Pp + a - p.pad_top;
+            if (Pp > P_hi || h < 0 || h >= p.H) continue;
+            const int wp = w + p.pad_left;
+            float sum = 0.0f;
+            // taps s = wp - v q for q = floor(wp / v) down to the first with s >= S
+            for (int q = wp / p.v; q >= 0; --q) {
+                const int s = wp - p.v * q;
+                if (s >= p.S) break;
+                if (q < p.Q) sum += Z[(zr * QP + q) * ZP + s];
+            }
+            float* o = dx + (int64_t)n * p.syn + (int64_t)c * p.syk + (int64_t)h * p.syp + (int64_t)w * p.syq;
+            *o = beta != 0.0f ? alpha * sum + beta * *o : alpha * sum;
+        }
     }
 }
 
@@ -234,14 +267,34 @@ bool bwd_data_taps_fits(const ConvParams& p)
            p.u >= 1;
 }
 
+// dy values per staging load: V consecutive columns at V-aligned addresses
+static int taps_vector_width(const ConvParams& p)
+{
+    for (int v = 4; v > 1; v /= 2)
+        if (p.sxw == 1 && p.Q % v == 0 && p.sxh % v == 0 && p.sxc % v == 0 && p.sxn % v == 0 &&
+            reinterpret_cast<uintptr_t>(p.x) % (4 * v) == 0)
+            return v;
+    return 1;
+}
+
+template <int V>
+static void launch_taps_v(const ConvParams& p, int bands, int64_t grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((conv_bwd_data_taps_kernel<kTapsTB, kTapsQB, kTapsIS, V>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p, bands);
+}
+
 hipError_t launch_bwd_data_taps(const ConvParams& p, hipStream_t stream)
 {
     if (!bwd_data_taps_fits(p)) return hipErrorInvalidValue;
     const int bands = (taps_rows_per_phase(p) + kTapsTB - 1) / kTapsTB;
     const int64_t grid = (int64_t)p.N * p.C * p.u * bands;
     if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((conv_bwd_data_taps_kernel<kTapsTB, kTapsQB, kTapsIS>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, p, bands);
+    switch (taps_vector_width(p)) {
+    case 4: launch_taps_v<4>(p, bands, grid, stream); break;
+    case 2: launch_taps_v<2>(p, bands, grid, stream); break;
+    default: launch_taps_v<1>(p, bands, grid, stream); break;
+    }
     return hipGetLastError();
 }
 
