@@ -47,7 +47,11 @@ namespace miconv {
 // aligned): a chunk's CB = 4 channels lie side by side, so the halo moves as
 // one 16-byte load per (slot, column).  WB: blocked filters
 // ([K/kb][C/cb][R][S][cb][kb]).  Both false: NCHW x and packed KCRS filters.
-template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP, bool XB, bool WB>
+// XV (unblocked x): the halo moves XV = 1, 2 or 4 consecutive columns per
+// load; the host picks XV > 1 when W, pad_left and x's strides are multiples
+// of XV (a unit then lies wholly inside or wholly outside the row) and x is
+// aligned to XV values (speech layer 2: XV = 2, 2264 -> about 2100 us).
+template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP, bool XB, bool WB, int XV>
 __global__ void __launch_bounds__(256)
 conv_fwd_rows_kernel(const ConvParams p)
 {
@@ -64,8 +68,12 @@ conv_fwd_rows_kernel(const ConvParams p)
     constexpr int HALO = CB * PLANE;                // floats
     constexpr int SLAB = S * CB * TN;               // floats: [s][c][k]
     constexpr int BUF = HALO + SLAB;
-    // halo elements (XB: 4-channel groups) per thread per chunk
-    constexpr int NH = XB ? (PLANE + NT - 1) / NT : (HALO + NT - 1) / NT;
+    // halo units per thread per chunk (XB: 4-channel groups; else XV columns)
+    static_assert(XV == 1 || XV == 2 || XV == 4, "column units");
+    static_assert(!XB || XV == 1, "blocked x moves channel groups");
+    static_assert(WP % XV == 0, "whole units per staged row");
+    constexpr int HE = XB ? PLANE : HALO / XV;      // halo units per chunk
+    constexpr int NH = (HE + NT - 1) / NT;
     constexpr int STEPS = S * (CB / G);
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
     static_assert(!XB || CB == 4, "blocked x: one 16-byte load per chunk column");
@@ -103,17 +111,17 @@ conv_fwd_rows_kernel(const ConvParams p)
     const int row0 = out_row(m0);
     const int nrows = p.N * p.P;
 
-    // ---- halo loader: element e = (channel, slot, column), column fastest
+    // ---- halo loader: unit e = (channel, slot, XV columns), columns fastest
     // (XB: e = (slot, column) carrying the chunk's four channels)
-    constexpr int HE = XB ? PLANE : HALO;
     int h_base[NH];                                  // x offset of (n, slot row's p*u - pad_top, column), channel 0
     int h_row[NH];                                   // input row p*u - pad_top (r added per chunk)
     uint32_t h_ok = 0;
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
         const int e = tid + NT * i;
-        const int cl = e / PLANE;
-        const int rem = e - cl * PLANE;
+        const int el = XB ? e : e * XV;              // first staged element of the unit
+        const int cl = el / PLANE;
+        const int rem = el - cl * PLANE;
         const int sl = rem / WP;
         const int col = rem - sl * WP;
         const int orow = row0 + sl;
@@ -134,7 +142,8 @@ conv_fwd_rows_kernel(const ConvParams p)
     const int kk = s_ok ? n0 + sk : 0;
     const int s_base = WB ? (kk / p.wkb) * (p.C / p.wcb) * (p.R * S * p.wcb * p.wkb) + kk % p.wkb : kk * p.Kred;
 
-    using HV = typename std::conditional<XB, float4, float>::type;
+    using HV = typename std::conditional<
+        XB || XV == 4, float4, typename std::conditional<XV == 2, float2, float>::type>::type;
     HV hv[NH];
     uint32_t hv_ok = 0;                              // validity of the chunk in registers
     float sv[SH];
@@ -183,7 +192,7 @@ conv_fwd_rows_kernel(const ConvParams p)
                     dst[3 * PLANE + e] = ok ? v.w : 0.0f;
                 }
             } else {
-                if (HALO % NT == 0 || e < HALO) dst[e] = (hv_ok >> i) & 1u ? hv[i] : 0.0f;
+                if (HE % NT == 0 || e < HE) reinterpret_cast<HV*>(dst)[e] = (hv_ok >> i) & 1u ? hv[i] : HV{};
             }
         }
 #pragma unroll
@@ -276,8 +285,20 @@ conv_fwd_rows_kernel(const ConvParams p)
 // channel and RB filter rows, so that it holds RB * SP / 2 steps.  The chunk
 // stages, per filter row j and output-row slot, one input row of WP
 // columns; the operand of (slot, q) at (j, s) is halo[j][slot][q*v + s].
-template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int RB, int NSL, int WP>
-__global__ void __launch_bounds__(256)
+//
+// waves_per_eu(6): the register allocator keeps a lane under 85 registers, so
+// six workgroups share a CU and cover each other's chunk edges (measured on
+// MI355X: 5-6% faster on speech layer 1 and Overfeat layer 1 than the four
+// workgroups that 109 registers allow).  Measured and not kept: the next
+// chunk's loads and LDS stores spread over the MFMA steps (3% slower), two
+// filter rows per chunk (6-12% slower), the row stored by column phase so
+// that stride-v operand reads hit distinct banks (6% slower: the loader
+// then gathers x at stride v).
+//
+// XV: consecutive columns per halo load, as for the multi-channel kernel
+// (speech layer 1: XV = 4).
+template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int RB, int NSL, int WP, int XV>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6)))
 conv_fwd_rows1_kernel(const ConvParams p)
 {
     using Pol = PolF32;
@@ -294,7 +315,9 @@ conv_fwd_rows1_kernel(const ConvParams p)
     constexpr int HALO = RB * ROWP;
     constexpr int SLAB = RB * SP * TN;              // [j][s][k]
     constexpr int BUF = HALO + SLAB;
-    constexpr int NH = (HALO + NT - 1) / NT;
+    static_assert((XV == 1 || XV == 2 || XV == 4) && WP % XV == 0, "column units");
+    constexpr int HE = HALO / XV;                   // halo units of XV columns
+    constexpr int NH = (HE + NT - 1) / NT;
     constexpr int NS = (SLAB + NT - 1) / NT;
     constexpr int STEPS = RB * (SP / G);
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
@@ -327,22 +350,23 @@ conv_fwd_rows1_kernel(const ConvParams p)
     const int row0 = out_row(m0);
     const int nrows = p.N * p.P;
 
-    // ---- halo loader: element e = (filter row j, slot, column), column fastest
+    // ---- halo loader: unit e = (filter row j, slot, XV columns), columns fastest
     int h_base[NH];
     int h_row[NH];                                   // input row of filter row j at chunk row 0
     uint32_t h_ok = 0;
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
         const int e = tid + NT * i;
-        const int j = e / ROWP;
-        const int rem = e - j * ROWP;
+        const int el = e * XV;                       // the unit's first staged element
+        const int j = el / ROWP;
+        const int rem = el - j * ROWP;
         const int sl = rem / WP;
         const int col = rem - sl * WP;
         const int orow = row0 + sl;
         const int n = orow / p.P;
         const int pp = orow - n * p.P;
         const int wc = col - p.pad_left;
-        const bool ok = e < HALO && orow < nrows && (unsigned)wc < (unsigned)p.W;
+        const bool ok = e < HE && orow < nrows && (unsigned)wc < (unsigned)p.W;
         h_row[i] = pp * p.u - p.pad_top + j;
         h_base[i] = ok ? n * p.sxn + wc * p.sxw : 0;     // channel added per chunk
         h_ok |= (ok ? 1u : 0u) << i;
@@ -362,7 +386,9 @@ conv_fwd_rows1_kernel(const ConvParams p)
         s_ok0 |= (ok ? 1u : 0u) << i;
     }
 
-    float hv[NH], sv[NS];
+    using HV = typename std::conditional<XV == 4, float4, typename std::conditional<XV == 2, float2, float>::type>::type;
+    HV hv[NH];
+    float sv[NS];
     uint32_t hv_ok = 0, sv_ok = 0;
     const int nrb = (p.R + RB - 1) / RB;
     const int nch = p.C * nrb;                       // chunk = (filter row block, channel), channel fastest
@@ -375,7 +401,7 @@ conv_fwd_rows1_kernel(const ConvParams p)
         for (int i = 0; i < NH; ++i) {
             const int h = h_row[i] + r0;
             const bool ok = ((h_ok >> i) & 1u) && (unsigned)h < (unsigned)p.H;
-            hv[i] = x[ok ? h_base[i] + c * p.sxc + h * p.sxh : 0];
+            hv[i] = *reinterpret_cast<const HV*>(x + (ok ? h_base[i] + c * p.sxc + h * p.sxh : 0));
             m |= (ok ? 1u : 0u) << i;
         }
         hv_ok = m;
@@ -395,7 +421,7 @@ conv_fwd_rows1_kernel(const ConvParams p)
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
             const int e = tid + NT * i;
-            if (HALO % NT == 0 || e < HALO) dst[e] = (hv_ok >> i) & 1u ? hv[i] : 0.0f;
+            if (HE % NT == 0 || e < HE) reinterpret_cast<HV*>(dst)[e] = (hv_ok >> i) & 1u ? hv[i] : HV{};
         }
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
@@ -738,6 +764,19 @@ hipError_t launch_bwd_data_rows_mfma(const ConvParams& p0, hipStream_t stream)
     return hipSuccess;
 }
 
+// Columns per halo load of unblocked x: 4 or 2 when W, pad_left and x's
+// strides are multiples of it (a unit of consecutive columns then lies
+// wholly inside or wholly outside the row, at an aligned address), with unit
+// column stride and x aligned to it; else 1.
+static int rows_column_unit(const ConvParams& p)
+{
+    for (int v = 4; v > 1; v /= 2)
+        if (p.sxw == 1 && p.W % v == 0 && p.pad_left % v == 0 && p.sxh % v == 0 && p.sxc % v == 0 &&
+            p.sxn % v == 0 && reinterpret_cast<uintptr_t>(p.x) % (4 * v) == 0)
+            return v;
+    return 1;
+}
+
 // Eligibility: fp32, S and the filter row length of the instance, C a
 // multiple of the channel block, every tile inside NSL output rows
 // (Q >= TM), the staged row width (Q - 1) * v + S <= WP.
@@ -767,18 +806,27 @@ static hipError_t launch_rows_variant(const ConvParams& p0, hipStream_t stream)
     p.m_tiles = (p.M + TM - 1) / TM;
     p.n_tiles = (p.K + TN - 1) / TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
+    const int xv = xb ? 1 : rows_column_unit(p);
+#define MICONV_ROWS_LAUNCH(XBV, WBV, XVV)                                                                        \
+    hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP, XBV, WBV, XVV>), grid,     \
+                       dim3(256), 0, stream, p)
     if (xb && wb)
-        hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP, true, true>), grid,
-                           dim3(256), 0, stream, p);
+        MICONV_ROWS_LAUNCH(true, true, 1);
     else if (xb)
-        hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP, true, false>), grid,
-                           dim3(256), 0, stream, p);
+        MICONV_ROWS_LAUNCH(true, false, 1);
+    else if (wb && xv == 4)
+        MICONV_ROWS_LAUNCH(false, true, 4);
+    else if (wb && xv == 2)
+        MICONV_ROWS_LAUNCH(false, true, 2);
     else if (wb)
-        hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP, false, true>), grid,
-                           dim3(256), 0, stream, p);
+        MICONV_ROWS_LAUNCH(false, true, 1);
+    else if (xv == 4)
+        MICONV_ROWS_LAUNCH(false, false, 4);
+    else if (xv == 2)
+        MICONV_ROWS_LAUNCH(false, false, 2);
     else
-        hipLaunchKernelGGL((conv_fwd_rows_kernel<TM, TN, WAVES_M, WAVES_N, S, CB, NSL, WP, false, false>), grid,
-                           dim3(256), 0, stream, p);
+        MICONV_ROWS_LAUNCH(false, false, 1);
+#undef MICONV_ROWS_LAUNCH
     return hipGetLastError();
 }
 
@@ -810,8 +858,19 @@ static hipError_t launch_rows1_variant(const ConvParams& p0, hipStream_t stream)
     p.m_tiles = (p.M + kRows1TM - 1) / kRows1TM;
     p.n_tiles = (p.K + kRows1TN - 1) / kRows1TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
-    hipLaunchKernelGGL((conv_fwd_rows1_kernel<kRows1TM, kRows1TN, 4, 1, kRows1S, kRows1RB, NSL, WP>), grid,
-                       dim3(256), 0, stream, p);
+    switch (rows_column_unit(p)) {
+    case 4:
+        hipLaunchKernelGGL((conv_fwd_rows1_kernel<kRows1TM, kRows1TN, 4, 1, kRows1S, kRows1RB, NSL, WP, 4>), grid,
+                           dim3(256), 0, stream, p);
+        break;
+    case 2:
+        hipLaunchKernelGGL((conv_fwd_rows1_kernel<kRows1TM, kRows1TN, 4, 1, kRows1S, kRows1RB, NSL, WP, 2>), grid,
+                           dim3(256), 0, stream, p);
+        break;
+    default:
+        hipLaunchKernelGGL((conv_fwd_rows1_kernel<kRows1TM, kRows1TN, 4, 1, kRows1S, kRows1RB, NSL, WP, 1>), grid,
+                           dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

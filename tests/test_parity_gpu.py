@@ -109,6 +109,9 @@ def _run(lay, x, w, y, alpha=1.0, beta=0.0):
 FWD_SHAPES = SMALL_SHAPES + [
     dict(name="rows_5x11", N=2, C=16, Hh=25, Ww=270, K=40, R=5, S=11, stride=(2, 1), pads=(2, 2, 0, 10)),
     dict(name="rows_21x11", N=1, C=8, Hh=41, Ww=260, K=32, R=21, S=11, stride=(2, 1), pads=(10, 10, 0, 10)),
+    # an odd row width and left pad: the halo loads one column at a time (rows_5x11 and
+    # rows_21x11 load 2 and 4)
+    dict(name="rows_5x11_odd", N=2, C=8, Hh=21, Ww=271, K=40, R=5, S=11, stride=(1, 1), pads=(2, 2, 1, 9)),
     # one input channel (adjacent taps paired): speech-like 41x11 / (2, 2) with padding on three
     # sides and K = 40 (a ragged filter tile); 7 filter rows (the last chunk of 4 half empty)
     dict(name="rows1_41x11", N=1, C=1, Hh=61, Ww=530, K=40, R=41, S=11, stride=(2, 2), pads=(20, 20, 0, 10)),
