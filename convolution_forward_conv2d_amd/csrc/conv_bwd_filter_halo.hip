@@ -344,7 +344,9 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
 
 // row pitch WPH and plane pitch PLANE: the smallest with at most two-way
 // (fp64 three-way) bank conflicts on the halo reads, searched offline
-// (QD: output rows of exactly QD columns, the steps along them only)
+// (QD: output rows of exactly QD columns, the steps along them only).
+// 64 x 48 tiles: 256 filters x 2400 columns (96 channels, 5x5) make 200
+// tiles instead of 152 of 64 x 64 on the 256 compute units.
 //        name                     policy   TM  TN  waves  R  S  WPH  PR  PLANE  KS  QD
 #define MICONV_WGH_VARIANTS(X)                                              \
     X(WGH_F32_3x3_W16, PolF32, 64, 64, 2, 2, 3, 3, 16, 13, 243, 2, 0)       \
@@ -357,7 +359,9 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     X(WGH_F32_3x3_Q12_64x96, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 12, 247, 2, 12)     \
     X(WGH_F32_3x3_Q13, PolF32, 64, 64, 2, 2, 3, 3, 16, 14, 259, 2, 13)                \
     X(WGH_F32X16_5x5_Q20, PolF32x16, 64, 64, 2, 2, 5, 5, 24, 4, 197, 2, 20)          \
-    X(WGH_F32X16_5x5_Q27, PolF32x16, 64, 64, 2, 2, 5, 5, 32, 4, 261, 2, 27)
+    X(WGH_F32X16_5x5_Q27, PolF32x16, 64, 64, 2, 2, 5, 5, 32, 4, 261, 2, 27)          \
+    X(WGH_F32X16_5x5_Q20_64x48, PolF32x16, 64, 48, 4, 1, 5, 5, 24, 4, 197, 2, 20)    \
+    X(WGH_F32X16_5x5_Q27_64x48, PolF32x16, 64, 48, 4, 1, 5, 5, 32, 4, 261, 2, 27)
 
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream)
 {

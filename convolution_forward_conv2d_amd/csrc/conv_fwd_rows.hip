@@ -521,7 +521,11 @@ conv_fwd_rows1_kernel(const ConvParams p)
 // (the MFMA columns), C = dy's channels (the reduction), R = the phase's
 // tap rows; pad_top carries P0(h0), pad_left the column pad, u the filter
 // row step, Hp the phase a; M = N * h' * W, div_pq / div_q by h'*W and W.
-template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP>
+//
+// XV: consecutive dy columns per halo load (1, 2 or 4), as for the forward
+// kernel: the host picks XV > 1 when Q, the first staged column and dy's
+// strides are multiples of it and dy is aligned to it.
+template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP, int XV>
 __global__ void __launch_bounds__(256)
 conv_bwd_data_rows_mfma_kernel(const ConvParams p)
 {
@@ -538,7 +542,9 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
     constexpr int HALO = CB * PLANE;
     constexpr int SLAB = S * CB * TN;
     constexpr int BUF = HALO + SLAB;
-    constexpr int NH = (HALO + NT - 1) / NT;
+    static_assert((XV == 1 || XV == 2 || XV == 4) && WP % XV == 0, "column units");
+    constexpr int HE = HALO / XV;                    // halo units of XV columns
+    constexpr int NH = (HE + NT - 1) / NT;
     constexpr int STEPS = S * (CB / G);
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
     constexpr int SROWS = TN * CB;                   // slab rows (output channel, dy channel) of S taps
@@ -578,22 +584,23 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
     const int row0 = out_row(m0);
     const int nrows = p.N * hq;
 
-    // ---- halo loader: element e = (dy channel, slot, column), column fastest
+    // ---- halo loader: unit e = (dy channel, slot, XV columns), columns fastest
     int h_base[NH];
     int h_row[NH];                                    // dy row of tap row 0 (i subtracted per chunk)
     uint32_t h_ok = 0;
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
         const int e = tid + NT * i;
-        const int cl = e / PLANE;
-        const int rem = e - cl * PLANE;
+        const int el = e * XV;                        // the unit's first staged element
+        const int cl = el / PLANE;
+        const int rem = el - cl * PLANE;
         const int sl = rem / WP;
         const int col = rem - sl * WP;
         const int orow = row0 + sl;
         const int n = orow / hq;
         const int hh = orow - n * hq;
         const int qc = col + qoff;
-        const bool ok = e < HALO && orow < nrows && (unsigned)qc < (unsigned)p.Q;
+        const bool ok = e < HE && orow < nrows && (unsigned)qc < (unsigned)p.Q;
         h_row[i] = P0f + hh;
         h_base[i] = ok ? n * p.sxn + cl * p.sxc + qc * p.sxw : 0;
         h_ok |= (ok ? 1u : 0u) << i;
@@ -605,7 +612,8 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
     const bool s_ok = n0 + sk < p.K;
     const int RS = p.R * S;                           // p.R here: the filter's full row count
 
-    float hv[NH];
+    using HV = typename std::conditional<XV == 4, float4, typename std::conditional<XV == 2, float2, float>::type>::type;
+    HV hv[NH];
     uint32_t hv_ok = 0;
     float sv[SH];
     const int ncb = p.C / CB;
@@ -619,7 +627,7 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
         for (int e = 0; e < NH; ++e) {
             const int pr = h_row[e] - i;
             const bool ok = ((h_ok >> e) & 1u) && (unsigned)pr < (unsigned)p.P;
-            hv[e] = dy[ok ? h_base[e] + k0 * p.sxc + pr * p.sxh : 0];
+            hv[e] = *reinterpret_cast<const HV*>(dy + (ok ? h_base[e] + k0 * p.sxc + pr * p.sxh : 0));
             m |= (ok ? 1u : 0u) << e;
         }
         hv_ok = m;
@@ -633,7 +641,7 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
 #pragma unroll
         for (int e = 0; e < NH; ++e) {
             const int ee = tid + NT * e;
-            if (HALO % NT == 0 || ee < HALO) dst[ee] = (hv_ok >> e) & 1u ? hv[e] : 0.0f;
+            if (HE % NT == 0 || ee < HE) reinterpret_cast<HV*>(dst)[ee] = (hv_ok >> e) & 1u ? hv[e] : HV{};
         }
 #pragma unroll
         for (int j = 0; j < SH; ++j) {
@@ -730,6 +738,16 @@ bool bwd_data_rows_mfma_fits(const ConvParams& p)
 hipError_t launch_bwd_data_rows_mfma(const ConvParams& p0, hipStream_t stream)
 {
     if (!bwd_data_rows_mfma_fits(p0)) return hipErrorInvalidValue;
+    // dy columns per halo load: the first staged column pad_left - (S - 1),
+    // Q and dy's strides multiples of it, unit column stride, dy aligned
+    int xv = 1;
+    const int qoff = p0.pad_left - (kDgRowsS - 1);
+    for (int v = 4; v > 1; v /= 2)
+        if (p0.sxw == 1 && p0.Q % v == 0 && ((qoff % v) + v) % v == 0 && p0.sxh % v == 0 && p0.sxc % v == 0 &&
+            p0.sxn % v == 0 && reinterpret_cast<uintptr_t>(p0.x) % (4 * v) == 0) {
+            xv = v;
+            break;
+        }
     const int u = p0.u;
     for (int a = 0; a < u; ++a) {
         // rows h with (h + pad_top) mod u == a: h = h0 + u*h'
@@ -755,9 +773,18 @@ hipError_t launch_bwd_data_rows_mfma(const ConvParams& p0, hipStream_t stream)
         p.n_tiles = (p.K + kDgRowsTN - 1) / kDgRowsTN;
         const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
         if (nr == 0 && p.beta == 1.0) continue;      // nothing to add (alpha * 0 + dx)
-        hipLaunchKernelGGL((conv_bwd_data_rows_mfma_kernel<kDgRowsTM, kDgRowsTN, 4, 1, kDgRowsS, kDgRowsCB, 2,
-                                                           kDgRowsWP>),
-                           grid, dim3(256), 0, stream, p);
+        if (xv == 4)
+            hipLaunchKernelGGL((conv_bwd_data_rows_mfma_kernel<kDgRowsTM, kDgRowsTN, 4, 1, kDgRowsS, kDgRowsCB, 2,
+                                                               kDgRowsWP, 4>),
+                               grid, dim3(256), 0, stream, p);
+        else if (xv == 2)
+            hipLaunchKernelGGL((conv_bwd_data_rows_mfma_kernel<kDgRowsTM, kDgRowsTN, 4, 1, kDgRowsS, kDgRowsCB, 2,
+                                                               kDgRowsWP, 2>),
+                               grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((conv_bwd_data_rows_mfma_kernel<kDgRowsTM, kDgRowsTN, 4, 1, kDgRowsS, kDgRowsCB, 2,
+                                                               kDgRowsWP, 1>),
+                               grid, dim3(256), 0, stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -188,6 +188,8 @@ const WgCandidate kWg[] = {
     {{Variant::WGH_F32_3x3_Q13, 64, 64, "wgh_f32_3x3_q13_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 27.3, 1, 13},
     {{Variant::WGH_F32X16_5x5_Q20, 64, 64, "wgh_f32x16_5x5_q20_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 25.2, 1, 20},
     {{Variant::WGH_F32X16_5x5_Q27, 64, 64, "wgh_f32x16_5x5_q27_64x64"}, DType::F32, WgKind::HALO, 5, 5, 32, 29.6, 1, 27},
+    {{Variant::WGH_F32X16_5x5_Q20_64x48, 64, 48, "wgh_f32x16_5x5_q20_64x48"}, DType::F32, WgKind::HALO, 5, 5, 24, 19.9, 1, 20},
+    {{Variant::WGH_F32X16_5x5_Q27_64x48, 64, 48, "wgh_f32x16_5x5_q27_64x48"}, DType::F32, WgKind::HALO, 5, 5, 32, 23.4, 1, 27},
     {{Variant::WGS_F32_32x32, 32, 32, "wgs_f32_32x32"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 12.5, 1},
     {{Variant::WGS_F32_16x16, 16, 16, "wgs_f32_16x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 7.1, 2},
     {{Variant::WGS_F32_8x16, 8, 16, "wgs_f32_8x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 4.5, 2},
@@ -216,7 +218,8 @@ bool is_wgh(Variant v)
            v == Variant::WGH_F32_3x3_W16_64x96 || v == Variant::WGH_F32X16_3x3_W16 ||
            v == Variant::WGH_F32X16_5x5_W24 || v == Variant::WGH_F64_3x3_W16 || v == Variant::WGH_F32_3x3_Q12_64x96 ||
            v == Variant::WGH_F32_3x3_Q13 || v == Variant::WGH_F32X16_5x5_Q20 ||
-           v == Variant::WGH_F32X16_5x5_Q27;
+           v == Variant::WGH_F32X16_5x5_Q27 || v == Variant::WGH_F32X16_5x5_Q20_64x48 ||
+           v == Variant::WGH_F32X16_5x5_Q27_64x48;
 }
 
 bool is_wgr(Variant v) { return v == Variant::WGR_F32_S11_V2 || v == Variant::WGR_F32_S11_V4; }

@@ -89,6 +89,8 @@ SHAPES = SMALL_SHAPES + [
     dict(name="dg_rows_21x11", N=1, C=40, Hh=41, Ww=260, K=16, R=21, S=11, stride=(2, 1),
          pads=(10, 10, 0, 10)),
     dict(name="dg_rows_s3", N=2, C=16, Hh=20, Ww=270, K=8, R=7, S=11, stride=(3, 1), pads=(2, 1, 3, 7)),
+    # dy rows staged 4 columns per load (dg_rows_21x11: 2, dg_rows_s3: 1)
+    dict(name="dg_rows_v4", N=2, C=16, Hh=17, Ww=264, K=16, R=5, S=11, stride=(2, 1), pads=(2, 1, 2, 8)),
     # stride phases as GEMM columns: strides (2, 3) with 48 columns and uneven padding;
     # strides (3, 2) with 120 columns (a ragged second column tile), 17 dy channels (a
     # ragged channel block) and filters not a multiple of the stride
