@@ -30,7 +30,8 @@
 // chunk and steps along their QD real columns only, so no step lands on a
 // padding column; step u of the group is row G * (u / QD) + g, column
 // u % QD, at the compile-time offset G * WPH * (u / QD) + u % QD from the
-// group's base g * WPH.  Half 0 takes steps [0, SEGH), half 1 the rest
+// group's base g * WPH.  With KS groups of 4 waves ("halves", KS = 1, 2 or
+// 4), group h takes steps [h * SEGH, (h + 1) * SEGH) (the last may take fewer)
 // (one fewer when SEGP is odd), each in its own unrolled copy of the steps.
 //
 // No workspace: the reduction is not split across workgroups.  The
@@ -82,7 +83,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     constexpr int FN = WN / BM;
     constexpr int NPOS = PR * WPH;                   // positions per chunk
     constexpr int SEGP = QD > 0 ? PR / G * QD : NPOS / G;   // MFMA steps per chunk
-    constexpr int SEGH = (SEGP + KS - 1) / KS;       // ... of half 0 (QD > 0: half 1 may take one fewer)
+    constexpr int SEGH = (SEGP + KS - 1) / KS;       // ... of half 0 (QD > 0: the last half may take fewer)
     static_assert(QD == 0 || (PR % G == 0 && QD + S - 1 <= WPH), "whole rows per lane group");
     constexpr int DYP = NPOS + 1;                    // DY row pitch (odd: rows fall on other banks)
     constexpr int HROWS = PR + R - 1;
@@ -107,18 +108,19 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     static_assert(Pol::V == 1, "scalar-operand MFMA policies only");
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
     static_assert(NPOS % G == 0 && NT % TM == 0 && WPH % TPK == 0, "loader shapes");
-    static_assert((KS == 1 || KS == 2) && (QD > 0 || SEGP % KS == 0), "one or two halves split the steps");
+    static_assert((KS == 1 || KS == 2 || KS == 4) && (QD > 0 || SEGP % KS == 0) && SEGP > (KS - 1) * SEGH,
+                  "one, two or four halves split the steps");
     static_assert(NDY <= 64 && NH <= 32, "validity masks");
     static_assert(2 * BUF_BYTES <= 160 * 1024, "two chunk buffers fit the LDS");
     static_assert((SEGP + DYP) * ES < 65536, "LDS immediate offsets");
     static_assert(4 * BM * (BM + 1) * (int)sizeof(typename Pol::Acc) <= 2 * BUF_BYTES, "epilogue stage fits");
 
-    static_assert(KS == 1 || 4 * FM * FN * Pol::NACC * 64 * (int)sizeof(typename Pol::Acc) <= 2 * BUF_BYTES,
+    static_assert((KS - 1) * 4 * FM * FN * Pol::NACC * 64 * (int)sizeof(typename Pol::Acc) <= 2 * BUF_BYTES,
                   "partial sums fit in the chunk buffers");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF_BYTES];
 
-    const int half = KS == 2 ? (int)(threadIdx.x >> 8) : 0;
+    const int half = KS > 1 ? (int)(threadIdx.x >> 8) : 0;
     const int tid = threadIdx.x & 255;               // thread within its half
     const int lane = tid & 63;
     const int wave = tid >> 6;                       // wave within its half
@@ -196,7 +198,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         if constexpr (q < NDY) {
             constexpr int prs = KS * (q / QPT);
             constexpr int qj = q % QPT;
-            if (PR % KS == 0 || half + prs < PR)     // (an odd PR leaves half 1 one row short)
+            if (PR % KS == 0 || half + prs < PR)     // (PR not a multiple of KS leaves the last halves a row short)
                 dyl[kr * DYP + half * WPH + q0 + prs * WPH + TPK * qj] = ((dy_ok >> q) & 1) ? dy_val[q] : In(0);
         } else {
             constexpr int i = q - NDY;
@@ -255,7 +257,8 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         }
     };
     auto run_steps = [&](auto hc, const In* buf, int cur) {
-        constexpr int NSTEP = decltype(hc)::value == 0 ? SEGH : SEGP - SEGH;   // this half's steps
+        constexpr int H = decltype(hc)::value;
+        constexpr int NSTEP = SEGP - H * SEGH < SEGH ? SEGP - H * SEGH : SEGH;   // this half's steps
         // operands are read one step ahead of their MFMA
         In a[FM], b[FN];
 #pragma unroll
@@ -296,31 +299,41 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         const In* buf = reinterpret_cast<const In*>(smem + cur * BUF_BYTES);
         if (QD == 0 || half == 0)
             run_steps(std::integral_constant<int, 0>{}, buf, cur);
-        else
+        else if (KS == 2 || half == 1)
             run_steps(std::integral_constant<int, 1>{}, buf, cur);
+        else if constexpr (KS == 4) {
+            if (half == 2)
+                run_steps(std::integral_constant<int, 2>{}, buf, cur);
+            else
+                run_steps(std::integral_constant<int, 3>{}, buf, cur);
+        }
         __syncthreads();
     }
 
-    if constexpr (KS == 2) {
-        // half 1's partial sums -> LDS -> added by half 0 in a fixed order
+    if constexpr (KS > 1) {
+        // halves 1 .. KS-1 hand their partial sums to half 0 through LDS,
+        // which adds them in half order (a fixed order: no timing dependence)
         typename Pol::Acc* red = reinterpret_cast<typename Pol::Acc*>(smem);
+        constexpr int PART = 4 * FM * FN * Pol::NACC * 64;     // one half's partial sums
         auto red_at = [&](int i, int j, int e) { return ((((wave * FM + i) * FN + j) * Pol::NACC + e) << 6) + lane; };
-        if (half == 1) {
+        if (half > 0) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int e = 0; e < Pol::NACC; ++e) red[red_at(i, j, e)] = acc[i][j][e];
+                    for (int e = 0; e < Pol::NACC; ++e) red[(half - 1) * PART + red_at(i, j, e)] = acc[i][j][e];
         }
         __syncthreads();
         if (half == 0) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int h = 1; h < KS; ++h)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int e = 0; e < Pol::NACC; ++e) acc[i][j][e] += red[red_at(i, j, e)];
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int e = 0; e < Pol::NACC; ++e) acc[i][j][e] += red[(h - 1) * PART + red_at(i, j, e)];
         }
         __syncthreads();
     }
@@ -361,7 +374,12 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     X(WGH_F32X16_5x5_Q20, PolF32x16, 64, 64, 2, 2, 5, 5, 24, 4, 197, 2, 20)          \
     X(WGH_F32X16_5x5_Q27, PolF32x16, 64, 64, 2, 2, 5, 5, 32, 4, 261, 2, 27)          \
     X(WGH_F32X16_5x5_Q20_64x48, PolF32x16, 64, 48, 4, 1, 5, 5, 24, 4, 197, 2, 20)    \
-    X(WGH_F32X16_5x5_Q27_64x48, PolF32x16, 64, 48, 4, 1, 5, 5, 32, 4, 261, 2, 27)
+    X(WGH_F32X16_5x5_Q27_64x48, PolF32x16, 64, 48, 4, 1, 5, 5, 32, 4, 261, 2, 27)   \
+    X(WGH_F32_3x3_Q13_KS4, PolF32, 64, 64, 2, 2, 3, 3, 16, 14, 259, 4, 13)            \
+    X(WGH_F32_3x3_W16_64x96_KS4, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 13, 247, 4, 0)  \
+    X(WGH_F32_3x3_Q12_64x96_KS4, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 12, 247, 4, 12)  \
+    X(WGH_F32X16_5x5_Q20_64x48_KS4, PolF32x16, 64, 48, 4, 1, 5, 5, 24, 4, 197, 4, 20) \
+    X(WGH_F32X16_5x5_Q27_64x48_KS4, PolF32x16, 64, 48, 4, 1, 5, 5, 32, 4, 261, 4, 27)
 
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream)
 {

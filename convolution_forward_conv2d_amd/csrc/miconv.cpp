@@ -190,6 +190,13 @@ const WgCandidate kWg[] = {
     {{Variant::WGH_F32X16_5x5_Q27, 64, 64, "wgh_f32x16_5x5_q27_64x64"}, DType::F32, WgKind::HALO, 5, 5, 32, 29.6, 1, 27},
     {{Variant::WGH_F32X16_5x5_Q20_64x48, 64, 48, "wgh_f32x16_5x5_q20_64x48"}, DType::F32, WgKind::HALO, 5, 5, 24, 19.9, 1, 20},
     {{Variant::WGH_F32X16_5x5_Q27_64x48, 64, 48, "wgh_f32x16_5x5_q27_64x48"}, DType::F32, WgKind::HALO, 5, 5, 32, 23.4, 1, 27},
+    // four groups of waves per tile (16 waves a CU, latency hidden within the
+    // tile; measured on MI355X: AlexNet conv3/conv5 616 -> 576 us, conv4 952 -> 834)
+    {{Variant::WGH_F32_3x3_Q13_KS4, 64, 64, "wgh_f32_3x3_q13_64x64_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 25.5, 1, 13},
+    {{Variant::WGH_F32_3x3_W16_64x96_KS4, 64, 96, "wgh_f32_3x3_64x96_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 38.5, 1},
+    {{Variant::WGH_F32_3x3_Q12_64x96_KS4, 64, 96, "wgh_f32_3x3_q12_64x96_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 27.7, 1, 12},
+    {{Variant::WGH_F32X16_5x5_Q20_64x48_KS4, 64, 48, "wgh_f32x16_5x5_q20_64x48_ks4"}, DType::F32, WgKind::HALO, 5, 5, 24, 18.4, 1, 20},
+    {{Variant::WGH_F32X16_5x5_Q27_64x48_KS4, 64, 48, "wgh_f32x16_5x5_q27_64x48_ks4"}, DType::F32, WgKind::HALO, 5, 5, 32, 20.8, 1, 27},
     {{Variant::WGS_F32_32x32, 32, 32, "wgs_f32_32x32"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 12.5, 1},
     {{Variant::WGS_F32_16x16, 16, 16, "wgs_f32_16x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 7.1, 2},
     {{Variant::WGS_F32_8x16, 8, 16, "wgs_f32_8x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 4.5, 2},
@@ -219,7 +226,9 @@ bool is_wgh(Variant v)
            v == Variant::WGH_F32X16_5x5_W24 || v == Variant::WGH_F64_3x3_W16 || v == Variant::WGH_F32_3x3_Q12_64x96 ||
            v == Variant::WGH_F32_3x3_Q13 || v == Variant::WGH_F32X16_5x5_Q20 ||
            v == Variant::WGH_F32X16_5x5_Q27 || v == Variant::WGH_F32X16_5x5_Q20_64x48 ||
-           v == Variant::WGH_F32X16_5x5_Q27_64x48;
+           v == Variant::WGH_F32X16_5x5_Q27_64x48 || v == Variant::WGH_F32_3x3_Q13_KS4 ||
+           v == Variant::WGH_F32_3x3_W16_64x96_KS4 || v == Variant::WGH_F32_3x3_Q12_64x96_KS4 ||
+           v == Variant::WGH_F32X16_5x5_Q20_64x48_KS4 || v == Variant::WGH_F32X16_5x5_Q27_64x48_KS4;
 }
 
 bool is_wgr(Variant v) { return v == Variant::WGR_F32_S11_V2 || v == Variant::WGR_F32_S11_V4; }
