@@ -34,6 +34,15 @@
 // 4), group h takes steps [h * SEGH, (h + 1) * SEGH) (the last may take fewer)
 // (one fewer when SEGP is odd), each in its own unrolled copy of the steps.
 //
+// R = 0 ("pairs"; any filter height, any row stride u, column stride 1):
+// instead of every input row of CH whole channels, a chunk stages, for each
+// (channel c, filter row r) pair the tile's columns touch (at most
+// (TN - 2 + S) / S + 1 of them), the input rows (p0 + pr) * u + r - pad_top
+// of its PR output rows, WPH columns each, at PLANE >= PR * WPH + S - 1 per
+// pair.  B[pos, (c, r, s)] is then PAIR[(c, r)][pos + s] with the same
+// position index as DY: tall filters (21 rows onto 32 channels at stride 2,
+// the speech network's second layer) whose channel planes would not fit.
+//
 // No workspace: the reduction is not split across workgroups.  The
 // epilogue stores dw (packed K,C,R,S) along j as conv_bwd_filter.hip does.
 //
@@ -77,6 +86,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     constexpr int G = Pol::G;
     constexpr int ES = (int)sizeof(In);
     constexpr int RS = R * S;
+    constexpr int RS1 = RS > 0 ? RS : 1;             // (pairs: R = 0; divisions by RS not taken)
     constexpr int WM = TM / WAVES_M;
     constexpr int WN = TN / WAVES_N;
     constexpr int FM = WM / BM;
@@ -86,21 +96,27 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     constexpr int SEGH = (SEGP + KS - 1) / KS;       // ... of half 0 (QD > 0: the last half may take fewer)
     static_assert(QD == 0 || (PR % G == 0 && QD + S - 1 <= WPH), "whole rows per lane group");
     constexpr int DYP = NPOS + 1;                    // DY row pitch (odd: rows fall on other banks)
-    constexpr int HROWS = PR + R - 1;
+    constexpr bool PAIRS = R == 0;                   // staged rows: the tile's (channel, filter row) pairs
+    constexpr int HROWS = PAIRS ? PR : PR + R - 1;
     // A padding position's tap (q + s up to WPH + S - 2) reads up to S - 1
     // elements past the plane's last row: PLANE >= HROWS * WPH + S - 1 leaves
     // spare elements, zeroed once, so such reads see finite zeros.  Beyond
     // that, WPH and PLANE are chosen so the 32 columns (c, r, s) a half-wave
     // reads land on distinct LDS banks but for at most two-way conflicts.
-    static_assert(PLANE >= HROWS * WPH + S - 1, "plane spare");
-    constexpr int CH = (RS - 1 + TN - 1) / RS + 1;   // channels TN consecutive columns can touch
+    static_assert(PLANE >= HROWS * WPH + S - 1, "plane spare");   // (pairs: HROWS = PR)
+    // channels (pairs) TN consecutive columns can touch
+    constexpr int CH = PAIRS ? (TN - 2 + S) / S + 1 : (RS - 1 + TN - 1) / RS1 + 1;
     constexpr int DY_ELEMS = TM * DYP;
     constexpr int BUF_BYTES = ((DY_ELEMS + CH * PLANE) * ES + 15) / 16 * 16;
     // DY loader: in each half TPK threads per filter row; half h takes rows
-    // pr = h + KS * i, a thread positions q0 + TPK * j of them
-    constexpr int TPK = NT / TM;
+    // pr = h + KS * i, a thread positions q0 + TPK * j of them.  With fewer
+    // rows than halves (DY_ALL) all threads share every row instead: TPK =
+    // the workgroup's threads per filter row.
+    constexpr bool DY_ALL = PR < KS;
+    constexpr int TPK = (DY_ALL ? NTT : NT) / TM;
     constexpr int QPT = WPH / TPK;                   // q values a thread visits per row
-    constexpr int PRH = (PR + KS - 1) / KS;          // rows per half
+    constexpr int PRH = DY_ALL ? PR : (PR + KS - 1) / KS;   // rows per thread
+    constexpr int RSTEP = DY_ALL ? 1 : KS;           // between a thread's rows
     constexpr int NDY = PRH * QPT;                   // DY elements per thread per chunk
     // halo loader: units (channel, row, column), column fastest, over all threads
     constexpr int HU = CH * HROWS * WPH;
@@ -108,6 +124,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     static_assert(Pol::V == 1, "scalar-operand MFMA policies only");
     static_assert(WAVES_M * WAVES_N == 4 && WM % BM == 0 && WN % BM == 0, "wave tiling");
     static_assert(NPOS % G == 0 && NT % TM == 0 && WPH % TPK == 0, "loader shapes");
+    static_assert(PLANE >= (PAIRS ? PR * WPH : 0) + S - 1, "pair spare");
     static_assert((KS == 1 || KS == 2 || KS == 4) && (QD > 0 || SEGP % KS == 0) && SEGP > (KS - 1) * SEGH,
                   "one, two or four halves split the steps");
     static_assert(NDY <= 64 && NH <= 32, "validity masks");
@@ -129,7 +146,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     const int nt = tile - mt * p.n_tiles;
     const int m0 = mt * TM;
     const int n0 = nt * TN;
-    const int c_lo = n0 / RS;
+    const int c_lo = PAIRS ? n0 / S : n0 / RS1;     // first channel (pair) the tile's columns touch
 
     const In* __restrict__ x = static_cast<const In*>(p.x);
     const In* __restrict__ dy = static_cast<const In*>(p.w);
@@ -141,11 +158,13 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         reinterpret_cast<u32x4*>(smem)[i] = u32x4{0, 0, 0, 0};
     __syncthreads();
 
-    // ---- DY loader geometry: filter row kr, first position q0
-    const int kr = tid / TPK;
-    const int q0 = tid % TPK;
+    // ---- DY loader geometry: filter row kr, first position q0, first row rh
+    const int ltid = DY_ALL ? (int)threadIdx.x : tid;
+    const int kr = ltid / TPK;
+    const int q0 = ltid % TPK;
+    const int rh = DY_ALL ? 0 : half;
     const bool k_ok = m0 + kr < p.M;
-    const int dy_thread = (m0 + (k_ok ? kr : 0)) * p.sdk + half * p.sdp + q0 * p.sdq;
+    const int dy_thread = (m0 + (k_ok ? kr : 0)) * p.sdk + rh * p.sdp + q0 * p.sdq;
     uint32_t q_ok = 0;                               // bit j: q0 + TPK * j < Q
 #pragma unroll
     for (int j = 0; j < QPT; ++j) q_ok |= (q0 + TPK * j < p.Q ? 1u : 0u) << j;
@@ -154,6 +173,29 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     uint64_t dy_ok = 0;
     In h_val[NH];
     uint32_t h_ok = 0;
+
+    // pairs: a halo piece's (channel, column) offset and its input row at
+    // chunk row 0 (the chunk adds p0 * u), fixed for the tile
+    int pz_off[PAIRS ? NH : 1], pz_row[PAIRS ? NH : 1];
+    uint32_t pz_ok = 0;
+    if constexpr (PAIRS) {
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int e = (int)threadIdx.x + NTT * i;
+            const int hc = e % WPH;
+            const int rowi = e / WPH;
+            const int chl = rowi / HROWS;
+            const int hr = rowi - chl * HROWS;
+            const int cr = c_lo + chl;
+            const int c = cr / p.R;
+            const int r = cr - c * p.R;
+            const int w = hc - p.pad_left;
+            const bool ok = e < HU && c < p.C && (unsigned)w < (unsigned)p.W;
+            pz_off[i] = ok ? c * p.sxc + w * p.sxw : 0;
+            pz_row[i] = hr * p.u + r - p.pad_top;
+            pz_ok |= (ok ? 1u : 0u) << i;
+        }
+    }
 
     // The next chunk moves global -> registers -> LDS in NL pieces (one
     // element each) spread over the current chunk's MFMA steps: loads over
@@ -171,12 +213,18 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     auto load_piece = [&](auto qc) {
         constexpr int q = decltype(qc)::value;
         if constexpr (q < NDY) {
-            constexpr int prs = KS * (q / QPT);      // row half + prs, column q0 + TPK * qj
+            constexpr int prs = RSTEP * (q / QPT);   // row rh + prs, column q0 + TPK * qj
             constexpr int qj = q % QPT;
-            const bool ok = k_ok && ((q_ok >> qj) & 1) && half + prs < PR && cp0 + half + prs < p.P;
+            const bool ok = k_ok && ((q_ok >> qj) & 1) && rh + prs < PR && cp0 + rh + prs < p.P;
             const int off = cdy + dy_thread + prs * p.sdp + TPK * qj * p.sdq;
             dy_val[q] = load_elem(dy + (ok ? off : 0));
             dy_ok |= (uint64_t)(ok ? 1u : 0u) << q;
+        } else if constexpr (PAIRS) {
+            constexpr int i = q - NDY;
+            const int h = cp0 * p.u + pz_row[i];
+            const bool ok = ((pz_ok >> i) & 1) && (unsigned)h < (unsigned)p.H;
+            h_val[i] = load_elem(x + (ok ? cn * p.sxn + pz_off[i] + h * p.sxh : 0));
+            h_ok |= (ok ? 1u : 0u) << i;
         } else {
             constexpr int i = q - NDY;
             const int e = (int)threadIdx.x + NTT * i;
@@ -196,10 +244,11 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         constexpr int q = decltype(qc)::value;
         In* dyl = reinterpret_cast<In*>(smem + buf * BUF_BYTES);
         if constexpr (q < NDY) {
-            constexpr int prs = KS * (q / QPT);
+            constexpr int prs = RSTEP * (q / QPT);
             constexpr int qj = q % QPT;
-            if (PR % KS == 0 || half + prs < PR)     // (PR not a multiple of KS leaves the last halves a row short)
-                dyl[kr * DYP + half * WPH + q0 + prs * WPH + TPK * qj] = ((dy_ok >> q) & 1) ? dy_val[q] : In(0);
+            // (PR not a multiple of KS leaves the last halves a row short)
+            if (DY_ALL || PR % KS == 0 || rh + prs < PR)
+                dyl[kr * DYP + rh * WPH + q0 + prs * WPH + TPK * qj] = ((dy_ok >> q) & 1) ? dy_val[q] : In(0);
         } else {
             constexpr int i = q - NDY;
             const int e = (int)threadIdx.x + NTT * i;
@@ -228,10 +277,16 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int col = n0 + wn * WN + j * BM + lrow;        // past C*R*S: a zero region, masked at the store
-        uint32_t c, rs, r, s;
-        p.div_rs.divmod((uint32_t)col, c, rs);
-        p.div_s.divmod(rs, r, s);
-        b_base[j] = DY_ELEMS + ((int)c - c_lo) * PLANE + (int)r * WPH + (int)s + pos_base;
+        if constexpr (PAIRS) {
+            uint32_t cr, s;
+            p.div_s.divmod((uint32_t)col, cr, s);
+            b_base[j] = DY_ELEMS + ((int)cr - c_lo) * PLANE + (int)s + pos_base;
+        } else {
+            uint32_t c, rs, r, s;
+            p.div_rs.divmod((uint32_t)col, c, rs);
+            p.div_s.divmod(rs, r, s);
+            b_base[j] = DY_ELEMS + ((int)c - c_lo) * PLANE + (int)r * WPH + (int)s + pos_base;
+        }
     }
 
     AccV acc[FM][FN];
@@ -345,7 +400,8 @@ template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int
 static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
 {
     ConvParams p = p0;
-    if (p.u != 1 || p.v != 1 || p.R != R || p.S != S || p.Q + S - 1 > WPH || (QD > 0 && p.Q != QD))
+    // R = 0 (pairs): any filter height and row stride
+    if ((R > 0 && (p.u != 1 || p.R != R)) || p.v != 1 || p.S != S || p.Q + S - 1 > WPH || (QD > 0 && p.Q != QD))
         return hipErrorInvalidValue;
     p.m_tiles = (p.M + TM - 1) / TM;
     p.n_tiles = (p.K + TN - 1) / TN;
@@ -379,7 +435,9 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     X(WGH_F32_3x3_W16_64x96_KS4, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 13, 247, 4, 0)  \
     X(WGH_F32_3x3_Q12_64x96_KS4, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 12, 247, 4, 12)  \
     X(WGH_F32X16_5x5_Q20_64x48_KS4, PolF32x16, 64, 48, 4, 1, 5, 5, 24, 4, 197, 4, 20) \
-    X(WGH_F32X16_5x5_Q27_64x48_KS4, PolF32x16, 64, 48, 4, 1, 5, 5, 32, 4, 261, 4, 27)
+    X(WGH_F32X16_5x5_Q27_64x48_KS4, PolF32x16, 64, 48, 4, 1, 5, 5, 32, 4, 261, 4, 27)   \
+    X(WGH_F32X16_PAIRS_S11_32x32, PolF32x16, 32, 32, 2, 2, 0, 11, 368, 1, 378, 2, 0)      \
+    X(WGH_F32X16_PAIRS_S11_32x32_KS4, PolF32x16, 32, 32, 2, 2, 0, 11, 384, 1, 394, 4, 0)
 
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream)
 {

@@ -197,6 +197,10 @@ const WgCandidate kWg[] = {
     {{Variant::WGH_F32_3x3_Q12_64x96_KS4, 64, 96, "wgh_f32_3x3_q12_64x96_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 27.7, 1, 12},
     {{Variant::WGH_F32X16_5x5_Q20_64x48_KS4, 64, 48, "wgh_f32x16_5x5_q20_64x48_ks4"}, DType::F32, WgKind::HALO, 5, 5, 24, 18.4, 1, 20},
     {{Variant::WGH_F32X16_5x5_Q27_64x48_KS4, 64, 48, "wgh_f32x16_5x5_q27_64x48_ks4"}, DType::F32, WgKind::HALO, 5, 5, 32, 20.8, 1, 27},
+    // r = 0: the (channel, filter row) pairs of the tile's columns staged, any
+    // filter height and row stride (speech layer 2: 21 x 11 at stride (2, 1))
+    {{Variant::WGH_F32X16_PAIRS_S11_32x32, 32, 32, "wgh_f32x16_pairs_s11_32x32"}, DType::F32, WgKind::HALO, 0, 11, 368, 9.6, 1},
+    {{Variant::WGH_F32X16_PAIRS_S11_32x32_KS4, 32, 32, "wgh_f32x16_pairs_s11_32x32_ks4"}, DType::F32, WgKind::HALO, 0, 11, 384, 8.0, 1},
     {{Variant::WGS_F32_32x32, 32, 32, "wgs_f32_32x32"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 12.5, 1},
     {{Variant::WGS_F32_16x16, 16, 16, "wgs_f32_16x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 7.1, 2},
     {{Variant::WGS_F32_8x16, 8, 16, "wgs_f32_8x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 4.5, 2},
@@ -228,7 +232,8 @@ bool is_wgh(Variant v)
            v == Variant::WGH_F32X16_5x5_Q27 || v == Variant::WGH_F32X16_5x5_Q20_64x48 ||
            v == Variant::WGH_F32X16_5x5_Q27_64x48 || v == Variant::WGH_F32_3x3_Q13_KS4 ||
            v == Variant::WGH_F32_3x3_W16_64x96_KS4 || v == Variant::WGH_F32_3x3_Q12_64x96_KS4 ||
-           v == Variant::WGH_F32X16_5x5_Q20_64x48_KS4 || v == Variant::WGH_F32X16_5x5_Q27_64x48_KS4;
+           v == Variant::WGH_F32X16_5x5_Q20_64x48_KS4 || v == Variant::WGH_F32X16_5x5_Q27_64x48_KS4 ||
+           v == Variant::WGH_F32X16_PAIRS_S11_32x32 || v == Variant::WGH_F32X16_PAIRS_S11_32x32_KS4;
 }
 
 bool is_wgr(Variant v) { return v == Variant::WGR_F32_S11_V2 || v == Variant::WGR_F32_S11_V4; }
@@ -1064,8 +1069,9 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
         if (force && strcmp(force, wc.c.name) != 0) continue;
         bool ok = true;
         if (wc.kind == WgKind::HALO)
-            ok = wc.r == wd->r && wc.s == wd->s && cd->u == 1 && cd->v == 1 && Q + wc.s - 1 <= wc.wph &&
-                 (wc.qd == 0 || Q == wc.qd);
+            // (r = 0: any filter height and row stride)
+            ok = (wc.r == 0 || (wc.r == wd->r && cd->u == 1)) && wc.s == wd->s && cd->v == 1 &&
+                 Q + wc.s - 1 <= wc.wph && (wc.qd == 0 || Q == wc.qd);
         else if (wc.kind == WgKind::SPLIT)
             ok = split_fits;
         else if (wc.kind == WgKind::ROWS)

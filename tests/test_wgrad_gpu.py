@@ -45,7 +45,8 @@ WG_VARIANTS = {
 WG_VARIANTS["f32"] += ["wgh_f32_3x3_q12_64x96", "wgh_f32_3x3_q13_64x64", "wgh_f32x16_5x5_q20_64x64",
                        "wgh_f32x16_5x5_q27_64x64", "wgh_f32x16_5x5_q20_64x48", "wgh_f32x16_5x5_q27_64x48",
                        "wgh_f32_3x3_q13_64x64_ks4", "wgh_f32_3x3_64x96_ks4", "wgh_f32_3x3_q12_64x96_ks4",
-                       "wgh_f32x16_5x5_q20_64x48_ks4", "wgh_f32x16_5x5_q27_64x48_ks4"]
+                       "wgh_f32x16_5x5_q20_64x48_ks4", "wgh_f32x16_5x5_q27_64x48_ks4",
+                       "wgh_f32x16_pairs_s11_32x32", "wgh_f32x16_pairs_s11_32x32_ks4"]
 # the first-layer kernels on the vector ALU (wgr_): 11-wide filter rows at column stride 2 or 4
 WG_VARIANTS["f32"] += ["wgr_f32_s11_v2", "wgr_f32_s11_v4"]
 # the halo variants (wgh_) take stride-1 layers of their filter size whose rows fit their pitch, the
@@ -101,6 +102,12 @@ WG_SHAPES = SMALL_SHAPES + [
     dict(name="wgh_q13", N=2, C=12, Hh=13, Ww=13, K=70, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
     dict(name="wgh_q20_5x5", N=2, C=7, Hh=22, Ww=24, K=40, R=5, S=5, stride=(1, 1), pads=(1, 1, 0, 0)),
     dict(name="wgh_q27_5x5", N=2, C=5, Hh=10, Ww=27, K=70, R=5, S=5, stride=(1, 1), pads=(2, 2, 2, 2)),
+    # (channel, filter row) pairs staged: 21x11 at stride (2, 1) onto 3 channels (693 columns, a
+    # ragged last 32-column tile; filter count 20 ragged against 32), row stride 3 with rows in the
+    # padding, and stride 1 with a 358-wide output row (the staged row is 368)
+    dict(name="pairs_21x11_s2", N=2, C=3, Hh=41, Ww=120, K=20, R=21, S=11, stride=(2, 1), pads=(10, 10, 0, 10)),
+    dict(name="pairs_7x11_s3", N=3, C=2, Hh=25, Ww=50, K=36, R=7, S=11, stride=(3, 1), pads=(4, 1, 3, 2)),
+    dict(name="pairs_3x11_wide", N=1, C=2, Hh=6, Ww=360, K=8, R=3, S=11, stride=(1, 1), pads=(1, 1, 4, 4)),
 ]
 
 
