@@ -46,8 +46,7 @@ sys.path.insert(0, ROOT)
 # MI355X dense MFMA peaks (256 CU x 2.4 GHz): fp32 256, fp64 128, bf16 4096 FLOP/clk/CU
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "bf16": 2516.6}
 # committed rocprofv3 counter summaries, per workload (HBM bytes per launch of the dominant kernel)
-PROFILE_TRAFFIC = {"overfeat": os.path.join(ROOT, "profiles", "traffic_overfeat_fp32.md"),
-                   "alexnet": os.path.join(ROOT, "profiles", "traffic_alexnet_fp32.md")}
+PROFILE_TRAFFIC = {"overfeat": os.path.join(ROOT, "profiles", "traffic_overfeat_fp32.md")}
 WORKLOADS = ("alexnet", "overfeat", "speech", "tiny", "prec_f64", "prec_bf16", "alexnet_pool", "alexnet_fc",
              "alexnet_fc_f64", "alexnet_fc_bf16")
 HBM_PEAK_GBS = 8000.0
