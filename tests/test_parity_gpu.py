@@ -90,6 +90,13 @@ SMALL_SHAPES = [
          pads=(1, 1, 1, 1), layout="nhwc", pitch=16),
     # one 16-channel block, stride 2, asymmetric padding, non-square input
     dict(name="halo3_c16_s2", N=2, C=16, Hh=14, Ww=12, K=40, R=3, S=3, stride=(2, 2), pads=(1, 0, 1, 1)),
+    # NCHW rows on a 16-element pitch: bf16 rows loaded 8 pixels at a time (a whole and a
+    # 5-pixel segment per row; the tensor's last row read pixel by pixel), two channel blocks
+    dict(name="halo3_c32_pitch16", N=3, C=32, Hh=13, Ww=13, K=72, R=3, S=3, stride=(1, 1),
+         pads=(1, 1, 1, 1), pitch=16),
+    # ... 8-pixel rows (one whole segment) with asymmetric padding
+    dict(name="halo3_w8_pitch16", N=2, C=16, Hh=9, Ww=8, K=40, R=3, S=3, stride=(1, 1),
+         pads=(0, 2, 2, 0), pitch=16),
 ]
 
 
