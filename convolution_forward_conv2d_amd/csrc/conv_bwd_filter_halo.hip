@@ -437,7 +437,9 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     X(WGH_F32X16_5x5_Q20_64x48_KS4, PolF32x16, 64, 48, 4, 1, 5, 5, 24, 4, 197, 4, 20) \
     X(WGH_F32X16_5x5_Q27_64x48_KS4, PolF32x16, 64, 48, 4, 1, 5, 5, 32, 4, 261, 4, 27)   \
     X(WGH_F32X16_PAIRS_S11_32x32, PolF32x16, 32, 32, 2, 2, 0, 11, 368, 1, 378, 2, 0)      \
-    X(WGH_F32X16_PAIRS_S11_32x32_KS4, PolF32x16, 32, 32, 2, 2, 0, 11, 384, 1, 394, 4, 0)
+    X(WGH_F32X16_PAIRS_S11_32x32_KS4, PolF32x16, 32, 32, 2, 2, 0, 11, 384, 1, 394, 4, 0)  \
+    X(WGH_F64_3x3_W16_KS4, PolF64, 64, 64, 2, 2, 3, 3, 16, 7, 147, 4, 0)                  \
+    X(WGH_F64_3x3_W16_64x96, PolF64, 64, 96, 2, 2, 3, 3, 16, 7, 147, 2, 0)
 
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream)
 {

@@ -77,6 +77,8 @@ enum class Variant : int {
     WGH_F32X16_5x5_Q27_64x48_KS4,  // 5x5, 27 columns, 64 x 48, four groups of waves per tile
     WGH_F32X16_PAIRS_S11_32x32,     // 11-wide filter rows, any height and row stride: (c, r) pairs staged
     WGH_F32X16_PAIRS_S11_32x32_KS4, // ... four groups of waves per tile
+    WGH_F64_3x3_W16_KS4,            // fp64 3x3 64x64, four groups of waves per tile
+    WGH_F64_3x3_W16_64x96,          // fp64 3x3 64x96
     WGC_BF16_64x64,         // filter gradient, bf16, channels-last x and dy (conv_bwd_filter_cl.hip)
     WGC_BF16_64x64_KS2,     // ... two groups of waves split the reduction
     WGC_BF16_64x64_KS3,     // ... three groups

@@ -201,6 +201,10 @@ const WgCandidate kWg[] = {
     // filter height and row stride (speech layer 2: 21 x 11 at stride (2, 1))
     {{Variant::WGH_F32X16_PAIRS_S11_32x32, 32, 32, "wgh_f32x16_pairs_s11_32x32"}, DType::F32, WgKind::HALO, 0, 11, 368, 9.6, 1},
     {{Variant::WGH_F32X16_PAIRS_S11_32x32_KS4, 32, 32, "wgh_f32x16_pairs_s11_32x32_ks4"}, DType::F32, WgKind::HALO, 0, 11, 384, 8.0, 1},
+    // fp64: four wave groups (AlexNet-shape conv3 / conv5 560 -> 519 us); 64x96
+    // tiles where 64x64 would take a second round (conv4: 324 -> 216 tiles, 1110 -> 765 us)
+    {{Variant::WGH_F64_3x3_W16_KS4, 64, 64, "wgh_f64_3x3_64x64_ks4"}, DType::F64, WgKind::HALO, 3, 3, 16, 48.1, 1},
+    {{Variant::WGH_F64_3x3_W16_64x96, 64, 96, "wgh_f64_3x3_64x96"}, DType::F64, WgKind::HALO, 3, 3, 16, 71.7, 1},
     {{Variant::WGS_F32_32x32, 32, 32, "wgs_f32_32x32"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 12.5, 1},
     {{Variant::WGS_F32_16x16, 16, 16, "wgs_f32_16x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 7.1, 2},
     {{Variant::WGS_F32_8x16, 8, 16, "wgs_f32_8x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 4.5, 2},
@@ -233,7 +237,8 @@ bool is_wgh(Variant v)
            v == Variant::WGH_F32X16_5x5_Q27_64x48 || v == Variant::WGH_F32_3x3_Q13_KS4 ||
            v == Variant::WGH_F32_3x3_W16_64x96_KS4 || v == Variant::WGH_F32_3x3_Q12_64x96_KS4 ||
            v == Variant::WGH_F32X16_5x5_Q20_64x48_KS4 || v == Variant::WGH_F32X16_5x5_Q27_64x48_KS4 ||
-           v == Variant::WGH_F32X16_PAIRS_S11_32x32 || v == Variant::WGH_F32X16_PAIRS_S11_32x32_KS4;
+           v == Variant::WGH_F32X16_PAIRS_S11_32x32 || v == Variant::WGH_F32X16_PAIRS_S11_32x32_KS4 ||
+           v == Variant::WGH_F64_3x3_W16_KS4 || v == Variant::WGH_F64_3x3_W16_64x96;
 }
 
 bool is_wgr(Variant v) { return v == Variant::WGR_F32_S11_V2 || v == Variant::WGR_F32_S11_V4; }

@@ -38,7 +38,8 @@ WG_VARIANTS = {
     "f32": ["wg_f32_128x128", "wg_f32_64x128", "wg_f32_128x64", "wg_f32_64x64", "wgh_f32_3x3_64x64",
             "wgh_f32_5x5_w24_64x64", "wgh_f32_5x5_w36_64x64", "wgh_f32_3x3_64x96", "wgh_f32x16_3x3_64x64",
             "wgh_f32x16_5x5_w24_64x64", "wgs_f32_32x32", "wgs_f32_16x16", "wgs_f32_8x16"],
-    "f64": ["wg_f64_128x64", "wg_f64_64x64", "wgh_f64_3x3_64x64", "wgs_f64_32x32", "wgs_f64_16x16"],
+    "f64": ["wg_f64_128x64", "wg_f64_64x64", "wgh_f64_3x3_64x64", "wgs_f64_32x32", "wgs_f64_16x16",
+            "wgh_f64_3x3_64x64_ks4", "wgh_f64_3x3_64x96"],
     "bf16": ["wg_bf16_128x128", "wg_bf16_64x64", "wgs_bf16_32x32"],
 }
 # the 3x3 halo kernel that steps along output rows of exactly 12 columns (no padding positions)
