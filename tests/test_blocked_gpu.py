@@ -125,8 +125,11 @@ def _full(lay, cb, integer=False):
     return x64, w64, case, (N, K, P, Q)
 
 
+# AlexNet conv3 on the fp32 halo kernel, bf16 conv4 on the bf16 halo kernel's transposing
+# filter loader, speech L2 on the row-streamed kernel's channel-group loads
 FULL = [(workloads.ALEXNET[1], 16), (workloads.ALEXNET[1], 32),
-        ([l for l in workloads.PRECISION if l.name == "prec_conv4_bf16_nchw"][0], 32)]
+        ([l for l in workloads.PRECISION if l.name == "prec_conv4_bf16_nchw"][0], 32),
+        (workloads.by_name("speech_l2"), 16)]
 
 
 @pytest.mark.parametrize("lay,cb", FULL, ids=lambda v: v.name if hasattr(v, "name") else str(v))
