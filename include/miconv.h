@@ -124,9 +124,11 @@ mic_status mic_tensor_desc_get(mic_tensor_desc desc, mic_dtype* dtype,
  * c must be a multiple of cb (no padding channels), cb >= 1, else
  * MIC_STATUS_BAD_PARAM.  Accepted by mic_conv_forward for x and y, any cb:
  * the tap-batched kernels read blocked x when cb is a multiple of their
- * channel chunk (2 or 4 channels fp32/fp64, 16 bf16), the gather kernel's
- * tap order when it is a multiple of 16 (32 bf16); other blockings run the
- * gather kernel's flat order or the direct kernel.  The other operations
+ * channel chunk (2 or 4 channels fp32/fp64, 16 bf16), the row-streamed
+ * kernel (11-wide filter rows) when it is a multiple of 4 and x is 16-byte
+ * aligned, the gather kernel's tap order when it is a multiple of 16 (32
+ * bf16); other blockings run the gather kernel's flat order or the direct
+ * kernel.  The other operations
  * return MIC_STATUS_NOT_SUPPORTED for blocked descriptors.
  * mic_tensor_desc_set / _set_packed reset a descriptor to unblocked. */
 mic_status mic_tensor_desc_set_blocked(mic_tensor_desc desc, mic_dtype dtype, int n, int c, int h, int w,
@@ -153,10 +155,11 @@ mic_status mic_filter_desc_get(mic_filter_desc desc, mic_dtype* dtype, int* k, i
  *   ((k/kb)*(C/cb) + c/cb)*R*S*cb*kb + ((r*S + s)*cb + c%cb)*kb + k%kb.
  * k must be a multiple of kb and c of cb (kb, cb >= 1), else
  * MIC_STATUS_BAD_PARAM.  Forward pass only, as for blocked tensors: the
- * fp32/fp64 tap-batched kernels read them when cb is a multiple of their
- * channel chunk and kb of 4 (fp32) or 2 (fp64) with w 16-byte aligned, the
- * gather kernel when cb is a multiple of 16 (32 bf16), else the direct
- * kernel runs.  mic_filter_desc_set resets a descriptor to packed KCRS. */
+ * tap-batched kernels read them when cb is a multiple of their channel
+ * chunk and kb of 4 (fp32), 2 (fp64) or 8 (bf16, cb a multiple of 16) with
+ * w 16-byte aligned, the row-streamed kernel tap by tap, the gather kernel
+ * when cb is a multiple of 16 (32 bf16), else the direct kernel runs.
+ * mic_filter_desc_set resets a descriptor to packed KCRS. */
 mic_status mic_filter_desc_set_blocked(mic_filter_desc desc, mic_dtype dtype, int k, int c, int r, int s,
                                        int kb, int cb);
 
