@@ -51,8 +51,14 @@ namespace miconv {
 // CU but whose unconstrained allocation would not (Overfeat L2 on 208 x 64
 // tiles: 603 -> 520 us; AlexNet conv2-conv4 and the fp64 128 x 64 tiles
 // 1-2% faster); a cap would hurt the instances that run three.
+//
+// XR: x rows with unit column stride, 16-byte aligned, W a multiple of VX =
+// 16 / sizeof(element): the halo moves as 16-byte loads of VX consecutive
+// pixels of one (channel, slot) row, stored element by element at their
+// padded columns; pixels outside the plane (padding columns, rows outside x,
+// slots past the tile) are never written -- the halo starts zeroed.
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS,
-          bool DG, bool WB, int WPE>
+          bool DG, bool WB, int WPE, bool XR>
 __global__ void __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(WPE)))
 conv_fwd_halo_kernel(const ConvParams p)
 {
@@ -74,6 +80,11 @@ conv_fwd_halo_kernel(const ConvParams p)
     constexpr int PLANE = SL * WP + 16;
     constexpr int HALO_BYTES = CB * PLANE * ES;
     constexpr int HE = (CB * SL * WP) / NT;      // halo elements per thread per chunk
+    constexpr int VX = 16 / ES;                  // XR: pixels per 16-byte load
+    constexpr int NSX = WP / VX;                 // ... segments per staged row (W <= WP)
+    constexpr int HUX = CB * SL * NSX;           // ... units per chunk
+    constexpr int HXT = XR ? (HUX + NT - 1) / NT : 0;
+    static_assert(!XR || ((SL * WP + 16) * ES) % 16 == 0 && (WP * ES) % 16 == 0, "16-byte aligned rows and planes");
     // filter slab: TN rows of TK values; row pitch an odd number of 8-byte units
     constexpr int ROW8 = (TK * ES + 7) / 8;
     constexpr int BROW = 8 * (ROW8 % 2 ? ROW8 : ROW8 + 1);
@@ -112,6 +123,12 @@ conv_fwd_halo_kernel(const ConvParams p)
     const int lane = tid & 63;
     const int wave = tid >> 6;                   // wave within its half
     unsigned char* smem = smem_all + half * 2 * BUF_BYTES;
+    if constexpr (XR) {
+        // every halo buffer starts zeroed: the row loader writes only pixels inside x
+        for (int i = (int)threadIdx.x; i < KS * 2 * BUF_BYTES / 16; i += NT * KS)
+            reinterpret_cast<u32x4*>(smem_all)[i] = u32x4{0, 0, 0, 0};
+        __syncthreads();
+    }
 
     const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
     const TileRC rc = grouped_tile(tile, p.m_tiles, p.n_tiles, p.n_group);
@@ -153,6 +170,28 @@ conv_fwd_halo_kernel(const ConvParams p)
         h_off[i] = ok ? (int)n * p.sxn + cl * p.sxc + h * p.sxh + wcol * p.sxw : 0;
         h_ok |= (ok ? 1u : 0u) << i;
     }
+
+    // XR: unit u = (channel, slot, segment): pixels w0 .. w0 + VX - 1, w0 = VX * segment
+    int x_off[XR ? HXT : 1], x_dst[XR ? HXT : 1];
+    uint32_t x_ok = 0;
+    if constexpr (XR) {
+#pragma unroll
+        for (int i = 0; i < HXT; ++i) {
+            const int u = tid + NT * i;
+            const int seg = u % NSX;
+            const int slot = (u / NSX) % SL;
+            const int cl = u / (NSX * SL);
+            uint32_t n, hp;
+            p.div_hp.divmod((uint32_t)(vr_first + slot), n, hp);
+            const int h = (int)hp - p.pad_top;
+            const int w0 = VX * seg;
+            const bool ok = u < HUX && slot < nslots && (int)n < p.N && h >= 0 && h < p.H && w0 < p.W;
+            x_off[i] = ok ? (int)n * p.sxn + cl * p.sxc + h * p.sxh + w0 : 0;
+            x_dst[i] = cl * PLANE + slot * WP + w0 + p.pad_left;     // element index of pixel w0
+            x_ok |= (ok ? 1u : 0u) << i;
+        }
+    }
+    u32x4 x_val[XR ? HXT : 1];
 
     // ---- slab loader: thread -> NVB (filter row, vector) positions
     // (DG: thread -> NDU (slab row, channel) runs of R*S taps instead)
@@ -210,8 +249,13 @@ conv_fwd_halo_kernel(const ConvParams p)
 
     auto load_chunk = [&](int c0) {
         const int xo = blk_off(p.div_xcb, p.sxcb, p.sxc, c0);
+        if constexpr (XR) {
 #pragma unroll
-        for (int i = 0; i < HE; ++i) h_val[i] = ((h_ok >> i) & 1) ? load_elem(x + h_off[i] + xo) : In(0);
+            for (int i = 0; i < HXT; ++i) x_val[i] = *reinterpret_cast<const u32x4*>(x + x_off[i] + xo);
+        } else {
+#pragma unroll
+            for (int i = 0; i < HE; ++i) h_val[i] = ((h_ok >> i) & 1) ? load_elem(x + h_off[i] + xo) : In(0);
+        }
         if constexpr (DG) {
             const int wo = c0 * p.K * RS;
 #pragma unroll
@@ -242,13 +286,32 @@ conv_fwd_halo_kernel(const ConvParams p)
 
     auto store_chunk = [&](int buf) {
         unsigned char* hb = smem + buf * BUF_BYTES;
+        if constexpr (XR) {
+            // a segment starts on a 16-byte LDS boundary when pad_left is a
+            // multiple of VX (the plane and row pitches are): one 16-byte store
+            const bool whole = p.pad_left % VX == 0;
 #pragma unroll
-        for (int i = 0; i < HE; ++i) {
-            const int e = tid + NT * i;
-            const int col = e % WP;
-            const int slot = (e / WP) % SL;
-            const int cl = e / (WP * SL);
-            reinterpret_cast<In*>(hb)[cl * PLANE + slot * WP + col] = h_val[i];
+            for (int i = 0; i < HXT; ++i) {
+                if ((x_ok >> i) & 1) {
+                    if (whole) {
+                        *reinterpret_cast<u32x4*>(hb + x_dst[i] * ES) = x_val[i];
+                    } else {
+                        In v[VX];
+                        __builtin_memcpy(v, &x_val[i], 16);
+#pragma unroll
+                        for (int e = 0; e < VX; ++e) reinterpret_cast<In*>(hb)[x_dst[i] + e] = v[e];
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < HE; ++i) {
+                const int e = tid + NT * i;
+                const int col = e % WP;
+                const int slot = (e / WP) % SL;
+                const int cl = e / (WP * SL);
+                reinterpret_cast<In*>(hb)[cl * PLANE + slot * WP + col] = h_val[i];
+            }
         }
         unsigned char* bb = hb + HALO_BYTES;
         if constexpr (DG) {
@@ -427,14 +490,32 @@ static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStrea
         if (dgrad || p.wcb % CB != 0 || p.wkb % VK != 0 || p.K % p.wkb != 0 || p.C % p.wcb != 0 ||
             (uintptr_t)p.w % 16 != 0)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, true, WPE>),
-                           grid, dim3(256 * KS), 0, stream, p);
+        hipLaunchKernelGGL(
+            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, true, WPE, false>), grid,
+            dim3(256 * KS), 0, stream, p);
+        return hipGetLastError();
+    }
+    // 16-byte row segments of x: unit column stride, W and x's strides
+    // multiples of the segment, x aligned (no segment reaches past a row)
+    constexpr int VX = 16 / (int)sizeof(typename Pol::In);
+    const bool xr = p.div_xcb.d == kOneBlock && p.sxw == 1 && (uintptr_t)p.x % 16 == 0 && p.W % VX == 0 &&
+                    p.sxh % VX == 0 && p.sxc % VX == 0 && p.sxn % VX == 0;
+    if (dgrad && xr) {
+        hipLaunchKernelGGL(
+            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, true, false, WPE, true>), grid,
+            dim3(256 * KS), 0, stream, p);
     } else if (dgrad) {
-        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, true, false, WPE>),
-                           grid, dim3(256 * KS), 0, stream, p);
+        hipLaunchKernelGGL(
+            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, true, false, WPE, false>), grid,
+            dim3(256 * KS), 0, stream, p);
+    } else if (xr) {
+        hipLaunchKernelGGL(
+            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, false, WPE, true>), grid,
+            dim3(256 * KS), 0, stream, p);
     } else {
-        hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, false, WPE>),
-                           grid, dim3(256 * KS), 0, stream, p);
+        hipLaunchKernelGGL(
+            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, false, WPE, false>), grid,
+            dim3(256 * KS), 0, stream, p);
     }
     return hipGetLastError();
 }
