@@ -52,13 +52,18 @@ namespace miconv {
 // tiles: 603 -> 520 us; AlexNet conv2-conv4 and the fp64 128 x 64 tiles
 // 1-2% faster); a cap would hurt the instances that run three.
 //
-// XR: x rows with unit column stride, 16-byte aligned, W a multiple of VX =
-// 16 / sizeof(element): the halo moves as 16-byte loads of VX consecutive
-// pixels of one (channel, slot) row, stored element by element at their
-// padded columns; pixels outside the plane (padding columns, rows outside x,
-// slots past the tile) are never written -- the halo starts zeroed.
+// XR: x rows with unit column stride, 16-byte aligned, whole VX-pixel
+// segments inside every row's storage (VX = 16 / sizeof(element): W a
+// multiple of VX, or a row pitch reaching the last segment's end): the halo
+// moves as 16-byte loads of VX consecutive pixels of one (channel, slot)
+// row, stored at their padded columns; pixels outside the plane (padding
+// columns, pixels past W, rows outside x, slots past the tile) are never
+// written -- the halo starts zeroed.  XR = 1: W a multiple of VX (whole
+// segments only).  XR = 2: a padded row pitch; the tensor's last row ends
+// x's storage, so a segment reaching past W there is read pixel by pixel
+// (the forward pass only: on the data gradient's dy it measured slower).
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS,
-          bool DG, bool WB, int WPE, bool XR>
+          bool DG, bool WB, int WPE, int XR>
 __global__ void __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(WPE)))
 conv_fwd_halo_kernel(const ConvParams p)
 {
@@ -172,8 +177,8 @@ conv_fwd_halo_kernel(const ConvParams p)
     }
 
     // XR: unit u = (channel, slot, segment): pixels w0 .. w0 + VX - 1, w0 = VX * segment
-    int x_off[XR ? HXT : 1], x_dst[XR ? HXT : 1];
-    uint32_t x_ok = 0;
+    int x_off[XR ? HXT : 1], x_dst[XR ? HXT : 1], x_np[XR ? HXT : 1];
+    uint32_t x_ok = 0, x_last = 0;
     if constexpr (XR) {
 #pragma unroll
         for (int i = 0; i < HXT; ++i) {
@@ -188,7 +193,11 @@ conv_fwd_halo_kernel(const ConvParams p)
             const bool ok = u < HUX && slot < nslots && (int)n < p.N && h >= 0 && h < p.H && w0 < p.W;
             x_off[i] = ok ? (int)n * p.sxn + cl * p.sxc + h * p.sxh + w0 : 0;
             x_dst[i] = cl * PLANE + slot * WP + w0 + p.pad_left;     // element index of pixel w0
+            x_np[i] = ok ? min(VX, p.W - w0) : 0;                      // pixels inside the row
             x_ok |= (ok ? 1u : 0u) << i;
+            // the last row: image N-1, row H-1, channel C-1 (the last chunk's channel CB-1)
+            const bool last = ok && (int)n == p.N - 1 && h == p.H - 1 && cl == CB - 1 && w0 + VX > p.W;
+            x_last |= (last ? 1u : 0u) << i;
         }
     }
     u32x4 x_val[XR ? HXT : 1];
@@ -251,7 +260,16 @@ conv_fwd_halo_kernel(const ConvParams p)
         const int xo = blk_off(p.div_xcb, p.sxcb, p.sxc, c0);
         if constexpr (XR) {
 #pragma unroll
-            for (int i = 0; i < HXT; ++i) x_val[i] = *reinterpret_cast<const u32x4*>(x + x_off[i] + xo);
+            for (int i = 0; i < HXT; ++i) {
+                const In* src = x + x_off[i] + xo;
+                if (XR == 2 && ((x_last >> i) & 1) && c0 + CB == p.C) {
+                    In v[VX] = {};
+                    for (int e = 0; e < x_np[i]; ++e) v[e] = src[e];
+                    __builtin_memcpy(&x_val[i], v, 16);
+                } else {
+                    x_val[i] = *reinterpret_cast<const u32x4*>(src);
+                }
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < HE; ++i) h_val[i] = ((h_ok >> i) & 1) ? load_elem(x + h_off[i] + xo) : In(0);
@@ -293,13 +311,14 @@ conv_fwd_halo_kernel(const ConvParams p)
 #pragma unroll
             for (int i = 0; i < HXT; ++i) {
                 if ((x_ok >> i) & 1) {
-                    if (whole) {
+                    if (whole && (XR == 1 || x_np[i] == VX)) {
                         *reinterpret_cast<u32x4*>(hb + x_dst[i] * ES) = x_val[i];
                     } else {
                         In v[VX];
                         __builtin_memcpy(v, &x_val[i], 16);
 #pragma unroll
-                        for (int e = 0; e < VX; ++e) reinterpret_cast<In*>(hb)[x_dst[i] + e] = v[e];
+                        for (int e = 0; e < VX; ++e)
+                            if (XR == 1 || e < x_np[i]) reinterpret_cast<In*>(hb)[x_dst[i] + e] = v[e];
                     }
                 }
             }
@@ -491,32 +510,36 @@ static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStrea
             (uintptr_t)p.w % 16 != 0)
             return hipErrorInvalidValue;
         hipLaunchKernelGGL(
-            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, true, WPE, false>), grid,
+            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, true, WPE, 0>), grid,
             dim3(256 * KS), 0, stream, p);
         return hipGetLastError();
     }
-    // 16-byte row segments of x: unit column stride, W and x's strides
-    // multiples of the segment, x aligned (no segment reaches past a row)
+    // 16-byte row segments of x: unit column stride, x's strides multiples of
+    // the segment, x aligned; whole segments (W a multiple of one), or in the
+    // forward pass every row's storage holding its last segment whole (a
+    // padded row pitch) with NCHW nesting, so that only the tensor's last row
+    // ends x's storage
     constexpr int VX = 16 / (int)sizeof(typename Pol::In);
-    const bool xr = p.div_xcb.d == kOneBlock && p.sxw == 1 && (uintptr_t)p.x % 16 == 0 && p.W % VX == 0 &&
-                    p.sxh % VX == 0 && p.sxc % VX == 0 && p.sxn % VX == 0;
-    if (dgrad && xr) {
-        hipLaunchKernelGGL(
-            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, true, false, WPE, true>), grid,
-            dim3(256 * KS), 0, stream, p);
-    } else if (dgrad) {
-        hipLaunchKernelGGL(
-            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, true, false, WPE, false>), grid,
-            dim3(256 * KS), 0, stream, p);
-    } else if (xr) {
-        hipLaunchKernelGGL(
-            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, false, WPE, true>), grid,
-            dim3(256 * KS), 0, stream, p);
-    } else {
-        hipLaunchKernelGGL(
-            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, false, WPE, false>), grid,
-            dim3(256 * KS), 0, stream, p);
-    }
+    const bool xv = p.div_xcb.d == kOneBlock && p.sxw == 1 && (uintptr_t)p.x % 16 == 0 && p.sxh % VX == 0 &&
+                    p.sxc % VX == 0 && p.sxn % VX == 0;
+    const bool xr1 = xv && p.W % VX == 0;
+    const bool xr2 = xv && !xr1 && !dgrad && p.sxh >= (p.W + VX - 1) / VX * VX &&
+                     (int64_t)p.sxc >= (int64_t)p.sxh * p.H && (int64_t)p.sxn >= (int64_t)p.sxc * p.C;
+#define MICONV_HALO_LAUNCH(DGV, XRV)                                                                              \
+    hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, DGV, false, WPE, \
+                                             XRV>),                                                               \
+                       grid, dim3(256 * KS), 0, stream, p)
+    if (dgrad && xr1)
+        MICONV_HALO_LAUNCH(true, 1);
+    else if (dgrad)
+        MICONV_HALO_LAUNCH(true, 0);
+    else if (xr1)
+        MICONV_HALO_LAUNCH(false, 1);
+    else if (xr2)
+        MICONV_HALO_LAUNCH(false, 2);
+    else
+        MICONV_HALO_LAUNCH(false, 0);
+#undef MICONV_HALO_LAUNCH
     return hipGetLastError();
 }
 
