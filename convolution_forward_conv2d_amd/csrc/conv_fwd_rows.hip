@@ -275,6 +275,31 @@ conv_fwd_rows_kernel(const ConvParams p)
                                 wave, lane);
 }
 
+namespace {
+constexpr int kRowsBufWord3 = 0x00020000;         // raw 32-bit buffer, range-checked per dword
+constexpr int kRowsOutside = (int)0x80000000u;    // an offset past any buffer (host: x, w < 2^31 bytes)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRowsBufWord3);
+}
+template <class T>
+__device__ __forceinline__ T rows_load(__amdgpu_buffer_rsrc_t r, int voff, int soff = 0)
+{
+    if constexpr (std::is_same<T, float4>::value) {
+        typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        return float4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+    } else if constexpr (std::is_same<T, float2>::value) {
+        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        return float2{__uint_as_float(v[0]), __uint_as_float(v[1])};
+    } else {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+}
+}  // namespace
+
 // ------------------------------------------------------------------ one input channel
 //
 // The same streaming for one to four input channels (the speech network's
@@ -292,8 +317,19 @@ conv_fwd_rows_kernel(const ConvParams p)
 // workgroups that 109 registers allow).  Measured and not kept: the next
 // chunk's loads and LDS stores spread over the MFMA steps (3% slower), two
 // filter rows per chunk (6-12% slower), the row stored by column phase so
-// that stride-v operand reads hit distinct banks (6% slower: the loader
-// then gathers x at stride v).
+// that stride-v operand reads hit distinct banks (6% slower with the loader
+// gathering x at stride v; 8% slower with coalesced loads scattered into the
+// phases, Overfeat layer 1 342 -> 369 us, although the LDS bank conflicts
+// fell to zero and the LDS-active cycles by half), one tap per step on
+// v_mfma_f32_32x32x1_2b_f32 (two 32-row blocks per instruction: 11 MFMAs a
+// filter row instead of 12, no padding tap; 343 -> 345 us, speech layer 1
+// 274 -> 282 us), 96 filters a tile (256 x 96 at three waves per SIMD: 353
+// us; 128 x 96 at four or five: 381-388 us).  Neither the operand reads nor
+// the MFMA count bounds this kernel; its vector-ALU work does: the loads
+// through range-checked buffer descriptors (one add and one compare per unit
+// and chunk, no store masks, no division per chunk) halved the loop's VALU
+// and SALU instructions and took Overfeat layer 1 343 -> 284 us, speech
+// layer 1 274 -> 246 us.
 //
 // XV: consecutive columns per halo load, as for the multi-channel kernel
 // (speech layer 1: XV = 4).
@@ -350,10 +386,17 @@ conv_fwd_rows1_kernel(const ConvParams p)
     const int row0 = out_row(m0);
     const int nrows = p.N * p.P;
 
+    // Loads go through range-checked buffer descriptors: a unit outside x (or
+    // a filter outside w) reads at an offset past the buffer and gets zeros,
+    // so the stores need no masks and a chunk's offsets are one add each.
+    const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + (int64_t)(p.C - 1) * p.sxc + (int64_t)(p.H - 1) * p.sxh +
+                            (int64_t)(p.W - 1) * p.sxw + 1;
+    const __amdgpu_buffer_rsrc_t xr = rows_rsrc(p.x, (int)(4 * x_elems));
+    const __amdgpu_buffer_rsrc_t wr = rows_rsrc(p.w, 4 * p.K * p.Kred);
+
     // ---- halo loader: unit e = (filter row j, slot, XV columns), columns fastest
-    int h_base[NH];
-    int h_row[NH];                                   // input row of filter row j at chunk row 0
-    uint32_t h_ok = 0;
+    uint32_t h_voff[NH];                             // byte offset at channel 0, filter row 0
+    int h_row[NH];                                   // input row of filter row j at chunk row 0 (far negative: no unit)
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
         const int e = tid + NT * i;
@@ -367,13 +410,13 @@ conv_fwd_rows1_kernel(const ConvParams p)
         const int pp = orow - n * p.P;
         const int wc = col - p.pad_left;
         const bool ok = e < HE && orow < nrows && (unsigned)wc < (unsigned)p.W;
-        h_row[i] = pp * p.u - p.pad_top + j;
-        h_base[i] = ok ? n * p.sxn + wc * p.sxw : 0;     // channel added per chunk
-        h_ok |= (ok ? 1u : 0u) << i;
+        const int hr = pp * p.u - p.pad_top + j;
+        h_row[i] = ok ? hr : -(1 << 30);
+        h_voff[i] = 4u * (uint32_t)(n * p.sxn + wc * p.sxw + hr * p.sxh);   // (wraps; valid once a chunk's row is added)
     }
     // ---- slab loader: element e = (filter row j, tap s, filter k), k fastest
-    int s_off[NS];
-    uint32_t s_ok0 = 0;
+    int s_voff[NS];
+    int s_row[NS];                                   // filter row j of the element
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int e = tid + NT * i;
@@ -382,51 +425,39 @@ conv_fwd_rows1_kernel(const ConvParams p)
         const int ss = rem / TN;
         const int k = rem - ss * TN;
         const bool ok = e < SLAB && ss < S && n0 + k < p.K;
-        s_off[i] = ok ? (n0 + k) * p.Kred + j * S + ss : 0;   // packed K,C,R,S; (c, r0) added per chunk
-        s_ok0 |= (ok ? 1u : 0u) << i;
+        s_voff[i] = ok ? 4 * ((n0 + k) * p.Kred + j * S + ss) : kRowsOutside;   // packed K,C,R,S
+        s_row[i] = j;
     }
 
     using HV = typename std::conditional<XV == 4, float4, typename std::conditional<XV == 2, float2, float>::type>::type;
     HV hv[NH];
     float sv[NS];
-    uint32_t hv_ok = 0, sv_ok = 0;
-    const int nrb = (p.R + RB - 1) / RB;
-    const int nch = p.C * nrb;                       // chunk = (filter row block, channel), channel fastest
-    auto load_chunk = [&](int ch) {
-        const int rb = ch / p.C;
-        const int c = ch - rb * p.C;
-        const int r0 = rb * RB;
-        uint32_t m = 0;
+    // chunk = (filter row block, channel), channel fastest
+    auto load_chunk = [&](int c, int r0) {
+        const uint32_t chunk_off = 4u * (uint32_t)(c * p.sxc + r0 * p.sxh);
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
-            const int h = h_row[i] + r0;
-            const bool ok = ((h_ok >> i) & 1u) && (unsigned)h < (unsigned)p.H;
-            hv[i] = *reinterpret_cast<const HV*>(x + (ok ? h_base[i] + c * p.sxc + h * p.sxh : 0));
-            m |= (ok ? 1u : 0u) << i;
+            const bool ok = (unsigned)(h_row[i] + r0) < (unsigned)p.H;
+            hv[i] = rows_load<HV>(xr, ok ? (int)(h_voff[i] + chunk_off) : kRowsOutside);
         }
-        hv_ok = m;
-        uint32_t ms = 0;
+        const int s_chunk = 4 * (c * p.R + r0) * S;
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            const int e = tid + NT * i;
-            const int j = e / (SP * TN);
-            const bool ok = ((s_ok0 >> i) & 1u) && r0 + j < p.R;
-            sv[i] = w[ok ? s_off[i] + (c * p.R + r0) * S : 0];
-            ms |= (ok ? 1u : 0u) << i;
+            const int vo = RB == 1 || r0 + s_row[i] < p.R ? s_voff[i] : kRowsOutside;
+            sv[i] = rows_load<float>(wr, vo, s_chunk);
         }
-        sv_ok = ms;
     };
     auto store_chunk = [&](int buf) {
         float* dst = smem + buf * BUF;
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
             const int e = tid + NT * i;
-            if (HE % NT == 0 || e < HE) reinterpret_cast<HV*>(dst)[e] = (hv_ok >> i) & 1u ? hv[i] : HV{};
+            if (HE % NT == 0 || e < HE) reinterpret_cast<HV*>(dst)[e] = hv[i];
         }
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             const int e = tid + NT * i;
-            if (SLAB % NT == 0 || e < SLAB) dst[HALO + e] = (sv_ok >> i) & 1u ? sv[i] : 0.0f;
+            if (SLAB % NT == 0 || e < SLAB) dst[HALO + e] = sv[i];
         }
     };
 
@@ -458,13 +489,19 @@ conv_fwd_rows1_kernel(const ConvParams p)
     auto a_off = [](int t) { const int j = t / (SP / G), sp = t % (SP / G); return j * ROWP + G * sp; };
     auto b_off = [](int t) { const int j = t / (SP / G), sp = t % (SP / G); return (j * SP + G * sp) * TN; };
 
-    load_chunk(0);
+    const int nch = p.C * ((p.R + RB - 1) / RB);
+    int lc = 0, lr0 = 0;                             // the chunk last loaded
+    load_chunk(lc, lr0);
     store_chunk(0);
     __syncthreads();
     for (int ch = 0; ch < nch; ++ch) {
         const int cur = ch & 1;
         const bool more = ch + 1 < nch;
-        load_chunk(more ? ch + 1 : ch);
+        if (more && ++lc == p.C) {
+            lc = 0;
+            lr0 += RB;
+        }
+        load_chunk(lc, lr0);
         __builtin_amdgcn_sched_barrier(0);
         const float* buf = smem + cur * BUF;
         float av[FM], bv[FN];
@@ -873,8 +910,14 @@ template <int NSL, int WP>
 static bool rows1_variant_fits(const ConvParams& p)
 {
     const int spanned = (kRows1TM - 1 + p.Q - 1) / p.Q + 1;    // output rows a tile can touch
+    // x and w each under 2^31 bytes: their buffer descriptors' ranges, and
+    // an offset of 2^31 lies past both
+    const int64_t x_bytes = 4 * ((int64_t)(p.N - 1) * p.sxn + (int64_t)(p.C - 1) * p.sxc +
+                                 (int64_t)(p.H - 1) * p.sxh + (int64_t)(p.W - 1) * p.sxw + 1);
+    const int64_t w_bytes = 4 * (int64_t)p.K * p.Kred;
     return p.C >= 1 && p.C <= 4 && p.S == kRows1S && spanned <= NSL &&
-           (int64_t)(p.Q - 1) * p.v + kRows1S + 1 <= WP;
+           (int64_t)(p.Q - 1) * p.v + kRows1S + 1 <= WP && x_bytes < ((int64_t)1 << 31) &&
+           w_bytes < ((int64_t)1 << 31);
 }
 
 template <int NSL, int WP>

@@ -129,6 +129,9 @@ FWD_SHAPES = SMALL_SHAPES + [
     dict(name="rows1n6_c2", N=2, C=2, Hh=20, Ww=60, K=40, R=9, S=11, stride=(1, 1), pads=(2, 3, 4, 1)),
     # odd stride 3
     dict(name="rows1n6_c3_s3", N=2, C=3, Hh=40, Ww=160, K=20, R=5, S=11, stride=(3, 3), pads=(1, 1, 2, 2)),
+    # stride 4 with padding on three sides, an odd output row width (Q = 53), a ragged last
+    # tile and filter tile
+    dict(name="rows1n6_s4_pad", N=3, C=2, Hh=45, Ww=217, K=40, R=11, S=11, stride=(4, 4), pads=(2, 0, 1, 2)),
 ]
 
 
