@@ -43,6 +43,45 @@
 
 namespace miconv {
 
+namespace {
+constexpr int kRowsBufWord3 = 0x00020000;         // raw 32-bit buffer, range-checked per dword
+constexpr int kRowsOutside = (int)0x80000000u;    // an offset past any buffer (host: x, w < 2^31 bytes)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRowsBufWord3);
+}
+template <class T>
+__device__ __forceinline__ T rows_load(__amdgpu_buffer_rsrc_t r, int voff, int soff = 0)
+{
+    if constexpr (std::is_same<T, float4>::value) {
+        typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        return float4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+    } else if constexpr (std::is_same<T, float2>::value) {
+        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        return float2{__uint_as_float(v[0]), __uint_as_float(v[1])};
+    } else {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+}
+// elements x spans: its last element's offset + 1 (every index at its
+// largest; blocked x: the last channel lies in the last block)
+__host__ __device__ __forceinline__ int64_t rows_x_elems(const ConvParams& p)
+{
+    return (int64_t)(p.N - 1) * p.sxn + blk_off(p.div_xcb, p.sxcb, p.sxc, p.C - 1) + (int64_t)(p.H - 1) * p.sxh +
+           (int64_t)(p.W - 1) * p.sxw + 1;
+}
+
+// x and w within the range a buffer descriptor checks (an offset of 2^31
+// then lies past both)
+static bool rows_buffers_fit(const ConvParams& p)
+{
+    return 4 * rows_x_elems(p) < ((int64_t)1 << 31) && 4 * (int64_t)p.K * p.Kred < ((int64_t)1 << 31);
+}
+}  // namespace
+
 // XB: x channel-blocked ([N][C/cb][H][W][cb], cb a multiple of CB, 16-byte
 // aligned): a chunk's CB = 4 channels lie side by side, so the halo moves as
 // one 16-byte load per (slot, column).  WB: blocked filters
@@ -111,11 +150,17 @@ conv_fwd_rows_kernel(const ConvParams p)
     const int row0 = out_row(m0);
     const int nrows = p.N * p.P;
 
+    // Loads go through range-checked buffer descriptors (as in the one-channel
+    // kernel below): a unit outside x, or a filter past K, reads at an offset
+    // past the buffer and gets zeros (speech layer 2: 2148 -> 1897 us against
+    // masked global loads).
+    const int64_t x_elems = rows_x_elems(p);
+    const __amdgpu_buffer_rsrc_t xr = rows_rsrc(p.x, (int)(4 * x_elems));
+
     // ---- halo loader: unit e = (channel, slot, XV columns), columns fastest
     // (XB: e = (slot, column) carrying the chunk's four channels)
-    int h_base[NH];                                  // x offset of (n, slot row's p*u - pad_top, column), channel 0
-    int h_row[NH];                                   // input row p*u - pad_top (r added per chunk)
-    uint32_t h_ok = 0;
+    uint32_t h_voff[NH];                             // byte offset of (n, channel, row p*u - pad_top, column)
+    int h_row[NH];                                   // input row p*u - pad_top (far negative: no unit)
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
         const int e = tid + NT * i;
@@ -129,9 +174,9 @@ conv_fwd_rows_kernel(const ConvParams p)
         const int pp = orow - n * p.P;
         const int wc = col - p.pad_left;
         const bool ok = e < HE && orow < nrows && (unsigned)wc < (unsigned)p.W;
-        h_row[i] = pp * p.u - p.pad_top;
-        h_base[i] = ok ? n * p.sxn + cl * p.sxc + wc * p.sxw : 0;
-        h_ok |= (ok ? 1u : 0u) << i;
+        const int hr = pp * p.u - p.pad_top;
+        h_row[i] = ok ? hr : -(1 << 30);
+        h_voff[i] = 4u * (uint32_t)(n * p.sxn + cl * p.sxc + wc * p.sxw + hr * p.sxh);   // (wraps; valid with a row)
     }
     // ---- slab loader: thread -> (filter k, channel c, taps sh*SH ... sh*SH + SH - 1) of row r
     const int sk = tid % TN;
@@ -141,29 +186,25 @@ conv_fwd_rows_kernel(const ConvParams p)
     // packed KCRS: filter k's row of C*R*S; blocked: its block row and place in the block
     const int kk = s_ok ? n0 + sk : 0;
     const int s_base = WB ? (kk / p.wkb) * (p.C / p.wcb) * (p.R * S * p.wcb * p.wkb) + kk % p.wkb : kk * p.Kred;
+    const __amdgpu_buffer_rsrc_t wr = rows_rsrc(p.w, 4 * p.K * p.Kred);
+    // packed: byte offset of tap 0 of (filter, channel sc, row 0); a chunk adds (c0 R + r) S
+    const int s_voff = s_ok ? 4 * (s_base + sc * p.R * S) : kRowsOutside;
 
     using HV = typename std::conditional<
         XB || XV == 4, float4, typename std::conditional<XV == 2, float2, float>::type>::type;
     HV hv[NH];
-    uint32_t hv_ok = 0;                              // validity of the chunk in registers
     float sv[SH];
     const int ncb = p.C / CB;
     const int nch = ncb * p.R;
-    auto load_chunk = [&](int ch) {
-        const int r = ch / ncb;
-        const int c0 = (ch - r * ncb) * CB;
+    auto load_chunk = [&](int c0, int r) {
         // x offset of the chunk's first channel (blocked x: the chunk lies in one block)
         const int xo = XB ? blk_off(p.div_xcb, p.sxcb, p.sxc, c0) : c0 * p.sxc;
-        // unconditional loads at a valid address; zeros are chosen at the store
-        uint32_t m = 0;
+        const uint32_t chunk_off = 4u * (uint32_t)(xo + r * p.sxh);
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
-            const int h = h_row[i] + r;
-            const bool ok = ((h_ok >> i) & 1u) && (unsigned)h < (unsigned)p.H;
-            hv[i] = *reinterpret_cast<const HV*>(x + (ok ? h_base[i] + xo + h * p.sxh : 0));
-            m |= (ok ? 1u : 0u) << i;
+            const bool ok = (unsigned)(h_row[i] + r) < (unsigned)p.H;
+            hv[i] = rows_load<HV>(xr, ok ? (int)(h_voff[i] + chunk_off) : kRowsOutside);
         }
-        hv_ok = m;
         if (WB) {
             // the channel's block once per chunk, then the taps at a stride of cb*kb
             const int c = c0 + sc;
@@ -172,9 +213,9 @@ conv_fwd_rows_kernel(const ConvParams p)
 #pragma unroll
             for (int i = 0; i < SH; ++i) sv[i] = w[wo + min(sh * SH + i, S - 1) * p.wcb * p.wkb];
         } else {
-            const int fo = s_base + ((c0 + sc) * p.R + r) * S;
+            const int s_chunk = 4 * (c0 * p.R + r) * S;
 #pragma unroll
-            for (int i = 0; i < SH; ++i) sv[i] = w[fo + min(sh * SH + i, S - 1)];
+            for (int i = 0; i < SH; ++i) sv[i] = rows_load<float>(wr, s_voff + 4 * min(sh * SH + i, S - 1), s_chunk);
         }
     };
     auto store_chunk = [&](int buf) {
@@ -184,21 +225,20 @@ conv_fwd_rows_kernel(const ConvParams p)
             const int e = tid + NT * i;
             if constexpr (XB) {
                 if (PLANE % NT == 0 || e < PLANE) {
-                    const bool ok = (hv_ok >> i) & 1u;
                     const float4 v = hv[i];
-                    dst[e] = ok ? v.x : 0.0f;
-                    dst[PLANE + e] = ok ? v.y : 0.0f;
-                    dst[2 * PLANE + e] = ok ? v.z : 0.0f;
-                    dst[3 * PLANE + e] = ok ? v.w : 0.0f;
+                    dst[e] = v.x;
+                    dst[PLANE + e] = v.y;
+                    dst[2 * PLANE + e] = v.z;
+                    dst[3 * PLANE + e] = v.w;
                 }
             } else {
-                if (HE % NT == 0 || e < HE) reinterpret_cast<HV*>(dst)[e] = (hv_ok >> i) & 1u ? hv[i] : HV{};
+                if (HE % NT == 0 || e < HE) reinterpret_cast<HV*>(dst)[e] = hv[i];
             }
         }
 #pragma unroll
         for (int i = 0; i < SH; ++i) {
             const int s = sh * SH + i;
-            if (SPLIT * SH == S || s < S) dst[HALO + (s * CB + sc) * TN + sk] = s_ok ? sv[i] : 0.0f;
+            if (SPLIT * SH == S || s < S) dst[HALO + (s * CB + sc) * TN + sk] = WB && !s_ok ? 0.0f : sv[i];
         }
     };
 
@@ -232,13 +272,18 @@ conv_fwd_rows_kernel(const ConvParams p)
     auto a_off = [](int t) { const int s = t / (CB / G), cp = t % (CB / G); return G * cp * PLANE + s; };
     auto b_off = [](int t) { const int s = t / (CB / G), cp = t % (CB / G); return (s * CB + G * cp) * TN; };
 
-    load_chunk(0);
+    int lc0 = 0, lr = 0;                             // the chunk last loaded: channel block, filter row
+    load_chunk(lc0, lr);
     store_chunk(0);
     __syncthreads();
     for (int ch = 0; ch < nch; ++ch) {
         const int cur = ch & 1;
         const bool more = ch + 1 < nch;
-        load_chunk(more ? ch + 1 : ch);
+        if (more && (lc0 += CB) == p.C) {
+            lc0 = 0;
+            ++lr;
+        }
+        load_chunk(lc0, lr);
         __builtin_amdgcn_sched_barrier(0);
         const float* buf = smem + cur * BUF;
         float a[FM], b[FN];
@@ -274,31 +319,6 @@ conv_fwd_rows_kernel(const ConvParams p)
     store_acc_tile<Pol, FM, FN>(p, reinterpret_cast<unsigned char*>(smem), acc, m0 + wm * WM, n0 + wn * WN, m_end,
                                 wave, lane);
 }
-
-namespace {
-constexpr int kRowsBufWord3 = 0x00020000;         // raw 32-bit buffer, range-checked per dword
-constexpr int kRowsOutside = (int)0x80000000u;    // an offset past any buffer (host: x, w < 2^31 bytes)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRowsBufWord3);
-}
-template <class T>
-__device__ __forceinline__ T rows_load(__amdgpu_buffer_rsrc_t r, int voff, int soff = 0)
-{
-    if constexpr (std::is_same<T, float4>::value) {
-        typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-        return float4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
-    } else if constexpr (std::is_same<T, float2>::value) {
-        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-        return float2{__uint_as_float(v[0]), __uint_as_float(v[1])};
-    } else {
-        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-    }
-}
-}  // namespace
 
 // ------------------------------------------------------------------ one input channel
 //
@@ -389,8 +409,7 @@ conv_fwd_rows1_kernel(const ConvParams p)
     // Loads go through range-checked buffer descriptors: a unit outside x (or
     // a filter outside w) reads at an offset past the buffer and gets zeros,
     // so the stores need no masks and a chunk's offsets are one add each.
-    const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + (int64_t)(p.C - 1) * p.sxc + (int64_t)(p.H - 1) * p.sxh +
-                            (int64_t)(p.W - 1) * p.sxw + 1;
+    const int64_t x_elems = rows_x_elems(p);
     const __amdgpu_buffer_rsrc_t xr = rows_rsrc(p.x, (int)(4 * x_elems));
     const __amdgpu_buffer_rsrc_t wr = rows_rsrc(p.w, 4 * p.K * p.Kred);
 
@@ -848,7 +867,7 @@ template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int 
 static bool rows_variant_fits(const ConvParams& p)
 {
     static_assert(NSL >= 2, "a tile within two output rows");
-    return p.S == S && p.C % CB == 0 && p.Q >= TM && (int64_t)(p.Q - 1) * p.v + S <= WP;
+    return p.S == S && p.C % CB == 0 && p.Q >= TM && (int64_t)(p.Q - 1) * p.v + S <= WP && rows_buffers_fit(p);
 }
 
 template <int TM, int TN, int WAVES_M, int WAVES_N, int S, int CB, int NSL, int WP>
@@ -910,14 +929,8 @@ template <int NSL, int WP>
 static bool rows1_variant_fits(const ConvParams& p)
 {
     const int spanned = (kRows1TM - 1 + p.Q - 1) / p.Q + 1;    // output rows a tile can touch
-    // x and w each under 2^31 bytes: their buffer descriptors' ranges, and
-    // an offset of 2^31 lies past both
-    const int64_t x_bytes = 4 * ((int64_t)(p.N - 1) * p.sxn + (int64_t)(p.C - 1) * p.sxc +
-                                 (int64_t)(p.H - 1) * p.sxh + (int64_t)(p.W - 1) * p.sxw + 1);
-    const int64_t w_bytes = 4 * (int64_t)p.K * p.Kred;
     return p.C >= 1 && p.C <= 4 && p.S == kRows1S && spanned <= NSL &&
-           (int64_t)(p.Q - 1) * p.v + kRows1S + 1 <= WP && x_bytes < ((int64_t)1 << 31) &&
-           w_bytes < ((int64_t)1 << 31);
+           (int64_t)(p.Q - 1) * p.v + kRows1S + 1 <= WP && rows_buffers_fit(p);
 }
 
 template <int NSL, int WP>
