@@ -1066,6 +1066,9 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
     // zeros at offset 2^31 (range-checked buffer loads)
     const int64_t es = (int64_t)dtype_size(xd->dtype);
     const bool split_fits = extent(*xd) * es < INT32_MAX && extent(*dyd) * es < INT32_MAX;
+    // the halo kernels' buffer loads: x and dy under 2^30 bytes (an offset of
+    // 2^30 lies past both, and three such offsets still fit 32 bits)
+    const bool halo_bufs_fit = extent(*xd) * es < (int64_t(1) << 30) && extent(*dyd) * es < (int64_t(1) << 30);
     const bool unit_q = xd->sw == 1 && dyd->sw == 1;
     double best = 0;
     bool found = false;
@@ -1076,7 +1079,7 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
         if (wc.kind == WgKind::HALO)
             // (r = 0: any filter height and row stride)
             ok = (wc.r == 0 || (wc.r == wd->r && cd->u == 1)) && wc.s == wd->s && cd->v == 1 &&
-                 Q + wc.s - 1 <= wc.wph && (wc.qd == 0 || Q == wc.qd);
+                 Q + wc.s - 1 <= wc.wph && (wc.qd == 0 || Q == wc.qd) && halo_bufs_fit;
         else if (wc.kind == WgKind::SPLIT)
             ok = split_fits;
         else if (wc.kind == WgKind::ROWS)
