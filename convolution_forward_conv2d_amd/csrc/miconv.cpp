@@ -177,29 +177,29 @@ const WgCandidate kWg[] = {
     {{Variant::WG_F64_64x64, 64, 64, "wg_f64_64x64"}, DType::F64, WgKind::GATHER, 0, 0, 0, 93.0, 1},
     {{Variant::WG_BF16_128x128, 128, 128, "wg_bf16_128x128"}, DType::BF16, WgKind::GATHER, 0, 0, 0, 190.0, 1},
     {{Variant::WG_BF16_64x64, 64, 64, "wg_bf16_64x64"}, DType::BF16, WgKind::GATHER, 0, 0, 0, 75.0, 1},
-    {{Variant::WGH_F32_3x3_W16, 64, 64, "wgh_f32_3x3_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 34.0, 1},
-    {{Variant::WGH_F32_5x5_W24, 64, 64, "wgh_f32_5x5_w24_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 32.0, 1},
-    {{Variant::WGH_F32_5x5_W36, 64, 64, "wgh_f32_5x5_w36_64x64"}, DType::F32, WgKind::HALO, 5, 5, 36, 39.0, 1},
-    {{Variant::WGH_F32_3x3_W16_64x96, 64, 96, "wgh_f32_3x3_64x96"}, DType::F32, WgKind::HALO, 3, 3, 16, 44.0, 1},
-    {{Variant::WGH_F32X16_3x3_W16, 64, 64, "wgh_f32x16_3x3_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 33.0, 1},
-    {{Variant::WGH_F32X16_5x5_W24, 64, 64, "wgh_f32x16_5x5_w24_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 30.8, 1},
+    {{Variant::WGH_F32_3x3_W16, 64, 64, "wgh_f32_3x3_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 21.5, 1},
+    {{Variant::WGH_F32_5x5_W24, 64, 64, "wgh_f32_5x5_w24_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 22, 1},
+    {{Variant::WGH_F32_5x5_W36, 64, 64, "wgh_f32_5x5_w36_64x64"}, DType::F32, WgKind::HALO, 5, 5, 36, 23.7, 1},
+    {{Variant::WGH_F32_3x3_W16_64x96, 64, 96, "wgh_f32_3x3_64x96"}, DType::F32, WgKind::HALO, 3, 3, 16, 29.9, 1},
+    {{Variant::WGH_F32X16_3x3_W16, 64, 64, "wgh_f32x16_3x3_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 21.6, 1},
+    {{Variant::WGH_F32X16_5x5_W24, 64, 64, "wgh_f32x16_5x5_w24_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 22.4, 1},
     {{Variant::WGH_F64_3x3_W16, 64, 64, "wgh_f64_3x3_64x64"}, DType::F64, WgKind::HALO, 3, 3, 16, 52.0, 1},
-    {{Variant::WGH_F32_3x3_Q12_64x96, 64, 96, "wgh_f32_3x3_q12_64x96"}, DType::F32, WgKind::HALO, 3, 3, 16, 30.5, 1, 12},
-    {{Variant::WGH_F32_3x3_Q13, 64, 64, "wgh_f32_3x3_q13_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 27.3, 1, 13},
-    {{Variant::WGH_F32X16_5x5_Q20, 64, 64, "wgh_f32x16_5x5_q20_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 25.2, 1, 20},
-    {{Variant::WGH_F32X16_5x5_Q27, 64, 64, "wgh_f32x16_5x5_q27_64x64"}, DType::F32, WgKind::HALO, 5, 5, 32, 29.6, 1, 27},
-    {{Variant::WGH_F32X16_5x5_Q20_64x48, 64, 48, "wgh_f32x16_5x5_q20_64x48"}, DType::F32, WgKind::HALO, 5, 5, 24, 19.9, 1, 20},
-    {{Variant::WGH_F32X16_5x5_Q27_64x48, 64, 48, "wgh_f32x16_5x5_q27_64x48"}, DType::F32, WgKind::HALO, 5, 5, 32, 23.4, 1, 27},
+    {{Variant::WGH_F32_3x3_Q12_64x96, 64, 96, "wgh_f32_3x3_q12_64x96"}, DType::F32, WgKind::HALO, 3, 3, 16, 25.1, 1, 12},
+    {{Variant::WGH_F32_3x3_Q13, 64, 64, "wgh_f32_3x3_q13_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 18, 1, 13},
+    {{Variant::WGH_F32X16_5x5_Q20, 64, 64, "wgh_f32x16_5x5_q20_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 19, 1, 20},
+    {{Variant::WGH_F32X16_5x5_Q27, 64, 64, "wgh_f32x16_5x5_q27_64x64"}, DType::F32, WgKind::HALO, 5, 5, 32, 20.2, 1, 27},
+    {{Variant::WGH_F32X16_5x5_Q20_64x48, 64, 48, "wgh_f32x16_5x5_q20_64x48"}, DType::F32, WgKind::HALO, 5, 5, 24, 16.8, 1, 20},
+    {{Variant::WGH_F32X16_5x5_Q27_64x48, 64, 48, "wgh_f32x16_5x5_q27_64x48"}, DType::F32, WgKind::HALO, 5, 5, 32, 19.96, 1, 27},
     // four groups of waves per tile (16 waves a CU, latency hidden within the
     // tile; measured on MI355X: AlexNet conv3/conv5 616 -> 576 us, conv4 952 -> 834)
-    {{Variant::WGH_F32_3x3_Q13_KS4, 64, 64, "wgh_f32_3x3_q13_64x64_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 25.5, 1, 13},
-    {{Variant::WGH_F32_3x3_W16_64x96_KS4, 64, 96, "wgh_f32_3x3_64x96_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 38.5, 1},
-    {{Variant::WGH_F32_3x3_Q12_64x96_KS4, 64, 96, "wgh_f32_3x3_q12_64x96_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 27.7, 1, 12},
-    {{Variant::WGH_F32X16_5x5_Q20_64x48_KS4, 64, 48, "wgh_f32x16_5x5_q20_64x48_ks4"}, DType::F32, WgKind::HALO, 5, 5, 24, 18.4, 1, 20},
-    {{Variant::WGH_F32X16_5x5_Q27_64x48_KS4, 64, 48, "wgh_f32x16_5x5_q27_64x48_ks4"}, DType::F32, WgKind::HALO, 5, 5, 32, 20.8, 1, 27},
+    {{Variant::WGH_F32_3x3_Q13_KS4, 64, 64, "wgh_f32_3x3_q13_64x64_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 19.2, 1, 13},
+    {{Variant::WGH_F32_3x3_W16_64x96_KS4, 64, 96, "wgh_f32_3x3_64x96_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 29.7, 1},
+    {{Variant::WGH_F32_3x3_Q12_64x96_KS4, 64, 96, "wgh_f32_3x3_q12_64x96_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 26.2, 1, 12},
+    {{Variant::WGH_F32X16_5x5_Q20_64x48_KS4, 64, 48, "wgh_f32x16_5x5_q20_64x48_ks4"}, DType::F32, WgKind::HALO, 5, 5, 24, 17.6, 1, 20},
+    {{Variant::WGH_F32X16_5x5_Q27_64x48_KS4, 64, 48, "wgh_f32x16_5x5_q27_64x48_ks4"}, DType::F32, WgKind::HALO, 5, 5, 32, 20.2, 1, 27},
     // r = 0: the (channel, filter row) pairs of the tile's columns staged, any
     // filter height and row stride (speech layer 2: 21 x 11 at stride (2, 1))
-    {{Variant::WGH_F32X16_PAIRS_S11_32x32, 32, 32, "wgh_f32x16_pairs_s11_32x32"}, DType::F32, WgKind::HALO, 0, 11, 368, 9.6, 1},
+    {{Variant::WGH_F32X16_PAIRS_S11_32x32, 32, 32, "wgh_f32x16_pairs_s11_32x32"}, DType::F32, WgKind::HALO, 0, 11, 368, 7.4, 1},
     {{Variant::WGH_F32X16_PAIRS_S11_32x32_KS4, 32, 32, "wgh_f32x16_pairs_s11_32x32_ks4"}, DType::F32, WgKind::HALO, 0, 11, 384, 8.0, 1},
     // fp64: four wave groups (AlexNet-shape conv3 / conv5 560 -> 519 us); 64x96
     // tiles where 64x64 would take a second round (conv4: 324 -> 216 tiles, 1110 -> 765 us)

@@ -470,12 +470,12 @@ def test_wgrad_kernel_choice_host_only():
     11-wide first layers, the split-reduction kernel where dw has few tiles or where its finer
     tiles round better (AlexNet conv2, the bf16 layers), the gather kernel for channels-last bf16."""
     want = {"tiny": "wgs_f32_8x16",
-            "alexnet_conv2": "wgh_f32x16_5x5_q27_64x48_ks4", "alexnet_conv3": "wgh_f32_3x3_q13_64x64_ks4",
-            "alexnet_conv4": "wgh_f32_3x3_64x96_ks4", "alexnet_conv5": "wgh_f32_3x3_q13_64x64_ks4",
-            "overfeat_l1": "wgr_f32_s11_v4", "overfeat_l2": "wgh_f32x16_5x5_q20_64x48_ks4",
-            "overfeat_l3": "wgh_f32_3x3_q12_64x96_ks4", "overfeat_l4": "wgh_f32_3x3_q12_64x96_ks4",
-            "overfeat_l5": "wgh_f32_3x3_q12_64x96_ks4",
-            "speech_l1": "wgr_f32_s11_v2", "speech_l2": "wgh_f32x16_pairs_s11_32x32_ks4"}
+            "alexnet_conv2": "wgh_f32x16_5x5_q27_64x48", "alexnet_conv3": "wgh_f32_3x3_q13_64x64",
+            "alexnet_conv4": "wgh_f32_3x3_64x96_ks4", "alexnet_conv5": "wgh_f32_3x3_q13_64x64",
+            "overfeat_l1": "wgr_f32_s11_v4", "overfeat_l2": "wgh_f32x16_5x5_q20_64x48",
+            "overfeat_l3": "wgh_f32_3x3_q12_64x96", "overfeat_l4": "wgh_f32_3x3_q12_64x96",
+            "overfeat_l5": "wgh_f32_3x3_q12_64x96",
+            "speech_l1": "wgr_f32_s11_v2", "speech_l2": "wgh_f32x16_pairs_s11_32x32"}
     for lay in workloads.ALL_LAYERS:
         name = _wgrad_name(lay)
         if lay.name in want:
