@@ -46,6 +46,42 @@
 
 namespace miconv {
 
+namespace {
+constexpr int kTapsBufWord3 = 0x00020000;         // raw 32-bit buffer, range-checked per dword
+constexpr int kTapsOutside = (int)0x80000000u;    // an offset past dy and F (both under 2^31 bytes)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t taps_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kTapsBufWord3);
+}
+template <class T>
+__device__ __forceinline__ T taps_load(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    if constexpr (std::is_same<T, float4>::value) {
+        typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        return float4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+    } else if constexpr (std::is_same<T, float2>::value) {
+        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        return float2{__uint_as_float(v[0]), __uint_as_float(v[1])};
+    } else {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+}
+
+// dy's and the filters' element counts
+__host__ __device__ __forceinline__ int64_t taps_dy_elems(const ConvParams& p)
+{
+    return (int64_t)(p.N - 1) * p.sxn + (int64_t)(p.K - 1) * p.sxc + (int64_t)(p.P - 1) * p.sxh +
+           (int64_t)(p.Q - 1) * p.sxw + 1;
+}
+__host__ __device__ __forceinline__ int64_t taps_f_elems(const ConvParams& p)
+{
+    return (int64_t)p.K * p.C * p.R * p.S;
+}
+}  // namespace
+
 // V: dy values per staging load (1, 2 or 4 consecutive columns; V > 1 needs
 // unit column stride, Q and the row, channel and image strides multiples of
 // V and dy's address aligned to V values)
@@ -96,15 +132,16 @@ conv_bwd_data_taps_kernel(const ConvParams p, int bands)
     if (P0 > P_hi) return;                        // uniform: the band lies past the phase's rows
     const int Ia = (p.R - a + p.u - 1) / p.u;     // taps i of the phase (a + u i < R)
 
-    const float* __restrict__ dy = static_cast<const float*>(p.x);
-    const float* __restrict__ F = static_cast<const float*>(p.w);
-    const float* __restrict__ dyn = dy + (int64_t)n * p.sxn;
+    // Loads go through range-checked buffer descriptors: a unit outside dy,
+    // or a tap past the filter, reads past the buffer and gets zero, so the
+    // stores and products need no masks; channel k is the scalar offset.
+    const __amdgpu_buffer_rsrc_t dr = taps_rsrc(p.x, 4 * taps_dy_elems(p));
+    const __amdgpu_buffer_rsrc_t fr = taps_rsrc(p.w, 4 * taps_f_elems(p));
 
     // ---- staging: unit e = (staged row j, columns q ... q + V - 1): dy row
     // P0 + TB - 1 - j (the host keeps Q a multiple of V: a unit lies in one row)
     using VT = typename std::conditional<V == 4, float4, typename std::conditional<V == 2, float2, float>::type>::type;
-    int st_off[NL];
-    uint64_t st_ok = 0;
+    int st_voff[NL];                              // byte offset in dy at channel 0
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
         const int e = tid + NT * i;
@@ -112,22 +149,19 @@ conv_bwd_data_taps_kernel(const ConvParams p, int bands)
         const int q = V * (e - j * (QP / V));
         const int prow = P0 + TB - 1 - j;
         const bool ok = e < NU && prow >= 0 && prow < p.P && q < p.Q;
-        st_off[i] = ok ? prow * p.sxh + q * p.sxw : 0;
-        st_ok |= (ok ? uint64_t(1) : uint64_t(0)) << i;
+        st_voff[i] = ok ? 4 * (n * p.sxn + prow * p.sxh + q * p.sxw) : kTapsOutside;
     }
     VT sv[NL];
-    // unconditional loads at a valid address; zeros are chosen at the store
     auto load_chunk = [&](int k) {
-        const float* src = dyn + k * p.sxc;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) sv[i] = *reinterpret_cast<const VT*>(src + st_off[i]);
+        for (int i = 0; i < NL; ++i) sv[i] = taps_load<VT>(dr, st_voff[i], 4 * k * p.sxc);
     };
     auto store_chunk = [&](int buf) {
         VT* dst = reinterpret_cast<VT*>(smem + buf * BUF);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int e = tid + NT * i;
-            if (NU % NT == 0 || e < NU) dst[e] = (st_ok >> i) & 1 ? sv[i] : VT{};
+            if (NU % NT == 0 || e < NU) dst[e] = sv[i];
         }
     };
 
@@ -146,15 +180,13 @@ conv_bwd_data_taps_kernel(const ConvParams p, int bands)
     }
     // B: F[k, c, a + u i, s] with i = 4t + g and s = l16 (zero past the taps)
     const bool s_ok = l16 < p.S;
-    int b_off[IS];
-    uint32_t b_ok = 0;
+    int b_voff[IS];                               // byte offset in F at k = 0
 #pragma unroll
     for (int t = 0; t < IS; ++t) {
         const int i = 4 * t + g;
         const int r = a + p.u * i;
         const bool ok = s_ok && i < Ia && r < p.R;
-        b_off[t] = ok ? (c * p.R + r) * p.S + l16 : 0;
-        b_ok |= (ok ? 1u : 0u) << t;
+        b_voff[t] = ok ? 4 * ((c * p.R + r) * p.S + l16) : kTapsOutside;
     }
     const int fk = p.C * p.R * p.S;               // filter stride between k
 
@@ -162,11 +194,10 @@ conv_bwd_data_taps_kernel(const ConvParams p, int bands)
 #pragma unroll
     for (int f = 0; f < FM; ++f) acc[f] = AccV{};
 
-    // filter taps: unconditional loads at a valid address, zeros chosen after
     float bv[IS];
     auto load_b = [&](int k) {
 #pragma unroll
-        for (int t = 0; t < IS; ++t) bv[t] = F[k * fk + b_off[t]];
+        for (int t = 0; t < IS; ++t) bv[t] = taps_load<float>(fr, b_voff[t], 4 * k * fk);
     };
     auto blk_ok = [&](int f) { return NBLK % 4 == 0 || wave + 4 * f < NBLK; };
 
@@ -181,7 +212,7 @@ conv_bwd_data_taps_kernel(const ConvParams p, int bands)
         const float* buf = smem + cur * BUF;
         float bcur[IS];
 #pragma unroll
-        for (int t = 0; t < IS; ++t) bcur[t] = (b_ok >> t) & 1u ? bv[t] : 0.0f;
+        for (int t = 0; t < IS; ++t) bcur[t] = bv[t];
         load_b(more ? k + 1 : k);
         // keep the next chunk's loads ahead of this chunk's products
         __builtin_amdgcn_sched_barrier(0);
@@ -264,7 +295,7 @@ constexpr int kTapsTB = 2, kTapsQB = 22, kTapsIS = 6;
 bool bwd_data_taps_fits(const ConvParams& p)
 {
     return p.S <= 16 && p.Q <= 16 * kTapsQB && (p.R + p.u - 1) / p.u <= 4 * kTapsIS && p.K >= 1 && p.v >= 1 &&
-           p.u >= 1;
+           p.u >= 1 && 4 * taps_dy_elems(p) < ((int64_t)1 << 31) && 4 * taps_f_elems(p) < ((int64_t)1 << 31);
 }
 
 // dy values per staging load: V consecutive columns at V-aligned addresses

@@ -640,10 +640,18 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
     const int row0 = out_row(m0);
     const int nrows = p.N * hq;
 
+    // Loads go through range-checked buffer descriptors (as in the forward
+    // kernels above): a unit outside dy, or an output channel past K, reads
+    // past the buffer and gets zeros.
+    const int64_t dy_elems = (int64_t)(p.N - 1) * p.sxn + (int64_t)(p.C - 1) * p.sxc + (int64_t)(p.P - 1) * p.sxh +
+                             (int64_t)(p.Q - 1) * p.sxw + 1;
+    const __amdgpu_buffer_rsrc_t dr = rows_rsrc(p.x, (int)(4 * dy_elems));
+    const int RS = p.R * S;                           // p.R here: the filter's full row count
+    const __amdgpu_buffer_rsrc_t fr = rows_rsrc(p.w, 4 * p.C * p.K * RS);
+
     // ---- halo loader: unit e = (dy channel, slot, XV columns), columns fastest
-    int h_base[NH];
-    int h_row[NH];                                    // dy row of tap row 0 (i subtracted per chunk)
-    uint32_t h_ok = 0;
+    uint32_t h_voff[NH];                              // byte offset at dy channel 0, tap row 0
+    int h_row[NH];                                    // dy row of tap row 0 (i subtracted per chunk; far negative: no unit)
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
         const int e = tid + NT * i;
@@ -657,52 +665,44 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
         const int hh = orow - n * hq;
         const int qc = col + qoff;
         const bool ok = e < HE && orow < nrows && (unsigned)qc < (unsigned)p.Q;
-        h_row[i] = P0f + hh;
-        h_base[i] = ok ? n * p.sxn + cl * p.sxc + qc * p.sxw : 0;
-        h_ok |= (ok ? 1u : 0u) << i;
+        h_row[i] = ok ? P0f + hh : -(1 << 30);
+        h_voff[i] = 4u * (uint32_t)(n * p.sxn + cl * p.sxc + qc * p.sxw + (P0f + hh) * p.sxh);   // (wraps)
     }
     // ---- slab loader: thread -> (output channel c, dy channel k, taps sh*SH ...) of row a + u*i
     const int sk = tid % TN;                          // output channel within the tile
     const int sc = (tid / TN) % CB;                   // dy channel within the block
     const int sh = tid / SROWS;
-    const bool s_ok = n0 + sk < p.K;
-    const int RS = p.R * S;                           // p.R here: the filter's full row count
+    // F[k0 + sc][n0 + sk][a + u*i][s], packed K,C,R,S: this thread's part (past w for a channel past K)
+    const int s_voff = n0 + sk < p.K ? 4 * ((sc * p.K + n0 + sk) * RS + a * S) : kRowsOutside;
 
     using HV = typename std::conditional<XV == 4, float4, typename std::conditional<XV == 2, float2, float>::type>::type;
     HV hv[NH];
-    uint32_t hv_ok = 0;
     float sv[SH];
     const int ncb = p.C / CB;
     const int nri = p.Kred;                           // tap rows of the phase
     const int nch = ncb * nri;
-    auto load_chunk = [&](int ch) {
-        const int i = ch / ncb;
-        const int k0 = (ch - i * ncb) * CB;
-        uint32_t m = 0;
+    auto load_chunk = [&](int k0, int i) {
+        const uint32_t chunk_off = 4u * (uint32_t)(k0 * p.sxc - i * p.sxh);
 #pragma unroll
         for (int e = 0; e < NH; ++e) {
-            const int pr = h_row[e] - i;
-            const bool ok = ((h_ok >> e) & 1u) && (unsigned)pr < (unsigned)p.P;
-            hv[e] = *reinterpret_cast<const HV*>(dy + (ok ? h_base[e] + k0 * p.sxc + pr * p.sxh : 0));
-            m |= (ok ? 1u : 0u) << e;
+            const bool ok = (unsigned)(h_row[e] - i) < (unsigned)p.P;
+            hv[e] = rows_load<HV>(dr, ok ? (int)(h_voff[e] + chunk_off) : kRowsOutside);
         }
-        hv_ok = m;
-        // F[k0 + sc][c][a + u*i][0 .. S-1], packed K,C,R,S
-        const int fo = ((k0 + sc) * p.K + (s_ok ? n0 + sk : 0)) * RS + (a + p.u * i) * S;
+        const int s_chunk = 4 * (k0 * p.K * RS + p.u * i * S);
 #pragma unroll
-        for (int j = 0; j < SH; ++j) sv[j] = f[fo + min(sh * SH + j, S - 1)];
+        for (int j = 0; j < SH; ++j) sv[j] = rows_load<float>(fr, s_voff + 4 * min(sh * SH + j, S - 1), s_chunk);
     };
     auto store_chunk = [&](int buf) {
         float* dst = smem + buf * BUF;
 #pragma unroll
         for (int e = 0; e < NH; ++e) {
             const int ee = tid + NT * e;
-            if (HE % NT == 0 || ee < HE) reinterpret_cast<HV*>(dst)[ee] = (hv_ok >> e) & 1u ? hv[e] : HV{};
+            if (HE % NT == 0 || ee < HE) reinterpret_cast<HV*>(dst)[ee] = hv[e];
         }
 #pragma unroll
         for (int j = 0; j < SH; ++j) {
             const int s = sh * SH + j;
-            if (SPLIT * SH == S || s < S) dst[HALO + (s * CB + sc) * TN + sk] = s_ok ? sv[j] : 0.0f;
+            if (SPLIT * SH == S || s < S) dst[HALO + (s * CB + sc) * TN + sk] = sv[j];
         }
     };
 
@@ -734,15 +734,20 @@ conv_bwd_data_rows_mfma_kernel(const ConvParams p)
     auto a_off = [](int t) { const int s = t / (CB / G), cp = t % (CB / G); return G * cp * PLANE - s; };
     auto b_off = [](int t) { const int s = t / (CB / G), cp = t % (CB / G); return (s * CB + G * cp) * TN; };
 
+    int lk0 = 0, li = 0;                              // the chunk last loaded: dy channel block, tap row
     if (nch > 0) {
-        load_chunk(0);
+        load_chunk(lk0, li);
         store_chunk(0);
         __syncthreads();
     }
     for (int ch = 0; ch < nch; ++ch) {
         const int cur = ch & 1;
         const bool more = ch + 1 < nch;
-        load_chunk(more ? ch + 1 : ch);
+        if (more && (lk0 += CB) == p.C) {
+            lk0 = 0;
+            ++li;
+        }
+        load_chunk(lk0, li);
         __builtin_amdgcn_sched_barrier(0);
         const float* buf = smem + cur * BUF;
         float av[FM], bv[FN];
@@ -794,6 +799,11 @@ bool bwd_data_rows_mfma_fits(const ConvParams& p)
 hipError_t launch_bwd_data_rows_mfma(const ConvParams& p0, hipStream_t stream)
 {
     if (!bwd_data_rows_mfma_fits(p0)) return hipErrorInvalidValue;
+    // buffer descriptor ranges: dy and the filters under 2^31 bytes
+    const int64_t dy_elems = (int64_t)(p0.N - 1) * p0.sxn + (int64_t)(p0.K - 1) * p0.sxc + (int64_t)(p0.P - 1) * p0.sxh +
+                             (int64_t)(p0.Q - 1) * p0.sxw + 1;
+    if (4 * dy_elems >= ((int64_t)1 << 31) || 4 * (int64_t)p0.K * p0.C * p0.R * p0.S >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;
     // dy columns per halo load: the first staged column pad_left - (S - 1),
     // Q and dy's strides multiples of it, unit column stride, dy aligned
     int xv = 1;

@@ -853,7 +853,9 @@ Plan make_dgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* dyd, cons
         // forward pass's row-streamed kernel per stride phase (speech layer 2:
         // 5.0 ms through the gather kernel)
         bool rows_mfma_ok = false;
-        if (pl.dt == DType::F32 && C >= 16) {
+        // (its buffer loads: dy and the filters under 2^31 bytes)
+        if (pl.dt == DType::F32 && C >= 16 && extent(*dyd) * 4 < (int64_t(1) << 31) &&
+            (int64_t)k * C * R * S * 4 < (int64_t(1) << 31)) {
             ConvParams q = p;
             q.K = k;
             q.W = W;
