@@ -66,6 +66,26 @@ namespace miconv {
 // filter n of a tile keeps group g of a tap at 16-byte unit 2n + (g ^ swz(n))
 __device__ __forceinline__ int slab_swz(int n) { return ((n >> 2) ^ (n >> 3)) & 1; }
 
+namespace {
+constexpr int kBf16BufWord3 = 0x00020000;         // raw 32-bit buffer, range-checked per dword
+constexpr int kBf16Outside = (int)0x80000000u;    // an offset past x and w (both under 2^31 bytes)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bf16_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBf16BufWord3);
+}
+__device__ __forceinline__ u32x4 bf16_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return u32x4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ uint32_t bf16_load2(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+}  // namespace
+
 template <int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WP, int SL, bool CVEC, bool DG, bool WB,
           bool RV>
 __global__ void __launch_bounds__(256)
@@ -125,6 +145,14 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
 
     const uint16_t* __restrict__ x = static_cast<const uint16_t*>(p.x);
     const uint16_t* __restrict__ w = static_cast<const uint16_t*>(p.w);
+    // x (and the packed filters of the forward pass) through range-checked
+    // buffer descriptors: a unit outside x or past K reads at an offset past
+    // the buffer and gets zeros, so the stores need no masks and a chunk's
+    // channel offset is the scalar offset (host: x, w under 2^31 bytes)
+    const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + blk_off(p.div_xcb, p.sxcb, p.sxc, p.C - 1) +
+                            (int64_t)(p.H - 1) * p.sxh + (int64_t)(p.W - 1) * p.sxw + 1;
+    const __amdgpu_buffer_rsrc_t xr = bf16_rsrc(p.x, 2 * x_elems);
+    const __amdgpu_buffer_rsrc_t wr = bf16_rsrc(p.w, 2 * (int64_t)p.K * p.Kred);
 
     if constexpr (RV) {
         // both halo buffers start zeroed: the row loader writes only pixels inside x
@@ -145,8 +173,7 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
     const int nslots = vrow(m_end - 1) + R - vr_first;   // <= SL (host-checked)
 
     // ---- halo loader: unit e = (group g, pixel), pixel fastest along the lanes
-    int h_off[HUT];
-    uint32_t h_ok = 0;
+    int h_voff[HUT];                                 // byte offset at the chunk's first channel
 #pragma unroll
     for (int i = 0; i < HUT; ++i) {
         const int e = tid + NT * i;
@@ -160,8 +187,7 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
         const int wcol = col - p.pad_left;
         const bool ok = e < HU && slot < nslots && (int)n < p.N && h >= 0 && h < p.H && wcol >= 0 &&
                         wcol < p.W;
-        h_off[i] = ok ? (int)n * p.sxn + 8 * g * p.sxc + h * p.sxh + wcol * p.sxw : 0;
-        h_ok |= (ok ? 1u : 0u) << i;
+        h_voff[i] = ok ? 2 * ((int)n * p.sxn + 8 * g * p.sxc + h * p.sxh + wcol * p.sxw) : kBf16Outside;
     }
 
     // RV (x with unit column stride, 16-byte aligned rows): block b = (group g,
@@ -173,8 +199,8 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
     // written: the halo starts zeroed.  (Measured on the 13x13 layers at a
     // 16-element pitch: 1-3% faster than eight 2-byte loads per pixel group;
     // the blocks spread over all four waves instead of the first: 5-7% slower.)
-    int rv_off[RV ? NBT : 1], rv_pix[RV ? NBT : 1], rv_np[RV ? NBT : 1];
-    uint32_t rv_ok = 0, rv_last = 0;
+    int rv_voff[RV ? NBT : 1], rv_pix[RV ? NBT : 1], rv_np[RV ? NBT : 1];
+    uint32_t rv_last = 0;
     if constexpr (RV) {
 #pragma unroll
         for (int i = 0; i < NBT; ++i) {
@@ -187,10 +213,9 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
             const int h = (int)hp - p.pad_top;
             const int w0 = 8 * seg;
             const bool ok = b < NBX && slot < nslots && (int)n < p.N && h >= 0 && h < p.H && w0 < p.W;
-            rv_off[i] = ok ? (int)n * p.sxn + 8 * g * p.sxc + h * p.sxh + w0 : 0;
+            rv_voff[i] = ok ? 2 * ((int)n * p.sxn + 8 * g * p.sxc + h * p.sxh + w0) : kBf16Outside;
             rv_pix[i] = (slot * WP + w0 + p.pad_left) * PIX + 16 * g;   // LDS byte offset of pixel w0
             rv_np[i] = ok ? min(8, p.W - w0) : 0;                      // pixels inside the row
-            rv_ok |= (ok ? 1u : 0u) << i;
             // the tensor's last row (channel C-1 is group 1, channel 7 of the
             // last chunk) ends x's storage: a segment reaching past W there
             // is read pixel by pixel
@@ -201,7 +226,7 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
     u32x4 rv_val[RV ? NBT : 1][8];
 
     // ---- slab loader: unit e = (filter row, 8-channel group)
-    int s_off[SUT];
+    int s_off[SUT];                                  // DG: elements (masked); else byte offsets (past w: none)
     uint32_t s_ok = 0;
 #pragma unroll
     for (int i = 0; i < SUT; ++i) {
@@ -216,14 +241,13 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
         if constexpr (DG)
             s_off[i] = ok ? ((8 * g + 4 * half) * p.K + n0 + row) * RS : 0;
         else
-            s_off[i] = ok ? (n0 + row) * p.Kred + 8 * g * RS : 0;
+            s_off[i] = ok ? 2 * ((n0 + row) * p.Kred + 8 * g * RS) : kBf16Outside;
         s_ok |= (ok ? 1u : 0u) << i;
     }
 
     // WB: block b = (tap t, group g, octet o), octet fastest (consecutive lanes
     // read consecutive 16-byte pieces of one (channel, tap) filter row)
-    int wb_off[WB ? WBT : 1];
-    uint32_t wb_ok = 0;
+    int wb_voff[WB ? WBT : 1];                      // byte offsets (past w: none)
     if constexpr (WB) {
         const int cblk = RS * p.wcb * p.wkb;             // elements of one (filter block, channel block)
 #pragma unroll
@@ -235,8 +259,8 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
             const int t = tg >> 1;
             const int k = n0 + 8 * o;
             const bool ok = b < NB && k < p.K;
-            wb_off[i] = ok ? (k / p.wkb) * (p.C / p.wcb) * cblk + (t * p.wcb + 8 * g) * p.wkb + k % p.wkb : 0;
-            wb_ok |= (ok ? 1u : 0u) << i;
+            wb_voff[i] = ok ? 2 * ((k / p.wkb) * (p.C / p.wcb) * cblk + (t * p.wcb + 8 * g) * p.wkb + k % p.wkb)
+                            : kBf16Outside;
         }
     }
     u32x4 wb_val[WB ? WBT : 1][8];
@@ -254,9 +278,10 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
     constexpr int NL = NLH + (WB ? 8 * WBT : SUT * (DG ? ND : NV));   // load pieces per chunk
     constexpr int NS = HSP + (WB ? 8 * WBT : SUT * RS);              // store pieces per chunk
 
-    // Loads are unconditional (a unit outside the input or past K reads the
-    // chunk's first element of x or w instead, which exists) and their
-    // values are replaced by zeros at the store, so no load sits in a branch.
+    // No load sits in a branch: the halo and the forward pass's filters come
+    // through the buffer descriptors (zeros outside); the data gradient's
+    // filter loads are unconditional at a valid address and their values are
+    // replaced by zeros at the store.
     // x offset of a chunk's first channel (channel-blocked x: the chunk lies in one block)
     auto x_chunk = [&](int c0) { return blk_off(p.div_xcb, p.sxcb, p.sxc, c0); };
     auto load_piece = [&](int q, int c0) {
@@ -264,32 +289,32 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
             if constexpr (RV) {
                 // block i, channel j (unconditional: an empty block reads the chunk's first row)
                 const int i = q / 8, j = q % 8;
-                const uint16_t* src = x + rv_off[i] + x_chunk(c0) + j * p.sxc;
                 if (j == 7 && ((rv_last >> i) & 1) && c0 + CB == p.C) {
+                    const uint16_t* src = x + rv_voff[i] / 2 + x_chunk(c0) + j * p.sxc;
                     uint32_t v[4] = {0, 0, 0, 0};
                     for (int f = 0; f < rv_np[i]; ++f) v[f >> 1] |= (uint32_t)src[f] << (16 * (f & 1));
                     rv_val[i][j] = u32x4{v[0], v[1], v[2], v[3]};
                 } else {
-                    rv_val[i][j] = *reinterpret_cast<const u32x4*>(src);
+                    rv_val[i][j] = bf16_load16(xr, rv_voff[i], 2 * (x_chunk(c0) + j * p.sxc));
                 }
             } else if constexpr (CVEC) {
-                h_vec[q] = *reinterpret_cast<const u32x4*>(x + h_off[q] + x_chunk(c0));
+                h_vec[q] = bf16_load16(xr, h_voff[q], 2 * x_chunk(c0));
             } else {
                 const int i = q / 8, j = q % 8;
-                h_raw[i][j] = x[h_off[i] + x_chunk(c0) + j * p.sxc];
+                h_raw[i][j] = bf16_load2(xr, h_voff[i], 2 * (x_chunk(c0) + j * p.sxc));
             }
         } else if constexpr (WB) {
             // the chunk's 16 channels lie in one channel block
             const int i = (q - NLH) / 8, j = (q - NLH) % 8;
             const int co = (c0 / p.wcb) * (RS * p.wcb * p.wkb) + (c0 % p.wcb) * p.wkb;
-            wb_val[i][j] = *reinterpret_cast<const u32x4*>(w + wb_off[i] + co + j * p.wkb);
+            wb_val[i][j] = bf16_load16(wr, wb_voff[i], 2 * (co + j * p.wkb));
         } else if constexpr (DG) {
             const int i = (q - NLH) / ND, v = (q - NLH) % ND;
             const int j = v / RS, t = v % RS;
             s_raw[i][v] = w[s_off[i] + (c0 + j) * p.K * RS + t];
         } else {
             const int i = (q - NLH) / NV, v = (q - NLH) % NV;
-            s_val[i][v] = *reinterpret_cast<const u32x4*>(w + s_off[i] + c0 * RS + 8 * v);
+            s_val[i][v] = bf16_load16(wr, s_off[i] + 16 * v, 2 * c0 * RS);
         }
     };
 
@@ -319,7 +344,6 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
             if (HU % NT == 0 || e < HU) {
                 const int pix = e % (SL * WP);
                 const int g = e / (SL * WP);
-                const bool ok = (h_ok >> i) & 1;
                 u32x4 val;
                 if constexpr (CVEC) {
                     val = h_vec[i];
@@ -331,8 +355,6 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
 #pragma unroll
                     for (int d = 0; d < 4; ++d) val[d] = h_raw[i][2 * d] | (h_raw[i][2 * d + 1] << 16);
                 }
-#pragma unroll
-                for (int d = 0; d < 4; ++d) val[d] = ok ? val[d] : 0u;
                 *reinterpret_cast<u32x4*>(hb + pix * PIX + 16 * g) = val;
             }
         } else if constexpr (WB) {
@@ -346,14 +368,12 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
                 const int g = tg & 1;
                 const int t = tg >> 1;
                 const int row = 8 * o + f;
-                const bool ok = (wb_ok >> i) & 1;
                 u32x4 out;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     const uint32_t lo = wb_val[i][2 * d][f >> 1];
                     const uint32_t hi = wb_val[i][2 * d + 1][f >> 1];
-                    const uint32_t v = (f & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-                    out[d] = ok ? v : 0u;
+                    out[d] = (f & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
                 }
                 *reinterpret_cast<u32x4*>(hb + HALO_BYTES + t * TAP_BYTES + 16 * (2 * row + (g ^ slab_swz(row)))) = out;
             }
@@ -391,7 +411,7 @@ conv_fwd_halo_bf16_kernel(const ConvParams p)
                         const uint32_t whi = words[khi >> 1];
                         const uint32_t lo = (klo & 1) ? (wlo >> 16) : (wlo & 0xffffu);
                         const uint32_t hi = (khi & 1) ? (whi & 0xffff0000u) : (whi << 16);
-                        out[d] = ok ? (lo | hi) : 0u;
+                        out[d] = lo | hi;
                     }
                     *reinterpret_cast<u32x4*>(dst + t * TAP_BYTES) = out;
                 }

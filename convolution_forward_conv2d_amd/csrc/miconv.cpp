@@ -449,6 +449,12 @@ bool halo_eligible(const HaloCandidate& h, DType dt, const ConvParams& p, const 
                    bool dgrad = false)
 {
     if (h.dt != dt || h.r != p.R || h.s != p.S) return false;
+    if (dt == DType::BF16) {
+        // the bf16 kernel's buffer descriptors: x and the filters under 2^31 bytes
+        const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + miconv::blk_off(p.div_xcb, p.sxcb, p.sxc, p.C - 1) +
+                                (int64_t)(p.H - 1) * p.sxh + (int64_t)(p.W - 1) * p.sxw + 1;
+        if (2 * x_elems >= (int64_t(1) << 31) || 2 * (int64_t)p.K * p.Kred >= (int64_t(1) << 31)) return false;
+    }
     if (p.C % h.cb != 0) return false;
     // channel-blocked x: a chunk of h.cb channels must lie in one block
     if (p.div_xcb.d != miconv::kOneBlock && p.div_xcb.d % h.cb != 0) return false;
