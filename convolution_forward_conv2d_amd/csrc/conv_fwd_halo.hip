@@ -46,6 +46,37 @@
 
 namespace miconv {
 
+namespace {
+constexpr int kHaloBufWord3 = 0x00020000;         // raw 32-bit buffer, range-checked per dword
+constexpr int kHaloOutside = (int)0x80000000u;    // an offset past x and w (both under 2^31 bytes)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t halo_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kHaloBufWord3);
+}
+__device__ __forceinline__ u32x4 halo_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return u32x4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ u32x2 halo_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return u32x2{v[0], v[1]};
+}
+__device__ __forceinline__ void halo_load_elem(float& v, __amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void halo_load_elem(double& v, __amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    const u32x2 t = halo_load8(r, voff, soff);
+    v = __hiloint2double((int)t[1], (int)t[0]);
+}
+}  // namespace
+
 // WPE: the fewest waves per SIMD the register allocation must leave room for
 // (1: no constraint).  Two for instances whose LDS admits two workgroups per
 // CU but whose unconstrained allocation would not (Overfeat L2 on 208 x 64
@@ -63,7 +94,7 @@ namespace miconv {
 // x's storage, so a segment reaching past W there is read pixel by pixel
 // (the forward pass only: on the data gradient's dy it measured slower).
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS,
-          bool DG, bool WB, int WPE, int XR>
+          bool DG, bool WB, int WPE, int XR, bool BL>
 __global__ void __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(WPE)))
 conv_fwd_halo_kernel(const ConvParams p)
 {
@@ -147,6 +178,14 @@ conv_fwd_halo_kernel(const ConvParams p)
 
     const In* __restrict__ x = static_cast<const In*>(p.x);
     const In* __restrict__ w = static_cast<const In*>(p.w);
+    // x and w through range-checked buffer descriptors: a unit outside x or
+    // past the filters reads at an offset past the buffer and gets zeros, so
+    // no load sits in a branch or needs a select; a chunk's channel offset is
+    // the scalar offset (host: x, w under 2^31 bytes)
+    const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + blk_off(p.div_xcb, p.sxcb, p.sxc, p.C - 1) +
+                            (int64_t)(p.H - 1) * p.sxh + (int64_t)(p.W - 1) * p.sxw + 1;
+    const __amdgpu_buffer_rsrc_t xr = halo_rsrc(p.x, x_elems * ES);
+    const __amdgpu_buffer_rsrc_t wr = halo_rsrc(p.w, (int64_t)p.C * p.K * RS * ES);
 
     // virtual padded row of output row m (tap r adds r): n * Hp + p * u
     auto vrow = [&](int m) {
@@ -159,8 +198,7 @@ conv_fwd_halo_kernel(const ConvParams p)
     const int nslots = vrow(m_end - 1) + R - vr_first;  // <= SL (host-checked)
 
     // ---- halo loader: thread -> HE (channel, slot, column) positions, fixed for the tile
-    int h_off[HE];
-    uint32_t h_ok = 0;
+    int h_voff[HE];                                  // byte offsets at channel 0 (past x: none)
 #pragma unroll
     for (int i = 0; i < HE; ++i) {
         const int e = tid + NT * i;
@@ -172,8 +210,8 @@ conv_fwd_halo_kernel(const ConvParams p)
         const int h = (int)hp - p.pad_top;
         const int wcol = col - p.pad_left;
         const bool ok = slot < nslots && (int)n < p.N && h >= 0 && h < p.H && wcol >= 0 && wcol < p.W;
-        h_off[i] = ok ? (int)n * p.sxn + cl * p.sxc + h * p.sxh + wcol * p.sxw : 0;
-        h_ok |= (ok ? 1u : 0u) << i;
+        const int off = (int)n * p.sxn + cl * p.sxc + h * p.sxh + wcol * p.sxw;
+        h_voff[i] = BL ? (ok ? off * ES : kHaloOutside) : (ok ? off : -1);   // (!BL: elements, -1 none)
     }
 
     // XR: unit u = (channel, slot, segment): pixels w0 .. w0 + VX - 1, w0 = VX * segment
@@ -191,7 +229,8 @@ conv_fwd_halo_kernel(const ConvParams p)
             const int h = (int)hp - p.pad_top;
             const int w0 = VX * seg;
             const bool ok = u < HUX && slot < nslots && (int)n < p.N && h >= 0 && h < p.H && w0 < p.W;
-            x_off[i] = ok ? (int)n * p.sxn + cl * p.sxc + h * p.sxh + w0 : 0;
+            const int off = (int)n * p.sxn + cl * p.sxc + h * p.sxh + w0;
+            x_off[i] = BL ? (ok ? off * ES : kHaloOutside) : (ok ? off : 0);   // bytes (!BL: elements)
             x_dst[i] = cl * PLANE + slot * WP + w0 + p.pad_left;     // element index of pixel w0
             x_np[i] = ok ? min(VX, p.W - w0) : 0;                      // pixels inside the row
             x_ok |= (ok ? 1u : 0u) << i;
@@ -206,8 +245,7 @@ conv_fwd_halo_kernel(const ConvParams p)
     // (DG: thread -> NDU (slab row, channel) runs of R*S taps instead)
     constexpr int DU = TN * CB;
     constexpr int NDU = DG ? (DU + NT - 1) / NT : 1;
-    int d_off[NDU];
-    uint32_t d_ok = 0;
+    int d_off[NDU];                                  // byte offsets at chunk 0 (past w: none)
     if constexpr (DG) {
 #pragma unroll
         for (int i = 0; i < NDU; ++i) {
@@ -215,12 +253,11 @@ conv_fwd_halo_kernel(const ConvParams p)
             const int row = e % TN;
             const int cl = e / TN;
             const bool ok = e < DU && n0 + row < p.K;
-            d_off[i] = ok ? (cl * p.K + n0 + row) * RS : 0;          // elements
-            d_ok |= (ok ? 1u : 0u) << i;
+            const int off = (cl * p.K + n0 + row) * RS;
+            d_off[i] = BL ? (ok ? off * ES : kHaloOutside) : (ok ? off : -1);
         }
     }
-    int b_off[WB ? 1 : NVB];
-    uint32_t b_ok = 0;
+    int b_off[WB ? 1 : NVB];                         // byte offsets at chunk 0 (past w: none)
     if constexpr (!WB) {
 #pragma unroll
         for (int i = 0; i < NVB; ++i) {
@@ -228,8 +265,8 @@ conv_fwd_halo_kernel(const ConvParams p)
             const int row = e / VPR;
             const int vec = e - row * VPR;
             const bool ok = e < TN * VPR && n0 + row < p.K;
-            b_off[i] = ok ? (n0 + row) * p.Kred + vec * (VB / ES) : 0;   // elements
-            b_ok |= (ok ? 1u : 0u) << i;
+            const int off = (n0 + row) * p.Kred + vec * (VB / ES);
+            b_off[i] = BL ? (ok ? off * ES : kHaloOutside) : (ok ? off : -1);
         }
     }
     // WB: unit u -> slab column e = (channel cl, tap t), quad kq; its element
@@ -261,41 +298,58 @@ conv_fwd_halo_kernel(const ConvParams p)
         if constexpr (XR) {
 #pragma unroll
             for (int i = 0; i < HXT; ++i) {
-                const In* src = x + x_off[i] + xo;
                 if (XR == 2 && ((x_last >> i) & 1) && c0 + CB == p.C) {
+                    const In* src = x + (BL ? x_off[i] / ES : x_off[i]) + xo;
                     In v[VX] = {};
                     for (int e = 0; e < x_np[i]; ++e) v[e] = src[e];
                     __builtin_memcpy(&x_val[i], v, 16);
+                } else if constexpr (BL) {
+                    x_val[i] = halo_load16(xr, x_off[i], xo * ES);
                 } else {
-                    x_val[i] = *reinterpret_cast<const u32x4*>(src);
+                    x_val[i] = *reinterpret_cast<const u32x4*>(x + x_off[i] + xo);
                 }
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < HE; ++i) h_val[i] = ((h_ok >> i) & 1) ? load_elem(x + h_off[i] + xo) : In(0);
+            for (int i = 0; i < HE; ++i) {
+                if constexpr (BL)
+                    halo_load_elem(h_val[i], xr, h_voff[i], xo * ES);
+                else
+                    h_val[i] = h_voff[i] >= 0 ? load_elem(x + h_voff[i] + xo) : In(0);
+            }
         }
         if constexpr (DG) {
-            const int wo = c0 * p.K * RS;
+            const int wo = c0 * p.K * RS * ES;
 #pragma unroll
             for (int i = 0; i < NDU; ++i) {
-                const bool ok = (d_ok >> i) & 1;
 #pragma unroll
-                for (int t = 0; t < RS; ++t) d_val[i][t] = ok ? load_elem(w + d_off[i] + wo + t) : In(0);
+                for (int t = 0; t < RS; ++t) {
+                    if constexpr (BL)
+                        halo_load_elem(d_val[i][t], wr, d_off[i] + t * ES, wo);
+                    else
+                        d_val[i][t] = d_off[i] >= 0 ? load_elem(w + d_off[i] + wo / ES + t) : In(0);
+                }
             }
         } else if constexpr (WB) {
             const int wo = (c0 / p.wcb) * (RS * p.wcb * p.wkb) + (c0 % p.wcb) * p.wkb;
 #pragma unroll
             for (int i = 0; i < NWB; ++i) b_val[i] = *reinterpret_cast<const u32x4*>(w + w_off[i] + wo);
         } else {
-            const int wo = c0 * RS;
+            const int wo = c0 * RS * ES;
 #pragma unroll
             for (int i = 0; i < NVB; ++i) {
-                if constexpr (VB == 16) {
-                    b_val[i] = ((b_ok >> i) & 1) ? *reinterpret_cast<const u32x4*>(w + b_off[i] + wo)
-                                                 : u32x4{0, 0, 0, 0};
+                if constexpr (!BL) {
+                    const In* src = w + b_off[i] + wo / ES;
+                    if constexpr (VB == 16) {
+                        b_val[i] = b_off[i] >= 0 ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+                    } else {
+                        const u32x2 t = b_off[i] >= 0 ? *reinterpret_cast<const u32x2*>(src) : u32x2{0, 0};
+                        b_val[i] = u32x4{t[0], t[1], 0, 0};
+                    }
+                } else if constexpr (VB == 16) {
+                    b_val[i] = halo_load16(wr, b_off[i], wo);
                 } else {
-                    const u32x2 t = ((b_ok >> i) & 1) ? *reinterpret_cast<const u32x2*>(w + b_off[i] + wo)
-                                                      : u32x2{0, 0};
+                    const u32x2 t = halo_load8(wr, b_off[i], wo);
                     b_val[i] = u32x4{t[0], t[1], 0, 0};
                 }
             }
@@ -484,7 +538,13 @@ conv_fwd_halo_kernel(const ConvParams p)
 
 // ------------------------------------------------------------------ instances and launch
 
-template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS, int WPE>
+// BLM: loads through buffer descriptors (BL) always (1), never (0: masked
+// global loads), or in the forward pass only (2) -- per instance, as measured
+// on MI355X: the 16x16-block tiles of 144 and 176 rows, whose registers are
+// full, ran 4-10% slower with them (their SGPRs spill), fp64 176x64 in the
+// data gradient 6% slower; every other instance 2-9% faster.
+template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int CB, int WP, int SL, int KS, int WPE,
+          int BLM>
 static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStream_t stream)
 {
     ConvParams p = p0;
@@ -510,7 +570,7 @@ static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStrea
             (uintptr_t)p.w % 16 != 0)
             return hipErrorInvalidValue;
         hipLaunchKernelGGL(
-            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, true, WPE, 0>), grid,
+            (conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, false, true, WPE, 0, BLM != 0>), grid,
             dim3(256 * KS), 0, stream, p);
         return hipGetLastError();
     }
@@ -527,7 +587,7 @@ static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStrea
                      (int64_t)p.sxc >= (int64_t)p.sxh * p.H && (int64_t)p.sxn >= (int64_t)p.sxc * p.C;
 #define MICONV_HALO_LAUNCH(DGV, XRV)                                                                              \
     hipLaunchKernelGGL((conv_fwd_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, CB, WP, SL, KS, DGV, false, WPE, \
-                                             XRV>),                                                               \
+                                             XRV, BLM == 1 || (BLM == 2 && !DGV)>),                               \
                        grid, dim3(256 * KS), 0, stream, p)
     if (dgrad && xr1)
         MICONV_HALO_LAUNCH(true, 1);
@@ -543,31 +603,32 @@ static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStrea
     return hipGetLastError();
 }
 
-//        name                     policy     TM   TN  waves  R  S  CB  WP  SL  KS  WPE
+//        name                     policy     TM   TN  waves  R  S  CB  WP  SL  KS  WPE  BLM
 #define MICONV_HALO_VARIANTS(X)                                                 \
-    X(HALO_F32_3x3_128x128, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1, 2)          \
-    X(HALO_F32_3x3_128x64, PolF32, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1, 1)            \
-    X(HALO_F32_3x3_64x128, PolF32, 64, 128, 2, 2, 3, 3, 4, 16, 16, 1, 1)            \
-    X(HALO_F32_3x3_96x128, PolF32, 96, 128, 1, 4, 3, 3, 4, 16, 16, 1, 1)            \
-    X(HALO_F32_5x5_128x128, PolF32, 128, 128, 2, 2, 5, 5, 4, 32, 16, 1, 1)          \
-    X(HALO_F32_5x5_128x128_C2, PolF32, 128, 128, 2, 2, 5, 5, 2, 32, 16, 1, 2)       \
-    X(HALO_F32_5x5_128x96_C2, PolF32, 128, 96, 4, 1, 5, 5, 2, 32, 16, 1, 1)         \
-    X(HALO_F32x16_5x5_208x64, PolF32x16, 208, 64, 1, 4, 5, 5, 4, 32, 24, 1, 2)      \
-    X(HALO_F32x16_3x3_176x128, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 1, 1)    \
-    X(HALO_F32x16_3x3_144x128, PolF32x16, 144, 128, 1, 4, 3, 3, 4, 16, 16, 1, 1)    \
-    X(HALO_F32x16_5x5_128x96, PolF32x16, 128, 96, 2, 2, 5, 5, 4, 32, 16, 1, 1)      \
-    X(HALO_F32x16_3x3_176x128_KS2, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 2, 1) \
-    X(HALO_F32_3x3_128x128_KS2, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 2, 1)      \
-    X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1, 1)          \
-    X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16, 1, 1)               \
-    X(HALO_F64_3x3_128x64, PolF64, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1, 2)            \
-    X(HALO_F64_3x3_176x64_KS2, PolF64, 176, 64, 1, 4, 3, 3, 4, 16, 16, 2, 1)
+    X(HALO_F32_3x3_128x128, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1, 2, 1)          \
+    X(HALO_F32_3x3_128x64, PolF32, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1, 1, 1)            \
+    X(HALO_F32_3x3_64x128, PolF32, 64, 128, 2, 2, 3, 3, 4, 16, 16, 1, 1, 1)            \
+    X(HALO_F32_3x3_96x128, PolF32, 96, 128, 1, 4, 3, 3, 4, 16, 16, 1, 1, 1)            \
+    X(HALO_F32_5x5_128x128, PolF32, 128, 128, 2, 2, 5, 5, 4, 32, 16, 1, 1, 1)          \
+    X(HALO_F32_5x5_128x128_C2, PolF32, 128, 128, 2, 2, 5, 5, 2, 32, 16, 1, 2, 1)       \
+    X(HALO_F32_5x5_128x96_C2, PolF32, 128, 96, 4, 1, 5, 5, 2, 32, 16, 1, 1, 1)         \
+    X(HALO_F32x16_5x5_208x64, PolF32x16, 208, 64, 1, 4, 5, 5, 4, 32, 24, 1, 2, 1)      \
+    X(HALO_F32x16_3x3_176x128, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 1, 1, 1)    \
+    X(HALO_F32x16_3x3_144x128, PolF32x16, 144, 128, 1, 4, 3, 3, 4, 16, 16, 1, 1, 0)    \
+    X(HALO_F32x16_5x5_128x96, PolF32x16, 128, 96, 2, 2, 5, 5, 4, 32, 16, 1, 1, 1)      \
+    X(HALO_F32x16_3x3_176x128_KS2, PolF32x16, 176, 128, 1, 4, 3, 3, 4, 16, 16, 2, 1, 0) \
+    X(HALO_F32_3x3_128x128_KS2, PolF32, 128, 128, 2, 2, 3, 3, 4, 16, 16, 2, 1, 1)      \
+    X(HALO_F64_3x3_128x128, PolF64, 128, 128, 2, 2, 3, 3, 4, 16, 16, 1, 1, 1)          \
+    X(HALO_F64_3x3_64x64, PolF64, 64, 64, 2, 2, 3, 3, 4, 16, 16, 1, 1, 1)               \
+    X(HALO_F64_3x3_128x64, PolF64, 128, 64, 2, 2, 3, 3, 4, 16, 16, 1, 2, 1)            \
+    X(HALO_F64_3x3_176x64_KS2, PolF64, 176, 64, 1, 4, 3, 3, 4, 16, 16, 2, 1, 2)
 
 hipError_t launch_halo(Variant v, const ConvParams& p, bool dgrad, hipStream_t stream)
 {
     switch (v) {
-#define X(name, pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks, wpe) \
-    case Variant::name: return launch_halo_variant<pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks, wpe>(p, dgrad, stream);
+#define X(name, pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks, wpe, blm) \
+    case Variant::name:                                                \
+        return launch_halo_variant<pol, tm, tn, wmm, wnn, r, s, cb, wp, sl, ks, wpe, blm>(p, dgrad, stream);
         MICONV_HALO_VARIANTS(X)
 #undef X
     default: return dgrad ? hipErrorInvalidValue : launch_halo_bf16(v, p, stream);
