@@ -55,7 +55,8 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20, help="steps per timed region (five regions)")
+    ap.add_argument("--steps", type=int, default=25,
+                    help="steps per timed region (five regions; the default keeps an Overfeat region above 100 ms)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="overfeat", choices=WORKLOADS)
     ap.add_argument("--op", default="fprop", choices=("fprop", "dgrad", "wgrad"),
