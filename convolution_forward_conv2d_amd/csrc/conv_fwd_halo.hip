@@ -284,7 +284,8 @@ conv_fwd_halo_kernel(const ConvParams p)
             const int k = n0 + kq * VK;
             const bool ok = u < NWU && kq < QT && k < p.K;
             const int cl = e / RS, t = e - cl * RS;
-            w_off[i] = ok ? (k / p.wkb) * (p.C / p.wcb) * blk + (t * p.wcb + cl) * p.wkb + k % p.wkb : 0;
+            const int off = (k / p.wkb) * (p.C / p.wcb) * blk + (t * p.wcb + cl) * p.wkb + k % p.wkb;
+            w_off[i] = BL ? (ok ? off * ES : kHaloOutside) : (ok ? off : 0);   // (BL: bytes)
             w_ok |= (ok ? 1u : 0u) << i;
         }
     }
@@ -333,7 +334,12 @@ conv_fwd_halo_kernel(const ConvParams p)
         } else if constexpr (WB) {
             const int wo = (c0 / p.wcb) * (RS * p.wcb * p.wkb) + (c0 % p.wcb) * p.wkb;
 #pragma unroll
-            for (int i = 0; i < NWB; ++i) b_val[i] = *reinterpret_cast<const u32x4*>(w + w_off[i] + wo);
+            for (int i = 0; i < NWB; ++i) {
+                if constexpr (BL)
+                    b_val[i] = halo_load16(wr, w_off[i], wo * ES);
+                else
+                    b_val[i] = *reinterpret_cast<const u32x4*>(w + w_off[i] + wo);
+            }
         } else {
             const int wo = c0 * RS * ES;
 #pragma unroll
@@ -409,7 +415,7 @@ conv_fwd_halo_kernel(const ConvParams p)
                 const int e = (u >> 3) % TK;
                 if (NWU % NT == 0 || u < NWU) {
                     if (kq < QT) {
-                        const bool ok = (w_ok >> i) & 1;
+                        const bool ok = BL || ((w_ok >> i) & 1);   // (BL: zeros read past w)
                         In v[VK];
                         __builtin_memcpy(v, &b_val[i], 16);
 #pragma unroll

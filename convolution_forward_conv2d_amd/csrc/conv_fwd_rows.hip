@@ -207,11 +207,13 @@ conv_fwd_rows_kernel(const ConvParams p)
         }
         if (WB) {
             // the channel's block once per chunk, then the taps at a stride of cb*kb
+            // (a filter past K reads past w: zero)
             const int c = c0 + sc;
             const int wo = s_base + (c / p.wcb) * (p.R * S * p.wcb * p.wkb) + (c % p.wcb) * p.wkb +
                            r * S * p.wcb * p.wkb;
+            const int vo = s_ok ? 4 * wo : kRowsOutside;
 #pragma unroll
-            for (int i = 0; i < SH; ++i) sv[i] = w[wo + min(sh * SH + i, S - 1) * p.wcb * p.wkb];
+            for (int i = 0; i < SH; ++i) sv[i] = rows_load<float>(wr, vo + 4 * min(sh * SH + i, S - 1) * p.wcb * p.wkb);
         } else {
             const int s_chunk = 4 * (c0 * p.R + r) * S;
 #pragma unroll
@@ -238,7 +240,7 @@ conv_fwd_rows_kernel(const ConvParams p)
 #pragma unroll
         for (int i = 0; i < SH; ++i) {
             const int s = sh * SH + i;
-            if (SPLIT * SH == S || s < S) dst[HALO + (s * CB + sc) * TN + sk] = WB && !s_ok ? 0.0f : sv[i];
+            if (SPLIT * SH == S || s < S) dst[HALO + (s * CB + sc) * TN + sk] = sv[i];
         }
     };
 
