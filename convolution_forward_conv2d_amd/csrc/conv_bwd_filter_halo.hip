@@ -424,6 +424,13 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     // R = 0 (pairs): any filter height and row stride
     if ((R > 0 && (p.u != 1 || p.R != R)) || p.v != 1 || p.S != S || p.Q + S - 1 > WPH || (QD > 0 && p.Q != QD))
         return hipErrorInvalidValue;
+    // the buffer descriptors' range: x and dy under 2^30 bytes
+    constexpr int64_t ES = (int64_t)sizeof(typename Pol::In);
+    const int64_t dy_elems = (int64_t)(p.N - 1) * p.sdn + (int64_t)(p.M - 1) * p.sdk + (int64_t)(p.P - 1) * p.sdp +
+                             (int64_t)(p.Q - 1) * p.sdq + 1;
+    const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + (int64_t)(p.C - 1) * p.sxc + (int64_t)(p.H - 1) * p.sxh +
+                            (int64_t)(p.W - 1) * p.sxw + 1;
+    if (ES * dy_elems >= ((int64_t)1 << 30) || ES * x_elems >= ((int64_t)1 << 30)) return hipErrorInvalidValue;
     p.m_tiles = (p.M + TM - 1) / TM;
     p.n_tiles = (p.K + TN - 1) / TN;
     const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));

@@ -554,6 +554,14 @@ template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int
 static hipError_t launch_halo_variant(const ConvParams& p0, bool dgrad, hipStream_t stream)
 {
     ConvParams p = p0;
+    {
+        // the buffer descriptors' range: x (dy) and the filters under 2^31 bytes
+        constexpr int64_t ES = (int64_t)sizeof(typename Pol::In);
+        const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + blk_off(p.div_xcb, p.sxcb, p.sxc, p.C - 1) +
+                                (int64_t)(p.H - 1) * p.sxh + (int64_t)(p.W - 1) * p.sxw + 1;
+        if (BLM != 0 && (ES * x_elems >= ((int64_t)1 << 31) || ES * p.C * (int64_t)p.K * R * S >= ((int64_t)1 << 31)))
+            return hipErrorInvalidValue;
+    }
     if (p.m_step <= 0 || p.m_step > TM) p.m_step = TM;   // the host sets P*Q for image tiles
     p.m_tiles = (p.M + p.m_step - 1) / p.m_step;
     p.n_tiles = (p.K + TN - 1) / TN;

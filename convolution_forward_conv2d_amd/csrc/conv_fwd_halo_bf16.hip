@@ -598,13 +598,23 @@ static hipError_t launch_halo_bf16_any(Variant v, const ConvParams& p, bool dgra
     }
 }
 
+// the buffer descriptors' range: x (dy) and the filters under 2^31 bytes
+static bool bf16_buffers_fit(const ConvParams& p)
+{
+    const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + blk_off(p.div_xcb, p.sxcb, p.sxc, p.C - 1) +
+                            (int64_t)(p.H - 1) * p.sxh + (int64_t)(p.W - 1) * p.sxw + 1;
+    return 2 * x_elems < ((int64_t)1 << 31) && 2 * (int64_t)p.C * p.K * p.R * p.S < ((int64_t)1 << 31);
+}
+
 hipError_t launch_halo_bf16(Variant v, const ConvParams& p, hipStream_t stream)
 {
+    if (!bf16_buffers_fit(p)) return hipErrorInvalidValue;
     return launch_halo_bf16_any(v, p, false, stream);
 }
 
 hipError_t launch_halo_bf16_dgrad(Variant v, const ConvParams& p, hipStream_t stream)
 {
+    if (!bf16_buffers_fit(p)) return hipErrorInvalidValue;
     return launch_halo_bf16_any(v, p, true, stream);
 }
 

@@ -449,11 +449,13 @@ bool halo_eligible(const HaloCandidate& h, DType dt, const ConvParams& p, const 
                    bool dgrad = false)
 {
     if (h.dt != dt || h.r != p.R || h.s != p.S) return false;
-    if (dt == DType::BF16) {
-        // the bf16 kernel's buffer descriptors: x and the filters under 2^31 bytes
+    {
+        // the halo kernels' buffer descriptors: x (dy) and the filters under 2^31 bytes
+        const int64_t es = dt == DType::F64 ? 8 : dt == DType::BF16 ? 2 : 4;
         const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + miconv::blk_off(p.div_xcb, p.sxcb, p.sxc, p.C - 1) +
                                 (int64_t)(p.H - 1) * p.sxh + (int64_t)(p.W - 1) * p.sxw + 1;
-        if (2 * x_elems >= (int64_t(1) << 31) || 2 * (int64_t)p.K * p.Kred >= (int64_t(1) << 31)) return false;
+        if (es * x_elems >= (int64_t(1) << 31) || es * p.C * (int64_t)p.K * p.R * p.S >= (int64_t(1) << 31))
+            return false;
     }
     if (p.C % h.cb != 0) return false;
     // channel-blocked x: a chunk of h.cb channels must lie in one block

@@ -644,3 +644,32 @@ def test_brgemm_argument_errors(monkeypatch):
     assert mic.brgemm_kernel_name(torch.float32, 128, 128, 128, b_strides=(0, 1, 128)) == "ws_f32_32x64"
     with pytest.raises(mic.MicError):
         mic.brgemm_kernel_name(torch.float32, 128, 128, 102, b_strides=(0, 1, 102))   # k % 4 != 0
+
+
+def test_buffer_load_kernels_refuse_tensors_past_their_range():
+    """The staging kernels read x (dy) and the filters through range-checked buffer
+    descriptors whose record count is 32-bit: tensors of 2^31 bytes or more must go to
+    another kernel (the gather kernel), just under it the fast kernels stay."""
+    import dataclasses
+    F32 = mic.MIC_DTYPE_F32
+
+    def fwd(lay):
+        d = _descs(lay, F32, F32, F32)
+        try:
+            return mic.mic_conv_forward_kernel_name(None, *d)
+        finally:
+            _free(*d)
+
+    l1, l5, sp2 = (workloads.by_name(n) for n in ("overfeat_l1", "overfeat_l5", "speech_l2"))
+    # Overfeat L1: x = N * 3 * 231 * 231 * 4 bytes (N = 3000: 1.92e9; 3400: 2.18e9)
+    assert fwd(dataclasses.replace(l1, N=3000)) == "rows1n6_f32_s11_256x32"
+    assert not fwd(dataclasses.replace(l1, N=3400)).startswith("rows")
+    # Overfeat L5: x = N * 1024 * 144 * 4 bytes (N = 1024: 0.60e9; 4096: 2.42e9)
+    assert fwd(dataclasses.replace(l5, N=1024)).startswith("halo_")
+    big5 = dataclasses.replace(l5, N=4096)
+    assert not fwd(big5).startswith("halo_")
+    assert not _dgrad_name(big5).startswith("dgrad_halo")
+    assert not _wgrad_name(big5).startswith("wgh_")
+    # speech L2: x = N * 32 * 81 * 350 * 4 bytes (N = 500: 1.81e9; 700: 2.54e9)
+    assert fwd(dataclasses.replace(sp2, N=500)) == "rows_f32_s11_256x32"
+    assert not fwd(dataclasses.replace(sp2, N=700)).startswith("rows")
