@@ -13,9 +13,10 @@
 // y's unit stride: along q, or along c for channels-innermost y.
 //
 // Index arithmetic is 32-bit (the plan keeps N*C*P*Q below 2^30) with
-// multiply-shift division.  A 3x3 window (AlexNet's) has an instance with
-// the window unrolled, so its nine loads (clamped to the plane's first
-// element where they fall outside it) issue together; other windows loop.
+// multiply-shift division.  A 3x3 window (AlexNet's) has an instance per
+// mode with the window unrolled, so its nine loads (clamped to the plane's
+// first element where they fall outside it) issue together and only the
+// mode's own arithmetic runs; other windows loop.
 //
 // Parameters: x, its strides sx*; y, its strides sy*; N, C, H, W; window
 // R x S; P, Q; u, v; pad_top, pad_left; M = N*P*Q; div_pq, div_q divide by
@@ -40,7 +41,9 @@ __device__ __forceinline__ float widen_pool(Bf16Pool v) { return __uint_as_float
 
 }  // namespace
 
-template <class In, class Acc, class Out, int RT, int ST>
+// MODE: the pooling mode as a compile-time constant (0 max, 1 average over
+// R*S, 2 average over the positions inside), or -1 to read it from Kred.
+template <class In, class Acc, class Out, int RT, int ST, int MODE>
 __global__ void __launch_bounds__(256) pool_fwd_kernel(const ConvParams p)
 {
     const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
@@ -67,21 +70,50 @@ __global__ void __launch_bounds__(256) pool_fwd_kernel(const ConvParams p)
         ++inside;
     };
     if constexpr (RT > 0) {
+        // the window's rows and columns tested once each; a position outside
+        // the plane reads x's first element and is left out by its mask
+        uint32_t rok = 0, cok = 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) rok |= ((unsigned)(h0 + r) < (unsigned)p.H ? 1u : 0u) << r;
+#pragma unroll
+        for (int s = 0; s < ST; ++s) cok |= ((unsigned)(w0 + s) < (unsigned)p.W ? 1u : 0u) << s;
+        const In* xw = x + h0 * p.sxh + w0 * p.sxw;
         Acc vals[RT][ST];
-        bool ok[RT][ST];
 #pragma unroll
         for (int r = 0; r < RT; ++r)
 #pragma unroll
             for (int s = 0; s < ST; ++s) {
-                const int h = h0 + r, w = w0 + s;
-                ok[r][s] = (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
-                vals[r][s] = widen_pool(x[ok[r][s] ? h * p.sxh + w * p.sxw : 0]);
+                const bool ok = ((rok >> r) & (cok >> s) & 1u) != 0;
+                vals[r][s] = widen_pool((ok ? xw : x)[ok ? r * p.sxh + s * p.sxw : 0]);
             }
+        if constexpr (MODE == 0) {
+            // max: the first inside value, then any larger one
+            bool any = false;
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
+            for (int r = 0; r < RT; ++r)
 #pragma unroll
-            for (int s = 0; s < ST; ++s)
-                if (ok[r][s]) take(vals[r][s]);
+                for (int s = 0; s < ST; ++s) {
+                    const bool ok = ((rok >> r) & (cok >> s) & 1u) != 0;
+                    best = ok && (!any || vals[r][s] > best) ? vals[r][s] : best;
+                    any = any || ok;
+                }
+            inside = any ? 1 : 0;
+        } else if constexpr (MODE == 1 || MODE == 2) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+                for (int s = 0; s < ST; ++s) {
+                    const bool ok = ((rok >> r) & (cok >> s) & 1u) != 0;
+                    sum += ok ? vals[r][s] : Acc(0);
+                }
+            if constexpr (MODE == 2) inside = __builtin_popcount(rok) * __builtin_popcount(cok);
+        } else {
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+                for (int s = 0; s < ST; ++s)
+                    if (((rok >> r) & (cok >> s) & 1u) != 0) take(vals[r][s]);
+        }
     } else {
         for (int r = 0; r < p.R; ++r) {
             const int h = h0 + r;
@@ -94,9 +126,10 @@ __global__ void __launch_bounds__(256) pool_fwd_kernel(const ConvParams p)
         }
     }
     Acc acc;
-    if (p.Kred == 0)
+    const int mode = MODE >= 0 ? MODE : p.Kred;
+    if (mode == 0)
         acc = inside ? best : Acc(0);
-    else if (p.Kred == 1)
+    else if (mode == 1)
         acc = sum / (Acc)(p.R * p.S);
     else
         acc = inside ? sum / (Acc)inside : Acc(0);
@@ -114,10 +147,14 @@ static hipError_t launch_pool_t(const ConvParams& p, hipStream_t stream)
 {
     const int64_t total = (int64_t)p.M * p.C;
     const dim3 grid((unsigned)((total + 255) / 256));
-    if (p.R == 3 && p.S == 3)
-        hipLaunchKernelGGL((pool_fwd_kernel<In, Acc, Out, 3, 3>), grid, dim3(256), 0, stream, p);
+    if (p.R == 3 && p.S == 3 && p.Kred == 0)
+        hipLaunchKernelGGL((pool_fwd_kernel<In, Acc, Out, 3, 3, 0>), grid, dim3(256), 0, stream, p);
+    else if (p.R == 3 && p.S == 3 && p.Kred == 1)
+        hipLaunchKernelGGL((pool_fwd_kernel<In, Acc, Out, 3, 3, 1>), grid, dim3(256), 0, stream, p);
+    else if (p.R == 3 && p.S == 3)
+        hipLaunchKernelGGL((pool_fwd_kernel<In, Acc, Out, 3, 3, 2>), grid, dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((pool_fwd_kernel<In, Acc, Out, 0, 0>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((pool_fwd_kernel<In, Acc, Out, 0, 0, -1>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
