@@ -361,6 +361,21 @@ __device__ __forceinline__ void ws_reduce_store(const ConvParams& p, typename Po
 // workgroup barrier.  Loads run NBUF - 1 chunks ahead in registers.  A and
 // B must be contiguous along k with k a multiple of a 16-byte vector and
 // every vector aligned (brgemm_ws_run).
+namespace {
+constexpr int kBrBufWord3 = 0x00020000;           // raw 32-bit buffer, range-checked per dword
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t br_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBrBufWord3);
+}
+__device__ __forceinline__ u32x4 br_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+    return u32x4{v[0], v[1], v[2], v[3]};
+}
+}  // namespace
+
 template <class Pol, int TM, int TN, int NW, int TKW, int NBUF>
 __global__ void __launch_bounds__(NW * 64)
 brgemm_ws_kernel(const ConvParams p)
@@ -396,51 +411,55 @@ brgemm_ws_kernel(const ConvParams p)
     const int m0 = tc.mt * TM;
     const int n0 = tc.nt * TN;
 
-    const In* __restrict__ a = static_cast<const In*>(p.x);
-    const In* __restrict__ b = static_cast<const In*>(p.w);
     const int kb = p.Kred;
     const int L = p.N * kb;
+    // A and B through range-checked buffer descriptors (host: each under
+    // 2^30 bytes): a row past M or N, or a chunk past the reduction, reads at
+    // an offset of at least 2^30 and gets zeros, so nothing is selected when
+    // the chunk is written to LDS and no load waits on a test
+    constexpr uint32_t OUT = 0x40000000u;
+    constexpr int ES = (int)sizeof(In);
+    const int64_t a_elems = (int64_t)(p.N - 1) * p.sxn + (int64_t)(p.M - 1) * p.sxh + (int64_t)(kb - 1) * p.sxw + 1;
+    const int64_t b_elems = (int64_t)(p.N - 1) * p.sdn + (int64_t)(p.K - 1) * p.sdq + (int64_t)(kb - 1) * p.sdk + 1;
+    const __amdgpu_buffer_rsrc_t ar = br_rsrc(p.x, a_elems * ES);
+    const __amdgpu_buffer_rsrc_t brs = br_rsrc(p.w, b_elems * ES);
 
     // loader coordinates: row lr (+ 8 per instruction), 16-byte segment sg
     const int lr = lane >> 3;
     const int sg = lane & 7;
-    const In* arow[AI];
-    bool aok[AI];
+    uint32_t arow[AI];                                  // byte offset of the row (OUT: none)
 #pragma unroll
     for (int j = 0; j < AI; ++j) {
         const int r = m0 + j * 8 + lr;
-        aok[j] = r < p.M;
-        arow[j] = a + (aok[j] ? r : 0) * p.sxh;
+        arow[j] = r < p.M ? (uint32_t)(r * p.sxh * ES) : OUT;
     }
-    const In* bcol[BI];
-    bool bok[BI];
+    uint32_t bcol[BI];
 #pragma unroll
     for (int j = 0; j < BI; ++j) {
         const int c = n0 + j * 8 + lr;
-        bok[j] = c < p.K;
-        bcol[j] = b + (bok[j] ? c : 0) * p.sdq;
+        bcol[j] = c < p.K ? (uint32_t)(c * p.sdq * ES) : OUT;
     }
 
-    // The loaded values stay raw in the ring; out-of-range rows and chunks
-    // are zeroed when the chunk is written to LDS, so nothing waits on a
-    // load before its chunk is due.
+    // The loaded values stay raw in the ring until the chunk is due.
     u32x4 sa[NBUF][AI];
     u32x4 sb[NBUF][BI];
-    bool sin[NBUF];
-    const u32x4 zero = {0, 0, 0, 0};
     auto load = [&](auto buf_c, int ch) {
         constexpr int B = decltype(buf_c)::value;
         const int t = ch * TK + wave * TKW + sg * VE;
         const bool in = t < L;
-        sin[B] = in;
         uint32_t i, kk;
-        p.div_rs.divmod((uint32_t)(in ? t : 0), i, kk);
-        const int aoff = (int)i * p.sxn + (int)kk;
-        const int boff = (int)i * p.sdn + (int)kk;
+        if (p.N == 1) {                                 // one product: no batch index
+            i = 0;
+            kk = (uint32_t)t;
+        } else {
+            p.div_rs.divmod((uint32_t)(in ? t : 0), i, kk);
+        }
+        const uint32_t aoff = in ? (uint32_t)(((int)i * p.sxn + (int)kk) * ES) : OUT;
+        const uint32_t boff = in ? (uint32_t)(((int)i * p.sdn + (int)kk) * ES) : OUT;
 #pragma unroll
-        for (int j = 0; j < AI; ++j) sa[B][j] = *reinterpret_cast<const u32x4*>(arow[j] + aoff);
+        for (int j = 0; j < AI; ++j) sa[B][j] = br_load16(ar, arow[j] + aoff);
 #pragma unroll
-        for (int j = 0; j < BI; ++j) sb[B][j] = *reinterpret_cast<const u32x4*>(bcol[j] + boff);
+        for (int j = 0; j < BI; ++j) sb[B][j] = br_load16(brs, bcol[j] + boff);
     };
 
     unsigned char* region = smem + wave * WBYTES;
@@ -453,12 +472,10 @@ brgemm_ws_kernel(const ConvParams p)
         constexpr int B = decltype(buf_c)::value;
 #pragma unroll
         for (int j = 0; j < AI; ++j)
-            *reinterpret_cast<u32x4*>(region + (j * 8 + lr) * RB + ((sg ^ lr) << 4)) =
-                (sin[B] && aok[j]) ? sa[B][j] : zero;
+            *reinterpret_cast<u32x4*>(region + (j * 8 + lr) * RB + ((sg ^ lr) << 4)) = sa[B][j];
 #pragma unroll
         for (int j = 0; j < BI; ++j)
-            *reinterpret_cast<u32x4*>(region + (TM + j * 8 + lr) * RB + ((sg ^ lr) << 4)) =
-                (sin[B] && bok[j]) ? sb[B][j] : zero;
+            *reinterpret_cast<u32x4*>(region + (TM + j * 8 + lr) * RB + ((sg ^ lr) << 4)) = sb[B][j];
         // vector v of lane group g is segment v*G + g of its row
 #pragma unroll
         for (int f = 0; f < FM; ++f)
@@ -565,6 +582,11 @@ static hipError_t launch_ws_variant(const ConvParams& p0, hipStream_t stream)
     const bool vec = vec_ok<In>(VE, p.x, p.sxn, p.sxh, p.sxw, p.Kred, p.N, p.M) &&
                      vec_ok<In>(VE, p.w, p.sdn, p.sdq, p.sdk, p.Kred, p.N, p.K);
     if (!vec) return hipErrorInvalidValue;     // the host picks these variants only for such operands
+    // the buffer descriptors' range: A and B under 2^30 bytes
+    const int64_t es = (int64_t)sizeof(In);
+    const int64_t a_elems = (int64_t)(p.N - 1) * p.sxn + (int64_t)(p.M - 1) * p.sxh + (int64_t)(p.Kred - 1) * p.sxw + 1;
+    const int64_t b_elems = (int64_t)(p.N - 1) * p.sdn + (int64_t)(p.K - 1) * p.sdq + (int64_t)(p.Kred - 1) * p.sdk + 1;
+    if (es * a_elems >= ((int64_t)1 << 30) || es * b_elems >= ((int64_t)1 << 30)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((brgemm_ws_kernel<Pol, TM, TN, NW, TKW, NBUF>), grid, dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }

@@ -1226,6 +1226,11 @@ Plan make_brgemm_plan(const mic_handle_st* h, mic_dtype dtype, int m, int n, int
         if (run == 0 || k == 0 || batch == 0 || sa_k != 1 || sb_k != 1 || k % run) return false;
         if (batch > 1 && (sa_i % ve || sb_i % ve)) return false;
         if ((m > 1 && sa_m % ve) || (n > 1 && sb_n % ve)) return false;
+        // its buffer descriptors: A and B under 2^30 bytes
+        const int64_t es = (int64_t)dtype_size(dtype);
+        if ((operand_extent(batch, sa_i, m, sa_m, k, sa_k) + 1) * es >= (int64_t(1) << 30) ||
+            (operand_extent(batch, sb_i, n, sb_n, k, sb_k) + 1) * es >= (int64_t(1) << 30))
+            return false;
         return !need_pointers || ((uintptr_t)a % 16 == 0 && (uintptr_t)b % 16 == 0);
     };
     const int num_cu = h ? h->num_cu : kDefaultCUs;
