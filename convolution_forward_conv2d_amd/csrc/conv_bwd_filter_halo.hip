@@ -442,6 +442,11 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
 // row pitch WPH and plane pitch PLANE: the smallest with at most two-way
 // (fp64 three-way) bank conflicts on the halo reads, searched offline
 // (QD: output rows of exactly QD columns, the steps along them only).
+// The 27-column 5x5 form on 64 x 48 tiles takes pitch 40 / plane 333: at
+// 32 / 261 its B reads ran up to 5-way conflicts (73% of the LDS cycles
+// conflict cycles, measured), and once the loads had stopped bounding the
+// kernel the wider rows won (AlexNet conv2 1878 -> 1737 us); pitch 20 on
+// the 12-column 3x3 form (2-way -> mostly conflict-free) ran 4% slower.
 // 64 x 48 tiles: 256 filters x 2400 columns (96 channels, 5x5) make 200
 // tiles instead of 152 of 64 x 64 on the 256 compute units.
 //        name                     policy   TM  TN  waves  R  S  WPH  PR  PLANE  KS  QD
@@ -458,7 +463,7 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     X(WGH_F32X16_5x5_Q20, PolF32x16, 64, 64, 2, 2, 5, 5, 24, 4, 197, 2, 20)          \
     X(WGH_F32X16_5x5_Q27, PolF32x16, 64, 64, 2, 2, 5, 5, 32, 4, 261, 2, 27)          \
     X(WGH_F32X16_5x5_Q20_64x48, PolF32x16, 64, 48, 4, 1, 5, 5, 24, 4, 197, 2, 20)    \
-    X(WGH_F32X16_5x5_Q27_64x48, PolF32x16, 64, 48, 4, 1, 5, 5, 32, 4, 261, 2, 27)   \
+    X(WGH_F32X16_5x5_Q27_64x48, PolF32x16, 64, 48, 4, 1, 5, 5, 40, 4, 333, 2, 27)   \
     X(WGH_F32_3x3_Q13_KS4, PolF32, 64, 64, 2, 2, 3, 3, 16, 14, 259, 4, 13)            \
     X(WGH_F32_3x3_W16_64x96_KS4, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 13, 247, 4, 0)  \
     X(WGH_F32_3x3_Q12_64x96_KS4, PolF32x16, 64, 96, 2, 2, 3, 3, 16, 12, 247, 4, 12)  \

@@ -189,7 +189,7 @@ const WgCandidate kWg[] = {
     {{Variant::WGH_F32X16_5x5_Q20, 64, 64, "wgh_f32x16_5x5_q20_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 19, 1, 20},
     {{Variant::WGH_F32X16_5x5_Q27, 64, 64, "wgh_f32x16_5x5_q27_64x64"}, DType::F32, WgKind::HALO, 5, 5, 32, 20.2, 1, 27},
     {{Variant::WGH_F32X16_5x5_Q20_64x48, 64, 48, "wgh_f32x16_5x5_q20_64x48"}, DType::F32, WgKind::HALO, 5, 5, 24, 16.8, 1, 20},
-    {{Variant::WGH_F32X16_5x5_Q27_64x48, 64, 48, "wgh_f32x16_5x5_q27_64x48"}, DType::F32, WgKind::HALO, 5, 5, 32, 19.96, 1, 27},
+    {{Variant::WGH_F32X16_5x5_Q27_64x48, 64, 48, "wgh_f32x16_5x5_q27_64x48"}, DType::F32, WgKind::HALO, 5, 5, 40, 18.6, 1, 27},
     // four groups of waves per tile (16 waves a CU, latency hidden within the
     // tile; measured on MI355X: AlexNet conv3/conv5 616 -> 576 us, conv4 952 -> 834)
     {{Variant::WGH_F32_3x3_Q13_KS4, 64, 64, "wgh_f32_3x3_q13_64x64_ks4"}, DType::F32, WgKind::HALO, 3, 3, 16, 19.2, 1, 13},
