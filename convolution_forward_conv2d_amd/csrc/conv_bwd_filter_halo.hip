@@ -43,8 +43,17 @@
 // position index as DY: tall filters (21 rows onto 32 channels at stride 2,
 // the speech network's second layer) whose channel planes would not fit.
 //
-// No workspace: the reduction is not split across workgroups.  The
-// epilogue stores dw (packed K,C,R,S) along j as conv_bwd_filter.hip does.
+// No workspace.  The epilogue stores dw (packed K,C,R,S) along j as
+// conv_bwd_filter.hip does; or, with split_ch > 0 (beta = 0 only), the
+// launch runs every tile twice: workgroup b < T (T tiles) takes the chunks
+// [0, split_ch) of its tile, workgroup T + b the chunks [split_ch, end),
+// and both add alpha times their sum into dw, zeroed beforehand, with
+// atomic adds.  Two terms added onto zero give the same bits in either
+// order (fp addition commutes), so the result does not depend on which
+// workgroup lands first.  This fills the compute units a one-round launch
+// leaves idle: with T tiles on U units and k = ceil(T / (U - T)), the long
+// parts (a fraction k / (k + 1) of the chunks) run on T units while the
+// other U - T units take the short ones k at a time.
 //
 // Parameters as for conv_bwd_filter.hip: x, strides sx*; w = dy, strides
 // sd*; y = dw with syn = C*R*S, syk = 1; M = K, K = C*R*S; div_pq = div_q = 1;
@@ -96,7 +105,7 @@ __device__ __forceinline__ void unroll_for(F&& f)
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WPH, int PR, int PLANE, int KS,
           int QD>
 __global__ void __launch_bounds__(256 * KS)
-conv_bwd_filter_halo_kernel(const ConvParams p)
+conv_bwd_filter_halo_kernel(const ConvParams p, int split_ch)
 {
     using In = typename Pol::In;
     using AccV = typename Pol::AccV;
@@ -161,7 +170,9 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     const int tid = threadIdx.x & 255;               // thread within its half
     const int lane = tid & 63;
     const int wave = tid >> 6;                       // wave within its half
-    const int tile = xcd_logical_tile((int)blockIdx.x, p.m_tiles * p.n_tiles, p.tile_rev);
+    const int ntl = p.m_tiles * p.n_tiles;
+    const int part = split_ch > 0 && (int)blockIdx.x >= ntl ? 1 : 0;   // the reduction part (split launches)
+    const int tile = xcd_logical_tile((int)blockIdx.x - part * ntl, ntl, p.tile_rev);
     const int mt = tile / p.n_tiles;
     const int nt = tile - mt * p.n_tiles;
     const int m0 = mt * TM;
@@ -169,7 +180,9 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
     const int c_lo = PAIRS ? n0 / S : n0 / RS1;     // first channel (pair) the tile's columns touch
 
     const int PB = (p.P + PR - 1) / PR;              // row blocks per image
-    const int nch = p.N * PB;
+    const int nch_all = p.N * PB;                    // chunks of the whole reduction
+    const int ch0 = part ? split_ch : 0;             // this workgroup's chunks [ch0, ch0 + nch)
+    const int nch = split_ch > 0 ? (part ? nch_all - split_ch : split_ch) : nch_all;
 
     // both chunk buffers start zeroed (the planes' spare elements stay so)
     for (int i = (int)threadIdx.x; i < 2 * BUF_BYTES / 16; i += NTT)
@@ -311,7 +324,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         for (int j = 0; j < FN; ++j) acc[i][j] = AccV{};
 
     if (nch > 0) {
-        set_chunk(0, 0);
+        set_chunk(ch0 / PB, (ch0 % PB) * PR);
         unroll_for<0, NL>([&](auto qc) { load_piece(qc); });
         unroll_for<0, NL>([&](auto qc) { store_piece(qc, 0); });
         __syncthreads();
@@ -413,12 +426,42 @@ conv_bwd_filter_halo_kernel(const ConvParams p)
         }
         __syncthreads();
     }
+    if (split_ch > 0) {
+        // a part's sum times alpha, added into the zeroed packed dw
+        static_assert(std::is_same<typename Pol::Acc, typename Pol::Out>::value, "atomic adds in the sum's type");
+        using Acc = typename Pol::Acc;
+        if (half == 0) {
+            Acc* dw = static_cast<Acc*>(p.y);
+            const Acc alpha = (Acc)p.alpha;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int e = 0; e < Pol::NACC; ++e) {
+                    const int gm = m0 + wm * WM + i * BM + Pol::row(e, lane);
+                    if (gm >= p.M) continue;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int gk = n0 + wn * WN + j * BM + Pol::col(e, lane);
+                        if (gk < p.K) unsafeAtomicAdd(dw + (int64_t)gm * p.syn + gk, alpha * acc[i][j][e]);
+                    }
+                }
+        }
+        return;
+    }
     store_acc_tile<Pol, FM, FN>(p, smem, acc, m0 + wm * WM, n0 + wn * WN, p.M, wave, lane, half == 0);
+}
+
+// dw <- 0 ahead of a split launch (a kernel rather than a memset: callers may
+// capture the launch in a graph)
+template <class T>
+__global__ void __launch_bounds__(256) wgh_zero_kernel(T* __restrict__ y, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) y[i] = T(0);
 }
 
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WPH, int PR, int PLANE, int KS,
           int QD>
-static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
+static hipError_t launch_wgh_variant(const ConvParams& p0, int split_k, hipStream_t stream)
 {
     ConvParams p = p0;
     // R = 0 (pairs): any filter height and row stride
@@ -433,9 +476,24 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     if (ES * dy_elems >= ((int64_t)1 << 30) || ES * x_elems >= ((int64_t)1 << 30)) return hipErrorInvalidValue;
     p.m_tiles = (p.M + TM - 1) / TM;
     p.n_tiles = (p.K + TN - 1) / TN;
-    const dim3 grid((unsigned)(p.m_tiles * p.n_tiles));
+    const int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
+    // split_k > 0: the first part takes k / (k + 1) of the chunks (at least
+    // one each); with beta = 0 only, and at least two chunks
+    if (split_k < 0 || (split_k > 0 && p.beta != 0.0)) return hipErrorInvalidValue;
+    const int64_t nch = (int64_t)p.N * ((p.P + PR - 1) / PR);
+    int split_ch = 0;
+    if (split_k > 0 && nch >= 2 && tiles > 0) {
+        const int64_t c = (nch * split_k + (split_k + 1) / 2) / (split_k + 1);
+        split_ch = (int)(c < 1 ? 1 : c > nch - 1 ? nch - 1 : c);
+        using Acc = typename Pol::Acc;
+        const int64_t n = (int64_t)p.M * p.K;
+        const int64_t blocks = (n + 255) / 256;
+        hipLaunchKernelGGL(wgh_zero_kernel<Acc>, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0,
+                           stream, static_cast<Acc*>(p.y), n);
+    }
+    const dim3 grid((unsigned)(tiles * (split_ch > 0 ? 2 : 1)));
     hipLaunchKernelGGL((conv_bwd_filter_halo_kernel<Pol, TM, TN, WAVES_M, WAVES_N, R, S, WPH, PR, PLANE, KS, QD>),
-                       grid, dim3(256 * KS), 0, stream, p);
+                       grid, dim3(256 * KS), 0, stream, p, split_ch);
     return hipGetLastError();
 }
 
@@ -474,11 +532,12 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, hipStream_t stream)
     X(WGH_F64_3x3_W16_KS4, PolF64, 64, 64, 2, 2, 3, 3, 16, 7, 147, 4, 0)                  \
     X(WGH_F64_3x3_W16_64x96, PolF64, 64, 96, 2, 2, 3, 3, 16, 7, 147, 2, 0)
 
-hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream)
+hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, int split_k, hipStream_t stream)
 {
     switch (v) {
 #define X(name, pol, tm, tn, wmm, wnn, r, s, wph, pr, plane, ks, qd) \
-    case Variant::name: return launch_wgh_variant<pol, tm, tn, wmm, wnn, r, s, wph, pr, plane, ks, qd>(p, stream);
+    case Variant::name:                                                 \
+        return launch_wgh_variant<pol, tm, tn, wmm, wnn, r, s, wph, pr, plane, ks, qd>(p, split_k, stream);
         MICONV_WGH_VARIANTS(X)
 #undef X
     default: return hipErrorInvalidValue;

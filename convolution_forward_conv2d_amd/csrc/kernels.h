@@ -128,8 +128,10 @@ hipError_t launch_direct(DType dt, const ConvParams& p, hipStream_t stream);
 // Filter gradient (implicit GEMM over the output positions); p laid out as
 // conv_bwd_filter.hip describes.
 // Filter gradient of a stride-1 layer through an LDS halo (R, S, dtype and
-// Q + S - 1 <= the variant's row pitch, host-checked).
-hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, hipStream_t stream);
+// Q + S - 1 <= the variant's row pitch, host-checked).  split_k > 0 (beta = 0
+// only): dw is zeroed and each tile's reduction runs as two workgroups, the
+// first taking k / (k + 1) of it, both adding into dw atomically.
+hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, int split_k, hipStream_t stream);
 hipError_t launch_bwd_filter(Variant v, const ConvParams& p, hipStream_t stream);
 hipError_t launch_bwd_filter_split(Variant v, const ConvParams& p, hipStream_t stream);
 hipError_t launch_bwd_filter_cl(Variant v, const ConvParams& p, hipStream_t stream);

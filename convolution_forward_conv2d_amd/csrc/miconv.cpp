@@ -11,6 +11,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
 #include <new>
 
 #include <hip/hip_runtime.h>
@@ -167,6 +169,7 @@ struct WgCandidate {
     double ns;
     int per_cu;
     int qd;             // halo kernel: output rows of exactly qd columns (0: any width)
+    int res2;           // halo kernel: two workgroups fit on a CU (LDS, registers)
 };
 const WgCandidate kWg[] = {
     {{Variant::WG_F32_128x128, 128, 128, "wg_f32_128x128"}, DType::F32, WgKind::GATHER, 0, 0, 0, 170.0, 1},
@@ -188,7 +191,7 @@ const WgCandidate kWg[] = {
     {{Variant::WGH_F32_3x3_Q13, 64, 64, "wgh_f32_3x3_q13_64x64"}, DType::F32, WgKind::HALO, 3, 3, 16, 18, 1, 13},
     {{Variant::WGH_F32X16_5x5_Q20, 64, 64, "wgh_f32x16_5x5_q20_64x64"}, DType::F32, WgKind::HALO, 5, 5, 24, 19, 1, 20},
     {{Variant::WGH_F32X16_5x5_Q27, 64, 64, "wgh_f32x16_5x5_q27_64x64"}, DType::F32, WgKind::HALO, 5, 5, 32, 20.2, 1, 27},
-    {{Variant::WGH_F32X16_5x5_Q20_64x48, 64, 48, "wgh_f32x16_5x5_q20_64x48"}, DType::F32, WgKind::HALO, 5, 5, 24, 16.8, 1, 20},
+    {{Variant::WGH_F32X16_5x5_Q20_64x48, 64, 48, "wgh_f32x16_5x5_q20_64x48"}, DType::F32, WgKind::HALO, 5, 5, 24, 16.8, 1, 20, 1},
     {{Variant::WGH_F32X16_5x5_Q27_64x48, 64, 48, "wgh_f32x16_5x5_q27_64x48"}, DType::F32, WgKind::HALO, 5, 5, 40, 18.6, 1, 27},
     // four groups of waves per tile (16 waves a CU, latency hidden within the
     // tile; measured on MI355X: AlexNet conv3/conv5 616 -> 576 us, conv4 952 -> 834)
@@ -338,6 +341,7 @@ struct Plan {
     Candidate cand;
     bool bvec;
     bool tap;          // gather kernel: reduction in channel blocks per filter tap
+    int split_k;       // filter-gradient halo kernel: reduction in two parts, k : 1 (0: one part)
     char name[64];     // variant name as reported and as MIC_FORCE_VARIANT spells it
 };
 
@@ -1080,6 +1084,13 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
     // 2^30 lies past both, and three such offsets still fit 32 bits)
     const bool halo_bufs_fit = extent(*xd) * es < (int64_t(1) << 30) && extent(*dyd) * es < (int64_t(1) << 30);
     const bool unit_q = xd->sw == 1 && dyd->sw == 1;
+    // The halo kernel's reduction split in two (beta = 0: both parts add into
+    // a zeroed dw) when its tiles leave compute units idle in a single round.
+    // MIC_WGRAD_SPLIT=off keeps one part (tests compare the two); =k (1-15)
+    // sets the ratio k : 1 wherever the split is allowed (measurements).
+    const char* split_env = getenv("MIC_WGRAD_SPLIT");
+    const int split_force = split_env ? atoi(split_env) : 0;
+    const bool split_allowed = beta == 0.0 && L >= 2 && !(split_env && strcmp(split_env, "off") == 0);
     double best = 0;
     bool found = false;
     for (const WgCandidate& wc : kWg) {
@@ -1119,9 +1130,28 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
         double cost = (double)rounds * wc.ns;
         if (wc.kind == WgKind::SPLIT && !unit_q) cost *= split_strided_penalty(pl.dt);
         if (wc.kind == WgKind::ROWS) cost /= Q;
+        // split: T tiles, U slots; the long parts (k / (k + 1) of the
+        // reduction) on T units, the short ones about T / (U - T) at a time on
+        // the other U - T.  Each short part also pays a fixed cost (prologue,
+        // first chunk, atomic epilogue: about 12 us measured), so past three
+        // short parts per unit k takes two more.  Where two workgroups fit on
+        // a CU the halves share the units: k = 1.  Measured on MI355X (AlexNet
+        // conv2, 200 tiles: 1746 us in one part, 1713 at k = 4, 1498 at k = 6;
+        // conv3, 216 tiles: 408 / 411 at k = 6 / 376 at k = 8; 144 tiles of
+        // 64 x 96: 654 / 447 at k = 2 / 523 at k = 4; Overfeat L2, 200 tiles
+        // two to a CU: 867 / 717 at k = 1 / 802 at k = 6); the gain seldom
+        // beats 15%, which the cost takes as its floor.
+        int split_k = 0;
+        if (wc.kind == WgKind::HALO && split_allowed && tiles > 0 && tiles < slots) {
+            const double r = (double)tiles / (double)(slots - tiles);
+            split_k = 2 * tiles <= slots || wc.res2 ? 1 : (int)std::ceil(r) + (r > 3.0 ? 2 : 0);
+            cost *= std::max((double)split_k / (split_k + 1), 0.85);
+            if (split_force >= 1 && split_force <= 15) split_k = split_force;
+        }
         if (!found || cost < best) {
             best = cost;
             pl.cand = wc.c;
+            pl.split_k = split_k;
             found = true;
         }
     }
@@ -1730,7 +1760,8 @@ mic_status mic_conv_backward_filter(mic_handle handle, double alpha, mic_tensor_
     Plan pl = make_wgrad_plan(handle, x_desc, x, dy_desc, dy, conv, dw_desc, dw, alpha, beta, true);
     if (pl.status != MIC_STATUS_SUCCESS) return pl.status;
     pl.p.tile_rev = tile_order_reversed();
-    const hipError_t err = is_wgh(pl.cand.v)   ? miconv::launch_bwd_filter_halo(pl.cand.v, pl.p, handle->stream)
+    const hipError_t err = is_wgh(pl.cand.v)
+                               ? miconv::launch_bwd_filter_halo(pl.cand.v, pl.p, pl.split_k, handle->stream)
                            : is_wgc(pl.cand.v) ? miconv::launch_bwd_filter_cl(pl.cand.v, pl.p, handle->stream)
                            : is_wgs(pl.cand.v) ? miconv::launch_bwd_filter_split(pl.cand.v, pl.p, handle->stream)
                            : is_wgr(pl.cand.v) ? miconv::launch_bwd_filter_rows(pl.cand.v, pl.p, handle->stream)

@@ -257,6 +257,62 @@ def test_alpha_beta_first_layer_kernels(stride, monkeypatch):
     assert np.array_equal(dw.double().cpu().numpy(), 0.5 * acc + 0.25 * old), var
 
 
+# the halo kernel's reduction in two parts (beta = 0, tiles that leave compute units idle in one
+# round): AlexNet conv2's geometry at N = 2 makes 200 tiles of 64 x 48 (long parts 4/5 of the 14
+# chunks), 152 of 64 x 64 (2/3); the 3x3 layer 216 tiles of 64 x 64 (6/7)
+SPLIT_CASES = [
+    ("conv2_n2", dict(N=2, C=96, Hh=27, Ww=27, K=256, R=5, S=5, stride=(1, 1), pads=(2, 2, 2, 2)),
+     ["auto", "wgh_f32x16_5x5_q27_64x48", "wgh_f32x16_5x5_q27_64x64", "wgh_f32x16_5x5_q27_64x48_ks4"]),
+    ("conv3_n2", dict(N=2, C=256, Hh=13, Ww=13, K=384, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
+     ["auto", "wgh_f32_3x3_q13_64x64", "wgh_f32_3x3_q13_64x64_ks4", "wgh_f32_3x3_64x96_ks4"]),
+    ("conv3_n2_f64", dict(N=2, C=256, Hh=13, Ww=13, K=384, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
+     ["auto", "wgh_f64_3x3_64x64_ks4", "wgh_f64_3x3_64x96"]),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: c[0])
+def test_split_reduction(case, monkeypatch):
+    """Two reduction parts added atomically into a zeroed dw: the same tolerance against the
+    oracle as one part, bit-identical with the tiles reversed and on a rerun (two terms onto zero
+    commute), and exact on integer data with alpha = 0.5."""
+    name, shape, variants = case
+    dtype = "f64" if name.endswith("f64") else "f32"
+    lay = _small(name, **shape, dtype=dtype)
+    x64, _ = H.inputs(lay)
+    N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
+    dy64 = _dy(lay, (N, K, P, Q))
+    ref, bound = oracle.conv2d_bwd_filter(x64, dy64, lay.w_shape, lay.stride, lay.padding)
+    x = H.to_device(x64, dtype)
+    dy = H.to_device(dy64, dtype)
+    xi64, _ = H.inputs(lay, ("integers", -4, 4), ("integers", -4, 4))
+    dyi64 = _dy(lay, (N, K, P, Q), integer=True)
+    acc_i, _ = oracle.conv2d_bwd_filter(xi64, dyi64, lay.w_shape, lay.stride, lay.padding)
+    xi = H.to_device(xi64, dtype)
+    dyi = H.to_device(dyi64, dtype)
+    for var in variants:
+        if var == "auto":
+            monkeypatch.delenv("MIC_FORCE_WGRAD_VARIANT", raising=False)
+        else:
+            monkeypatch.setenv("MIC_FORCE_WGRAD_VARIANT", var)
+        print("case", name, var, flush=True)
+        what = "%s/%s" % (name, var)
+        monkeypatch.setenv("MIC_WGRAD_SPLIT", "off")
+        one = _run(lay, x, dy, _out(lay))
+        monkeypatch.delenv("MIC_WGRAD_SPLIT")
+        two = _run(lay, x, dy, _out(lay))
+        for got, how in ((one, "one part"), (two, "two parts")):
+            H.check(dtype, got.double().cpu().numpy(), ref, bound, what=what + " " + how,
+                    rel_scale=H.rel_l2_scale(N * P * Q))
+        assert not torch.equal(one, two) or var == "auto", what + ": the split changed no bit (not taken?)"
+        monkeypatch.setenv("MIC_TILE_ORDER", "reverse")
+        rev = _run(lay, x, dy, _out(lay))
+        monkeypatch.delenv("MIC_TILE_ORDER")
+        assert torch.equal(two, rev), what + ": reversed tile order changed the two-part result"
+        assert torch.equal(two, _run(lay, x, dy, _out(lay))), what + ": rerun not bit-identical"
+        dw = _run(lay, xi, dyi, _out(lay), alpha=0.5)
+        assert np.array_equal(dw.double().cpu().numpy(), 0.5 * acc_i), what + ": integer data not exact"
+
+
 def test_wgrad_error_statuses_on_device():
     lay = workloads.TINY[0]
     x = torch.zeros(lay.x_shape, device=H.dev())
