@@ -270,8 +270,13 @@ mic_status mic_conv_backward_data_kernel_name(mic_handle handle, mic_filter_desc
  * (N, K, P, Q).  Element types (x, dy, dw): (F32, F32, F32), (F64, F64,
  * F64), (BF16, BF16, F32).  x and dy with any element strides; dw packed.
  * alpha, beta, ownership and size rules as for mic_conv_forward.  No
- * workspace: the reduction over N*P*Q positions is not split across
- * workgroups, so the parallelism is the number of dw tiles.
+ * workspace: the reduction over N*P*Q positions is split across at most two
+ * workgroups.  With beta == 0 and dw tiles too few to fill the GPU, the call
+ * first zeroes dw, then two workgroups per tile add alpha times their
+ * partial sums into it with atomic adds; two terms added onto zero give the
+ * same bits in either order, so the result is still deterministic (reruns
+ * and any workgroup order bit-identical).  dw's prior contents are not read
+ * when beta == 0.
  *
  * Errors: MIC_STATUS_BAD_PARAM (null handle/descriptor/pointer, unset
  * descriptor, dy dims not the forward output dims), MIC_STATUS_NOT_SUPPORTED
