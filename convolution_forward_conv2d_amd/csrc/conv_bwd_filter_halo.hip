@@ -92,6 +92,26 @@ __device__ __forceinline__ void wgh_load(double& v, __amdgpu_buffer_rsrc_t r, ui
     v = __hiloint2double((int)t[1], (int)t[0]);
 }
 
+// a global element of type G into a staged register: bf16 (the upper half of
+// an fp32) widened exactly, fp32 / fp64 as they are
+template <class G, class T>
+__device__ __forceinline__ void wgh_gload(T& v, __amdgpu_buffer_rsrc_t r, uint32_t voff, int soff)
+{
+    if constexpr (std::is_same<G, uint16_t>::value)
+        v = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, soff, 0) << 16);
+    else
+        wgh_load(v, r, voff, soff);
+}
+
+template <class Pol, class = void>
+struct wgh_gin {
+    using type = typename Pol::In;
+};
+template <class Pol>
+struct wgh_gin<Pol, std::void_t<typename Pol::GIn>> {
+    using type = typename Pol::GIn;
+};
+
 template <int B, int E, class F>
 __device__ __forceinline__ void unroll_for(F&& f)
 {
@@ -102,18 +122,29 @@ __device__ __forceinline__ void unroll_for(F&& f)
 }
 }  // namespace
 
+// bf16 x and dy (GIn: their 2-byte storage) widened to fp32 as they are
+// staged, then the fp32 MFMA of P: products and sums in fp32, as the pages'
+// fp32 filter gradient, from inputs that are exact in fp32
+template <class P>
+struct WghBf16 : P {
+    using GIn = uint16_t;
+    static_assert(std::is_same<typename P::In, float>::value, "fp32 staging");
+};
+
 template <class Pol, int TM, int TN, int WAVES_M, int WAVES_N, int R, int S, int WPH, int PR, int PLANE, int KS,
           int QD>
 __global__ void __launch_bounds__(256 * KS)
 conv_bwd_filter_halo_kernel(const ConvParams p, int split_ch)
 {
-    using In = typename Pol::In;
+    using In = typename Pol::In;                     // staged (LDS) element
+    using GIn = typename wgh_gin<Pol>::type;         // stored element of x and dy
     using AccV = typename Pol::AccV;
     constexpr int NT = 256;                          // threads per half
     constexpr int NTT = NT * KS;                     // threads of the workgroup
     constexpr int BM = Pol::BM;
     constexpr int G = Pol::G;
     constexpr int ES = (int)sizeof(In);
+    constexpr int GES = (int)sizeof(GIn);
     constexpr int RS = R * S;
     constexpr int RS1 = RS > 0 ? RS : 1;             // (pairs: R = 0; divisions by RS not taken)
     constexpr int WM = TM / WAVES_M;
@@ -199,8 +230,8 @@ conv_bwd_filter_halo_kernel(const ConvParams p, int split_ch)
                              (int64_t)(p.Q - 1) * p.sdq + 1;
     const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + (int64_t)(p.C - 1) * p.sxc + (int64_t)(p.H - 1) * p.sxh +
                             (int64_t)(p.W - 1) * p.sxw + 1;
-    const __amdgpu_buffer_rsrc_t dr = wgh_rsrc(p.w, dy_elems * ES);
-    const __amdgpu_buffer_rsrc_t xr = wgh_rsrc(p.x, x_elems * ES);
+    const __amdgpu_buffer_rsrc_t dr = wgh_rsrc(p.w, dy_elems * GES);
+    const __amdgpu_buffer_rsrc_t xr = wgh_rsrc(p.x, x_elems * GES);
 
     // ---- DY loader geometry: filter row kr, first position q0, first row rh
     const int ltid = DY_ALL ? (int)threadIdx.x : tid;
@@ -209,13 +240,13 @@ conv_bwd_filter_halo_kernel(const ConvParams p, int split_ch)
     const int rh = DY_ALL ? 0 : half;
     const bool k_ok = m0 + kr < p.M;
     // piece (row pr, column qj): dy_tb + dy_rowc[pr] + dy_col[qj], each past dy where invalid
-    const uint32_t dy_tb = k_ok ? (uint32_t)(((m0 + kr) * p.sdk + rh * p.sdp + q0 * p.sdq) * ES) : kWghOutside;
+    const uint32_t dy_tb = k_ok ? (uint32_t)(((m0 + kr) * p.sdk + rh * p.sdp + q0 * p.sdq) * GES) : kWghOutside;
     uint32_t dy_row[PRH], dy_col[QPT];
 #pragma unroll
     for (int i = 0; i < PRH; ++i)
-        dy_row[i] = rh + RSTEP * i < PR ? (uint32_t)(RSTEP * i * p.sdp * ES) : kWghOutside;
+        dy_row[i] = rh + RSTEP * i < PR ? (uint32_t)(RSTEP * i * p.sdp * GES) : kWghOutside;
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) dy_col[j] = q0 + TPK * j < p.Q ? (uint32_t)(TPK * j * p.sdq * ES) : kWghOutside;
+    for (int j = 0; j < QPT; ++j) dy_col[j] = q0 + TPK * j < p.Q ? (uint32_t)(TPK * j * p.sdq * GES) : kWghOutside;
 
     In dy_val[NDY];
     In h_val[NH];
@@ -243,7 +274,7 @@ conv_bwd_filter_halo_kernel(const ConvParams p, int split_ch)
         }
         const bool ok = e < HU && c < p.C && (unsigned)w < (unsigned)p.W;
         h_row[i] = ok ? row : -(1 << 30);
-        h_voff[i] = (uint32_t)((c * p.sxc + w * p.sxw + row * p.sxh) * ES);   // (wraps; valid with a chunk's row)
+        h_voff[i] = (uint32_t)((c * p.sxc + w * p.sxw + row * p.sxh) * GES);   // (wraps; valid with a chunk's row)
         h_lds[i] = DY_ELEMS + chl * PLANE + hr * WPH + hc;
     }
 
@@ -258,21 +289,21 @@ conv_bwd_filter_halo_kernel(const ConvParams p, int split_ch)
     auto set_chunk = [&](int n, int pr0) {
         cn = n;
         cp0 = pr0;
-        dy_soff = (cn * p.sdn + cp0 * p.sdp) * ES;
-        x_soff = cn * p.sxn * ES;
+        dy_soff = (cn * p.sdn + cp0 * p.sdp) * GES;
+        x_soff = cn * p.sxn * GES;
         crow = PAIRS ? cp0 * p.u : cp0;
-        x_rowoff = (uint32_t)(crow * p.sxh * ES);
+        x_rowoff = (uint32_t)(crow * p.sxh * GES);
 #pragma unroll
         for (int i = 0; i < PRH; ++i) dy_rowc[i] = cp0 + rh + RSTEP * i < p.P ? dy_row[i] : kWghOutside;
     };
     auto load_piece = [&](auto qc) {
         constexpr int q = decltype(qc)::value;
         if constexpr (q < NDY) {
-            wgh_load(dy_val[q], dr, dy_tb + dy_rowc[q / QPT] + dy_col[q % QPT], dy_soff);
+            wgh_gload<GIn>(dy_val[q], dr, dy_tb + dy_rowc[q / QPT] + dy_col[q % QPT], dy_soff);
         } else {
             constexpr int i = q - NDY;
             const bool ok = (unsigned)(h_row[i] + crow) < (unsigned)p.H;
-            wgh_load(h_val[i], xr, ok ? h_voff[i] + x_rowoff : kWghOutside, x_soff);
+            wgh_gload<GIn>(h_val[i], xr, ok ? h_voff[i] + x_rowoff : kWghOutside, x_soff);
         }
     };
     auto store_piece = [&](auto qc, int buf) {
@@ -468,7 +499,7 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, int split_k, hipStrea
     if ((R > 0 && (p.u != 1 || p.R != R)) || p.v != 1 || p.S != S || p.Q + S - 1 > WPH || (QD > 0 && p.Q != QD))
         return hipErrorInvalidValue;
     // the buffer descriptors' range: x and dy under 2^30 bytes
-    constexpr int64_t ES = (int64_t)sizeof(typename Pol::In);
+    constexpr int64_t ES = (int64_t)sizeof(typename wgh_gin<Pol>::type);
     const int64_t dy_elems = (int64_t)(p.N - 1) * p.sdn + (int64_t)(p.M - 1) * p.sdk + (int64_t)(p.P - 1) * p.sdp +
                              (int64_t)(p.Q - 1) * p.sdq + 1;
     const int64_t x_elems = (int64_t)(p.N - 1) * p.sxn + (int64_t)(p.C - 1) * p.sxc + (int64_t)(p.H - 1) * p.sxh +
@@ -530,7 +561,10 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, int split_k, hipStrea
     X(WGH_F32X16_PAIRS_S11_32x32, PolF32x16, 32, 32, 2, 2, 0, 11, 368, 1, 378, 2, 0)      \
     X(WGH_F32X16_PAIRS_S11_32x32_KS4, PolF32x16, 32, 32, 2, 2, 0, 11, 384, 1, 394, 4, 0)  \
     X(WGH_F64_3x3_W16_KS4, PolF64, 64, 64, 2, 2, 3, 3, 16, 7, 147, 4, 0)                  \
-    X(WGH_F64_3x3_W16_64x96, PolF64, 64, 96, 2, 2, 3, 3, 16, 7, 147, 2, 0)
+    X(WGH_F64_3x3_W16_64x96, PolF64, 64, 96, 2, 2, 3, 3, 16, 7, 147, 2, 0)                \
+    X(WGH_BF16_3x3_W16, WghBf16<PolF32>, 64, 64, 2, 2, 3, 3, 16, 13, 243, 2, 0)            \
+    X(WGH_BF16_3x3_Q13, WghBf16<PolF32>, 64, 64, 2, 2, 3, 3, 16, 14, 259, 2, 13)           \
+    X(WGH_BF16_3x3_W16_64x96_KS4, WghBf16<PolF32x16>, 64, 96, 2, 2, 3, 3, 16, 13, 247, 4, 0)
 
 hipError_t launch_bwd_filter_halo(Variant v, const ConvParams& p, int split_k, hipStream_t stream)
 {

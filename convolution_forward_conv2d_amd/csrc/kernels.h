@@ -79,6 +79,9 @@ enum class Variant : int {
     WGH_F32X16_PAIRS_S11_32x32_KS4, // ... four groups of waves per tile
     WGH_F64_3x3_W16_KS4,            // fp64 3x3 64x64, four groups of waves per tile
     WGH_F64_3x3_W16_64x96,          // fp64 3x3 64x96
+    WGH_BF16_3x3_W16,               // bf16 x and dy staged as fp32: 3x3 64x64
+    WGH_BF16_3x3_Q13,               // ... 13 columns
+    WGH_BF16_3x3_W16_64x96_KS4,     // ... 64x96, four groups of waves per tile
     WGC_BF16_64x64,         // filter gradient, bf16, channels-last x and dy (conv_bwd_filter_cl.hip)
     WGC_BF16_64x64_KS2,     // ... two groups of waves split the reduction
     WGC_BF16_64x64_KS3,     // ... three groups

@@ -11,7 +11,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <algorithm>
 #include <cmath>
 #include <new>
 
@@ -208,6 +207,11 @@ const WgCandidate kWg[] = {
     // tiles where 64x64 would take a second round (conv4: 324 -> 216 tiles, 1110 -> 765 us)
     {{Variant::WGH_F64_3x3_W16_KS4, 64, 64, "wgh_f64_3x3_64x64_ks4"}, DType::F64, WgKind::HALO, 3, 3, 16, 48.1, 1},
     {{Variant::WGH_F64_3x3_W16_64x96, 64, 96, "wgh_f64_3x3_64x96"}, DType::F64, WgKind::HALO, 3, 3, 16, 71.7, 1},
+    // bf16 x and dy widened to fp32 as they are staged, fp32 MFMA (the
+    // fp32 forms' instances; times from AlexNet conv3 at N = 64 in one part)
+    {{Variant::WGH_BF16_3x3_W16, 64, 64, "wgh_bf16_3x3_64x64"}, DType::BF16, WgKind::HALO, 3, 3, 16, 29.5, 1},
+    {{Variant::WGH_BF16_3x3_Q13, 64, 64, "wgh_bf16_3x3_q13_64x64"}, DType::BF16, WgKind::HALO, 3, 3, 16, 32.8, 1, 13},
+    {{Variant::WGH_BF16_3x3_W16_64x96_KS4, 64, 96, "wgh_bf16_3x3_64x96_ks4"}, DType::BF16, WgKind::HALO, 3, 3, 16, 31.3, 1},
     {{Variant::WGS_F32_32x32, 32, 32, "wgs_f32_32x32"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 12.5, 1},
     {{Variant::WGS_F32_16x16, 16, 16, "wgs_f32_16x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 7.1, 2},
     {{Variant::WGS_F32_8x16, 8, 16, "wgs_f32_8x16"}, DType::F32, WgKind::SPLIT, 0, 0, 0, 4.5, 2},
@@ -241,7 +245,8 @@ bool is_wgh(Variant v)
            v == Variant::WGH_F32_3x3_W16_64x96_KS4 || v == Variant::WGH_F32_3x3_Q12_64x96_KS4 ||
            v == Variant::WGH_F32X16_5x5_Q20_64x48_KS4 || v == Variant::WGH_F32X16_5x5_Q27_64x48_KS4 ||
            v == Variant::WGH_F32X16_PAIRS_S11_32x32 || v == Variant::WGH_F32X16_PAIRS_S11_32x32_KS4 ||
-           v == Variant::WGH_F64_3x3_W16_KS4 || v == Variant::WGH_F64_3x3_W16_64x96;
+           v == Variant::WGH_F64_3x3_W16_KS4 || v == Variant::WGH_F64_3x3_W16_64x96 ||
+           v == Variant::WGH_BF16_3x3_W16 || v == Variant::WGH_BF16_3x3_Q13 || v == Variant::WGH_BF16_3x3_W16_64x96_KS4;
 }
 
 bool is_wgr(Variant v) { return v == Variant::WGR_F32_S11_V2 || v == Variant::WGR_F32_S11_V4; }
@@ -1139,13 +1144,17 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
         // conv2, 200 tiles: 1746 us in one part, 1713 at k = 4, 1498 at k = 6;
         // conv3, 216 tiles: 408 / 411 at k = 6 / 376 at k = 8; 144 tiles of
         // 64 x 96: 654 / 447 at k = 2 / 523 at k = 4; Overfeat L2, 200 tiles
-        // two to a CU: 867 / 717 at k = 1 / 802 at k = 6); the gain seldom
-        // beats 15%, which the cost takes as its floor.
+        // two to a CU: 867 / 717 at k = 1 / 802 at k = 6).
         int split_k = 0;
         if (wc.kind == WgKind::HALO && split_allowed && tiles > 0 && tiles < slots) {
+            // the 5x5 forms on 64 x 64 tiles gain far less than k / (k + 1)
+            // (AlexNet conv2, 152 tiles: 1859 -> 1646 us at k = 2, where 200
+            // tiles of 64 x 48 at k = 6 take 1498; Overfeat L2: 981 -> 844):
+            // not chosen split
+            if (wc.r == 5 && wc.c.tn == 64 && !force) continue;
             const double r = (double)tiles / (double)(slots - tiles);
             split_k = 2 * tiles <= slots || wc.res2 ? 1 : (int)std::ceil(r) + (r > 3.0 ? 2 : 0);
-            cost *= std::max((double)split_k / (split_k + 1), 0.85);
+            cost *= (double)split_k / (split_k + 1);
             if (split_force >= 1 && split_force <= 15) split_k = split_force;
         }
         if (!found || cost < best) {

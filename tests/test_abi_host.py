@@ -467,8 +467,9 @@ def test_wgrad_kernel_choice_host_only():
     save a round (AlexNet conv4; Overfeat L3-L5 in the form that steps along their 12-column output
     rows only, as AlexNet conv2/conv3/conv5 and Overfeat L2 along 27, 13 and 20), the vector-ALU
     row-staged kernel for the strided
-    11-wide first layers, the split-reduction kernel where dw has few tiles or where its finer
-    tiles round better (AlexNet conv2, the bf16 layers), the gather kernel for channels-last bf16."""
+    11-wide first layers, the split-reduction kernel where dw has few tiles (the tiny layer), and
+    for bf16 the halo kernel with x and dy widened to fp32 as they are staged (dy here in NCHW;
+    with channels-last x and dy the channels-last kernel, tested below)."""
     want = {"tiny": "wgs_f32_8x16",
             "alexnet_conv2": "wgh_f32x16_5x5_q27_64x48", "alexnet_conv3": "wgh_f32_3x3_q13_64x64",
             "alexnet_conv4": "wgh_f32_3x3_64x96_ks4", "alexnet_conv5": "wgh_f32_3x3_q13_64x64",
@@ -484,11 +485,10 @@ def test_wgrad_kernel_choice_host_only():
             # 384 x 3456 (conv4): 64x96 tiles in one round; else 64x64 with four wave groups
             want64 = "wgh_f64_3x3_64x96" if "conv4" in lay.name else "wgh_f64_3x3_64x64_ks4"
             assert name == want64, (lay.name, name)
-        elif lay.name.endswith("nhwc"):
-            # channels-last: the split kernel's position-ordered loads would gather
-            assert name.startswith("wg_%s_" % lay.dtype), (lay.name, name)
         else:
-            assert name == "wgs_bf16_32x32", (lay.name, name)
+            # bf16: 64x96 tiles with four wave groups, the reduction in two parts (144 tiles on
+            # conv3 / conv5, 216 on conv4)
+            assert name == "wgh_bf16_3x3_64x96_ks4", (lay.name, name)
 
 
 def test_wgrad_split_kernel_needs_small_tensors(monkeypatch):

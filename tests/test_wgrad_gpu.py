@@ -56,6 +56,8 @@ WG_VARIANTS["f32"] += ["wgr_f32_s11_v2", "wgr_f32_s11_v4"]
 # the channels-last bf16 kernel (wgc_) takes x and dy with channel stride 1 and
 # 8-aligned strides and channel counts
 WG_VARIANTS["bf16"] += ["wgc_bf16_64x64", "wgc_bf16_64x64_ks2", "wgc_bf16_64x64_ks3"]
+# the halo kernel on bf16 x and dy, widened to fp32 as they are staged (fp32 MFMA)
+WG_VARIANTS["bf16"] += ["wgh_bf16_3x3_64x64", "wgh_bf16_3x3_q13_64x64", "wgh_bf16_3x3_64x96_ks4"]
 _MAY_REFUSE = ("wgh_", "wgr_", "wgc_")
 _ran = set()
 
@@ -267,6 +269,8 @@ SPLIT_CASES = [
      ["auto", "wgh_f32_3x3_q13_64x64", "wgh_f32_3x3_q13_64x64_ks4", "wgh_f32_3x3_64x96_ks4"]),
     ("conv3_n2_f64", dict(N=2, C=256, Hh=13, Ww=13, K=384, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
      ["auto", "wgh_f64_3x3_64x64_ks4", "wgh_f64_3x3_64x96"]),
+    ("conv3_n2_bf16", dict(N=2, C=256, Hh=13, Ww=13, K=384, R=3, S=3, stride=(1, 1), pads=(1, 1, 1, 1)),
+     ["auto", "wgh_bf16_3x3_q13_64x64", "wgh_bf16_3x3_64x96_ks4"]),
 ]
 
 
@@ -276,7 +280,7 @@ def test_split_reduction(case, monkeypatch):
     oracle as one part, bit-identical with the tiles reversed and on a rerun (two terms onto zero
     commute), and exact on integer data with alpha = 0.5."""
     name, shape, variants = case
-    dtype = "f64" if name.endswith("f64") else "f32"
+    dtype = name.rsplit("_", 1)[1] if name.endswith(("f64", "bf16")) else "f32"
     lay = _small(name, **shape, dtype=dtype)
     x64, _ = H.inputs(lay)
     N, K, P, Q = mic.output_shape(lay.x_shape, lay.w_shape, lay.stride, lay.padding)
