@@ -560,6 +560,7 @@ static hipError_t launch_wgh_variant(const ConvParams& p0, int split_k, hipStrea
     X(WGH_F32X16_5x5_Q27_64x48_KS4, PolF32x16, 64, 48, 4, 1, 5, 5, 32, 4, 261, 4, 27)   \
     X(WGH_F32X16_PAIRS_S11_32x32, PolF32x16, 32, 32, 2, 2, 0, 11, 368, 1, 378, 2, 0)      \
     X(WGH_F32X16_PAIRS_S11_32x32_KS4, PolF32x16, 32, 32, 2, 2, 0, 11, 384, 1, 394, 4, 0)  \
+    X(WGH_F32X16_PAIRS_S11_32x64, PolF32x16, 32, 64, 2, 2, 0, 11, 368, 1, 378, 2, 0)      \
     X(WGH_F64_3x3_W16_KS4, PolF64, 64, 64, 2, 2, 3, 3, 16, 7, 147, 4, 0)                  \
     X(WGH_F64_3x3_W16_64x96, PolF64, 64, 96, 2, 2, 3, 3, 16, 7, 147, 2, 0)                \
     X(WGH_BF16_3x3_W16, WghBf16<PolF32>, 64, 64, 2, 2, 3, 3, 16, 13, 243, 2, 0)            \

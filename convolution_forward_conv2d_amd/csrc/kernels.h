@@ -77,6 +77,7 @@ enum class Variant : int {
     WGH_F32X16_5x5_Q27_64x48_KS4,  // 5x5, 27 columns, 64 x 48, four groups of waves per tile
     WGH_F32X16_PAIRS_S11_32x32,     // 11-wide filter rows, any height and row stride: (c, r) pairs staged
     WGH_F32X16_PAIRS_S11_32x32_KS4, // ... four groups of waves per tile
+    WGH_F32X16_PAIRS_S11_32x64,     // ... 32 filters x 64 columns
     WGH_F64_3x3_W16_KS4,            // fp64 3x3 64x64, four groups of waves per tile
     WGH_F64_3x3_W16_64x96,          // fp64 3x3 64x96
     WGH_BF16_3x3_W16,               // bf16 x and dy staged as fp32: 3x3 64x64

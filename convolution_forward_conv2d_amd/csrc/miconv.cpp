@@ -203,6 +203,9 @@ const WgCandidate kWg[] = {
     // filter height and row stride (speech layer 2: 21 x 11 at stride (2, 1))
     {{Variant::WGH_F32X16_PAIRS_S11_32x32, 32, 32, "wgh_f32x16_pairs_s11_32x32"}, DType::F32, WgKind::HALO, 0, 11, 368, 7.4, 1},
     {{Variant::WGH_F32X16_PAIRS_S11_32x32_KS4, 32, 32, "wgh_f32x16_pairs_s11_32x32_ks4"}, DType::F32, WgKind::HALO, 0, 11, 384, 8.0, 1},
+    // 32 x 64: half the tiles, so that a two-part split fits one round (speech
+    // L2: 116 tiles, 4232 us in one part, 2135 at k = 1; 231 of 32 x 32: 2877)
+    {{Variant::WGH_F32X16_PAIRS_S11_32x64, 32, 64, "wgh_f32x16_pairs_s11_32x64"}, DType::F32, WgKind::HALO, 0, 11, 368, 9.2, 1},
     // fp64: four wave groups (AlexNet-shape conv3 / conv5 560 -> 519 us); 64x96
     // tiles where 64x64 would take a second round (conv4: 324 -> 216 tiles, 1110 -> 765 us)
     {{Variant::WGH_F64_3x3_W16_KS4, 64, 64, "wgh_f64_3x3_64x64_ks4"}, DType::F64, WgKind::HALO, 3, 3, 16, 48.1, 1},
@@ -245,6 +248,7 @@ bool is_wgh(Variant v)
            v == Variant::WGH_F32_3x3_W16_64x96_KS4 || v == Variant::WGH_F32_3x3_Q12_64x96_KS4 ||
            v == Variant::WGH_F32X16_5x5_Q20_64x48_KS4 || v == Variant::WGH_F32X16_5x5_Q27_64x48_KS4 ||
            v == Variant::WGH_F32X16_PAIRS_S11_32x32 || v == Variant::WGH_F32X16_PAIRS_S11_32x32_KS4 ||
+           v == Variant::WGH_F32X16_PAIRS_S11_32x64 ||
            v == Variant::WGH_F64_3x3_W16_KS4 || v == Variant::WGH_F64_3x3_W16_64x96 ||
            v == Variant::WGH_BF16_3x3_W16 || v == Variant::WGH_BF16_3x3_Q13 || v == Variant::WGH_BF16_3x3_W16_64x96_KS4;
 }
@@ -1154,7 +1158,10 @@ Plan make_wgrad_plan(const mic_handle_st* h, const mic_tensor_desc_st* xd, const
             if (wc.r == 5 && wc.c.tn == 64 && !force) continue;
             const double r = (double)tiles / (double)(slots - tiles);
             split_k = 2 * tiles <= slots || wc.res2 ? 1 : (int)std::ceil(r) + (r > 3.0 ? 2 : 0);
-            cost *= (double)split_k / (split_k + 1);
+            // past six short parts per idle CU the fixed costs eat the gain
+            // (speech L2, 231 tiles of 32 x 32: 2896 -> 2881 us at k = 12)
+            if (split_k > 8 && !(split_force >= 1 && split_force <= 15)) split_k = 0;
+            if (split_k > 0) cost *= (double)split_k / (split_k + 1);
             if (split_force >= 1 && split_force <= 15) split_k = split_force;
         }
         if (!found || cost < best) {

@@ -476,7 +476,7 @@ def test_wgrad_kernel_choice_host_only():
             "overfeat_l1": "wgr_f32_s11_v4", "overfeat_l2": "wgh_f32x16_5x5_q20_64x48",
             "overfeat_l3": "wgh_f32_3x3_q12_64x96", "overfeat_l4": "wgh_f32_3x3_q12_64x96",
             "overfeat_l5": "wgh_f32_3x3_q12_64x96",
-            "speech_l1": "wgr_f32_s11_v2", "speech_l2": "wgh_f32x16_pairs_s11_32x32"}
+            "speech_l1": "wgr_f32_s11_v2", "speech_l2": "wgh_f32x16_pairs_s11_32x64"}
     for lay in workloads.ALL_LAYERS:
         name = _wgrad_name(lay)
         if lay.name in want:

@@ -47,7 +47,8 @@ WG_VARIANTS["f32"] += ["wgh_f32_3x3_q12_64x96", "wgh_f32_3x3_q13_64x64", "wgh_f3
                        "wgh_f32x16_5x5_q27_64x64", "wgh_f32x16_5x5_q20_64x48", "wgh_f32x16_5x5_q27_64x48",
                        "wgh_f32_3x3_q13_64x64_ks4", "wgh_f32_3x3_64x96_ks4", "wgh_f32_3x3_q12_64x96_ks4",
                        "wgh_f32x16_5x5_q20_64x48_ks4", "wgh_f32x16_5x5_q27_64x48_ks4",
-                       "wgh_f32x16_pairs_s11_32x32", "wgh_f32x16_pairs_s11_32x32_ks4"]
+                       "wgh_f32x16_pairs_s11_32x32", "wgh_f32x16_pairs_s11_32x32_ks4",
+                       "wgh_f32x16_pairs_s11_32x64"]
 # the first-layer kernels on the vector ALU (wgr_): 11-wide filter rows at column stride 2 or 4
 WG_VARIANTS["f32"] += ["wgr_f32_s11_v2", "wgr_f32_s11_v4"]
 # the halo variants (wgh_) take stride-1 layers of their filter size whose rows fit their pitch, the
