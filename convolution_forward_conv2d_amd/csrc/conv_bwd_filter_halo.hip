@@ -370,41 +370,38 @@ conv_bwd_filter_halo_kernel(const ConvParams p, int split_ch)
             return t;
         }
     };
+    // operands are read PD steps ahead of their MFMA: two where a step has at
+    // most four MFMAs, too few to cover an LDS read's latency on their own
+    constexpr int PD = FM * FN <= 4 ? 2 : 1;
     auto run_steps = [&](auto hc, const In* buf, int cur) {
         constexpr int H = decltype(hc)::value;
         constexpr int NSTEP = SEGP - H * SEGH < SEGH ? SEGP - H * SEGH : SEGH;   // this half's steps
-        // operands are read one step ahead of their MFMA
-        In a[FM], b[FN];
+        In a[PD + 1][FM], b[PD + 1][FN];             // step t's operands in slot t % (PD + 1)
+        auto read_step = [&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            if constexpr (u < NSTEP) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) a[i] = buf[a_base[i] + step_off(hc, 0)];
+                for (int i = 0; i < FM; ++i) a[u % (PD + 1)][i] = buf[a_base[i] + step_off(hc, u)];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) b[j] = buf[b_base[j] + step_off(hc, 0)];
+                for (int j = 0; j < FN; ++j) b[u % (PD + 1)][j] = buf[b_base[j] + step_off(hc, u)];
+            }
+        };
+        unroll_for<0, PD>([&](auto uc) { read_step(uc); });
         unroll_for<0, NSTEP>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             unroll_for<0, NL>([&](auto qc) {
                 if constexpr (decltype(qc)::value * (NSTEP / 2) / NL == t) load_piece(qc);
             });
-            In an[FM], bn[FN];
-            if constexpr (t + 1 < NSTEP) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i) an[i] = buf[a_base[i] + step_off(hc, t + 1)];
-#pragma unroll
-                for (int j = 0; j < FN; ++j) bn[j] = buf[b_base[j] + step_off(hc, t + 1)];
-            }
+            read_step(std::integral_constant<int, t + PD>{});
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = Pol::mfma_s(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = Pol::mfma_s(a[t % (PD + 1)][i], b[t % (PD + 1)][j], acc[i][j]);
             unroll_for<0, NL>([&](auto qc) {
                 if constexpr (NSTEP / 2 + decltype(qc)::value * (NSTEP - NSTEP / 2) / NL == t) store_piece(qc, cur ^ 1);
             });
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (t + 1 < NSTEP) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i) a[i] = an[i];
-#pragma unroll
-                for (int j = 0; j < FN; ++j) b[j] = bn[j];
-            }
         });
     };
     for (int ch = 0; ch < nch; ++ch) {
