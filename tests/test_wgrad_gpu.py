@@ -5,7 +5,9 @@ full for every kernel variant, also with the tiles run in reverse order (bit
 for bit the same result); every workload layer's filter gradient is run at
 full size and its whole dw compared with the whole oracle output (canary
 cells around dw untouched, reruns bit-identical), and integer-valued inputs
-are bit-exact on sampled (k, c, r, s) coordinates in every layout.  x is the layer's
+are bit-exact on sampled (k, c, r, s) coordinates in every layout.  The halo kernel's
+reduction in two parts (added atomically into a zeroed dw) is compared with one part, in
+reversed tile order and on reruns (bit-identical: two terms added onto zero commute).  x is the layer's
 seeded input, dy seeded uniform [-1, 1] (tensor id 3), both rounded to the
 layer's storage type.
 
